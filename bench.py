@@ -1,0 +1,245 @@
+"""Decode-step benchmark: one attention layer's absorbed-MLA decode on one GPU.
+
+A step is the whole hot path on one batch: rope_relocate_q (per distinct
+segment shift) -> mla_absorb_q -> mla_decode_splitkv -> mla_combine_lse ->
+mla_out_uv, on seeded synthetic inputs already resident in HBM.  Prints one
+JSON line with decode tokens/s, the decode kernel's achieved HBM GB/s against
+the MI355X roofline, and the fp64 CPU oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload small]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode tokens/s + achieved HBM GB/s & % roofline (latent-cache attention)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+MALL_BYTES = 256 << 20          # Infinity Cache: rotate caches so every step reads HBM
+DECODE_SRC = os.path.join(ROOT, "mla_latent_cache_amd", "csrc", "mla_decode_bf16.hip")
+SEEDS = {"toy": 0, "small": 1, "dsv3": 2, "long": 3, "merge": 4}
+
+
+def _rows(x):
+    return [int(s.seq_lens.sum()) for s in x.segments]
+
+
+def algorithmic(x):
+    """Decode-kernel algorithmic bytes and FLOPs per launch: every stored row
+    [c_t | kr_t] read once (1152 B in bf16), and per row and query row
+    2 * (576 + 512) FLOPs (scores over [c | kr], weighted sum over c)."""
+    sp = x.spec
+    el = x.segments[0].cache.element_size()
+    nbytes = sum(r * sp.row_width * el for r in _rows(x))
+    flops = sum(2 * r * s.head_count * sp.s_q * (sp.row_width + sp.d_c) for r, s in zip(_rows(x), x.segments))
+    return nbytes, flops
+
+
+def kernel_hash() -> str:
+    with open(DECODE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per decode launch from the committed counter summary, or None
+    when there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", txt)
+    m_val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_hash or not m_val or m_hash.group(1) != kernel_hash():
+        return None
+    return float(m_val.group(1))
+
+
+def cpu_baseline(x, budget_s: float):
+    """Time the oracle as it stands on a bounded sample of the same inputs:
+    whole requests (all heads) in order until the budget is spent; for very
+    long requests, chunks of heads.  Reported in query tokens/s."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    import oracle.mla_direct as O
+
+    def f64(t):
+        return t.to(torch.float64).numpy()
+
+    sp = x.spec
+    segs = [O.OracleSegment(rows=(lambda b, s=s: f64(s.rows(b))), shift=s.shift.tolist(),
+                            head_begin=s.head_begin, head_count=s.head_count, causal=s.causal)
+            for s in x.segments]
+    q_nope, q_pe, w_uk, w_uv = f64(x.q_nope), f64(x.q_pe), f64(x.w_uk), f64(x.w_uv)
+    q_pos = x.q_pos.numpy()
+    rows_per_req = max(_rows(x)) / sp.batch
+    hchunk = sp.heads if rows_per_req * sp.heads <= 64 * 4096 else max(1, (64 * 4096) // int(rows_per_req) or 1)
+    done_pairs = 0
+    t0 = time.perf_counter()
+    b = 0
+    while True:
+        for h0 in range(0, sp.heads, hchunk):
+            hs = list(range(h0, min(sp.heads, h0 + hchunk)))
+            O.direct_mla_decode(q_nope, q_pe, q_pos, w_uk, w_uv, segs, x.scale, x.rope_base, sp.s_q,
+                                requests=[b % sp.batch], heads=hs)
+            done_pairs += len(hs)
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+        b += 1
+    el = time.perf_counter() - t0
+    tokens = done_pairs / sp.heads * sp.s_q
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return {"value": tokens / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done_pairs} (request, head) pairs = {tokens:.3g} query tokens of the same seeded "
+                      f"workload, fp64 direct form, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="small", choices=["small", "dsv3", "long", "merge", "toy"])
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--n-wg", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--detail", action="store_true", help="also time each call separately")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: the decode path has no multi-GPU mode in this library "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mla_inputs as M
+    from mla_latent_cache_amd import load
+    from mla_latent_cache_amd.step import DecodeStep, StepSegment, run_calls, step_from_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    load()
+    torch.cuda.set_device(0)
+    seed = SEEDS[args.workload] if args.seed is None else args.seed
+    x = M.make(args.workload, seed)
+    sp = x.spec
+
+    # Cache copies: enough that the rotated set exceeds twice the 256 MiB
+    # Infinity Cache, so every step streams its cache from HBM.
+    nbytes, flops = algorithmic(x)
+    n_copies = max(1, math.ceil(2 * MALL_BYTES / max(1, nbytes)))
+    base = step_from_inputs(x, n_wg=args.n_wg)
+    steps = [base]
+    for _ in range(n_copies - 1):
+        segs = []
+        for bs, s in zip(base.segments, x.segments):
+            shift_tok = x.token_shift(s)
+            segs.append(StepSegment(cache=bs.cache.clone(), seq_lens=bs.seq_lens, seq_lens_host=s.seq_lens.tolist(),
+                                    shift=shift_tok.to(bs.cache.device), shift_host=shift_tok.tolist(),
+                                    block_table=bs.block_table, head_begin=bs.head_begin,
+                                    head_count=bs.head_count, causal=bs.causal))
+        steps.append(DecodeStep(base.q_nope, base.q_pe, base.q_pos, base.w_uk, base.w_uv, segs, sp.batch, sp.s_q,
+                                x.scale, x.rope_base, n_wg=args.n_wg, n_split=base.n_split))
+    stream = torch.cuda.current_stream()
+    bound = [st.bind(stream) for st in steps]
+
+    def one(i, ev=None):
+        pre, dec, post = bound[i % n_copies]
+        run_calls(pre)
+        if ev is not None:
+            ev[0].record(stream)
+        run_calls(dec)
+        if ev is not None:
+            ev[1].record(stream)
+        run_calls(post)
+
+    for i in range(args.warmup):
+        one(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one(i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_us = 1000.0 * sum(dec_ms) / len(dec_ms)
+
+    detail = None
+    if args.detail:
+        names = ["rope", "absorb", "decode", "combine", "out_uv"]
+        detail = {}
+        reps = 50
+        pre, dec, post = bound[0]
+        groups = {"rope": pre[:-1], "absorb": pre[-1:], "decode": dec, "combine": post[:1], "out_uv": post[1:]}
+        for nm in names:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            for j in range(5):
+                run_calls(bound[j % n_copies][0] if nm in ("rope", "absorb") else groups[nm])
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for j in range(reps):
+                pj, dj, qj = bound[j % n_copies]
+                g = {"rope": pj[:-1], "absorb": pj[-1:], "decode": dj, "combine": qj[:1], "out_uv": qj[1:]}[nm]
+                run_calls(g)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            detail[nm + "_us"] = round(1000.0 * e0.elapsed_time(e1) / reps, 3)
+
+    n_tok = sp.n_tok
+    value = n_tok * args.steps / elapsed
+    achieved = nbytes / (dec_us * 1e-6) / 1e9
+    traffic = traffic_from_profile(args.workload)
+    res = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1000.0 * elapsed / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if sp.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": sp.description, "name": sp.name, "batch": sp.batch, "heads": sp.heads,
+                   "s_q": sp.s_q, "d_c": sp.d_c, "d_rope": sp.d_rope, "d_nope": sp.d_nope, "d_v": sp.d_v,
+                   "cache_rows": sum(_rows(x)), "seed": seed, "cache_copies_rotated": n_copies,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "mla_decode_splitkv (decode_bf16_kernel)",
+                     "decode_us": round(dec_us, 3), "algorithmic_bytes": nbytes,
+                     "algorithmic_flops": flops,
+                     "tflops": round(flops / (dec_us * 1e-6) / 1e12, 2),
+                     "mfma_frac": round(flops / (dec_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "cpu_baseline": None,
+    }
+    if detail:
+        res["detail"] = detail
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,224 @@
+/*
+ * mla_latent.h -- C ABI of the absorbed Multi-head Latent Attention decode
+ * library for MI355X (gfx950).
+ *
+ * Pages this interface follows:
+ *  [T] "Multi-Head Latent Attention: How DeepSeek Compressed the Cache
+ *      Further" (MLA tutorial page), sections "Learn a Smaller Shared
+ *      Representation", "Move the Key Projection Into the Query", "Move the
+ *      Value Expansion After the Weighted Sum", "Position Rotations
+ *      Complicate the Absorption", "Count the Cache That Is Actually Stored".
+ *  [R] "RedKnot-MLA: Multi-Head Offline-Online Reuse for DeepSeek-V4
+ *      Long-Context Serving" (abstract): documents cached at canonical
+ *      position zero, query-side RoPE relocation, offline and online paths
+ *      merged before one shared output projection, the packed latent never
+ *      split.
+ *
+ * One decode step of one attention layer is five calls:
+ *   rope_relocate_q  -> q_rot      (per KV segment: rotary query at pos - shift)
+ *   mla_absorb_q     -> q_lat      (U_K^T q_nope, once per query)
+ *   mla_decode_splitkv -> partial (o_lat, lse) states per KV split / segment
+ *   mla_combine_lse  -> o_lat, lse (log-sum-exp merge of the partial states)
+ *   mla_out_uv       -> out        (U_V o_lat, once per query)
+ *
+ * Conventions shared by every call
+ *  - All tensor pointers are DEVICE pointers (HIP device memory), row-major,
+ *    densely packed in the shapes stated.  The caller allocates and owns every
+ *    buffer; the library never allocates device memory, never creates
+ *    streams and never synchronises the host.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    work is enqueued on it, asynchronously; results are ready once the
+ *    stream has reached that point.
+ *  - dtype arguments are MLA_BF16 (bf16 storage) or MLA_F32; arithmetic and
+ *    accumulation are fp32 throughout.  The bf16-cache decode requires
+ *    d_c = 512, d_rope = 64; the fp32-cache decode takes any d_c <= 512,
+ *    d_rope <= 128.
+ *  - Inputs and outputs must not alias.  Outputs are overwritten, never
+ *    accumulated into.
+ *  - Arguments are validated on the host before anything is enqueued.  On a
+ *    bad argument the call returns a nonzero mla_status, enqueues nothing and
+ *    records a message readable through mla_last_error() (per thread).  A
+ *    launch failure returns MLA_ERR_HIP.
+ *  - Numerics: log-sum-exp values are natural logarithms of
+ *    sum_t exp(scaled score); a query row with no visible key has lse = -inf
+ *    and output 0.  Rows a request may not see never enter any arithmetic.
+ */
+#ifndef MLA_LATENT_H
+#define MLA_LATENT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,        /* a required pointer is NULL */
+  MLA_ERR_SHAPE = 2,       /* a size is out of range or sizes disagree */
+  MLA_ERR_DTYPE = 3,       /* unknown dtype */
+  MLA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  MLA_ERR_UNSUPPORTED = 5, /* valid request the library does not implement */
+  MLA_ERR_WORKSPACE = 6,   /* reserved */
+  MLA_ERR_HIP = 7          /* the HIP runtime reported an error */
+} mla_status;
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+
+/*
+ * rope_relocate_q -- rotary query for one KV segment.
+ * [T] "Position Rotations Complicate the Absorption": the score has a separate
+ * position part q^R . k^R_t computed on rotated feature pairs.  [R]: a segment
+ * cached at canonical position zero is read by rotating the query by
+ * (true position - shift) instead of re-rotating the cached keys.
+ *
+ *   q_rot[t][h][2i:2i+2] = Rot((pos[t] - shift[t]) * base^(-2i/d_rope)) q_pe[t][h][2i:2i+2]
+ *   with Rot(a) = [[cos a, -sin a], [sin a, cos a]] (adjacent pairs).
+ *
+ * q_pe   [n_tok][n_heads][d_rope]  input, in_dtype, unrotated
+ * q_rot  [n_tok][n_heads][d_rope]  output, out_dtype (fp32 keeps the rotated
+ *                                  query exact to ~1e-7 for the decode call)
+ * pos    [n_tok] int64             true position of each query token
+ * shift  [n_tok] int64 or NULL     stored-to-true position shift of the
+ *                                  segment for that token's request (NULL = 0)
+ * The position difference is taken in int64 and the angle in fp64.
+ * d_rope must be even, 2..128.
+ */
+mla_status rope_relocate_q(const void* q_pe, int in_dtype, void* q_rot, int out_dtype,
+                           const int64_t* pos, const int64_t* shift, int n_tok, int n_heads,
+                           int d_rope, double base, void* stream);
+
+/*
+ * mla_absorb_q -- fold the key up-projection into the query.
+ * [T] "Move the Key Projection Into the Query": q^T (U_K c_t) = (U_K^T q)^T c_t,
+ * so the new query is transformed once and compared with the stored latents.
+ *
+ *   q_lat[t][h][j] = sum_i w_uk[h][i][j] * q_nope[t][h][i]
+ *
+ * q_nope [n_tok][n_heads][d_nope]  input, in_dtype
+ * w_uk   [n_heads][d_nope][d_c]    U_K of each head (maps d_c -> d_nope), in_dtype
+ * q_lat  [n_tok][n_heads][d_c]     output, out_dtype (fp32 accumulation; an fp32
+ *                                  q_lat keeps the decode scores exact to ~1e-6,
+ *                                  a bf16 one costs ~1e-3 in the scores)
+ */
+mla_status mla_absorb_q(const void* q_nope, const void* w_uk, int in_dtype, void* q_lat,
+                        int out_dtype, int n_tok, int n_heads, int d_nope, int d_c, void* stream);
+
+/*
+ * One KV segment read by mla_decode_splitkv.  Host struct holding device
+ * pointers.  A cache row is [c_t | k^R_t] (d_c + d_rope numbers, [T] "Count
+ * the Cache That Is Actually Stored"); rows are read whole, never split ([R]).
+ */
+typedef struct {
+  const void* cache;          /* contiguous: [batch][max_rows][d_c+d_rope];
+                                 paged: pool [n_pages][page_size][d_c+d_rope] */
+  const int32_t* block_table; /* paged: [batch][max_pages] physical page ids
+                                 (entries past a request's pages are ignored);
+                                 NULL => contiguous layout */
+  const int32_t* seq_lens;    /* [batch] valid rows T_b of each request, 0..max rows */
+  const void* q_rot;          /* [n_tok][n_heads][d_rope] rotary query for THIS segment
+                                 (output of rope_relocate_q with the segment's shift) */
+  int64_t max_rows;           /* contiguous: rows allocated per request (>= every T_b) */
+  int page_size;              /* paged: rows per page (the bf16 path takes 64) */
+  int max_pages;              /* paged: entries per block-table row */
+  int n_pages;                /* paged: pages in the pool (ids must be < n_pages) */
+  int head_begin;             /* heads [head_begin, head_begin+head_count) read it */
+  int head_count;
+  int causal;                 /* 0: every row visible; 1: query s of s_q sees
+                                 rows t <= T_b - s_q + s */
+  int part_begin;             /* this segment writes partial slots */
+  int n_split;                /* [part_begin, part_begin + n_split) of its rows */
+} mla_segment;
+
+/*
+ * mla_decode_splitkv -- the latent-cache attention pass.
+ * [T] "Move the Key Projection Into the Query" (score against the stored
+ * latent), "Position Rotations Complicate the Absorption" (content + position
+ * score, scaled, masked, softmaxed), "Move the Value Expansion After the
+ * Weighted Sum" (mix the latents, expand later).  [R]: separate KV segments
+ * give partial states merged later by mla_combine_lse.
+ *
+ * For every segment g, request b, query token s, head h in g's range, and each
+ * KV split j of g's rows of request b:
+ *   s_t   = scale * (q_lat[t][h] . c_t + q_rot_g[t][h] . k^R_t)     (t visible rows of split j)
+ *   o_part[tok][h][part_begin_g + j][:] = sum_t softmax_j(s)_t c_t   (fp32, normalised in the split)
+ *   lse_part[tok][h][part_begin_g + j]  = ln sum_t exp(s_t)          (-inf if the split is empty)
+ * where tok = b * s_q + s.  The library chooses the split boundaries (balanced
+ * over the grid) subject to at most n_split splits per request; every slot of
+ * [part_begin, part_begin + n_split) of every (tok, h in range) gets its lse
+ * written, and its o_part row too when the lse is finite.  Across segments the
+ * slot ranges of each head must tile [0, n_part) exactly.
+ *
+ * q_lat    [n_tok][n_heads][d_c]                 q_dtype, from mla_absorb_q; each
+ *          segment's q_rot has q_dtype too
+ * caches   cache_dtype.  MLA_BF16 caches take an fp32 query (split into bf16
+ *          hi + lo parts, two MFMAs per step) or a bf16 query (one MFMA);
+ *          MLA_F32 caches take an fp32 query.
+ * o_part   [n_tok][n_heads][n_part][d_c] fp32    output
+ * lse_part [n_tok][n_heads][n_part]      fp32    output
+ * n_tok = batch * s_q.  n_wg = workgroups per segment (0 = one per compute unit).
+ * bf16 path: d_c = 512, d_rope = 64, page_size = 64, s_q * head_count <= 512.
+ */
+mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q_lat, int q_dtype,
+                              int cache_dtype, int batch, int s_q, int n_heads, int d_c, int d_rope,
+                              float scale, float* o_part, float* lse_part, int n_part, int n_wg,
+                              void* stream);
+
+/*
+ * mla_combine_lse -- merge partial attention states by log-sum-exp.
+ * [R]: the offline and online paths are merged before one shared output
+ * projection.  For every row r (a (token, head) pair):
+ *   lse[r]   = ln sum_j exp(lse_part[r][j])      (slots with -inf skipped)
+ *   o_lat[r] = sum_j exp(lse_part[r][j] - lse[r]) o_part[r][j]
+ * A row whose slots are all -inf gives o_lat = 0, lse = -inf.  o_part rows of
+ * -inf slots are never read.
+ *
+ * o_part   [n_rows][n_part][d_c] fp32
+ * lse_part [n_rows][n_part]      fp32
+ * o_lat    [n_rows][d_c]         out_dtype (MLA_BF16 or MLA_F32)
+ * lse      [n_rows]              fp32, or NULL if not wanted
+ */
+mla_status mla_combine_lse(const float* o_part, const float* lse_part, int n_rows, int n_part,
+                           int d_c, void* o_lat, int out_dtype, float* lse, void* stream);
+
+/*
+ * mla_out_uv -- expand the mixed latent once per query.
+ * [T] "Move the Value Expansion After the Weighted Sum": U_V (sum_t a_t c_t)
+ * equals sum_t a_t (U_V c_t), so the value up-projection follows the sum.
+ *
+ *   out[t][h][i] = sum_j w_uv[h][i][j] * o_lat[t][h][j]
+ *
+ * o_lat [n_tok][n_heads][d_c]   o_dtype
+ * w_uv  [n_heads][d_v][d_c]     U_V of each head (maps d_c -> d_v), w_dtype
+ * out   [n_tok][n_heads][d_v]   out_dtype (fp32 accumulation)
+ */
+mla_status mla_out_uv(const void* o_lat, int o_dtype, const void* w_uv, int w_dtype, void* out,
+                      int out_dtype, int n_tok, int n_heads, int d_c, int d_v, void* stream);
+
+/* Text of a status code (static storage). */
+const char* mla_status_string(int status);
+
+/* Detail of the last failing call on this thread ("" if none). */
+const char* mla_last_error(void);
+
+/* Library ABI version (major * 100 + minor). */
+int mla_version(void);
+
+/* Compute units of the current device (0 on error): the default n_wg. */
+int mla_device_cu_count(void);
+
+/*
+ * Number of row shares the bf16 decode cuts one segment into for a grid of
+ * n_wg workgroups (0 = one per compute unit) when s_q * head_count query rows
+ * read it.  A request of T_b rows uses at most ceil(T_b / share) + 1 split
+ * slots, share = 32 * ceil(ceil(sum_b T_b / shares) / 32); a caller picks
+ * n_split from it.  Returns 0 on a bad argument.
+ */
+int mla_decode_shares(int s_q, int head_count, int n_wg);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_LATENT_H */

@@ -68,6 +68,8 @@ class Segment:
             return self.cache[b, :t]
         ps = self.page_size
         n_pages = (t + ps - 1) // ps
+        if n_pages == 0:
+            return self.cache.new_empty((0, self.cache.shape[-1]))
         ids = self.block_table[b, :n_pages].long()
         return self.cache[ids].reshape(n_pages * ps, -1)[:t]
 

@@ -1,0 +1,232 @@
+// C ABI of the MLA decode library: argument validation, then launches on the
+// caller's stream.  Declarations and contracts: include/mla_latent.h.
+#include "../../include/mla_latent.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <vector>
+
+#include "mla_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mla_status fail(mla_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+mla_status ok() {
+  g_err[0] = '\0';
+  return MLA_OK;
+}
+
+mla_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dtype_ok(int dt) { return dt == MLA_F32 || dt == MLA_BF16; }
+
+int cu_count() {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lk(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+constexpr int kBf16Dc = 512;
+constexpr int kBf16Dr = 64;
+constexpr int kPage = 64;
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int st) {
+  switch (st) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL: return "null pointer";
+    case MLA_ERR_SHAPE: return "bad shape";
+    case MLA_ERR_DTYPE: return "bad dtype";
+    case MLA_ERR_ALIGN: return "misaligned pointer";
+    case MLA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MLA_ERR_WORKSPACE: return "workspace too small";
+    case MLA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* mla_last_error(void) { return g_err; }
+
+int mla_version(void) { return 100; }
+
+int mla_device_cu_count(void) { return cu_count(); }
+
+int mla_decode_shares(int s_q, int head_count, int n_wg) {
+  if (s_q <= 0 || head_count <= 0 || n_wg < 0 || (int64_t)s_q * head_count > 512) return 0;
+  const int wg = n_wg > 0 ? n_wg : cu_count();
+  if (wg <= 0) return 0;
+  int n_share = 0, n_rg = 0;
+  mla::decode_bf16_grid(s_q * head_count, wg, &n_share, &n_rg);
+  return n_share;
+}
+
+mla_status rope_relocate_q(const void* q_pe, int in_dtype, void* q_rot, int out_dtype, const int64_t* pos,
+                           const int64_t* shift, int n_tok, int n_heads, int d_rope, double base,
+                           void* stream) {
+  if (!q_pe || !q_rot || !pos) return fail(MLA_ERR_NULL, "rope_relocate_q: q_pe, q_rot and pos are required");
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
+    return fail(MLA_ERR_DTYPE, "rope_relocate_q: dtypes %d, %d", in_dtype, out_dtype);
+  if (n_tok < 0 || n_heads <= 0 || d_rope < 2 || d_rope > 128 || (d_rope & 1))
+    return fail(MLA_ERR_SHAPE, "rope_relocate_q: n_tok=%d n_heads=%d d_rope=%d", n_tok, n_heads, d_rope);
+  if (!(base > 1.0) || !std::isfinite(base)) return fail(MLA_ERR_SHAPE, "rope_relocate_q: base=%g", base);
+  if (n_tok == 0) return ok();
+  return hip_status(mla::launch_rope(q_pe, in_dtype == MLA_BF16, q_rot, out_dtype == MLA_BF16, pos, shift,
+                                     n_tok, n_heads, d_rope, base, (hipStream_t)stream),
+                    "rope_relocate_q launch");
+}
+
+mla_status mla_absorb_q(const void* q_nope, const void* w_uk, int in_dtype, void* q_lat, int out_dtype,
+                        int n_tok, int n_heads, int d_nope, int d_c, void* stream) {
+  if (!q_nope || !w_uk || !q_lat) return fail(MLA_ERR_NULL, "mla_absorb_q: null pointer");
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
+    return fail(MLA_ERR_DTYPE, "mla_absorb_q: dtypes %d, %d", in_dtype, out_dtype);
+  if (n_tok < 0 || n_heads <= 0 || d_nope <= 0 || d_nope > 256 || d_c <= 0 || d_c > 4096 || n_heads > 65535)
+    return fail(MLA_ERR_SHAPE, "mla_absorb_q: n_tok=%d n_heads=%d d_nope=%d d_c=%d", n_tok, n_heads, d_nope, d_c);
+  if (n_tok == 0) return ok();
+  return hip_status(mla::launch_absorb(q_nope, w_uk, in_dtype == MLA_BF16, q_lat, out_dtype == MLA_BF16, n_tok,
+                                       n_heads, d_nope, d_c, (hipStream_t)stream),
+                    "mla_absorb_q launch");
+}
+
+mla_status mla_out_uv(const void* o_lat, int o_dtype, const void* w_uv, int w_dtype, void* out, int out_dtype,
+                      int n_tok, int n_heads, int d_c, int d_v, void* stream) {
+  if (!o_lat || !w_uv || !out) return fail(MLA_ERR_NULL, "mla_out_uv: null pointer");
+  if (!dtype_ok(o_dtype) || !dtype_ok(w_dtype) || !dtype_ok(out_dtype))
+    return fail(MLA_ERR_DTYPE, "mla_out_uv: dtypes %d, %d, %d", o_dtype, w_dtype, out_dtype);
+  if (n_tok < 0 || n_heads <= 0 || n_heads > 65535 || d_c <= 0 || d_c > 1024 || d_v <= 0 || d_v > 4 * 65535)
+    return fail(MLA_ERR_SHAPE, "mla_out_uv: n_tok=%d n_heads=%d d_c=%d d_v=%d", n_tok, n_heads, d_c, d_v);
+  if (n_tok == 0) return ok();
+  return hip_status(mla::launch_out_uv(o_lat, o_dtype == MLA_BF16, w_uv, w_dtype == MLA_BF16, out,
+                                       out_dtype == MLA_BF16, n_tok, n_heads, d_c, d_v, (hipStream_t)stream),
+                    "mla_out_uv launch");
+}
+
+mla_status mla_combine_lse(const float* o_part, const float* lse_part, int n_rows, int n_part, int d_c,
+                           void* o_lat, int out_dtype, float* lse, void* stream) {
+  if (!o_part || !lse_part || !o_lat) return fail(MLA_ERR_NULL, "mla_combine_lse: null pointer");
+  if (!dtype_ok(out_dtype)) return fail(MLA_ERR_DTYPE, "mla_combine_lse: out_dtype %d", out_dtype);
+  if (n_rows < 0 || n_part <= 0 || d_c <= 0 || d_c > 1024)
+    return fail(MLA_ERR_SHAPE, "mla_combine_lse: n_rows=%d n_part=%d d_c=%d", n_rows, n_part, d_c);
+  if (n_rows == 0) return ok();
+  return hip_status(mla::launch_combine(o_part, lse_part, n_rows, n_part, d_c, o_lat, out_dtype == MLA_BF16,
+                                        lse, (hipStream_t)stream),
+                    "mla_combine_lse launch");
+}
+
+mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q_lat, int q_dtype,
+                              int cache_dtype, int batch, int s_q, int n_heads, int d_c, int d_rope, float scale,
+                              float* o_part, float* lse_part, int n_part, int n_wg, void* stream) {
+  if (!segs || !q_lat || !o_part || !lse_part) return fail(MLA_ERR_NULL, "mla_decode_splitkv: null pointer");
+  if (!dtype_ok(q_dtype) || !dtype_ok(cache_dtype))
+    return fail(MLA_ERR_DTYPE, "mla_decode_splitkv: dtypes %d, %d", q_dtype, cache_dtype);
+  if (cache_dtype == MLA_F32 && q_dtype != MLA_F32)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_decode_splitkv: an fp32 cache needs an fp32 query");
+  if (n_segs <= 0 || n_segs > 64 || batch < 0 || s_q <= 0 || n_heads <= 0 || n_part <= 0 || n_wg < 0)
+    return fail(MLA_ERR_SHAPE, "mla_decode_splitkv: n_segs=%d batch=%d s_q=%d n_heads=%d n_part=%d n_wg=%d",
+                n_segs, batch, s_q, n_heads, n_part, n_wg);
+  if (!std::isfinite(scale)) return fail(MLA_ERR_SHAPE, "mla_decode_splitkv: scale is not finite");
+  const bool bf = cache_dtype == MLA_BF16;
+  const bool q32 = q_dtype == MLA_F32;
+  if (bf) {
+    if (d_c != kBf16Dc || d_rope != kBf16Dr)
+      return fail(MLA_ERR_UNSUPPORTED, "mla_decode_splitkv: bf16 path needs d_c=512, d_rope=64 (got %d, %d)", d_c,
+                  d_rope);
+    if (!aligned16(q_lat) || !aligned16(o_part))
+      return fail(MLA_ERR_ALIGN, "mla_decode_splitkv: q_lat and o_part must be 16-byte aligned");
+  } else if (d_c <= 0 || d_c > 512 || d_rope <= 0 || d_rope > 128) {
+    return fail(MLA_ERR_SHAPE, "mla_decode_splitkv: fp32 path needs d_c<=512, d_rope<=128 (got %d, %d)", d_c,
+                d_rope);
+  }
+  // every head's slot ranges must tile [0, n_part) exactly
+  std::vector<int> cover((size_t)n_heads * n_part, 0);
+  for (int g = 0; g < n_segs; ++g) {
+    const mla_segment& s = segs[g];
+    if (!s.cache || !s.seq_lens || !s.q_rot) return fail(MLA_ERR_NULL, "segment %d: cache, seq_lens, q_rot required", g);
+    if (s.head_begin < 0 || s.head_count <= 0 || s.head_begin + s.head_count > n_heads)
+      return fail(MLA_ERR_SHAPE, "segment %d: heads [%d, %d) outside [0, %d)", g, s.head_begin,
+                  s.head_begin + s.head_count, n_heads);
+    if (s.n_split <= 0 || s.part_begin < 0 || s.part_begin + s.n_split > n_part)
+      return fail(MLA_ERR_SHAPE, "segment %d: slots [%d, %d) outside [0, %d)", g, s.part_begin,
+                  s.part_begin + s.n_split, n_part);
+    if (s.causal != 0 && s.causal != 1) return fail(MLA_ERR_SHAPE, "segment %d: causal must be 0 or 1", g);
+    if (s.block_table) {
+      if (s.page_size <= 0 || s.max_pages <= 0 || s.n_pages <= 0)
+        return fail(MLA_ERR_SHAPE, "segment %d: paged layout needs page_size, max_pages, n_pages > 0", g);
+      if (bf && s.page_size != kPage)
+        return fail(MLA_ERR_UNSUPPORTED, "segment %d: bf16 path needs page_size 64 (got %d)", g, s.page_size);
+    } else if (s.max_rows <= 0 && batch > 0) {
+      return fail(MLA_ERR_SHAPE, "segment %d: contiguous layout needs max_rows > 0", g);
+    }
+    if (bf) {
+      if (!aligned16(s.cache) || !aligned16(s.q_rot))
+        return fail(MLA_ERR_ALIGN, "segment %d: cache and q_rot must be 16-byte aligned", g);
+      if ((int64_t)s_q * s.head_count > 512)
+        return fail(MLA_ERR_UNSUPPORTED, "segment %d: s_q * head_count = %d > 512", g, s_q * s.head_count);
+    } else if ((int64_t)batch * s_q * s.head_count > 65535 || s.n_split > 65535) {
+      return fail(MLA_ERR_UNSUPPORTED, "segment %d: fp32 path grid too large", g);
+    }
+    for (int h = s.head_begin; h < s.head_begin + s.head_count; ++h)
+      for (int k = s.part_begin; k < s.part_begin + s.n_split; ++k) cover[(size_t)h * n_part + k]++;
+  }
+  for (int h = 0; h < n_heads; ++h)
+    for (int k = 0; k < n_part; ++k)
+      if (cover[(size_t)h * n_part + k] != 1)
+        return fail(MLA_ERR_SHAPE, "head %d slot %d is covered by %d segments (must be exactly 1)", h, k,
+                    cover[(size_t)h * n_part + k]);
+  if (batch == 0) return ok();
+  int wg = n_wg > 0 ? n_wg : cu_count();
+  if (wg <= 0) return fail(MLA_ERR_HIP, "mla_decode_splitkv: could not query the device");
+  for (int g = 0; g < n_segs; ++g) {
+    const mla_segment& s = segs[g];
+    mla::DecodeArgs a;
+    a.seg = mla::SegArgs{s.cache,     s.block_table, s.seq_lens,  s.q_rot,      s.max_rows,
+                         s.page_size, s.max_pages,   s.n_pages,   s.head_begin, s.head_count,
+                         s.causal,    s.part_begin,  s.n_split};
+    a.q_lat = q_lat;
+    a.o_part = o_part;
+    a.lse_part = lse_part;
+    a.batch = batch;
+    a.s_q = s_q;
+    a.n_heads = n_heads;
+    a.d_c = d_c;
+    a.d_rope = d_rope;
+    a.n_part = n_part;
+    a.scale = scale;
+    hipError_t e = bf ? mla::launch_decode_bf16(a, wg, q32, (hipStream_t)stream)
+                      : mla::launch_decode_f32(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "mla_decode_splitkv launch");
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+// Host-side launchers of the HIP kernels (internal; the public ABI is
+// include/mla_latent.h).  Arguments are validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// One KV segment as the decode kernels receive it.
+struct SegArgs {
+  const void* cache;
+  const int32_t* block_table;  // nullptr => contiguous
+  const int32_t* seq_lens;
+  const void* q_rot;
+  int64_t max_rows;            // contiguous: rows per request in storage
+  int page_size;
+  int max_pages;
+  int n_pages;
+  int head_begin;
+  int head_count;
+  int causal;
+  int part_begin;
+  int n_split;
+};
+
+struct DecodeArgs {
+  SegArgs seg;
+  const void* q_lat;
+  float* o_part;
+  float* lse_part;
+  int batch;
+  int s_q;
+  int n_heads;
+  int d_c;
+  int d_rope;
+  int n_part;
+  float scale;
+};
+
+// Dtype flags below: true = bf16 storage, false = fp32.
+hipError_t launch_rope(const void* q_pe, bool in_bf16, void* q_rot, bool out_bf16, const int64_t* pos,
+                       const int64_t* shift, int n_tok, int n_heads, int d_rope, double base,
+                       hipStream_t stream);
+hipError_t launch_absorb(const void* q_nope, const void* w_uk, bool in_bf16, void* q_lat, bool out_bf16,
+                         int n_tok, int n_heads, int d_nope, int d_c, hipStream_t stream);
+hipError_t launch_out_uv(const void* o_lat, bool o_bf16, const void* w_uv, bool w_bf16, void* out,
+                         bool out_bf16, int n_tok, int n_heads, int d_c, int d_v, hipStream_t stream);
+hipError_t launch_combine(const float* o_part, const float* lse_part, int n_rows, int n_part,
+                          int d_c, void* o_lat, bool out_bf16, float* lse, hipStream_t stream);
+// Generic fp32 decode (any d_c <= 512, d_rope <= 128): one wave per
+// (query row, split), equal-length splits per request.
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
+// bf16 MFMA decode (d_c = 512, d_rope = 64, page 64).  n_wg workgroups per
+// row group; balanced split of all rows of the segment over them.
+// q_f32: q_lat / q_rot are fp32 (split into bf16 hi + lo) instead of bf16.
+hipError_t launch_decode_bf16(const DecodeArgs& a, int n_wg, bool q_f32, hipStream_t stream);
+// Grid shape of the bf16 decode for one segment: row groups and shares.
+void decode_bf16_grid(int rows_total, int n_wg, int* n_share, int* n_rg);
+
+}  // namespace mla

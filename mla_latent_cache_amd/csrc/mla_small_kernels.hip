@@ -1,0 +1,345 @@
+// Per-query kernels of the MLA decode step: RoPE relocation of the query,
+// key-side absorption (U_K^T q), value-side expansion (U_V o_lat) and the
+// log-sum-exp merge of partial attention states.  Their cost is O(H * d)
+// per query token, independent of the context length.
+#include "mla_common.h"
+#include "mla_kernels.h"
+
+#include <math.h>
+
+namespace mla {
+
+// ---------------------------------------------------------------------------
+// RoPE relocation (MLA tutorial page, "Position Rotations Complicate the
+// Absorption"; RedKnot-MLA abstract: query-side relocation).  Adjacent pairs
+// (2i, 2i+1) rotate counter-clockwise by (pos - shift) * base^(-2i/d_rope).
+// The position difference is int64 and the angle fp64 (positions reach 2^18,
+// where an fp32 angle would be off by ~0.02 rad); the rotation itself is fp32.
+// ---------------------------------------------------------------------------
+template <typename TI, typename TO>
+__global__ __launch_bounds__(256) void rope_kernel(const TI* __restrict__ q_pe, TO* __restrict__ q_rot,
+                                                   const int64_t* __restrict__ pos,
+                                                   const int64_t* __restrict__ shift, int n_tok,
+                                                   int n_heads, int d_rope, double base) {
+  const int half = d_rope / 2;
+  const int64_t total = (int64_t)n_tok * n_heads * half;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int i = (int)(idx % half);
+    const int64_t th = idx / half;  // token * n_heads + head
+    const int t = (int)(th / n_heads);
+    const int64_t rel = pos[t] - (shift ? shift[t] : 0);
+    const double theta = pow(base, -2.0 * (double)i / (double)d_rope);
+    double s, c;
+    sincos((double)rel * theta, &s, &c);
+    const float cf = (float)c, sf = (float)s;
+    const TI* x = q_pe + th * d_rope + 2 * i;
+    const float x0 = load_f(x), x1 = load_f(x + 1);
+    TO* y = q_rot + th * d_rope + 2 * i;
+    store_f(y, x0 * cf - x1 * sf);
+    store_f(y + 1, x0 * sf + x1 * cf);
+  }
+}
+
+template <typename TI, typename TO>
+static void rope_launch(const void* q_pe, void* q_rot, const int64_t* pos, const int64_t* shift, int n_tok,
+                        int n_heads, int d_rope, double base, int blocks, hipStream_t stream) {
+  hipLaunchKernelGGL((rope_kernel<TI, TO>), dim3(blocks), dim3(256), 0, stream, (const TI*)q_pe, (TO*)q_rot,
+                     pos, shift, n_tok, n_heads, d_rope, base);
+}
+
+hipError_t launch_rope(const void* q_pe, bool in_bf, void* q_rot, bool out_bf, const int64_t* pos,
+                       const int64_t* shift, int n_tok, int n_heads, int d_rope, double base,
+                       hipStream_t stream) {
+  const int64_t total = (int64_t)n_tok * n_heads * (d_rope / 2);
+  int blocks = (int)((total + 255) / 256);
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  if (in_bf && out_bf) rope_launch<bf16, bf16>(q_pe, q_rot, pos, shift, n_tok, n_heads, d_rope, base, blocks, stream);
+  else if (in_bf) rope_launch<bf16, float>(q_pe, q_rot, pos, shift, n_tok, n_heads, d_rope, base, blocks, stream);
+  else if (out_bf) rope_launch<float, bf16>(q_pe, q_rot, pos, shift, n_tok, n_heads, d_rope, base, blocks, stream);
+  else rope_launch<float, float>(q_pe, q_rot, pos, shift, n_tok, n_heads, d_rope, base, blocks, stream);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Key absorption (MLA tutorial page, "Move the Key Projection Into the
+// Query"): q_lat[t][h][j] = sum_i w_uk[h][i][j] q_nope[t][h][i].
+// Grid (heads, column blocks of 256); each thread owns one output column j and
+// a chunk of TCH tokens; q_nope of the chunk is staged in LDS.  Reads each
+// weight column once per token chunk (coalesced along j).
+// ---------------------------------------------------------------------------
+constexpr int kAbsorbTch = 16;
+constexpr int kAbsorbMaxNope = 256;
+
+template <typename T, typename TO>
+__global__ __launch_bounds__(256) void absorb_kernel(const T* __restrict__ q_nope,
+                                                     const T* __restrict__ w_uk, TO* __restrict__ q_lat,
+                                                     int n_tok, int n_heads, int d_nope, int d_c) {
+  __shared__ float qs[kAbsorbTch][kAbsorbMaxNope];
+  const int h = blockIdx.x;
+  const int j = blockIdx.y * 256 + threadIdx.x;
+  const T* w = w_uk + (int64_t)h * d_nope * d_c;
+  for (int t0 = 0; t0 < n_tok; t0 += kAbsorbTch) {
+    const int nt = min(kAbsorbTch, n_tok - t0);
+    __syncthreads();
+    for (int e = threadIdx.x; e < nt * d_nope; e += 256) {
+      const int tt = e / d_nope, i = e % d_nope;
+      qs[tt][i] = load_f(q_nope + ((int64_t)(t0 + tt) * n_heads + h) * d_nope + i);
+    }
+    __syncthreads();
+    if (j < d_c) {
+      float acc[kAbsorbTch];
+#pragma unroll
+      for (int tt = 0; tt < kAbsorbTch; ++tt) acc[tt] = 0.f;
+      for (int i = 0; i < d_nope; ++i) {
+        const float wv = load_f(w + (int64_t)i * d_c + j);
+#pragma unroll
+        for (int tt = 0; tt < kAbsorbTch; ++tt) acc[tt] += wv * qs[tt][i];
+      }
+      for (int tt = 0; tt < nt; ++tt)
+        store_f(q_lat + ((int64_t)(t0 + tt) * n_heads + h) * d_c + j, acc[tt]);
+    }
+  }
+}
+
+hipError_t launch_absorb(const void* q_nope, const void* w_uk, bool in_bf, void* q_lat, bool out_bf, int n_tok,
+                         int n_heads, int d_nope, int d_c, hipStream_t stream) {
+  dim3 grid(n_heads, (d_c + 255) / 256);
+#define MLA_ABSORB(TI, TO)                                                                                \
+  hipLaunchKernelGGL((absorb_kernel<TI, TO>), grid, dim3(256), 0, stream, (const TI*)q_nope, (const TI*)w_uk, \
+                     (TO*)q_lat, n_tok, n_heads, d_nope, d_c)
+  if (in_bf && out_bf) MLA_ABSORB(bf16, bf16);
+  else if (in_bf) MLA_ABSORB(bf16, float);
+  else if (out_bf) MLA_ABSORB(float, bf16);
+  else MLA_ABSORB(float, float);
+#undef MLA_ABSORB
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Value expansion (MLA tutorial page, "Move the Value Expansion After the
+// Weighted Sum"): out[t][h][i] = sum_j w_uv[h][i][j] o_lat[t][h][j].
+// One wave per (head, output row i): the weight row stays in registers, the
+// wave loops over tokens with a shuffle reduction.
+// ---------------------------------------------------------------------------
+constexpr int kOutMaxK = 16;  // d_c <= 1024
+
+template <typename TL, typename TW, typename TO>
+__global__ __launch_bounds__(256) void out_uv_kernel(const TL* __restrict__ o_lat,
+                                                     const TW* __restrict__ w_uv, TO* __restrict__ out,
+                                                     int n_tok, int n_heads, int d_c, int d_v) {
+  const int h = blockIdx.x;
+  const int i = blockIdx.y * 4 + threadIdx.x / 64;
+  const int lane = threadIdx.x % 64;
+  if (i >= d_v) return;
+  const TW* w = w_uv + ((int64_t)h * d_v + i) * d_c;
+  float wr[kOutMaxK];
+#pragma unroll
+  for (int k = 0; k < kOutMaxK; ++k) {
+    const int j = lane + 64 * k;
+    wr[k] = j < d_c ? load_f(w + j) : 0.f;
+  }
+  for (int t = 0; t < n_tok; ++t) {
+    const TL* o = o_lat + ((int64_t)t * n_heads + h) * d_c;
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < kOutMaxK; ++k) {
+      const int j = lane + 64 * k;
+      if (j < d_c) acc += wr[k] * load_f(o + j);
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) store_f(out + ((int64_t)t * n_heads + h) * d_v + i, acc);
+  }
+}
+
+template <typename TL, typename TW>
+static void out_uv_launch(const void* o_lat, const void* w_uv, void* out, bool out_bf, int n_tok, int n_heads,
+                          int d_c, int d_v, hipStream_t stream) {
+  dim3 grid(n_heads, (d_v + 3) / 4);
+  if (out_bf)
+    hipLaunchKernelGGL((out_uv_kernel<TL, TW, bf16>), grid, dim3(256), 0, stream, (const TL*)o_lat,
+                       (const TW*)w_uv, (bf16*)out, n_tok, n_heads, d_c, d_v);
+  else
+    hipLaunchKernelGGL((out_uv_kernel<TL, TW, float>), grid, dim3(256), 0, stream, (const TL*)o_lat,
+                       (const TW*)w_uv, (float*)out, n_tok, n_heads, d_c, d_v);
+}
+
+hipError_t launch_out_uv(const void* o_lat, bool o_bf, const void* w_uv, bool w_bf, void* out, bool out_bf,
+                         int n_tok, int n_heads, int d_c, int d_v, hipStream_t stream) {
+  if (o_bf && w_bf) out_uv_launch<bf16, bf16>(o_lat, w_uv, out, out_bf, n_tok, n_heads, d_c, d_v, stream);
+  else if (o_bf) out_uv_launch<bf16, float>(o_lat, w_uv, out, out_bf, n_tok, n_heads, d_c, d_v, stream);
+  else if (w_bf) out_uv_launch<float, bf16>(o_lat, w_uv, out, out_bf, n_tok, n_heads, d_c, d_v, stream);
+  else out_uv_launch<float, float>(o_lat, w_uv, out, out_bf, n_tok, n_heads, d_c, d_v, stream);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Log-sum-exp merge of partial states (RedKnot-MLA abstract: the paths are
+// merged before one shared output projection).  One wave per row; slots whose
+// lse is -inf are skipped without reading their o_part row.
+// ---------------------------------------------------------------------------
+template <typename TO>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o_part,
+                                                      const float* __restrict__ lse_part, int n_rows,
+                                                      int n_part, int d_c, TO* __restrict__ o_lat,
+                                                      float* __restrict__ lse) {
+  const int row = blockIdx.x * 4 + threadIdx.x / 64;
+  const int lane = threadIdx.x % 64;
+  if (row >= n_rows) return;
+  const float* lp = lse_part + (int64_t)row * n_part;
+  const float* op = o_part + (int64_t)row * n_part * d_c;
+  float m = -INFINITY;
+  for (int j = lane; j < n_part; j += 64) m = fmaxf(m, lp[j]);
+  m = wave_max(m);
+  TO* orow = o_lat + (int64_t)row * d_c;
+  if (m == -INFINITY) {
+    for (int d = lane; d < d_c; d += 64) store_f(orow + d, 0.f);
+    if (lse && lane == 0) lse[row] = -INFINITY;
+    return;
+  }
+  float tot = 0.f;
+  for (int j = lane; j < n_part; j += 64) tot += expf(lp[j] - m);
+  tot = wave_sum(tot);
+  const float inv = 1.f / tot;
+  float acc[kOutMaxK];
+#pragma unroll
+  for (int k = 0; k < kOutMaxK; ++k) acc[k] = 0.f;
+  for (int j = 0; j < n_part; ++j) {
+    const float l = lp[j];
+    if (l == -INFINITY) continue;
+    const float wgt = expf(l - m) * inv;
+    const float* o = op + (int64_t)j * d_c;
+#pragma unroll
+    for (int k = 0; k < kOutMaxK; ++k) {
+      const int d = lane + 64 * k;
+      if (d < d_c) acc[k] += wgt * o[d];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kOutMaxK; ++k) {
+    const int d = lane + 64 * k;
+    if (d < d_c) store_f(orow + d, acc[k]);
+  }
+  if (lse && lane == 0) lse[row] = m + logf(tot);
+}
+
+hipError_t launch_combine(const float* o_part, const float* lse_part, int n_rows, int n_part,
+                          int d_c, void* o_lat, bool out_bf16, float* lse, hipStream_t stream) {
+  dim3 grid((n_rows + 3) / 4);
+  if (out_bf16)
+    hipLaunchKernelGGL(combine_kernel<bf16>, grid, dim3(256), 0, stream, o_part, lse_part, n_rows,
+                       n_part, d_c, (bf16*)o_lat, lse);
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, stream, o_part, lse_part, n_rows,
+                       n_part, d_c, (float*)o_lat, lse);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Generic fp32 decode: one wave per (query row, split); split j of request b
+// covers rows [j*L, min((j+1)*L, T_b)) with L = ceil(T_b / n_split).  Scores
+// in fp32 against the stored latent and rotary key (absorbed form), online
+// softmax, latent accumulation; writes the normalised partial and its lse.
+// ---------------------------------------------------------------------------
+constexpr int kF32MaxDc = 512;
+constexpr int kF32MaxDr = 128;
+
+__device__ __forceinline__ const float* f32_row(const SegArgs& s, int b, int t, int rw) {
+  if (!s.block_table) return (const float*)s.cache + ((int64_t)b * s.max_rows + t) * rw;
+  const int page = s.block_table[(int64_t)b * s.max_pages + t / s.page_size];
+  if (page < 0 || page >= s.n_pages) return nullptr;
+  return (const float*)s.cache + ((int64_t)page * s.page_size + t % s.page_size) * rw;
+}
+
+__global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
+  __shared__ float qs[kF32MaxDc + kF32MaxDr];
+  __shared__ float ps[64];
+  const SegArgs& sg = a.seg;
+  const int lane = threadIdx.x;
+  const int split = blockIdx.x;
+  const int row = blockIdx.y;  // over batch * s_q * head_count
+  const int hc = sg.head_count;
+  const int b = row / (a.s_q * hc);
+  const int rem = row % (a.s_q * hc);
+  const int s = rem / hc;
+  const int h = sg.head_begin + rem % hc;
+  const int tok = b * a.s_q + s;
+  const int d_c = a.d_c, d_r = a.d_rope, rw = d_c + d_r;
+  int64_t cap = sg.block_table ? (int64_t)sg.max_pages * sg.page_size : sg.max_rows;
+  int T = sg.seq_lens[b];
+  T = (int)max((int64_t)0, min((int64_t)T, cap));
+  int vis = sg.causal ? T - a.s_q + s + 1 : T;
+  vis = max(0, min(vis, T));
+  const int L = (T + sg.n_split - 1) / sg.n_split;
+  const int r0 = split * L;
+  const int r1 = min(r0 + L, T);
+  const int64_t out_row = ((int64_t)tok * a.n_heads + h) * a.n_part + sg.part_begin + split;
+
+  const float* ql = (const float*)a.q_lat + ((int64_t)tok * a.n_heads + h) * d_c;
+  const float* qr = (const float*)sg.q_rot + ((int64_t)tok * a.n_heads + h) * d_r;
+  for (int d = lane; d < d_c; d += 64) qs[d] = ql[d];
+  for (int d = lane; d < d_r; d += 64) qs[d_c + d] = qr[d];
+  __syncthreads();
+
+  float m = -INFINITY, l = 0.f;
+  float acc[kF32MaxDc / 64];
+#pragma unroll
+  for (int k = 0; k < kF32MaxDc / 64; ++k) acc[k] = 0.f;
+  const int rend = min(r1, vis);
+  for (int t0 = r0; t0 < rend; t0 += 64) {
+    const int t = t0 + lane;
+    float sc = -INFINITY;
+    if (t < rend) {
+      const float* rp = f32_row(sg, b, t, rw);
+      if (rp) {
+        float dot = 0.f;
+        for (int d = 0; d < rw; ++d) dot += qs[d] * rp[d];
+        sc = dot * a.scale;
+      }
+    }
+    const float mt = wave_max(sc);
+    if (mt == -INFINITY) continue;  // nothing visible in this tile
+    const float mn = fmaxf(m, mt);
+    const float alpha = (m == -INFINITY) ? 0.f : expf(m - mn);
+    const float p = (sc == -INFINITY) ? 0.f : expf(sc - mn);
+    l = l * alpha + wave_sum(p);
+#pragma unroll
+    for (int k = 0; k < kF32MaxDc / 64; ++k) acc[k] *= alpha;
+    ps[lane] = p;
+    __syncthreads();
+    const int nt = min(64, rend - t0);
+    for (int jj = 0; jj < nt; ++jj) {
+      const float pj = ps[jj];
+      if (pj == 0.f) continue;
+      const float* rp = f32_row(sg, b, t0 + jj, rw);
+#pragma unroll
+      for (int k = 0; k < kF32MaxDc / 64; ++k) {
+        const int d = lane + 64 * k;
+        if (d < d_c) acc[k] += pj * rp[d];
+      }
+    }
+    __syncthreads();
+    m = mn;
+  }
+  if (l > 0.f) {
+    const float inv = 1.f / l;
+    float* o = a.o_part + out_row * d_c;
+#pragma unroll
+    for (int k = 0; k < kF32MaxDc / 64; ++k) {
+      const int d = lane + 64 * k;
+      if (d < d_c) o[d] = acc[k] * inv;
+    }
+    if (lane == 0) a.lse_part[out_row] = m + logf(l);
+  } else if (lane == 0) {
+    a.lse_part[out_row] = -INFINITY;
+  }
+}
+
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream) {
+  dim3 grid(a.seg.n_split, a.batch * a.s_q * a.seg.head_count);
+  hipLaunchKernelGGL(decode_f32_kernel, grid, dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,148 @@
+"""Torch-tensor wrappers of the five decode calls (argument marshalling only).
+
+Tensors must be contiguous and on the current HIP device; work is enqueued on
+torch's current stream.  Shapes and meaning: ``include/mla_latent.h``.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import torch
+
+from . import _lib
+from ._lib import MLA_BF16, MLA_F32, MlaSegment
+
+_DT = {torch.float32: MLA_F32, torch.bfloat16: MLA_BF16}
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def rope_relocate_q(q_pe: torch.Tensor, pos: torch.Tensor, shift: Optional[torch.Tensor] = None,
+                    base: float = 10000.0, out: Optional[torch.Tensor] = None,
+                    out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    n_tok, n_heads, d_rope = q_pe.shape
+    if out is None:
+        out = torch.empty_like(q_pe, dtype=out_dtype or q_pe.dtype)
+    _lib.call("rope_relocate_q", _ptr(q_pe), _dt(q_pe), _ptr(out), _dt(out), _ptr(pos), _ptr(shift), n_tok,
+              n_heads, d_rope, float(base), _stream())
+    return out
+
+
+def absorb_q(q_nope: torch.Tensor, w_uk: torch.Tensor, out: Optional[torch.Tensor] = None,
+             out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    n_tok, n_heads, d_nope = q_nope.shape
+    d_c = w_uk.shape[2]
+    if w_uk.shape != (n_heads, d_nope, d_c) or w_uk.dtype != q_nope.dtype:
+        raise ValueError("w_uk must be [n_heads, d_nope, d_c] of q_nope's dtype")
+    if out is None:
+        out = torch.empty((n_tok, n_heads, d_c), dtype=out_dtype or q_nope.dtype, device=q_nope.device)
+    _lib.call("mla_absorb_q", _ptr(q_nope), _ptr(w_uk), _dt(q_nope), _ptr(out), _dt(out), n_tok, n_heads,
+              d_nope, d_c, _stream())
+    return out
+
+
+def out_uv(o_lat: torch.Tensor, w_uv: torch.Tensor, out: Optional[torch.Tensor] = None,
+           out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    n_tok, n_heads, d_c = o_lat.shape
+    d_v = w_uv.shape[1]
+    if w_uv.shape != (n_heads, d_v, d_c):
+        raise ValueError("w_uv must be [n_heads, d_v, d_c]")
+    if out is None:
+        out = torch.empty((n_tok, n_heads, d_v), dtype=out_dtype or w_uv.dtype, device=o_lat.device)
+    _lib.call("mla_out_uv", _ptr(o_lat), _dt(o_lat), _ptr(w_uv), _dt(w_uv), _ptr(out), _dt(out), n_tok,
+              n_heads, d_c, d_v, _stream())
+    return out
+
+
+def combine_lse(o_part: torch.Tensor, lse_part: torch.Tensor, out_dtype: torch.dtype,
+                o_lat: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """o_part [..., n_part, d_c] fp32, lse_part [..., n_part] -> (o_lat [..., d_c], lse [...])."""
+    lead = o_part.shape[:-2]
+    n_part, d_c = o_part.shape[-2:]
+    n_rows = 1
+    for x in lead:
+        n_rows *= x
+    if o_lat is None:
+        o_lat = torch.empty(tuple(lead) + (d_c,), dtype=out_dtype, device=o_part.device)
+    if lse is None:
+        lse = torch.empty(tuple(lead), dtype=torch.float32, device=o_part.device)
+    _lib.call("mla_combine_lse", _ptr(o_part), _ptr(lse_part), n_rows, n_part, d_c, _ptr(o_lat),
+              _DT[out_dtype], _ptr(lse), _stream())
+    return o_lat, lse
+
+
+@dataclass
+class Segment:
+    """Device tensors of one KV segment (see ``mla_segment``)."""
+    cache: torch.Tensor                   # [B, max_rows, R] or pool [P, page, R]
+    seq_lens: torch.Tensor                # int32 [B]
+    q_rot: torch.Tensor                   # [n_tok, H, d_rope]
+    block_table: Optional[torch.Tensor] = None   # int32 [B, max_pages]
+    head_begin: int = 0
+    head_count: int = 0
+    causal: bool = False
+    part_begin: int = 0
+    n_split: int = 1
+
+    def to_c(self) -> MlaSegment:
+        s = MlaSegment()
+        s.cache = _ptr(self.cache)
+        s.block_table = _ptr(self.block_table)
+        s.seq_lens = _ptr(self.seq_lens)
+        s.q_rot = _ptr(self.q_rot)
+        if self.block_table is None:
+            s.max_rows = self.cache.shape[1]
+            s.page_size = s.max_pages = s.n_pages = 0
+        else:
+            s.max_rows = 0
+            s.page_size = self.cache.shape[1]
+            s.max_pages = self.block_table.shape[1]
+            s.n_pages = self.cache.shape[0]
+        s.head_begin = self.head_begin
+        s.head_count = self.head_count
+        s.causal = int(self.causal)
+        s.part_begin = self.part_begin
+        s.n_split = self.n_split
+        return s
+
+
+def decode_splitkv(segments: Sequence[Segment], q_lat: torch.Tensor, batch: int, s_q: int, scale: float,
+                   o_part: torch.Tensor, lse_part: torch.Tensor, n_wg: int = 0) -> None:
+    """o_part [n_tok, H, n_part, d_c] fp32 and lse_part [n_tok, H, n_part] are written."""
+    n_tok, n_heads, d_c = q_lat.shape
+    d_rope = segments[0].q_rot.shape[2]
+    n_part = o_part.shape[2]
+    cache_dt = _dt(segments[0].cache)
+    for s in segments:
+        if _dt(s.cache) != cache_dt or s.q_rot.dtype != q_lat.dtype:
+            raise ValueError("segments must share the cache dtype; q_rot must have q_lat's dtype")
+    arr = (MlaSegment * len(segments))(*[s.to_c() for s in segments])
+    _lib.call("mla_decode_splitkv", arr, len(segments), _ptr(q_lat), _dt(q_lat), cache_dt, batch, s_q, n_heads,
+              d_c, d_rope, float(scale), _ptr(o_part), _ptr(lse_part), n_part, n_wg, _stream())
+
+
+def cu_count() -> int:
+    return _lib.load().mla_device_cu_count()
+
+
+def decode_shares(s_q: int, head_count: int, n_wg: int = 0) -> int:
+    return _lib.load().mla_decode_shares(s_q, head_count, n_wg)

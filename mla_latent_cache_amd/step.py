@@ -1,0 +1,193 @@
+"""One decode step of one attention layer: the five calls, with buffers.
+
+``DecodeStep`` owns the device buffers of the chain
+
+    rope_relocate_q (once per distinct segment shift) -> mla_absorb_q
+    -> mla_decode_splitkv (all segments) -> mla_combine_lse -> mla_out_uv
+
+and lays out the partial-state slots: segments with disjoint head ranges that
+follow each other share a slot range (e.g. a document read by the Local heads
+at a relocated position and its recomputed copy read by the Global heads),
+later ranges stack after it, so each head's slots tile [0, n_part).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import torch
+
+from . import ops
+
+
+@dataclass
+class StepSegment:
+    cache: torch.Tensor                 # device
+    seq_lens: torch.Tensor              # device int32 [B]
+    seq_lens_host: Sequence[int]
+    shift: torch.Tensor                 # device int64 [n_tok]
+    shift_host: Sequence[int]
+    block_table: Optional[torch.Tensor] = None
+    head_begin: int = 0
+    head_count: int = 0
+    causal: bool = False
+
+
+def _ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+class DecodeStep:
+    def __init__(self, q_nope, q_pe, q_pos, w_uk, w_uv, segments: List[StepSegment], batch: int, s_q: int,
+                 scale: float, rope_base: float = 10000.0, n_wg: int = 0,
+                 n_split: Optional[Sequence[int]] = None):
+        self.q_nope, self.q_pe, self.q_pos = q_nope, q_pe, q_pos
+        self.w_uk, self.w_uv = w_uk, w_uv
+        self.batch, self.s_q, self.scale, self.rope_base, self.n_wg = batch, s_q, scale, rope_base, n_wg
+        dev, dt = q_nope.device, q_nope.dtype
+        n_tok, H, _ = q_nope.shape
+        d_c = w_uk.shape[2]
+        d_v = w_uv.shape[1]
+        self.bf16 = dt == torch.bfloat16
+
+        # The query enters the decode in fp32 (q_lat and the rotated q_rot):
+        # the kernel splits it into bf16 hi + lo parts, so the scores are not
+        # limited by a bf16-rounded query.
+        q_dt = torch.float32
+        # one rotated query per distinct shift
+        self.q_rots = []
+        keys = {}
+        self.seg_rot = []
+        for s in segments:
+            key = tuple(int(v) for v in s.shift_host)
+            if key not in keys:
+                keys[key] = len(self.q_rots)
+                self.q_rots.append((s.shift, torch.empty_like(q_pe, dtype=q_dt)))
+            self.seg_rot.append(keys[key])
+
+        # split counts
+        if n_split is None:
+            n_split = [self._auto_split(s) for s in segments]
+        # slot layout: runs of head-disjoint segments share one slot range
+        layers, cur, used = [], [], set()
+        for i, s in enumerate(segments):
+            hs = set(range(s.head_begin, s.head_begin + s.head_count))
+            if cur and (hs & used):
+                layers.append(cur)
+                cur, used = [], set()
+            cur.append(i)
+            used |= hs
+        layers.append(cur)
+        self.n_split = list(n_split)
+        part_begin = [0] * len(segments)
+        pb = 0
+        for layer in layers:
+            m = max(self.n_split[i] for i in layer)
+            for i in layer:
+                self.n_split[i] = m
+                part_begin[i] = pb
+            pb += m
+        self.n_part = pb
+        self.segments = [
+            ops.Segment(cache=s.cache, seq_lens=s.seq_lens, q_rot=self.q_rots[self.seg_rot[i]][1],
+                        block_table=s.block_table, head_begin=s.head_begin, head_count=s.head_count,
+                        causal=s.causal, part_begin=part_begin[i], n_split=self.n_split[i])
+            for i, s in enumerate(segments)
+        ]
+        self.q_lat = torch.empty((n_tok, H, d_c), dtype=q_dt, device=dev)
+        self.o_part = torch.empty((n_tok, H, self.n_part, d_c), dtype=torch.float32, device=dev)
+        self.lse_part = torch.empty((n_tok, H, self.n_part), dtype=torch.float32, device=dev)
+        self.o_lat = torch.empty((n_tok, H, d_c), dtype=dt, device=dev)
+        self.lse = torch.empty((n_tok, H), dtype=torch.float32, device=dev)
+        self.out = torch.empty((n_tok, H, d_v), dtype=dt, device=dev)
+
+    def _auto_split(self, s: StepSegment) -> int:
+        lens = [int(x) for x in s.seq_lens_host]
+        tmax = max(lens) if lens else 0
+        tsum = sum(lens)
+        if not self.bf16:
+            return 2 if tmax >= 2 else 1
+        if tsum == 0:
+            return 1
+        shares = ops.decode_shares(self.s_q, s.head_count, self.n_wg)
+        share = 32 * _ceil_div(_ceil_div(tsum, shares), 32)
+        return _ceil_div(tmax, share) + 1
+
+    def rope(self):
+        for shift, q_rot in self.q_rots:
+            ops.rope_relocate_q(self.q_pe, self.q_pos, shift, self.rope_base, out=q_rot)
+
+    def absorb(self):
+        ops.absorb_q(self.q_nope, self.w_uk, out=self.q_lat)
+
+    def decode(self):
+        ops.decode_splitkv(self.segments, self.q_lat, self.batch, self.s_q, self.scale, self.o_part,
+                           self.lse_part, self.n_wg)
+
+    def combine(self):
+        ops.combine_lse(self.o_part, self.lse_part, self.o_lat.dtype, o_lat=self.o_lat, lse=self.lse)
+
+    def expand(self):
+        ops.out_uv(self.o_lat, self.w_uv, out=self.out)
+
+    def run(self):
+        self.rope()
+        self.absorb()
+        self.decode()
+        self.combine()
+        self.expand()
+        return self.out, self.o_lat, self.lse
+
+    # -- low-overhead replay: ctypes arguments built once for a fixed stream --
+    def bind(self, stream: Optional[torch.cuda.Stream] = None):
+        """Precompute the C calls of one step on ``stream`` (default: current).
+        Returns (pre, decode, post): lists of (function, args) to run in order."""
+        from . import _lib
+        lib = _lib.load()
+        st = (stream or torch.cuda.current_stream()).cuda_stream
+        dt = ops._dt
+        pre = []
+        for shift, q_rot in self.q_rots:
+            n_tok, H, d_r = self.q_pe.shape
+            pre.append((lib.rope_relocate_q, (self.q_pe.data_ptr(), dt(self.q_pe), q_rot.data_ptr(), dt(q_rot),
+                                              self.q_pos.data_ptr(), shift.data_ptr(), n_tok, H, d_r,
+                                              float(self.rope_base), st)))
+        n_tok, H, d_nope = self.q_nope.shape
+        d_c = self.w_uk.shape[2]
+        pre.append((lib.mla_absorb_q, (self.q_nope.data_ptr(), self.w_uk.data_ptr(), dt(self.q_nope),
+                                       self.q_lat.data_ptr(), dt(self.q_lat), n_tok, H, d_nope, d_c, st)))
+        self._seg_arr = (_lib.MlaSegment * len(self.segments))(*[sg.to_c() for sg in self.segments])
+        d_r = self.segments[0].q_rot.shape[2]
+        dec = [(lib.mla_decode_splitkv, (self._seg_arr, len(self.segments), self.q_lat.data_ptr(), dt(self.q_lat),
+                                         dt(self.segments[0].cache), self.batch, self.s_q, H, d_c, d_r,
+                                         float(self.scale), self.o_part.data_ptr(), self.lse_part.data_ptr(),
+                                         self.n_part, self.n_wg, st))]
+        post = [(lib.mla_combine_lse, (self.o_part.data_ptr(), self.lse_part.data_ptr(), n_tok * H, self.n_part,
+                                       d_c, self.o_lat.data_ptr(), dt(self.o_lat), self.lse.data_ptr(), st)),
+                (lib.mla_out_uv, (self.o_lat.data_ptr(), dt(self.o_lat), self.w_uv.data_ptr(), dt(self.w_uv),
+                                  self.out.data_ptr(), dt(self.out), n_tok, H, d_c, self.w_uv.shape[1], st))]
+        return pre, dec, post
+
+
+def run_calls(calls) -> None:
+    """Run bound calls; raise on the first failing status."""
+    from . import _lib
+    for fn, args in calls:
+        st = fn(*args)
+        if st != 0:
+            raise _lib.MlaError(fn.__name__, st, _lib.load().mla_last_error().decode())
+
+
+def step_from_inputs(x, device="cuda", n_wg: int = 0, n_split=None) -> DecodeStep:
+    """Upload a seeded input set (``mla_inputs.MlaInputs``) and build its step."""
+    d = torch.device(device)
+    segs = []
+    for s in x.segments:
+        shift_tok = x.token_shift(s)
+        segs.append(StepSegment(
+            cache=s.cache.to(d), seq_lens=s.seq_lens.to(d), seq_lens_host=s.seq_lens.tolist(),
+            shift=shift_tok.to(d), shift_host=shift_tok.tolist(),
+            block_table=None if s.block_table is None else s.block_table.to(d),
+            head_begin=s.head_begin, head_count=s.head_count, causal=s.causal))
+    return DecodeStep(x.q_nope.to(d), x.q_pe.to(d), x.q_pos.to(d), x.w_uk.to(d), x.w_uv.to(d), segs,
+                      x.spec.batch, x.spec.s_q, x.scale, x.rope_base, n_wg=n_wg, n_split=n_split)

@@ -1,0 +1,117 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares with the argument count the binding uses, and rejects bad arguments
+before touching the GPU."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_latent.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    decls = {}
+    for m in re.finditer(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(([^)]*)\)\s*;", src, flags=re.M):
+        name, args = m.group(1), m.group(2).strip()
+        n = 0 if args in ("", "void") else args.count(",") + 1
+        decls[name] = n
+    return decls
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from mla_latent_cache_amd import _lib
+    return _lib.load()
+
+
+def test_header_declares_the_five_calls():
+    d = _declared()
+    for name in ("rope_relocate_q", "mla_absorb_q", "mla_decode_splitkv", "mla_combine_lse", "mla_out_uv"):
+        assert name in d
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    from mla_latent_cache_amd._lib import SIGNATURES
+    decls = _declared()
+    assert set(decls) == set(SIGNATURES), (set(decls) ^ set(SIGNATURES))
+    for name, nargs in decls.items():
+        assert hasattr(lib, name), name
+        assert len(SIGNATURES[name][1]) == nargs, (name, nargs)
+
+
+def test_segment_struct_layout(tmp_path):
+    """ctypes' mirror of mla_segment has the C compiler's size and offsets."""
+    import subprocess
+    from mla_latent_cache_amd._lib import MlaSegment
+    fields = [f for f, _ in MlaSegment._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "mla_latent.h"\nint main(void){\n'
+                   'printf("%zu\\n", sizeof(mla_segment));\n'
+                   + "".join(f'printf("%zu\\n", offsetof(mla_segment, {f}));\n' for f in fields)
+                   + "return 0;}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    vals = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(MlaSegment)
+    assert vals[1:] == [getattr(MlaSegment, f).offset for f in fields]
+
+
+def test_status_strings(lib):
+    assert lib.mla_status_string(0) == b"ok"
+    assert lib.mla_status_string(7) == b"HIP runtime error"
+    assert lib.mla_version() == 100
+
+
+def _st(lib, name, *args):
+    return getattr(lib, name)(*args)
+
+
+def test_null_and_shape_errors_before_any_gpu_call(lib):
+    from mla_latent_cache_amd._lib import MlaSegment
+    P = 16  # fake, aligned, non-null address: validation fails before it is used
+    assert _st(lib, "rope_relocate_q", None, 1, P, 0, P, None, 1, 1, 64, 1e4, None) == 1
+    assert _st(lib, "rope_relocate_q", P, 1, P, 0, P, None, 1, 1, 63, 1e4, None) == 2
+    assert _st(lib, "rope_relocate_q", P, 5, P, 0, P, None, 1, 1, 64, 1e4, None) == 3
+    assert _st(lib, "rope_relocate_q", P, 1, P, 0, P, None, 1, 1, 64, 0.5, None) == 2
+    assert b"base" in lib.mla_last_error()
+    assert _st(lib, "mla_absorb_q", P, None, 1, P, 0, 1, 1, 128, 512, None) == 1
+    assert _st(lib, "mla_absorb_q", P, P, 1, P, 9, 1, 1, 128, 512, None) == 3
+    assert _st(lib, "mla_absorb_q", P, P, 1, P, 0, 1, 0, 128, 512, None) == 2
+    assert _st(lib, "mla_out_uv", P, 1, P, 1, P, 1, -1, 1, 512, 128, None) == 2
+    assert _st(lib, "mla_combine_lse", P, P, 1, 0, 512, P, 1, None, None) == 2
+    assert _st(lib, "mla_combine_lse", P, None, 1, 1, 512, P, 1, None, None) == 1
+    # zero-size calls succeed without launching anything
+    assert _st(lib, "mla_absorb_q", P, P, 1, P, 0, 0, 1, 128, 512, None) == 0
+
+    def seg(**kw):
+        s = MlaSegment()
+        s.cache, s.seq_lens, s.q_rot = P, P, P
+        s.max_rows, s.head_begin, s.head_count, s.part_begin, s.n_split = 64, 0, 4, 0, 2
+        for k, v in kw.items():
+            setattr(s, k, v)
+        return s
+
+    def dec(segs, n_heads=4, n_part=2, dtype=1, d_c=512, d_r=64, q=P, o=P, q_dtype=0):
+        arr = (MlaSegment * len(segs))(*segs)
+        return _st(lib, "mla_decode_splitkv", arr, len(segs), q, q_dtype, dtype, 2, 1, n_heads, d_c, d_r, 0.1,
+                   o, P, n_part, 0, None)
+
+    assert dec([seg()], q=None) == 1
+    assert dec([seg(cache=None)]) == 1
+    assert dec([seg()], d_c=256) == 5                     # bf16 needs d_c 512
+    assert dec([seg()], q=P + 8) == 4                     # misaligned q_lat
+    assert dec([seg(head_count=5)]) == 2                  # heads out of range
+    assert dec([seg(n_split=3)]) == 2                     # slots past n_part
+    assert dec([seg(n_split=1)]) == 2                     # slot 1 uncovered
+    assert b"covered" in lib.mla_last_error()
+    assert dec([seg(), seg()]) == 2                       # slots covered twice
+    assert dec([seg(block_table=P, page_size=32, max_pages=4, n_pages=8)]) == 5  # bf16 page 64 only
+    assert dec([seg(causal=2)]) == 2
+    assert dec([seg(head_count=4)], n_heads=4, dtype=7) == 3
+    assert dec([seg()], dtype=0, q_dtype=1) == 5          # fp32 cache needs an fp32 query

@@ -1,0 +1,211 @@
+"""GPU parity: the HIP library against the fp64 oracle, through the C ABI.
+
+Every test here needs an MI355X and the built ``libmla_latent.so``.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import mla_inputs as M
+import oracle.mla_direct as O
+from mla_inputs.configs import SegSpec, Spec, WORKLOADS, WORKLOAD_ORDER
+from parity_util import check_step, f64, sample_pairs, tol_check
+
+pytestmark = pytest.mark.gpu
+
+SEEDS = {name: i for i, name in enumerate(WORKLOAD_ORDER)}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    from mla_latent_cache_amd import load
+    load()  # loud failure if the library is not built
+    yield
+
+
+def _run(x, **kw):
+    from mla_latent_cache_amd.step import step_from_inputs
+    st = step_from_inputs(x, **kw)
+    out, o_lat, lse = st.run()
+    torch.cuda.synchronize()
+    return st, out, o_lat, lse
+
+
+# ------------------------------------------------------------ whole chain, small
+@pytest.mark.parametrize("name", WORKLOAD_ORDER)
+def test_chain_mini(name):
+    x = M.make(name, SEEDS[name], mini=True, poison=True)
+    print(f"[parity] mini {name} seed {SEEDS[name]}", flush=True)
+    _, out, o_lat, lse = _run(x)
+    errs = check_step(x, out, o_lat, lse, label=name)
+    print(f"[parity] {name}: {errs}", flush=True)
+
+
+@pytest.mark.parametrize("n_wg", [1, 3, 8, 64, 256])
+def test_split_invariance_dsv3_mini(n_wg):
+    x = M.make("dsv3", 7, mini=True, poison=True)
+    _, out, o_lat, lse = _run(x, n_wg=n_wg)
+    check_step(x, out, o_lat, lse, label=f"dsv3-mini n_wg={n_wg}")
+
+
+@pytest.mark.parametrize("n_split", [1, 2, 3, 9])
+def test_forced_n_split(n_split):
+    x = M.make("long", 8, mini=True, poison=True)
+    _, out, o_lat, lse = _run(x, n_wg=64, n_split=[n_split])
+    check_step(x, out, o_lat, lse, label=f"long-mini n_split={n_split}")
+
+
+def test_repeatable_bitwise():
+    x = M.make("merge", 9, mini=True)
+    st, out, o_lat, lse = _run(x)
+    a = (out.clone(), o_lat.clone(), lse.clone())
+    st.run()
+    torch.cuda.synchronize()
+    for u, v in zip(a, (st.out, st.o_lat, st.lse)):
+        assert torch.equal(u.view(torch.uint8) if u.dtype != torch.float32 else u.view(torch.int32),
+                           v.view(torch.uint8) if v.dtype != torch.float32 else v.view(torch.int32))
+
+
+def test_outputs_fully_overwritten():
+    x = M.make("dsv3", 10, mini=True, poison=True)
+    from mla_latent_cache_amd.step import step_from_inputs
+    st = step_from_inputs(x)
+    for t in (st.o_lat, st.lse, st.out, st.q_lat):
+        t.fill_(float("nan"))
+    st.run()
+    torch.cuda.synchronize()
+    for t in (st.o_lat, st.lse, st.out, st.q_lat):
+        assert torch.isfinite(t.float()).all()
+    check_step(x, st.out, st.o_lat, st.lse, label="sentinel")
+
+
+# ------------------------------------------------------------ edge cases
+def _custom(name, dtype="bf16", heads=16, s_q=1, batch=None, segs=None, **kw):
+    dims = dict(d_c=512, d_nope=128, d_rope=64, d_v=128) if dtype == "bf16" else \
+        dict(d_c=4, d_nope=4, d_rope=2, d_v=4)
+    return Spec(name=name, batch=batch, heads=heads, s_q=s_q, dtype=dtype, segments=segs, **dims, **kw)
+
+
+EDGE = {
+    "empty_and_one_row": _custom("edge-empty", batch=5, segs=(
+        SegSpec("kv", lengths=(0, 1, 0, 65, 33), online=True),)),
+    "all_empty": _custom("edge-all-empty", batch=2, segs=(SegSpec("kv", lengths=(0, 0), online=True),)),
+    "many_requests": _custom("edge-many", batch=150, heads=8, segs=(
+        SegSpec("kv", length_range=(0, 40), layout="paged", page_size=64, online=True),)),
+    "rows_17": _custom("edge-rows17", batch=3, heads=17, segs=(
+        SegSpec("kv", lengths=(100, 31, 257), online=True),)),
+    "rows_48_sq3": _custom("edge-rows48", batch=2, heads=16, s_q=3, segs=(
+        SegSpec("kv", lengths=(90, 3), causal=True, online=True),)),
+    "rows_100": _custom("edge-rows100", batch=2, heads=100, segs=(
+        SegSpec("kv", lengths=(300, 64), layout="paged", page_size=64, spare_pages=2, online=True),)),
+    "causal_short_online": _custom("edge-causal", batch=2, heads=64, s_q=4, offset_range=(0, 200000), segs=(
+        SegSpec("doc_off", lengths=(40, 0), head_begin=0, head_count=56, shift_offset=True),
+        SegSpec("doc_on", lengths=(40, 0), head_begin=56, head_count=8, base_offset=True),
+        SegSpec("online", lengths=(2, 5), causal=True, base_offset=True, base_after="doc_on", online=True),
+    )),
+    "toy_f32_ragged": _custom("edge-f32", dtype="f32", batch=3, heads=2, scale=1 / math.sqrt(6), segs=(
+        SegSpec("kv", lengths=(16, 0, 130), layout="paged", page_size=8, spare_pages=1, online=True),)),
+}
+
+
+@pytest.mark.parametrize("case", sorted(EDGE))
+def test_edge_case(case):
+    x = M.make_inputs(EDGE[case], seed=11, poison=True)
+    print(f"[parity] edge {case}", flush=True)
+    _, out, o_lat, lse = _run(x)
+    check_step(x, out, o_lat, lse, label=case)
+
+
+# ------------------------------------------------------------ single calls
+def _rand(shape, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(shape, generator=g).to(dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_rope_relocate_call(dtype):
+    from mla_latent_cache_amd import ops
+    n_tok, H, d_r = 9, 5, (64 if dtype == torch.bfloat16 else 2)
+    q_pe = _rand((n_tok, H, d_r), dtype, 1)
+    g = torch.Generator().manual_seed(2)
+    pos = torch.randint(0, 262144, (n_tok,), generator=g, dtype=torch.int64)
+    shift = torch.randint(0, 200001, (n_tok,), generator=g, dtype=torch.int64)
+    for sh, odt in ((None, dtype), (shift, dtype), (shift, torch.float32)):
+        got = ops.rope_relocate_q(q_pe.cuda(), pos.cuda(), None if sh is None else sh.cuda(), 10000.0,
+                                  out_dtype=odt)
+        ref = O.rope_relocate(f64(q_pe), pos.numpy(), np.zeros(n_tok, np.int64) if sh is None else sh.numpy(),
+                              10000.0)
+        err = np.abs(f64(got) - ref)
+        if odt == torch.float32:
+            assert err.max() <= 1e-5, err.max()
+        else:
+            assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-5), err.max()
+
+
+@pytest.mark.parametrize("dtype,dims", [(torch.float32, (4, 4, 7)), (torch.bfloat16, (128, 512, 33))])
+def test_absorb_and_out_uv_calls(dtype, dims):
+    from mla_latent_cache_amd import ops
+    d_nope, d_c, n_tok = dims
+    H = 6
+    q = _rand((n_tok, H, d_nope), dtype, 3)
+    w = (_rand((H, d_nope, d_c), torch.float32, 4) / math.sqrt(d_c)).to(dtype)
+    ref = O.absorb_query(f64(w), f64(q))
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    for odt in {dtype, torch.float32}:
+        got = ops.absorb_q(q.cuda(), w.cuda(), out_dtype=odt)
+        rel = 1e-6 if odt == torch.float32 else 2.0 ** -8
+        assert np.all(np.abs(f64(got) - ref) <= rel * np.abs(ref) + 1e-5 * rms), odt
+    o = _rand((n_tok, H, d_c), dtype, 5)
+    wv = (_rand((H, d_nope, d_c), torch.float32, 6) / math.sqrt(d_c)).to(dtype)
+    ref = O.output_expand(f64(wv), f64(o))
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    for odt in {dtype, torch.float32}:
+        got = ops.out_uv(o.cuda(), wv.cuda(), out_dtype=odt)
+        rel = 1e-6 if odt == torch.float32 else 2.0 ** -8
+        assert np.all(np.abs(f64(got) - ref) <= rel * np.abs(ref) + 1e-5 * rms), odt
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_combine_call(out_dtype):
+    from mla_latent_cache_amd import ops
+    n_rows, n_part, d_c = 37, 5, 512
+    g = torch.Generator().manual_seed(12)
+    o_part = torch.randn((n_rows, n_part, d_c), generator=g)
+    lse_part = torch.randn((n_rows, n_part), generator=g) * 4
+    lse_part[3, :] = -math.inf                # empty row
+    lse_part[4, 1:] = -math.inf               # one live slot
+    lse_part[5, ::2] = -math.inf
+    o_part[lse_part == -math.inf] = float("nan")  # never read
+    o_lat, lse = ops.combine_lse(o_part.cuda(), lse_part.cuda(), out_dtype)
+    torch.cuda.synchronize()
+    for r in range(n_rows):
+        o_ref, l_ref = O.merge_lse(f64(o_part[r]), f64(lse_part[r]))
+        got = f64(o_lat[r])
+        if math.isinf(l_ref):
+            assert float(lse[r]) == -math.inf and not np.any(got)
+            continue
+        assert abs(float(lse[r]) - l_ref) <= 1e-5 * max(1.0, abs(l_ref))
+        rel = 1e-5 if out_dtype == torch.float32 else 2.0 ** -8
+        assert np.all(np.abs(got - o_ref) <= rel * np.abs(o_ref) + 1e-6), r
+
+
+# ------------------------------------------------------------ full sizes, sampled
+@pytest.mark.parametrize("name", ["small", "dsv3", "long", "merge"])
+def test_full_size_sampled(name):
+    """The bench's launch configuration (default grid) at full size; the
+    oracle checks sampled (request, head) pairs."""
+    x = M.make(name, SEEDS[name])
+    print(f"[parity] full {name} seed {SEEDS[name]}", flush=True)
+    _, out, o_lat, lse = _run(x)
+    n_req = {"small": 2, "dsv3": 3, "long": 1, "merge": 2}[name]
+    reqs, heads = sample_pairs(x, n_req, 3, seed=SEEDS[name])
+    errs = check_step(x, out, o_lat, lse, requests=reqs, heads=heads, label=f"{name} full")
+    print(f"[parity] {name} full reqs={reqs} heads={heads}: {errs}", flush=True)
+    # every output finite, every lse finite (no request is empty at full size)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
