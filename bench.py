@@ -119,6 +119,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--detail", action="store_true", help="also time each call separately")
+    ap.add_argument("--eager", action="store_true", help="host launches instead of a HIP graph")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -156,6 +157,59 @@ def main():
                                     head_count=bs.head_count, causal=bs.causal))
         steps.append(DecodeStep(base.q_nope, base.q_pe, base.q_pos, base.w_uk, base.w_uv, segs, sp.batch, sp.s_q,
                                 x.scale, x.rope_base, n_wg=args.n_wg, n_split=base.n_split))
+    # Launch path.  Graph mode (default): the step is captured into a HIP
+    # graph of U consecutive steps (cycling the cache copies) and the timed
+    # region replays it, so small workloads are bound by the GPU rather than
+    # by five host launches per step.  The decode kernel's duration is then
+    # timed, right after the timed region, by HIP events around a graph of U
+    # back-to-back decode launches (so it includes the dispatch gap between
+    # kernels; HIP does not allow timing events inside a captured graph).
+    # Eager mode (--eager, or if capture fails): host launches, with events
+    # around every decode launch inside the timed region.
+    launch = "eager" if args.eager else "graph"
+    dec_us = None
+    if launch == "graph":
+        try:
+            cap = torch.cuda.Stream()
+            bound_cap = [st.bind(cap) for st in steps]
+            U = n_copies * max(1, math.ceil(8 / n_copies))
+
+            def build_graph(n_steps, parts=("pre", "dec", "post")):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    for k in range(n_steps):
+                        pre, dec, post = bound_cap[k % n_copies]
+                        for name, calls in zip(("pre", "dec", "post"), (pre, dec, post)):
+                            if name in parts:
+                                run_calls(calls)
+                return g
+
+            g_full = build_graph(U)
+            rem = args.steps % U
+            g_rem = build_graph(rem) if rem else None
+            g_dec = build_graph(U, parts=("dec",))
+            for _ in range(max(1, math.ceil(args.warmup / U))):
+                g_full.replay()
+            g_dec.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps // U):
+                g_full.replay()
+            if g_rem is not None:
+                g_rem.replay()
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = max(1, math.ceil(args.steps / U))
+            e0.record()
+            for _ in range(reps):
+                g_dec.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            dec_us = 1000.0 * e0.elapsed_time(e1) / (reps * U)
+        except Exception as e:  # noqa: BLE001 - fall back to host launches, and say so
+            print(f"graph capture unavailable ({type(e).__name__}: {e}); timing host launches", file=sys.stderr)
+            launch = "eager"
     stream = torch.cuda.current_stream()
     bound = [st.bind(stream) for st in steps]
 
@@ -169,31 +223,29 @@ def main():
             ev[1].record(stream)
         run_calls(post)
 
-    for i in range(args.warmup):
-        one(i)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        one(i, evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    if launch == "eager":
+        for i in range(args.warmup):
+            one(i)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            one(i, evs[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        dec_ms = [a.elapsed_time(b) for a, b in evs]
+        dec_us = 1000.0 * sum(dec_ms) / len(dec_ms)
     elapsed = t1 - t0
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
-    dec_us = 1000.0 * sum(dec_ms) / len(dec_ms)
 
     detail = None
     if args.detail:
-        names = ["rope", "absorb", "decode", "combine", "out_uv"]
+        # each call alone, back to back on the stream (host launches)
         detail = {}
         reps = 50
-        pre, dec, post = bound[0]
-        groups = {"rope": pre[:-1], "absorb": pre[-1:], "decode": dec, "combine": post[:1], "out_uv": post[1:]}
-        for nm in names:
+        for nm in ["rope", "absorb", "decode", "combine", "out_uv"]:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            for j in range(5):
-                run_calls(bound[j % n_copies][0] if nm in ("rope", "absorb") else groups[nm])
             torch.cuda.synchronize()
             e0.record(stream)
             for j in range(reps):
@@ -224,7 +276,7 @@ def main():
         "config": {"workload": sp.description, "name": sp.name, "batch": sp.batch, "heads": sp.heads,
                    "s_q": sp.s_q, "d_c": sp.d_c, "d_rope": sp.d_rope, "d_nope": sp.d_nope, "d_v": sp.d_v,
                    "cache_rows": sum(_rows(x)), "seed": seed, "cache_copies_rotated": n_copies,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", "launch": launch},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "mla_decode_splitkv (decode_bf16_kernel)",

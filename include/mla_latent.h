@@ -174,8 +174,8 @@ mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q
  * A row whose slots are all -inf gives o_lat = 0, lse = -inf.  o_part rows of
  * -inf slots are never read.
  *
- * o_part   [n_rows][n_part][d_c] fp32
- * lse_part [n_rows][n_part]      fp32
+ * o_part   [n_rows][n_part][d_c] fp32 (16-byte aligned, d_c a multiple of 4)
+ * lse_part [n_rows][n_part]      fp32 (n_part <= 1024)
  * o_lat    [n_rows][d_c]         out_dtype (MLA_BF16 or MLA_F32)
  * lse      [n_rows]              fp32, or NULL if not wanted
  */

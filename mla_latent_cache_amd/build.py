@@ -17,12 +17,14 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmla_latent.so")
-SOURCES = ["mla_api.cpp", "mla_small_kernels.hip", "mla_decode_bf16.hip"]
+SOURCES = ["mla_api.cpp", "mla_small_kernels.hip", "mla_decode_bf16.hip", "mla_proj_mfma.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are disabled: hipcc would otherwise generate
-# them from ordinary float code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# them from ordinary float code.  Private arrays are never promoted to LDS:
+# the kernels budget their LDS themselves.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-disable-promote-alloca-to-lds"]
 
 
 def hipcc() -> str:
@@ -53,7 +55,7 @@ def _compile(src: str, verbose: bool) -> str:
 def build(verbose: bool = False) -> str:
     """Compile and link the library; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs

@@ -135,8 +135,10 @@ mla_status mla_combine_lse(const float* o_part, const float* lse_part, int n_row
                            void* o_lat, int out_dtype, float* lse, void* stream) {
   if (!o_part || !lse_part || !o_lat) return fail(MLA_ERR_NULL, "mla_combine_lse: null pointer");
   if (!dtype_ok(out_dtype)) return fail(MLA_ERR_DTYPE, "mla_combine_lse: out_dtype %d", out_dtype);
-  if (n_rows < 0 || n_part <= 0 || d_c <= 0 || d_c > 1024)
-    return fail(MLA_ERR_SHAPE, "mla_combine_lse: n_rows=%d n_part=%d d_c=%d", n_rows, n_part, d_c);
+  if (n_rows < 0 || n_part <= 0 || n_part > 1024 || d_c <= 0 || d_c > 4096 || (d_c & 3) ||
+      ((reinterpret_cast<uintptr_t>(o_part) & 15u) != 0))
+    return fail(MLA_ERR_SHAPE, "mla_combine_lse: n_rows=%d n_part=%d (<= 1024) d_c=%d (multiple of 4, "
+                "o_part 16-byte aligned)", n_rows, n_part, d_c);
   if (n_rows == 0) return ok();
   return hip_status(mla::launch_combine(o_part, lse_part, n_rows, n_part, d_c, o_lat, out_dtype == MLA_BF16,
                                         lse, (hipStream_t)stream),

@@ -5,6 +5,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 namespace mla {
 
 typedef __bf16 bf16;
@@ -70,6 +73,21 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   return v;
+}
+
+// Launch a kernel and return the status of this launch itself
+// (hipLaunchKernel), never an error left behind by an unrelated earlier call.
+template <typename... KArgs, typename Tuple, size_t... I>
+inline hipError_t launch_tuple(void (*k)(KArgs...), dim3 grid, dim3 block, hipStream_t stream, Tuple& t,
+                               std::index_sequence<I...>) {
+  void* argv[] = {(void*)&std::get<I>(t)..., nullptr};
+  return hipLaunchKernel((const void*)k, grid, block, argv, 0, stream);
+}
+template <typename... KArgs, typename... Args>
+inline hipError_t launch(void (*k)(KArgs...), dim3 grid, dim3 block, hipStream_t stream, Args&&... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+  std::tuple<KArgs...> t(std::forward<Args>(args)...);
+  return launch_tuple(k, grid, block, stream, t, std::index_sequence_for<KArgs...>{});
 }
 
 }  // namespace mla

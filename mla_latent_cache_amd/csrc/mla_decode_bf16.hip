@@ -8,32 +8,40 @@
 //   s_t = scale * ([q_lat | q_rot] . [c_t | kr_t]),  p = softmax over the range,
 //   o_part = sum_t p_t c_t  (fp32, normalised),  lse_part = ln sum_t exp(s_t).
 //
-// Design (MI355X, 256 CUs, 160 KiB LDS per CU, 64-lane waves):
-//  * One workgroup (4 waves) owns up to MT query rows (all heads of a request
-//    for the segment, or a row group of them) and streams 32-row tiles of
-//    cache rows [c_t | kr_t] (576 bf16 = 1152 B) HBM -> LDS with direct-to-LDS
-//    loads, 3 stages deep.  Every tile is read from HBM once and shared by all
-//    MT query rows (the latent serves every head's key and value).
-//  * LDS rows are padded to 73 slots of 16 B so the 16 rows one MFMA operand
+// Design (MI355X: 256 CUs, 4 SIMDs and 160 KiB LDS per CU, 64-lane waves):
+//  * One workgroup of 8 waves (2 per SIMD) owns up to MT = 64 query rows (all
+//    heads of a request for the segment, or a 64-row group of them) and
+//    streams 32-row tiles of cache rows [c_t | kr_t] (576 bf16 = 1152 B)
+//    HBM -> LDS with direct-to-LDS loads, 3 stages deep.  Every tile is read
+//    from HBM once and shared by all MT query rows: the latent serves every
+//    head's key and value.
+//  * LDS rows are padded to 73 slots of 16 B so the 16 rows an MFMA operand
 //    read touches fall on distinct bank groups.
-//  * QK: S^T[tokens x rows] = K_tile . [q_lat|q_rot]^T with
-//    v_mfma_f32_16x16x32_bf16; query rows stay in registers; each QK wave
-//    owns whole rows, so the online-softmax row max and sum are in-wave.
-//  * Softmax in the exp2 domain with lazy rescaling: the running max is only
-//    raised when a tile max exceeds it by more than TAU (=8, log2 units), so
-//    the O rescale is almost never executed; p <= 2^TAU stays exact in fp32
-//    and representable in bf16.
-//  * PV: O^T[d x rows] += C_tile^T . P^T; the 512 latent columns are split over
-//    the 4 waves (128 each); the C^T operand comes from ds_read_b64_tr_b16
-//    transposed LDS reads, P^T from LDS.
+//  * QK: S^T[tokens x rows] = K_tile . [q_lat|q_rot]^T on
+//    v_mfma_f32_16x16x32_bf16.  The 576-long contraction is split in two
+//    halves over a pair of waves, so each wave keeps only 16 query rows x 288
+//    k in registers; the pair swaps partial scores through LDS and both then
+//    hold the full, bitwise-identical score block of their rows.
+//  * The query arrives in fp32 and is split into bf16 hi + lo parts (q = hi +
+//    lo to ~2^-17): two MFMAs per k-step into separate accumulators.  A
+//    bf16-rounded query would put ~1e-3 error into the scores.
+//  * Softmax in the exp2 domain (raw v_exp_f32) with lazy rescaling: the
+//    running max only moves when a tile max exceeds it by more than TAU = 8
+//    (log2 units), so the O rescale almost never runs; p <= 2^8 stays exact in
+//    fp32 and representable in bf16.  Full tiles skip all masking.
+//  * PV: O^T[d x rows] += C_tile^T . P^T; the 512 latent columns are split
+//    over the 8 waves (64 each); C^T comes from ds_read_b64_tr_b16 transposed
+//    LDS reads, P^T from LDS.
 //  * Work split: all rows of the segment (concatenated over requests) are cut
-//    into equal shares, one per workgroup (balanced regardless of the length
-//    mix); a share that crosses a request boundary yields several pieces.  At
-//    most n_split pieces per request; unused slots get lse = -inf.  Each
-//    workgroup derives its share from seq_lens on the device (no host sync).
+//    into equal shares, one per workgroup, whatever the length mix; a share
+//    crossing a request boundary yields several pieces.  At most n_split
+//    pieces per request; unused slots get lse = -inf.  Each workgroup derives
+//    its share from seq_lens on the device (no host synchronisation).
 //  * Grid: n_share workgroups per row group; the row groups of one share sit
 //    on the same XCD (workgroups are dispatched round-robin over 8 XCDs) so
 //    the second read of a tile hits that XCD's L2.
+//  * Synchronisation: a raw s_barrier plus explicit vmcnt/lgkmcnt waits;
+//    __syncthreads()' fence would drain the in-flight tile loads.
 #include "mla_common.h"
 #include "mla_kernels.h"
 
@@ -42,26 +50,29 @@ namespace {
 
 constexpr int kDc = 512;
 constexpr int kDr = 64;
-constexpr int kRow = kDc + kDr;          // elements per cache row
-constexpr int kRowBytes = kRow * 2;      // 1152
-constexpr int kTile = 32;                // cache rows per tile
-constexpr int kSlots = kRowBytes / 16;   // 72 16-byte chunks per row
-constexpr int kSlotStride = kSlots + 1;  // 73: one pad slot per LDS row
-constexpr int kLRow = kSlotStride * 16;  // 1168 bytes per LDS row
+constexpr int kRowBytes = (kDc + kDr) * 2;  // 1152
+constexpr int kTile = 32;                   // cache rows per tile
+constexpr int kSlots = kRowBytes / 16;      // 72 16-byte chunks per row
+constexpr int kSlotStride = kSlots + 1;     // 73: one pad slot per LDS row
+constexpr int kLRow = kSlotStride * 16;     // 1168 bytes per LDS row
 constexpr int kStageBytes = kTile * kLRow;
 constexpr int kNStage = 3;
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
 constexpr int kNDma = (kTile * kSlotStride + 63) / 64;  // 37 wave-instructions per tile
-constexpr int kPStr = 80;                // bytes per P row (32 bf16 + pad)
+constexpr int kPStr = 80;                   // bytes per P row (32 bf16 + pad)
 constexpr float kTau = 8.f;
 constexpr int kPageSize = 64;
 constexpr int kMaxPieces = 64;
+constexpr int kKSteps = (kDc + kDr) / 32;   // 18 MFMA k-steps over [c | kr]
+constexpr int kKHalf = kKSteps / 2;         // 9 per wave of a pair
 
 struct Piece {
   int b, r0, r1, slot;
 };
 
-// DMA instructions wave w issues for a full tile: k = w, w+4, ... < kNDma.
-__device__ __forceinline__ int dma_per_wave(int w) { return (kNDma - w + 3) / 4; }
+// DMA wave-instructions wave w issues for a full tile: k = w, w + 8, ... < kNDma.
+__device__ __forceinline__ int dma_per_wave(int w) { return (kNDma - w + kWaves - 1) / kWaves; }
 
 __device__ __forceinline__ int sload_i32(const int32_t* p) {
   // Scalar (SMEM) load: counted by lgkmcnt, so it never forces the in-flight
@@ -71,37 +82,90 @@ __device__ __forceinline__ int sload_i32(const int32_t* p) {
   return v;
 }
 
+// Issue the direct-to-LDS loads of one tile: rows [t0, t0 + nvalid) of one
+// request into an LDS stage (73 slots of 16 B per row; slot 72 is padding).
+// Wave `wave` issues wave-instructions k = wave, wave + 8, ... (64 slots
+// each).  Rows past nvalid are zero-filled so no stale value is ever read.
+// All arguments are plain values: no pointer to the kernel-argument block is
+// captured, so no load (and no vmcnt wait) precedes the DMA instructions.
+__device__ __forceinline__ void issue_tile_dma(char* st, const char* cache, const char* req_base,
+                                               const int32_t* bt_row, int n_pages, int t0, int nvalid,
+                                               int wave, int lane) {
+  int pg0 = 0, pg1 = 0;
+  if (bt_row) {
+    pg0 = sload_i32(bt_row + t0 / kPageSize);
+    pg1 = sload_i32(bt_row + (t0 + nvalid - 1) / kPageSize);
+  }
+  for (int k = wave; k < kNDma; k += kWaves) {
+    const int slotl = k * 64 + lane;
+    const int r = slotl / kSlotStride;
+    const int c = slotl - r * kSlotStride;
+    const bool in_tile = slotl < kTile * kSlotStride && c < kSlots;
+    bool ok = in_tile && r < nvalid;
+    const char* src = nullptr;
+    if (bt_row) {
+      const int t = t0 + r;
+      const int pg = (t / kPageSize == t0 / kPageSize) ? pg0 : pg1;
+      ok = ok && pg >= 0 && pg < n_pages;
+      src = cache + ((int64_t)pg * kPageSize + (t % kPageSize)) * kRowBytes + c * 16;
+    } else {
+      src = req_base + (int64_t)(t0 + r) * kRowBytes + c * 16;
+    }
+    if (ok) {
+      __builtin_amdgcn_global_load_lds((const void*)src, (MLA_LDS void*)(st + k * 1024), 16, 0, 0);
+    } else if (in_tile) {
+      *(int4*)(st + slotl * 16) = int4{0, 0, 0, 0};
+    }
+  }
+}
+
 template <int MT>
 struct Smem {
   char stage[kNStage][kStageBytes];
   char p[2][MT * kPStr];
+  f32x4 sx[MT / 16][2][2][64];  // partial scores: [row block][writer k-half][token block][lane]
   float alpha[2][MT];
+  float lpart[2][MT];
   float rowinv[MT];
   int flag[2][4];
   Piece pieces[kMaxPieces];
   int n_pieces;
-  int base_next;
   int done;
-  int red_i[8];
+  int red_i[2 * kWaves];
 };
 
 }  // namespace
 
-// QF32: the query (q_lat, q_rot) arrives in fp32 and is split into bf16
-// hi + lo parts (q = hi + lo to ~2^-17 relative), each multiplied with the
-// bf16 cache tile; two MFMAs per k-step keep the score error ~1e-6 instead of
-// the ~1e-3 a bf16-rounded query gives.  With a bf16 query, one MFMA.
 template <int MT, bool QF32>
-__global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a, int n_share, int n_rg,
-                                                             int rows_total) {
-  constexpr int NQH = QF32 ? 2 : 1;            // query parts (hi, lo)
-  constexpr int NQW = MT >= 64 ? 4 : MT / 16;  // waves that run QK + softmax
-  constexpr int RW = MT / NQW;                 // query rows per QK wave (16 or 32)
-  constexpr int RB = RW / 16;
-  constexpr int QB = MT / 16;                  // row blocks in PV
+__global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, int n_share, int n_rg,
+                                                                  int rows_total) {
+  constexpr int NQH = QF32 ? 2 : 1;  // query parts (hi, lo)
+  constexpr int NRB = MT / 16;       // 16-row blocks
+  constexpr int NQW = 2 * NRB;       // waves running QK + softmax: (row block, k-half)
   __shared__ __attribute__((aligned(16))) Smem<MT> sm;
 
-  const SegArgs& sg = a.seg;
+  // every argument field as a local value (see issue_tile_dma)
+  const char* const cache = (const char*)a.seg.cache;
+  const int32_t* const block_table = a.seg.block_table;
+  const int32_t* const seq_lens = a.seg.seq_lens;
+  const void* const q_rot_p = a.seg.q_rot;
+  const void* const q_lat_p = a.q_lat;
+  float* const o_part = a.o_part;
+  float* const lse_part = a.lse_part;
+  const int64_t max_rows = a.seg.max_rows;
+  const int max_pages = a.seg.max_pages;
+  const int n_pages = a.seg.n_pages;
+  const int head_begin = a.seg.head_begin;
+  const int hc = a.seg.head_count;
+  const int causal = a.seg.causal;
+  const int part_begin = a.seg.part_begin;
+  const int n_split = a.seg.n_split;
+  const int s_q = a.s_q;
+  const int n_heads = a.n_heads;
+  const int n_part = a.n_part;
+  const int B = a.batch;
+  const float sl2 = a.scale * kLog2e;
+
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -117,17 +181,15 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a, int n
     rg = (blockIdx.x / 8) % n_rg;
     j = (blockIdx.x / (8 * n_rg)) * 8 + blockIdx.x % 8;
   }
-  const int row0 = rg * MT;                       // first segment row of this group
-  const int nrows = min(MT, rows_total - row0);   // rows in this group
-  const int hc = sg.head_count;
-  const int B = a.batch;
-  const int64_t cap = sg.block_table ? (int64_t)sg.max_pages * kPageSize : sg.max_rows;
-  auto clampT = [&](int t) -> int { return (int)max((int64_t)0, min((int64_t)t, cap)); };
+  const int row0 = rg * MT;                      // first segment row of this group
+  const int nrows = min(MT, rows_total - row0);  // rows in this group
+  const int64_t cap = block_table ? (int64_t)max_pages * kPageSize : max_rows;
+  auto clampT = [cap](int t) -> int { return (int)max((int64_t)0, min((int64_t)t, cap)); };
 
   // ---- plan pass 1: total and longest request ----
   int tsum = 0, tmax = 0;
-  for (int b = tid; b < B; b += 256) {
-    const int T = clampT(sg.seq_lens[b]);
+  for (int b = tid; b < B; b += kThreads) {
+    const int T = clampT(seq_lens[b]);
     tsum += T;
     tmax = max(tmax, T);
   }
@@ -138,46 +200,42 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a, int n
   }
   if (lane == 0) {
     sm.red_i[wave] = tsum;
-    sm.red_i[4 + wave] = tmax;
+    sm.red_i[kWaves + wave] = tmax;
   }
   __syncthreads();
-  tsum = sm.red_i[0] + sm.red_i[1] + sm.red_i[2] + sm.red_i[3];
-  tmax = max(max(sm.red_i[4], sm.red_i[5]), max(sm.red_i[6], sm.red_i[7]));
-  const bool req_mode = sg.n_split == 1;
+  tsum = 0;
+  tmax = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    tsum += sm.red_i[w];
+    tmax = max(tmax, sm.red_i[kWaves + w]);
+  }
+  const bool req_mode = n_split == 1;
   int share = 0;
   if (!req_mode) {
     share = (tsum + n_share - 1) / n_share;
-    share = max(share, (tmax + sg.n_split - 2) / (sg.n_split - 1));
+    share = max(share, (tmax + n_split - 2) / (n_split - 1));
     share = max(kTile, (share + kTile - 1) / kTile * kTile);
   }
   const int lo = j * share, hi = lo + share;
-  const float sl2 = a.scale * kLog2e;
 
-  // ---- per-row constants of the QK waves ----
-  // query row handled by this lane in row block rb: local index qrow
-  int vis_last[RB];   // last visible request-local row for this query row (causal), filled per piece
-  int s_of[RB];
-  bool rvalid[RB];
-  int64_t q_off[RB];  // (tok * n_heads + h) for the row, without tok's request part
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int qrow = wave * RW + rb * 16 + l16;
-    const int R = row0 + qrow;
-    rvalid[rb] = wave < NQW && qrow < nrows;
-    const int Rc = rvalid[rb] ? R : 0;
-    s_of[rb] = Rc / hc;
-    q_off[rb] = (int64_t)s_of[rb] * a.n_heads + sg.head_begin + Rc % hc;
-    vis_last[rb] = 0;
-  }
-
-  const char* cache = (const char*)sg.cache;
+  // ---- the query row of this lane in the QK waves ----
+  const bool qk_wave = wave < NQW;
+  const int rb = wave % NRB;        // row block (QK waves)
+  const int kh = wave / NRB;        // k-half (QK waves)
+  const int qrow = rb * 16 + l16;   // local row
+  const bool rvalid = qk_wave && qrow < nrows;
+  const int Rc = rvalid ? row0 + qrow : row0;
+  const int s_row = Rc / hc;
+  const int64_t q_off = (int64_t)s_row * n_heads + head_begin + Rc % hc;  // without the request part
+  const int s_min = row0 / hc;      // smallest token index among the group's rows
 
   int base = 0;  // prefix of T over requests scanned so far (wave 0)
   for (int chunk = 0;; ++chunk) {
     // ---- plan pass 2: wave 0 scans 64 requests, lists pieces, writes -inf tails ----
     if (wave == 0) {
       const int b = chunk * 64 + lane;
-      const int T = b < B ? clampT(sg.seq_lens[b]) : 0;
+      const int T = b < B ? clampT(seq_lens[b]) : 0;
       int incl = T;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -191,7 +249,6 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a, int n
         is_piece = b < B && T > 0 && (b % n_share) == j;
         r1 = T;
         tail = b < B && T == 0 && (b % n_share) == j;
-        cnt = 0;
       } else {
         is_piece = b < B && T > 0 && S < hi && S + T > lo;
         r0 = max(lo, S) - S;
@@ -199,7 +256,7 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a, int n
         slot = j - S / share;
         const int jf = min(S / share, n_share - 1);
         cnt = T > 0 ? (S + T - 1) / share - S / share + 1 : 0;
-        tail = b < B && jf == j && cnt < sg.n_split;
+        tail = b < B && jf == j && cnt < n_split;
       }
       const uint64_t pm = __ballot(is_piece);
       if (is_piece) {
@@ -213,20 +270,19 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a, int n
         tm &= tm - 1;
         const int tb_ = __shfl(b, src);
         const int tc = __shfl(cnt, src);
-        const int nsl = sg.n_split - tc;
+        const int nsl = n_split - tc;
         for (int e = lane; e < nsl * nrows; e += 64) {
           const int k = tc + e / nrows;
           const int R = row0 + e % nrows;
-          const int tok = tb_ * a.s_q + R / hc;
-          const int h = sg.head_begin + R % hc;
-          a.lse_part[((int64_t)tok * a.n_heads + h) * a.n_part + sg.part_begin + k] = -INFINITY;
+          const int tok = tb_ * s_q + R / hc;
+          const int h = head_begin + R % hc;
+          lse_part[((int64_t)tok * n_heads + h) * n_part + part_begin + k] = -INFINITY;
         }
       }
       const int total = __shfl(incl, 63);
       if (lane == 0) {
         sm.n_pieces = __popcll(pm);
-        const int nb = base + total;
-        const bool past = !req_mode && nb >= hi && j < n_share - 1;
+        const bool past = !req_mode && base + total >= hi && j < n_share - 1;
         sm.done = (chunk * 64 + 64 >= B) || past;
       }
       base += total;
@@ -241,248 +297,217 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a, int n
       const int pr0 = __builtin_amdgcn_readfirstlane(pc.r0);
       const int pr1 = __builtin_amdgcn_readfirstlane(pc.r1);
       const int slot = __builtin_amdgcn_readfirstlane(pc.slot);
-      const int T = clampT(sg.seq_lens[b]);
+      const int T = clampT(seq_lens[b]);
+      const int vis_last = causal ? T - s_q + s_row : T - 1;  // last visible row of this lane's query
+      const int vis_min = causal ? T - s_q + s_min : T - 1;   // ... of the group's first query row
 
-      // ---- query rows into registers: [q_lat | q_rot] k-chunks of this lane ----
-      bf16x8 qreg[NQH][RB][18];
+      // ---- this wave's half of its query rows: [q_lat | q_rot], k-steps kh*9 .. kh*9+8 ----
+      bf16x8 qreg[NQH][kKHalf];
+      if (qk_wave) {
+        const int64_t qi = (int64_t)b * s_q * n_heads + q_off;
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int64_t qi = (int64_t)b * a.s_q * a.n_heads + q_off[rb];
-        vis_last[rb] = sg.causal ? T - a.s_q + s_of[rb] : T - 1;
-#pragma unroll
-        for (int ks = 0; ks < 18; ++ks) {
-          const int k0 = 32 * ks + 8 * lg;
+        for (int kk = 0; kk < kKHalf; ++kk) {
+          const int k0 = 32 * (kh * kKHalf + kk) + 8 * lg;
           if constexpr (QF32) {
             f32x4 v0 = f32x4{0.f, 0.f, 0.f, 0.f}, v1 = v0;
-            if (rvalid[rb]) {
-              const float* src = k0 < kDc ? (const float*)a.q_lat + qi * kDc + k0
-                                          : (const float*)sg.q_rot + qi * kDr + (k0 - kDc);
+            if (rvalid) {
+              const float* src = k0 < kDc ? (const float*)q_lat_p + qi * kDc + k0
+                                          : (const float*)q_rot_p + qi * kDr + (k0 - kDc);
               v0 = *(const f32x4*)src;
               v1 = *(const f32x4*)(src + 4);
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               const float v = e < 4 ? v0[e] : v1[e - 4];
-              const bf16 hi = (bf16)v;
-              qreg[0][rb][ks][e] = hi;
-              qreg[1][rb][ks][e] = (bf16)(v - (float)hi);
+              const bf16 h = (bf16)v;
+              qreg[0][kk][e] = h;
+              qreg[1][kk][e] = (bf16)(v - (float)h);
             }
           } else {
-            qreg[0][rb][ks] = rvalid[rb]
-                ? (k0 < kDc ? *(const bf16x8*)((const bf16*)a.q_lat + qi * kDc + k0)
-                            : *(const bf16x8*)((const bf16*)sg.q_rot + qi * kDr + (k0 - kDc)))
-                : bf16x8{};
+            qreg[0][kk] = rvalid ? (k0 < kDc ? *(const bf16x8*)((const bf16*)q_lat_p + qi * kDc + k0)
+                                             : *(const bf16x8*)((const bf16*)q_rot_p + qi * kDr + (k0 - kDc)))
+                                 : bf16x8{};
           }
         }
       }
 
-      // ---- tile DMA: rows [t0, t0 + nvalid) of request b into stage st ----
-      const char* req_base = cache + (int64_t)b * sg.max_rows * kRowBytes;  // contiguous layout
-      auto issue_tile = [&](int it) {
-        const int t0 = pr0 + it * kTile;
-        const int nvalid = min(kTile, pr1 - t0);
-        char* st = sm.stage[it % kNStage];
-        int pg0 = 0, pg1 = 0;
-        if (sg.block_table) {
-          const int32_t* bt = sg.block_table + (int64_t)b * sg.max_pages;
-          pg0 = sload_i32(bt + t0 / kPageSize);
-          pg1 = sload_i32(bt + (t0 + nvalid - 1) / kPageSize);
-        }
-        for (int k = wave; k < kNDma; k += 4) {
-          const int slotl = k * 64 + lane;
-          const int r = slotl / kSlotStride;
-          const int c = slotl - r * kSlotStride;
-          const bool in_tile = slotl < kTile * kSlotStride && c < kSlots;
-          bool ok = in_tile && r < nvalid;
-          const char* src = nullptr;
-          if (ok) {
-            const int t = t0 + r;
-            if (sg.block_table) {
-              const int pg = (t / kPageSize == t0 / kPageSize) ? pg0 : pg1;
-              ok = pg >= 0 && pg < sg.n_pages;
-              src = cache + ((int64_t)pg * kPageSize + (t % kPageSize)) * kRowBytes + c * 16;
-            } else {
-              src = req_base + (int64_t)t * kRowBytes + c * 16;
-            }
-          }
-          if (ok) {
-            __builtin_amdgcn_global_load_lds((const void*)src, (MLA_LDS void*)(st + k * 1024), 16, 0, 0);
-          } else if (in_tile) {
-            *(int4*)(st + slotl * 16) = int4{0, 0, 0, 0};  // rows past the piece: zeros, never stale
-          }
-        }
-      };
-
+      const char* const req_base = cache + (int64_t)b * max_rows * kRowBytes;  // contiguous layout
+      const int32_t* const bt_row = block_table ? block_table + (int64_t)b * max_pages : nullptr;
       const int n_tiles = (pr1 - pr0 + kTile - 1) / kTile;
-      issue_tile(0);
-      if (n_tiles > 1) issue_tile(1);
+      issue_tile_dma(sm.stage[0], cache, req_base, bt_row, n_pages, pr0, min(kTile, pr1 - pr0), wave, lane);
+      if (n_tiles > 1)
+        issue_tile_dma(sm.stage[1], cache, req_base, bt_row, n_pages, pr0 + kTile, min(kTile, pr1 - pr0 - kTile),
+                       wave, lane);
 
-      // ---- running state ----
-      float m_used[RB], l_part[RB];
+      float m_used = -INFINITY;  // running max (log2 units) of this lane's query row
+      float l_part = 0.f;        // sum of p over this wave's token half, this lane's 4 tokens
+      f32x4 acc_o[4][NRB];
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        m_used[rb] = -INFINITY;
-        l_part[rb] = 0.f;
-      }
-      f32x4 acc_o[8][QB];
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int db = 0; db < 8; ++db)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) acc_o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < NRB; ++q) acc_o[db][q] = f32x4{0.f, 0.f, 0.f, 0.f};
 
       for (int it = 0; it < n_tiles; ++it) {
-        // tile `it` landed: at most the (full) next tile's loads may remain in flight
-        const bool next_full = it + 1 < n_tiles && (pr1 - (pr0 + (it + 1) * kTile)) >= kTile;
-        if (next_full) {
+        // tile `it` landed: at most the (full) next tile's loads may still be in flight
+        const int t0 = pr0 + it * kTile;
+        const bool next_full = it + 1 < n_tiles && pr1 - (t0 + kTile) >= kTile;
+        if (next_full)
           wait_vmcnt_dyn(dma_per_wave(wave));
-        } else {
+        else
           wait_vmcnt<0>();
-        }
         wait_lgkm0();
         barrier_raw();
-        if (it + 2 < n_tiles) issue_tile(it + 2);
-
+        if (it + 2 < n_tiles) {
+          const int t2 = t0 + 2 * kTile;
+          issue_tile_dma(sm.stage[(it + 2) % kNStage], cache, req_base, bt_row, n_pages, t2,
+                         min(kTile, pr1 - t2), wave, lane);
+        }
         const char* st = sm.stage[it % kNStage];
-        const int t0 = pr0 + it * kTile;
         const int buf = it & 1;
+        const bool full = t0 + kTile <= pr1 && t0 + kTile - 1 <= vis_min;
 
-        // ---------------- QK + softmax (waves < NQW) ----------------
-        if (wave < NQW) {
-          f32x4 sacc[2][RB];
+        // ---------------- QK: partial scores over this wave's k-half ----------------
+        f32x4 sp[2];
+        if (qk_wave) {
+          f32x4 sacc[2][NQH];
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) sacc[tb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int hl = 0; hl < NQH; ++hl) sacc[tb][hl] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int ks = 0; ks < 18; ++ks) {
+          for (int kk = 0; kk < kKHalf; ++kk) {
+            const int ks = kh * kKHalf + kk;
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb) {
               const bf16x8 ak = *(const bf16x8*)(st + (16 * tb + l16) * kLRow + (4 * ks + lg) * 16);
 #pragma unroll
-              for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                for (int hl = 0; hl < NQH; ++hl)
-                  sacc[tb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, qreg[hl][rb][ks], sacc[tb][rb], 0, 0, 0);
+              for (int hl = 0; hl < NQH; ++hl)
+                sacc[tb][hl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, qreg[hl][kk], sacc[tb][hl], 0, 0, 0);
             }
           }
-          bool need_any = false;
-          float alpha_r[RB];
-          float pv[2][RB][4];
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            float mt = -INFINITY;
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int t = t0 + 16 * tb + 4 * lg + e;
-                const bool v = t < pr1 && t <= vis_last[rb];
-                const float s2 = v ? sacc[tb][rb][e] * sl2 : -INFINITY;
-                pv[tb][rb][e] = s2;
-                mt = fmaxf(mt, s2);
-              }
-            mt = fmaxf(mt, __shfl_xor(mt, 16));
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            const bool need = mt > m_used[rb] + kTau;
-            alpha_r[rb] = 1.f;
-            if (need) {
-              alpha_r[rb] = exp2f(m_used[rb] - mt);  // 0 when m_used was -inf
-              m_used[rb] = mt;
-              l_part[rb] *= alpha_r[rb];
-            }
-            need_any |= need;
+          for (int tb = 0; tb < 2; ++tb) {
+            sp[tb] = sacc[tb][0];
+            if constexpr (QF32) sp[tb] += sacc[tb][1];
+            sm.sx[rb][kh][tb][lane] = sp[tb];
           }
-          const bool any = __ballot(need_any) != 0;
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            const int qrow = wave * RW + rb * 16 + l16;
-            float lsum = 0.f;
-            bf16x4 pk[2];
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float s2 = pv[tb][rb][e];
-                const float p = s2 == -INFINITY ? 0.f : exp2f(s2 - m_used[rb]);
-                lsum += p;
-                pk[tb][e] = (bf16)p;
-              }
-            l_part[rb] += lsum;
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
-              *(bf16x4*)(sm.p[buf] + qrow * kPStr + (16 * tb + 4 * lg) * 2) = pk[tb];
-            if (lg == 0) sm.alpha[buf][qrow] = alpha_r[rb];  // read by PV if any wave rescaled
-          }
-          if (lane == 0) sm.flag[buf][wave] = any ? 1 : 0;
         }
         wait_lgkm0();
         barrier_raw();
 
-        // ---------------- PV: O^T[d x rows] += C^T . P^T ----------------
+        // ---------------- softmax (QK waves): full scores, this wave's token half ----------------
+        if (qk_wave) {
+          float s2[2][4];
+          float mt = -INFINITY;
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb) {
+            const f32x4 other = sm.sx[rb][1 - kh][tb][lane];
+            // both waves of the pair add the same two values: identical scores
+            const f32x4 full_s = sp[tb] + other;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float v = full_s[e] * sl2;
+              if (!full) {
+                const int t = t0 + 16 * tb + 4 * lg + e;
+                v = (t < pr1 && t <= vis_last) ? v : -INFINITY;
+              }
+              s2[tb][e] = v;
+              mt = fmaxf(mt, v);
+            }
+          }
+          mt = fmaxf(mt, __shfl_xor(mt, 16));
+          mt = fmaxf(mt, __shfl_xor(mt, 32));
+          const bool need = mt > m_used + kTau;
+          float alpha = 1.f;
+          if (need) {
+            alpha = __builtin_amdgcn_exp2f(m_used - mt);  // 0 when m_used was -inf
+            m_used = mt;
+            l_part *= alpha;
+          }
+          const bool any = __ballot(need) != 0;
+          const float msub = m_used == -INFINITY ? 0.f : m_used;
+          bf16x4 pk;
+          float lsum = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p = __builtin_amdgcn_exp2f((kh ? s2[1][e] : s2[0][e]) - msub);  // exp2(-inf) = 0
+            lsum += p;
+            pk[e] = (bf16)p;
+          }
+          l_part += lsum;
+          *(bf16x4*)(sm.p[buf] + qrow * kPStr + (16 * kh + 4 * lg) * 2) = pk;
+          if (kh == 0) {
+            if (lg == 0) sm.alpha[buf][qrow] = alpha;
+            if (lane == 0) sm.flag[buf][rb] = any ? 1 : 0;
+          }
+        }
+        wait_lgkm0();
+        barrier_raw();
+
+        // ---------------- PV: O^T[d x rows] += C^T . P^T, 64 columns per wave ----------------
         {
           int flag = 0;
 #pragma unroll
-          for (int w = 0; w < NQW; ++w) flag |= sm.flag[buf][w];
-          bf16x8 bq[QB];
+          for (int r = 0; r < NRB; ++r) flag |= sm.flag[buf][r];
+          bf16x8 bq[NRB];
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            bq[qb] = *(const bf16x8*)(sm.p[buf] + (16 * qb + l16) * kPStr + lg * 16);
+          for (int q = 0; q < NRB; ++q) bq[q] = *(const bf16x8*)(sm.p[buf] + (16 * q + l16) * kPStr + lg * 16);
           if (flag) {
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-              const float al = sm.alpha[buf][16 * qb + l16];
+            for (int q = 0; q < NRB; ++q) {
+              const float al = sm.alpha[buf][16 * q + l16];
 #pragma unroll
-              for (int db = 0; db < 8; ++db) acc_o[db][qb] *= al;
+              for (int db = 0; db < 4; ++db) acc_o[db][q] *= al;
             }
           }
-          const int rq = (lane & 15) >> 2, qq = lane & 3;
+          const int rq = l16 >> 2, qq = lane & 3;
 #pragma unroll
-          for (int db = 0; db < 8; ++db) {
-            const int d0 = 128 * wave + 16 * db;
+          for (int db = 0; db < 4; ++db) {
+            const int d0 = 64 * wave + 16 * db;
             const char* p0 = st + (8 * lg + rq) * kLRow + (d0 + 4 * qq) * 2;
             const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p0));
             const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p0 + 4 * kLRow));
             const bf16x8 ac = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-              acc_o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ac, bq[qb], acc_o[db][qb], 0, 0, 0);
+            for (int q = 0; q < NRB; ++q)
+              acc_o[db][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ac, bq[q], acc_o[db][q], 0, 0, 0);
           }
         }
       }
 
-      // ---- piece epilogue: normalise and write the partial state ----
-      if (wave < NQW) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          float lt = l_part[rb];
-          lt += __shfl_xor(lt, 16);
-          lt += __shfl_xor(lt, 32);
-          const int qrow = wave * RW + rb * 16 + l16;
-          const float inv = lt > 0.f ? 1.f / lt : 0.f;
-          if (lg == 0) {
-            sm.rowinv[qrow] = inv;
-            if (rvalid[rb]) {
-              const int64_t ri = (int64_t)b * a.s_q * a.n_heads + q_off[rb];
-              a.lse_part[ri * a.n_part + sg.part_begin + slot] =
-                  lt > 0.f ? (m_used[rb] + __log2f(lt)) * kLn2 : -INFINITY;
-            }
+      // ---- piece epilogue: row sums of both halves, lse, normalised partial ----
+      if (qk_wave) {
+        float lt = l_part;
+        lt += __shfl_xor(lt, 16);
+        lt += __shfl_xor(lt, 32);
+        if (lg == 0) sm.lpart[kh][qrow] = lt;
+      }
+      wait_lgkm0();
+      barrier_raw();
+      if (qk_wave && kh == 0) {
+        const float lt = sm.lpart[0][qrow] + sm.lpart[1][qrow];
+        if (lg == 0) {
+          sm.rowinv[qrow] = lt > 0.f ? 1.f / lt : 0.f;
+          if (rvalid) {
+            const int64_t ri = (int64_t)b * s_q * n_heads + q_off;
+            lse_part[ri * n_part + part_begin + slot] = lt > 0.f ? (m_used + __log2f(lt)) * kLn2 : -INFINITY;
           }
         }
       }
       wait_lgkm0();
       barrier_raw();
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int qrow = 16 * qb + l16;
-        const float inv = sm.rowinv[qrow];
-        if (qrow < nrows && inv > 0.f) {
-          const int R = row0 + qrow;
-          const int tok = b * a.s_q + R / hc;
-          const int h = sg.head_begin + R % hc;
-          float* o = a.o_part + (((int64_t)tok * a.n_heads + h) * a.n_part + sg.part_begin + slot) * kDc +
-                     128 * wave + 4 * lg;
+      for (int q = 0; q < NRB; ++q) {
+        const int qr = 16 * q + l16;
+        const float inv = sm.rowinv[qr];
+        if (qr < nrows && inv > 0.f) {
+          const int R = row0 + qr;
+          const int tok = b * s_q + R / hc;
+          const int h = head_begin + R % hc;
+          float* o = o_part + (((int64_t)tok * n_heads + h) * n_part + part_begin + slot) * kDc + 64 * wave +
+                     4 * lg;
 #pragma unroll
-          for (int db = 0; db < 8; ++db) *(f32x4*)(o + 16 * db) = acc_o[db][qb] * inv;
+          for (int db = 0; db < 4; ++db) *(f32x4*)(o + 16 * db) = acc_o[db][q] * inv;
         }
       }
       barrier_raw();  // stage buffers, P and rowinv are reused by the next piece
@@ -492,8 +517,8 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a, int n
   }
 }
 
-// Row groups of at most 64 query rows: 64 keeps the query block, the O
-// accumulator and the score tile in registers without spilling.
+// Row groups of at most 64 query rows: 64 keeps each wave's half of the query
+// block, its O columns and the scores in registers without spilling.
 static int row_tile(int rows_total) { return rows_total <= 16 ? 16 : rows_total <= 32 ? 32 : 64; }
 
 void decode_bf16_grid(int rows_total, int n_wg, int* n_share, int* n_rg) {
@@ -508,19 +533,16 @@ void decode_bf16_grid(int rows_total, int n_wg, int* n_share, int* n_rg) {
 }
 
 template <bool QF32>
-static void launch_mt(const DecodeArgs& a, int mt, dim3 grid, int n_share, int n_rg, int rows_total,
-                      hipStream_t stream) {
-  const dim3 block(256);
+static hipError_t launch_mt(const DecodeArgs& a, int mt, dim3 grid, int n_share, int n_rg, int rows_total,
+                            hipStream_t stream) {
+  const dim3 block(kThreads);
   switch (mt) {
     case 16:
-      hipLaunchKernelGGL((decode_bf16_kernel<16, QF32>), grid, block, 0, stream, a, n_share, n_rg, rows_total);
-      break;
+      return launch((decode_bf16_kernel<16, QF32>), grid, block, stream, a, n_share, n_rg, rows_total);
     case 32:
-      hipLaunchKernelGGL((decode_bf16_kernel<32, QF32>), grid, block, 0, stream, a, n_share, n_rg, rows_total);
-      break;
+      return launch((decode_bf16_kernel<32, QF32>), grid, block, stream, a, n_share, n_rg, rows_total);
     default:
-      hipLaunchKernelGGL((decode_bf16_kernel<64, QF32>), grid, block, 0, stream, a, n_share, n_rg, rows_total);
-      break;
+      return launch((decode_bf16_kernel<64, QF32>), grid, block, stream, a, n_share, n_rg, rows_total);
   }
 }
 
@@ -530,11 +552,8 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, int n_wg, bool q_f32, hipStre
   int n_share, n_rg;
   decode_bf16_grid(rows_total, n_wg, &n_share, &n_rg);
   const dim3 grid(n_share * n_rg);
-  if (q_f32)
-    launch_mt<true>(a, mt, grid, n_share, n_rg, rows_total, stream);
-  else
-    launch_mt<false>(a, mt, grid, n_share, n_rg, rows_total, stream);
-  return hipGetLastError();
+  if (q_f32) return launch_mt<true>(a, mt, grid, n_share, n_rg, rows_total, stream);
+  return launch_mt<false>(a, mt, grid, n_share, n_rg, rows_total, stream);
 }
 
 }  // namespace mla

@@ -46,6 +46,13 @@ hipError_t launch_absorb(const void* q_nope, const void* w_uk, bool in_bf16, voi
                          int n_tok, int n_heads, int d_nope, int d_c, hipStream_t stream);
 hipError_t launch_out_uv(const void* o_lat, bool o_bf16, const void* w_uv, bool w_bf16, void* out,
                          bool out_bf16, int n_tok, int n_heads, int d_c, int d_v, hipStream_t stream);
+// bf16 MFMA variants (d_nope = 128, d_c = 512, d_v = 128, 16-byte aligned).
+bool absorb_mfma_ok(const void* q_nope, const void* w_uk, int d_nope, int d_c);
+hipError_t launch_absorb_mfma(const void* q_nope, const void* w_uk, void* q_lat, bool out_bf16, int n_tok,
+                              int n_heads, hipStream_t stream);
+bool out_uv_mfma_ok(const void* o_lat, const void* w_uv, int d_c, int d_v);
+hipError_t launch_out_uv_mfma(const void* o_lat, const void* w_uv, void* out, bool out_bf16, int n_tok,
+                              int n_heads, hipStream_t stream);
 hipError_t launch_combine(const float* o_part, const float* lse_part, int n_rows, int n_part,
                           int d_c, void* o_lat, bool out_bf16, float* lse, hipStream_t stream);
 // Generic fp32 decode (any d_c <= 512, d_rope <= 128): one wave per

@@ -1,0 +1,145 @@
+// Per-query projections on bf16 MFMA (gfx950 v_mfma_f32_16x16x32_bf16).
+//
+// absorb:  q_lat[t][h][j] = sum_i q_nope[t][h][i] * w_uk[h][i][j]
+//          (MLA tutorial page, "Move the Key Projection Into the Query")
+// out_uv:  out[t][h][v]   = sum_c o_lat[t][h][c] * w_uv[h][v][c]
+//          (MLA tutorial page, "Move the Value Expansion After the Weighted Sum")
+//
+// Both are per head a small GEMM [n_tok x K] . [K x N] whose cost is reading
+// the head's weights once (128 x 512 bf16 = 128 KiB); tokens are padded to
+// 16-row MFMA blocks.  For absorb the contraction index i is the row index of
+// w_uk, so the B operand (8 consecutive i per lane) is taken from an LDS copy
+// of the weight slice with ds_read_b64_tr_b16; for out_uv the contraction
+// index c is contiguous in both operands, which are loaded straight from HBM.
+#include "mla_common.h"
+#include "mla_kernels.h"
+
+namespace mla {
+namespace {
+
+constexpr int kNope = 128;        // d_nope of the bf16 fast path
+constexpr int kLat = 512;         // d_c
+constexpr int kAbsCols = 128;     // output columns per absorb workgroup
+constexpr int kAbsLds = kAbsCols * 2 + 16;  // bytes per LDS weight row (padded)
+
+template <typename TO>
+__global__ __launch_bounds__(256) void absorb_mfma_kernel(const bf16* __restrict__ q_nope,
+                                                          const bf16* __restrict__ w_uk, TO* __restrict__ q_lat,
+                                                          int n_tok, int n_heads) {
+  __shared__ __attribute__((aligned(16))) char wl[kNope * kAbsLds];
+  const int h = blockIdx.x;
+  const int j0 = blockIdx.y * kAbsCols;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l16 = lane & 15, lg = lane >> 4;
+  // weight slice w_uk[h][0:128][j0:j0+128] -> LDS (row i: 256 B + pad)
+  const bf16* w = w_uk + (int64_t)h * kNope * kLat + j0;
+  for (int e = tid; e < kNope * (kAbsCols / 8); e += 256) {
+    const int i = e / (kAbsCols / 8), c8 = e % (kAbsCols / 8);
+    *(bf16x8*)(wl + i * kAbsLds + c8 * 16) = *(const bf16x8*)(w + (int64_t)i * kLat + c8 * 8);
+  }
+  __syncthreads();
+  const int rq = l16 >> 2, qq = lane & 3;
+  for (int t0 = 0; t0 < n_tok; t0 += 16) {
+    // A operand: 16 tokens x 128 i, lane row l16, k = 32 ks + 8 lg + (0..7)
+    bf16x8 qa[4];
+    const int t = t0 + l16;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qa[ks] = t < n_tok ? *(const bf16x8*)(q_nope + ((int64_t)t * n_heads + h) * kNope + 32 * ks + 8 * lg)
+                         : bf16x8{};
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int c0 = 32 * wave + 16 * cb;  // column block within the slice
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        // B operand: lane col c0 + l16, k = 32 ks + 8 lg + (0..7) via two transposed reads
+        const char* p0 = wl + (32 * ks + 8 * lg + rq) * kAbsLds + (c0 + 4 * qq) * 2;
+        const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p0));
+        const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p0 + 4 * kAbsLds));
+        const bf16x8 wb = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], wb, acc, 0, 0, 0);
+      }
+      // D layout: lane holds column c0 + l16, rows (tokens) 4 lg + e
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tt = t0 + 4 * lg + e;
+        if (tt < n_tok) store_f(q_lat + ((int64_t)tt * n_heads + h) * kLat + j0 + c0 + l16, acc[e]);
+      }
+    }
+  }
+}
+
+constexpr int kDv = 128;
+
+template <typename TO>
+__global__ __launch_bounds__(256) void out_uv_mfma_kernel(const bf16* __restrict__ o_lat,
+                                                          const bf16* __restrict__ w_uv, TO* __restrict__ out,
+                                                          int n_tok, int n_heads) {
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l16 = lane & 15, lg = lane >> 4;
+  // B operand straight from HBM: lane col v = 32 wave + 16 cb + l16, k = 32 ks + 8 lg + (0..7)
+  bf16x8 wb[2][16];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const bf16* wr = w_uv + ((int64_t)h * kDv + 32 * wave + 16 * cb + l16) * kLat + 8 * lg;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) wb[cb][ks] = *(const bf16x8*)(wr + 32 * ks);
+  }
+  for (int t0 = 0; t0 < n_tok; t0 += 16) {
+    const int t = t0 + l16;
+    const bf16* orow = o_lat + ((int64_t)t * n_heads + h) * kLat + 8 * lg;
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      const bf16x8 oa = t < n_tok ? *(const bf16x8*)(orow + 32 * ks) : bf16x8{};
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa, wb[cb][ks], acc[cb], 0, 0, 0);
+    }
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tt = t0 + 4 * lg + e;
+        if (tt < n_tok) store_f(out + ((int64_t)tt * n_heads + h) * kDv + 32 * wave + 16 * cb + l16, acc[cb][e]);
+      }
+  }
+}
+
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+bool absorb_mfma_ok(const void* q_nope, const void* w_uk, int d_nope, int d_c) {
+  return d_nope == kNope && d_c == kLat && al16(q_nope) && al16(w_uk);
+}
+
+hipError_t launch_absorb_mfma(const void* q_nope, const void* w_uk, void* q_lat, bool out_bf16, int n_tok,
+                              int n_heads, hipStream_t stream) {
+  dim3 grid(n_heads, kLat / kAbsCols);
+  if (out_bf16)
+    return launch(absorb_mfma_kernel<bf16>, grid, dim3(256), stream, (const bf16*)q_nope, (const bf16*)w_uk,
+                       (bf16*)q_lat, n_tok, n_heads);
+  else
+    return launch(absorb_mfma_kernel<float>, grid, dim3(256), stream, (const bf16*)q_nope,
+                       (const bf16*)w_uk, (float*)q_lat, n_tok, n_heads);
+}
+
+bool out_uv_mfma_ok(const void* o_lat, const void* w_uv, int d_c, int d_v) {
+  return d_c == kLat && d_v == kDv && al16(o_lat) && al16(w_uv);
+}
+
+hipError_t launch_out_uv_mfma(const void* o_lat, const void* w_uv, void* out, bool out_bf16, int n_tok,
+                              int n_heads, hipStream_t stream) {
+  dim3 grid(n_heads);
+  if (out_bf16)
+    return launch(out_uv_mfma_kernel<bf16>, grid, dim3(256), stream, (const bf16*)o_lat, (const bf16*)w_uv,
+                       (bf16*)out, n_tok, n_heads);
+  else
+    return launch(out_uv_mfma_kernel<float>, grid, dim3(256), stream, (const bf16*)o_lat,
+                       (const bf16*)w_uv, (float*)out, n_tok, n_heads);
+}
+
+}  // namespace mla

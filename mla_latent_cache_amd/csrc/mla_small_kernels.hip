@@ -42,9 +42,9 @@ __global__ __launch_bounds__(256) void rope_kernel(const TI* __restrict__ q_pe, 
 }
 
 template <typename TI, typename TO>
-static void rope_launch(const void* q_pe, void* q_rot, const int64_t* pos, const int64_t* shift, int n_tok,
+static hipError_t rope_launch(const void* q_pe, void* q_rot, const int64_t* pos, const int64_t* shift, int n_tok,
                         int n_heads, int d_rope, double base, int blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((rope_kernel<TI, TO>), dim3(blocks), dim3(256), 0, stream, (const TI*)q_pe, (TO*)q_rot,
+  return launch((rope_kernel<TI, TO>), dim3(blocks), dim3(256), stream, (const TI*)q_pe, (TO*)q_rot,
                      pos, shift, n_tok, n_heads, d_rope, base);
 }
 
@@ -55,11 +55,10 @@ hipError_t launch_rope(const void* q_pe, bool in_bf, void* q_rot, bool out_bf, c
   int blocks = (int)((total + 255) / 256);
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
-  if (in_bf && out_bf) rope_launch<bf16, bf16>(q_pe, q_rot, pos, shift, n_tok, n_heads, d_rope, base, blocks, stream);
-  else if (in_bf) rope_launch<bf16, float>(q_pe, q_rot, pos, shift, n_tok, n_heads, d_rope, base, blocks, stream);
-  else if (out_bf) rope_launch<float, bf16>(q_pe, q_rot, pos, shift, n_tok, n_heads, d_rope, base, blocks, stream);
-  else rope_launch<float, float>(q_pe, q_rot, pos, shift, n_tok, n_heads, d_rope, base, blocks, stream);
-  return hipGetLastError();
+  if (in_bf && out_bf) return rope_launch<bf16, bf16>(q_pe, q_rot, pos, shift, n_tok, n_heads, d_rope, base, blocks, stream);
+  if (in_bf) return rope_launch<bf16, float>(q_pe, q_rot, pos, shift, n_tok, n_heads, d_rope, base, blocks, stream);
+  if (out_bf) return rope_launch<float, bf16>(q_pe, q_rot, pos, shift, n_tok, n_heads, d_rope, base, blocks, stream);
+  return rope_launch<float, float>(q_pe, q_rot, pos, shift, n_tok, n_heads, d_rope, base, blocks, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -105,16 +104,17 @@ __global__ __launch_bounds__(256) void absorb_kernel(const T* __restrict__ q_nop
 
 hipError_t launch_absorb(const void* q_nope, const void* w_uk, bool in_bf, void* q_lat, bool out_bf, int n_tok,
                          int n_heads, int d_nope, int d_c, hipStream_t stream) {
+  if (in_bf && absorb_mfma_ok(q_nope, w_uk, d_nope, d_c))
+    return launch_absorb_mfma(q_nope, w_uk, q_lat, out_bf, n_tok, n_heads, stream);
   dim3 grid(n_heads, (d_c + 255) / 256);
 #define MLA_ABSORB(TI, TO)                                                                                \
-  hipLaunchKernelGGL((absorb_kernel<TI, TO>), grid, dim3(256), 0, stream, (const TI*)q_nope, (const TI*)w_uk, \
+  return launch((absorb_kernel<TI, TO>), grid, dim3(256), stream, (const TI*)q_nope, (const TI*)w_uk, \
                      (TO*)q_lat, n_tok, n_heads, d_nope, d_c)
   if (in_bf && out_bf) MLA_ABSORB(bf16, bf16);
-  else if (in_bf) MLA_ABSORB(bf16, float);
-  else if (out_bf) MLA_ABSORB(float, bf16);
-  else MLA_ABSORB(float, float);
+  if (in_bf) MLA_ABSORB(bf16, float);
+  if (out_bf) MLA_ABSORB(float, bf16);
+  MLA_ABSORB(float, float);
 #undef MLA_ABSORB
-  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -154,86 +154,112 @@ __global__ __launch_bounds__(256) void out_uv_kernel(const TL* __restrict__ o_la
 }
 
 template <typename TL, typename TW>
-static void out_uv_launch(const void* o_lat, const void* w_uv, void* out, bool out_bf, int n_tok, int n_heads,
+static hipError_t out_uv_launch(const void* o_lat, const void* w_uv, void* out, bool out_bf, int n_tok, int n_heads,
                           int d_c, int d_v, hipStream_t stream) {
   dim3 grid(n_heads, (d_v + 3) / 4);
   if (out_bf)
-    hipLaunchKernelGGL((out_uv_kernel<TL, TW, bf16>), grid, dim3(256), 0, stream, (const TL*)o_lat,
+    return launch((out_uv_kernel<TL, TW, bf16>), grid, dim3(256), stream, (const TL*)o_lat,
                        (const TW*)w_uv, (bf16*)out, n_tok, n_heads, d_c, d_v);
   else
-    hipLaunchKernelGGL((out_uv_kernel<TL, TW, float>), grid, dim3(256), 0, stream, (const TL*)o_lat,
+    return launch((out_uv_kernel<TL, TW, float>), grid, dim3(256), stream, (const TL*)o_lat,
                        (const TW*)w_uv, (float*)out, n_tok, n_heads, d_c, d_v);
 }
 
 hipError_t launch_out_uv(const void* o_lat, bool o_bf, const void* w_uv, bool w_bf, void* out, bool out_bf,
                          int n_tok, int n_heads, int d_c, int d_v, hipStream_t stream) {
-  if (o_bf && w_bf) out_uv_launch<bf16, bf16>(o_lat, w_uv, out, out_bf, n_tok, n_heads, d_c, d_v, stream);
-  else if (o_bf) out_uv_launch<bf16, float>(o_lat, w_uv, out, out_bf, n_tok, n_heads, d_c, d_v, stream);
-  else if (w_bf) out_uv_launch<float, bf16>(o_lat, w_uv, out, out_bf, n_tok, n_heads, d_c, d_v, stream);
-  else out_uv_launch<float, float>(o_lat, w_uv, out, out_bf, n_tok, n_heads, d_c, d_v, stream);
-  return hipGetLastError();
+  if (o_bf && w_bf && out_uv_mfma_ok(o_lat, w_uv, d_c, d_v))
+    return launch_out_uv_mfma(o_lat, w_uv, out, out_bf, n_tok, n_heads, stream);
+  if (o_bf && w_bf) return out_uv_launch<bf16, bf16>(o_lat, w_uv, out, out_bf, n_tok, n_heads, d_c, d_v, stream);
+  if (o_bf) return out_uv_launch<bf16, float>(o_lat, w_uv, out, out_bf, n_tok, n_heads, d_c, d_v, stream);
+  if (w_bf) return out_uv_launch<float, bf16>(o_lat, w_uv, out, out_bf, n_tok, n_heads, d_c, d_v, stream);
+  return out_uv_launch<float, float>(o_lat, w_uv, out, out_bf, n_tok, n_heads, d_c, d_v, stream);
 }
 
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of partial states (RedKnot-MLA abstract: the paths are
-// merged before one shared output projection).  One wave per row; slots whose
-// lse is -inf are skipped without reading their o_part row.
+// merged before one shared output projection).  One 128-thread block per row:
+// wave 0 compacts the live slots (lse > -inf) in slot order with their
+// weights exp(lse_j - max), so -inf slots are never read and the sum order is
+// fixed (bitwise repeatable); then every thread owns 4 columns and streams the
+// live o_part rows with 4 float4 loads in flight.
 // ---------------------------------------------------------------------------
+constexpr int kCombMaxPart = 1024;
+
 template <typename TO>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o_part,
+__global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ o_part,
                                                       const float* __restrict__ lse_part, int n_rows,
                                                       int n_part, int d_c, TO* __restrict__ o_lat,
                                                       float* __restrict__ lse) {
-  const int row = blockIdx.x * 4 + threadIdx.x / 64;
-  const int lane = threadIdx.x % 64;
-  if (row >= n_rows) return;
+  __shared__ int live_idx[kCombMaxPart];
+  __shared__ float live_w[kCombMaxPart];
+  __shared__ float s_inv, s_lse;
+  __shared__ int s_n;
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const float* lp = lse_part + (int64_t)row * n_part;
-  const float* op = o_part + (int64_t)row * n_part * d_c;
-  float m = -INFINITY;
-  for (int j = lane; j < n_part; j += 64) m = fmaxf(m, lp[j]);
-  m = wave_max(m);
-  TO* orow = o_lat + (int64_t)row * d_c;
-  if (m == -INFINITY) {
-    for (int d = lane; d < d_c; d += 64) store_f(orow + d, 0.f);
-    if (lse && lane == 0) lse[row] = -INFINITY;
-    return;
-  }
-  float tot = 0.f;
-  for (int j = lane; j < n_part; j += 64) tot += expf(lp[j] - m);
-  tot = wave_sum(tot);
-  const float inv = 1.f / tot;
-  float acc[kOutMaxK];
-#pragma unroll
-  for (int k = 0; k < kOutMaxK; ++k) acc[k] = 0.f;
-  for (int j = 0; j < n_part; ++j) {
-    const float l = lp[j];
-    if (l == -INFINITY) continue;
-    const float wgt = expf(l - m) * inv;
-    const float* o = op + (int64_t)j * d_c;
-#pragma unroll
-    for (int k = 0; k < kOutMaxK; ++k) {
-      const int d = lane + 64 * k;
-      if (d < d_c) acc[k] += wgt * o[d];
+  if (tid < 64) {
+    float m = -INFINITY;
+    for (int j = lane; j < n_part; j += 64) m = fmaxf(m, lp[j]);
+    m = wave_max(m);
+    float tot = 0.f;
+    int n = 0;
+    for (int base = 0; base < n_part; base += 64) {
+      const int j = base + lane;
+      const float l = j < n_part ? lp[j] : -INFINITY;
+      const bool live = l != -INFINITY;
+      const float w = live ? expf(l - m) : 0.f;
+      tot += w;
+      const uint64_t bal = __ballot(live);
+      if (live) {
+        const int pos = n + __popcll(bal & ((1ull << lane) - 1));
+        live_idx[pos] = j;
+        live_w[pos] = w;
+      }
+      n += __popcll(bal);
+    }
+    tot = wave_sum(tot);
+    if (lane == 0) {
+      s_n = n;
+      s_inv = n > 0 ? 1.f / tot : 0.f;
+      s_lse = n > 0 ? m + logf(tot) : -INFINITY;
     }
   }
+  __syncthreads();
+  const int n = s_n;
+  const float inv = s_inv;
+  if (lse && tid == 0) lse[row] = s_lse;
+  const float* op = o_part + (int64_t)row * n_part * d_c;
+  TO* orow = o_lat + (int64_t)row * d_c;
+  for (int c = 4 * tid; c < d_c; c += 512) {
+    const bool vec = c + 4 <= d_c;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    int i = 0;
+    if (vec) {
+      for (; i + 4 <= n; i += 4) {
+        f32x4 v[4];
 #pragma unroll
-  for (int k = 0; k < kOutMaxK; ++k) {
-    const int d = lane + 64 * k;
-    if (d < d_c) store_f(orow + d, acc[k]);
+        for (int u = 0; u < 4; ++u) v[u] = *(const f32x4*)(op + (int64_t)live_idx[i + u] * d_c + c);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc += live_w[i + u] * v[u];
+      }
+      for (; i < n; ++i) acc += live_w[i] * *(const f32x4*)(op + (int64_t)live_idx[i] * d_c + c);
+    } else {
+      for (; i < n; ++i)
+        for (int e = 0; e < 4 && c + e < d_c; ++e) acc[e] += live_w[i] * op[(int64_t)live_idx[i] * d_c + c + e];
+    }
+    for (int e = 0; e < 4 && c + e < d_c; ++e) store_f(orow + c + e, acc[e] * inv);
   }
-  if (lse && lane == 0) lse[row] = m + logf(tot);
 }
 
-hipError_t launch_combine(const float* o_part, const float* lse_part, int n_rows, int n_part,
-                          int d_c, void* o_lat, bool out_bf16, float* lse, hipStream_t stream) {
-  dim3 grid((n_rows + 3) / 4);
+hipError_t launch_combine(const float* o_part, const float* lse_part, int n_rows, int n_part, int d_c,
+                          void* o_lat, bool out_bf16, float* lse, hipStream_t stream) {
   if (out_bf16)
-    hipLaunchKernelGGL(combine_kernel<bf16>, grid, dim3(256), 0, stream, o_part, lse_part, n_rows,
+    return launch(combine_kernel<bf16>, dim3(n_rows), dim3(128), stream, o_part, lse_part, n_rows,
                        n_part, d_c, (bf16*)o_lat, lse);
   else
-    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, stream, o_part, lse_part, n_rows,
+    return launch(combine_kernel<float>, dim3(n_rows), dim3(128), stream, o_part, lse_part, n_rows,
                        n_part, d_c, (float*)o_lat, lse);
-  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -338,8 +364,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
 
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream) {
   dim3 grid(a.seg.n_split, a.batch * a.s_q * a.seg.head_count);
-  hipLaunchKernelGGL(decode_f32_kernel, grid, dim3(64), 0, stream, a);
-  return hipGetLastError();
+  return launch(decode_f32_kernel, grid, dim3(64), stream, a);
 }
 
 }  // namespace mla

@@ -209,3 +209,31 @@ def test_full_size_sampled(name):
     print(f"[parity] {name} full reqs={reqs} heads={heads}: {errs}", flush=True)
     # every output finite, every lse finite (no request is empty at full size)
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+
+
+# ------------------------------------------------------------ graph capture
+@pytest.mark.parametrize("name", ["dsv3", "merge"])
+def test_graph_replay_matches_eager(name):
+    """The five calls enqueue only kernels on the caller's stream, so a step
+    can be captured into a HIP graph; every replay must equal the eager run."""
+    from mla_latent_cache_amd.step import run_calls, step_from_inputs
+    x = M.make(name, 21, mini=True, poison=True)
+    st = step_from_inputs(x)
+    st.run()
+    torch.cuda.synchronize()
+    ref = (st.out.clone(), st.o_lat.clone(), st.lse.clone())
+    cap = torch.cuda.Stream()
+    pre, dec, post = st.bind(cap)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        run_calls(pre)
+        run_calls(dec)
+        run_calls(post)
+    for rep in range(3):
+        for t in (st.out, st.o_lat, st.lse):
+            t.fill_(float("nan"))         # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, (st.out, st.o_lat, st.lse)):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager step"
