@@ -71,8 +71,15 @@ struct Piece {
   int b, r0, r1, slot;
 };
 
-// DMA wave-instructions wave w issues for a full tile: k = w, w + 8, ... < kNDma.
-__device__ __forceinline__ int dma_per_wave(int w) { return (kNDma - w + kWaves - 1) / kWaves; }
+// Wait until at most the DMA wave-instructions of one full tile issued by this
+// wave are in flight (waves 0..4 issue 5 per tile, waves 5..7 issue 4).
+__device__ __forceinline__ void wait_all_but_one_tile(int wave) {
+  static_assert((kNDma + kWaves - 1) / kWaves == 5 && kNDma - 4 * kWaves == 5, "DMA split");
+  if (wave < kNDma - 4 * kWaves)
+    wait_vmcnt<5>();
+  else
+    wait_vmcnt<4>();
+}
 
 __device__ __forceinline__ int sload_i32(const int32_t* p) {
   // Scalar (SMEM) load: counted by lgkmcnt, so it never forces the in-flight
@@ -82,41 +89,48 @@ __device__ __forceinline__ int sload_i32(const int32_t* p) {
   return v;
 }
 
-// Issue the direct-to-LDS loads of one tile: rows [t0, t0 + nvalid) of one
-// request into an LDS stage (73 slots of 16 B per row; slot 72 is padding).
-// Wave `wave` issues wave-instructions k = wave, wave + 8, ... (64 slots
-// each).  Rows past nvalid are zero-filled so no stale value is ever read.
-// All arguments are plain values: no pointer to the kernel-argument block is
-// captured, so no load (and no vmcnt wait) precedes the DMA instructions.
-__device__ __forceinline__ void issue_tile_dma(char* st, const char* cache, const char* req_base,
-                                               const int32_t* bt_row, int n_pages, int t0, int nvalid,
-                                               int wave, int lane) {
-  int pg0 = 0, pg1 = 0;
-  if (bt_row) {
-    pg0 = sload_i32(bt_row + t0 / kPageSize);
-    pg1 = sload_i32(bt_row + (t0 + nvalid - 1) / kPageSize);
-  }
-  for (int k = wave; k < kNDma; k += kWaves) {
-    const int slotl = k * 64 + lane;
-    const int r = slotl / kSlotStride;
-    const int c = slotl - r * kSlotStride;
-    const bool in_tile = slotl < kTile * kSlotStride && c < kSlots;
-    bool ok = in_tile && r < nvalid;
-    const char* src = nullptr;
-    if (bt_row) {
-      const int t = t0 + r;
-      const int pg = (t / kPageSize == t0 / kPageSize) ? pg0 : pg1;
-      ok = ok && pg >= 0 && pg < n_pages;
-      src = cache + ((int64_t)pg * kPageSize + (t % kPageSize)) * kRowBytes + c * 16;
-    } else {
-      src = req_base + (int64_t)(t0 + r) * kRowBytes + c * 16;
-    }
-    if (ok) {
-      __builtin_amdgcn_global_load_lds((const void*)src, (MLA_LDS void*)(st + k * 1024), 16, 0, 0);
-    } else if (in_tile) {
-      *(int4*)(st + slotl * 16) = int4{0, 0, 0, 0};
+// Issue the loads of one tile: `nvalid` rows that are contiguous in memory
+// from `src` (tiles are aligned to 32 rows inside a request and never cross a
+// 64-row page).  Wave-instruction k = wave + 8 i covers LDS slots 64 k ..
+// 64 k + 63 (73 slots of 16 B per LDS row, slot 72 is padding); lane `lane`
+// moves the 16-byte chunk (row r, chunk c), byte offset r * 1152 + c * 16.
+// Rows past nvalid are zero-filled so no stale value is ever read.  `src` is
+// a plain value: nothing is loaded before the DMA instructions, so none of
+// them waits for the loads already in flight.
+__device__ __forceinline__ void issue_tile_dma(char* st, const char* src, int nvalid, int wave, int lane) {
+  const int lim = nvalid * kRowBytes;
+  // Opaque copy of the lane index: the offsets below are recomputed at every
+  // tile (a few integer ops) instead of being hoisted out of the tile loop and
+  // pinning five registers for the whole loop.
+  asm volatile("" : "+v"(lane));
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int k = wave + kWaves * i;
+    if (k < kNDma) {
+      const int slotl = k * 64 + lane;
+      const int r = slotl / kSlotStride;
+      const int c = slotl - r * kSlotStride;
+      const int off = r * kRowBytes + c * 16;
+      const bool in_tile = slotl < kTile * kSlotStride && c < kSlots;
+      if (in_tile && off < lim) {
+        __builtin_amdgcn_global_load_lds((const void*)(src + off), (MLA_LDS void*)(st + k * 1024), 16, 0, 0);
+      } else if (in_tile) {
+        *(int4*)(st + slotl * 16) = int4{0, 0, 0, 0};
+      }
     }
   }
+}
+
+// First byte of tile rows [t0, ...) of request b: contiguous cache, or the
+// page holding row t0 (scalar load of the block-table entry; an id outside
+// [0, n_pages) makes the tile read as zeros).
+__device__ __forceinline__ const char* tile_src(const char* cache, const char* req_base, const int32_t* bt_row,
+                                                int n_pages, int t0, bool* ok) {
+  *ok = true;
+  if (!bt_row) return req_base + (int64_t)t0 * kRowBytes;
+  const int pg = sload_i32(bt_row + t0 / kPageSize);
+  *ok = pg >= 0 && pg < n_pages;
+  return cache + ((int64_t)(*ok ? pg : 0) * kPageSize + (t0 % kPageSize)) * kRowBytes;
 }
 
 template <int MT>
@@ -186,10 +200,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
   const int64_t cap = block_table ? (int64_t)max_pages * kPageSize : max_rows;
   auto clampT = [cap](int t) -> int { return (int)max((int64_t)0, min((int64_t)t, cap)); };
 
-  // ---- plan pass 1: total and longest request ----
+  // ---- plan pass 1: total and longest request, each padded to whole tiles ----
+  // (a share then starts on a tile boundary of every request it touches, and
+  // no tile crosses a 64-row page)
+  auto padT = [](int t) -> int { return (t + kTile - 1) / kTile * kTile; };
   int tsum = 0, tmax = 0;
   for (int b = tid; b < B; b += kThreads) {
-    const int T = clampT(seq_lens[b]);
+    const int T = padT(clampT(seq_lens[b]));
     tsum += T;
     tmax = max(tmax, T);
   }
@@ -230,12 +247,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
   const int64_t q_off = (int64_t)s_row * n_heads + head_begin + Rc % hc;  // without the request part
   const int s_min = row0 / hc;      // smallest token index among the group's rows
 
-  int base = 0;  // prefix of T over requests scanned so far (wave 0)
+  int base = 0;  // prefix of padded T over requests scanned so far (wave 0)
   for (int chunk = 0;; ++chunk) {
     // ---- plan pass 2: wave 0 scans 64 requests, lists pieces, writes -inf tails ----
     if (wave == 0) {
       const int b = chunk * 64 + lane;
-      const int T = b < B ? clampT(seq_lens[b]) : 0;
+      const int Tr = b < B ? clampT(seq_lens[b]) : 0;  // rows
+      const int T = padT(Tr);                           // rows padded to whole tiles
       int incl = T;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -247,12 +265,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
       int r0 = 0, r1 = 0, slot = 0, cnt = 0;
       if (req_mode) {
         is_piece = b < B && T > 0 && (b % n_share) == j;
-        r1 = T;
+        r1 = Tr;
         tail = b < B && T == 0 && (b % n_share) == j;
       } else {
         is_piece = b < B && T > 0 && S < hi && S + T > lo;
         r0 = max(lo, S) - S;
-        r1 = min(hi, S + T) - S;
+        r1 = min(min(hi, S + T) - S, Tr);  // a piece starting below Tr, clipped to the real rows
         slot = j - S / share;
         const int jf = min(S / share, n_share - 1);
         cnt = T > 0 ? (S + T - 1) / share - S / share + 1 : 0;
@@ -334,10 +352,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
       const char* const req_base = cache + (int64_t)b * max_rows * kRowBytes;  // contiguous layout
       const int32_t* const bt_row = block_table ? block_table + (int64_t)b * max_pages : nullptr;
       const int n_tiles = (pr1 - pr0 + kTile - 1) / kTile;
-      issue_tile_dma(sm.stage[0], cache, req_base, bt_row, n_pages, pr0, min(kTile, pr1 - pr0), wave, lane);
-      if (n_tiles > 1)
-        issue_tile_dma(sm.stage[1], cache, req_base, bt_row, n_pages, pr0 + kTile, min(kTile, pr1 - pr0 - kTile),
-                       wave, lane);
+      auto load_tile = [&](int it) {
+        const int t0 = pr0 + it * kTile;
+        bool ok;
+        const char* src = tile_src(cache, req_base, bt_row, n_pages, t0, &ok);
+        issue_tile_dma(sm.stage[it % kNStage], src, ok ? min(kTile, pr1 - t0) : 0, wave, lane);
+      };
+      load_tile(0);
+      if (n_tiles > 1) load_tile(1);
 
       float m_used = -INFINITY;  // running max (log2 units) of this lane's query row
       float l_part = 0.f;        // sum of p over this wave's token half, this lane's 4 tokens
@@ -352,16 +374,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
         const int t0 = pr0 + it * kTile;
         const bool next_full = it + 1 < n_tiles && pr1 - (t0 + kTile) >= kTile;
         if (next_full)
-          wait_vmcnt_dyn(dma_per_wave(wave));
+          wait_all_but_one_tile(wave);
         else
           wait_vmcnt<0>();
         wait_lgkm0();
         barrier_raw();
-        if (it + 2 < n_tiles) {
-          const int t2 = t0 + 2 * kTile;
-          issue_tile_dma(sm.stage[(it + 2) % kNStage], cache, req_base, bt_row, n_pages, t2,
-                         min(kTile, pr1 - t2), wave, lane);
-        }
+        if (it + 2 < n_tiles) load_tile(it + 2);
         const char* st = sm.stage[it % kNStage];
         const int buf = it & 1;
         const bool full = t0 + kTile <= pr1 && t0 + kTile - 1 <= vis_min;
@@ -397,24 +415,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
 
         // ---------------- softmax (QK waves): full scores, this wave's token half ----------------
         if (qk_wave) {
-          float s2[2][4];
-          float mt = -INFINITY;
-#pragma unroll
-          for (int tb = 0; tb < 2; ++tb) {
-            const f32x4 other = sm.sx[rb][1 - kh][tb][lane];
-            // both waves of the pair add the same two values: identical scores
-            const f32x4 full_s = sp[tb] + other;
+          // both waves of the pair add the same two values: identical scores
+          f32x4 sa = (sp[0] + sm.sx[rb][1 - kh][0][lane]) * sl2;
+          f32x4 sb = (sp[1] + sm.sx[rb][1 - kh][1][lane]) * sl2;
+          if (!full) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              float v = full_s[e] * sl2;
-              if (!full) {
-                const int t = t0 + 16 * tb + 4 * lg + e;
-                v = (t < pr1 && t <= vis_last) ? v : -INFINITY;
-              }
-              s2[tb][e] = v;
-              mt = fmaxf(mt, v);
+              const int t = t0 + 4 * lg + e;
+              sa[e] = (t < pr1 && t <= vis_last) ? sa[e] : -INFINITY;
+              sb[e] = (t + 16 < pr1 && t + 16 <= vis_last) ? sb[e] : -INFINITY;
             }
           }
+          float mt = fmaxf(fmaxf(fmaxf(sa[0], sa[1]), fmaxf(sa[2], sa[3])),
+                           fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3])));
           mt = fmaxf(mt, __shfl_xor(mt, 16));
           mt = fmaxf(mt, __shfl_xor(mt, 32));
           const bool need = mt > m_used + kTau;
@@ -428,9 +441,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
           const float msub = m_used == -INFINITY ? 0.f : m_used;
           bf16x4 pk;
           float lsum = 0.f;
+          const f32x4 mine = kh ? sb : sa;  // this wave's token half
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float p = __builtin_amdgcn_exp2f((kh ? s2[1][e] : s2[0][e]) - msub);  // exp2(-inf) = 0
+            const float p = __builtin_amdgcn_exp2f(mine[e] - msub);  // exp2(-inf) = 0
             lsum += p;
             pk[e] = (bf16)p;
           }
