@@ -120,6 +120,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--detail", action="store_true", help="also time each call separately")
     ap.add_argument("--eager", action="store_true", help="host launches instead of a HIP graph")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="before the timed region, run one plain device copy of this many bytes (fp32 "
+                         "elementwise, read N and write N) whose HBM counters calibrate the decode kernel's")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -166,6 +169,13 @@ def main():
     # kernels; HIP does not allow timing events inside a captured graph).
     # Eager mode (--eager, or if capture fails): host launches, with events
     # around every decode launch inside the timed region.
+    if args.copy_bytes > 0:
+        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     launch = "eager" if args.eager else "graph"
     dec_us = None
     if launch == "graph":

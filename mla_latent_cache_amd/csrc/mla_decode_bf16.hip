@@ -56,7 +56,7 @@ constexpr int kSlots = kRowBytes / 16;      // 72 16-byte chunks per row
 constexpr int kSlotStride = kSlots + 1;     // 73: one pad slot per LDS row
 constexpr int kLRow = kSlotStride * 16;     // 1168 bytes per LDS row
 constexpr int kStageBytes = kTile * kLRow;
-constexpr int kNStage = 3;
+constexpr int kNStage = 4;
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kNDma = (kTile * kSlotStride + 63) / 64;  // 37 wave-instructions per tile
@@ -65,21 +65,10 @@ constexpr float kTau = 8.f;
 constexpr int kPageSize = 64;
 constexpr int kMaxPieces = 64;
 constexpr int kKSteps = (kDc + kDr) / 32;   // 18 MFMA k-steps over [c | kr]
-constexpr int kKHalf = kKSteps / 2;         // 9 per wave of a pair
 
 struct Piece {
   int b, r0, r1, slot;
 };
-
-// Wait until at most the DMA wave-instructions of one full tile issued by this
-// wave are in flight (waves 0..4 issue 5 per tile, waves 5..7 issue 4).
-__device__ __forceinline__ void wait_all_but_one_tile(int wave) {
-  static_assert((kNDma + kWaves - 1) / kWaves == 5 && kNDma - 4 * kWaves == 5, "DMA split");
-  if (wave < kNDma - 4 * kWaves)
-    wait_vmcnt<5>();
-  else
-    wait_vmcnt<4>();
-}
 
 __device__ __forceinline__ int sload_i32(const int32_t* p) {
   // Scalar (SMEM) load: counted by lgkmcnt, so it never forces the in-flight
@@ -137,9 +126,7 @@ template <int MT>
 struct Smem {
   char stage[kNStage][kStageBytes];
   char p[2][MT * kPStr];
-  f32x4 sx[MT / 16][2][2][64];  // partial scores: [row block][writer k-half][token block][lane]
   float alpha[2][MT];
-  float lpart[2][MT];
   float rowinv[MT];
   int flag[2][4];
   Piece pieces[kMaxPieces];
@@ -148,14 +135,27 @@ struct Smem {
   int red_i[2 * kWaves];
 };
 
+// Wait until at most `after` tiles issued after the needed one are still in
+// flight; `after_full` says they are all full tiles (a partial tile may issue
+// fewer instructions, then everything is waited for).
+__device__ __forceinline__ void wait_tiles(int wave, int after, bool after_full) {
+  if (!after_full || after == 0) {
+    wait_vmcnt<0>();
+  } else if (wave < kNDma - 4 * kWaves) {  // waves issuing 5 instructions per tile
+    if (after == 1) wait_vmcnt<5>(); else wait_vmcnt<10>();
+  } else {                                  // waves issuing 4
+    if (after == 1) wait_vmcnt<4>(); else wait_vmcnt<8>();
+  }
+}
+
 }  // namespace
 
+// QF32: q_lat / q_rot are fp32 and split into bf16 hi + lo parts.
 template <int MT, bool QF32>
 __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, int n_share, int n_rg,
                                                                   int rows_total) {
   constexpr int NQH = QF32 ? 2 : 1;  // query parts (hi, lo)
-  constexpr int NRB = MT / 16;       // 16-row blocks
-  constexpr int NQW = 2 * NRB;       // waves running QK + softmax: (row block, k-half)
+  constexpr int NRB = MT / 16;       // 16-row blocks = score waves
   __shared__ __attribute__((aligned(16))) Smem<MT> sm;
 
   // every argument field as a local value (see issue_tile_dma)
@@ -236,16 +236,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
   }
   const int lo = j * share, hi = lo + share;
 
-  // ---- the query row of this lane in the QK waves ----
-  const bool qk_wave = wave < NQW;
-  const int rb = wave % NRB;        // row block (QK waves)
-  const int kh = wave / NRB;        // k-half (QK waves)
-  const int qrow = rb * 16 + l16;   // local row
+  // ---- roles: waves 0..NRB-1 score 16 query rows each; waves 4..7 own 128 latent columns each ----
+  const bool qk_wave = wave < NRB;
+  const bool pv_wave = wave >= 4;
+  const int qrow = wave * 16 + l16;  // local row of this lane (score waves)
   const bool rvalid = qk_wave && qrow < nrows;
   const int Rc = rvalid ? row0 + qrow : row0;
   const int s_row = Rc / hc;
   const int64_t q_off = (int64_t)s_row * n_heads + head_begin + Rc % hc;  // without the request part
-  const int s_min = row0 / hc;      // smallest token index among the group's rows
+  const int s_min = row0 / hc;       // smallest token index among the group's rows
+  const int pw = wave - 4;           // column slice of a PV wave
 
   int base = 0;  // prefix of padded T over requests scanned so far (wave 0)
   for (int chunk = 0;; ++chunk) {
@@ -318,107 +318,85 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
       const int T = clampT(seq_lens[b]);
       const int vis_last = causal ? T - s_q + s_row : T - 1;  // last visible row of this lane's query
       const int vis_min = causal ? T - s_q + s_min : T - 1;   // ... of the group's first query row
-
-      // ---- this wave's half of its query rows: [q_lat | q_rot], k-steps kh*9 .. kh*9+8 ----
-      bf16x8 qreg[NQH][kKHalf];
-      if (qk_wave) {
-        const int64_t qi = (int64_t)b * s_q * n_heads + q_off;
-#pragma unroll
-        for (int kk = 0; kk < kKHalf; ++kk) {
-          const int k0 = 32 * (kh * kKHalf + kk) + 8 * lg;
-          if constexpr (QF32) {
-            f32x4 v0 = f32x4{0.f, 0.f, 0.f, 0.f}, v1 = v0;
-            if (rvalid) {
-              const float* src = k0 < kDc ? (const float*)q_lat_p + qi * kDc + k0
-                                          : (const float*)q_rot_p + qi * kDr + (k0 - kDc);
-              v0 = *(const f32x4*)src;
-              v1 = *(const f32x4*)(src + 4);
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float v = e < 4 ? v0[e] : v1[e - 4];
-              const bf16 h = (bf16)v;
-              qreg[0][kk][e] = h;
-              qreg[1][kk][e] = (bf16)(v - (float)h);
-            }
-          } else {
-            qreg[0][kk] = rvalid ? (k0 < kDc ? *(const bf16x8*)((const bf16*)q_lat_p + qi * kDc + k0)
-                                             : *(const bf16x8*)((const bf16*)q_rot_p + qi * kDr + (k0 - kDc)))
-                                 : bf16x8{};
-          }
-        }
-      }
+      const int n_tiles = (pr1 - pr0 + kTile - 1) / kTile;
+      const bool last_full = (pr1 - pr0) % kTile == 0;       // only the last tile can be partial
 
       const char* const req_base = cache + (int64_t)b * max_rows * kRowBytes;  // contiguous layout
       const int32_t* const bt_row = block_table ? block_table + (int64_t)b * max_pages : nullptr;
-      const int n_tiles = (pr1 - pr0 + kTile - 1) / kTile;
       auto load_tile = [&](int it) {
         const int t0 = pr0 + it * kTile;
         bool ok;
         const char* src = tile_src(cache, req_base, bt_row, n_pages, t0, &ok);
         issue_tile_dma(sm.stage[it % kNStage], src, ok ? min(kTile, pr1 - t0) : 0, wave, lane);
       };
-      load_tile(0);
-      if (n_tiles > 1) load_tile(1);
 
-      float m_used = -INFINITY;  // running max (log2 units) of this lane's query row
-      float l_part = 0.f;        // sum of p over this wave's token half, this lane's 4 tokens
-      f32x4 acc_o[4][NRB];
+      // The two roles run separate copies of the tile loop with the same
+      // barrier sequence (1 + n_tiles + 1 barriers), so the register
+      // allocator never holds the query block and the O accumulator at once.
+      if (qk_wave) {
+        // ---- score wave: 16 query rows, all 18 k-steps (hi and lo parts) ----
+        bf16x8 qreg[NQH][kKSteps];
+        {
+          const int64_t qi = (int64_t)b * s_q * n_heads + q_off;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+          for (int ks = 0; ks < kKSteps; ++ks) {
+            const int k0 = 32 * ks + 8 * lg;
+            if constexpr (QF32) {
+              f32x4 v0 = f32x4{0.f, 0.f, 0.f, 0.f}, v1 = v0;
+              if (rvalid) {
+                const float* src = k0 < kDc ? (const float*)q_lat_p + qi * kDc + k0
+                                            : (const float*)q_rot_p + qi * kDr + (k0 - kDc);
+                v0 = *(const f32x4*)src;
+                v1 = *(const f32x4*)(src + 4);
+              }
 #pragma unroll
-        for (int q = 0; q < NRB; ++q) acc_o[db][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+              for (int e = 0; e < 8; ++e) {
+                const float v = e < 4 ? v0[e] : v1[e - 4];
+                const bf16 h = (bf16)v;
+                qreg[0][ks][e] = h;
+                qreg[1][ks][e] = (bf16)(v - (float)h);
+              }
+            } else {
+              qreg[0][ks] = rvalid ? (k0 < kDc ? *(const bf16x8*)((const bf16*)q_lat_p + qi * kDc + k0)
+                                               : *(const bf16x8*)((const bf16*)q_rot_p + qi * kDr + (k0 - kDc)))
+                                   : bf16x8{};
+            }
+          }
+        }
+        load_tile(0);
+        if (n_tiles > 1) load_tile(1);
+        if (n_tiles > 2) load_tile(2);
+        float m_used = -INFINITY;  // running max (log2 units) of this lane's query row
+        float l_part = 0.f;        // this lane's share of the row's sum of p
 
-      for (int it = 0; it < n_tiles; ++it) {
-        // tile `it` landed: at most the (full) next tile's loads may still be in flight
-        const int t0 = pr0 + it * kTile;
-        const bool next_full = it + 1 < n_tiles && pr1 - (t0 + kTile) >= kTile;
-        if (next_full)
-          wait_all_but_one_tile(wave);
-        else
-          wait_vmcnt<0>();
-        wait_lgkm0();
-        barrier_raw();
-        if (it + 2 < n_tiles) load_tile(it + 2);
-        const char* st = sm.stage[it % kNStage];
-        const int buf = it & 1;
-        const bool full = t0 + kTile <= pr1 && t0 + kTile - 1 <= vis_min;
-
-        // ---------------- QK: partial scores over this wave's k-half ----------------
-        f32x4 sp[2];
-        if (qk_wave) {
+        // scores, softmax and P of tile `it`, into P / alpha / flag buffer it & 1
+        auto score_tile = [&](int it) {
+          const char* st = sm.stage[it % kNStage];
+          const int t0 = pr0 + it * kTile;
+          const int buf = it & 1;
           f32x4 sacc[2][NQH];
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
             for (int hl = 0; hl < NQH; ++hl) sacc[tb][hl] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int kk = 0; kk < kKHalf; ++kk) {
-            const int ks = kh * kKHalf + kk;
+          for (int ks = 0; ks < kKSteps; ++ks) {
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb) {
               const bf16x8 ak = *(const bf16x8*)(st + (16 * tb + l16) * kLRow + (4 * ks + lg) * 16);
 #pragma unroll
               for (int hl = 0; hl < NQH; ++hl)
-                sacc[tb][hl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, qreg[hl][kk], sacc[tb][hl], 0, 0, 0);
+                sacc[tb][hl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, qreg[hl][ks], sacc[tb][hl], 0, 0, 0);
             }
           }
-#pragma unroll
-          for (int tb = 0; tb < 2; ++tb) {
-            sp[tb] = sacc[tb][0];
-            if constexpr (QF32) sp[tb] += sacc[tb][1];
-            sm.sx[rb][kh][tb][lane] = sp[tb];
+          f32x4 sa = sacc[0][0], sb = sacc[1][0];
+          if constexpr (QF32) {
+            sa += sacc[0][1];
+            sb += sacc[1][1];
           }
-        }
-        wait_lgkm0();
-        barrier_raw();
-
-        // ---------------- softmax (QK waves): full scores, this wave's token half ----------------
-        if (qk_wave) {
-          // both waves of the pair add the same two values: identical scores
-          f32x4 sa = (sp[0] + sm.sx[rb][1 - kh][0][lane]) * sl2;
-          f32x4 sb = (sp[1] + sm.sx[rb][1 - kh][1][lane]) * sl2;
-          if (!full) {
+          sa *= sl2;
+          sb *= sl2;
+          if (!(t0 + kTile <= pr1 && t0 + kTile - 1 <= vis_min)) {  // partial or causal-edge tile
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int t = t0 + 4 * lg + e;
@@ -439,27 +417,68 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
           }
           const bool any = __ballot(need) != 0;
           const float msub = m_used == -INFINITY ? 0.f : m_used;
-          bf16x4 pk;
+          bf16x4 pa, pb;
           float lsum = 0.f;
-          const f32x4 mine = kh ? sb : sa;  // this wave's token half
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float p = __builtin_amdgcn_exp2f(mine[e] - msub);  // exp2(-inf) = 0
-            lsum += p;
-            pk[e] = (bf16)p;
+            const float p0 = __builtin_amdgcn_exp2f(sa[e] - msub);  // exp2(-inf) = 0
+            const float p1 = __builtin_amdgcn_exp2f(sb[e] - msub);
+            lsum += p0 + p1;
+            pa[e] = (bf16)p0;
+            pb[e] = (bf16)p1;
           }
           l_part += lsum;
-          *(bf16x4*)(sm.p[buf] + qrow * kPStr + (16 * kh + 4 * lg) * 2) = pk;
-          if (kh == 0) {
-            if (lg == 0) sm.alpha[buf][qrow] = alpha;
-            if (lane == 0) sm.flag[buf][rb] = any ? 1 : 0;
+          char* prow = sm.p[buf] + qrow * kPStr + 4 * lg * 2;
+          *(bf16x4*)(prow) = pa;
+          *(bf16x4*)(prow + 32) = pb;
+          if (lg == 0) sm.alpha[buf][qrow] = alpha;
+          if (lane == 0) sm.flag[buf][wave] = any ? 1 : 0;
+        };
+
+        // tile 0 must be in LDS; tiles 1, 2 may still be in flight
+        wait_tiles(wave, min(n_tiles - 1, 2), min(n_tiles - 1, 2) < n_tiles - 1 || last_full);
+        wait_lgkm0();
+        barrier_raw();
+        score_tile(0);
+        for (int it = 0; it < n_tiles; ++it) {
+          // before barrier `it`: P(it) is written; tile it+1 is in LDS (at most tile it+2 in flight)
+          if (it + 1 < n_tiles) {
+            const int issued = min(it + 2, n_tiles - 1);
+            wait_tiles(wave, issued - (it + 1), issued < n_tiles - 1 || last_full);
+          }
+          wait_lgkm0();
+          barrier_raw();
+          if (it + 3 < n_tiles) load_tile(it + 3);  // into the stage of tile it-1, free after its PV
+          if (it + 1 < n_tiles) score_tile(it + 1);
+        }
+        // epilogue: lse and 1/l of this wave's rows
+        float lt = l_part;
+        lt += __shfl_xor(lt, 16);
+        lt += __shfl_xor(lt, 32);
+        if (lg == 0) {
+          sm.rowinv[qrow] = lt > 0.f ? 1.f / lt : 0.f;
+          if (rvalid) {
+            const int64_t ri = (int64_t)b * s_q * n_heads + q_off;
+            lse_part[ri * n_part + part_begin + slot] = lt > 0.f ? (m_used + __log2f(lt)) * kLn2 : -INFINITY;
           }
         }
         wait_lgkm0();
         barrier_raw();
+      } else {
+        // ---- PV wave (waves 4..7): 128 latent columns of all rows; other waves only load ----
+        load_tile(0);
+        if (n_tiles > 1) load_tile(1);
+        if (n_tiles > 2) load_tile(2);
+        f32x4 acc_o[8][NRB];
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+#pragma unroll
+          for (int q = 0; q < NRB; ++q) acc_o[db][q] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        // ---------------- PV: O^T[d x rows] += C^T . P^T, 64 columns per wave ----------------
-        {
+        // O^T[d x rows] += C^T . P^T of tile `it` for this wave's 128 columns
+        auto pv_tile = [&](int it) {
+          const char* st = sm.stage[it % kNStage];
+          const int buf = it & 1;
           int flag = 0;
 #pragma unroll
           for (int r = 0; r < NRB; ++r) flag |= sm.flag[buf][r];
@@ -471,13 +490,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
             for (int q = 0; q < NRB; ++q) {
               const float al = sm.alpha[buf][16 * q + l16];
 #pragma unroll
-              for (int db = 0; db < 4; ++db) acc_o[db][q] *= al;
+              for (int db = 0; db < 8; ++db) acc_o[db][q] *= al;
             }
           }
           const int rq = l16 >> 2, qq = lane & 3;
 #pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            const int d0 = 64 * wave + 16 * db;
+          for (int db = 0; db < 8; ++db) {
+            const int d0 = 128 * pw + 16 * db;
             const char* p0 = st + (8 * lg + rq) * kLRow + (d0 + 4 * qq) * 2;
             const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p0));
             const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p0 + 4 * kLRow));
@@ -486,42 +505,38 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
             for (int q = 0; q < NRB; ++q)
               acc_o[db][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ac, bq[q], acc_o[db][q], 0, 0, 0);
           }
-        }
-      }
+        };
 
-      // ---- piece epilogue: row sums of both halves, lse, normalised partial ----
-      if (qk_wave) {
-        float lt = l_part;
-        lt += __shfl_xor(lt, 16);
-        lt += __shfl_xor(lt, 32);
-        if (lg == 0) sm.lpart[kh][qrow] = lt;
-      }
-      wait_lgkm0();
-      barrier_raw();
-      if (qk_wave && kh == 0) {
-        const float lt = sm.lpart[0][qrow] + sm.lpart[1][qrow];
-        if (lg == 0) {
-          sm.rowinv[qrow] = lt > 0.f ? 1.f / lt : 0.f;
-          if (rvalid) {
-            const int64_t ri = (int64_t)b * s_q * n_heads + q_off;
-            lse_part[ri * n_part + part_begin + slot] = lt > 0.f ? (m_used + __log2f(lt)) * kLn2 : -INFINITY;
+        wait_tiles(wave, min(n_tiles - 1, 2), min(n_tiles - 1, 2) < n_tiles - 1 || last_full);
+        wait_lgkm0();
+        barrier_raw();
+        for (int it = 0; it < n_tiles; ++it) {
+          if (it + 1 < n_tiles) {
+            const int issued = min(it + 2, n_tiles - 1);
+            wait_tiles(wave, issued - (it + 1), issued < n_tiles - 1 || last_full);
           }
+          wait_lgkm0();
+          barrier_raw();
+          if (it + 3 < n_tiles) load_tile(it + 3);
+          if (pv_wave) pv_tile(it);
         }
-      }
-      wait_lgkm0();
-      barrier_raw();
+        wait_lgkm0();
+        barrier_raw();
+        if (pv_wave) {
 #pragma unroll
-      for (int q = 0; q < NRB; ++q) {
-        const int qr = 16 * q + l16;
-        const float inv = sm.rowinv[qr];
-        if (qr < nrows && inv > 0.f) {
-          const int R = row0 + qr;
-          const int tok = b * s_q + R / hc;
-          const int h = head_begin + R % hc;
-          float* o = o_part + (((int64_t)tok * n_heads + h) * n_part + part_begin + slot) * kDc + 64 * wave +
-                     4 * lg;
+          for (int q = 0; q < NRB; ++q) {
+            const int qr = 16 * q + l16;
+            const float inv = sm.rowinv[qr];
+            if (qr < nrows && inv > 0.f) {
+              const int R = row0 + qr;
+              const int tok = b * s_q + R / hc;
+              const int h = head_begin + R % hc;
+              float* o = o_part + (((int64_t)tok * n_heads + h) * n_part + part_begin + slot) * kDc + 128 * pw +
+                         4 * lg;
 #pragma unroll
-          for (int db = 0; db < 4; ++db) *(f32x4*)(o + 16 * db) = acc_o[db][q] * inv;
+              for (int db = 0; db < 8; ++db) *(f32x4*)(o + 16 * db) = acc_o[db][q] * inv;
+            }
+          }
         }
       }
       barrier_raw();  // stage buffers, P and rowinv are reused by the next piece
