@@ -12,26 +12,29 @@
 //  * One workgroup of 8 waves (2 per SIMD) owns up to MT = 64 query rows (all
 //    heads of a request for the segment, or a 64-row group of them) and
 //    streams 32-row tiles of cache rows [c_t | kr_t] (576 bf16 = 1152 B)
-//    HBM -> LDS with direct-to-LDS loads, 3 stages deep.  Every tile is read
-//    from HBM once and shared by all MT query rows: the latent serves every
-//    head's key and value.
-//  * LDS rows are padded to 73 slots of 16 B so the 16 rows an MFMA operand
-//    read touches fall on distinct bank groups.
-//  * QK: S^T[tokens x rows] = K_tile . [q_lat|q_rot]^T on
-//    v_mfma_f32_16x16x32_bf16.  The 576-long contraction is split in two
-//    halves over a pair of waves, so each wave keeps only 16 query rows x 288
-//    k in registers; the pair swaps partial scores through LDS and both then
-//    hold the full, bitwise-identical score block of their rows.
+//    HBM -> LDS with direct-to-LDS loads into a 4-stage ring (3 tiles in
+//    flight).  Every tile is read from HBM once and shared by all MT query
+//    rows: the latent serves every head's key and value.
+//  * LDS rows are padded to 74 slots of 16 B (1184 B): the 16-row operand
+//    reads of the score MFMAs then run without bank conflicts.
+//  * Wave roles, one tile apart: score waves 0..MT/16-1 each hold the query
+//    of 16 rows in registers and compute S^T[tokens x rows] = K_tile .
+//    [q_lat|q_rot]^T of tile it+1 on v_mfma_f32_16x16x32_bf16, the online
+//    softmax and P (bf16, in LDS); PV waves 4..7 each own 128 latent columns
+//    and accumulate O^T[d x rows] += C_tile^T . P^T of tile it, with C^T from
+//    ds_read_b64_tr_b16 transposed LDS reads.  The PV waves also issue all
+//    tile loads (spread between their MFMAs): an LDS-direct load holds its
+//    wave for tens of cycles at issue, and the score waves set the pace.
+//    Waves in between (MT < 64) only keep the barrier count.
 //  * The query arrives in fp32 and is split into bf16 hi + lo parts (q = hi +
 //    lo to ~2^-17): two MFMAs per k-step into separate accumulators.  A
 //    bf16-rounded query would put ~1e-3 error into the scores.
 //  * Softmax in the exp2 domain (raw v_exp_f32) with lazy rescaling: the
 //    running max only moves when a tile max exceeds it by more than TAU = 8
 //    (log2 units), so the O rescale almost never runs; p <= 2^8 stays exact in
-//    fp32 and representable in bf16.  Full tiles skip all masking.
-//  * PV: O^T[d x rows] += C_tile^T . P^T; the 512 latent columns are split
-//    over the 8 waves (64 each); C^T comes from ds_read_b64_tr_b16 transposed
-//    LDS reads, P^T from LDS.
+//    fp32 and representable in bf16.  Full tiles skip all masking.  Row
+//    reductions over the four 16-lane rows use the gfx950 row-swap
+//    instructions (VALU only).
 //  * Work split: all rows of the segment (concatenated over requests) are cut
 //    into equal shares, one per workgroup, whatever the length mix; a share
 //    crossing a request boundary yields several pieces.  At most n_split
@@ -53,13 +56,14 @@ constexpr int kDr = 64;
 constexpr int kRowBytes = (kDc + kDr) * 2;  // 1152
 constexpr int kTile = 32;                   // cache rows per tile
 constexpr int kSlots = kRowBytes / 16;      // 72 16-byte chunks per row
-constexpr int kSlotStride = kSlots + 1;     // 73: one pad slot per LDS row
-constexpr int kLRow = kSlotStride * 16;     // 1168 bytes per LDS row
+constexpr int kSlotStride = kSlots + 2;     // 74: two pad slots per LDS row
+constexpr int kLRow = kSlotStride * 16;     // 1184 bytes per LDS row
 constexpr int kStageBytes = kTile * kLRow;
 constexpr int kNStage = 4;
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-constexpr int kNDma = (kTile * kSlotStride + 63) / 64;  // 37 wave-instructions per tile
+constexpr int kNDma = kTile * kSlotStride / 64;  // 37 wave-instructions per tile
+static_assert(kTile * kSlotStride == kNDma * 64, "a tile fills whole DMA instructions");
 constexpr int kPStr = 80;                   // bytes per P row (32 bf16 + pad)
 constexpr float kTau = 8.f;
 constexpr int kPageSize = 64;
@@ -78,35 +82,65 @@ __device__ __forceinline__ int sload_i32(const int32_t* p) {
   return v;
 }
 
-// Issue the loads of one tile: `nvalid` rows that are contiguous in memory
+// Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32,
+// l^48) with the gfx950 row-swap instructions: VALU only, no LDS round trip.
+// permlane16_swap(x, x) leaves rows (0,0,2,2) / (1,1,3,3) in its two results,
+// permlane32_swap(x, x) rows (0,1,0,1) / (2,3,2,3).
+__device__ __forceinline__ float rows_max(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Loads of one tile: `lim` bytes (whole rows) that are contiguous in memory
 // from `src` (tiles are aligned to 32 rows inside a request and never cross a
-// 64-row page).  Wave-instruction k = wave + 8 i covers LDS slots 64 k ..
-// 64 k + 63 (73 slots of 16 B per LDS row, slot 72 is padding); lane `lane`
-// moves the 16-byte chunk (row r, chunk c), byte offset r * 1152 + c * 16.
-// Rows past nvalid are zero-filled so no stale value is ever read.  `src` is
-// a plain value: nothing is loaded before the DMA instructions, so none of
-// them waits for the loads already in flight.
-__device__ __forceinline__ void issue_tile_dma(char* st, const char* src, int nvalid, int wave, int lane) {
-  const int lim = nvalid * kRowBytes;
-  // Opaque copy of the lane index: the offsets below are recomputed at every
-  // tile (a few integer ops) instead of being hoisted out of the tile loop and
-  // pinning five registers for the whole loop.
+// 64-row page).  Wave-instruction k (0 <= k < 37) covers LDS slots 64 k ..
+// 64 k + 63 (74 slots of 16 B per LDS row, slots 72 and 73 are padding); lane
+// `lane` moves the 16-byte chunk (row r, chunk c), byte offset r * 1152 +
+// c * 16.  Rows past the valid ones are zero-filled so no stale value is ever
+// read.  The four PV waves issue all tile loads: loader l = wave - 4 issues
+// k = l + 4 i, i < 10 (9 for l = 1..3).  An LDS-direct load keeps its wave
+// busy for ~60 cycles at issue, so the score waves, which set the pace, issue
+// none.
+struct TileDma {
+  char* dst;        // LDS stage
+  const char* src;  // first cache byte of the tile
+  int lim;          // valid bytes at src
+};
+
+__device__ __forceinline__ void issue_dma_one(const TileDma& d, int k, int lane) {
+  // Opaque copy of the lane index: the offsets are recomputed at every
+  // instruction (a few integer ops) instead of being hoisted out of the tile
+  // loop and pinning registers for the whole loop.
   asm volatile("" : "+v"(lane));
+  const int slotl = k * 64 + lane;
+  const int r = slotl / kSlotStride;
+  const int c = slotl - r * kSlotStride;
+  const int off = r * kRowBytes + c * 16;
+  const bool in_tile = c < kSlots;
+  if (in_tile && off < d.lim) {
+    __builtin_amdgcn_global_load_lds((const void*)(d.src + off), (MLA_LDS void*)(d.dst + k * 1024), 16, 0, 0);
+  } else if (in_tile) {
+    *(int4*)(d.dst + slotl * 16) = int4{0, 0, 0, 0};
+  }
+}
+
+constexpr int kLoaders = 4;  // waves issuing tile loads (the PV waves)
+constexpr int kDmaPerWave = (kNDma + kLoaders - 1) / kLoaders;  // 10 (wave 0), 9 (waves 1..3)
+
+// All of loader `ld`'s instructions of a tile at once.
+__device__ __forceinline__ void issue_tile_dma(const TileDma& d, int ld, int lane) {
 #pragma unroll
-  for (int i = 0; i < 5; ++i) {
-    const int k = wave + kWaves * i;
-    if (k < kNDma) {
-      const int slotl = k * 64 + lane;
-      const int r = slotl / kSlotStride;
-      const int c = slotl - r * kSlotStride;
-      const int off = r * kRowBytes + c * 16;
-      const bool in_tile = slotl < kTile * kSlotStride && c < kSlots;
-      if (in_tile && off < lim) {
-        __builtin_amdgcn_global_load_lds((const void*)(src + off), (MLA_LDS void*)(st + k * 1024), 16, 0, 0);
-      } else if (in_tile) {
-        *(int4*)(st + slotl * 16) = int4{0, 0, 0, 0};
-      }
-    }
+  for (int i = 0; i < kDmaPerWave; ++i) {
+    const int k = ld + kLoaders * i;
+    if (k < kNDma) issue_dma_one(d, k, lane);
   }
 }
 
@@ -135,16 +169,17 @@ struct Smem {
   int red_i[2 * kWaves];
 };
 
-// Wait until at most `after` tiles issued after the needed one are still in
-// flight; `after_full` says they are all full tiles (a partial tile may issue
-// fewer instructions, then everything is waited for).
-__device__ __forceinline__ void wait_tiles(int wave, int after, bool after_full) {
+// Loader `ld`: wait until at most `after` tiles issued after the needed one
+// are still in flight; `after_full` says they are all full tiles (a partial
+// tile issues fewer instructions, then everything is waited for).
+__device__ __forceinline__ void wait_tiles(int ld, int after, bool after_full) {
+  static_assert(kNDma == kLoaders * (kDmaPerWave - 1) + 1, "loader 0 issues one more than loaders 1..3");
   if (!after_full || after == 0) {
     wait_vmcnt<0>();
-  } else if (wave < kNDma - 4 * kWaves) {  // waves issuing 5 instructions per tile
-    if (after == 1) wait_vmcnt<5>(); else wait_vmcnt<10>();
-  } else {                                  // waves issuing 4
-    if (after == 1) wait_vmcnt<4>(); else wait_vmcnt<8>();
+  } else if (ld == 0) {
+    if (after == 1) wait_vmcnt<kDmaPerWave>(); else wait_vmcnt<2 * kDmaPerWave>();
+  } else {
+    if (after == 1) wait_vmcnt<kDmaPerWave - 1>(); else wait_vmcnt<2 * (kDmaPerWave - 1)>();
   }
 }
 
@@ -323,12 +358,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
 
       const char* const req_base = cache + (int64_t)b * max_rows * kRowBytes;  // contiguous layout
       const int32_t* const bt_row = block_table ? block_table + (int64_t)b * max_pages : nullptr;
-      auto load_tile = [&](int it) {
+      // where tile `it` comes from and goes to (lim = 0: all zeros)
+      auto tile_dma = [&](int it) -> TileDma {
         const int t0 = pr0 + it * kTile;
         bool ok;
         const char* src = tile_src(cache, req_base, bt_row, n_pages, t0, &ok);
-        issue_tile_dma(sm.stage[it % kNStage], src, ok ? min(kTile, pr1 - t0) : 0, wave, lane);
+        return TileDma{sm.stage[it % kNStage], src, ok ? min(kTile, pr1 - t0) * kRowBytes : 0};
       };
+      auto load_tile = [&](int it) { issue_tile_dma(tile_dma(it), wave - 4, lane); };
 
       // The two roles run separate copies of the tile loop with the same
       // barrier sequence (1 + n_tiles + 1 barriers), so the register
@@ -363,9 +400,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
             }
           }
         }
-        load_tile(0);
-        if (n_tiles > 1) load_tile(1);
-        if (n_tiles > 2) load_tile(2);
         float m_used = -INFINITY;  // running max (log2 units) of this lane's query row
         float l_part = 0.f;        // this lane's share of the row's sum of p
 
@@ -379,15 +413,27 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
           for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
             for (int hl = 0; hl < NQH; ++hl) sacc[tb][hl] = f32x4{0.f, 0.f, 0.f, 0.f};
+          // K operands are read two k-steps ahead of their MFMAs
+          constexpr int kPre = 2;
+          const char* ap = st + l16 * kLRow + lg * 16;
+          bf16x8 ak[kPre + 1][2];
+#pragma unroll
+          for (int ks = 0; ks < kPre; ++ks)
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) ak[ks][tb] = *(const bf16x8*)(ap + 16 * tb * kLRow + ks * 64);
 #pragma unroll
           for (int ks = 0; ks < kKSteps; ++ks) {
+            if (ks + kPre < kKSteps) {
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
-              const bf16x8 ak = *(const bf16x8*)(st + (16 * tb + l16) * kLRow + (4 * ks + lg) * 16);
+              for (int tb = 0; tb < 2; ++tb)
+                ak[(ks + kPre) % (kPre + 1)][tb] = *(const bf16x8*)(ap + 16 * tb * kLRow + (ks + kPre) * 64);
+            }
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
               for (int hl = 0; hl < NQH; ++hl)
-                sacc[tb][hl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, qreg[hl][ks], sacc[tb][hl], 0, 0, 0);
-            }
+                sacc[tb][hl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[ks % (kPre + 1)][tb], qreg[hl][ks],
+                                                                      sacc[tb][hl], 0, 0, 0);
           }
           f32x4 sa = sacc[0][0], sb = sacc[1][0];
           if constexpr (QF32) {
@@ -406,8 +452,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
           }
           float mt = fmaxf(fmaxf(fmaxf(sa[0], sa[1]), fmaxf(sa[2], sa[3])),
                            fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3])));
-          mt = fmaxf(mt, __shfl_xor(mt, 16));
-          mt = fmaxf(mt, __shfl_xor(mt, 32));
+          mt = rows_max(mt);
           const bool need = mt > m_used + kTau;
           float alpha = 1.f;
           if (need) {
@@ -435,26 +480,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
           if (lane == 0) sm.flag[buf][wave] = any ? 1 : 0;
         };
 
-        // tile 0 must be in LDS; tiles 1, 2 may still be in flight
-        wait_tiles(wave, min(n_tiles - 1, 2), min(n_tiles - 1, 2) < n_tiles - 1 || last_full);
-        wait_lgkm0();
+        // tile 0 is in LDS after the first barrier (the PV waves load)
         barrier_raw();
         score_tile(0);
         for (int it = 0; it < n_tiles; ++it) {
           // before barrier `it`: P(it) is written; tile it+1 is in LDS (at most tile it+2 in flight)
-          if (it + 1 < n_tiles) {
-            const int issued = min(it + 2, n_tiles - 1);
-            wait_tiles(wave, issued - (it + 1), issued < n_tiles - 1 || last_full);
-          }
           wait_lgkm0();
           barrier_raw();
-          if (it + 3 < n_tiles) load_tile(it + 3);  // into the stage of tile it-1, free after its PV
           if (it + 1 < n_tiles) score_tile(it + 1);
         }
         // epilogue: lse and 1/l of this wave's rows
-        float lt = l_part;
-        lt += __shfl_xor(lt, 16);
-        lt += __shfl_xor(lt, 32);
+        const float lt = rows_sum(l_part);
         if (lg == 0) {
           sm.rowinv[qrow] = lt > 0.f ? 1.f / lt : 0.f;
           if (rvalid) {
@@ -464,8 +500,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
         }
         wait_lgkm0();
         barrier_raw();
+      } else if (!pv_wave) {
+        // ---- waves NRB..3 (when MT < 64): idle, same barriers ----
+        barrier_raw();
+        for (int it = 0; it < n_tiles; ++it) barrier_raw();
+        barrier_raw();
       } else {
-        // ---- PV wave (waves 4..7): 128 latent columns of all rows; other waves only load ----
+        // ---- PV wave (waves 4..7): 128 latent columns of all rows, and all tile loads ----
         load_tile(0);
         if (n_tiles > 1) load_tile(1);
         if (n_tiles > 2) load_tile(2);
@@ -475,54 +516,77 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
 #pragma unroll
           for (int q = 0; q < NRB; ++q) acc_o[db][q] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        // O^T[d x rows] += C^T . P^T of tile `it` for this wave's 128 columns
-        auto pv_tile = [&](int it) {
-          const char* st = sm.stage[it % kNStage];
-          const int buf = it & 1;
+        // O^T[d x rows] += C^T . P^T of one tile (stage `st`, P / alpha / flags
+        // of its buffer) for this wave's 128 columns, with this wave's loads of
+        // a later tile (into `dma_dst`) spread over the column blocks.  The LDS
+        // operands arrive as restrict pointers: the compiler then knows that the
+        // transposed reads never touch the stage being loaded and does not make
+        // them wait for every load in flight.
+        auto pv_tile = [&](const char* __restrict__ st, const char* __restrict__ pbuf,
+                           const float* __restrict__ alph, const int* __restrict__ flg,
+                           char* __restrict__ dma_dst, const char* dma_src, int dma_lim, bool with_dma) {
+          const TileDma dma{dma_dst, dma_src, dma_lim};
+          // all C^T operands of the tile first (16 transposed reads in flight),
+          // then P, the rescale flags and factors
+          const int rq = l16 >> 2, qq = lane & 3;
+          bf16x8 ac[8];
+          const char* p0 = st + (8 * lg + rq) * kLRow + (128 * pw + 4 * qq) * 2;
+#pragma unroll
+          for (int db = 0; db < 8; ++db) {
+            const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p0 + 32 * db));
+            const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p0 + 32 * db + 4 * kLRow));
+            ac[db] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
           int flag = 0;
 #pragma unroll
-          for (int r = 0; r < NRB; ++r) flag |= sm.flag[buf][r];
+          for (int r = 0; r < NRB; ++r) flag |= flg[r];
           bf16x8 bq[NRB];
 #pragma unroll
-          for (int q = 0; q < NRB; ++q) bq[q] = *(const bf16x8*)(sm.p[buf] + (16 * q + l16) * kPStr + lg * 16);
+          for (int q = 0; q < NRB; ++q) bq[q] = *(const bf16x8*)(pbuf + (16 * q + l16) * kPStr + lg * 16);
           if (flag) {
 #pragma unroll
             for (int q = 0; q < NRB; ++q) {
-              const float al = sm.alpha[buf][16 * q + l16];
+              const float al = alph[16 * q + l16];
 #pragma unroll
               for (int db = 0; db < 8; ++db) acc_o[db][q] *= al;
             }
           }
-          const int rq = l16 >> 2, qq = lane & 3;
+          // the MFMAs, with this wave's loads issued between them
 #pragma unroll
           for (int db = 0; db < 8; ++db) {
-            const int d0 = 128 * pw + 16 * db;
-            const char* p0 = st + (8 * lg + rq) * kLRow + (d0 + 4 * qq) * 2;
-            const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p0));
-            const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p0 + 4 * kLRow));
-            const bf16x8 ac = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+            if (with_dma) {  // load i = db, plus i = 8 at db 2 and i = 9 at db 5
+              issue_dma_one(dma, pw + kLoaders * db, lane);
+              if (db == 2) issue_dma_one(dma, pw + kLoaders * 8, lane);
+              if (db == 5 && pw + kLoaders * 9 < kNDma) issue_dma_one(dma, pw + kLoaders * 9, lane);
+            }
 #pragma unroll
             for (int q = 0; q < NRB; ++q)
-              acc_o[db][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ac, bq[q], acc_o[db][q], 0, 0, 0);
+              acc_o[db][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ac[db], bq[q], acc_o[db][q], 0, 0, 0);
           }
         };
 
-        wait_tiles(wave, min(n_tiles - 1, 2), min(n_tiles - 1, 2) < n_tiles - 1 || last_full);
+        // tile 0 must be in LDS; tiles 1, 2 may still be in flight
+        wait_tiles(pw, min(n_tiles - 1, 2), min(n_tiles - 1, 2) < n_tiles - 1 || last_full);
         wait_lgkm0();
         barrier_raw();
         for (int it = 0; it < n_tiles; ++it) {
+          // before barrier `it`: tile it+1 is in LDS (tile it+2 may be in flight)
           if (it + 1 < n_tiles) {
             const int issued = min(it + 2, n_tiles - 1);
-            wait_tiles(wave, issued - (it + 1), issued < n_tiles - 1 || last_full);
+            wait_tiles(pw, issued - (it + 1), issued < n_tiles - 1 || last_full);
           }
           wait_lgkm0();
           barrier_raw();
-          if (it + 3 < n_tiles) load_tile(it + 3);
-          if (pv_wave) pv_tile(it);
+          // tile it+3 goes into the stage of tile it-1, free after its PV
+          const bool with_dma = it + 3 < n_tiles;
+          const TileDma dma = with_dma ? tile_dma(it + 3) : TileDma{sm.stage[(it + 3) % kNStage], cache, 0};
+          const int buf = it & 1;
+          pv_tile(sm.stage[it % kNStage], sm.p[buf], sm.alpha[buf], sm.flag[buf], dma.dst, dma.src, dma.lim,
+                  with_dma);
         }
         wait_lgkm0();
         barrier_raw();
-        if (pv_wave) {
+        {
 #pragma unroll
           for (int q = 0; q < NRB; ++q) {
             const int qr = 16 * q + l16;
