@@ -71,40 +71,41 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const bf16* __restrict
 }
 
 constexpr int kDv = 128;
+constexpr int kUvCols = 16;  // output columns per workgroup (one wave)
 
+// One wave per (head, 16 output columns): the wave holds its 16 x 512 slice
+// of w_uv as the B operand (64 registers), so a head's weights are spread
+// over 8 workgroups and the loads of a small batch are not serialised on a
+// few compute units.
 template <typename TO>
-__global__ __launch_bounds__(256) void out_uv_mfma_kernel(const bf16* __restrict__ o_lat,
-                                                          const bf16* __restrict__ w_uv, TO* __restrict__ out,
-                                                          int n_tok, int n_heads) {
+__global__ __launch_bounds__(64) void out_uv_mfma_kernel(const bf16* __restrict__ o_lat,
+                                                         const bf16* __restrict__ w_uv, TO* __restrict__ out,
+                                                         int n_tok, int n_heads) {
   const int h = blockIdx.x;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int v0 = blockIdx.y * kUvCols;
+  const int lane = threadIdx.x;
   const int l16 = lane & 15, lg = lane >> 4;
-  // B operand straight from HBM: lane col v = 32 wave + 16 cb + l16, k = 32 ks + 8 lg + (0..7)
-  bf16x8 wb[2][16];
+  // B operand straight from HBM: lane col v = v0 + l16, k = 32 ks + 8 lg + (0..7)
+  bf16x8 wb[16];
+  const bf16* wr = w_uv + ((int64_t)h * kDv + v0 + l16) * kLat + 8 * lg;
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const bf16* wr = w_uv + ((int64_t)h * kDv + 32 * wave + 16 * cb + l16) * kLat + 8 * lg;
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) wb[cb][ks] = *(const bf16x8*)(wr + 32 * ks);
-  }
+  for (int ks = 0; ks < 16; ++ks) wb[ks] = *(const bf16x8*)(wr + 32 * ks);
   for (int t0 = 0; t0 < n_tok; t0 += 16) {
     const int t = t0 + l16;
     const bf16* orow = o_lat + ((int64_t)t * n_heads + h) * kLat + 8 * lg;
+    bf16x8 oa[16];
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) oa[ks] = t < n_tok ? *(const bf16x8*)(orow + 32 * ks) : bf16x8{};
     f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      const bf16x8 oa = t < n_tok ? *(const bf16x8*)(orow + 32 * ks) : bf16x8{};
+    for (int ks = 0; ks < 16; ++ks)
+      acc[ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa[ks], wb[ks], acc[ks & 1], 0, 0, 0);
+    const f32x4 r = acc[0] + acc[1];
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa, wb[cb][ks], acc[cb], 0, 0, 0);
+    for (int e = 0; e < 4; ++e) {
+      const int tt = t0 + 4 * lg + e;
+      if (tt < n_tok) store_f(out + ((int64_t)tt * n_heads + h) * kDv + v0 + l16, r[e]);
     }
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int tt = t0 + 4 * lg + e;
-        if (tt < n_tok) store_f(out + ((int64_t)tt * n_heads + h) * kDv + 32 * wave + 16 * cb + l16, acc[cb][e]);
-      }
   }
 }
 
@@ -133,12 +134,12 @@ bool out_uv_mfma_ok(const void* o_lat, const void* w_uv, int d_c, int d_v) {
 
 hipError_t launch_out_uv_mfma(const void* o_lat, const void* w_uv, void* out, bool out_bf16, int n_tok,
                               int n_heads, hipStream_t stream) {
-  dim3 grid(n_heads);
+  dim3 grid(n_heads, kDv / kUvCols);
   if (out_bf16)
-    return launch(out_uv_mfma_kernel<bf16>, grid, dim3(256), stream, (const bf16*)o_lat, (const bf16*)w_uv,
+    return launch(out_uv_mfma_kernel<bf16>, grid, dim3(64), stream, (const bf16*)o_lat, (const bf16*)w_uv,
                        (bf16*)out, n_tok, n_heads);
   else
-    return launch(out_uv_mfma_kernel<float>, grid, dim3(256), stream, (const bf16*)o_lat,
+    return launch(out_uv_mfma_kernel<float>, grid, dim3(64), stream, (const bf16*)o_lat,
                        (const bf16*)w_uv, (float*)out, n_tok, n_heads);
 }
 

@@ -177,21 +177,25 @@ hipError_t launch_out_uv(const void* o_lat, bool o_bf, const void* w_uv, bool w_
 
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of partial states (RedKnot-MLA abstract: the paths are
-// merged before one shared output projection).  One 128-thread block per row:
-// wave 0 compacts the live slots (lse > -inf) in slot order with their
-// weights exp(lse_j - max), so -inf slots are never read and the sum order is
-// fixed (bitwise repeatable); then every thread owns 4 columns and streams the
-// live o_part rows with 4 float4 loads in flight.
+// merged before one shared output projection).  One 256-thread block per
+// (row, chunk of `cols` = 128, 256 or 512 columns): wave 0 compacts the live
+// slots (lse > -inf) in slot order with their weights exp(lse_j - max), so
+// -inf slots are never read; the threads then split into G = 256 / (cols/4)
+// slot groups of cols/4 column threads (float4 each), group g summing live
+// slots g, g + G, ... with 4 loads in flight, and the G group sums are added
+// in a fixed order, so the result is bitwise repeatable.  Few rows get narrow
+// chunks (more blocks in flight), many rows whole-row blocks.
 // ---------------------------------------------------------------------------
 constexpr int kCombMaxPart = 1024;
 
 template <typename TO>
-__global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ o_part,
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o_part,
                                                       const float* __restrict__ lse_part, int n_rows,
-                                                      int n_part, int d_c, TO* __restrict__ o_lat,
+                                                      int n_part, int d_c, int cols, TO* __restrict__ o_lat,
                                                       float* __restrict__ lse) {
   __shared__ int live_idx[kCombMaxPart];
   __shared__ float live_w[kCombMaxPart];
+  __shared__ f32x4 red[224];  // (G - 1) * cols / 4 <= 224 for cols >= 128
   __shared__ float s_inv, s_lse;
   __shared__ int s_n;
   const int row = blockIdx.x;
@@ -228,38 +232,45 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
   __syncthreads();
   const int n = s_n;
   const float inv = s_inv;
-  if (lse && tid == 0) lse[row] = s_lse;
-  const float* op = o_part + (int64_t)row * n_part * d_c;
-  TO* orow = o_lat + (int64_t)row * d_c;
-  for (int c = 4 * tid; c < d_c; c += 512) {
-    const bool vec = c + 4 <= d_c;
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    int i = 0;
-    if (vec) {
-      for (; i + 4 <= n; i += 4) {
-        f32x4 v[4];
+  if (lse && blockIdx.y == 0 && tid == 0) lse[row] = s_lse;
+  const int ct_n = cols / 4;       // column threads per group
+  const int G = 256 / ct_n;        // slot groups
+  const int g = tid / ct_n, ct = tid % ct_n;
+  const int c = blockIdx.y * cols + 4 * ct;  // d_c is a multiple of 4: c < d_c means 4 whole columns
+  const float* op = o_part + (int64_t)row * n_part * d_c + c;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (c < d_c) {
+    int i = g;
+    for (; i + 3 * G < n; i += 4 * G) {
+      f32x4 v[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = *(const f32x4*)(op + (int64_t)live_idx[i + u] * d_c + c);
+      for (int u = 0; u < 4; ++u) v[u] = *(const f32x4*)(op + (int64_t)live_idx[i + u * G] * d_c);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc += live_w[i + u] * v[u];
-      }
-      for (; i < n; ++i) acc += live_w[i] * *(const f32x4*)(op + (int64_t)live_idx[i] * d_c + c);
-    } else {
-      for (; i < n; ++i)
-        for (int e = 0; e < 4 && c + e < d_c; ++e) acc[e] += live_w[i] * op[(int64_t)live_idx[i] * d_c + c + e];
+      for (int u = 0; u < 4; ++u) acc += live_w[i + u * G] * v[u];
     }
-    for (int e = 0; e < 4 && c + e < d_c; ++e) store_f(orow + c + e, acc[e] * inv);
+    for (; i < n; i += G) acc += live_w[i] * *(const f32x4*)(op + (int64_t)live_idx[i] * d_c);
+  }
+  if (g > 0) red[(g - 1) * ct_n + ct] = acc;
+  __syncthreads();
+  if (g == 0 && c < d_c) {
+    for (int k = 0; k < G - 1; ++k) acc += red[k * ct_n + ct];
+    TO* orow = o_lat + (int64_t)row * d_c + c;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_f(orow + e, acc[e] * inv);
   }
 }
 
 hipError_t launch_combine(const float* o_part, const float* lse_part, int n_rows, int n_part, int d_c,
                           void* o_lat, bool out_bf16, float* lse, hipStream_t stream) {
+  // chunk width: ~1024 blocks in flight for few rows, whole 512-column rows for many
+  const int cols = n_rows >= 1024 ? 512 : n_rows >= 512 ? 256 : 128;
+  const dim3 grid(n_rows, (d_c + cols - 1) / cols);
   if (out_bf16)
-    return launch(combine_kernel<bf16>, dim3(n_rows), dim3(128), stream, o_part, lse_part, n_rows,
-                       n_part, d_c, (bf16*)o_lat, lse);
+    return launch(combine_kernel<bf16>, grid, dim3(256), stream, o_part, lse_part, n_rows, n_part, d_c, cols,
+                  (bf16*)o_lat, lse);
   else
-    return launch(combine_kernel<float>, dim3(n_rows), dim3(128), stream, o_part, lse_part, n_rows,
-                       n_part, d_c, (float*)o_lat, lse);
+    return launch(combine_kernel<float>, grid, dim3(256), stream, o_part, lse_part, n_rows, n_part, d_c, cols,
+                  (float*)o_lat, lse);
 }
 
 // ---------------------------------------------------------------------------
