@@ -17,15 +17,18 @@
 //    rows: the latent serves every head's key and value.
 //  * LDS rows are padded to 74 slots of 16 B (1184 B): the 16-row operand
 //    reads of the score MFMAs then run without bank conflicts.
-//  * Wave roles, one tile apart: score waves 0..MT/16-1 each hold the query
-//    of 16 rows in registers and compute S^T[tokens x rows] = K_tile .
+//  * Wave roles, one tile apart: score waves 0..3 hold the query of a 16-row
+//    block in registers and compute S^T[tokens x rows] = K_tile .
 //    [q_lat|q_rot]^T of tile it+1 on v_mfma_f32_16x16x32_bf16, the online
-//    softmax and P (bf16, in LDS); PV waves 4..7 each own 128 latent columns
+//    softmax and P (bf16, in LDS).  With MT = 64 each score wave owns one row
+//    block and all 18 k-steps; with MT = 32 / 16 the 2 / 4 waves of a row
+//    block split the k-steps, add their partial scores through LDS (one extra
+//    barrier per tile) and the first of them runs the softmax, which shortens
+//    the per-tile latency of small head counts.  PV waves 4..7 each own 128 latent columns
 //    and accumulate O^T[d x rows] += C_tile^T . P^T of tile it, with C^T from
 //    ds_read_b64_tr_b16 transposed LDS reads.  The PV waves also issue all
 //    tile loads (spread between their MFMAs): an LDS-direct load holds its
 //    wave for tens of cycles at issue, and the score waves set the pace.
-//    Waves in between (MT < 64) only keep the barrier count.
 //  * The query arrives in fp32 and is split into bf16 hi + lo parts (q = hi +
 //    lo to ~2^-17): two MFMAs per k-step into separate accumulators.  A
 //    bf16-rounded query would put ~1e-3 error into the scores.
@@ -158,8 +161,12 @@ __device__ __forceinline__ const char* tile_src(const char* cache, const char* r
 
 template <int MT>
 struct Smem {
+  static constexpr int NRB = MT / 16;
+  static constexpr int KS = 4 / NRB;  // k-parts per 16-row block (score waves 0..3)
   char stage[kNStage][kStageBytes];
   char p[2][MT * kPStr];
+  // partial scores of k-parts 1..KS-1 of each row block: [part][tb][lane][4]
+  float xbuf[KS > 1 ? NRB * (KS - 1) * 2 * 64 * 4 : 1];
   float alpha[2][MT];
   float rowinv[MT];
   int flag[2][4];
@@ -190,7 +197,9 @@ template <int MT, bool QF32>
 __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, int n_share, int n_rg,
                                                                   int rows_total) {
   constexpr int NQH = QF32 ? 2 : 1;  // query parts (hi, lo)
-  constexpr int NRB = MT / 16;       // 16-row blocks = score waves
+  constexpr int NRB = MT / 16;       // 16-row blocks
+  constexpr int KS = 4 / NRB;        // score waves per row block, each with a part of the 18 k-steps
+  constexpr int KMAX = (kKSteps + KS - 1) / KS;
   __shared__ __attribute__((aligned(16))) Smem<MT> sm;
 
   // every argument field as a local value (see issue_tile_dma)
@@ -271,10 +280,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
   }
   const int lo = j * share, hi = lo + share;
 
-  // ---- roles: waves 0..NRB-1 score 16 query rows each; waves 4..7 own 128 latent columns each ----
-  const bool qk_wave = wave < NRB;
+  // ---- roles: waves 0..3 score (row block rb, k-part kp); waves 4..7 own 128 latent columns each ----
+  const bool qk_wave = wave < 4;
   const bool pv_wave = wave >= 4;
-  const int qrow = wave * 16 + l16;  // local row of this lane (score waves)
+  const int rb = (wave & 3) / KS;    // 16-row block of a score wave
+  const int kp = (wave & 3) % KS;    // its part of the k-steps: [ks0, ks0 + kcnt)
+  const int kcnt = kKSteps / KS + (kp < kKSteps % KS ? 1 : 0);
+  const int ks0 = kp * (kKSteps / KS) + min(kp, kKSteps % KS);
+  const int qrow = rb * 16 + l16;    // local row of this lane (score waves)
   const bool rvalid = qk_wave && qrow < nrows;
   const int Rc = rvalid ? row0 + qrow : row0;
   const int s_row = Rc / hc;
@@ -368,19 +381,21 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
       auto load_tile = [&](int it) { issue_tile_dma(tile_dma(it), wave - 4, lane); };
 
       // The two roles run separate copies of the tile loop with the same
-      // barrier sequence (1 + n_tiles + 1 barriers), so the register
-      // allocator never holds the query block and the O accumulator at once.
+      // barrier sequence (1 + n_tiles + 1 barriers, plus one exchange barrier
+      // per scored tile when KS > 1), so the register allocator never holds
+      // the query block and the O accumulator at once.
       if (qk_wave) {
-        // ---- score wave: 16 query rows, all 18 k-steps (hi and lo parts) ----
-        bf16x8 qreg[NQH][kKSteps];
+        // ---- score wave: 16 query rows (row block rb), k-steps [ks0, ks0 + kcnt), hi and lo parts ----
+        bf16x8 qreg[NQH][KMAX];
         {
           const int64_t qi = (int64_t)b * s_q * n_heads + q_off;
 #pragma unroll
-          for (int ks = 0; ks < kKSteps; ++ks) {
-            const int k0 = 32 * ks + 8 * lg;
+          for (int i = 0; i < KMAX; ++i) {
+            const int k0 = 32 * (ks0 + i) + 8 * lg;
+            const bool in = rvalid && i < kcnt;
             if constexpr (QF32) {
               f32x4 v0 = f32x4{0.f, 0.f, 0.f, 0.f}, v1 = v0;
-              if (rvalid) {
+              if (in) {
                 const float* src = k0 < kDc ? (const float*)q_lat_p + qi * kDc + k0
                                             : (const float*)q_rot_p + qi * kDr + (k0 - kDc);
                 v0 = *(const f32x4*)src;
@@ -390,20 +405,22 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
               for (int e = 0; e < 8; ++e) {
                 const float v = e < 4 ? v0[e] : v1[e - 4];
                 const bf16 h = (bf16)v;
-                qreg[0][ks][e] = h;
-                qreg[1][ks][e] = (bf16)(v - (float)h);
+                qreg[0][i][e] = h;
+                qreg[1][i][e] = (bf16)(v - (float)h);
               }
             } else {
-              qreg[0][ks] = rvalid ? (k0 < kDc ? *(const bf16x8*)((const bf16*)q_lat_p + qi * kDc + k0)
-                                               : *(const bf16x8*)((const bf16*)q_rot_p + qi * kDr + (k0 - kDc)))
-                                   : bf16x8{};
+              qreg[0][i] = in ? (k0 < kDc ? *(const bf16x8*)((const bf16*)q_lat_p + qi * kDc + k0)
+                                          : *(const bf16x8*)((const bf16*)q_rot_p + qi * kDr + (k0 - kDc)))
+                              : bf16x8{};
             }
           }
         }
-        float m_used = -INFINITY;  // running max (log2 units) of this lane's query row
-        float l_part = 0.f;        // this lane's share of the row's sum of p
+        float m_used = -INFINITY;  // running max (log2 units) of this lane's query row (k-part 0)
+        float l_part = 0.f;        // this lane's share of the row's sum of p (k-part 0)
 
-        // scores, softmax and P of tile `it`, into P / alpha / flag buffer it & 1
+        // scores, softmax and P of tile `it`, into P / alpha / flag buffer it & 1.
+        // With KS > 1 the waves of a row block exchange partial scores through
+        // LDS (one extra barrier) and k-part 0 runs the softmax.
         auto score_tile = [&](int it) {
           const char* st = sm.stage[it % kNStage];
           const int t0 = pr0 + it * kTile;
@@ -415,30 +432,47 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
             for (int hl = 0; hl < NQH; ++hl) sacc[tb][hl] = f32x4{0.f, 0.f, 0.f, 0.f};
           // K operands are read two k-steps ahead of their MFMAs
           constexpr int kPre = 2;
-          const char* ap = st + l16 * kLRow + lg * 16;
+          const char* ap = st + l16 * kLRow + lg * 16 + ks0 * 64;
           bf16x8 ak[kPre + 1][2];
 #pragma unroll
-          for (int ks = 0; ks < kPre; ++ks)
+          for (int i = 0; i < kPre; ++i)
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb) ak[ks][tb] = *(const bf16x8*)(ap + 16 * tb * kLRow + ks * 64);
+            for (int tb = 0; tb < 2; ++tb) ak[i][tb] = *(const bf16x8*)(ap + 16 * tb * kLRow + i * 64);
 #pragma unroll
-          for (int ks = 0; ks < kKSteps; ++ks) {
-            if (ks + kPre < kKSteps) {
+          for (int i = 0; i < KMAX; ++i) {
+            if (i < kcnt) {
+              if (i + kPre < kcnt) {
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb)
+                  ak[(i + kPre) % (kPre + 1)][tb] = *(const bf16x8*)(ap + 16 * tb * kLRow + (i + kPre) * 64);
+              }
 #pragma unroll
               for (int tb = 0; tb < 2; ++tb)
-                ak[(ks + kPre) % (kPre + 1)][tb] = *(const bf16x8*)(ap + 16 * tb * kLRow + (ks + kPre) * 64);
+#pragma unroll
+                for (int hl = 0; hl < NQH; ++hl)
+                  sacc[tb][hl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[i % (kPre + 1)][tb], qreg[hl][i],
+                                                                        sacc[tb][hl], 0, 0, 0);
             }
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-              for (int hl = 0; hl < NQH; ++hl)
-                sacc[tb][hl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[ks % (kPre + 1)][tb], qreg[hl][ks],
-                                                                      sacc[tb][hl], 0, 0, 0);
           }
           f32x4 sa = sacc[0][0], sb = sacc[1][0];
           if constexpr (QF32) {
             sa += sacc[0][1];
             sb += sacc[1][1];
+          }
+          if constexpr (KS > 1) {
+            f32x4* xb = (f32x4*)sm.xbuf;  // [part][tb][lane]
+            if (kp > 0) {
+              xb[((rb * (KS - 1) + kp - 1) * 2 + 0) * 64 + lane] = sa;
+              xb[((rb * (KS - 1) + kp - 1) * 2 + 1) * 64 + lane] = sb;
+            }
+            wait_lgkm0();
+            barrier_raw();
+            if (kp > 0) return;
+#pragma unroll
+            for (int j = 0; j < KS - 1; ++j) {
+              sa += xb[((rb * (KS - 1) + j) * 2 + 0) * 64 + lane];
+              sb += xb[((rb * (KS - 1) + j) * 2 + 1) * 64 + lane];
+            }
           }
           sa *= sl2;
           sb *= sl2;
@@ -477,7 +511,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
           *(bf16x4*)(prow) = pa;
           *(bf16x4*)(prow + 32) = pb;
           if (lg == 0) sm.alpha[buf][qrow] = alpha;
-          if (lane == 0) sm.flag[buf][wave] = any ? 1 : 0;
+          if (lane == 0) sm.flag[buf][rb] = any ? 1 : 0;
         };
 
         // tile 0 is in LDS after the first barrier (the PV waves load)
@@ -489,9 +523,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
           barrier_raw();
           if (it + 1 < n_tiles) score_tile(it + 1);
         }
-        // epilogue: lse and 1/l of this wave's rows
+        // epilogue: lse and 1/l of this row block's rows (k-part 0)
         const float lt = rows_sum(l_part);
-        if (lg == 0) {
+        if (kp == 0 && lg == 0) {
           sm.rowinv[qrow] = lt > 0.f ? 1.f / lt : 0.f;
           if (rvalid) {
             const int64_t ri = (int64_t)b * s_q * n_heads + q_off;
@@ -499,11 +533,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
           }
         }
         wait_lgkm0();
-        barrier_raw();
-      } else if (!pv_wave) {
-        // ---- waves NRB..3 (when MT < 64): idle, same barriers ----
-        barrier_raw();
-        for (int it = 0; it < n_tiles; ++it) barrier_raw();
         barrier_raw();
       } else {
         // ---- PV wave (waves 4..7): 128 latent columns of all rows, and all tile loads ----
@@ -524,7 +553,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
         // them wait for every load in flight.
         auto pv_tile = [&](const char* __restrict__ st, const char* __restrict__ pbuf,
                            const float* __restrict__ alph, const int* __restrict__ flg,
-                           char* __restrict__ dma_dst, const char* dma_src, int dma_lim, bool with_dma) {
+                           char* __restrict__ dma_dst, const char* dma_src, int dma_lim, bool with_dma,
+                           bool with_x) {
           const TileDma dma{dma_dst, dma_src, dma_lim};
           // all C^T operands of the tile first (16 transposed reads in flight),
           // then P, the rescale flags and factors
@@ -543,6 +573,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
           bf16x8 bq[NRB];
 #pragma unroll
           for (int q = 0; q < NRB; ++q) bq[q] = *(const bf16x8*)(pbuf + (16 * q + l16) * kPStr + lg * 16);
+          // the score waves' mid-tile exchange barrier (their next tile), with this
+          // tile's reads in flight
+          if (with_x) barrier_raw();
           if (flag) {
 #pragma unroll
             for (int q = 0; q < NRB; ++q) {
@@ -569,6 +602,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
         wait_tiles(pw, min(n_tiles - 1, 2), min(n_tiles - 1, 2) < n_tiles - 1 || last_full);
         wait_lgkm0();
         barrier_raw();
+        if constexpr (KS > 1) barrier_raw();  // the score waves' exchange of tile 0
         for (int it = 0; it < n_tiles; ++it) {
           // before barrier `it`: tile it+1 is in LDS (tile it+2 may be in flight)
           if (it + 1 < n_tiles) {
@@ -582,7 +616,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
           const TileDma dma = with_dma ? tile_dma(it + 3) : TileDma{sm.stage[(it + 3) % kNStage], cache, 0};
           const int buf = it & 1;
           pv_tile(sm.stage[it % kNStage], sm.p[buf], sm.alpha[buf], sm.flag[buf], dma.dst, dma.src, dma.lim,
-                  with_dma);
+                  with_dma, KS > 1 && it + 1 < n_tiles);
         }
         wait_lgkm0();
         barrier_raw();
