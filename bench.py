@@ -1,8 +1,9 @@
 """Decode-step benchmark: one attention layer's absorbed-MLA decode on one GPU.
 
 A step is the whole hot path on one batch: rope_relocate_q (per distinct
-segment shift) -> mla_absorb_q -> mla_decode_splitkv -> mla_combine_lse ->
-mla_out_uv, on seeded synthetic inputs already resident in HBM.  Prints one
+segment shift) and mla_absorb_q (one mla_prepare_q launch) ->
+mla_decode_splitkv -> mla_combine_lse -> mla_out_uv, on seeded synthetic
+inputs already resident in HBM.  Prints one
 JSON line with decode tokens/s, the decode kernel's achieved HBM GB/s against
 the MI355X roofline, and the fp64 CPU oracle timed on a bounded sample.
 
@@ -254,13 +255,13 @@ def main():
         # each call alone, back to back on the stream (host launches)
         detail = {}
         reps = 50
-        for nm in ["rope", "absorb", "decode", "combine", "out_uv"]:
+        for nm in ["prepare", "decode", "combine", "out_uv"]:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             e0.record(stream)
             for j in range(reps):
                 pj, dj, qj = bound[j % n_copies]
-                g = {"rope": pj[:-1], "absorb": pj[-1:], "decode": dj, "combine": qj[:1], "out_uv": qj[1:]}[nm]
+                g = {"prepare": pj, "decode": dj, "combine": qj[:1], "out_uv": qj[1:]}[nm]
                 run_calls(g)
             e1.record(stream)
             torch.cuda.synchronize()

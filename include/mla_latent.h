@@ -20,6 +20,7 @@
  *   mla_decode_splitkv -> partial (o_lat, lse) states per KV split / segment
  *   mla_combine_lse  -> o_lat, lse (log-sum-exp merge of the partial states)
  *   mla_out_uv       -> out        (U_V o_lat, once per query)
+ * mla_prepare_q runs the first two in one launch (all segment shifts at once).
  *
  * Conventions shared by every call
  *  - All tensor pointers are DEVICE pointers (HIP device memory), row-major,
@@ -181,6 +182,29 @@ mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q
  */
 mla_status mla_combine_lse(const float* o_part, const float* lse_part, int n_rows, int n_part,
                            int d_c, void* o_lat, int out_dtype, float* lse, void* stream);
+
+/*
+ * mla_prepare_q -- rope_relocate_q for n_shift segment shifts and
+ * mla_absorb_q, fused into one launch where the absorption runs on its MFMA
+ * path (in_dtype bf16, d_nope 128, d_c 512, 16-byte aligned q_nope / w_uk);
+ * other shapes run the two kernels one after the other.  Same arithmetic and
+ * layouts as those two calls ([T] "Move the Key Projection Into the Query",
+ * "Position Rotations Complicate the Absorption"; [R] query-side relocation):
+ *
+ *   q_lat     = mla_absorb_q(q_nope, w_uk)                 (lat_dtype)
+ *   q_rots[k] = rope_relocate_q(q_pe, pos, shifts[k])      (rot_dtype), k < n_shift
+ *
+ * q_nope, w_uk, q_lat, q_pe, pos: as in mla_absorb_q / rope_relocate_q; q_pe
+ * has in_dtype.  q_rots: host array of n_shift device pointers
+ * [n_tok][n_heads][d_rope]; shifts: host array of n_shift device pointers
+ * ([n_tok] int64, an entry may be NULL = no shift) or NULL for all zero.
+ * n_shift 0..8.  A small decode batch spends most of these two kernels in
+ * launch latency, so one launch instead of 1 + n_shift shortens the step.
+ */
+mla_status mla_prepare_q(const void* q_nope, const void* q_pe, const void* w_uk, int in_dtype, void* q_lat,
+                         int lat_dtype, void* const* q_rots, const int64_t* const* shifts, int n_shift,
+                         int rot_dtype, const int64_t* pos, int n_tok, int n_heads, int d_nope, int d_rope, int d_c,
+                         double base, void* stream);
 
 /*
  * mla_out_uv -- expand the mixed latent once per query.

@@ -75,6 +75,21 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Rotation of one adjacent feature pair (2i, 2i+1) of a rotary query by
+// rel * base^(-2i/d_rope), counter-clockwise (MLA tutorial page, "Position
+// Rotations Complicate the Absorption").  rel is an int64 position
+// difference and the angle is formed in fp64 (positions reach 2^18, where an
+// fp32 angle is off by ~0.02 rad); the rotation itself is fp32.
+__device__ __forceinline__ void rope_pair(float x0, float x1, int64_t rel, int i, int d_rope, double base,
+                                          float* y0, float* y1) {
+  const double theta = pow(base, -2.0 * (double)i / (double)d_rope);
+  double sn, cs;
+  sincos((double)rel * theta, &sn, &cs);
+  const float cf = (float)cs, sf = (float)sn;
+  *y0 = x0 * cf - x1 * sf;
+  *y1 = x0 * sf + x1 * cf;
+}
+
 // Launch a kernel and return the status of this launch itself
 // (hipLaunchKernel), never an error left behind by an unrelated earlier call.
 template <typename... KArgs, typename Tuple, size_t... I>

@@ -48,6 +48,17 @@ hipError_t launch_out_uv(const void* o_lat, bool o_bf16, const void* w_uv, bool 
                          bool out_bf16, int n_tok, int n_heads, int d_c, int d_v, hipStream_t stream);
 // bf16 MFMA variants (d_nope = 128, d_c = 512, d_v = 128, 16-byte aligned).
 bool absorb_mfma_ok(const void* q_nope, const void* w_uk, int d_nope, int d_c);
+
+// Rotation targets of the fused query preparation (one per segment shift).
+constexpr int kMaxShift = 8;
+struct RopeTargets {
+  void* q_rot[kMaxShift];
+  const int64_t* shift[kMaxShift];
+  int n;
+};
+hipError_t launch_prepare_mfma(const void* q_nope, const void* w_uk, void* q_lat, bool lat_bf16, const void* q_pe,
+                               const int64_t* pos, const RopeTargets& rt, bool rot_bf16, int n_tok, int n_heads,
+                               int d_rope, double base, hipStream_t stream);
 hipError_t launch_absorb_mfma(const void* q_nope, const void* w_uk, void* q_lat, bool out_bf16, int n_tok,
                               int n_heads, hipStream_t stream);
 bool out_uv_mfma_ok(const void* o_lat, const void* w_uv, int d_c, int d_v);

@@ -14,6 +14,8 @@
 #include "mla_common.h"
 #include "mla_kernels.h"
 
+#include <algorithm>
+
 namespace mla {
 namespace {
 
@@ -22,13 +24,11 @@ constexpr int kLat = 512;         // d_c
 constexpr int kAbsCols = 128;     // output columns per absorb workgroup
 constexpr int kAbsLds = kAbsCols * 2 + 16;  // bytes per LDS weight row (padded)
 
+// Workgroup (head h, output columns j0 .. j0 + 127) of the absorption.
 template <typename TO>
-__global__ __launch_bounds__(256) void absorb_mfma_kernel(const bf16* __restrict__ q_nope,
-                                                          const bf16* __restrict__ w_uk, TO* __restrict__ q_lat,
-                                                          int n_tok, int n_heads) {
+__device__ __forceinline__ void absorb_block(const bf16* __restrict__ q_nope, const bf16* __restrict__ w_uk,
+                                             TO* __restrict__ q_lat, int n_tok, int n_heads, int h, int j0) {
   __shared__ __attribute__((aligned(16))) char wl[kNope * kAbsLds];
-  const int h = blockIdx.x;
-  const int j0 = blockIdx.y * kAbsCols;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, lg = lane >> 4;
   // weight slice w_uk[h][0:128][j0:j0+128] -> LDS (row i: 256 B + pad)
@@ -67,6 +67,44 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const bf16* __restrict
         if (tt < n_tok) store_f(q_lat + ((int64_t)tt * n_heads + h) * kLat + j0 + c0 + l16, acc[e]);
       }
     }
+  }
+}
+
+template <typename TO>
+__global__ __launch_bounds__(256) void absorb_mfma_kernel(const bf16* __restrict__ q_nope,
+                                                          const bf16* __restrict__ w_uk, TO* __restrict__ q_lat,
+                                                          int n_tok, int n_heads) {
+  absorb_block(q_nope, w_uk, q_lat, n_tok, n_heads, blockIdx.x, blockIdx.y * kAbsCols);
+}
+
+// rope_relocate_q for up to kMaxShift shifts and the absorption in one launch:
+// grid (heads, 4 + R); y < 4 are the absorption workgroups, y = 4 .. 4+R-1
+// rotate the head's rotary query pairs (all tokens and shifts) between them.
+template <typename TL, typename TR>
+__global__ __launch_bounds__(256) void prepare_mfma_kernel(const bf16* __restrict__ q_nope,
+                                                           const bf16* __restrict__ w_uk, TL* __restrict__ q_lat,
+                                                           const bf16* __restrict__ q_pe,
+                                                           const int64_t* __restrict__ pos, RopeTargets rt,
+                                                           int n_tok, int n_heads, int d_rope, double base) {
+  const int h = blockIdx.x;
+  if (blockIdx.y < kLat / kAbsCols) {
+    absorb_block(q_nope, w_uk, q_lat, n_tok, n_heads, h, blockIdx.y * kAbsCols);
+    return;
+  }
+  const int half = d_rope / 2;
+  const int per_shift = n_tok * half;
+  const int r = blockIdx.y - kLat / kAbsCols, n_r = gridDim.y - kLat / kAbsCols;
+  for (int idx = r * blockDim.x + threadIdx.x; idx < rt.n * per_shift; idx += n_r * blockDim.x) {
+    const int k = idx / per_shift;
+    const int t = (idx % per_shift) / half;
+    const int i = idx % half;
+    const int64_t th = (int64_t)t * n_heads + h;
+    const bf16* x = q_pe + th * d_rope + 2 * i;
+    float y0, y1;
+    rope_pair((float)x[0], (float)x[1], pos[t] - (rt.shift[k] ? rt.shift[k][t] : 0), i, d_rope, base, &y0, &y1);
+    TR* y = (TR*)rt.q_rot[k] + th * d_rope + 2 * i;
+    store_f(y, y0);
+    store_f(y + 1, y1);
   }
 }
 
@@ -115,6 +153,30 @@ bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool absorb_mfma_ok(const void* q_nope, const void* w_uk, int d_nope, int d_c) {
   return d_nope == kNope && d_c == kLat && al16(q_nope) && al16(w_uk);
+}
+
+template <typename TL, typename TR>
+static hipError_t prepare_launch(const void* q_nope, const void* w_uk, void* q_lat, const void* q_pe,
+                                 const int64_t* pos, const RopeTargets& rt, int n_tok, int n_heads, int d_rope,
+                                 double base, hipStream_t stream) {
+  // rotation workgroups per head: one per 256 pairs (all tokens and shifts), at most 64
+  const int pairs = rt.n * n_tok * (d_rope / 2);
+  const int n_r = std::max(1, std::min(64, (pairs + 255) / 256));
+  return launch(prepare_mfma_kernel<TL, TR>, dim3(n_heads, kLat / kAbsCols + n_r), dim3(256), stream,
+                (const bf16*)q_nope, (const bf16*)w_uk, (TL*)q_lat, (const bf16*)q_pe, pos, rt, n_tok, n_heads,
+                d_rope, base);
+}
+
+hipError_t launch_prepare_mfma(const void* q_nope, const void* w_uk, void* q_lat, bool lat_bf16, const void* q_pe,
+                               const int64_t* pos, const RopeTargets& rt, bool rot_bf16, int n_tok, int n_heads,
+                               int d_rope, double base, hipStream_t stream) {
+  if (lat_bf16 && rot_bf16)
+    return prepare_launch<bf16, bf16>(q_nope, w_uk, q_lat, q_pe, pos, rt, n_tok, n_heads, d_rope, base, stream);
+  if (lat_bf16)
+    return prepare_launch<bf16, float>(q_nope, w_uk, q_lat, q_pe, pos, rt, n_tok, n_heads, d_rope, base, stream);
+  if (rot_bf16)
+    return prepare_launch<float, bf16>(q_nope, w_uk, q_lat, q_pe, pos, rt, n_tok, n_heads, d_rope, base, stream);
+  return prepare_launch<float, float>(q_nope, w_uk, q_lat, q_pe, pos, rt, n_tok, n_heads, d_rope, base, stream);
 }
 
 hipError_t launch_absorb_mfma(const void* q_nope, const void* w_uk, void* q_lat, bool out_bf16, int n_tok,

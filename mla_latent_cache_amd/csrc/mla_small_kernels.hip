@@ -12,9 +12,8 @@ namespace mla {
 // ---------------------------------------------------------------------------
 // RoPE relocation (MLA tutorial page, "Position Rotations Complicate the
 // Absorption"; RedKnot-MLA abstract: query-side relocation).  Adjacent pairs
-// (2i, 2i+1) rotate counter-clockwise by (pos - shift) * base^(-2i/d_rope).
-// The position difference is int64 and the angle fp64 (positions reach 2^18,
-// where an fp32 angle would be off by ~0.02 rad); the rotation itself is fp32.
+// (2i, 2i+1) rotate counter-clockwise by (pos - shift) * base^(-2i/d_rope)
+// (rope_pair: int64 position difference, fp64 angle, fp32 rotation).
 // ---------------------------------------------------------------------------
 template <typename TI, typename TO>
 __global__ __launch_bounds__(256) void rope_kernel(const TI* __restrict__ q_pe, TO* __restrict__ q_rot,
@@ -29,15 +28,12 @@ __global__ __launch_bounds__(256) void rope_kernel(const TI* __restrict__ q_pe, 
     const int64_t th = idx / half;  // token * n_heads + head
     const int t = (int)(th / n_heads);
     const int64_t rel = pos[t] - (shift ? shift[t] : 0);
-    const double theta = pow(base, -2.0 * (double)i / (double)d_rope);
-    double s, c;
-    sincos((double)rel * theta, &s, &c);
-    const float cf = (float)c, sf = (float)s;
     const TI* x = q_pe + th * d_rope + 2 * i;
-    const float x0 = load_f(x), x1 = load_f(x + 1);
+    float y0, y1;
+    rope_pair(load_f(x), load_f(x + 1), rel, i, d_rope, base, &y0, &y1);
     TO* y = q_rot + th * d_rope + 2 * i;
-    store_f(y, x0 * cf - x1 * sf);
-    store_f(y + 1, x0 * sf + x1 * cf);
+    store_f(y, y0);
+    store_f(y + 1, y1);
   }
 }
 

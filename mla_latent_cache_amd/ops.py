@@ -60,6 +60,34 @@ def absorb_q(q_nope: torch.Tensor, w_uk: torch.Tensor, out: Optional[torch.Tenso
     return out
 
 
+def prepare_args(q_nope: torch.Tensor, q_pe: torch.Tensor, w_uk: torch.Tensor, q_lat: torch.Tensor,
+                 q_rots: Sequence[torch.Tensor], shifts: Sequence[Optional[torch.Tensor]], pos: torch.Tensor,
+                 base: float, stream: int):
+    """Argument tuple of mla_prepare_q (the two pointer arrays are part of it
+    and must stay alive while the tuple is used)."""
+    import ctypes
+    n_tok, n_heads, d_nope = q_nope.shape
+    d_rope = q_pe.shape[2]
+    d_c = w_uk.shape[2]
+    n = len(q_rots)
+    rot_arr = (ctypes.c_void_p * max(1, n))(*[r.data_ptr() for r in q_rots])
+    sh_arr = (ctypes.c_void_p * max(1, n))(*[_ptr(s) for s in shifts])
+    rot_dt = _dt(q_rots[0]) if n else 0
+    return (_ptr(q_nope), _ptr(q_pe), _ptr(w_uk), _dt(q_nope), _ptr(q_lat), _dt(q_lat), rot_arr, sh_arr, n, rot_dt,
+            _ptr(pos), n_tok, n_heads, d_nope, d_rope, d_c, float(base), stream)
+
+
+def prepare_q(q_nope: torch.Tensor, q_pe: torch.Tensor, w_uk: torch.Tensor, pos: torch.Tensor,
+              shifts: Sequence[Optional[torch.Tensor]], base: float = 10000.0,
+              lat_dtype: Optional[torch.dtype] = None, rot_dtype: Optional[torch.dtype] = None):
+    """mla_prepare_q: (q_lat, [q_rot per shift]) in one launch."""
+    n_tok, n_heads, _ = q_nope.shape
+    q_lat = torch.empty((n_tok, n_heads, w_uk.shape[2]), dtype=lat_dtype or q_nope.dtype, device=q_nope.device)
+    q_rots = [torch.empty_like(q_pe, dtype=rot_dtype or q_pe.dtype) for _ in shifts]
+    _lib.call("mla_prepare_q", *prepare_args(q_nope, q_pe, w_uk, q_lat, q_rots, shifts, pos, base, _stream()))
+    return q_lat, q_rots
+
+
 def out_uv(o_lat: torch.Tensor, w_uv: torch.Tensor, out: Optional[torch.Tensor] = None,
            out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
     n_tok, n_heads, d_c = o_lat.shape

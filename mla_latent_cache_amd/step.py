@@ -5,6 +5,8 @@
     rope_relocate_q (once per distinct segment shift) -> mla_absorb_q
     -> mla_decode_splitkv (all segments) -> mla_combine_lse -> mla_out_uv
 
+(the first two as one mla_prepare_q launch for up to 8 distinct shifts)
+
 and lays out the partial-state slots: segments with disjoint head ranges that
 follow each other share a slot range (e.g. a document read by the Local heads
 at a relocated position and its recomputed copy read by the Global heads),
@@ -130,9 +132,19 @@ class DecodeStep:
     def expand(self):
         ops.out_uv(self.o_lat, self.w_uv, out=self.out)
 
+    def prepare(self):
+        """rope (all shifts) and absorb in one launch (mla_prepare_q)."""
+        if len(self.q_rots) > 8:
+            self.rope()
+            self.absorb()
+            return
+        from . import _lib
+        _lib.call("mla_prepare_q", *ops.prepare_args(self.q_nope, self.q_pe, self.w_uk, self.q_lat,
+                                                      [r for _, r in self.q_rots], [s for s, _ in self.q_rots],
+                                                      self.q_pos, self.rope_base, ops._stream()))
+
     def run(self):
-        self.rope()
-        self.absorb()
+        self.prepare()
         self.decode()
         self.combine()
         self.expand()
@@ -146,18 +158,22 @@ class DecodeStep:
         lib = _lib.load()
         st = (stream or torch.cuda.current_stream()).cuda_stream
         dt = ops._dt
-        pre = []
-        for shift, q_rot in self.q_rots:
-            n_tok, H, d_r = self.q_pe.shape
-            pre.append((lib.rope_relocate_q, (self.q_pe.data_ptr(), dt(self.q_pe), q_rot.data_ptr(), dt(q_rot),
-                                              self.q_pos.data_ptr(), shift.data_ptr(), n_tok, H, d_r,
-                                              float(self.rope_base), st)))
         n_tok, H, d_nope = self.q_nope.shape
         d_c = self.w_uk.shape[2]
-        pre.append((lib.mla_absorb_q, (self.q_nope.data_ptr(), self.w_uk.data_ptr(), dt(self.q_nope),
-                                       self.q_lat.data_ptr(), dt(self.q_lat), n_tok, H, d_nope, d_c, st)))
+        d_r = self.q_pe.shape[2]
+        if len(self.q_rots) <= 8:  # one launch for rope (all shifts) and absorb
+            self._prep_args = ops.prepare_args(self.q_nope, self.q_pe, self.w_uk, self.q_lat,
+                                               [r for _, r in self.q_rots], [s for s, _ in self.q_rots],
+                                               self.q_pos, self.rope_base, st)
+            pre = [(lib.mla_prepare_q, self._prep_args)]
+        else:
+            pre = [(lib.rope_relocate_q, (self.q_pe.data_ptr(), dt(self.q_pe), q_rot.data_ptr(), dt(q_rot),
+                                          self.q_pos.data_ptr(), shift.data_ptr(), n_tok, H, d_r,
+                                          float(self.rope_base), st))
+                   for shift, q_rot in self.q_rots]
+            pre.append((lib.mla_absorb_q, (self.q_nope.data_ptr(), self.w_uk.data_ptr(), dt(self.q_nope),
+                                           self.q_lat.data_ptr(), dt(self.q_lat), n_tok, H, d_nope, d_c, st)))
         self._seg_arr = (_lib.MlaSegment * len(self.segments))(*[sg.to_c() for sg in self.segments])
-        d_r = self.segments[0].q_rot.shape[2]
         dec = [(lib.mla_decode_splitkv, (self._seg_arr, len(self.segments), self.q_lat.data_ptr(), dt(self.q_lat),
                                          dt(self.segments[0].cache), self.batch, self.s_q, H, d_c, d_r,
                                          float(self.scale), self.o_part.data_ptr(), self.lse_part.data_ptr(),

@@ -171,10 +171,42 @@ def test_absorb_and_out_uv_calls(dtype, dims):
         assert np.all(np.abs(f64(got) - ref) <= rel * np.abs(ref) + 1e-5 * rms), odt
 
 
-@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_combine_call(out_dtype):
+@pytest.mark.parametrize("dtype,dims", [(torch.float32, (4, 4, 2, 7)), (torch.bfloat16, (128, 512, 64, 33))])
+def test_prepare_call(dtype, dims):
+    """mla_prepare_q (rope for several shifts + absorb in one launch, or the
+    two kernels in turn off the MFMA path) gives exactly what the separate
+    calls give, and matches the oracle."""
     from mla_latent_cache_amd import ops
-    n_rows, n_part, d_c = 37, 5, 512
+    d_nope, d_c, d_r, n_tok = dims
+    H = 6
+    q = _rand((n_tok, H, d_nope), dtype, 21)
+    q_pe = _rand((n_tok, H, d_r), dtype, 22)
+    w = (_rand((H, d_nope, d_c), torch.float32, 23) / math.sqrt(d_c)).to(dtype)
+    g = torch.Generator().manual_seed(24)
+    pos = torch.randint(0, 262144, (n_tok,), generator=g, dtype=torch.int64)
+    shifts = [None] + [torch.randint(0, 200001, (n_tok,), generator=g, dtype=torch.int64) for _ in range(2)]
+    dq, dpe, dw, dpos = q.cuda(), q_pe.cuda(), w.cuda(), pos.cuda()
+    dsh = [None if s is None else s.cuda() for s in shifts]
+    q_lat, q_rots = ops.prepare_q(dq, dpe, dw, dpos, dsh, 10000.0, lat_dtype=torch.float32,
+                                  rot_dtype=torch.float32)
+    lat_sep = ops.absorb_q(dq, dw, out_dtype=torch.float32)
+    assert torch.equal(q_lat, lat_sep)
+    for s, r in zip(dsh, q_rots):
+        assert torch.equal(r, ops.rope_relocate_q(dpe, dpos, s, 10000.0, out_dtype=torch.float32))
+    ref = O.absorb_query(f64(w), f64(q))
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    assert np.all(np.abs(f64(q_lat) - ref) <= 1e-6 * np.abs(ref) + 1e-5 * rms)
+    for s, r in zip(shifts, q_rots):
+        ref_r = O.rope_relocate(f64(q_pe), pos.numpy(), np.zeros(n_tok, np.int64) if s is None else s.numpy(),
+                                10000.0)
+        assert np.abs(f64(r) - ref_r).max() <= 1e-5
+
+
+@pytest.mark.parametrize("out_dtype,n_rows", [(torch.float32, 37), (torch.bfloat16, 37), (torch.float32, 600),
+                                              (torch.float32, 1100)])
+def test_combine_call(out_dtype, n_rows):
+    from mla_latent_cache_amd import ops
+    n_part, d_c = 5, 512
     g = torch.Generator().manual_seed(12)
     o_part = torch.randn((n_rows, n_part, d_c), generator=g)
     lse_part = torch.randn((n_rows, n_part), generator=g) * 4
