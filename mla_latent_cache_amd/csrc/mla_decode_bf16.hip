@@ -63,6 +63,7 @@ constexpr int kSlotStride = kSlots + 2;     // 74: two pad slots per LDS row
 constexpr int kLRow = kSlotStride * 16;     // 1184 bytes per LDS row
 constexpr int kStageBytes = kTile * kLRow;
 constexpr int kNStage = 4;
+constexpr int kAhead = kNStage - 1;         // tiles in flight beyond the two being computed on
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kNDma = kTile * kSlotStride / 64;  // 37 wave-instructions per tile
@@ -73,8 +74,10 @@ constexpr int kPageSize = 64;
 constexpr int kMaxPieces = 64;
 constexpr int kKSteps = (kDc + kDr) / 32;   // 18 MFMA k-steps over [c | kr]
 
+// One piece of a workgroup's share: rows [r0, r1) of request b (T rows in
+// all) into partial slot `slot`; b and slot are packed (both < 2^16).
 struct Piece {
-  int b, r0, r1, slot;
+  int b_slot, r0, r1, T;
 };
 
 __device__ __forceinline__ int sload_i32(const int32_t* p) {
@@ -137,6 +140,31 @@ __device__ __forceinline__ void issue_dma_one(const TileDma& d, int k, int lane)
 
 constexpr int kLoaders = 4;  // waves issuing tile loads (the PV waves)
 constexpr int kDmaPerWave = (kNDma + kLoaders - 1) / kLoaders;  // 10 (wave 0), 9 (waves 1..3)
+
+// Byte offset inside a full tile of loader `ld`'s i-th instruction (k = ld +
+// 4 i) for this lane, or -1 where the lane's LDS slot is padding or k is past
+// the tile.  Fixed by the tile geometry, so computed once per wave.
+__device__ __forceinline__ int dma_lane_offset(int ld, int i, int lane) {
+  const int k = ld + kLoaders * i;
+  const int slotl = k * 64 + lane;
+  const int r = slotl / kSlotStride;
+  const int c = slotl - r * kSlotStride;
+  return (k < kNDma && c < kSlots) ? r * kRowBytes + c * 16 : -1;
+}
+
+// Loader `ld`'s i-th instruction of a tile: full tiles take the precomputed
+// offset (a uniform base plus a 32-bit lane offset, nothing else to compute),
+// a partial tile the bounds-checked path with zero fill.
+__device__ __forceinline__ void issue_dma_fast(const TileDma& d, int ld, int i, int off, int lane) {
+  const int k = ld + kLoaders * i;
+  if (d.lim == kTile * kRowBytes) {
+    if (off >= 0)
+      __builtin_amdgcn_global_load_lds((const void*)(d.src + (unsigned)off), (MLA_LDS void*)(d.dst + k * 1024), 16,
+                                       0, 0);
+  } else if (k < kNDma) {
+    issue_dma_one(d, k, lane);
+  }
+}
 
 // All of loader `ld`'s instructions of a tile at once.
 __device__ __forceinline__ void issue_tile_dma(const TileDma& d, int ld, int lane) {
@@ -246,30 +274,46 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
 
   // ---- plan pass 1: total and longest request, each padded to whole tiles ----
   // (a share then starts on a tile boundary of every request it touches, and
-  // no tile crosses a 64-row page)
+  // no tile crosses a 64-row page).  Only wave 0 plans; with B <= 64 it takes
+  // the totals from the same per-lane load its piece scan uses (one global
+  // round trip and no workgroup barrier before the scan).
   auto padT = [](int t) -> int { return (t + kTile - 1) / kTile * kTile; };
   int tsum = 0, tmax = 0;
-  for (int b = tid; b < B; b += kThreads) {
-    const int T = padT(clampT(seq_lens[b]));
-    tsum += T;
-    tmax = max(tmax, T);
-  }
+  int Tr_lane = 0;  // rows of request `lane` (wave 0, B <= 64)
+  if (B <= 64) {
+    if (wave == 0) {
+      Tr_lane = lane < B ? clampT(seq_lens[lane]) : 0;
+      tsum = padT(Tr_lane);
+      tmax = tsum;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    tsum += __shfl_xor(tsum, o);
-    tmax = max(tmax, __shfl_xor(tmax, o));
-  }
-  if (lane == 0) {
-    sm.red_i[wave] = tsum;
-    sm.red_i[kWaves + wave] = tmax;
-  }
-  __syncthreads();
-  tsum = 0;
-  tmax = 0;
+      for (int o = 32; o > 0; o >>= 1) {
+        tsum += __shfl_xor(tsum, o);
+        tmax = max(tmax, __shfl_xor(tmax, o));
+      }
+    }
+  } else {
+    for (int b = tid; b < B; b += kThreads) {
+      const int T = padT(clampT(seq_lens[b]));
+      tsum += T;
+      tmax = max(tmax, T);
+    }
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    tsum += sm.red_i[w];
-    tmax = max(tmax, sm.red_i[kWaves + w]);
+    for (int o = 32; o > 0; o >>= 1) {
+      tsum += __shfl_xor(tsum, o);
+      tmax = max(tmax, __shfl_xor(tmax, o));
+    }
+    if (lane == 0) {
+      sm.red_i[wave] = tsum;
+      sm.red_i[kWaves + wave] = tmax;
+    }
+    __syncthreads();
+    tsum = 0;
+    tmax = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      tsum += sm.red_i[w];
+      tmax = max(tmax, sm.red_i[kWaves + w]);
+    }
   }
   const bool req_mode = n_split == 1;
   int share = 0;
@@ -300,7 +344,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
     // ---- plan pass 2: wave 0 scans 64 requests, lists pieces, writes -inf tails ----
     if (wave == 0) {
       const int b = chunk * 64 + lane;
-      const int Tr = b < B ? clampT(seq_lens[b]) : 0;  // rows
+      const int Tr = B <= 64 ? Tr_lane : b < B ? clampT(seq_lens[b]) : 0;  // rows
       const int T = padT(Tr);                           // rows padded to whole tiles
       int incl = T;
 #pragma unroll
@@ -327,7 +371,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
       const uint64_t pm = __ballot(is_piece);
       if (is_piece) {
         const int pos = __popcll(pm & ((1ull << lane) - 1));
-        sm.pieces[pos] = Piece{b, r0, r1, slot};
+        sm.pieces[pos] = Piece{b | (slot << 16), r0, r1, Tr};
       }
       // slots a request does not use: lse = -inf (their o_part rows are never read)
       uint64_t tm = __ballot(tail);
@@ -359,11 +403,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
 
     for (int pi = 0; pi < n_pieces; ++pi) {
       const Piece pc = sm.pieces[pi];
-      const int b = __builtin_amdgcn_readfirstlane(pc.b);
+      const int b_slot = __builtin_amdgcn_readfirstlane(pc.b_slot);
+      const int b = b_slot & 0xffff;
+      const int slot = b_slot >> 16;
       const int pr0 = __builtin_amdgcn_readfirstlane(pc.r0);
       const int pr1 = __builtin_amdgcn_readfirstlane(pc.r1);
-      const int slot = __builtin_amdgcn_readfirstlane(pc.slot);
-      const int T = clampT(seq_lens[b]);
+      const int T = __builtin_amdgcn_readfirstlane(pc.T);
       const int vis_last = causal ? T - s_q + s_row : T - 1;  // last visible row of this lane's query
       const int vis_min = causal ? T - s_q + s_min : T - 1;   // ... of the group's first query row
       const int n_tiles = (pr1 - pr0 + kTile - 1) / kTile;
@@ -518,7 +563,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
         barrier_raw();
         score_tile(0);
         for (int it = 0; it < n_tiles; ++it) {
-          // before barrier `it`: P(it) is written; tile it+1 is in LDS (at most tile it+2 in flight)
+          // before barrier `it`: P(it) is written; tile it+1 is in LDS
           wait_lgkm0();
           barrier_raw();
           if (it + 1 < n_tiles) score_tile(it + 1);
@@ -536,9 +581,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
         barrier_raw();
       } else {
         // ---- PV wave (waves 4..7): 128 latent columns of all rows, and all tile loads ----
-        load_tile(0);
-        if (n_tiles > 1) load_tile(1);
-        if (n_tiles > 2) load_tile(2);
+        int doff[kDmaPerWave];  // this lane's offsets of the wave's loads of a full tile
+#pragma unroll
+        for (int i = 0; i < kDmaPerWave; ++i) doff[i] = dma_lane_offset(pw, i, lane);
+#pragma unroll
+        for (int t = 0; t < kAhead; ++t)
+          if (t < n_tiles) load_tile(t);
         f32x4 acc_o[8][NRB];
 #pragma unroll
         for (int db = 0; db < 8; ++db)
@@ -588,9 +636,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
 #pragma unroll
           for (int db = 0; db < 8; ++db) {
             if (with_dma) {  // load i = db, plus i = 8 at db 2 and i = 9 at db 5
-              issue_dma_one(dma, pw + kLoaders * db, lane);
-              if (db == 2) issue_dma_one(dma, pw + kLoaders * 8, lane);
-              if (db == 5 && pw + kLoaders * 9 < kNDma) issue_dma_one(dma, pw + kLoaders * 9, lane);
+              issue_dma_fast(dma, pw, db, doff[db], lane);
+              if (db == 2) issue_dma_fast(dma, pw, 8, doff[8], lane);
+              if (db == 5) issue_dma_fast(dma, pw, 9, doff[9], lane);
             }
 #pragma unroll
             for (int q = 0; q < NRB; ++q)
@@ -598,22 +646,22 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
           }
         };
 
-        // tile 0 must be in LDS; tiles 1, 2 may still be in flight
-        wait_tiles(pw, min(n_tiles - 1, 2), min(n_tiles - 1, 2) < n_tiles - 1 || last_full);
+        // tile 0 must be in LDS; tiles 1 .. kAhead-1 may still be in flight
+        wait_tiles(pw, min(n_tiles - 1, kAhead - 1), min(n_tiles - 1, kAhead - 1) < n_tiles - 1 || last_full);
         wait_lgkm0();
         barrier_raw();
         if constexpr (KS > 1) barrier_raw();  // the score waves' exchange of tile 0
         for (int it = 0; it < n_tiles; ++it) {
           // before barrier `it`: tile it+1 is in LDS (tile it+2 may be in flight)
           if (it + 1 < n_tiles) {
-            const int issued = min(it + 2, n_tiles - 1);
+            const int issued = min(it + kAhead - 1, n_tiles - 1);
             wait_tiles(pw, issued - (it + 1), issued < n_tiles - 1 || last_full);
           }
           wait_lgkm0();
           barrier_raw();
-          // tile it+3 goes into the stage of tile it-1, free after its PV
-          const bool with_dma = it + 3 < n_tiles;
-          const TileDma dma = with_dma ? tile_dma(it + 3) : TileDma{sm.stage[(it + 3) % kNStage], cache, 0};
+          // tile it+kAhead goes into the stage of tile it-1, free after its PV
+          const bool with_dma = it + kAhead < n_tiles;
+          const TileDma dma = with_dma ? tile_dma(it + kAhead) : TileDma{sm.stage[(it + kAhead) % kNStage], cache, 0};
           const int buf = it & 1;
           pv_tile(sm.stage[it % kNStage], sm.p[buf], sm.alpha[buf], sm.flag[buf], dma.dst, dma.src, dma.lim,
                   with_dma, KS > 1 && it + 1 < n_tiles);
