@@ -58,16 +58,19 @@ constexpr int kDc = 512;
 constexpr int kDr = 64;
 constexpr int kRowBytes = (kDc + kDr) * 2;  // 1152
 constexpr int kTile = 32;                   // cache rows per tile
-constexpr int kSlots = kRowBytes / 16;      // 72 16-byte chunks per row
-constexpr int kSlotStride = kSlots + 2;     // 74: two pad slots per LDS row
-constexpr int kLRow = kSlotStride * 16;     // 1184 bytes per LDS row
-constexpr int kStageBytes = kTile * kLRow;
-constexpr int kNStage = 4;
+constexpr int kCBytes = kDc * 2;            // 1024: latent part c_t of a row
+constexpr int kRBytes = kDr * 2;            // 128: rotary part kr_t of a row
+constexpr int kCStage = kTile * kCBytes;    // latent ring stage (32 KiB)
+constexpr int kRStage = kTile * kRBytes;    // rotary ring stage (4 KiB)
+constexpr int kNStage = 4;                  // latent ring: read by the score waves, then the PV waves
 constexpr int kAhead = kNStage - 1;         // tiles in flight beyond the two being computed on
+constexpr int kNRStage = kAhead;            // rotary ring: dead once its tile is scored
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-constexpr int kNDma = kTile * kSlotStride / 64;  // 37 wave-instructions per tile
-static_assert(kTile * kSlotStride == kNDma * 64, "a tile fills whole DMA instructions");
+// wave-instructions per tile: one per latent row (64 lanes x 16 B), then 4
+// for the rotary parts (8 rows x 8 chunks each)
+constexpr int kNDma = kTile + kRStage / 1024;
+static_assert(kNDma == 36 && kRStage % 1024 == 0, "tile geometry");
 constexpr int kPStr = 80;                   // bytes per P row (32 bf16 + pad)
 constexpr float kTau = 8.f;
 constexpr int kPageSize = 64;
@@ -105,63 +108,69 @@ __device__ __forceinline__ float rows_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// LDS layout of a tile (no padding, 16-byte chunks XOR-swizzled per row):
+// latent row r holds chunk c (0..63) at position c ^ (r & 15), rotary row r
+// chunk j (0..7) at position j ^ ((r >> 1) & 7).  A score-operand read (16
+// consecutive rows, one chunk) and a transposed read then touch 16 distinct
+// bank groups, like a padded layout, while the tile fits in 36 KiB.
+__device__ __forceinline__ int cpos(int r, int c) { return c ^ (r & 15); }
+__device__ __forceinline__ int rpos(int r, int j) { return j ^ ((r >> 1) & 7); }
+
 // Loads of one tile: `lim` bytes (whole rows) that are contiguous in memory
 // from `src` (tiles are aligned to 32 rows inside a request and never cross a
-// 64-row page).  Wave-instruction k (0 <= k < 37) covers LDS slots 64 k ..
-// 64 k + 63 (74 slots of 16 B per LDS row, slots 72 and 73 are padding); lane
-// `lane` moves the 16-byte chunk (row r, chunk c), byte offset r * 1152 +
-// c * 16.  Rows past the valid ones are zero-filled so no stale value is ever
-// read.  The four PV waves issue all tile loads: loader l = wave - 4 issues
-// k = l + 4 i, i < 10 (9 for l = 1..3).  An LDS-direct load keeps its wave
-// busy for ~60 cycles at issue, so the score waves, which set the pace, issue
-// none.
+// 64-row page).  Wave-instruction k < 32 fills latent LDS row k: lane l moves
+// the chunk stored at position l, cache bytes k * 1152 + (l ^ (k & 15)) * 16.
+// k = 32..35 fill rotary rows 8 (k - 32) + l / 8 at position l % 8.  Rows past
+// the valid ones are zero-filled so no stale value is ever read.  The four PV
+// waves issue all tile loads: loader l = wave - 4 issues k = l + 4 i, i < 9.
+// An LDS-direct load keeps its wave busy at issue, so the score waves, which
+// set the pace, issue none.
 struct TileDma {
-  char* dst;        // LDS stage
+  char* cdst;       // latent ring stage
+  char* rdst;       // rotary ring stage
   const char* src;  // first cache byte of the tile
   int lim;          // valid bytes at src
 };
+
+// Cache byte offset (within the tile) and LDS destination of instruction k for this lane.
+__device__ __forceinline__ int dma_src_off(int k, int lane) {
+  if (k < kTile) return k * kRowBytes + cpos(k, lane) * 16;
+  const int r = 8 * (k - kTile) + (lane >> 3);
+  return r * kRowBytes + kCBytes + rpos(r, lane & 7) * 16;
+}
+__device__ __forceinline__ char* dma_dst(const TileDma& d, int k) {
+  return k < kTile ? d.cdst + k * 1024 : d.rdst + (k - kTile) * 1024;
+}
 
 __device__ __forceinline__ void issue_dma_one(const TileDma& d, int k, int lane) {
   // Opaque copy of the lane index: the offsets are recomputed at every
   // instruction (a few integer ops) instead of being hoisted out of the tile
   // loop and pinning registers for the whole loop.
   asm volatile("" : "+v"(lane));
-  const int slotl = k * 64 + lane;
-  const int r = slotl / kSlotStride;
-  const int c = slotl - r * kSlotStride;
-  const int off = r * kRowBytes + c * 16;
-  const bool in_tile = c < kSlots;
-  if (in_tile && off < d.lim) {
-    __builtin_amdgcn_global_load_lds((const void*)(d.src + off), (MLA_LDS void*)(d.dst + k * 1024), 16, 0, 0);
-  } else if (in_tile) {
-    *(int4*)(d.dst + slotl * 16) = int4{0, 0, 0, 0};
+  const int off = dma_src_off(k, lane);
+  char* dst = dma_dst(d, k);
+  if (off < d.lim) {  // the lane's row is a valid row of the tile
+    __builtin_amdgcn_global_load_lds((const void*)(d.src + off), (MLA_LDS void*)dst, 16, 0, 0);
+  } else {
+    *(int4*)(dst + lane * 16) = int4{0, 0, 0, 0};
   }
 }
 
 constexpr int kLoaders = 4;  // waves issuing tile loads (the PV waves)
-constexpr int kDmaPerWave = (kNDma + kLoaders - 1) / kLoaders;  // 10 (wave 0), 9 (waves 1..3)
+constexpr int kDmaPerWave = kNDma / kLoaders;  // 9
+static_assert(kNDma % kLoaders == 0, "every loader issues the same count");
 
-// Byte offset inside a full tile of loader `ld`'s i-th instruction (k = ld +
-// 4 i) for this lane, or -1 where the lane's LDS slot is padding or k is past
-// the tile.  Fixed by the tile geometry, so computed once per wave.
-__device__ __forceinline__ int dma_lane_offset(int ld, int i, int lane) {
-  const int k = ld + kLoaders * i;
-  const int slotl = k * 64 + lane;
-  const int r = slotl / kSlotStride;
-  const int c = slotl - r * kSlotStride;
-  return (k < kNDma && c < kSlots) ? r * kRowBytes + c * 16 : -1;
-}
-
-// Loader `ld`'s i-th instruction of a tile: full tiles take the precomputed
-// offset (a uniform base plus a 32-bit lane offset, nothing else to compute),
-// a partial tile the bounds-checked path with zero fill.
-__device__ __forceinline__ void issue_dma_fast(const TileDma& d, int ld, int i, int off, int lane) {
+// Loader `ld`'s i-th instruction of a tile (k = ld + 4 i): a full tile
+// issues it from a uniform base plus a lane offset of two or three integer
+// ops (no bounds check, every lane valid), a partial tile takes the
+// bounds-checked path with zero fill.  `lane` should be opaque to the
+// compiler, or it hoists the nine offsets into live registers.
+__device__ __forceinline__ void issue_dma_fast(const TileDma& d, int ld, int i, int lane) {
   const int k = ld + kLoaders * i;
   if (d.lim == kTile * kRowBytes) {
-    if (off >= 0)
-      __builtin_amdgcn_global_load_lds((const void*)(d.src + (unsigned)off), (MLA_LDS void*)(d.dst + k * 1024), 16,
-                                       0, 0);
-  } else if (k < kNDma) {
+    __builtin_amdgcn_global_load_lds((const void*)(d.src + (unsigned)dma_src_off(k, lane)),
+                                     (MLA_LDS void*)dma_dst(d, k), 16, 0, 0);
+  } else {
     issue_dma_one(d, k, lane);
   }
 }
@@ -169,10 +178,7 @@ __device__ __forceinline__ void issue_dma_fast(const TileDma& d, int ld, int i, 
 // All of loader `ld`'s instructions of a tile at once.
 __device__ __forceinline__ void issue_tile_dma(const TileDma& d, int ld, int lane) {
 #pragma unroll
-  for (int i = 0; i < kDmaPerWave; ++i) {
-    const int k = ld + kLoaders * i;
-    if (k < kNDma) issue_dma_one(d, k, lane);
-  }
+  for (int i = 0; i < kDmaPerWave; ++i) issue_dma_one(d, ld + kLoaders * i, lane);
 }
 
 // First byte of tile rows [t0, ...) of request b: contiguous cache, or the
@@ -190,11 +196,14 @@ __device__ __forceinline__ const char* tile_src(const char* cache, const char* r
 template <int MT>
 struct Smem {
   static constexpr int NRB = MT / 16;
-  static constexpr int KS = 4 / NRB;  // k-parts per 16-row block (score waves 0..3)
-  char stage[kNStage][kStageBytes];
+  static constexpr int QBW = NRB == 4 ? 2 : 1;  // 16-row blocks per score wave
+  static constexpr int KS = 4 / (NRB / QBW);    // k-parts (score waves) per group of QBW blocks
+  char cst[kNStage][kCStage];   // latent ring
+  char rst[kNRStage][kRStage];  // rotary ring
   char p[2][MT * kPStr];
-  // partial scores of k-parts 1..KS-1 of each row block: [part][tb][lane][4]
-  float xbuf[KS > 1 ? NRB * (KS - 1) * 2 * 64 * 4 : 1];
+  // exchanged partial scores [slot][tb][lane][4]: QBW = 1, k-parts 1..KS-1 of each
+  // row block; QBW = 2, the partner's k-part of each row block
+  float xbuf[(QBW == 1 ? NRB * (KS - 1) : NRB) * 2 * 64 * 4];
   float alpha[2][MT];
   float rowinv[MT];
   int flag[2][4];
@@ -207,14 +216,13 @@ struct Smem {
 // Loader `ld`: wait until at most `after` tiles issued after the needed one
 // are still in flight; `after_full` says they are all full tiles (a partial
 // tile issues fewer instructions, then everything is waited for).
-__device__ __forceinline__ void wait_tiles(int ld, int after, bool after_full) {
-  static_assert(kNDma == kLoaders * (kDmaPerWave - 1) + 1, "loader 0 issues one more than loaders 1..3");
+__device__ __forceinline__ void wait_tiles(int after, bool after_full) {
   if (!after_full || after == 0) {
     wait_vmcnt<0>();
-  } else if (ld == 0) {
-    if (after == 1) wait_vmcnt<kDmaPerWave>(); else wait_vmcnt<2 * kDmaPerWave>();
+  } else if (after == 1) {
+    wait_vmcnt<kDmaPerWave>();
   } else {
-    if (after == 1) wait_vmcnt<kDmaPerWave - 1>(); else wait_vmcnt<2 * (kDmaPerWave - 1)>();
+    wait_vmcnt<2 * kDmaPerWave>();
   }
 }
 
@@ -226,7 +234,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
                                                                   int rows_total) {
   constexpr int NQH = QF32 ? 2 : 1;  // query parts (hi, lo)
   constexpr int NRB = MT / 16;       // 16-row blocks
-  constexpr int KS = 4 / NRB;        // score waves per row block, each with a part of the 18 k-steps
+  // Score waves 0..3 form NRB / QBW groups; a group's KS waves multiply its
+  // QBW row blocks, each over a part of the 18 k-steps, and add their partial
+  // scores through LDS.  MT = 16: 1 group of 4 waves (one block, four k-parts);
+  // MT = 32: 2 groups of 2; MT = 64: 2 groups of 2 waves that each multiply
+  // two blocks over half the k-steps, so each K operand read from LDS serves
+  // 32 query rows (half the LDS traffic of one block per wave).
+  constexpr int QBW = NRB == 4 ? 2 : 1;
+  constexpr int KS = 4 / (NRB / QBW);
   constexpr int KMAX = (kKSteps + KS - 1) / KS;
   __shared__ __attribute__((aligned(16))) Smem<MT> sm;
 
@@ -327,11 +342,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
   // ---- roles: waves 0..3 score (row block rb, k-part kp); waves 4..7 own 128 latent columns each ----
   const bool qk_wave = wave < 4;
   const bool pv_wave = wave >= 4;
-  const int rb = (wave & 3) / KS;    // 16-row block of a score wave
+  const int grp = (wave & 3) / KS;   // group of a score wave: row blocks grp * QBW ..
   const int kp = (wave & 3) % KS;    // its part of the k-steps: [ks0, ks0 + kcnt)
   const int kcnt = kKSteps / KS + (kp < kKSteps % KS ? 1 : 0);
   const int ks0 = kp * (kKSteps / KS) + min(kp, kKSteps % KS);
-  const int qrow = rb * 16 + l16;    // local row of this lane (score waves)
+  // the row block whose softmax this wave runs (QBW = 1: only k-part 0 runs one)
+  const int rb = QBW == 1 ? grp : grp * QBW + kp;
+  const bool smax_wave = QBW > 1 || kp == 0;
+  const int qrow = rb * 16 + l16;    // local softmax row of this lane (score waves)
   const bool rvalid = qk_wave && qrow < nrows;
   const int Rc = rvalid ? row0 + qrow : row0;
   const int s_row = Rc / hc;
@@ -421,7 +439,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
         const int t0 = pr0 + it * kTile;
         bool ok;
         const char* src = tile_src(cache, req_base, bt_row, n_pages, t0, &ok);
-        return TileDma{sm.stage[it % kNStage], src, ok ? min(kTile, pr1 - t0) * kRowBytes : 0};
+        return TileDma{sm.cst[it % kNStage], sm.rst[it % kNRStage], src, ok ? min(kTile, pr1 - t0) * kRowBytes : 0};
       };
       auto load_tile = [&](int it) { issue_tile_dma(tile_dma(it), wave - 4, lane); };
 
@@ -430,14 +448,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
       // per scored tile when KS > 1), so the register allocator never holds
       // the query block and the O accumulator at once.
       if (qk_wave) {
-        // ---- score wave: 16 query rows (row block rb), k-steps [ks0, ks0 + kcnt), hi and lo parts ----
-        bf16x8 qreg[NQH][KMAX];
-        {
-          const int64_t qi = (int64_t)b * s_q * n_heads + q_off;
+        // ---- score wave: row blocks grp * QBW .. + QBW-1, k-steps [ks0, ks0 + kcnt), hi and lo parts ----
+        bf16x8 qreg[NQH][QBW][KMAX];
+#pragma unroll
+        for (int j = 0; j < QBW; ++j) {
+          const int row = (grp * QBW + j) * 16 + l16;
+          const int Rj = row0 + row;
+          const int64_t qi = (int64_t)b * s_q * n_heads + (int64_t)(Rj / hc) * n_heads + head_begin + Rj % hc;
 #pragma unroll
           for (int i = 0; i < KMAX; ++i) {
             const int k0 = 32 * (ks0 + i) + 8 * lg;
-            const bool in = rvalid && i < kcnt;
+            const bool in = row < nrows && i < kcnt;
             if constexpr (QF32) {
               f32x4 v0 = f32x4{0.f, 0.f, 0.f, 0.f}, v1 = v0;
               if (in) {
@@ -450,13 +471,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
               for (int e = 0; e < 8; ++e) {
                 const float v = e < 4 ? v0[e] : v1[e - 4];
                 const bf16 h = (bf16)v;
-                qreg[0][i][e] = h;
-                qreg[1][i][e] = (bf16)(v - (float)h);
+                qreg[0][j][i][e] = h;
+                qreg[1][j][i][e] = (bf16)(v - (float)h);
               }
             } else {
-              qreg[0][i] = in ? (k0 < kDc ? *(const bf16x8*)((const bf16*)q_lat_p + qi * kDc + k0)
-                                          : *(const bf16x8*)((const bf16*)q_rot_p + qi * kDr + (k0 - kDc)))
-                              : bf16x8{};
+              qreg[0][j][i] = in ? (k0 < kDc ? *(const bf16x8*)((const bf16*)q_lat_p + qi * kDc + k0)
+                                             : *(const bf16x8*)((const bf16*)q_rot_p + qi * kDr + (k0 - kDc)))
+                                 : bf16x8{};
             }
           }
         }
@@ -467,57 +488,107 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
         // With KS > 1 the waves of a row block exchange partial scores through
         // LDS (one extra barrier) and k-part 0 runs the softmax.
         auto score_tile = [&](int it) {
-          const char* st = sm.stage[it % kNStage];
+          const char* cs = sm.cst[it % kNStage];
+          const char* rs = sm.rst[it % kNRStage];
           const int t0 = pr0 + it * kTile;
           const int buf = it & 1;
-          f32x4 sacc[2][NQH];
+          // accumulators: hi and lo parts separately with one row block (two
+          // independent chains would stall on each other), shared with two
+          // (four chains already, and half the registers)
+          constexpr int NACC = QBW == 1 ? NQH : 1;
+          f32x4 sacc[2][QBW][NACC];
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-            for (int hl = 0; hl < NQH; ++hl) sacc[tb][hl] = f32x4{0.f, 0.f, 0.f, 0.f};
-          // K operands are read two k-steps ahead of their MFMAs
-          constexpr int kPre = 2;
-          const char* ap = st + l16 * kLRow + lg * 16 + ks0 * 64;
+            for (int j = 0; j < QBW; ++j)
+#pragma unroll
+              for (int hl = 0; hl < NACC; ++hl) sacc[tb][j][hl] = f32x4{0.f, 0.f, 0.f, 0.f};
+          // K operand of key block tb, k-step ks: row r = 16 tb + l16, chunk
+          // 4 ks + lg (latent for ks < 16, rotary after), at its swizzled
+          // position.  With xh = l16 >> 2 < 4: cpos(r, 4 ks + lg) * 16 =
+          // ((ks ^ xh) << 6) + ((lg ^ l16) & 3) * 16, and (ks0 + i) ^ xh =
+          // ((ks0 + (i & 3)) ^ xh) + 4 (i >> 2); so four per-lane bases cover
+          // every k-step, the rest is an immediate offset.  rpos(r, j) = j ^
+          // ((l16 >> 1) & 7).  The swizzle key is opaque per tile so these
+          // bases are recomputed per tile rather than held across the loop.
+          int xs = l16;
+          asm volatile("" : "+v"(xs));
+          const char* cbase = cs + l16 * kCBytes + (((lg ^ xs) & 3) << 4);
+          const char* cb4[4];
+#pragma unroll
+          for (int n = 0; n < 4; ++n) cb4[n] = cbase + (((ks0 + n) ^ (xs >> 2)) << 6);
+          const char* rbase = rs + l16 * kRBytes;
+          const int xr = (xs >> 1) & 7;
+          auto kop = [&](int i, int tb) -> bf16x8 {  // k-step ks0 + i
+            if (ks0 + i < kDc / 32) return *(const bf16x8*)(cb4[i & 3] + tb * 16 * kCBytes + (i >> 2) * 256);
+            return *(const bf16x8*)(rbase + tb * 16 * kRBytes + (((4 * (ks0 + i - kDc / 32) + lg) ^ xr) << 4));
+          };
+          // K operands are read kPre k-steps ahead of their MFMAs (one with two
+          // row blocks per wave: eight MFMAs per k-step hide the read, and the
+          // registers are needed for the query)
+          constexpr int kPre = QBW == 2 ? 1 : 2;
           bf16x8 ak[kPre + 1][2];
 #pragma unroll
           for (int i = 0; i < kPre; ++i)
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb) ak[i][tb] = *(const bf16x8*)(ap + 16 * tb * kLRow + i * 64);
+            for (int tb = 0; tb < 2; ++tb) ak[i][tb] = kop(i, tb);
 #pragma unroll
           for (int i = 0; i < KMAX; ++i) {
             if (i < kcnt) {
               if (i + kPre < kcnt) {
 #pragma unroll
-                for (int tb = 0; tb < 2; ++tb)
-                  ak[(i + kPre) % (kPre + 1)][tb] = *(const bf16x8*)(ap + 16 * tb * kLRow + (i + kPre) * 64);
+                for (int tb = 0; tb < 2; ++tb) ak[(i + kPre) % (kPre + 1)][tb] = kop(i + kPre, tb);
               }
 #pragma unroll
-              for (int tb = 0; tb < 2; ++tb)
+              for (int hl = 0; hl < NQH; ++hl)
 #pragma unroll
-                for (int hl = 0; hl < NQH; ++hl)
-                  sacc[tb][hl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[i % (kPre + 1)][tb], qreg[hl][i],
-                                                                        sacc[tb][hl], 0, 0, 0);
+                for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                  for (int j = 0; j < QBW; ++j)
+                    sacc[tb][j][hl % NACC] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        ak[i % (kPre + 1)][tb], qreg[hl][j][i], sacc[tb][j][hl % NACC], 0, 0, 0);
             }
           }
-          f32x4 sa = sacc[0][0], sb = sacc[1][0];
-          if constexpr (QF32) {
-            sa += sacc[0][1];
-            sb += sacc[1][1];
-          }
-          if constexpr (KS > 1) {
-            f32x4* xb = (f32x4*)sm.xbuf;  // [part][tb][lane]
-            if (kp > 0) {
-              xb[((rb * (KS - 1) + kp - 1) * 2 + 0) * 64 + lane] = sa;
-              xb[((rb * (KS - 1) + kp - 1) * 2 + 1) * 64 + lane] = sb;
+          f32x4 sc[2][QBW];  // partial scores of this wave's k-part
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int j = 0; j < QBW; ++j) {
+              sc[tb][j] = sacc[tb][j][0];
+              if constexpr (NACC > 1) sc[tb][j] += sacc[tb][j][1];
             }
+          f32x4 sa, sb;  // scores of the softmax block rb, all k-steps
+          f32x4* xb = (f32x4*)sm.xbuf;  // [slot][tb][lane]
+          if constexpr (QBW == 1) {
+            sa = sc[0][0];
+            sb = sc[1][0];
+            if constexpr (KS > 1) {
+              // k-parts 1.. of the block write, k-part 0 adds them in order
+              if (kp > 0) {
+                xb[((rb * (KS - 1) + kp - 1) * 2 + 0) * 64 + lane] = sa;
+                xb[((rb * (KS - 1) + kp - 1) * 2 + 1) * 64 + lane] = sb;
+              }
+              wait_lgkm0();
+              barrier_raw();
+              if (kp > 0) return;
+#pragma unroll
+              for (int j = 0; j < KS - 1; ++j) {
+                sa += xb[((rb * (KS - 1) + j) * 2 + 0) * 64 + lane];
+                sb += xb[((rb * (KS - 1) + j) * 2 + 1) * 64 + lane];
+              }
+            }
+          } else {
+            // two k-parts of a group of two blocks: each wave hands its partner
+            // its partial of the partner's block and adds the partner's partial
+            // of its own (part 0 + part 1 either way, so bitwise identical)
+            static_assert(KS == 2 && QBW == 2, "pair layout");
+            const int ob = grp * 2 + (1 - kp);  // the partner's block
+            xb[(ob * 2 + 0) * 64 + lane] = kp == 0 ? sc[0][1] : sc[0][0];
+            xb[(ob * 2 + 1) * 64 + lane] = kp == 0 ? sc[1][1] : sc[1][0];
             wait_lgkm0();
             barrier_raw();
-            if (kp > 0) return;
-#pragma unroll
-            for (int j = 0; j < KS - 1; ++j) {
-              sa += xb[((rb * (KS - 1) + j) * 2 + 0) * 64 + lane];
-              sb += xb[((rb * (KS - 1) + j) * 2 + 1) * 64 + lane];
-            }
+            sa = (kp == 0 ? sc[0][0] : sc[0][1]) + xb[(rb * 2 + 0) * 64 + lane];
+            sb = (kp == 0 ? sc[1][0] : sc[1][1]) + xb[(rb * 2 + 1) * 64 + lane];
           }
           sa *= sl2;
           sb *= sl2;
@@ -570,7 +641,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
         }
         // epilogue: lse and 1/l of this row block's rows (k-part 0)
         const float lt = rows_sum(l_part);
-        if (kp == 0 && lg == 0) {
+        if (smax_wave && lg == 0) {
           sm.rowinv[qrow] = lt > 0.f ? 1.f / lt : 0.f;
           if (rvalid) {
             const int64_t ri = (int64_t)b * s_q * n_heads + q_off;
@@ -581,9 +652,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
         barrier_raw();
       } else {
         // ---- PV wave (waves 4..7): 128 latent columns of all rows, and all tile loads ----
-        int doff[kDmaPerWave];  // this lane's offsets of the wave's loads of a full tile
-#pragma unroll
-        for (int i = 0; i < kDmaPerWave; ++i) doff[i] = dma_lane_offset(pw, i, lane);
 #pragma unroll
         for (int t = 0; t < kAhead; ++t)
           if (t < n_tiles) load_tile(t);
@@ -601,18 +669,29 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
         // them wait for every load in flight.
         auto pv_tile = [&](const char* __restrict__ st, const char* __restrict__ pbuf,
                            const float* __restrict__ alph, const int* __restrict__ flg,
-                           char* __restrict__ dma_dst, const char* dma_src, int dma_lim, bool with_dma,
-                           bool with_x) {
-          const TileDma dma{dma_dst, dma_src, dma_lim};
+                           char* __restrict__ dma_cdst, char* __restrict__ dma_rdst, const char* dma_src,
+                           int dma_lim, bool with_dma, bool with_x) {
+          const TileDma dma{dma_cdst, dma_rdst, dma_src, dma_lim};
           // all C^T operands of the tile first (16 transposed reads in flight),
           // then P, the rescale flags and factors
           const int rq = l16 >> 2, qq = lane & 3;
           bf16x8 ac[8];
-          const char* p0 = st + (8 * lg + rq) * kLRow + (128 * pw + 4 * qq) * 2;
+          // lane (16 lg + 4 rq + qq) reads 4 bf16 of rows r0 = 8 lg + rq and r0 + 4
+          // at latent column 128 pw + 16 db + 4 qq, i.e. chunk c = 16 pw + 2 db +
+          // qq / 2; with x = r & 15 (< 16, bit 2 clear for r0):
+          // cpos(r, c) = 16 pw + 2 (db ^ (x >> 1)) + ((qq >> 1) ^ (x & 1)).
+          // The swizzle key is opaque per tile (no hoisted addresses).
+          const int r0 = 8 * lg + rq;
+          int x0 = r0 & 15;
+          asm volatile("" : "+v"(x0));
+          const int x1 = x0 ^ 4;  // (r0 + 4) & 15
+          const char* p0 = st + r0 * kCBytes + 256 * pw + 8 * (qq & 1) + (((qq >> 1) ^ (x0 & 1)) << 4);
+          const char* p1 = st + (r0 + 4) * kCBytes + 256 * pw + 8 * (qq & 1) + (((qq >> 1) ^ (x1 & 1)) << 4);
+          const int h0 = x0 >> 1, h1 = x1 >> 1;
 #pragma unroll
           for (int db = 0; db < 8; ++db) {
-            const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p0 + 32 * db));
-            const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p0 + 32 * db + 4 * kLRow));
+            const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p0 + ((db ^ h0) << 5)));
+            const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p1 + ((db ^ h1) << 5)));
             ac[db] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
           }
           int flag = 0;
@@ -621,9 +700,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
           bf16x8 bq[NRB];
 #pragma unroll
           for (int q = 0; q < NRB; ++q) bq[q] = *(const bf16x8*)(pbuf + (16 * q + l16) * kPStr + lg * 16);
-          // the score waves' mid-tile exchange barrier (their next tile), with this
-          // tile's reads in flight
-          if (with_x) barrier_raw();
+          // five of this wave's loads of a later tile while those reads are in
+          // flight (an LDS-direct load holds the wave at issue), the other four
+          // between the MFMAs
+          int dlane = lane;
+          asm volatile("" : "+v"(dlane));
+          if (with_dma) {
+#pragma unroll
+            for (int i = 0; i < 5; ++i) issue_dma_fast(dma, pw, i, dlane);
+          }
+
           if (flag) {
 #pragma unroll
             for (int q = 0; q < NRB; ++q) {
@@ -632,14 +718,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
               for (int db = 0; db < 8; ++db) acc_o[db][q] *= al;
             }
           }
-          // the MFMAs, with this wave's loads issued between them
+          // the MFMAs, with loads 5..8 issued between them
 #pragma unroll
           for (int db = 0; db < 8; ++db) {
-            if (with_dma) {  // load i = db, plus i = 8 at db 2 and i = 9 at db 5
-              issue_dma_fast(dma, pw, db, doff[db], lane);
-              if (db == 2) issue_dma_fast(dma, pw, 8, doff[8], lane);
-              if (db == 5) issue_dma_fast(dma, pw, 9, doff[9], lane);
-            }
+            // the score waves' mid-tile exchange barrier (their next tile): half
+            // of this tile's MFMAs and loads overlap their QK, half their softmax
+            if (db == 4 && with_x) barrier_raw();
+            if (with_dma && db % 2 == 0) issue_dma_fast(dma, pw, 5 + db / 2, dlane);
 #pragma unroll
             for (int q = 0; q < NRB; ++q)
               acc_o[db][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ac[db], bq[q], acc_o[db][q], 0, 0, 0);
@@ -647,7 +732,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
         };
 
         // tile 0 must be in LDS; tiles 1 .. kAhead-1 may still be in flight
-        wait_tiles(pw, min(n_tiles - 1, kAhead - 1), min(n_tiles - 1, kAhead - 1) < n_tiles - 1 || last_full);
+        wait_tiles(min(n_tiles - 1, kAhead - 1), min(n_tiles - 1, kAhead - 1) < n_tiles - 1 || last_full);
         wait_lgkm0();
         barrier_raw();
         if constexpr (KS > 1) barrier_raw();  // the score waves' exchange of tile 0
@@ -655,16 +740,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
           // before barrier `it`: tile it+1 is in LDS (tile it+2 may be in flight)
           if (it + 1 < n_tiles) {
             const int issued = min(it + kAhead - 1, n_tiles - 1);
-            wait_tiles(pw, issued - (it + 1), issued < n_tiles - 1 || last_full);
+            wait_tiles(issued - (it + 1), issued < n_tiles - 1 || last_full);
           }
           wait_lgkm0();
           barrier_raw();
           // tile it+kAhead goes into the stage of tile it-1, free after its PV
           const bool with_dma = it + kAhead < n_tiles;
-          const TileDma dma = with_dma ? tile_dma(it + kAhead) : TileDma{sm.stage[(it + kAhead) % kNStage], cache, 0};
+          const TileDma dma = with_dma ? tile_dma(it + kAhead)
+                                       : TileDma{sm.cst[(it + kAhead) % kNStage], sm.rst[(it + kAhead) % kNRStage], cache, 0};
           const int buf = it & 1;
-          pv_tile(sm.stage[it % kNStage], sm.p[buf], sm.alpha[buf], sm.flag[buf], dma.dst, dma.src, dma.lim,
-                  with_dma, KS > 1 && it + 1 < n_tiles);
+          pv_tile(sm.cst[it % kNStage], sm.p[buf], sm.alpha[buf], sm.flag[buf], dma.cdst, dma.rdst, dma.src,
+                  dma.lim, with_dma, KS > 1 && it + 1 < n_tiles);
         }
         wait_lgkm0();
         barrier_raw();
