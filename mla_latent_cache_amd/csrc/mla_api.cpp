@@ -237,6 +237,8 @@ mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q
         return fail(MLA_ERR_ALIGN, "segment %d: cache and q_rot must be 16-byte aligned", g);
       if ((int64_t)s_q * s.head_count > 512)
         return fail(MLA_ERR_UNSUPPORTED, "segment %d: s_q * head_count = %d > 512", g, s_q * s.head_count);
+      if (batch > 65535 || s.n_split > 65535)
+        return fail(MLA_ERR_UNSUPPORTED, "segment %d: bf16 path needs batch and n_split <= 65535", g);
     } else if ((int64_t)batch * s_q * s.head_count > 65535 || s.n_split > 65535) {
       return fail(MLA_ERR_UNSUPPORTED, "segment %d: fp32 path grid too large", g);
     }

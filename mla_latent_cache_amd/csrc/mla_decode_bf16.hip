@@ -12,26 +12,35 @@
 //  * One workgroup of 8 waves (2 per SIMD) owns up to MT = 64 query rows (all
 //    heads of a request for the segment, or a 64-row group of them) and
 //    streams 32-row tiles of cache rows [c_t | kr_t] (576 bf16 = 1152 B)
-//    HBM -> LDS with direct-to-LDS loads into a 4-stage ring (3 tiles in
-//    flight).  Every tile is read from HBM once and shared by all MT query
-//    rows: the latent serves every head's key and value.
-//  * LDS rows are padded to 74 slots of 16 B (1184 B): the 16-row operand
-//    reads of the score MFMAs then run without bank conflicts.
-//  * Wave roles, one tile apart: score waves 0..3 hold the query of a 16-row
-//    block in registers and compute S^T[tokens x rows] = K_tile .
-//    [q_lat|q_rot]^T of tile it+1 on v_mfma_f32_16x16x32_bf16, the online
-//    softmax and P (bf16, in LDS).  With MT = 64 each score wave owns one row
-//    block and all 18 k-steps; with MT = 32 / 16 the 2 / 4 waves of a row
-//    block split the k-steps, add their partial scores through LDS (one extra
-//    barrier per tile) and the first of them runs the softmax, which shortens
-//    the per-tile latency of small head counts.  PV waves 4..7 each own 128 latent columns
-//    and accumulate O^T[d x rows] += C_tile^T . P^T of tile it, with C^T from
-//    ds_read_b64_tr_b16 transposed LDS reads.  The PV waves also issue all
-//    tile loads (spread between their MFMAs): an LDS-direct load holds its
-//    wave for tens of cycles at issue, and the score waves set the pace.
-//  * The query arrives in fp32 and is split into bf16 hi + lo parts (q = hi +
-//    lo to ~2^-17): two MFMAs per k-step into separate accumulators.  A
-//    bf16-rounded query would put ~1e-3 error into the scores.
+//    HBM -> LDS with direct-to-LDS loads: latent parts into a 4-stage ring,
+//    rotary parts into a 3-stage ring (3 tiles in flight).  Every tile is read
+//    from HBM once and shared by all MT query rows: the latent serves every
+//    head's key and value.
+//  * LDS tiles are unpadded (36 KiB) with 16-byte chunks XOR-swizzled per row,
+//    so the 16-row score-operand reads and the transposed reads are free of
+//    bank conflicts.
+//  * Wave roles, one tile apart: score waves 0..3 hold the query in registers
+//    and compute S^T[tokens x rows] = K_tile . [q_lat|q_rot]^T of tile it+1 on
+//    v_mfma_f32_16x16x32_bf16, the online softmax and P (bf16, in LDS).  The
+//    score waves of a group split the 18 k-steps and add their partial scores
+//    through LDS (one exchange barrier per tile): MT = 16, one group of four
+//    k-parts; MT = 32, two groups of two; MT = 64, two groups of two waves
+//    that each multiply two row blocks over half the k-steps, so each K
+//    operand read serves 32 query rows.  PV waves 4..7 each own 128 latent
+//    columns and accumulate O^T[d x rows] += C_tile^T . P^T of tile it, with
+//    C^T from ds_read_b64_tr_b16 transposed LDS reads.  The PV waves also
+//    issue all tile loads, spread between their MFMAs.
+//  * An fp32 query is split into bf16 hi + lo parts (q = hi + lo to ~2^-17);
+//    a bf16-rounded query alone would put ~1e-3 into the scores.  MT <= 32
+//    multiplies both parts at every k-step.  MT = 64 multiplies lo only at the
+//    two rotary k-steps: with delta_t = scale (lo . c_t) the neglected part of
+//    a latent score, ln sum exp(s_t + delta_t) = lse + sum_t p_t delta_t +
+//    O(var_p delta) = lse + scale (lo . o) + O(delta^2), so the lse gains
+//    scale (lo . o) (the partial output o is at hand in the PV waves) and the
+//    score MFMAs drop from 36 to 20 k-steps per row block.  The remaining lse
+//    error is second order (about 1e-5 at these scales); the outputs keep a
+//    first-order term of size |delta| times the spread of c over the
+//    softmax, far inside their tolerance.
 //  * Softmax in the exp2 domain (raw v_exp_f32) with lazy rescaling: the
 //    running max only moves when a tile max exceeds it by more than TAU = 8
 //    (log2 units), so the O rescale almost never runs; p <= 2^8 stays exact in
@@ -47,7 +56,8 @@
 //    on the same XCD (workgroups are dispatched round-robin over 8 XCDs) so
 //    the second read of a tile hits that XCD's L2.
 //  * Synchronisation: a raw s_barrier plus explicit vmcnt/lgkmcnt waits;
-//    __syncthreads()' fence would drain the in-flight tile loads.
+//    __syncthreads()' fence would drain the in-flight tile loads.  Every
+//    branch on a wave's role is a scalar branch.
 #include "mla_common.h"
 #include "mla_kernels.h"
 
@@ -232,7 +242,6 @@ __device__ __forceinline__ void wait_tiles(int after, bool after_full) {
 template <int MT, bool QF32>
 __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, int n_share, int n_rg,
                                                                   int rows_total) {
-  constexpr int NQH = QF32 ? 2 : 1;  // query parts (hi, lo)
   constexpr int NRB = MT / 16;       // 16-row blocks
   // Score waves 0..3 form NRB / QBW groups; a group's KS waves multiply its
   // QBW row blocks, each over a part of the 18 k-steps, and add their partial
@@ -242,8 +251,22 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
   // 32 query rows (half the LDS traffic of one block per wave).
   constexpr int QBW = NRB == 4 ? 2 : 1;
   constexpr int KS = 4 / (NRB / QBW);
-  constexpr int KMAX = (kKSteps + KS - 1) / KS;
+  // An fp32 query is split into bf16 hi + lo parts (q = hi + lo to ~2^-17).
+  // MT <= 32 multiplies both parts at every k-step (NQH = 2).  MT = 64, where
+  // the score MFMAs dominate, multiplies lo only at the two rotary k-steps
+  // and restores the latent lo part's share of the scores to first order in
+  // the lse (LOC below, epilogue).
+  constexpr bool LOC = QF32 && MT == 64;
+  constexpr int NQH = QF32 && !LOC ? 2 : 1;
+  // The KS waves of a group cut the k-steps into parts of equal MFMA count:
+  // with LOC the two rotary k-steps cost two MFMAs each, so the 20 MFMA steps
+  // split 10 + 10, the rotary steps at the end of the last part.
+  constexpr int KCOST = LOC ? kKSteps + kDr / 32 : kKSteps;
+  static_assert(!LOC || KCOST % KS == 0, "equal parts");
+  constexpr int KMAX = (KCOST + KS - 1) / KS;
+  constexpr int KLAST = kKSteps - (KS - 1) * (KCOST / KS);  // k-steps of the last part (LOC)
   __shared__ __attribute__((aligned(16))) Smem<MT> sm;
+  static_assert(sizeof(sm.xbuf) >= 4 * MT * sizeof(float), "lse corrections fit the exchange buffer");
 
   // every argument field as a local value (see issue_tile_dma)
   const char* const cache = (const char*)a.seg.cache;
@@ -265,7 +288,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
   const int n_heads = a.n_heads;
   const int n_part = a.n_part;
   const int B = a.batch;
-  const float sl2 = a.scale * kLog2e;
+  const float scale = a.scale;
+  const float sl2 = scale * kLog2e;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -340,12 +364,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
   const int lo = j * share, hi = lo + share;
 
   // ---- roles: waves 0..3 score (row block rb, k-part kp); waves 4..7 own 128 latent columns each ----
-  const bool qk_wave = wave < 4;
-  const bool pv_wave = wave >= 4;
-  const int grp = (wave & 3) / KS;   // group of a score wave: row blocks grp * QBW ..
-  const int kp = (wave & 3) % KS;    // its part of the k-steps: [ks0, ks0 + kcnt)
-  const int kcnt = kKSteps / KS + (kp < kKSteps % KS ? 1 : 0);
-  const int ks0 = kp * (kKSteps / KS) + min(kp, kKSteps % KS);
+  // Role variables are wave-uniform scalars: every branch on them is a
+  // scalar branch.  (Under a divergent branch with an empty EXEC mask the
+  // matrix instructions would still run.)
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const bool qk_wave = wave_s < 4;
+  const bool pv_wave = wave_s >= 4;
+  const int grp = (wave_s & 3) / KS;   // group of a score wave: row blocks grp * QBW ..
+  const int kp = (wave_s & 3) % KS;    // its part of the k-steps: [ks0, ks0 + kcnt)
+  const int ks0 = LOC ? kp * (KCOST / KS) : kp * (kKSteps / KS) + min(kp, kKSteps % KS);
+  const int kcnt = LOC ? (kp == KS - 1 ? KLAST : KCOST / KS) : kKSteps / KS + (kp < kKSteps % KS ? 1 : 0);
+  const bool rope_part = kp == KS - 1;  // this score wave's part holds the rotary k-steps
   // the row block whose softmax this wave runs (QBW = 1: only k-part 0 runs one)
   const int rb = QBW == 1 ? grp : grp * QBW + kp;
   const bool smax_wave = QBW > 1 || kp == 0;
@@ -448,8 +477,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
       // per scored tile when KS > 1), so the register allocator never holds
       // the query block and the O accumulator at once.
       if (qk_wave) {
-        // ---- score wave: row blocks grp * QBW .. + QBW-1, k-steps [ks0, ks0 + kcnt), hi and lo parts ----
-        bf16x8 qreg[NQH][QBW][KMAX];
+        // ---- score wave: row blocks grp * QBW .. + QBW-1, k-steps [ks0, ks0 + kcnt) ----
+        bf16x8 qreg[NQH][QBW][KMAX];  // [hi, lo] parts of the query (hi only with LOC / a bf16 query)
+        bf16x8 qlo[QBW][2];           // LOC: lo parts of the two rotary k-steps (last part only)
 #pragma unroll
         for (int j = 0; j < QBW; ++j) {
           const int row = (grp * QBW + j) * 16 + l16;
@@ -467,13 +497,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
                 v0 = *(const f32x4*)src;
                 v1 = *(const f32x4*)(src + 4);
               }
+              bf16x8 h8, l8;
 #pragma unroll
               for (int e = 0; e < 8; ++e) {
                 const float v = e < 4 ? v0[e] : v1[e - 4];
                 const bf16 h = (bf16)v;
-                qreg[0][j][i][e] = h;
-                qreg[1][j][i][e] = (bf16)(v - (float)h);
+                h8[e] = h;
+                l8[e] = (bf16)(v - (float)h);
               }
+              qreg[0][j][i] = h8;
+              if constexpr (NQH == 2) qreg[NQH - 1][j][i] = l8;
+              if constexpr (LOC)
+                if (i >= KLAST - 2 && i < KLAST) qlo[j][i - (KLAST - 2)] = rope_part ? l8 : bf16x8{};
             } else {
               qreg[0][j][i] = in ? (k0 < kDc ? *(const bf16x8*)((const bf16*)q_lat_p + qi * kDc + k0)
                                              : *(const bf16x8*)((const bf16*)q_rot_p + qi * kDr + (k0 - kDc)))
@@ -481,6 +516,25 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
             }
           }
         }
+        // LOC: lo part of latent query row r (lane = 8-column chunk), for the
+        // lse correction
+        auto lo_row = [&](int r) -> bf16x8 {
+          f32x4 v0 = f32x4{0.f, 0.f, 0.f, 0.f}, v1 = v0;
+          if (r < nrows) {
+            const int Rr = row0 + r;
+            const int64_t qi = (int64_t)b * s_q * n_heads + (int64_t)(Rr / hc) * n_heads + head_begin + Rr % hc;
+            const float* src = (const float*)q_lat_p + qi * kDc + 8 * lane;
+            v0 = *(const f32x4*)src;
+            v1 = *(const f32x4*)(src + 4);
+          }
+          bf16x8 l8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float v = e < 4 ? v0[e] : v1[e - 4];
+            l8[e] = (bf16)(v - (float)(bf16)v);
+          }
+          return l8;
+        };
         float m_used = -INFINITY;  // running max (log2 units) of this lane's query row (k-part 0)
         float l_part = 0.f;        // this lane's share of the row's sum of p (k-part 0)
 
@@ -492,10 +546,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
           const char* rs = sm.rst[it % kNRStage];
           const int t0 = pr0 + it * kTile;
           const int buf = it & 1;
-          // accumulators: hi and lo parts separately with one row block (two
-          // independent chains would stall on each other), shared with two
-          // (four chains already, and half the registers)
-          constexpr int NACC = QBW == 1 ? NQH : 1;
+          // accumulators: hi and lo parts (else even and odd k-steps)
+          // separately with one row block (two independent chains would stall
+          // on each other), shared with two (four chains already)
+          constexpr int NACC = QBW == 1 ? 2 : 1;
           f32x4 sacc[2][QBW][NACC];
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb)
@@ -544,9 +598,21 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-                  for (int j = 0; j < QBW; ++j)
-                    sacc[tb][j][hl % NACC] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        ak[i % (kPre + 1)][tb], qreg[hl][j][i], sacc[tb][j][hl % NACC], 0, 0, 0);
+                  for (int j = 0; j < QBW; ++j) {
+                    const int ai = (NQH == 2 ? hl : i) % NACC;
+                    sacc[tb][j][ai] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[i % (kPre + 1)][tb], qreg[hl][j][i],
+                                                                             sacc[tb][j][ai], 0, 0, 0);
+                  }
+              if constexpr (LOC) {
+                if (i >= KLAST - 2 && i < KLAST && rope_part) {
+#pragma unroll
+                  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                    for (int j = 0; j < QBW; ++j)
+                      sacc[tb][j][(i + 1) % NACC] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                          ak[i % (kPre + 1)][tb], qlo[j][i - (KLAST - 2)], sacc[tb][j][(i + 1) % NACC], 0, 0, 0);
+                }
+              }
             }
           }
           f32x4 sc[2][QBW];  // partial scores of this wave's k-part
@@ -639,17 +705,42 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
           barrier_raw();
           if (it + 1 < n_tiles) score_tile(it + 1);
         }
-        // epilogue: lse and 1/l of this row block's rows (k-part 0)
+        // epilogue: 1/l of this row block's rows, and the lse
         const float lt = rows_sum(l_part);
-        if (smax_wave && lg == 0) {
-          sm.rowinv[qrow] = lt > 0.f ? 1.f / lt : 0.f;
-          if (rvalid) {
-            const int64_t ri = (int64_t)b * s_q * n_heads + q_off;
-            lse_part[ri * n_part + part_begin + slot] = lt > 0.f ? (m_used + __log2f(lt)) * kLn2 : -INFINITY;
-          }
+        const float linv = lt > 0.f ? 1.f / lt : 0.f;
+        if (smax_wave && lg == 0) sm.rowinv[qrow] = linv;
+        const int64_t lse_i = ((int64_t)b * s_q * n_heads + q_off) * n_part + part_begin + slot;
+        if constexpr (LOC) {
+          // While the PV waves finish the last tile: the lo parts of the latent
+          // query rows, lo = q - bf16(q) in bf16, into two free latent stages
+          // (rows 0..31 / 32..63, 16-byte chunks swizzled like the tiles).
+          // Score wave w takes rows 16 w .. 16 w + 15, four at a time.
+          char* const lo_a = sm.cst[n_tiles % kNStage];
+          char* const lo_b = sm.cst[(n_tiles + 1) % kNStage];
+#pragma unroll 1
+          for (int r4 = 0; r4 < MT / 4; r4 += 4)
+#pragma unroll
+            for (int rr = r4; rr < r4 + 4; ++rr) {
+              const int r = (wave_s & 3) * (MT / 4) + rr;
+              *(bf16x8*)((r < 32 ? lo_a : lo_b) + (r & 31) * kCBytes + ((lane ^ (r & 15)) << 4)) = lo_row(r);
+            }
+        } else {
+          if (smax_wave && lg == 0 && rvalid) lse_part[lse_i] = lt > 0.f ? (m_used + __log2f(lt)) * kLn2 : -INFINITY;
         }
         wait_lgkm0();
         barrier_raw();
+        wait_lgkm0();
+        barrier_raw();  // the PV waves have written their lse corrections
+        if constexpr (LOC) {
+          // lse = ln sum exp(s_hi) + scale * sum_d lo_d o_d: the first-order
+          // change of the log-sum-exp when the latent scores gain scale lo . c_t
+          // (exact to second order in that term, ~1e-5 here)
+          if (smax_wave && lg == 0 && rvalid) {
+            const float* corr = (const float*)sm.xbuf;  // [PV wave][row]
+            const float c = (corr[qrow] + corr[MT + qrow]) + (corr[2 * MT + qrow] + corr[3 * MT + qrow]);
+            lse_part[lse_i] = lt > 0.f ? (m_used + __log2f(lt)) * kLn2 + scale * linv * c : -INFINITY;
+          }
+        }
       } else {
         // ---- PV wave (waves 4..7): 128 latent columns of all rows, and all tile loads ----
 #pragma unroll
@@ -755,10 +846,26 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
         wait_lgkm0();
         barrier_raw();
         {
+          const char* const lo_a = sm.cst[n_tiles % kNStage];
+          const char* const lo_b = sm.cst[(n_tiles + 1) % kNStage];
 #pragma unroll
           for (int q = 0; q < NRB; ++q) {
             const int qr = 16 * q + l16;
             const float inv = sm.rowinv[qr];
+            if constexpr (LOC) {
+              // this wave's part of sum_d lo_d acc_d for row qr: lane holds
+              // columns 128 pw + 16 db + 4 lg + (0..3), chunk 16 pw + 2 db + lg / 2
+              const char* lrow = (qr < 32 ? lo_a : lo_b) + (qr & 31) * kCBytes + ((lg & 1) << 3);
+              float cs = 0.f;
+#pragma unroll
+              for (int db = 0; db < 8; ++db) {
+                const bf16x4 l4 = *(const bf16x4*)(lrow + (((16 * pw + 2 * db + (lg >> 1)) ^ (qr & 15)) << 4));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) cs += (float)l4[e] * acc_o[db][q][e];
+              }
+              cs = rows_sum(cs);
+              if (lg == 0) ((float*)sm.xbuf)[pw * MT + qr] = cs;
+            }
             if (qr < nrows && inv > 0.f) {
               const int R = row0 + qr;
               const int tok = b * s_q + R / hc;
@@ -770,8 +877,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
             }
           }
         }
+        wait_lgkm0();
+        barrier_raw();  // corrections written; stage buffers, P and rowinv are reused by the next piece
       }
-      barrier_raw();  // stage buffers, P and rowinv are reused by the next piece
     }
     __syncthreads();
     if (done) break;

@@ -109,6 +109,12 @@ EDGE = {
         SegSpec("doc_on", lengths=(40, 0), head_begin=56, head_count=8, base_offset=True),
         SegSpec("online", lengths=(2, 5), causal=True, base_offset=True, base_after="doc_on", online=True),
     )),
+    # 64-row groups score with the bf16-rounded latent query and correct the
+    # lse to first order; scores twice as spread as the default scale and a
+    # one-row request (lse = its score) make an uncorrected rounding of the
+    # query miss the lse bound several times over
+    "peaked_rows64": _custom("edge-peaked", batch=4, heads=64, scale=2 / math.sqrt(192), segs=(
+        SegSpec("kv", lengths=(1, 37, 300, 1000), online=True),)),
     "toy_f32_ragged": _custom("edge-f32", dtype="f32", batch=3, heads=2, scale=1 / math.sqrt(6), segs=(
         SegSpec("kv", lengths=(16, 0, 130), layout="paged", page_size=8, spare_pages=1, online=True),)),
 }
