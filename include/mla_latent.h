@@ -153,9 +153,13 @@ typedef struct {
  *
  * q_lat    [n_tok][n_heads][d_c]                 q_dtype, from mla_absorb_q; each
  *          segment's q_rot has q_dtype too
- * caches   cache_dtype.  MLA_BF16 caches take an fp32 query (split into bf16
- *          hi + lo parts, two MFMAs per step) or a bf16 query (one MFMA);
- *          MLA_F32 caches take an fp32 query.
+ * caches   cache_dtype.  MLA_BF16 caches take an fp32 query or a bf16 one.
+ *          An fp32 query is split into bf16 hi + lo parts: groups of up to
+ *          32 query rows multiply both parts; 64-row groups multiply lo
+ *          only on the rotary dims and add the latent lo part's share to
+ *          the lse to first order (scale * lo . o_part; lse error second
+ *          order, ~1e-5 at unit-variance inputs).  MLA_F32 caches take an
+ *          fp32 query.
  * o_part   [n_tok][n_heads][n_part][d_c] fp32    output
  * lse_part [n_tok][n_heads][n_part]      fp32    output
  * n_tok = batch * s_q.  n_wg = workgroups per segment (0 = one per compute unit).

@@ -210,9 +210,10 @@ struct Smem {
   static constexpr int KS = 4 / (NRB / QBW);    // k-parts (score waves) per group of QBW blocks
   char cst[kNStage][kCStage];   // latent ring
   char rst[kNRStage][kRStage];  // rotary ring
-  char p[2][MT * kPStr];
+  char p[2][MT * kPStr];         // P (bf16) of two tiles
   // exchanged partial scores [slot][tb][lane][4]: QBW = 1, k-parts 1..KS-1 of each
-  // row block; QBW = 2, the partner's k-part of each row block
+  // row block; QBW = 2, the partner's k-part of each row block.  After a
+  // piece's last tile: the PV waves' lse corrections [PV wave][row] (MT = 64).
   float xbuf[(QBW == 1 ? NRB * (KS - 1) : NRB) * 2 * 64 * 4];
   float alpha[2][MT];
   float rowinv[MT];
