@@ -121,6 +121,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--detail", action="store_true", help="also time each call separately")
     ap.add_argument("--eager", action="store_true", help="host launches instead of a HIP graph")
+    ap.add_argument("--no-fuse-post", action="store_true",
+                    help="merge and U_V as two calls even for few query tokens")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="before the timed region, run one plain device copy of this many bytes (fp32 "
                          "elementwise, read N and write N) whose HBM counters calibrate the decode kernel's")
@@ -149,7 +151,9 @@ def main():
     # Infinity Cache, so every step streams its cache from HBM.
     nbytes, flops = algorithmic(x)
     n_copies = max(1, math.ceil(2 * MALL_BYTES / max(1, nbytes)))
-    base = step_from_inputs(x, n_wg=args.n_wg)
+    fuse = False if args.no_fuse_post else None
+    base = step_from_inputs(x, n_wg=args.n_wg, fuse_post=fuse)
+    step_fused = base.fuse_post
     steps = [base]
     for _ in range(n_copies - 1):
         segs = []
@@ -160,7 +164,7 @@ def main():
                                     block_table=bs.block_table, head_begin=bs.head_begin,
                                     head_count=bs.head_count, causal=bs.causal))
         steps.append(DecodeStep(base.q_nope, base.q_pe, base.q_pos, base.w_uk, base.w_uv, segs, sp.batch, sp.s_q,
-                                x.scale, x.rope_base, n_wg=args.n_wg, n_split=base.n_split))
+                                x.scale, x.rope_base, n_wg=args.n_wg, n_split=base.n_split, fuse_post=fuse))
     # Launch path.  Graph mode (default): the step is captured into a HIP
     # graph of U consecutive steps (cycling the cache copies) and the timed
     # region replays it, so small workloads are bound by the GPU rather than
@@ -255,13 +259,14 @@ def main():
         # each call alone, back to back on the stream (host launches)
         detail = {}
         reps = 50
-        for nm in ["prepare", "decode", "combine", "out_uv"]:
+        names = ["prepare", "decode"] + (["combine_out_uv"] if step_fused else ["combine", "out_uv"])
+        for nm in names:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             e0.record(stream)
             for j in range(reps):
                 pj, dj, qj = bound[j % n_copies]
-                g = {"prepare": pj, "decode": dj, "combine": qj[:1], "out_uv": qj[1:]}[nm]
+                g = {"prepare": pj, "decode": dj, "combine": qj[:1], "out_uv": qj[1:], "combine_out_uv": qj}[nm]
                 run_calls(g)
             e1.record(stream)
             torch.cuda.synchronize()
@@ -287,7 +292,8 @@ def main():
         "config": {"workload": sp.description, "name": sp.name, "batch": sp.batch, "heads": sp.heads,
                    "s_q": sp.s_q, "d_c": sp.d_c, "d_rope": sp.d_rope, "d_nope": sp.d_nope, "d_v": sp.d_v,
                    "cache_rows": sum(_rows(x)), "seed": seed, "cache_copies_rotated": n_copies,
-                   "parallelism": "single GPU", "launch": launch},
+                   "parallelism": "single GPU", "launch": launch,
+                   "post": "combine_out_uv" if step_fused else "combine_lse + out_uv"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "mla_decode_splitkv (decode_bf16_kernel)",

@@ -20,7 +20,8 @@
  *   mla_decode_splitkv -> partial (o_lat, lse) states per KV split / segment
  *   mla_combine_lse  -> o_lat, lse (log-sum-exp merge of the partial states)
  *   mla_out_uv       -> out        (U_V o_lat, once per query)
- * mla_prepare_q runs the first two in one launch (all segment shifts at once).
+ * mla_prepare_q runs the first two in one launch (all segment shifts at once);
+ * mla_combine_out_uv runs the last two in one launch (few query tokens).
  *
  * Conventions shared by every call
  *  - All tensor pointers are DEVICE pointers (HIP device memory), row-major,
@@ -223,6 +224,32 @@ mla_status mla_prepare_q(const void* q_nope, const void* q_pe, const void* w_uk,
  */
 mla_status mla_out_uv(const void* o_lat, int o_dtype, const void* w_uv, int w_dtype, void* out,
                       int out_dtype, int n_tok, int n_heads, int d_c, int d_v, void* stream);
+
+/*
+ * mla_combine_out_uv -- mla_combine_lse followed by mla_out_uv, in one launch.
+ * [R]: the merged state goes through one shared output projection; [T]
+ * "Move the Value Expansion After the Weighted Sum".  For every (token t,
+ * head h) row r = t * n_heads + h:
+ *   lse[r]      = ln sum_j exp(lse_part[r][j])               (-inf slots skipped)
+ *   o[r]        = sum_j exp(lse_part[r][j] - lse[r]) o_part[r][j]   (fp32)
+ *   out[t][h][i] = sum_j w_uv[h][i][j] * o[r][j]             (fp32 accumulation)
+ * A row whose slots are all -inf gives o = 0, out = 0, lse = -inf; o_part
+ * rows of -inf slots are never read.  The merged row enters U_V in fp32 (the
+ * two-call path rounds o_lat to out_dtype first).  One workgroup per row
+ * reads its head's U_V: meant for few query tokens per head.
+ *
+ * o_part   [n_tok][n_heads][n_part][d_c] fp32 (16-byte aligned)
+ * lse_part [n_tok][n_heads][n_part]      fp32 (n_part <= 1024)
+ * w_uv     [n_heads][d_v][d_c]           w_dtype
+ * o_lat    [n_tok][n_heads][d_c]         out_dtype, or NULL if not wanted
+ * lse      [n_tok][n_heads]              fp32, or NULL if not wanted
+ * out      [n_tok][n_heads][d_v]         out_dtype
+ * Shapes: d_c a multiple of 4, d_c <= 512; d_v <= 128; n_tok, n_heads <= 65535.
+ * Errors: MLA_ERR_NULL, MLA_ERR_DTYPE, MLA_ERR_SHAPE as for the two calls.
+ */
+mla_status mla_combine_out_uv(const float* o_part, const float* lse_part, int n_tok, int n_heads, int n_part,
+                              int d_c, const void* w_uv, int w_dtype, int d_v, void* o_lat, float* lse, void* out,
+                              int out_dtype, void* stream);
 
 /* Text of a status code (static storage). */
 const char* mla_status_string(int status);

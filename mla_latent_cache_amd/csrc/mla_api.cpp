@@ -188,6 +188,23 @@ mla_status mla_combine_lse(const float* o_part, const float* lse_part, int n_row
                     "mla_combine_lse launch");
 }
 
+mla_status mla_combine_out_uv(const float* o_part, const float* lse_part, int n_tok, int n_heads, int n_part,
+                              int d_c, const void* w_uv, int w_dtype, int d_v, void* o_lat, float* lse, void* out,
+                              int out_dtype, void* stream) {
+  if (!o_part || !lse_part || !w_uv || !out) return fail(MLA_ERR_NULL, "mla_combine_out_uv: null pointer");
+  if (!dtype_ok(w_dtype) || !dtype_ok(out_dtype))
+    return fail(MLA_ERR_DTYPE, "mla_combine_out_uv: dtypes %d, %d", w_dtype, out_dtype);
+  if (n_tok < 0 || n_tok > 65535 || n_heads <= 0 || n_heads > 65535 || n_part <= 0 || n_part > 1024 || d_c <= 0 ||
+      d_c > 512 || (d_c & 3) || d_v <= 0 || d_v > 128 || ((reinterpret_cast<uintptr_t>(o_part) & 15u) != 0))
+    return fail(MLA_ERR_SHAPE, "mla_combine_out_uv: n_tok=%d n_heads=%d n_part=%d (<= 1024) d_c=%d (multiple of 4, "
+                "<= 512) d_v=%d (<= 128), o_part 16-byte aligned", n_tok, n_heads, n_part, d_c, d_v);
+  if (n_tok == 0) return ok();
+  return hip_status(mla::launch_combine_out_uv(o_part, lse_part, n_tok, n_heads, n_part, d_c, w_uv,
+                                               w_dtype == MLA_BF16, d_v, o_lat, lse, out, out_dtype == MLA_BF16,
+                                               (hipStream_t)stream),
+                    "mla_combine_out_uv launch");
+}
+
 mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q_lat, int q_dtype,
                               int cache_dtype, int batch, int s_q, int n_heads, int d_c, int d_rope, float scale,
                               float* o_part, float* lse_part, int n_part, int n_wg, void* stream) {

@@ -66,6 +66,11 @@ hipError_t launch_out_uv_mfma(const void* o_lat, const void* w_uv, void* out, bo
                               int n_heads, hipStream_t stream);
 hipError_t launch_combine(const float* o_part, const float* lse_part, int n_rows, int n_part,
                           int d_c, void* o_lat, bool out_bf16, float* lse, hipStream_t stream);
+// Merge and value expansion of (token, head) rows in one launch (d_c <= 512,
+// d_v <= 128); o_lat and lse may be null.
+hipError_t launch_combine_out_uv(const float* o_part, const float* lse_part, int n_tok, int n_heads, int n_part,
+                                 int d_c, const void* w_uv, bool w_bf16, int d_v, void* o_lat, float* lse,
+                                 void* out, bool out_bf16, hipStream_t stream);
 // Generic fp32 decode (any d_c <= 512, d_rope <= 128): one wave per
 // (query row, split), equal-length splits per request.
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);

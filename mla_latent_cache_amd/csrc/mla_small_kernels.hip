@@ -270,6 +270,161 @@ hipError_t launch_combine(const float* o_part, const float* lse_part, int n_rows
 }
 
 // ---------------------------------------------------------------------------
+// Log-sum-exp merge and value expansion in one pass (MLA tutorial page, "Move
+// the Value Expansion After the Weighted Sum"; RedKnot-MLA abstract: the
+// merged state goes through one shared output projection).  One 1024-thread
+// block per (token, head) row:
+//  * the head's U_V rows are loaded first (bf16, d_c = 512: thread (v, part)
+//    holds columns 64 k + 8 part .. + 7 of row v in registers), independent
+//    of the merge, so their latency overlaps it;
+//  * wave 0 compacts the live slots and their weights as combine_kernel does
+//    (its lse loads go out before its weight loads);
+//  * 8 slot groups of 128 column threads (float4) sum the live partials and
+//    the group sums are added in a fixed order into the fp32 row o (LDS),
+//    stored as o_lat when asked for;
+//  * out[v] = sum_c U_V[v][c] o[c]: the 8 threads of row v each take every
+//    8th group of 8 columns and add their sums with lane shuffles.  o enters
+//    the product in fp32.
+// Each block reads its head's d_v x d_c weights, so this suits few query
+// tokens; many tokens use combine_kernel and the out_uv kernels.
+// ---------------------------------------------------------------------------
+template <typename TO, typename TW, bool VEC>
+__global__ __launch_bounds__(1024) void combine_out_uv_kernel(const float* __restrict__ o_part,
+                                                              const float* __restrict__ lse_part, int n_heads,
+                                                              int n_part, int d_c, const TW* __restrict__ w_uv,
+                                                              int d_v, TO* __restrict__ o_lat,
+                                                              float* __restrict__ lse, TO* __restrict__ out) {
+  __shared__ int live_idx[kCombMaxPart];
+  __shared__ float live_w[kCombMaxPart];
+  __shared__ f32x4 red[7 * 128];
+  __shared__ __attribute__((aligned(16))) float o_s[512];
+  __shared__ float s_inv, s_lse;
+  __shared__ int s_n;
+  const int h = blockIdx.x, t = blockIdx.y;
+  const int64_t row = (int64_t)t * n_heads + h;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int v = tid >> 3, part = tid & 7;  // output column and its eighth of the d_c columns
+  const TW* wrow = w_uv + ((int64_t)h * d_v + (v < d_v ? v : 0)) * d_c;
+  const float* lp = lse_part + row * n_part;
+  // wave 0 issues its lse loads before the weights: loads return in order
+  float lv0 = -INFINITY, lv1 = -INFINITY;
+  if (tid < 64 && n_part <= 128) {
+    lv0 = lane < n_part ? lp[lane] : -INFINITY;
+    lv1 = lane + 64 < n_part ? lp[lane + 64] : -INFINITY;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  bf16x8 wv[VEC ? 8 : 1];
+  if constexpr (VEC) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) wv[k] = v < d_v ? *(const bf16x8*)(wrow + 64 * k + 8 * part) : bf16x8{};
+  }
+  if (tid < 64) {
+    float m = fmaxf(lv0, lv1);
+    if (n_part > 128)
+      for (int j = lane; j < n_part; j += 64) m = fmaxf(m, lp[j]);
+    m = wave_max(m);
+    float tot = 0.f;
+    int n = 0;
+    for (int base = 0; base < n_part; base += 64) {
+      const int j = base + lane;
+      const float l = n_part <= 128 ? (base == 0 ? lv0 : lv1) : j < n_part ? lp[j] : -INFINITY;
+      const bool live = l != -INFINITY;
+      const float w = live ? expf(l - m) : 0.f;
+      tot += w;
+      const uint64_t bal = __ballot(live);
+      if (live) {
+        const int pos = n + __popcll(bal & ((1ull << lane) - 1));
+        live_idx[pos] = j;
+        live_w[pos] = w;
+      }
+      n += __popcll(bal);
+    }
+    tot = wave_sum(tot);
+    if (lane == 0) {
+      s_n = n;
+      s_inv = n > 0 ? 1.f / tot : 0.f;
+      s_lse = n > 0 ? m + logf(tot) : -INFINITY;
+    }
+  }
+  __syncthreads();
+  const int n = s_n;
+  const float inv = s_inv;
+  if (lse && tid == 0) lse[row] = s_lse;
+  const int g = tid >> 7, ct = tid & 127;  // 8 slot groups x 128 column threads
+  const int c = 4 * ct;
+  const float* op = o_part + row * n_part * d_c + c;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (c < d_c) {
+    int i = g;
+    for (; i + 7 * 8 < n; i += 8 * 8) {  // 8 loads in flight: 64 live slots in one round
+      f32x4 x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = *(const f32x4*)(op + (int64_t)live_idx[i + u * 8] * d_c);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += live_w[i + u * 8] * x[u];
+    }
+    for (; i < n; i += 8) acc += live_w[i] * *(const f32x4*)(op + (int64_t)live_idx[i] * d_c);
+  }
+  if (g > 0) red[(g - 1) * 128 + ct] = acc;
+  __syncthreads();
+  if (g == 0 && c < d_c) {
+    for (int k = 0; k < 7; ++k) acc += red[k * 128 + ct];
+    acc *= inv;
+    *(f32x4*)(o_s + c) = acc;
+    if (o_lat) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) store_f(o_lat + row * d_c + c + e, acc[e]);
+    }
+  }
+  __syncthreads();
+  float sum = 0.f;
+  if (v < d_v) {
+    if constexpr (VEC) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const f32x4 a = *(const f32x4*)(o_s + 64 * k + 8 * part);
+        const f32x4 b = *(const f32x4*)(o_s + 64 * k + 8 * part + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sum += (float)wv[k][e] * a[e] + (float)wv[k][4 + e] * b[e];
+      }
+    } else {
+      for (int cc = part; cc < d_c; cc += 8) sum += load_f(wrow + cc) * o_s[cc];
+    }
+  }
+  sum += __shfl_xor(sum, 1);
+  sum += __shfl_xor(sum, 2);
+  sum += __shfl_xor(sum, 4);
+  if (v < d_v && part == 0) store_f(out + row * d_v + v, sum);
+}
+
+template <typename TO, typename TW>
+static hipError_t cou_launch(const float* o_part, const float* lse_part, int n_tok, int n_heads, int n_part,
+                             int d_c, const void* w_uv, int d_v, void* o_lat, float* lse, void* out,
+                             hipStream_t stream) {
+  const dim3 grid(n_heads, n_tok);
+  if constexpr (sizeof(TW) == 2) {
+    if (d_c == 512 && (reinterpret_cast<uintptr_t>(w_uv) & 15u) == 0)
+      return launch(combine_out_uv_kernel<TO, TW, true>, grid, dim3(1024), stream, o_part, lse_part, n_heads,
+                    n_part, d_c, (const TW*)w_uv, d_v, (TO*)o_lat, lse, (TO*)out);
+  }
+  return launch(combine_out_uv_kernel<TO, TW, false>, grid, dim3(1024), stream, o_part, lse_part, n_heads, n_part,
+                d_c, (const TW*)w_uv, d_v, (TO*)o_lat, lse, (TO*)out);
+}
+
+hipError_t launch_combine_out_uv(const float* o_part, const float* lse_part, int n_tok, int n_heads, int n_part,
+                                 int d_c, const void* w_uv, bool w_bf16, int d_v, void* o_lat, float* lse,
+                                 void* out, bool out_bf16, hipStream_t stream) {
+  if (out_bf16 && w_bf16)
+    return cou_launch<bf16, bf16>(o_part, lse_part, n_tok, n_heads, n_part, d_c, w_uv, d_v, o_lat, lse, out, stream);
+  if (out_bf16)
+    return cou_launch<bf16, float>(o_part, lse_part, n_tok, n_heads, n_part, d_c, w_uv, d_v, o_lat, lse, out, stream);
+  if (w_bf16)
+    return cou_launch<float, bf16>(o_part, lse_part, n_tok, n_heads, n_part, d_c, w_uv, d_v, o_lat, lse, out, stream);
+  return cou_launch<float, float>(o_part, lse_part, n_tok, n_heads, n_part, d_c, w_uv, d_v, o_lat, lse, out, stream);
+}
+
+// ---------------------------------------------------------------------------
 // Generic fp32 decode: one wave per (query row, split); split j of request b
 // covers rows [j*L, min((j+1)*L, T_b)) with L = ceil(T_b / n_split).  Scores
 // in fp32 against the stored latent and rotary key (absorbed form), online

@@ -118,6 +118,25 @@ def combine_lse(o_part: torch.Tensor, lse_part: torch.Tensor, out_dtype: torch.d
     return o_lat, lse
 
 
+def combine_out_uv(o_part: torch.Tensor, lse_part: torch.Tensor, w_uv: torch.Tensor, out_dtype: torch.dtype,
+                   out: Optional[torch.Tensor] = None, o_lat: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, want_o_lat: bool = True, want_lse: bool = True):
+    """o_part [n_tok, H, n_part, d_c] fp32, lse_part [n_tok, H, n_part], w_uv [H, d_v, d_c]
+    -> (out [n_tok, H, d_v], o_lat [n_tok, H, d_c] or None, lse [n_tok, H] or None)."""
+    n_tok, H, n_part, d_c = o_part.shape
+    d_v = w_uv.shape[1]
+    dev = o_part.device
+    if out is None:
+        out = torch.empty((n_tok, H, d_v), dtype=out_dtype, device=dev)
+    if o_lat is None and want_o_lat:
+        o_lat = torch.empty((n_tok, H, d_c), dtype=out_dtype, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((n_tok, H), dtype=torch.float32, device=dev)
+    _lib.call("mla_combine_out_uv", _ptr(o_part), _ptr(lse_part), n_tok, H, n_part, d_c, _ptr(w_uv),
+              _DT[w_uv.dtype], d_v, _ptr(o_lat), _ptr(lse), _ptr(out), _DT[out_dtype], _stream())
+    return out, o_lat, lse
+
+
 @dataclass
 class Segment:
     """Device tensors of one KV segment (see ``mla_segment``)."""

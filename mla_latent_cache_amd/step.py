@@ -42,7 +42,7 @@ def _ceil_div(a: int, b: int) -> int:
 class DecodeStep:
     def __init__(self, q_nope, q_pe, q_pos, w_uk, w_uv, segments: List[StepSegment], batch: int, s_q: int,
                  scale: float, rope_base: float = 10000.0, n_wg: int = 0,
-                 n_split: Optional[Sequence[int]] = None):
+                 n_split: Optional[Sequence[int]] = None, fuse_post: Optional[bool] = None):
         self.q_nope, self.q_pe, self.q_pos = q_nope, q_pe, q_pos
         self.w_uk, self.w_uv = w_uk, w_uv
         self.batch, self.s_q, self.scale, self.rope_base, self.n_wg = batch, s_q, scale, rope_base, n_wg
@@ -102,6 +102,11 @@ class DecodeStep:
         self.o_lat = torch.empty((n_tok, H, d_c), dtype=dt, device=dev)
         self.lse = torch.empty((n_tok, H), dtype=torch.float32, device=dev)
         self.out = torch.empty((n_tok, H, d_v), dtype=dt, device=dev)
+        # merge and U_V in one launch (mla_combine_out_uv) for few query
+        # tokens: each of its workgroups reads one head's U_V
+        if fuse_post is None:
+            fuse_post = n_tok <= 8
+        self.fuse_post = bool(fuse_post) and d_c <= 512 and d_v <= 128
 
     def _auto_split(self, s: StepSegment) -> int:
         lens = [int(x) for x in s.seq_lens_host]
@@ -143,11 +148,18 @@ class DecodeStep:
                                                       [r for _, r in self.q_rots], [s for s, _ in self.q_rots],
                                                       self.q_pos, self.rope_base, ops._stream()))
 
+    def combine_expand(self):
+        ops.combine_out_uv(self.o_part, self.lse_part, self.w_uv, self.out.dtype, out=self.out, o_lat=self.o_lat,
+                           lse=self.lse)
+
     def run(self):
         self.prepare()
         self.decode()
-        self.combine()
-        self.expand()
+        if self.fuse_post:
+            self.combine_expand()
+        else:
+            self.combine()
+            self.expand()
         return self.out, self.o_lat, self.lse
 
     # -- low-overhead replay: ctypes arguments built once for a fixed stream --
@@ -178,10 +190,16 @@ class DecodeStep:
                                          dt(self.segments[0].cache), self.batch, self.s_q, H, d_c, d_r,
                                          float(self.scale), self.o_part.data_ptr(), self.lse_part.data_ptr(),
                                          self.n_part, self.n_wg, st))]
-        post = [(lib.mla_combine_lse, (self.o_part.data_ptr(), self.lse_part.data_ptr(), n_tok * H, self.n_part,
-                                       d_c, self.o_lat.data_ptr(), dt(self.o_lat), self.lse.data_ptr(), st)),
-                (lib.mla_out_uv, (self.o_lat.data_ptr(), dt(self.o_lat), self.w_uv.data_ptr(), dt(self.w_uv),
-                                  self.out.data_ptr(), dt(self.out), n_tok, H, d_c, self.w_uv.shape[1], st))]
+        if self.fuse_post:
+            post = [(lib.mla_combine_out_uv, (self.o_part.data_ptr(), self.lse_part.data_ptr(), n_tok, H, self.n_part,
+                                              d_c, self.w_uv.data_ptr(), dt(self.w_uv), self.w_uv.shape[1],
+                                              self.o_lat.data_ptr(), self.lse.data_ptr(), self.out.data_ptr(),
+                                              dt(self.out), st))]
+        else:
+            post = [(lib.mla_combine_lse, (self.o_part.data_ptr(), self.lse_part.data_ptr(), n_tok * H, self.n_part,
+                                           d_c, self.o_lat.data_ptr(), dt(self.o_lat), self.lse.data_ptr(), st)),
+                    (lib.mla_out_uv, (self.o_lat.data_ptr(), dt(self.o_lat), self.w_uv.data_ptr(), dt(self.w_uv),
+                                      self.out.data_ptr(), dt(self.out), n_tok, H, d_c, self.w_uv.shape[1], st))]
         return pre, dec, post
 
 
@@ -194,7 +212,7 @@ def run_calls(calls) -> None:
             raise _lib.MlaError(fn.__name__, st, _lib.load().mla_last_error().decode())
 
 
-def step_from_inputs(x, device="cuda", n_wg: int = 0, n_split=None) -> DecodeStep:
+def step_from_inputs(x, device="cuda", n_wg: int = 0, n_split=None, fuse_post=None) -> DecodeStep:
     """Upload a seeded input set (``mla_inputs.MlaInputs``) and build its step."""
     d = torch.device(device)
     segs = []
@@ -206,4 +224,5 @@ def step_from_inputs(x, device="cuda", n_wg: int = 0, n_split=None) -> DecodeSte
             block_table=None if s.block_table is None else s.block_table.to(d),
             head_begin=s.head_begin, head_count=s.head_count, causal=s.causal))
     return DecodeStep(x.q_nope.to(d), x.q_pe.to(d), x.q_pos.to(d), x.w_uk.to(d), x.w_uv.to(d), segs,
-                      x.spec.batch, x.spec.s_q, x.scale, x.rope_base, n_wg=n_wg, n_split=n_split)
+                      x.spec.batch, x.spec.s_q, x.scale, x.rope_base, n_wg=n_wg, n_split=n_split,
+                      fuse_post=fuse_post)

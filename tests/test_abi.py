@@ -86,6 +86,14 @@ def test_null_and_shape_errors_before_any_gpu_call(lib):
     assert _st(lib, "mla_out_uv", P, 1, P, 1, P, 1, -1, 1, 512, 128, None) == 2
     assert _st(lib, "mla_combine_lse", P, P, 1, 0, 512, P, 1, None, None) == 2
     assert _st(lib, "mla_combine_lse", P, None, 1, 1, 512, P, 1, None, None) == 1
+    # mla_combine_out_uv(o_part, lse_part, n_tok, n_heads, n_part, d_c, w_uv, w_dtype, d_v, o_lat, lse, out, dt)
+    assert _st(lib, "mla_combine_out_uv", P, P, 1, 1, 4, 512, None, 1, 128, None, None, P, 1, None) == 1
+    assert _st(lib, "mla_combine_out_uv", P, P, 1, 1, 4, 512, P, 4, 128, None, None, P, 1, None) == 3
+    assert _st(lib, "mla_combine_out_uv", P, P, 1, 1, 4, 1024, P, 1, 128, None, None, P, 1, None) == 2
+    assert _st(lib, "mla_combine_out_uv", P, P, 1, 1, 4, 512, P, 1, 129, None, None, P, 1, None) == 2
+    assert _st(lib, "mla_combine_out_uv", P, P, 1, 1, 4, 510, P, 1, 128, None, None, P, 1, None) == 2
+    assert _st(lib, "mla_combine_out_uv", P + 4, P, 1, 1, 4, 512, P, 1, 128, None, None, P, 1, None) == 2
+    assert _st(lib, "mla_combine_out_uv", P, P, 0, 1, 4, 512, P, 1, 128, None, None, P, 1, None) == 0
     # zero-size calls succeed without launching anything
     assert _st(lib, "mla_absorb_q", P, P, 1, P, 0, 0, 1, 128, 512, None) == 0
 

@@ -234,6 +234,42 @@ def test_combine_call(out_dtype, n_rows):
 
 
 # ------------------------------------------------------------ full sizes, sampled
+@pytest.mark.parametrize("out_dtype,w_dtype,dims", [
+    (torch.bfloat16, torch.bfloat16, (4, 16, 65, 512, 128)),   # the 512-column register path
+    (torch.float32, torch.bfloat16, (3, 5, 9, 512, 128)),
+    (torch.float32, torch.bfloat16, (2, 3, 7, 64, 8)),          # bf16 weights, other widths
+    (torch.float32, torch.float32, (3, 2, 5, 4, 4)),            # the toy widths
+    (torch.bfloat16, torch.float32, (2, 3, 7, 36, 20)),
+])
+def test_combine_out_uv_call(out_dtype, w_dtype, dims):
+    from mla_latent_cache_amd import ops
+    n_tok, H, n_part, d_c, d_v = dims
+    g = torch.Generator().manual_seed(13)
+    o_part = torch.randn((n_tok, H, n_part, d_c), generator=g)
+    lse_part = torch.randn((n_tok, H, n_part), generator=g) * 4
+    lse_part[0, 0, :] = -math.inf              # empty row
+    lse_part[0, 1 % H, 1:] = -math.inf         # one live slot
+    lse_part[-1, -1, ::2] = -math.inf
+    o_part[lse_part == -math.inf] = float("nan")  # never read
+    w = (torch.randn((H, d_v, d_c), generator=g) / math.sqrt(d_c)).to(w_dtype)
+    out, o_lat, lse = ops.combine_out_uv(o_part.cuda(), lse_part.cuda(), w.cuda(), out_dtype)
+    torch.cuda.synchronize()
+    o_ref = np.zeros((n_tok, H, d_c))
+    l_ref = np.zeros((n_tok, H))
+    for t in range(n_tok):
+        for h in range(H):
+            o_ref[t, h], l_ref[t, h] = O.merge_lse(f64(o_part[t, h]), f64(lse_part[t, h]))
+    out_ref = O.output_expand(f64(w), o_ref)
+    assert float(lse[0, 0]) == -math.inf and not np.any(f64(o_lat[0, 0])) and not np.any(f64(out[0, 0]))
+    fin = np.isfinite(l_ref)
+    assert np.array_equal(np.isfinite(f64(lse)), fin)
+    assert np.all(np.abs(f64(lse)[fin] - l_ref[fin]) <= 1e-5 * np.maximum(1.0, np.abs(l_ref[fin])))
+    rel = 1e-5 if out_dtype == torch.float32 else 2.0 ** -8
+    assert np.all(np.abs(f64(o_lat) - o_ref) <= rel * np.abs(o_ref) + 1e-6)
+    rms = float(np.sqrt(np.mean(out_ref ** 2)))
+    assert np.all(np.abs(f64(out) - out_ref) <= rel * np.abs(out_ref) + 1e-5 * rms)
+
+
 @pytest.mark.parametrize("name", ["small", "dsv3", "long", "merge"])
 def test_full_size_sampled(name):
     """The bench's launch configuration (default grid) at full size; the
