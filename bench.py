@@ -29,7 +29,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 MALL_BYTES = 256 << 20          # Infinity Cache: rotate caches so every step reads HBM
 DECODE_SRC = os.path.join(ROOT, "mla_latent_cache_amd", "csrc", "mla_decode_bf16.hip")
-SEEDS = {"toy": 0, "small": 1, "dsv3": 2, "long": 3, "merge": 4}
+SEEDS = {"toy": 0, "small": 1, "dsv3": 2, "long": 3, "merge": 4, "prefill": 5}
 
 
 def _rows(x):
@@ -38,12 +38,17 @@ def _rows(x):
 
 def algorithmic(x):
     """Decode-kernel algorithmic bytes and FLOPs per launch: every stored row
-    [c_t | kr_t] read once (1152 B in bf16), and per row and query row
-    2 * (576 + 512) FLOPs (scores over [c | kr], weighted sum over c)."""
+    [c_t | kr_t] read once (1152 B in bf16), and per visible (row, query row)
+    pair 2 * (576 + 512) FLOPs (scores over [c | kr], weighted sum over c).
+    A causal segment shows query s of s_q the rows t <= T - s_q + s."""
     sp = x.spec
     el = x.segments[0].cache.element_size()
     nbytes = sum(r * sp.row_width * el for r in _rows(x))
-    flops = sum(2 * r * s.head_count * sp.s_q * (sp.row_width + sp.d_c) for r, s in zip(_rows(x), x.segments))
+    flops = 0
+    for s in x.segments:
+        for T in s.seq_lens.tolist():
+            pairs = sum(max(0, min(T, T - sp.s_q + q + 1)) for q in range(sp.s_q)) if s.causal else T * sp.s_q
+            flops += 2 * pairs * s.head_count * (sp.row_width + sp.d_c)
     return nbytes, flops
 
 
@@ -114,7 +119,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="small", choices=["small", "dsv3", "long", "merge", "toy"])
+    ap.add_argument("--workload", default="small", choices=["small", "dsv3", "long", "merge", "toy", "prefill"])
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--n-wg", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -275,6 +280,10 @@ def main():
     n_tok = sp.n_tok
     value = n_tok * args.steps / elapsed
     achieved = nbytes / (dec_us * 1e-6) / 1e9
+    tflops = flops / (dec_us * 1e-6) / 1e12
+    # bound: HBM unless the arithmetic intensity exceeds the ridge of the bf16
+    # MFMA and HBM peaks (the prefill chunk)
+    mfma_bound = flops / max(1, nbytes) > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     traffic = traffic_from_profile(args.workload)
     res = {
         "metric": METRIC,
@@ -294,13 +303,15 @@ def main():
                    "cache_rows": sum(_rows(x)), "seed": seed, "cache_copies_rotated": n_copies,
                    "parallelism": "single GPU", "launch": launch,
                    "post": "combine_out_uv" if step_fused else "combine_lse + out_uv"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "mla_decode_splitkv (decode_bf16_kernel)",
-                     "decode_us": round(dec_us, 3), "algorithmic_bytes": nbytes,
-                     "algorithmic_flops": flops,
-                     "tflops": round(flops / (dec_us * 1e-6) / 1e12, 2),
-                     "mfma_frac": round(flops / (dec_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "roofline": dict(
+            ({"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+              "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic, "hbm_gbs": round(achieved, 2)}
+             if mfma_bound else
+             {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+              "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}),
+            kernel="mla_decode_splitkv (decode_bf16_kernel)", decode_us=round(dec_us, 3),
+            algorithmic_bytes=nbytes, algorithmic_flops=flops, tflops=round(tflops, 2),
+            mfma_frac=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)),
         "cpu_baseline": None,
     }
     if detail:

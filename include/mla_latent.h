@@ -164,7 +164,8 @@ typedef struct {
  * o_part   [n_tok][n_heads][n_part][d_c] fp32    output
  * lse_part [n_tok][n_heads][n_part]      fp32    output
  * n_tok = batch * s_q.  n_wg = workgroups per segment (0 = one per compute unit).
- * bf16 path: d_c = 512, d_rope = 64, page_size = 64, s_q * head_count <= 512.
+ * bf16 path: d_c = 512, d_rope = 64, page_size = 64, s_q * head_count <= 4096
+ * (multi-token chunks: the rows form groups of 64, each streaming the rows).
  */
 mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q_lat, int q_dtype,
                               int cache_dtype, int batch, int s_q, int n_heads, int d_c, int d_rope,

@@ -118,8 +118,19 @@ WORKLOADS = {
     ),
 }
 
+# A multi-token query chunk over the merge layout (RedKnot-MLA abstract: the
+# online path recomputes in context, in chunks): the same relocated document
+# and online segments, read by a 64-token chunk, so every segment serves
+# 64 x heads query rows and the pass is bound by the MFMA units, not HBM.
+WORKLOADS["prefill"] = replace(
+    WORKLOADS["merge"], name="prefill", batch=4, s_q=64,
+    description="chunked prefill over relocated segments: B=4, H=64 (56 Local / 8 Global), a 64-token query "
+                "chunk, 16384-row document + 2048-row online segment, offsets U[0,200000]")
+
 # Order of the configurations as listed by the benchmark description.
 WORKLOAD_ORDER = ("toy", "small", "dsv3", "long", "merge")
+# Further workloads (beyond the five configurations)
+EXTRA_WORKLOADS = ("prefill",)
 
 
 def spec_for(name: str) -> Spec:
@@ -150,4 +161,11 @@ def mini_spec(name: str) -> Spec:
             replace(s.segments[2], length=None, lengths=(70, 4, 65)),
         )
         return replace(s, name="merge-mini", batch=3, segments=segs)
+    if name == "prefill":
+        segs = (
+            replace(s.segments[0], length=None, lengths=(300, 97)),
+            replace(s.segments[1], length=None, lengths=(300, 97)),
+            replace(s.segments[2], length=None, lengths=(70, 64)),   # >= s_q: the chunk is the newest rows
+        )
+        return replace(s, name="prefill-mini", batch=2, segments=segs)
     raise KeyError(name)

@@ -54,6 +54,8 @@ int cu_count() {
 }
 
 constexpr int kBf16Dc = 512;
+// Query rows (s_q * head_count) of one bf16 segment: 64 row groups of 64.
+constexpr int kBf16MaxRows = 4096;
 constexpr int kBf16Dr = 64;
 constexpr int kPage = 64;
 
@@ -82,7 +84,7 @@ int mla_version(void) { return 100; }
 int mla_device_cu_count(void) { return cu_count(); }
 
 int mla_decode_shares(int s_q, int head_count, int n_wg) {
-  if (s_q <= 0 || head_count <= 0 || n_wg < 0 || (int64_t)s_q * head_count > 512) return 0;
+  if (s_q <= 0 || head_count <= 0 || n_wg < 0 || (int64_t)s_q * head_count > kBf16MaxRows) return 0;
   const int wg = n_wg > 0 ? n_wg : cu_count();
   if (wg <= 0) return 0;
   int n_share = 0, n_rg = 0;
@@ -252,8 +254,9 @@ mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q
     if (bf) {
       if (!aligned16(s.cache) || !aligned16(s.q_rot))
         return fail(MLA_ERR_ALIGN, "segment %d: cache and q_rot must be 16-byte aligned", g);
-      if ((int64_t)s_q * s.head_count > 512)
-        return fail(MLA_ERR_UNSUPPORTED, "segment %d: s_q * head_count = %d > 512", g, s_q * s.head_count);
+      if ((int64_t)s_q * s.head_count > kBf16MaxRows)
+        return fail(MLA_ERR_UNSUPPORTED, "segment %d: s_q * head_count = %d > %d", g, s_q * s.head_count,
+                    kBf16MaxRows);
       if (batch > 65535 || s.n_split > 65535)
         return fail(MLA_ERR_UNSUPPORTED, "segment %d: bf16 path needs batch and n_split <= 65535", g);
     } else if ((int64_t)batch * s_q * s.head_count > 65535 || s.n_split > 65535) {

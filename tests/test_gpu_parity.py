@@ -13,12 +13,12 @@ import torch
 
 import mla_inputs as M
 import oracle.mla_direct as O
-from mla_inputs.configs import SegSpec, Spec, WORKLOADS, WORKLOAD_ORDER
+from mla_inputs.configs import EXTRA_WORKLOADS, SegSpec, Spec, WORKLOADS, WORKLOAD_ORDER
 from parity_util import check_step, f64, sample_pairs, tol_check
 
 pytestmark = pytest.mark.gpu
 
-SEEDS = {name: i for i, name in enumerate(WORKLOAD_ORDER)}
+SEEDS = {name: i for i, name in enumerate(WORKLOAD_ORDER + EXTRA_WORKLOADS)}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -38,7 +38,7 @@ def _run(x, **kw):
 
 
 # ------------------------------------------------------------ whole chain, small
-@pytest.mark.parametrize("name", WORKLOAD_ORDER)
+@pytest.mark.parametrize("name", WORKLOAD_ORDER + EXTRA_WORKLOADS)
 def test_chain_mini(name):
     x = M.make(name, SEEDS[name], mini=True, poison=True)
     print(f"[parity] mini {name} seed {SEEDS[name]}", flush=True)
@@ -270,14 +270,14 @@ def test_combine_out_uv_call(out_dtype, w_dtype, dims):
     assert np.all(np.abs(f64(out) - out_ref) <= rel * np.abs(out_ref) + 1e-5 * rms)
 
 
-@pytest.mark.parametrize("name", ["small", "dsv3", "long", "merge"])
+@pytest.mark.parametrize("name", ["small", "dsv3", "long", "merge", "prefill"])
 def test_full_size_sampled(name):
     """The bench's launch configuration (default grid) at full size; the
     oracle checks sampled (request, head) pairs."""
     x = M.make(name, SEEDS[name])
     print(f"[parity] full {name} seed {SEEDS[name]}", flush=True)
     _, out, o_lat, lse = _run(x)
-    n_req = {"small": 2, "dsv3": 3, "long": 1, "merge": 2}[name]
+    n_req = {"small": 2, "dsv3": 3, "long": 1, "merge": 2, "prefill": 1}[name]
     reqs, heads = sample_pairs(x, n_req, 3, seed=SEEDS[name])
     errs = check_step(x, out, o_lat, lse, requests=reqs, heads=heads, label=f"{name} full")
     print(f"[parity] {name} full reqs={reqs} heads={heads}: {errs}", flush=True)

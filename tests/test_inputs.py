@@ -5,10 +5,10 @@ import pytest
 import torch
 
 import mla_inputs as M
-from mla_inputs.configs import WORKLOAD_ORDER
+from mla_inputs.configs import EXTRA_WORKLOADS, WORKLOAD_ORDER
 
 
-@pytest.mark.parametrize("name", WORKLOAD_ORDER)
+@pytest.mark.parametrize("name", WORKLOAD_ORDER + EXTRA_WORKLOADS)
 def test_mini_deterministic_and_consistent(name):
     a = M.make(name, 3, mini=True)
     b = M.make(name, 3, mini=True)
