@@ -24,6 +24,8 @@ by regrouping.  Sources (the pages' titles and sections):
   Serving" (abstract): a document cached at canonical position zero is read at
   its true request position; partial results of separate paths are merged
   before one shared output projection.
+* The QK-Norm MLA page (abstract): query-key RMSNorm after the projections,
+  RMSNorm = a static weight times x over a dynamic root-mean-square.
 
 Readings taken where the pages are silent (each also listed in the design
 notes): RoPE rotates adjacent feature pairs (2i, 2i+1) counter-clockwise by
@@ -129,7 +131,8 @@ def softmax_lse(scores: np.ndarray):
 
 
 def attend_direct(q_nope: np.ndarray, q_rot: np.ndarray, c: np.ndarray, k_rope: np.ndarray,
-                  u_k: np.ndarray, u_v: np.ndarray, scale: float):
+                  u_k: np.ndarray, u_v: np.ndarray, scale: float,
+                  key_weight: Optional[np.ndarray] = None, key_rinv: Optional[np.ndarray] = None):
     """One query row of one head, in the direct form.
 
     q_nope [d_nope]; q_rot [d_rope] (rotated at the query's true position);
@@ -138,12 +141,18 @@ def attend_direct(q_nope: np.ndarray, q_rot: np.ndarray, c: np.ndarray, k_rope: 
 
     Expands k^C_t = U_K c_t and v_t = U_V c_t explicitly, scores
     s_t = scale * (q^C . k^C_t + q^R . k^R_t), softmaxes, and returns
-    (o = sum_t a_t v_t, o_lat = sum_t a_t c_t, lse)."""
+    (o = sum_t a_t v_t, o_lat = sum_t a_t c_t, lse).  With QK-Norm the
+    expanded content key is normalised first: k^C_t <- key_weight *
+    k^C_t * key_rinv[t] (key_rinv: inverse RMS of row t's key over all heads)."""
     n = c.shape[0]
     d_v, d_c = u_v.shape
     if n == 0:
         return np.zeros(d_v), np.zeros(d_c), NEG_INF
     k_c = expand(u_k, c)                   # [n, d_nope]
+    if key_weight is not None:
+        k_c = k_c * np.asarray(key_weight, np.float64)[None, :]
+    if key_rinv is not None:
+        k_c = k_c * np.asarray(key_rinv, np.float64)[:, None]
     s = scale * (k_c @ np.asarray(q_nope, np.float64) + np.asarray(k_rope, np.float64) @ q_rot)
     a, lse = softmax_lse(s)
     v = expand(u_v, c)                     # [n, d_v]
@@ -172,6 +181,39 @@ def merge_lse(o_parts: np.ndarray, lse_parts: np.ndarray):
 
 
 # --------------------------------------------------------------------------
+# QK-Norm (QK-Norm MLA page, abstract): RMSNorm after the projections
+# --------------------------------------------------------------------------
+@dataclass
+class QKNorm:
+    """Post-projection RMSNorm, RMSNorm(x) = g * x / sqrt(mean(x^2) + eps), of
+    the content query and the content key.  The statistic runs over the whole
+    projection of a token: the query over all heads' q_nope, the key over all
+    heads' U_K c_t (the heads share one latent, one KV group).  g_q, g_k
+    [H, d_nope].  The rotary parts are not normalised."""
+    g_q: np.ndarray
+    g_k: np.ndarray
+    eps: float
+
+
+def rms_inverse(x: np.ndarray, eps: float) -> float:
+    """1 / sqrt(mean(x^2) + eps) over every entry of x."""
+    x = np.asarray(x, np.float64)
+    return 1.0 / math.sqrt(float(np.mean(x * x)) + eps)
+
+
+def key_rms_inverse(w_uk: np.ndarray, c: np.ndarray, eps: float) -> np.ndarray:
+    """Inverse RMS of each row's expanded content key over all heads:
+    w_uk [H, d_nope, d_c], c [n, d_c] -> [n] (rows expanded in chunks)."""
+    w = np.asarray(w_uk, np.float64)
+    c = np.asarray(c, np.float64)
+    out = np.empty(c.shape[0])
+    for i in range(0, c.shape[0], 1024):
+        k = np.einsum("hjd,nd->nhj", w, c[i:i + 1024])   # U_K[h] c_t, every head
+        out[i:i + 1024] = 1.0 / np.sqrt(np.mean(k * k, axis=(1, 2)) + eps)
+    return out
+
+
+# --------------------------------------------------------------------------
 # Whole decode step over KV segments
 # --------------------------------------------------------------------------
 @dataclass
@@ -191,7 +233,8 @@ class OracleSegment:
 def direct_mla_decode(q_nope, q_pe, q_pos, w_uk, w_uv, segments: List[OracleSegment],
                       scale: float, rope_base: float, s_q: int,
                       requests: Optional[Sequence[int]] = None,
-                      heads: Optional[Sequence[int]] = None):
+                      heads: Optional[Sequence[int]] = None,
+                      qk_norm: Optional[QKNorm] = None):
     """Direct-form decode for query tokens t = b * s_q + s and heads h.
 
     Returns (o [n_tok, H, d_v], o_lat [n_tok, H, d_c], lse [n_tok, H]); entries
@@ -199,7 +242,8 @@ def direct_mla_decode(q_nope, q_pe, q_pos, w_uk, w_uv, segments: List[OracleSegm
     every segment whose head range holds it are concatenated into one softmax
     (step order: pick segments, expand content keys, move rotary keys to their
     true positions, rotate the query at its true position, score, softmax,
-    expand values, weight)."""
+    expand values, weight).  With qk_norm the expanded content query and key
+    are RMS-normalised before the score."""
     q_nope = np.asarray(q_nope, np.float64)
     q_pe = np.asarray(q_pe, np.float64)
     w_uk = np.asarray(w_uk, np.float64)
@@ -219,12 +263,14 @@ def direct_mla_decode(q_nope, q_pe, q_pos, w_uk, w_uv, segments: List[OracleSegm
             r = np.asarray(seg.rows(b), np.float64)
             c = r[:, :d_c]
             kr_true = rope_rotate(r[:, d_c:], int(seg.shift[b]), rope_base)  # key-side relocation
-            seg_rows.append((c, kr_true))
+            kinv = key_rms_inverse(w_uk, c, qk_norm.eps) if qk_norm is not None else None
+            seg_rows.append((c, kr_true, kinv))
         for s in range(s_q):
             t = b * s_q + s
+            qinv = rms_inverse(q_nope[t], qk_norm.eps) if qk_norm is not None else None
             for h in heads:
-                cs, ks = [], []
-                for seg, (c, kr) in zip(segments, seg_rows):
+                cs, ks, kis = [], [], []
+                for seg, (c, kr, kinv) in zip(segments, seg_rows):
                     if not (seg.head_begin <= h < seg.head_begin + seg.head_count):
                         continue
                     n = c.shape[0]
@@ -232,11 +278,20 @@ def direct_mla_decode(q_nope, q_pe, q_pos, w_uk, w_uv, segments: List[OracleSegm
                     vis = max(0, min(n, vis))
                     cs.append(c[:vis])
                     ks.append(kr[:vis])
+                    if kinv is not None:
+                        kis.append(kinv[:vis])
                 c_all = np.concatenate(cs) if cs else np.zeros((0, d_c))
                 k_all = np.concatenate(ks) if ks else np.zeros((0, q_pe.shape[2]))
                 q_rot = rope_rotate(q_pe[t, h], int(q_pos[t]), rope_base)
-                o[t, h], o_lat[t, h], lse[t, h] = attend_direct(
-                    q_nope[t, h], q_rot, c_all, k_all, w_uk[h], w_uv[h], scale)
+                if qk_norm is None:
+                    o[t, h], o_lat[t, h], lse[t, h] = attend_direct(
+                        q_nope[t, h], q_rot, c_all, k_all, w_uk[h], w_uv[h], scale)
+                else:
+                    q_c = np.asarray(qk_norm.g_q, np.float64)[h] * q_nope[t, h] * qinv
+                    k_inv = np.concatenate(kis) if kis else np.zeros(0)
+                    o[t, h], o_lat[t, h], lse[t, h] = attend_direct(
+                        q_c, q_rot, c_all, k_all, w_uk[h], w_uv[h], scale,
+                        key_weight=np.asarray(qk_norm.g_k, np.float64)[h], key_rinv=k_inv)
     return o, o_lat, lse
 
 

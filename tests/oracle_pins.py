@@ -372,6 +372,111 @@ def pin_brute_force(O):
     _close(lse, lb, 1e-12, "brute-force lse")
 
 
+# ------------------------------------------------------------------ QK-Norm
+def pin_qknorm_closed_form(O):
+    """QK-Norm MLA page (abstract), RMSNorm(x) = g x / sqrt(mean(x^2) + eps):
+    one head and one key with the tutorial's teaching numbers (U_K c =
+    [1,2,3,-1], q = [1,0,1,0], q . k = 4): the content score is
+    (g_q q . g_k k) / (sqrt(|q|^2/4 + eps) sqrt(|k|^2/4 + eps)), derived by hand."""
+    g = _golden()["key_side"]
+    U = np.array(g["up_key"])[None]           # [1, 4, 2]
+    c = np.array(g["latent"])[None, :]        # one row
+    q = np.array(g["query"])[None, None, :]   # one token, one head
+    rows = np.concatenate([c, np.zeros((1, 2))], axis=1)   # zero rotary key
+    seg = [O.OracleSegment(lambda b: rows, [0], 0, 1, False)]
+
+    def lse_of(g_q, g_k, eps):
+        qk = O.QKNorm(np.array([g_q], float), np.array([g_k], float), eps)
+        _, _, lse = O.direct_mla_decode(q, np.zeros((1, 1, 2)), np.array([0]), U, U, seg, 1.0, 10000.0, 1,
+                                        qk_norm=qk)
+        return float(lse[0, 0])
+
+    # |q|^2 = 2, |k|^2 = 15
+    assert abs(lse_of([1, 1, 1, 1], [1, 1, 1, 1], 0.0) - 16.0 / math.sqrt(30.0)) <= 1e-14
+    assert abs(lse_of([1, 1, 1, 1], [1, 1, 1, 1], 0.5) - 4.0 / math.sqrt(4.25)) <= 1e-14
+    # g_q * g_k weights the terms q_i k_i: 2*1*1*1 (i=0) + 1*0.5*1*3 (i=2) = 3.5
+    assert abs(lse_of([2, 1, 1, 1], [1, 1, 0.5, 1], 0.0) - 3.5 / math.sqrt(0.5 * 3.75)) <= 1e-14
+
+
+def pin_qknorm_invariances(O):
+    """With eps = 0 the normalised content scores ignore positive rescaling of a
+    token's whole query (all heads) and of any latent row: the lse is unchanged,
+    and scaling every latent of a request scales o and o_lat by the same
+    factor (values stay linear in c)."""
+    rng = np.random.default_rng(21)
+    B, S_q, H, d_c, d_nope, d_r, d_v = 1, 2, 3, 5, 4, 2, 3
+    rows = rng.standard_normal((6, d_c + d_r))
+    q_nope = rng.standard_normal((B * S_q, H, d_nope))
+    q_pe = rng.standard_normal((B * S_q, H, d_r))
+    q_pos = np.array([9, 10])
+    w_uk = rng.standard_normal((H, d_nope, d_c))
+    w_uv = rng.standard_normal((H, d_v, d_c))
+    qk = O.QKNorm(1.0 + 0.3 * rng.standard_normal((H, d_nope)), 1.0 + 0.3 * rng.standard_normal((H, d_nope)), 0.0)
+
+    def run(r, q):
+        return O.direct_mla_decode(q, q_pe, q_pos, w_uk, w_uv, [O.OracleSegment(lambda b: r, [0], 0, H, True)],
+                                   0.7, 10000.0, S_q, qk_norm=qk)
+
+    o, o_lat, lse = run(rows, q_nope)
+    q2 = q_nope.copy()
+    q2[1] *= 3.7                                        # one whole token
+    o2, _, lse2 = run(rows, q2)
+    _close(lse2, lse, 1e-12, "query rescaling: lse")
+    _close(o2, o, 1e-12, "query rescaling: o")
+    r2 = rows.copy()
+    r2[2, :d_c] *= 0.25                                 # one latent row
+    _, _, lse3 = run(r2, q_nope)
+    _close(lse3, lse, 1e-12, "latent row rescaling: lse")
+    r3 = rows.copy()
+    r3[:, :d_c] *= 2.5                                  # every latent row
+    o4, o_lat4, lse4 = run(r3, q_nope)
+    _close(lse4, lse, 1e-12, "latent rescaling: lse")
+    _close(o4, 2.5 * o, 1e-12, "latent rescaling: o")
+    _close(o_lat4, 2.5 * o_lat, 1e-12, "latent rescaling: o_lat")
+
+
+def pin_qknorm_absorbed(O):
+    """QK-Norm MLA page (abstract): the static key weight moves into the query
+    projection and the key statistic becomes one inverse-RMS scalar per row.
+    The absorbed form is written here from that statement: q' = U_K^T (g_q g_k
+    q) / rms(q) per head, r_t = 1 / sqrt(c_t^T M c_t / (H d_nope) + eps) with
+    M = sum_h U_K[h]^T U_K[h] (a quadratic form, no key expansion), score =
+    scale (r_t q'.c_t + q_rot.kr_t); it must equal the oracle's explicit form."""
+    rng = np.random.default_rng(22)
+    B, S_q, H, d_c, d_nope, d_r, d_v = 2, 2, 3, 6, 4, 4, 3
+    rows = [rng.standard_normal((n, d_c + d_r)) for n in (7, 4)]
+    q_nope = rng.standard_normal((B * S_q, H, d_nope))
+    q_pe = rng.standard_normal((B * S_q, H, d_r))
+    q_pos = np.array([30, 31, 12, 13])
+    w_uk = rng.standard_normal((H, d_nope, d_c))
+    w_uv = rng.standard_normal((H, d_v, d_c))
+    eps, scale, base = 0.3, 0.55, 10000.0
+    qk = O.QKNorm(1.0 + 0.2 * rng.standard_normal((H, d_nope)), 1.0 + 0.2 * rng.standard_normal((H, d_nope)), eps)
+    o, _, lse = O.direct_mla_decode(q_nope, q_pe, q_pos, w_uk, w_uv,
+                                    [O.OracleSegment(lambda b: rows[b], [0, 0], 0, H, True)],
+                                    scale, base, S_q, qk_norm=qk)
+    M = sum(w_uk[h].T @ w_uk[h] for h in range(H))
+    for b in range(B):
+        c, kr = rows[b][:, :d_c], rows[b][:, d_c:]
+        T = c.shape[0]
+        r = 1.0 / np.sqrt(np.einsum("nd,de,ne->n", c, M, c) / (H * d_nope) + eps)
+        for s in range(S_q):
+            t = b * S_q + s
+            rq = 1.0 / math.sqrt(float(np.mean(q_nope[t] ** 2)) + eps)
+            vis = T - S_q + s + 1
+            krot = np.array([_rot_complex(kr[j], 0, base) for j in range(vis)])
+            for h in range(H):
+                qa = w_uk[h].T @ (qk.g_q[h] * qk.g_k[h] * q_nope[t, h]) * rq
+                qr = np.array(_rot_complex(q_pe[t, h], q_pos[t], base))
+                sc = scale * (r[:vis] * (c[:vis] @ qa) + krot @ qr)
+                m = sc.max()
+                a = np.exp(sc - m)
+                ref_lse = m + math.log(a.sum())
+                ref_o = (a / a.sum()) @ (c[:vis] @ w_uv[h].T)
+                assert abs(lse[t, h] - ref_lse) <= 1e-12, (t, h, lse[t, h], ref_lse)
+                _close(o[t, h], ref_o, 1e-12, "absorbed QK-Norm o")
+
+
 ALL_PINS = [
     pin_worked_example_key_side,
     pin_worked_example_value_side,
@@ -384,4 +489,7 @@ ALL_PINS = [
     pin_relocation_invariance,
     pin_segment_merge,
     pin_brute_force,
+    pin_qknorm_closed_form,
+    pin_qknorm_invariances,
+    pin_qknorm_absorbed,
 ]

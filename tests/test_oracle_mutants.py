@@ -39,6 +39,15 @@ MUTANTS = {
     "merge_plain_sum_lse": ("lse = float(m + math.log(tot))", "lse = float(lse_parts[live].sum())"),
     "cache_factor_two": ("return n_layers * batch * tokens * (d_c + d_r) * bytes_per",
                          "return n_layers * batch * tokens * (2 * d_c + d_r) * bytes_per"),
+    "qknorm_key_rms_one_head": ("out[i:i + 1024] = 1.0 / np.sqrt(np.mean(k * k, axis=(1, 2)) + eps)",
+                                "out[i:i + 1024] = 1.0 / np.sqrt(np.mean(k[:, :1] * k[:, :1], axis=(1, 2)) + eps)"),
+    "qknorm_eps_outside_sqrt": ("out[i:i + 1024] = 1.0 / np.sqrt(np.mean(k * k, axis=(1, 2)) + eps)",
+                                "out[i:i + 1024] = 1.0 / (np.sqrt(np.mean(k * k, axis=(1, 2))) + eps)"),
+    "qknorm_key_weight_dropped": ("k_c = k_c * np.asarray(key_weight, np.float64)[None, :]", "k_c = k_c"),
+    "qknorm_query_rms_one_head": ("qinv = rms_inverse(q_nope[t], qk_norm.eps) if qk_norm is not None else None",
+                                  "qinv = rms_inverse(q_nope[t, 0], qk_norm.eps) if qk_norm is not None else None"),
+    "qknorm_query_weight_from_key": ("q_c = np.asarray(qk_norm.g_q, np.float64)[h] * q_nope[t, h] * qinv",
+                                     "q_c = np.asarray(qk_norm.g_k, np.float64)[h] * q_nope[t, h] * qinv"),
     "query_rot_wrong_pos": ("q_rot = rope_rotate(q_pe[t, h], int(q_pos[t]), rope_base)",
                             "q_rot = rope_rotate(q_pe[t, h], int(q_pos[t]) - 1, rope_base)"),
 }
