@@ -29,7 +29,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 MALL_BYTES = 256 << 20          # Infinity Cache: rotate caches so every step reads HBM
 DECODE_SRC = os.path.join(ROOT, "mla_latent_cache_amd", "csrc", "mla_decode_bf16.hip")
-SEEDS = {"toy": 0, "small": 1, "dsv3": 2, "long": 3, "merge": 4, "prefill": 5}
+SEEDS = {"toy": 0, "small": 1, "dsv3": 2, "long": 3, "merge": 4, "prefill": 5, "qknorm": 6}
 
 
 def _rows(x):
@@ -40,10 +40,11 @@ def algorithmic(x):
     """Decode-kernel algorithmic bytes and FLOPs per launch: every stored row
     [c_t | kr_t] read once (1152 B in bf16), and per visible (row, query row)
     pair 2 * (576 + 512) FLOPs (scores over [c | kr], weighted sum over c).
-    A causal segment shows query s of s_q the rows t <= T - s_q + s."""
+    A causal segment shows query s of s_q the rows t <= T - s_q + s.  With
+    QK-Norm each row also brings its 4-byte inverse key RMS."""
     sp = x.spec
     el = x.segments[0].cache.element_size()
-    nbytes = sum(r * sp.row_width * el for r in _rows(x))
+    nbytes = sum(r * (sp.row_width * el + (4 if sp.qk_norm else 0)) for r in _rows(x))
     flops = 0
     for s in x.segments:
         for T in s.seq_lens.tolist():
@@ -90,6 +91,7 @@ def cpu_baseline(x, budget_s: float):
             for s in x.segments]
     q_nope, q_pe, w_uk, w_uv = f64(x.q_nope), f64(x.q_pe), f64(x.w_uk), f64(x.w_uv)
     q_pos = x.q_pos.numpy()
+    qk = O.QKNorm(f64(x.g_q), f64(x.g_k), sp.qk_eps) if x.g_q is not None else None
     rows_per_req = max(_rows(x)) / sp.batch
     hchunk = sp.heads if rows_per_req * sp.heads <= 64 * 4096 else max(1, (64 * 4096) // int(rows_per_req) or 1)
     done_pairs = 0
@@ -99,7 +101,7 @@ def cpu_baseline(x, budget_s: float):
         for h0 in range(0, sp.heads, hchunk):
             hs = list(range(h0, min(sp.heads, h0 + hchunk)))
             O.direct_mla_decode(q_nope, q_pe, q_pos, w_uk, w_uv, segs, x.scale, x.rope_base, sp.s_q,
-                                requests=[b % sp.batch], heads=hs)
+                                requests=[b % sp.batch], heads=hs, qk_norm=qk)
             done_pairs += len(hs)
             if time.perf_counter() - t0 >= budget_s:
                 break
@@ -119,7 +121,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="small", choices=["small", "dsv3", "long", "merge", "toy", "prefill"])
+    ap.add_argument("--workload", default="small", choices=["small", "dsv3", "long", "merge", "toy", "prefill", "qknorm"])
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--n-wg", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)

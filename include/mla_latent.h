@@ -131,6 +131,11 @@ typedef struct {
                                  rows t <= T_b - s_q + s */
   int part_begin;             /* this segment writes partial slots */
   int n_split;                /* [part_begin, part_begin + n_split) of its rows */
+  const float* row_rinv;      /* QK-Norm: per stored row, the inverse RMS of its content
+                                 key (mla_qknorm_key_rinv), indexed like the cache rows
+                                 ([batch][max_rows] or [n_pages][page_size]); the
+                                 latent part of each score is multiplied by it.
+                                 NULL => no QK-Norm */
 } mla_segment;
 
 /*
@@ -251,6 +256,37 @@ mla_status mla_out_uv(const void* o_lat, int o_dtype, const void* w_uv, int w_dt
 mla_status mla_combine_out_uv(const float* o_part, const float* lse_part, int n_tok, int n_heads, int n_part,
                               int d_c, const void* w_uv, int w_dtype, int d_v, void* o_lat, float* lse, void* out,
                               int out_dtype, void* stream);
+
+/*
+ * QK-Norm MLA (QK-Norm MLA page, abstract): RMSNorm(x) = g x / sqrt(mean(x^2)
+ * + eps) of the content query and key after their projections, the statistic
+ * over a token's whole projection (all heads: the heads share one latent,
+ * one KV group).  The static key weight moves into the query, the key
+ * statistic becomes one inverse-RMS scalar per stored row:
+ *   score_t = scale * (rinv_t * (q'_lat . c_t) + q_rot . k^R_t),
+ *   q'_lat = U_K^T (g_q g_k q_nope) / rms(q_nope)   (mla_qknorm_query, then mla_absorb_q),
+ *   rinv_t = 1 / sqrt(mean_{h,i} (U_K[h] c_t)_i^2 + eps)
+ *          = 1 / sqrt(c_t^T G c_t / (n_heads * d_nope) + eps),  G = sum_h U_K[h]^T U_K[h].
+ * The rotary parts are not normalised.
+ *
+ * mla_qknorm_query: q_out[t][h][i] = g_q[h][i] g_k[h][i] q_nope[t][h][i] / rms_t,
+ *   rms_t = sqrt(mean_{h,i} q_nope[t][h][i]^2 + eps).
+ *   q_nope [n_tok][n_heads][d_nope] in_dtype; g_q, g_k [n_heads][d_nope] fp32;
+ *   q_out [n_tok][n_heads][d_nope] fp32 (then mla_absorb_q with in_dtype MLA_F32).
+ * mla_qknorm_key_gram: gram[a][b] = sum_{h,i} w_uk[h][i][a] w_uk[h][i][b],
+ *   w_uk [n_heads][d_nope][d_c] w_dtype, gram [d_c][d_c] fp32 (d_c <= 512).
+ * mla_qknorm_key_rinv: rinv[r] = 1 / sqrt(c_r^T gram c_r / (n_heads * d_nope) + eps)
+ *   for the n_rows stored rows of `rows` ([n_rows][row_width] row_dtype, the
+ *   latent c_r in the first d_c entries; a cache or a page pool viewed as rows);
+ *   rinv [n_rows] fp32.  The cache writer's part: once per stored row.
+ * Errors: MLA_ERR_NULL, MLA_ERR_DTYPE, MLA_ERR_SHAPE (eps < 0 or non-finite).
+ */
+mla_status mla_qknorm_query(const void* q_nope, int in_dtype, const float* g_q, const float* g_k, int n_tok,
+                            int n_heads, int d_nope, double eps, float* q_out, void* stream);
+mla_status mla_qknorm_key_gram(const void* w_uk, int w_dtype, int n_heads, int d_nope, int d_c, float* gram,
+                               void* stream);
+mla_status mla_qknorm_key_rinv(const void* rows, int row_dtype, int64_t n_rows, int row_width, const float* gram,
+                               int d_c, int n_heads, int d_nope, double eps, float* rinv, void* stream);
 
 /* Text of a status code (static storage). */
 const char* mla_status_string(int status);

@@ -57,6 +57,8 @@ class Spec:
     rope_base: float = 10000.0
     scale: Optional[float] = None  # None => 1/sqrt(d_nope + d_rope)
     offset_range: Optional[Tuple[int, int]] = None  # o_b ~ U{lo..hi}, inclusive
+    qk_norm: bool = False          # RMSNorm of the content query and key (weights g_q, g_k drawn)
+    qk_eps: float = 1e-6
     description: str = ""
 
     @property
@@ -127,10 +129,17 @@ WORKLOADS["prefill"] = replace(
     description="chunked prefill over relocated segments: B=4, H=64 (56 Local / 8 Global), a 64-token query "
                 "chunk, 16384-row document + 2048-row online segment, offsets U[0,200000]")
 
+# The small configuration with QK-Norm (QK-Norm MLA page, abstract): the
+# content query and key RMS-normalised after their projections.
+WORKLOADS["qknorm"] = replace(
+    WORKLOADS["small"], name="qknorm", qk_norm=True,
+    description="small bf16 with QK-Norm: B=4, H=16, T=4096 contiguous, 1 query token, RMSNorm of the "
+                "content query and key")
+
 # Order of the configurations as listed by the benchmark description.
 WORKLOAD_ORDER = ("toy", "small", "dsv3", "long", "merge")
 # Further workloads (beyond the five configurations)
-EXTRA_WORKLOADS = ("prefill",)
+EXTRA_WORKLOADS = ("prefill", "qknorm")
 
 
 def spec_for(name: str) -> Spec:
@@ -161,6 +170,9 @@ def mini_spec(name: str) -> Spec:
             replace(s.segments[2], length=None, lengths=(70, 4, 65)),
         )
         return replace(s, name="merge-mini", batch=3, segments=segs)
+    if name == "qknorm":
+        return replace(s, name="qknorm-mini", batch=3,
+                       segments=(SegSpec("kv", lengths=(1, 129, 777), online=True),))
     if name == "prefill":
         segs = (
             replace(s.segments[0], length=None, lengths=(300, 97)),

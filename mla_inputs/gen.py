@@ -8,7 +8,9 @@ Draw order for ``make_inputs(spec, seed)``, all from one
    physical page permutation (paged layout);
 3. per segment, in spec order: the cache storage, N(0, 1), in fixed chunks;
 4. ``q_nope`` then ``q_pe``, N(0, 1);
-5. ``w_uk`` then ``w_uv``, N(0, 1) / sqrt(d_c)  (fan-in of both is ``d_c``).
+5. ``w_uk`` then ``w_uv``, N(0, 1) / sqrt(d_c)  (fan-in of both is ``d_c``);
+6. with ``qk_norm``: the RMSNorm weights ``g_q`` then ``g_k`` [H, d_nope],
+   1 + 0.1 N(0, 1), kept in fp32.
 
 Floating tensors are then rounded to the spec dtype (bf16 rounds to nearest
 even, as ``Tensor.to(torch.bfloat16)`` does).  With ``poison=True`` every
@@ -85,6 +87,8 @@ class MlaInputs:
     w_uv: torch.Tensor        # [H, d_v, d_c]
     segments: List[Segment]
     offsets: torch.Tensor     # int64 [B]
+    g_q: Optional[torch.Tensor] = None   # fp32 [H, d_nope]: QK-Norm query weight (spec.qk_norm)
+    g_k: Optional[torch.Tensor] = None   # fp32 [H, d_nope]: QK-Norm key weight
 
     @property
     def scale(self) -> float:
@@ -184,6 +188,16 @@ def make_inputs(spec: Spec, seed: int, poison: bool = False) -> MlaInputs:
     w_uv = torch.empty((H, spec.d_v, spec.d_c), dtype=dt)
     _randn_into(w_uv, g, mul=spec.d_c ** -0.5)
 
+    # step 6: QK-Norm weights
+    g_q = g_k = None
+    if spec.qk_norm:
+        g_q = torch.empty((H, spec.d_nope), dtype=torch.float32)
+        _randn_into(g_q, g, mul=0.1)
+        g_q += 1.0
+        g_k = torch.empty((H, spec.d_nope), dtype=torch.float32)
+        _randn_into(g_k, g, mul=0.1)
+        g_k += 1.0
+
     # query positions: the last s_q rows of the online segment
     online = [seg for ss, seg in zip(spec.segments, segments) if ss.online]
     assert len(online) == 1, "exactly one segment holds the newest tokens"
@@ -199,7 +213,7 @@ def make_inputs(spec: Spec, seed: int, poison: bool = False) -> MlaInputs:
             _poison(seg)
 
     return MlaInputs(spec=spec, seed=seed, q_nope=q_nope, q_pe=q_pe, q_pos=q_pos,
-                     w_uk=w_uk, w_uv=w_uv, segments=segments, offsets=offsets)
+                     w_uk=w_uk, w_uv=w_uv, segments=segments, offsets=offsets, g_q=g_q, g_k=g_k)
 
 
 def _poison(seg: Segment) -> None:

@@ -35,6 +35,7 @@ class MlaSegment(ctypes.Structure):
         ("causal", c_int),
         ("part_begin", c_int),
         ("n_split", c_int),
+        ("row_rinv", c_void_p),
     ]
 
 
@@ -55,6 +56,11 @@ SIGNATURES = {
     "mla_prepare_q": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_int, POINTER(c_void_p),
                               POINTER(c_void_p), c_int, c_int, c_void_p, c_int, c_int, c_int, c_int, c_int,
                               c_double, c_void_p]),
+    "mla_qknorm_query": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_int, c_int, c_int, c_double, c_void_p,
+                                 c_void_p]),
+    "mla_qknorm_key_gram": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p]),
+    "mla_qknorm_key_rinv": (c_int, [c_void_p, c_int, c_int64, c_int, c_void_p, c_int, c_int, c_int, c_double,
+                                    c_void_p, c_void_p]),
     "mla_status_string": (ctypes.c_char_p, [c_int]),
     "mla_last_error": (ctypes.c_char_p, []),
     "mla_version": (c_int, []),

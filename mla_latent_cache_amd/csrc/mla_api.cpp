@@ -207,6 +207,44 @@ mla_status mla_combine_out_uv(const float* o_part, const float* lse_part, int n_
                     "mla_combine_out_uv launch");
 }
 
+mla_status mla_qknorm_query(const void* q_nope, int in_dtype, const float* g_q, const float* g_k, int n_tok,
+                            int n_heads, int d_nope, double eps, float* q_out, void* stream) {
+  if (!q_nope || !g_q || !g_k || !q_out) return fail(MLA_ERR_NULL, "mla_qknorm_query: null pointer");
+  if (!dtype_ok(in_dtype)) return fail(MLA_ERR_DTYPE, "mla_qknorm_query: in_dtype %d", in_dtype);
+  if (n_tok < 0 || n_tok > 65535 * 32 || n_heads <= 0 || d_nope <= 0 || (int64_t)n_heads * d_nope > (1 << 24) ||
+      !(eps >= 0.0) || !std::isfinite(eps))
+    return fail(MLA_ERR_SHAPE, "mla_qknorm_query: n_tok=%d n_heads=%d d_nope=%d eps=%g", n_tok, n_heads, d_nope, eps);
+  if (n_tok == 0) return ok();
+  return hip_status(mla::launch_qknorm_query(q_nope, in_dtype == MLA_BF16, g_q, g_k, n_tok, n_heads, d_nope,
+                                             (float)eps, q_out, (hipStream_t)stream),
+                    "mla_qknorm_query launch");
+}
+
+mla_status mla_qknorm_key_gram(const void* w_uk, int w_dtype, int n_heads, int d_nope, int d_c, float* gram,
+                               void* stream) {
+  if (!w_uk || !gram) return fail(MLA_ERR_NULL, "mla_qknorm_key_gram: null pointer");
+  if (!dtype_ok(w_dtype)) return fail(MLA_ERR_DTYPE, "mla_qknorm_key_gram: w_dtype %d", w_dtype);
+  if (n_heads <= 0 || d_nope <= 0 || (int64_t)n_heads * d_nope > (1 << 24) || d_c <= 0 || d_c > 512)
+    return fail(MLA_ERR_SHAPE, "mla_qknorm_key_gram: n_heads=%d d_nope=%d d_c=%d (<= 512)", n_heads, d_nope, d_c);
+  return hip_status(mla::launch_qknorm_key_gram(w_uk, w_dtype == MLA_BF16, n_heads, d_nope, d_c, gram,
+                                                (hipStream_t)stream),
+                    "mla_qknorm_key_gram launch");
+}
+
+mla_status mla_qknorm_key_rinv(const void* rows, int row_dtype, int64_t n_rows, int row_width, const float* gram,
+                               int d_c, int n_heads, int d_nope, double eps, float* rinv, void* stream) {
+  if (!rows || !gram || !rinv) return fail(MLA_ERR_NULL, "mla_qknorm_key_rinv: null pointer");
+  if (!dtype_ok(row_dtype)) return fail(MLA_ERR_DTYPE, "mla_qknorm_key_rinv: row_dtype %d", row_dtype);
+  if (n_rows < 0 || n_rows > ((int64_t)1 << 34) || d_c <= 0 || d_c > 512 || row_width < d_c || n_heads <= 0 ||
+      d_nope <= 0 || !(eps >= 0.0) || !std::isfinite(eps))
+    return fail(MLA_ERR_SHAPE, "mla_qknorm_key_rinv: n_rows=%lld row_width=%d d_c=%d (<= 512) n_heads=%d "
+                "d_nope=%d eps=%g", (long long)n_rows, row_width, d_c, n_heads, d_nope, eps);
+  if (n_rows == 0) return ok();
+  return hip_status(mla::launch_qknorm_key_rinv(rows, row_dtype == MLA_BF16, n_rows, row_width, gram, d_c,
+                                                n_heads * d_nope, (float)eps, rinv, (hipStream_t)stream),
+                    "mla_qknorm_key_rinv launch");
+}
+
 mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q_lat, int q_dtype,
                               int cache_dtype, int batch, int s_q, int n_heads, int d_c, int d_rope, float scale,
                               float* o_part, float* lse_part, int n_part, int n_wg, void* stream) {
@@ -259,6 +297,8 @@ mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q
                     kBf16MaxRows);
       if (batch > 65535 || s.n_split > 65535)
         return fail(MLA_ERR_UNSUPPORTED, "segment %d: bf16 path needs batch and n_split <= 65535", g);
+      if (s.row_rinv && q_dtype != MLA_F32)
+        return fail(MLA_ERR_UNSUPPORTED, "segment %d: QK-Norm (row_rinv) needs an fp32 query", g);
     } else if ((int64_t)batch * s_q * s.head_count > 65535 || s.n_split > 65535) {
       return fail(MLA_ERR_UNSUPPORTED, "segment %d: fp32 path grid too large", g);
     }
@@ -278,7 +318,7 @@ mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q
     mla::DecodeArgs a;
     a.seg = mla::SegArgs{s.cache,     s.block_table, s.seq_lens,  s.q_rot,      s.max_rows,
                          s.page_size, s.max_pages,   s.n_pages,   s.head_begin, s.head_count,
-                         s.causal,    s.part_begin,  s.n_split};
+                         s.causal,    s.part_begin,  s.n_split,   s.row_rinv};
     a.q_lat = q_lat;
     a.o_part = o_part;
     a.lse_part = lse_part;

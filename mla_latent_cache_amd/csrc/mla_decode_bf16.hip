@@ -240,7 +240,9 @@ __device__ __forceinline__ void wait_tiles(int after, bool after_full) {
 }  // namespace
 
 // QF32: q_lat / q_rot are fp32 and split into bf16 hi + lo parts.
-template <int MT, bool QF32>
+// QKN: QK-Norm, the latent part of every score is multiplied by the stored
+// row's inverse key RMS (seg.row_rinv).
+template <int MT, bool QF32, bool QKN>
 __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, int n_share, int n_rg,
                                                                   int rows_total) {
   constexpr int NRB = MT / 16;       // 16-row blocks
@@ -257,7 +259,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
   // the score MFMAs dominate, multiplies lo only at the two rotary k-steps
   // and restores the latent lo part's share of the scores to first order in
   // the lse (LOC below, epilogue).
-  constexpr bool LOC = QF32 && MT == 64;
+  // (the first-order correction needs sum_t p_t c_t to carry the latent
+  // scores' weights, which QK-Norm's per-row factor breaks)
+  constexpr bool LOC = QF32 && MT == 64 && !QKN;
   constexpr int NQH = QF32 && !LOC ? 2 : 1;
   // The KS waves of a group cut the k-steps into parts of equal MFMA count:
   // with LOC the two rotary k-steps cost two MFMAs each, so the 20 MFMA steps
@@ -277,6 +281,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
   const void* const q_lat_p = a.q_lat;
   float* const o_part = a.o_part;
   float* const lse_part = a.lse_part;
+  const float* const row_rinv = a.seg.row_rinv;
   const int64_t max_rows = a.seg.max_rows;
   const int max_pages = a.seg.max_pages;
   const int n_pages = a.seg.n_pages;
@@ -542,11 +547,34 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
         // scores, softmax and P of tile `it`, into P / alpha / flag buffer it & 1.
         // With KS > 1 the waves of a row block exchange partial scores through
         // LDS (one extra barrier) and k-part 0 runs the softmax.
-        auto score_tile = [&](int it) {
+        // QK-Norm factors: the lane's 8 rows of a tile (tokens 16 tb + 4 lg +
+        // e), 1 for rows past the piece.  rinv_row: the tile's first factor
+        // (a scalar block-table load, issued where no LDS access is pending).
+        auto rinv_row = [&](int it) -> const float* {
+          const int t0 = pr0 + it * kTile;
+          if (!bt_row) return row_rinv + (int64_t)b * max_rows + t0;
+          const int pg = sload_i32(bt_row + t0 / kPageSize);
+          return (pg >= 0 && pg < n_pages) ? row_rinv + (int64_t)pg * kPageSize + t0 % kPageSize : nullptr;
+        };
+        auto load_rinv = [&](int it, const float* rr, f32x4& r0v, f32x4& r1v) {
+          const int t0 = pr0 + it * kTile;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = 4 * lg + e;
+            r0v[e] = (rr && t0 + t < pr1) ? rr[t] : 1.f;
+            r1v[e] = (rr && t0 + 16 + t < pr1) ? rr[16 + t] : 1.f;
+          }
+        };
+        // scores of tile `it` with its QK-Norm factors (rc0, rc1) in
+        // registers; the factors of tile it+1 are loaded into (rn0, rn1)
+        auto score_tile = [&](int it, f32x4 rc0, f32x4 rc1, f32x4& rn0, f32x4& rn1) {
           const char* cs = sm.cst[it % kNStage];
           const char* rs = sm.rst[it % kNRStage];
           const int t0 = pr0 + it * kTile;
           const int buf = it & 1;
+          const float* rr_next = nullptr;
+          if constexpr (QKN)
+            if (it + 1 < n_tiles) rr_next = rinv_row(it + 1);
           // accumulators: hi and lo parts (else even and odd k-steps)
           // separately with one row block (two independent chains would stall
           // on each other), shared with two (four chains already)
@@ -558,6 +586,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
             for (int j = 0; j < QBW; ++j)
 #pragma unroll
               for (int hl = 0; hl < NACC; ++hl) sacc[tb][j][hl] = f32x4{0.f, 0.f, 0.f, 0.f};
+          // QK-Norm: the rotary k-steps accumulate apart (they take no factor)
+          f32x4 saccR[2][QKN ? QBW : 1];
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int j = 0; j < (QKN ? QBW : 1); ++j) saccR[tb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
           // K operand of key block tb, k-step ks: row r = 16 tb + l16, chunk
           // 4 ks + lg (latent for ks < 16, rotary after), at its swizzled
           // position.  With xh = l16 >> 2 < 4: cpos(r, 4 ks + lg) * 16 =
@@ -594,16 +628,27 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb) ak[(i + kPre) % (kPre + 1)][tb] = kop(i + kPre, tb);
               }
+              if (QKN && ks0 + i >= kDc / 32) {
 #pragma unroll
-              for (int hl = 0; hl < NQH; ++hl)
+                for (int hl = 0; hl < NQH; ++hl)
 #pragma unroll
-                for (int tb = 0; tb < 2; ++tb)
+                  for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-                  for (int j = 0; j < QBW; ++j) {
-                    const int ai = (NQH == 2 ? hl : i) % NACC;
-                    sacc[tb][j][ai] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[i % (kPre + 1)][tb], qreg[hl][j][i],
-                                                                             sacc[tb][j][ai], 0, 0, 0);
-                  }
+                    for (int j = 0; j < (QKN ? QBW : 1); ++j)
+                      saccR[tb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[i % (kPre + 1)][tb], qreg[hl][j][i],
+                                                                            saccR[tb][j], 0, 0, 0);
+              } else {
+#pragma unroll
+                for (int hl = 0; hl < NQH; ++hl)
+#pragma unroll
+                  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                    for (int j = 0; j < QBW; ++j) {
+                      const int ai = (NQH == 2 ? hl : i) % NACC;
+                      sacc[tb][j][ai] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                          ak[i % (kPre + 1)][tb], qreg[hl][j][i], sacc[tb][j][ai], 0, 0, 0);
+                    }
+              }
               if constexpr (LOC) {
                 if (i >= KLAST - 2 && i < KLAST && rope_part) {
 #pragma unroll
@@ -624,6 +669,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
               sc[tb][j] = sacc[tb][j][0];
               if constexpr (NACC > 1) sc[tb][j] += sacc[tb][j][1];
             }
+          if constexpr (QKN) {
+            // latent part times the row's factor, plus the rotary part; then
+            // the next tile's factors (used a tile from now)
+#pragma unroll
+            for (int j = 0; j < QBW; ++j) {
+              sc[0][j] = sc[0][j] * rc0 + saccR[0][(QKN ? j : 0)];
+              sc[1][j] = sc[1][j] * rc1 + saccR[1][(QKN ? j : 0)];
+            }
+            if (it + 1 < n_tiles) load_rinv(it + 1, rr_next, rn0, rn1);
+          }
           f32x4 sa, sb;  // scores of the softmax block rb, all k-steps
           f32x4* xb = (f32x4*)sm.xbuf;  // [slot][tb][lane]
           if constexpr (QBW == 1) {
@@ -697,14 +752,32 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
           if (lane == 0) sm.flag[buf][rb] = any ? 1 : 0;
         };
 
+        // QK-Norm factors of two tiles: the loop runs two tiles per pass so the
+        // pair swaps roles without a copy (a copy would wait for the loads)
+        f32x4 rA0 = f32x4{1.f, 1.f, 1.f, 1.f}, rA1 = rA0, rB0 = rA0, rB1 = rA0;
+        if constexpr (QKN) load_rinv(0, rinv_row(0), rA0, rA1);
         // tile 0 is in LDS after the first barrier (the PV waves load)
         barrier_raw();
-        score_tile(0);
-        for (int it = 0; it < n_tiles; ++it) {
-          // before barrier `it`: P(it) is written; tile it+1 is in LDS
-          wait_lgkm0();
-          barrier_raw();
-          if (it + 1 < n_tiles) score_tile(it + 1);
+        score_tile(0, rA0, rA1, rB0, rB1);
+        if constexpr (QKN) {
+          for (int it = 0; it < n_tiles; it += 2) {
+            // before barrier `it`: P(it) is written; tile it+1 is in LDS
+            wait_lgkm0();
+            barrier_raw();
+            if (it + 1 < n_tiles) score_tile(it + 1, rB0, rB1, rA0, rA1);
+            if (it + 1 < n_tiles) {
+              wait_lgkm0();
+              barrier_raw();
+              if (it + 2 < n_tiles) score_tile(it + 2, rA0, rA1, rB0, rB1);
+            }
+          }
+        } else {
+          for (int it = 0; it < n_tiles; ++it) {
+            // before barrier `it`: P(it) is written; tile it+1 is in LDS
+            wait_lgkm0();
+            barrier_raw();
+            if (it + 1 < n_tiles) score_tile(it + 1, rA0, rA1, rB0, rB1);
+          }
         }
         // epilogue: 1/l of this row block's rows, and the lse
         const float lt = rows_sum(l_part);
@@ -905,14 +978,27 @@ void decode_bf16_grid(int rows_total, int n_wg, int* n_share, int* n_rg) {
 template <bool QF32>
 static hipError_t launch_mt(const DecodeArgs& a, int mt, dim3 grid, int n_share, int n_rg, int rows_total,
                             hipStream_t stream) {
+  if constexpr (QF32) {
+    if (a.seg.row_rinv) {
+      const dim3 block(kThreads);
+      switch (mt) {
+        case 16:
+          return launch((decode_bf16_kernel<16, true, true>), grid, block, stream, a, n_share, n_rg, rows_total);
+        case 32:
+          return launch((decode_bf16_kernel<32, true, true>), grid, block, stream, a, n_share, n_rg, rows_total);
+        default:
+          return launch((decode_bf16_kernel<64, true, true>), grid, block, stream, a, n_share, n_rg, rows_total);
+      }
+    }
+  }
   const dim3 block(kThreads);
   switch (mt) {
     case 16:
-      return launch((decode_bf16_kernel<16, QF32>), grid, block, stream, a, n_share, n_rg, rows_total);
+      return launch((decode_bf16_kernel<16, QF32, false>), grid, block, stream, a, n_share, n_rg, rows_total);
     case 32:
-      return launch((decode_bf16_kernel<32, QF32>), grid, block, stream, a, n_share, n_rg, rows_total);
+      return launch((decode_bf16_kernel<32, QF32, false>), grid, block, stream, a, n_share, n_rg, rows_total);
     default:
-      return launch((decode_bf16_kernel<64, QF32>), grid, block, stream, a, n_share, n_rg, rows_total);
+      return launch((decode_bf16_kernel<64, QF32, false>), grid, block, stream, a, n_share, n_rg, rows_total);
   }
 }
 

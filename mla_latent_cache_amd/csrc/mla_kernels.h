@@ -22,6 +22,7 @@ struct SegArgs {
   int causal;
   int part_begin;
   int n_split;
+  const float* row_rinv;       // QK-Norm: inverse key RMS per stored row, nullptr => none
 };
 
 struct DecodeArgs {
@@ -71,6 +72,13 @@ hipError_t launch_combine(const float* o_part, const float* lse_part, int n_rows
 hipError_t launch_combine_out_uv(const float* o_part, const float* lse_part, int n_tok, int n_heads, int n_part,
                                  int d_c, const void* w_uv, bool w_bf16, int d_v, void* o_lat, float* lse,
                                  void* out, bool out_bf16, hipStream_t stream);
+// QK-Norm: query scaling, the key Gram matrix and the per-row inverse RMS.
+hipError_t launch_qknorm_query(const void* q_nope, bool in_bf16, const float* g_q, const float* g_k, int n_tok,
+                               int n_heads, int d_nope, float eps, float* q_out, hipStream_t stream);
+hipError_t launch_qknorm_key_gram(const void* w_uk, bool w_bf16, int n_heads, int d_nope, int d_c, float* gram,
+                                  hipStream_t stream);
+hipError_t launch_qknorm_key_rinv(const void* rows, bool row_bf16, int64_t n_rows, int row_width, const float* gram,
+                                  int d_c, int n_hd, float eps, float* rinv, hipStream_t stream);
 // Generic fp32 decode (any d_c <= 512, d_rope <= 128): one wave per
 // (query row, split), equal-length splits per request.
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);

@@ -425,6 +425,122 @@ hipError_t launch_combine_out_uv(const float* o_part, const float* lse_part, int
 }
 
 // ---------------------------------------------------------------------------
+// QK-Norm (QK-Norm MLA page, abstract): RMSNorm after the projections, the
+// statistic over a token's whole content projection.
+//  * qknorm_query_kernel: one block per query token; the sum of squares over
+//    all heads' q_nope, then q_out = g_q g_k q / rms (the static key weight
+//    moved into the query).
+//  * qknorm_gram_kernel: G = sum_h U_K[h]^T U_K[h] (d_c x d_c), one block per
+//    row a of G, threads over b; fp32 sums over the n_heads * d_nope terms.
+//  * qknorm_rinv_kernel: 16 stored rows per block, their latents in LDS;
+//    thread j forms (G c)_j for the 16 rows from column j of G (G is
+//    symmetric, so the reads run along rows of G), then c . G c per row and
+//    1 / sqrt(c.Gc / (n_heads d_nope) + eps), the inverse RMS of the row's
+//    expanded content key over all heads.
+// ---------------------------------------------------------------------------
+template <typename TI>
+__global__ __launch_bounds__(256) void qknorm_query_kernel(const TI* __restrict__ q_nope, const float* __restrict__ g_q,
+                                                           const float* __restrict__ g_k, int n_hd, float eps,
+                                                           float* __restrict__ q_out) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  const TI* q = q_nope + (int64_t)t * n_hd;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < n_hd; i += 256) {
+    const float v = load_f(q + i);
+    ss += v * v;
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  const float inv = 1.f / sqrtf(tot / (float)n_hd + eps);
+  float* o = q_out + (int64_t)t * n_hd;
+  for (int i = threadIdx.x; i < n_hd; i += 256) o[i] = g_q[i] * g_k[i] * load_f(q + i) * inv;
+}
+
+template <typename TW>
+__global__ __launch_bounds__(256) void qknorm_gram_kernel(const TW* __restrict__ w_uk, int n_hd, int d_c,
+                                                          float* __restrict__ gram) {
+  const int a = blockIdx.x;
+  for (int b = threadIdx.x; b < d_c; b += 256) {
+    float acc = 0.f;
+    for (int r = 0; r < n_hd; ++r) acc += load_f(w_uk + (int64_t)r * d_c + a) * load_f(w_uk + (int64_t)r * d_c + b);
+    gram[(int64_t)a * d_c + b] = acc;
+  }
+}
+
+template <typename TI>
+__global__ __launch_bounds__(256) void qknorm_rinv_kernel(const TI* __restrict__ rows, int64_t n_rows, int row_width,
+                                                          const float* __restrict__ gram, int d_c, int n_hd, float eps,
+                                                          float* __restrict__ rinv) {
+  constexpr int R = 16;  // rows per block
+  __shared__ float cs[R][512];
+  __shared__ float part[4][R];
+  const int64_t r0 = (int64_t)blockIdx.x * R;
+  for (int i = threadIdx.x; i < R * d_c; i += 256) {
+    const int rr = i / d_c, k = i % d_c;
+    cs[rr][k] = r0 + rr < n_rows ? load_f(rows + (r0 + rr) * row_width + k) : 0.f;
+  }
+  __syncthreads();
+  float q[R];
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) q[rr] = 0.f;
+  for (int j = threadIdx.x; j < d_c; j += 256) {
+    float y[R];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) y[rr] = 0.f;
+    for (int k = 0; k < d_c; ++k) {
+      const float gkj = gram[(int64_t)k * d_c + j];  // = G[j][k]
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) y[rr] += gkj * cs[rr][k];
+    }
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) q[rr] += cs[rr][j] * y[rr];
+  }
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    const float v = wave_sum(q[rr]);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6][rr] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < R && r0 + threadIdx.x < n_rows) {
+    const int rr = threadIdx.x;
+    const float tot = (part[0][rr] + part[1][rr]) + (part[2][rr] + part[3][rr]);
+    rinv[r0 + rr] = 1.f / sqrtf(tot / (float)n_hd + eps);
+  }
+}
+
+hipError_t launch_qknorm_query(const void* q_nope, bool in_bf16, const float* g_q, const float* g_k, int n_tok,
+                               int n_heads, int d_nope, float eps, float* q_out, hipStream_t stream) {
+  const int n_hd = n_heads * d_nope;
+  if (in_bf16)
+    return launch(qknorm_query_kernel<bf16>, dim3(n_tok), dim3(256), stream, (const bf16*)q_nope, g_q, g_k, n_hd, eps,
+                  q_out);
+  return launch(qknorm_query_kernel<float>, dim3(n_tok), dim3(256), stream, (const float*)q_nope, g_q, g_k, n_hd, eps,
+                q_out);
+}
+
+hipError_t launch_qknorm_key_gram(const void* w_uk, bool w_bf16, int n_heads, int d_nope, int d_c, float* gram,
+                                  hipStream_t stream) {
+  if (w_bf16)
+    return launch(qknorm_gram_kernel<bf16>, dim3(d_c), dim3(256), stream, (const bf16*)w_uk, n_heads * d_nope, d_c,
+                  gram);
+  return launch(qknorm_gram_kernel<float>, dim3(d_c), dim3(256), stream, (const float*)w_uk, n_heads * d_nope, d_c,
+                gram);
+}
+
+hipError_t launch_qknorm_key_rinv(const void* rows, bool row_bf16, int64_t n_rows, int row_width, const float* gram,
+                                  int d_c, int n_hd, float eps, float* rinv, hipStream_t stream) {
+  const dim3 grid((unsigned)((n_rows + 15) / 16));
+  if (row_bf16)
+    return launch(qknorm_rinv_kernel<bf16>, grid, dim3(256), stream, (const bf16*)rows, n_rows, row_width, gram, d_c,
+                  n_hd, eps, rinv);
+  return launch(qknorm_rinv_kernel<float>, grid, dim3(256), stream, (const float*)rows, n_rows, row_width, gram, d_c,
+                n_hd, eps, rinv);
+}
+
+// ---------------------------------------------------------------------------
 // Generic fp32 decode: one wave per (query row, split); split j of request b
 // covers rows [j*L, min((j+1)*L, T_b)) with L = ceil(T_b / n_split).  Scores
 // in fp32 against the stored latent and rotary key (absorbed form), online
@@ -432,6 +548,13 @@ hipError_t launch_combine_out_uv(const float* o_part, const float* lse_part, int
 // ---------------------------------------------------------------------------
 constexpr int kF32MaxDc = 512;
 constexpr int kF32MaxDr = 128;
+
+// Index of stored row t of request b in the cache's row order (the page
+// must be valid: f32_row returned non-null).
+__device__ __forceinline__ int64_t f32_row_index(const SegArgs& s, int b, int t) {
+  if (!s.block_table) return (int64_t)b * s.max_rows + t;
+  return (int64_t)s.block_table[(int64_t)b * s.max_pages + t / s.page_size] * s.page_size + t % s.page_size;
+}
 
 __device__ __forceinline__ const float* f32_row(const SegArgs& s, int b, int t, int rw) {
   if (!s.block_table) return (const float*)s.cache + ((int64_t)b * s.max_rows + t) * rw;
@@ -481,9 +604,11 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
     if (t < rend) {
       const float* rp = f32_row(sg, b, t, rw);
       if (rp) {
-        float dot = 0.f;
-        for (int d = 0; d < rw; ++d) dot += qs[d] * rp[d];
-        sc = dot * a.scale;
+        float dot = 0.f, dot_r = 0.f;
+        for (int d = 0; d < d_c; ++d) dot += qs[d] * rp[d];
+        for (int d = d_c; d < rw; ++d) dot_r += qs[d] * rp[d];
+        if (sg.row_rinv) dot *= sg.row_rinv[f32_row_index(sg, b, t)];
+        sc = (dot + dot_r) * a.scale;
       }
     }
     const float mt = wave_max(sc);

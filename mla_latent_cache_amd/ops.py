@@ -137,6 +137,43 @@ def combine_out_uv(o_part: torch.Tensor, lse_part: torch.Tensor, w_uv: torch.Ten
     return out, o_lat, lse
 
 
+def qknorm_query(q_nope: torch.Tensor, g_q: torch.Tensor, g_k: torch.Tensor, eps: float,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """QK-Norm of the content query with both static weights folded in:
+    [n_tok, H, d_nope] -> fp32 [n_tok, H, d_nope]."""
+    n_tok, n_heads, d_nope = q_nope.shape
+    if g_q.shape != (n_heads, d_nope) or g_k.shape != (n_heads, d_nope):
+        raise ValueError("g_q and g_k must be [n_heads, d_nope]")
+    if out is None:
+        out = torch.empty((n_tok, n_heads, d_nope), dtype=torch.float32, device=q_nope.device)
+    _lib.call("mla_qknorm_query", _ptr(q_nope), _dt(q_nope), _ptr(g_q), _ptr(g_k), n_tok, n_heads, d_nope,
+              float(eps), _ptr(out), _stream())
+    return out
+
+
+def qknorm_key_gram(w_uk: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """G = sum_h U_K[h]^T U_K[h]: [H, d_nope, d_c] -> fp32 [d_c, d_c]."""
+    n_heads, d_nope, d_c = w_uk.shape
+    if out is None:
+        out = torch.empty((d_c, d_c), dtype=torch.float32, device=w_uk.device)
+    _lib.call("mla_qknorm_key_gram", _ptr(w_uk), _dt(w_uk), n_heads, d_nope, d_c, _ptr(out), _stream())
+    return out
+
+
+def qknorm_key_rinv(rows: torch.Tensor, gram: torch.Tensor, n_heads: int, d_nope: int, eps: float,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Inverse RMS of each stored row's content key.  ``rows``: a cache or page
+    pool [..., row_width] (latent first); result fp32 of shape rows.shape[:-1]."""
+    d_c = gram.shape[0]
+    row_width = rows.shape[-1]
+    n_rows = rows.numel() // row_width
+    if out is None:
+        out = torch.empty(rows.shape[:-1], dtype=torch.float32, device=rows.device)
+    _lib.call("mla_qknorm_key_rinv", _ptr(rows), _dt(rows), n_rows, row_width, _ptr(gram), d_c, n_heads,
+              d_nope, float(eps), _ptr(out), _stream())
+    return out
+
+
 @dataclass
 class Segment:
     """Device tensors of one KV segment (see ``mla_segment``)."""
@@ -149,6 +186,7 @@ class Segment:
     causal: bool = False
     part_begin: int = 0
     n_split: int = 1
+    row_rinv: Optional[torch.Tensor] = None      # fp32, cache.shape[:2] (QK-Norm)
 
     def to_c(self) -> MlaSegment:
         s = MlaSegment()
@@ -169,6 +207,7 @@ class Segment:
         s.causal = int(self.causal)
         s.part_begin = self.part_begin
         s.n_split = self.n_split
+        s.row_rinv = _ptr(self.row_rinv)
         return s
 
 

@@ -5,7 +5,13 @@
     rope_relocate_q (once per distinct segment shift) -> mla_absorb_q
     -> mla_decode_splitkv (all segments) -> mla_combine_lse -> mla_out_uv
 
-(the first two as one mla_prepare_q launch for up to 8 distinct shifts)
+(the first two as one mla_prepare_q launch for up to 8 distinct shifts).
+
+With QK-Norm (``qk_norm=(g_q, g_k, eps)``) the chain starts with
+mla_qknorm_query (the normalised, weighted content query in fp32), absorbs
+that with an fp32 copy of U_K, and each segment carries the inverse RMS of
+its rows' content keys, computed once here from the cache (mla_qknorm_key_gram
+and mla_qknorm_key_rinv: the cache writer's share of the work).
 
 and lays out the partial-state slots: segments with disjoint head ranges that
 follow each other share a slot range (e.g. a document read by the Local heads
@@ -42,7 +48,8 @@ def _ceil_div(a: int, b: int) -> int:
 class DecodeStep:
     def __init__(self, q_nope, q_pe, q_pos, w_uk, w_uv, segments: List[StepSegment], batch: int, s_q: int,
                  scale: float, rope_base: float = 10000.0, n_wg: int = 0,
-                 n_split: Optional[Sequence[int]] = None, fuse_post: Optional[bool] = None):
+                 n_split: Optional[Sequence[int]] = None, fuse_post: Optional[bool] = None,
+                 qk_norm: Optional[tuple] = None):
         self.q_nope, self.q_pe, self.q_pos = q_nope, q_pe, q_pos
         self.w_uk, self.w_uv = w_uk, w_uv
         self.batch, self.s_q, self.scale, self.rope_base, self.n_wg = batch, s_q, scale, rope_base, n_wg
@@ -90,10 +97,23 @@ class DecodeStep:
                 part_begin[i] = pb
             pb += m
         self.n_part = pb
+        # QK-Norm: static weights and key statistics
+        self.qk_norm = qk_norm is not None
+        rinvs = [None] * len(segments)
+        if self.qk_norm:
+            g_q, g_k, eps = qk_norm
+            self.g_q = g_q.to(device=dev, dtype=torch.float32).contiguous()
+            self.g_k = g_k.to(device=dev, dtype=torch.float32).contiguous()
+            self.qk_eps = float(eps)
+            self.w_uk_f32 = w_uk.to(torch.float32).contiguous()
+            self.q_norm = torch.empty(q_nope.shape, dtype=torch.float32, device=dev)
+            self.gram = ops.qknorm_key_gram(w_uk)
+            d_nope = w_uk.shape[1]
+            rinvs = [ops.qknorm_key_rinv(s.cache, self.gram, H, d_nope, self.qk_eps) for s in segments]
         self.segments = [
             ops.Segment(cache=s.cache, seq_lens=s.seq_lens, q_rot=self.q_rots[self.seg_rot[i]][1],
                         block_table=s.block_table, head_begin=s.head_begin, head_count=s.head_count,
-                        causal=s.causal, part_begin=part_begin[i], n_split=self.n_split[i])
+                        causal=s.causal, part_begin=part_begin[i], n_split=self.n_split[i], row_rinv=rinvs[i])
             for i, s in enumerate(segments)
         ]
         self.q_lat = torch.empty((n_tok, H, d_c), dtype=q_dt, device=dev)
@@ -125,7 +145,11 @@ class DecodeStep:
             ops.rope_relocate_q(self.q_pe, self.q_pos, shift, self.rope_base, out=q_rot)
 
     def absorb(self):
-        ops.absorb_q(self.q_nope, self.w_uk, out=self.q_lat)
+        if self.qk_norm:
+            ops.qknorm_query(self.q_nope, self.g_q, self.g_k, self.qk_eps, out=self.q_norm)
+            ops.absorb_q(self.q_norm, self.w_uk_f32, out=self.q_lat)
+        else:
+            ops.absorb_q(self.q_nope, self.w_uk, out=self.q_lat)
 
     def decode(self):
         ops.decode_splitkv(self.segments, self.q_lat, self.batch, self.s_q, self.scale, self.o_part,
@@ -139,7 +163,7 @@ class DecodeStep:
 
     def prepare(self):
         """rope (all shifts) and absorb in one launch (mla_prepare_q)."""
-        if len(self.q_rots) > 8:
+        if len(self.q_rots) > 8 or self.qk_norm:
             self.rope()
             self.absorb()
             return
@@ -173,7 +197,7 @@ class DecodeStep:
         n_tok, H, d_nope = self.q_nope.shape
         d_c = self.w_uk.shape[2]
         d_r = self.q_pe.shape[2]
-        if len(self.q_rots) <= 8:  # one launch for rope (all shifts) and absorb
+        if len(self.q_rots) <= 8 and not self.qk_norm:  # one launch for rope (all shifts) and absorb
             self._prep_args = ops.prepare_args(self.q_nope, self.q_pe, self.w_uk, self.q_lat,
                                                [r for _, r in self.q_rots], [s for s, _ in self.q_rots],
                                                self.q_pos, self.rope_base, st)
@@ -183,8 +207,15 @@ class DecodeStep:
                                           self.q_pos.data_ptr(), shift.data_ptr(), n_tok, H, d_r,
                                           float(self.rope_base), st))
                    for shift, q_rot in self.q_rots]
-            pre.append((lib.mla_absorb_q, (self.q_nope.data_ptr(), self.w_uk.data_ptr(), dt(self.q_nope),
-                                           self.q_lat.data_ptr(), dt(self.q_lat), n_tok, H, d_nope, d_c, st)))
+            if self.qk_norm:
+                pre.append((lib.mla_qknorm_query, (self.q_nope.data_ptr(), dt(self.q_nope), self.g_q.data_ptr(),
+                                                   self.g_k.data_ptr(), n_tok, H, d_nope, self.qk_eps,
+                                                   self.q_norm.data_ptr(), st)))
+                pre.append((lib.mla_absorb_q, (self.q_norm.data_ptr(), self.w_uk_f32.data_ptr(), dt(self.q_norm),
+                                               self.q_lat.data_ptr(), dt(self.q_lat), n_tok, H, d_nope, d_c, st)))
+            else:
+                pre.append((lib.mla_absorb_q, (self.q_nope.data_ptr(), self.w_uk.data_ptr(), dt(self.q_nope),
+                                               self.q_lat.data_ptr(), dt(self.q_lat), n_tok, H, d_nope, d_c, st)))
         self._seg_arr = (_lib.MlaSegment * len(self.segments))(*[sg.to_c() for sg in self.segments])
         dec = [(lib.mla_decode_splitkv, (self._seg_arr, len(self.segments), self.q_lat.data_ptr(), dt(self.q_lat),
                                          dt(self.segments[0].cache), self.batch, self.s_q, H, d_c, d_r,
@@ -223,6 +254,9 @@ def step_from_inputs(x, device="cuda", n_wg: int = 0, n_split=None, fuse_post=No
             shift=shift_tok.to(d), shift_host=shift_tok.tolist(),
             block_table=None if s.block_table is None else s.block_table.to(d),
             head_begin=s.head_begin, head_count=s.head_count, causal=s.causal))
+    qk = None
+    if getattr(x, "g_q", None) is not None:
+        qk = (x.g_q.to(d), x.g_k.to(d), x.spec.qk_eps)
     return DecodeStep(x.q_nope.to(d), x.q_pe.to(d), x.q_pos.to(d), x.w_uk.to(d), x.w_uv.to(d), segs,
                       x.spec.batch, x.spec.s_q, x.scale, x.rope_base, n_wg=n_wg, n_split=n_split,
-                      fuse_post=fuse_post)
+                      fuse_post=fuse_post, qk_norm=qk)

@@ -28,9 +28,10 @@ def oracle_segments(x):
 
 def oracle_decode(x, requests=None, heads=None):
     """(o, o_lat, lse) of the direct form for the given requests/heads (NaN elsewhere)."""
+    qk = O.QKNorm(f64(x.g_q), f64(x.g_k), x.spec.qk_eps) if x.g_q is not None else None
     return O.direct_mla_decode(f64(x.q_nope), f64(x.q_pe), x.q_pos.numpy(), f64(x.w_uk), f64(x.w_uv),
                                oracle_segments(x), x.scale, x.rope_base, x.spec.s_q,
-                               requests=requests, heads=heads)
+                               requests=requests, heads=heads, qk_norm=qk)
 
 
 def tol_check(name, got, ref, fp32: bool, kind: str, mask=None):

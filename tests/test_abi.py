@@ -94,6 +94,22 @@ def test_null_and_shape_errors_before_any_gpu_call(lib):
     assert _st(lib, "mla_combine_out_uv", P, P, 1, 1, 4, 510, P, 1, 128, None, None, P, 1, None) == 2
     assert _st(lib, "mla_combine_out_uv", P + 4, P, 1, 1, 4, 512, P, 1, 128, None, None, P, 1, None) == 2
     assert _st(lib, "mla_combine_out_uv", P, P, 0, 1, 4, 512, P, 1, 128, None, None, P, 1, None) == 0
+    # mla_qknorm_query(q_nope, in_dtype, g_q, g_k, n_tok, n_heads, d_nope, eps, q_out, stream)
+    assert _st(lib, "mla_qknorm_query", P, 1, P, None, 1, 16, 128, 1e-6, P, None) == 1
+    assert _st(lib, "mla_qknorm_query", P, 3, P, P, 1, 16, 128, 1e-6, P, None) == 3
+    assert _st(lib, "mla_qknorm_query", P, 1, P, P, 1, 16, 128, -1.0, P, None) == 2
+    assert _st(lib, "mla_qknorm_query", P, 1, P, P, 1, 16, 128, float("inf"), P, None) == 2
+    assert _st(lib, "mla_qknorm_query", P, 1, P, P, 1, 0, 128, 1e-6, P, None) == 2
+    assert _st(lib, "mla_qknorm_query", P, 1, P, P, 0, 16, 128, 1e-6, P, None) == 0
+    # mla_qknorm_key_gram(w_uk, w_dtype, n_heads, d_nope, d_c, gram, stream)
+    assert _st(lib, "mla_qknorm_key_gram", None, 1, 16, 128, 512, P, None) == 1
+    assert _st(lib, "mla_qknorm_key_gram", P, 1, 16, 128, 1024, P, None) == 2
+    assert _st(lib, "mla_qknorm_key_gram", P, 2, 16, 128, 512, P, None) == 3
+    # mla_qknorm_key_rinv(rows, dtype, n_rows, row_width, gram, d_c, n_heads, d_nope, eps, rinv, stream)
+    assert _st(lib, "mla_qknorm_key_rinv", P, 1, 10, 500, P, 512, 16, 128, 1e-6, P, None) == 2
+    assert _st(lib, "mla_qknorm_key_rinv", P, 1, 10, 576, P, 512, 16, 128, float("nan"), P, None) == 2
+    assert _st(lib, "mla_qknorm_key_rinv", P, 1, 10, 576, None, 512, 16, 128, 1e-6, P, None) == 1
+    assert _st(lib, "mla_qknorm_key_rinv", P, 1, 0, 576, P, 512, 16, 128, 1e-6, P, None) == 0
     # zero-size calls succeed without launching anything
     assert _st(lib, "mla_absorb_q", P, P, 1, P, 0, 0, 1, 128, 512, None) == 0
 
@@ -123,3 +139,4 @@ def test_null_and_shape_errors_before_any_gpu_call(lib):
     assert dec([seg(causal=2)]) == 2
     assert dec([seg(head_count=4)], n_heads=4, dtype=7) == 3
     assert dec([seg()], dtype=0, q_dtype=1) == 5          # fp32 cache needs an fp32 query
+    assert dec([seg(row_rinv=P)], q_dtype=1) == 5         # QK-Norm factors need an fp32 query

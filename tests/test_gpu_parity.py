@@ -117,6 +117,14 @@ EDGE = {
         SegSpec("kv", lengths=(1, 37, 300, 1000), online=True),)),
     "toy_f32_ragged": _custom("edge-f32", dtype="f32", batch=3, heads=2, scale=1 / math.sqrt(6), segs=(
         SegSpec("kv", lengths=(16, 0, 130), layout="paged", page_size=8, spare_pages=1, online=True),)),
+    # QK-Norm: per-row key factors through each row-group size (16, 32, 64
+    # query rows), contiguous and paged, and the fp32 path
+    "qknorm_paged_rows64": _custom("edge-qkn64", batch=4, heads=64, qk_norm=True, segs=(
+        SegSpec("kv", lengths=(1, 37, 300, 1000), layout="paged", page_size=64, spare_pages=2, online=True),)),
+    "qknorm_rows32_sq2": _custom("edge-qkn32", batch=3, heads=16, s_q=2, qk_norm=True, qk_eps=0.5, segs=(
+        SegSpec("kv", lengths=(2, 95, 513), causal=True, online=True),)),
+    "qknorm_toy_f32": _custom("edge-qknf32", dtype="f32", batch=3, heads=2, qk_norm=True, segs=(
+        SegSpec("kv", lengths=(16, 0, 130), layout="paged", page_size=8, spare_pages=1, online=True),)),
 }
 
 
@@ -233,6 +241,35 @@ def test_combine_call(out_dtype, n_rows):
         assert np.all(np.abs(got - o_ref) <= rel * np.abs(o_ref) + 1e-6), r
 
 
+@pytest.mark.parametrize("dtype,dims", [(torch.float32, (7, 5, 24, 40, 48, 37)),
+                                        (torch.bfloat16, (3, 16, 128, 512, 576, 70))])
+def test_qknorm_calls(dtype, dims):
+    """mla_qknorm_query / _key_gram / _key_rinv against the direct RMS of the
+    query over all heads and of each row's expanded key U_K c over all heads."""
+    from mla_latent_cache_amd import ops
+    n_tok, H, d_nope, d_c, rw, n_rows = dims
+    eps = 0.25
+    q = _rand((n_tok, H, d_nope), dtype, 41)
+    g_q = 1 + 0.1 * _rand((H, d_nope), torch.float32, 42)
+    g_k = 1 + 0.1 * _rand((H, d_nope), torch.float32, 43)
+    w = (_rand((H, d_nope, d_c), torch.float32, 44) / math.sqrt(d_c)).to(dtype)
+    rows = _rand((n_rows, rw), dtype, 45)
+    rows[3] = 0                                 # zero key: rinv = 1/sqrt(eps) = 2
+    q_out = ops.qknorm_query(q.cuda(), g_q.cuda(), g_k.cuda(), eps)
+    gram = ops.qknorm_key_gram(w.cuda())
+    rinv = ops.qknorm_key_rinv(rows.cuda(), gram, H, d_nope, eps)
+    torch.cuda.synchronize()
+    for t in range(n_tok):
+        ref = f64(g_q) * f64(g_k) * f64(q[t]) * O.rms_inverse(f64(q[t]), eps)
+        assert np.all(np.abs(f64(q_out[t]) - ref) <= 1e-5 * np.abs(ref) + 1e-7), t
+    wf = f64(w).reshape(H * d_nope, d_c)
+    g_ref = wf.T @ wf
+    assert np.max(np.abs(f64(gram) - g_ref)) <= 1e-5 * np.max(np.abs(g_ref))
+    r_ref = O.key_rms_inverse(f64(w), f64(rows)[:, :d_c], eps)
+    assert abs(float(rinv[3]) - 2.0) <= 1e-6
+    assert np.all(np.abs(f64(rinv) - r_ref) <= 1e-4 * r_ref)
+
+
 # ------------------------------------------------------------ full sizes, sampled
 @pytest.mark.parametrize("out_dtype,w_dtype,dims", [
     (torch.bfloat16, torch.bfloat16, (4, 16, 65, 512, 128)),   # the 512-column register path
@@ -270,14 +307,14 @@ def test_combine_out_uv_call(out_dtype, w_dtype, dims):
     assert np.all(np.abs(f64(out) - out_ref) <= rel * np.abs(out_ref) + 1e-5 * rms)
 
 
-@pytest.mark.parametrize("name", ["small", "dsv3", "long", "merge", "prefill"])
+@pytest.mark.parametrize("name", ["small", "dsv3", "long", "merge", "prefill", "qknorm"])
 def test_full_size_sampled(name):
     """The bench's launch configuration (default grid) at full size; the
     oracle checks sampled (request, head) pairs."""
     x = M.make(name, SEEDS[name])
     print(f"[parity] full {name} seed {SEEDS[name]}", flush=True)
     _, out, o_lat, lse = _run(x)
-    n_req = {"small": 2, "dsv3": 3, "long": 1, "merge": 2, "prefill": 1}[name]
+    n_req = {"small": 2, "dsv3": 3, "long": 1, "merge": 2, "prefill": 1, "qknorm": 2}[name]
     reqs, heads = sample_pairs(x, n_req, 3, seed=SEEDS[name])
     errs = check_step(x, out, o_lat, lse, requests=reqs, heads=heads, label=f"{name} full")
     print(f"[parity] {name} full reqs={reqs} heads={heads}: {errs}", flush=True)
