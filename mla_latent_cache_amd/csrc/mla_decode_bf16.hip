@@ -152,11 +152,17 @@ __device__ __forceinline__ char* dma_dst(const TileDma& d, int k) {
   return k < kTile ? d.cdst + k * 1024 : d.rdst + (k - kTile) * 1024;
 }
 
+// UNI: the loader index (hence k) is wave-uniform and held opaque in a
+// scalar register, so the latent/rotary choice is a scalar branch and no
+// per-instruction offset is hoisted; else it is a lane value and both sides
+// run under the exec mask (fewer branches, more vector registers).
+template <bool UNI>
 __device__ __forceinline__ void issue_dma_one(const TileDma& d, int k, int lane) {
   // Opaque copy of the lane index: the offsets are recomputed at every
   // instruction (a few integer ops) instead of being hoisted out of the tile
   // loop and pinning registers for the whole loop.
   asm volatile("" : "+v"(lane));
+  if constexpr (UNI) asm volatile("" : "+s"(k));
   const int off = dma_src_off(k, lane);
   char* dst = dma_dst(d, k);
   if (off < d.lim) {  // the lane's row is a valid row of the tile
@@ -174,21 +180,25 @@ static_assert(kNDma % kLoaders == 0, "every loader issues the same count");
 // issues it from a uniform base plus a lane offset of two or three integer
 // ops (no bounds check, every lane valid), a partial tile takes the
 // bounds-checked path with zero fill.  `lane` should be opaque to the
-// compiler, or it hoists the nine offsets into live registers.
+// compiler, or it hoists the nine offsets into live registers (`ld` too with
+// UNI, see issue_dma_one).
+template <bool UNI>
 __device__ __forceinline__ void issue_dma_fast(const TileDma& d, int ld, int i, int lane) {
+  if constexpr (UNI) asm volatile("" : "+s"(ld));
   const int k = ld + kLoaders * i;
   if (d.lim == kTile * kRowBytes) {
     __builtin_amdgcn_global_load_lds((const void*)(d.src + (unsigned)dma_src_off(k, lane)),
                                      (MLA_LDS void*)dma_dst(d, k), 16, 0, 0);
   } else {
-    issue_dma_one(d, k, lane);
+    issue_dma_one<UNI>(d, k, lane);
   }
 }
 
 // All of loader `ld`'s instructions of a tile at once.
+template <bool UNI>
 __device__ __forceinline__ void issue_tile_dma(const TileDma& d, int ld, int lane) {
 #pragma unroll
-  for (int i = 0; i < kDmaPerWave; ++i) issue_dma_one(d, ld + kLoaders * i, lane);
+  for (int i = 0; i < kDmaPerWave; ++i) issue_dma_one<UNI>(d, ld + kLoaders * i, lane);
 }
 
 // First byte of tile rows [t0, ...) of request b: contiguous cache, or the
@@ -390,7 +400,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
   const int s_row = Rc / hc;
   const int64_t q_off = (int64_t)s_row * n_heads + head_begin + Rc % hc;  // without the request part
   const int s_min = row0 / hc;       // smallest token index among the group's rows
-  const int pw = wave - 4;           // column slice of a PV wave
+  // column slice of a PV wave and its loader index.  With QK-Norm (the
+  // register-heaviest variant) it is the scalar copy, so the tile loads
+  // branch on it (issue_dma_one); elsewhere the lane value measured faster.
+  const int pw = (QKN ? wave_s : wave) - 4;
 
   int base = 0;  // prefix of padded T over requests scanned so far (wave 0)
   for (int chunk = 0;; ++chunk) {
@@ -476,7 +489,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
         const char* src = tile_src(cache, req_base, bt_row, n_pages, t0, &ok);
         return TileDma{sm.cst[it % kNStage], sm.rst[it % kNRStage], src, ok ? min(kTile, pr1 - t0) * kRowBytes : 0};
       };
-      auto load_tile = [&](int it) { issue_tile_dma(tile_dma(it), wave - 4, lane); };
+      auto load_tile = [&](int it) { issue_tile_dma<QKN>(tile_dma(it), pw, lane); };
 
       // The two roles run separate copies of the tile loop with the same
       // barrier sequence (1 + n_tiles + 1 barriers, plus one exchange barrier
@@ -548,26 +561,34 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
         // With KS > 1 the waves of a row block exchange partial scores through
         // LDS (one extra barrier) and k-part 0 runs the softmax.
         // QK-Norm factors: the lane's 8 rows of a tile (tokens 16 tb + 4 lg +
-        // e), 1 for rows past the piece.  rinv_row: the tile's first factor
-        // (a scalar block-table load, issued where no LDS access is pending).
+        // e).  rinv_row: the tile's first factor (a scalar block-table load,
+        // issued where no LDS access is pending), null for a page outside the
+        // pool (its tile reads as zeros and takes factor 1).
         auto rinv_row = [&](int it) -> const float* {
           const int t0 = pr0 + it * kTile;
           if (!bt_row) return row_rinv + (int64_t)b * max_rows + t0;
           const int pg = sload_i32(bt_row + t0 / kPageSize);
           return (pg >= 0 && pg < n_pages) ? row_rinv + (int64_t)pg * kPageSize + t0 % kPageSize : nullptr;
         };
-        auto load_rinv = [&](int it, const float* rr, f32x4& r0v, f32x4& r1v) {
-          const int t0 = pr0 + it * kTile;
+        // The loads are unconditional (a select on a loaded value would wait
+        // for it here): rows past the piece repeat its last row's factor, in
+        // bounds and finite, and their scores are masked later.  Returns
+        // whether the factors are real (false: use 1).
+        auto load_rinv = [&](int it, const float* rr, f32x4& r0v, f32x4& r1v) -> bool {
+          const int lim = pr1 - 1 - (pr0 + it * kTile);  // >= 0: the tile starts inside the piece
+          const float* src = rr ? rr : row_rinv;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int t = 4 * lg + e;
-            r0v[e] = (rr && t0 + t < pr1) ? rr[t] : 1.f;
-            r1v[e] = (rr && t0 + 16 + t < pr1) ? rr[16 + t] : 1.f;
+            r0v[e] = src[min(t, lim)];
+            r1v[e] = src[min(16 + t, lim)];
           }
+          return rr != nullptr;
         };
-        // scores of tile `it` with its QK-Norm factors (rc0, rc1) in
-        // registers; the factors of tile it+1 are loaded into (rn0, rn1)
-        auto score_tile = [&](int it, f32x4 rc0, f32x4 rc1, f32x4& rn0, f32x4& rn1) {
+        // scores of tile `it` with its QK-Norm factors (rf0, rf1) in
+        // registers; once they are applied, the same registers receive the
+        // factors of tile it+1 (applied a tile later, so the loads have time)
+        auto score_tile = [&](int it, f32x4& rf0, f32x4& rf1, bool& rf_ok) {
           const char* cs = sm.cst[it % kNStage];
           const char* rs = sm.rst[it % kNRStage];
           const int t0 = pr0 + it * kTile;
@@ -586,12 +607,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
             for (int j = 0; j < QBW; ++j)
 #pragma unroll
               for (int hl = 0; hl < NACC; ++hl) sacc[tb][j][hl] = f32x4{0.f, 0.f, 0.f, 0.f};
-          // QK-Norm: the rotary k-steps accumulate apart (they take no factor)
-          f32x4 saccR[2][QKN ? QBW : 1];
-#pragma unroll
-          for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-            for (int j = 0; j < (QKN ? QBW : 1); ++j) saccR[tb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
           // K operand of key block tb, k-step ks: row r = 16 tb + l16, chunk
           // 4 ks + lg (latent for ks < 16, rotary after), at its swizzled
           // position.  With xh = l16 >> 2 < 4: cpos(r, 4 ks + lg) * 16 =
@@ -628,27 +643,28 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb) ak[(i + kPre) % (kPre + 1)][tb] = kop(i + kPre, tb);
               }
-              if (QKN && ks0 + i >= kDc / 32) {
+              if (QKN && ks0 + i == kDc / 32) {
+                // QK-Norm: the latent part so far takes the rows' factors
+                // before the rotary k-steps add to it (they take none)
 #pragma unroll
-                for (int hl = 0; hl < NQH; ++hl)
+                for (int tb = 0; tb < 2; ++tb) {
+                  const f32x4 f = !rf_ok ? f32x4{1.f, 1.f, 1.f, 1.f} : tb ? rf1 : rf0;
 #pragma unroll
-                  for (int tb = 0; tb < 2; ++tb)
+                  for (int j = 0; j < QBW; ++j)
 #pragma unroll
-                    for (int j = 0; j < (QKN ? QBW : 1); ++j)
-                      saccR[tb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[i % (kPre + 1)][tb], qreg[hl][j][i],
-                                                                            saccR[tb][j], 0, 0, 0);
-              } else {
-#pragma unroll
-                for (int hl = 0; hl < NQH; ++hl)
-#pragma unroll
-                  for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-                    for (int j = 0; j < QBW; ++j) {
-                      const int ai = (NQH == 2 ? hl : i) % NACC;
-                      sacc[tb][j][ai] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                          ak[i % (kPre + 1)][tb], qreg[hl][j][i], sacc[tb][j][ai], 0, 0, 0);
-                    }
+                    for (int hl = 0; hl < NACC; ++hl) sacc[tb][j][hl] *= f;
+                }
               }
+#pragma unroll
+              for (int hl = 0; hl < NQH; ++hl)
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                  for (int j = 0; j < QBW; ++j) {
+                    const int ai = (NQH == 2 ? hl : i) % NACC;
+                    sacc[tb][j][ai] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        ak[i % (kPre + 1)][tb], qreg[hl][j][i], sacc[tb][j][ai], 0, 0, 0);
+                  }
               if constexpr (LOC) {
                 if (i >= KLAST - 2 && i < KLAST && rope_part) {
 #pragma unroll
@@ -670,14 +686,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
               if constexpr (NACC > 1) sc[tb][j] += sacc[tb][j][1];
             }
           if constexpr (QKN) {
-            // latent part times the row's factor, plus the rotary part; then
-            // the next tile's factors (used a tile from now)
+            // a k-part with no rotary step applies the factors here; then the
+            // next tile's factors
+            if (ks0 + kcnt <= kDc / 32 && rf_ok) {
 #pragma unroll
-            for (int j = 0; j < QBW; ++j) {
-              sc[0][j] = sc[0][j] * rc0 + saccR[0][(QKN ? j : 0)];
-              sc[1][j] = sc[1][j] * rc1 + saccR[1][(QKN ? j : 0)];
+              for (int j = 0; j < QBW; ++j) {
+                sc[0][j] *= rf0;
+                sc[1][j] *= rf1;
+              }
             }
-            if (it + 1 < n_tiles) load_rinv(it + 1, rr_next, rn0, rn1);
+            if (it + 1 < n_tiles) rf_ok = load_rinv(it + 1, rr_next, rf0, rf1);
           }
           f32x4 sa, sb;  // scores of the softmax block rb, all k-steps
           f32x4* xb = (f32x4*)sm.xbuf;  // [slot][tb][lane]
@@ -752,32 +770,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
           if (lane == 0) sm.flag[buf][rb] = any ? 1 : 0;
         };
 
-        // QK-Norm factors of two tiles: the loop runs two tiles per pass so the
-        // pair swaps roles without a copy (a copy would wait for the loads)
-        f32x4 rA0 = f32x4{1.f, 1.f, 1.f, 1.f}, rA1 = rA0, rB0 = rA0, rB1 = rA0;
-        if constexpr (QKN) load_rinv(0, rinv_row(0), rA0, rA1);
+        // QK-Norm factors of the tile being scored (1 without QK-Norm)
+        f32x4 rf0 = f32x4{1.f, 1.f, 1.f, 1.f}, rf1 = rf0;
+        bool rf_ok = false;
+        if constexpr (QKN) rf_ok = load_rinv(0, rinv_row(0), rf0, rf1);
         // tile 0 is in LDS after the first barrier (the PV waves load)
         barrier_raw();
-        score_tile(0, rA0, rA1, rB0, rB1);
-        if constexpr (QKN) {
-          for (int it = 0; it < n_tiles; it += 2) {
-            // before barrier `it`: P(it) is written; tile it+1 is in LDS
-            wait_lgkm0();
-            barrier_raw();
-            if (it + 1 < n_tiles) score_tile(it + 1, rB0, rB1, rA0, rA1);
-            if (it + 1 < n_tiles) {
-              wait_lgkm0();
-              barrier_raw();
-              if (it + 2 < n_tiles) score_tile(it + 2, rA0, rA1, rB0, rB1);
-            }
-          }
-        } else {
-          for (int it = 0; it < n_tiles; ++it) {
-            // before barrier `it`: P(it) is written; tile it+1 is in LDS
-            wait_lgkm0();
-            barrier_raw();
-            if (it + 1 < n_tiles) score_tile(it + 1, rA0, rA1, rB0, rB1);
-          }
+        score_tile(0, rf0, rf1, rf_ok);
+        for (int it = 0; it < n_tiles; ++it) {
+          // before barrier `it`: P(it) is written; tile it+1 is in LDS
+          wait_lgkm0();
+          barrier_raw();
+          if (it + 1 < n_tiles) score_tile(it + 1, rf0, rf1, rf_ok);
         }
         // epilogue: 1/l of this row block's rows, and the lse
         const float lt = rows_sum(l_part);
@@ -872,7 +876,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
           asm volatile("" : "+v"(dlane));
           if (with_dma) {
 #pragma unroll
-            for (int i = 0; i < 5; ++i) issue_dma_fast(dma, pw, i, dlane);
+            for (int i = 0; i < 5; ++i) issue_dma_fast<QKN>(dma, pw, i, dlane);
           }
 
           if (flag) {
@@ -889,7 +893,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
             // the score waves' mid-tile exchange barrier (their next tile): half
             // of this tile's MFMAs and loads overlap their QK, half their softmax
             if (db == 4 && with_x) barrier_raw();
-            if (with_dma && db % 2 == 0) issue_dma_fast(dma, pw, 5 + db / 2, dlane);
+            if (with_dma && db % 2 == 0) issue_dma_fast<QKN>(dma, pw, 5 + db / 2, dlane);
 #pragma unroll
             for (int q = 0; q < NRB; ++q)
               acc_o[db][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ac[db], bq[q], acc_o[db][q], 0, 0, 0);
