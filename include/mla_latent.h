@@ -241,8 +241,10 @@ mla_status mla_out_uv(const void* o_lat, int o_dtype, const void* w_uv, int w_dt
  *   out[t][h][i] = sum_j w_uv[h][i][j] * o[r][j]             (fp32 accumulation)
  * A row whose slots are all -inf gives o = 0, out = 0, lse = -inf; o_part
  * rows of -inf slots are never read.  The merged row enters U_V in fp32 (the
- * two-call path rounds o_lat to out_dtype first).  One workgroup per row
- * reads its head's U_V: meant for few query tokens per head.
+ * two-call path rounds o_lat to out_dtype first).  Every row reads its
+ * head's U_V: meant for few query tokens per head.  With few rows (<= 128)
+ * each row's output columns are split over 2 or 4 workgroups, each of which
+ * merges the row itself.
  *
  * o_part   [n_tok][n_heads][n_part][d_c] fp32 (16-byte aligned)
  * lse_part [n_tok][n_heads][n_part]      fp32 (n_part <= 1024)
@@ -250,7 +252,8 @@ mla_status mla_out_uv(const void* o_lat, int o_dtype, const void* w_uv, int w_dt
  * o_lat    [n_tok][n_heads][d_c]         out_dtype, or NULL if not wanted
  * lse      [n_tok][n_heads]              fp32, or NULL if not wanted
  * out      [n_tok][n_heads][d_v]         out_dtype
- * Shapes: d_c a multiple of 4, d_c <= 512; d_v <= 128; n_tok, n_heads <= 65535.
+ * Shapes: d_c a multiple of 4, d_c <= 512; d_v <= 128; n_tok, n_heads <= 65535,
+ * n_tok * n_heads <= 2^24.
  * Errors: MLA_ERR_NULL, MLA_ERR_DTYPE, MLA_ERR_SHAPE as for the two calls.
  */
 mla_status mla_combine_out_uv(const float* o_part, const float* lse_part, int n_tok, int n_heads, int n_part,

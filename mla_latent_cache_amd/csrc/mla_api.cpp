@@ -196,10 +196,11 @@ mla_status mla_combine_out_uv(const float* o_part, const float* lse_part, int n_
   if (!o_part || !lse_part || !w_uv || !out) return fail(MLA_ERR_NULL, "mla_combine_out_uv: null pointer");
   if (!dtype_ok(w_dtype) || !dtype_ok(out_dtype))
     return fail(MLA_ERR_DTYPE, "mla_combine_out_uv: dtypes %d, %d", w_dtype, out_dtype);
-  if (n_tok < 0 || n_tok > 65535 || n_heads <= 0 || n_heads > 65535 || n_part <= 0 || n_part > 1024 || d_c <= 0 ||
-      d_c > 512 || (d_c & 3) || d_v <= 0 || d_v > 128 || ((reinterpret_cast<uintptr_t>(o_part) & 15u) != 0))
-    return fail(MLA_ERR_SHAPE, "mla_combine_out_uv: n_tok=%d n_heads=%d n_part=%d (<= 1024) d_c=%d (multiple of 4, "
-                "<= 512) d_v=%d (<= 128), o_part 16-byte aligned", n_tok, n_heads, n_part, d_c, d_v);
+  if (n_tok < 0 || n_tok > 65535 || n_heads <= 0 || n_heads > 65535 || (int64_t)n_tok * n_heads > (1 << 24) ||
+      n_part <= 0 || n_part > 1024 || d_c <= 0 || d_c > 512 || (d_c & 3) || d_v <= 0 || d_v > 128 ||
+      ((reinterpret_cast<uintptr_t>(o_part) & 15u) != 0))
+    return fail(MLA_ERR_SHAPE, "mla_combine_out_uv: n_tok=%d n_heads=%d (rows <= 2^24) n_part=%d (<= 1024) d_c=%d "
+                "(multiple of 4, <= 512) d_v=%d (<= 128), o_part 16-byte aligned", n_tok, n_heads, n_part, d_c, d_v);
   if (n_tok == 0) return ok();
   return hip_status(mla::launch_combine_out_uv(o_part, lse_part, n_tok, n_heads, n_part, d_c, w_uv,
                                                w_dtype == MLA_BF16, d_v, o_lat, lse, out, out_dtype == MLA_BF16,

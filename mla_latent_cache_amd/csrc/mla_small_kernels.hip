@@ -272,40 +272,60 @@ hipError_t launch_combine(const float* o_part, const float* lse_part, int n_rows
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge and value expansion in one pass (MLA tutorial page, "Move
 // the Value Expansion After the Weighted Sum"; RedKnot-MLA abstract: the
-// merged state goes through one shared output projection).  One 1024-thread
-// block per (token, head) row:
+// merged state goes through one shared output projection).  NQ 1024-thread
+// blocks per (token, head) row, block q producing output columns
+// [q dq, (q + 1) dq), dq = ceil(d_v / NQ); each merges the whole row (the
+// repeated partial reads of a row's NQ blocks meet in L2: a row's blocks,
+// and the rows of one head, are numbered onto one XCD):
 //  * the head's U_V rows are loaded first (bf16, d_c = 512: thread (v, part)
-//    holds columns 64 k + 8 part .. + 7 of row v in registers), independent
-//    of the merge, so their latency overlaps it;
+//    of the TPO = 8 NQ threads of row v holds columns 64 NQ k + 8 part .. + 7,
+//    k < 8 / NQ, in registers), independent of the merge, so their latency
+//    overlaps it;
 //  * wave 0 compacts the live slots and their weights as combine_kernel does
 //    (its lse loads go out before its weight loads);
 //  * 8 slot groups of 128 column threads (float4) sum the live partials and
 //    the group sums are added in a fixed order into the fp32 row o (LDS),
 //    stored as o_lat when asked for;
-//  * out[v] = sum_c U_V[v][c] o[c]: the 8 threads of row v each take every
-//    8th group of 8 columns and add their sums with lane shuffles.  o enters
-//    the product in fp32.
-// Each block reads its head's d_v x d_c weights, so this suits few query
-// tokens; many tokens use combine_kernel and the out_uv kernels.
+//  * out[v] = sum_c U_V[v][c] o[c]: the TPO threads of row v each take every
+//    TPO-th group of 8 columns and add their sums with lane shuffles.  o
+//    enters the product in fp32.
+// Each row reads its head's d_v x d_c weights, so this suits few query
+// tokens; many tokens use combine_kernel and the out_uv kernels.  NQ > 1
+// spreads few rows over more CUs (each block is bound by what one CU can
+// fetch).
 // ---------------------------------------------------------------------------
-template <typename TO, typename TW, bool VEC>
+template <typename TO, typename TW, bool VEC, int NQ>
 __global__ __launch_bounds__(1024) void combine_out_uv_kernel(const float* __restrict__ o_part,
-                                                              const float* __restrict__ lse_part, int n_heads,
-                                                              int n_part, int d_c, const TW* __restrict__ w_uv,
-                                                              int d_v, TO* __restrict__ o_lat,
-                                                              float* __restrict__ lse, TO* __restrict__ out) {
+                                                              const float* __restrict__ lse_part, int n_tok,
+                                                              int n_heads, int n_part, int d_c,
+                                                              const TW* __restrict__ w_uv, int d_v,
+                                                              TO* __restrict__ o_lat, float* __restrict__ lse,
+                                                              TO* __restrict__ out) {
+  constexpr int TPO = 8 * NQ;  // threads per output column
+  constexpr int NW = 8 / NQ;   // bf16x8 weight chunks per thread (VEC)
   __shared__ int live_idx[kCombMaxPart];
   __shared__ float live_w[kCombMaxPart];
   __shared__ f32x4 red[7 * 128];
   __shared__ __attribute__((aligned(16))) float o_s[512];
   __shared__ float s_inv, s_lse;
   __shared__ int s_n;
-  const int h = blockIdx.x, t = blockIdx.y;
+  // block -> (head, token, q): consecutive items share an XCD (block b runs
+  // on XCD b % 8); q fastest, then token, then head
+  const int n_items = n_heads * n_tok * NQ;
+  const int per = (n_items + 7) / 8;
+  const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (item >= n_items) return;
+  const int q = item % NQ;
+  const int t = (item / NQ) % n_tok;
+  const int h = item / (NQ * n_tok);
   const int64_t row = (int64_t)t * n_heads + h;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int v = tid >> 3, part = tid & 7;  // output column and its eighth of the d_c columns
-  const TW* wrow = w_uv + ((int64_t)h * d_v + (v < d_v ? v : 0)) * d_c;
+  const int dq = (d_v + NQ - 1) / NQ;
+  const int vl = tid / TPO, part = tid % TPO;  // output column (of this block's dq) and its share of d_c
+  const int v = q * dq + vl;
+  const bool v_ok = vl < dq && v < d_v;
+  const TW* wrow = w_uv + ((int64_t)h * d_v + (v_ok ? v : 0)) * d_c;
   const float* lp = lse_part + row * n_part;
   // wave 0 issues its lse loads before the weights: loads return in order
   float lv0 = -INFINITY, lv1 = -INFINITY;
@@ -314,10 +334,10 @@ __global__ __launch_bounds__(1024) void combine_out_uv_kernel(const float* __res
     lv1 = lane + 64 < n_part ? lp[lane + 64] : -INFINITY;
   }
   __builtin_amdgcn_sched_barrier(0);
-  bf16x8 wv[VEC ? 8 : 1];
+  bf16x8 wv[VEC ? NW : 1];
   if constexpr (VEC) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) wv[k] = v < d_v ? *(const bf16x8*)(wrow + 64 * k + 8 * part) : bf16x8{};
+    for (int k = 0; k < NW; ++k) wv[k] = v_ok ? *(const bf16x8*)(wrow + 8 * TPO * k + 8 * part) : bf16x8{};
   }
   if (tid < 64) {
     float m = fmaxf(lv0, lv1);
@@ -350,7 +370,7 @@ __global__ __launch_bounds__(1024) void combine_out_uv_kernel(const float* __res
   __syncthreads();
   const int n = s_n;
   const float inv = s_inv;
-  if (lse && tid == 0) lse[row] = s_lse;
+  if (lse && tid == 0 && q == 0) lse[row] = s_lse;
   const int g = tid >> 7, ct = tid & 127;  // 8 slot groups x 128 column threads
   const int c = 4 * ct;
   const float* op = o_part + row * n_part * d_c + c;
@@ -372,44 +392,60 @@ __global__ __launch_bounds__(1024) void combine_out_uv_kernel(const float* __res
     for (int k = 0; k < 7; ++k) acc += red[k * 128 + ct];
     acc *= inv;
     *(f32x4*)(o_s + c) = acc;
-    if (o_lat) {
+    if (o_lat && q == 0) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) store_f(o_lat + row * d_c + c + e, acc[e]);
     }
   }
   __syncthreads();
   float sum = 0.f;
-  if (v < d_v) {
+  if (v_ok) {
     if constexpr (VEC) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const f32x4 a = *(const f32x4*)(o_s + 64 * k + 8 * part);
-        const f32x4 b = *(const f32x4*)(o_s + 64 * k + 8 * part + 4);
+      for (int k = 0; k < NW; ++k) {
+        const f32x4 a = *(const f32x4*)(o_s + 8 * TPO * k + 8 * part);
+        const f32x4 b = *(const f32x4*)(o_s + 8 * TPO * k + 8 * part + 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) sum += (float)wv[k][e] * a[e] + (float)wv[k][4 + e] * b[e];
       }
     } else {
-      for (int cc = part; cc < d_c; cc += 8) sum += load_f(wrow + cc) * o_s[cc];
+      for (int cc = part; cc < d_c; cc += TPO) sum += load_f(wrow + cc) * o_s[cc];
     }
   }
-  sum += __shfl_xor(sum, 1);
-  sum += __shfl_xor(sum, 2);
-  sum += __shfl_xor(sum, 4);
-  if (v < d_v && part == 0) store_f(out + row * d_v + v, sum);
+#pragma unroll
+  for (int o = 1; o < TPO; o <<= 1) sum += __shfl_xor(sum, o);
+  if (v_ok && part == 0) store_f(out + row * d_v + v, sum);
 }
 
+template <typename TO, typename TW, int NQ>
+static hipError_t cou_launch_nq(const float* o_part, const float* lse_part, int n_tok, int n_heads, int n_part,
+                                int d_c, const void* w_uv, int d_v, void* o_lat, float* lse, void* out,
+                                hipStream_t stream) {
+  const int64_t n_items = (int64_t)n_heads * n_tok * NQ;
+  const dim3 grid((unsigned)(8 * ((n_items + 7) / 8)));
+  if constexpr (sizeof(TW) == 2) {
+    if (d_c == 512 && (reinterpret_cast<uintptr_t>(w_uv) & 15u) == 0)
+      return launch(combine_out_uv_kernel<TO, TW, true, NQ>, grid, dim3(1024), stream, o_part, lse_part, n_tok,
+                    n_heads, n_part, d_c, (const TW*)w_uv, d_v, (TO*)o_lat, lse, (TO*)out);
+  }
+  return launch(combine_out_uv_kernel<TO, TW, false, NQ>, grid, dim3(1024), stream, o_part, lse_part, n_tok,
+                n_heads, n_part, d_c, (const TW*)w_uv, d_v, (TO*)o_lat, lse, (TO*)out);
+}
+
+// NQ: blocks per row, so that about 256 blocks (one per CU) run
 template <typename TO, typename TW>
 static hipError_t cou_launch(const float* o_part, const float* lse_part, int n_tok, int n_heads, int n_part,
                              int d_c, const void* w_uv, int d_v, void* o_lat, float* lse, void* out,
                              hipStream_t stream) {
-  const dim3 grid(n_heads, n_tok);
-  if constexpr (sizeof(TW) == 2) {
-    if (d_c == 512 && (reinterpret_cast<uintptr_t>(w_uv) & 15u) == 0)
-      return launch(combine_out_uv_kernel<TO, TW, true>, grid, dim3(1024), stream, o_part, lse_part, n_heads,
-                    n_part, d_c, (const TW*)w_uv, d_v, (TO*)o_lat, lse, (TO*)out);
-  }
-  return launch(combine_out_uv_kernel<TO, TW, false>, grid, dim3(1024), stream, o_part, lse_part, n_heads, n_part,
-                d_c, (const TW*)w_uv, d_v, (TO*)o_lat, lse, (TO*)out);
+  const int64_t rows = (int64_t)n_tok * n_heads;
+  if (rows * 4 <= 256)
+    return cou_launch_nq<TO, TW, 4>(o_part, lse_part, n_tok, n_heads, n_part, d_c, w_uv, d_v, o_lat, lse, out,
+                                    stream);
+  if (rows * 2 <= 256)
+    return cou_launch_nq<TO, TW, 2>(o_part, lse_part, n_tok, n_heads, n_part, d_c, w_uv, d_v, o_lat, lse, out,
+                                    stream);
+  return cou_launch_nq<TO, TW, 1>(o_part, lse_part, n_tok, n_heads, n_part, d_c, w_uv, d_v, o_lat, lse, out,
+                                  stream);
 }
 
 hipError_t launch_combine_out_uv(const float* o_part, const float* lse_part, int n_tok, int n_heads, int n_part,

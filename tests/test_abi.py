@@ -94,6 +94,7 @@ def test_null_and_shape_errors_before_any_gpu_call(lib):
     assert _st(lib, "mla_combine_out_uv", P, P, 1, 1, 4, 510, P, 1, 128, None, None, P, 1, None) == 2
     assert _st(lib, "mla_combine_out_uv", P + 4, P, 1, 1, 4, 512, P, 1, 128, None, None, P, 1, None) == 2
     assert _st(lib, "mla_combine_out_uv", P, P, 0, 1, 4, 512, P, 1, 128, None, None, P, 1, None) == 0
+    assert _st(lib, "mla_combine_out_uv", P, P, 65535, 65535, 4, 512, P, 1, 128, None, None, P, 1, None) == 2
     # mla_qknorm_query(q_nope, in_dtype, g_q, g_k, n_tok, n_heads, d_nope, eps, q_out, stream)
     assert _st(lib, "mla_qknorm_query", P, 1, P, None, 1, 16, 128, 1e-6, P, None) == 1
     assert _st(lib, "mla_qknorm_query", P, 3, P, P, 1, 16, 128, 1e-6, P, None) == 3

@@ -277,6 +277,8 @@ def test_qknorm_calls(dtype, dims):
     (torch.float32, torch.bfloat16, (2, 3, 7, 64, 8)),          # bf16 weights, other widths
     (torch.float32, torch.float32, (3, 2, 5, 4, 4)),            # the toy widths
     (torch.bfloat16, torch.float32, (2, 3, 7, 36, 20)),
+    (torch.bfloat16, torch.bfloat16, (8, 12, 9, 512, 128)),    # 96 rows: two blocks per row
+    (torch.float32, torch.bfloat16, (3, 50, 5, 512, 128)),     # 150 rows: one block per row
 ])
 def test_combine_out_uv_call(out_dtype, w_dtype, dims):
     from mla_latent_cache_amd import ops
