@@ -81,12 +81,17 @@ def cpu_baseline(x, budget_s: float):
     from threadpoolctl import threadpool_info
 
     import oracle.mla_direct as O
+    import oracle.mla_quant as Q
 
     def f64(t):
         return t.to(torch.float64).numpy()
 
     sp = x.spec
-    segs = [O.OracleSegment(rows=(lambda b, s=s: f64(s.rows(b))), shift=s.shift.tolist(),
+
+    def rows(s, b):  # as attention reads them (int8 cache: the oracle's quantize/dequantize)
+        return Q.quantized_rows(s.rows(b).float().numpy(), sp.d_c) if sp.quant == "int8" else f64(s.rows(b))
+
+    segs = [O.OracleSegment(rows=(lambda b, s=s: rows(s, b)), shift=s.shift.tolist(),
                             head_begin=s.head_begin, head_count=s.head_count, causal=s.causal)
             for s in x.segments]
     q_nope, q_pe, w_uk, w_uv = f64(x.q_nope), f64(x.q_pe), f64(x.w_uk), f64(x.w_uv)

@@ -59,6 +59,8 @@ class Spec:
     offset_range: Optional[Tuple[int, int]] = None  # o_b ~ U{lo..hi}, inclusive
     qk_norm: bool = False          # RMSNorm of the content query and key (weights g_q, g_k drawn)
     qk_eps: float = 1e-6
+    quant: Optional[str] = None    # "int8": the cache holds per-row int8 latent codes (each side quantizes
+                                   # the drawn bf16 rows itself; nothing extra is drawn)
     description: str = ""
 
     @property

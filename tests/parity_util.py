@@ -14,14 +14,24 @@ import numpy as np
 import torch
 
 import oracle.mla_direct as O
+import oracle.mla_quant as Q
 
 
 def f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu", torch.float64).numpy()
 
 
+def oracle_rows(x, seg, b):
+    """Rows of request b as attention reads them: the stored bf16 rows, or
+    with an int8 cache the oracle's own quantize/dequantize of their latents."""
+    r = f64(seg.rows(b))
+    if x.spec.quant == "int8":
+        r = Q.quantized_rows(seg.rows(b).float().numpy(), x.spec.d_c)
+    return r
+
+
 def oracle_segments(x):
-    return [O.OracleSegment(rows=(lambda b, s=s: f64(s.rows(b))), shift=s.shift.tolist(),
+    return [O.OracleSegment(rows=(lambda b, s=s: oracle_rows(x, s, b)), shift=s.shift.tolist(),
                             head_begin=s.head_begin, head_count=s.head_count, causal=s.causal)
             for s in x.segments]
 
