@@ -29,7 +29,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 MALL_BYTES = 256 << 20          # Infinity Cache: rotate caches so every step reads HBM
 DECODE_SRC = os.path.join(ROOT, "mla_latent_cache_amd", "csrc", "mla_decode_bf16.hip")
-SEEDS = {"toy": 0, "small": 1, "dsv3": 2, "long": 3, "merge": 4, "prefill": 5, "qknorm": 6}
+SEEDS = {"toy": 0, "small": 1, "dsv3": 2, "long": 3, "merge": 4, "prefill": 5, "qknorm": 6, "int8": 7}
 
 
 def _rows(x):
@@ -41,16 +41,26 @@ def algorithmic(x):
     [c_t | kr_t] read once (1152 B in bf16), and per visible (row, query row)
     pair 2 * (576 + 512) FLOPs (scores over [c | kr], weighted sum over c).
     A causal segment shows query s of s_q the rows t <= T - s_q + s.  With
-    QK-Norm each row also brings its 4-byte inverse key RMS."""
+    QK-Norm each row also brings its 4-byte inverse key RMS; an int8 cache row
+    is d_c one-byte codes, the 16-bit rotary key and a 4-byte scale (644 B)."""
     sp = x.spec
     el = x.segments[0].cache.element_size()
-    nbytes = sum(r * (sp.row_width * el + (4 if sp.qk_norm else 0)) for r in _rows(x))
+    if sp.quant == "int8":
+        row = sp.d_c + 2 * sp.d_rope + 4
+    else:
+        row = sp.row_width * el + (4 if sp.qk_norm else 0)
+    nbytes = sum(r * row for r in _rows(x))
     flops = 0
     for s in x.segments:
         for T in s.seq_lens.tolist():
             pairs = sum(max(0, min(T, T - sp.s_q + q + 1)) for q in range(sp.s_q)) if s.causal else T * sp.s_q
             flops += 2 * pairs * s.head_count * (sp.row_width + sp.d_c)
     return nbytes, flops
+
+
+def ops_cache_dt(step) -> int:
+    from mla_latent_cache_amd import ops
+    return ops._cache_dt(step.segments[0].cache)
 
 
 def kernel_hash() -> str:
@@ -126,7 +136,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="small", choices=["small", "dsv3", "long", "merge", "toy", "prefill", "qknorm"])
+    ap.add_argument("--workload", default="small", choices=["small", "dsv3", "long", "merge", "toy", "prefill", "qknorm", "int8"])
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--n-wg", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -167,16 +177,22 @@ def main():
     base = step_from_inputs(x, n_wg=args.n_wg, fuse_post=fuse)
     step_fused = base.fuse_post
     steps = [base]
+    # every copy runs the same variant as the base step (QK-Norm factors of its
+    # own cache, an int8 cache quantized from its own bf16 rows)
+    qk = (base.g_q, base.g_k, base.qk_eps) if base.qk_norm else None
     for _ in range(n_copies - 1):
         segs = []
         for bs, s in zip(base.segments, x.segments):
             shift_tok = x.token_shift(s)
-            segs.append(StepSegment(cache=bs.cache.clone(), seq_lens=bs.seq_lens, seq_lens_host=s.seq_lens.tolist(),
+            cache = s.cache.to(bs.cache.device) if sp.quant else bs.cache.clone()
+            segs.append(StepSegment(cache=cache, seq_lens=bs.seq_lens, seq_lens_host=s.seq_lens.tolist(),
                                     shift=shift_tok.to(bs.cache.device), shift_host=shift_tok.tolist(),
                                     block_table=bs.block_table, head_begin=bs.head_begin,
                                     head_count=bs.head_count, causal=bs.causal))
         steps.append(DecodeStep(base.q_nope, base.q_pe, base.q_pos, base.w_uk, base.w_uv, segs, sp.batch, sp.s_q,
-                                x.scale, x.rope_base, n_wg=args.n_wg, n_split=base.n_split, fuse_post=fuse))
+                                x.scale, x.rope_base, n_wg=args.n_wg, n_split=base.n_split, fuse_post=fuse,
+                                qk_norm=qk, quant=sp.quant))
+    assert all(st.qk_norm == base.qk_norm and ops_cache_dt(st) == ops_cache_dt(base) for st in steps)
     # Launch path.  Graph mode (default): the step is captured into a HIP
     # graph of U consecutive steps (cycling the cache copies) and the timed
     # region replays it, so small workloads are bound by the GPU rather than

@@ -66,7 +66,11 @@ typedef enum {
   MLA_ERR_HIP = 7          /* the HIP runtime reported an error */
 } mla_status;
 
-typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+/* MLA_I8 is a cache format only (mla_decode_splitkv's cache_dtype): rows of
+ * d_c int8 latent codes followed by d_rope bf16 rotary entries (d_c + 2 d_rope
+ * bytes), one fp32 scale per row in mla_segment.row_scale; see
+ * mla_quantize_latent_i8. */
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1, MLA_I8 = 2 } mla_dtype;
 
 /*
  * rope_relocate_q -- rotary query for one KV segment.
@@ -136,6 +140,10 @@ typedef struct {
                                  ([batch][max_rows] or [n_pages][page_size]); the
                                  latent part of each score is multiplied by it.
                                  NULL => no QK-Norm */
+  const float* row_scale;     /* int8 cache (cache_dtype MLA_I8): per stored row the
+                                 scale of its latent codes (mla_quantize_latent_i8),
+                                 indexed like row_rinv; the latent is scale * code.
+                                 Must be NULL for 16-bit and fp32 caches */
 } mla_segment;
 
 /*
@@ -165,11 +173,16 @@ typedef struct {
  *          only on the rotary dims and add the latent lo part's share to
  *          the lse to first order (scale * lo . o_part; lse error second
  *          order, ~1e-5 at unit-variance inputs).  MLA_F32 caches take an
- *          fp32 query.
+ *          fp32 query.  MLA_I8 caches (QuantMLA abstract: a low-bit latent
+ *          cache dequantized inside attention) take an fp32 query and every
+ *          segment's row_scale: the latent score of row t is scale_t times
+ *          q_lat . code_t and its softmax weight multiplies scale_t code_t,
+ *          exactly the attention over the dequantized rows; not combined
+ *          with QK-Norm.
  * o_part   [n_tok][n_heads][n_part][d_c] fp32    output
  * lse_part [n_tok][n_heads][n_part]      fp32    output
  * n_tok = batch * s_q.  n_wg = workgroups per segment (0 = one per compute unit).
- * bf16 path: d_c = 512, d_rope = 64, page_size = 64, s_q * head_count <= 4096
+ * bf16 and int8 paths: d_c = 512, d_rope = 64, page_size = 64, s_q * head_count <= 4096
  * (multi-token chunks: the rows form groups of 64, each streaming the rows).
  */
 mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q_lat, int q_dtype,
@@ -259,6 +272,24 @@ mla_status mla_out_uv(const void* o_lat, int o_dtype, const void* w_uv, int w_dt
 mla_status mla_combine_out_uv(const float* o_part, const float* lse_part, int n_tok, int n_heads, int n_part,
                               int d_c, const void* w_uv, int w_dtype, int d_v, void* o_lat, float* lse, void* out,
                               int out_dtype, void* stream);
+
+/*
+ * mla_quantize_latent_i8 -- write an int8 latent cache (the cache writer's
+ * part; QuantMLA abstract: low-bit latent caching, here the plain per-row
+ * symmetric form).  For each of the n_rows stored rows [c | k^R] (bf16,
+ * d_c + d_rope entries; a cache or a page pool viewed as rows):
+ *   scale = max_i |c_i| / 127                       (fp32 quotient)
+ *   code_i = nearest integer to c_i / scale, ties to even, clamped to [-127, 127]
+ *            (the quotient in fp32; scale 0 gives codes 0)
+ *   out_rows[r] = [code_0 .. code_{d_c-1} (int8) | k^R (the d_rope bf16 entries, unchanged)]
+ *   scales[r]   = scale
+ * rows [n_rows][d_c + d_rope] bf16; out_rows [n_rows][d_c + 2 d_rope] bytes;
+ * scales [n_rows] fp32.  d_c a multiple of 8, <= 512; d_rope a multiple of 4,
+ * <= 128; rows and out_rows 8-byte aligned.
+ * Errors: MLA_ERR_NULL, MLA_ERR_DTYPE (rows not bf16), MLA_ERR_SHAPE, MLA_ERR_ALIGN.
+ */
+mla_status mla_quantize_latent_i8(const void* rows, int row_dtype, int64_t n_rows, int d_c, int d_rope,
+                                  void* out_rows, float* scales, void* stream);
 
 /*
  * QK-Norm MLA (QK-Norm MLA page, abstract): RMSNorm(x) = g x / sqrt(mean(x^2)

@@ -138,10 +138,19 @@ WORKLOADS["qknorm"] = replace(
     description="small bf16 with QK-Norm: B=4, H=16, T=4096 contiguous, 1 query token, RMSNorm of the "
                 "content query and key")
 
+# The long-context configuration read from an int8 latent cache (QuantMLA
+# abstract: low-bit latent caching; here per-row symmetric int8 codes, the
+# rotary key kept 16-bit).  The drawn rows are the same bf16 rows; each side
+# quantizes them itself.
+WORKLOADS["int8"] = replace(
+    WORKLOADS["long"], name="int8", quant="int8",
+    description="long context from an int8 latent cache: B=4, H=64, T=262144 contiguous, 1 query token; "
+                "per-row int8 latent codes + bf16 rotary key (640 B + a 4 B scale per row)")
+
 # Order of the configurations as listed by the benchmark description.
 WORKLOAD_ORDER = ("toy", "small", "dsv3", "long", "merge")
 # Further workloads (beyond the five configurations)
-EXTRA_WORKLOADS = ("prefill", "qknorm")
+EXTRA_WORKLOADS = ("prefill", "qknorm", "int8")
 
 
 def spec_for(name: str) -> Spec:
@@ -175,6 +184,10 @@ def mini_spec(name: str) -> Spec:
     if name == "qknorm":
         return replace(s, name="qknorm-mini", batch=3,
                        segments=(SegSpec("kv", lengths=(1, 129, 777), online=True),))
+    if name == "int8":
+        return replace(s, name="int8-mini", batch=3,
+                       segments=(SegSpec("kv", lengths=(1, 777, 2113), layout="paged", page_size=64,
+                                         spare_pages=2, online=True),))
     if name == "prefill":
         segs = (
             replace(s.segments[0], length=None, lengths=(300, 97)),

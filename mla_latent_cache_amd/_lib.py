@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_late
 
 MLA_F32 = 0
 MLA_BF16 = 1
+MLA_I8 = 2  # cache format: int8 latent codes + bf16 rotary entries per row, fp32 scale per row
 
 STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_DTYPE", 4: "MLA_ERR_ALIGN",
           5: "MLA_ERR_UNSUPPORTED", 6: "MLA_ERR_WORKSPACE", 7: "MLA_ERR_HIP"}
@@ -36,6 +37,7 @@ class MlaSegment(ctypes.Structure):
         ("part_begin", c_int),
         ("n_split", c_int),
         ("row_rinv", c_void_p),
+        ("row_scale", c_void_p),
     ]
 
 
@@ -56,6 +58,7 @@ SIGNATURES = {
     "mla_prepare_q": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_int, POINTER(c_void_p),
                               POINTER(c_void_p), c_int, c_int, c_void_p, c_int, c_int, c_int, c_int, c_int,
                               c_double, c_void_p]),
+    "mla_quantize_latent_i8": (c_int, [c_void_p, c_int, c_int64, c_int, c_int, c_void_p, c_void_p, c_void_p]),
     "mla_qknorm_query": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_int, c_int, c_int, c_double, c_void_p,
                                  c_void_p]),
     "mla_qknorm_key_gram": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p]),

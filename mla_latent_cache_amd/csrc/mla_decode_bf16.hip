@@ -126,45 +126,77 @@ __device__ __forceinline__ float rows_sum(float v) {
 __device__ __forceinline__ int cpos(int r, int c) { return c ^ (r & 15); }
 __device__ __forceinline__ int rpos(int r, int j) { return j ^ ((r >> 1) & 7); }
 
+// Ring geometry per cache format.  16-bit rows (1152 B): the tile loads land
+// directly in the latent ring the MFMAs read (4 stages, 3 tiles ahead).
+// int8 rows (640 B: 512 codes, then the 64 bf16 rotary entries): PV wave w
+// loads latent columns [128 w, 128 w + 128) of all 32 rows into an int8
+// landing stage and, during its PV step of tile i (under the MFMAs), converts
+// them for tile i+2 into a 16-bit stage: three 16-bit stages (i being read by
+// the PV waves, i+1 by the score waves, i+2 being written: the stage of tile
+// i-1, which every wave left before barrier i), two landing stages (tile i+3
+// is issued only once tile i+2 is converted).  The score and PV loops read
+// the 16-bit stages exactly as with 16-bit rows.
+template <bool I8>
+struct Geo {
+  static constexpr int RB = I8 ? kDc + kRBytes : kRowBytes;  // cache bytes per row
+  static constexpr int NST = I8 ? 3 : kNStage;                // 16-bit latent stages
+  static constexpr int AHEAD = kAhead;                        // tiles loading beyond the two in use
+  static constexpr int NRST = AHEAD;                          // rotary ring
+  static constexpr int NLAND = I8 ? 2 : 1;                    // int8 landing ring
+  static constexpr int NDMA = I8 ? kTile / 2 + kRStage / 1024 : kNDma;  // wave-instructions per tile
+  static constexpr int LAT = I8 ? kTile / 2 : kTile;          // of which latent
+};
+
 // Loads of one tile: `lim` bytes (whole rows) that are contiguous in memory
 // from `src` (tiles are aligned to 32 rows inside a request and never cross a
-// 64-row page).  Wave-instruction k < 32 fills latent LDS row k: lane l moves
-// the chunk stored at position l, cache bytes k * 1152 + (l ^ (k & 15)) * 16.
-// k = 32..35 fill rotary rows 8 (k - 32) + l / 8 at position l % 8.  Rows past
+// 64-row page).  16-bit rows: wave-instruction k < 32 fills latent LDS row k:
+// lane l moves the chunk stored at position l, cache bytes k * 1152 +
+// (l ^ (k & 15)) * 16.  int8 rows: instruction k < 16 fills 1 KiB of the
+// landing stage with rows 8 (k / 4) .. + 7, latent bytes 128 (k % 4) .. + 127
+// (lane l: row 8 (k / 4) + l / 8, bytes 128 (k % 4) + 16 (l % 8) .. + 15), so
+// loader w = k % 4 holds exactly the columns it converts and reads.
+// The next 4 fill rotary rows 8 (k - LAT) + l / 8 at position l % 8.  Rows past
 // the valid ones are zero-filled so no stale value is ever read.  The four PV
-// waves issue all tile loads: loader l = wave - 4 issues k = l + 4 i, i < 9.
+// waves issue all tile loads: loader l = wave - 4 issues k = l + 4 i.
 // An LDS-direct load keeps its wave busy at issue, so the score waves, which
 // set the pace, issue none.
 struct TileDma {
-  char* cdst;       // latent ring stage
+  char* cdst;       // latent ring stage (int8 rows: landing stage)
   char* rdst;       // rotary ring stage
   const char* src;  // first cache byte of the tile
   int lim;          // valid bytes at src
 };
 
 // Cache byte offset (within the tile) and LDS destination of instruction k for this lane.
+template <bool I8>
 __device__ __forceinline__ int dma_src_off(int k, int lane) {
-  if (k < kTile) return k * kRowBytes + cpos(k, lane) * 16;
-  const int r = 8 * (k - kTile) + (lane >> 3);
-  return r * kRowBytes + kCBytes + rpos(r, lane & 7) * 16;
+  using G = Geo<I8>;
+  if (k < G::LAT) {
+    if constexpr (I8) return (8 * (k >> 2) + (lane >> 3)) * G::RB + 128 * (k & 3) + 16 * (lane & 7);
+    return k * kRowBytes + cpos(k, lane) * 16;
+  }
+  const int r = 8 * (k - G::LAT) + (lane >> 3);
+  return r * G::RB + (I8 ? kDc : kCBytes) + rpos(r, lane & 7) * 16;
 }
+template <bool I8>
 __device__ __forceinline__ char* dma_dst(const TileDma& d, int k) {
-  return k < kTile ? d.cdst + k * 1024 : d.rdst + (k - kTile) * 1024;
+  using G = Geo<I8>;
+  return k < G::LAT ? d.cdst + k * 1024 : d.rdst + (k - G::LAT) * 1024;
 }
 
 // UNI: the loader index (hence k) is wave-uniform and held opaque in a
 // scalar register, so the latent/rotary choice is a scalar branch and no
 // per-instruction offset is hoisted; else it is a lane value and both sides
 // run under the exec mask (fewer branches, more vector registers).
-template <bool UNI>
+template <bool UNI, bool I8>
 __device__ __forceinline__ void issue_dma_one(const TileDma& d, int k, int lane) {
   // Opaque copy of the lane index: the offsets are recomputed at every
   // instruction (a few integer ops) instead of being hoisted out of the tile
   // loop and pinning registers for the whole loop.
   asm volatile("" : "+v"(lane));
   if constexpr (UNI) asm volatile("" : "+s"(k));
-  const int off = dma_src_off(k, lane);
-  char* dst = dma_dst(d, k);
+  const int off = dma_src_off<I8>(k, lane);
+  char* dst = dma_dst<I8>(d, k);
   if (off < d.lim) {  // the lane's row is a valid row of the tile
     __builtin_amdgcn_global_load_lds((const void*)(d.src + off), (MLA_LDS void*)dst, 16, 0, 0);
   } else {
@@ -173,8 +205,11 @@ __device__ __forceinline__ void issue_dma_one(const TileDma& d, int k, int lane)
 }
 
 constexpr int kLoaders = 4;  // waves issuing tile loads (the PV waves)
-constexpr int kDmaPerWave = kNDma / kLoaders;  // 9
-static_assert(kNDma % kLoaders == 0, "every loader issues the same count");
+template <bool I8>
+constexpr int dma_per_wave() {
+  static_assert(Geo<I8>::NDMA % kLoaders == 0, "every loader issues the same count");
+  return Geo<I8>::NDMA / kLoaders;  // 9 (16-bit rows) or 5 (int8 rows)
+}
 
 // Loader `ld`'s i-th instruction of a tile (k = ld + 4 i): a full tile
 // issues it from a uniform base plus a lane offset of two or three integer
@@ -182,44 +217,58 @@ static_assert(kNDma % kLoaders == 0, "every loader issues the same count");
 // bounds-checked path with zero fill.  `lane` should be opaque to the
 // compiler, or it hoists the nine offsets into live registers (`ld` too with
 // UNI, see issue_dma_one).
-template <bool UNI>
+template <bool UNI, bool I8>
 __device__ __forceinline__ void issue_dma_fast(const TileDma& d, int ld, int i, int lane) {
   if constexpr (UNI) asm volatile("" : "+s"(ld));
   const int k = ld + kLoaders * i;
-  if (d.lim == kTile * kRowBytes) {
-    __builtin_amdgcn_global_load_lds((const void*)(d.src + (unsigned)dma_src_off(k, lane)),
-                                     (MLA_LDS void*)dma_dst(d, k), 16, 0, 0);
+  if (d.lim == kTile * Geo<I8>::RB) {
+    __builtin_amdgcn_global_load_lds((const void*)(d.src + (unsigned)dma_src_off<I8>(k, lane)),
+                                     (MLA_LDS void*)dma_dst<I8>(d, k), 16, 0, 0);
   } else {
-    issue_dma_one<UNI>(d, k, lane);
+    issue_dma_one<UNI, I8>(d, k, lane);
   }
 }
 
 // All of loader `ld`'s instructions of a tile at once.
-template <bool UNI>
+template <bool UNI, bool I8>
 __device__ __forceinline__ void issue_tile_dma(const TileDma& d, int ld, int lane) {
 #pragma unroll
-  for (int i = 0; i < kDmaPerWave; ++i) issue_dma_one<UNI>(d, ld + kLoaders * i, lane);
+  for (int i = 0; i < dma_per_wave<I8>(); ++i) issue_dma_one<UNI, I8>(d, ld + kLoaders * i, lane);
 }
 
 // First byte of tile rows [t0, ...) of request b: contiguous cache, or the
 // page holding row t0 (scalar load of the block-table entry; an id outside
 // [0, n_pages) makes the tile read as zeros).
+template <bool I8>
 __device__ __forceinline__ const char* tile_src(const char* cache, const char* req_base, const int32_t* bt_row,
                                                 int n_pages, int t0, bool* ok) {
+  constexpr int RB = Geo<I8>::RB;
   *ok = true;
-  if (!bt_row) return req_base + (int64_t)t0 * kRowBytes;
+  if (!bt_row) return req_base + (int64_t)t0 * RB;
   const int pg = sload_i32(bt_row + t0 / kPageSize);
   *ok = pg >= 0 && pg < n_pages;
-  return cache + ((int64_t)(*ok ? pg : 0) * kPageSize + (t0 % kPageSize)) * kRowBytes;
+  return cache + ((int64_t)(*ok ? pg : 0) * kPageSize + (t0 % kPageSize)) * RB;
 }
 
-template <int MT>
+// 8 int8 latent codes -> 8 bf16 (exact: |code| <= 127 needs 7 bits)
+__device__ __forceinline__ bf16x8 i8x8_to_bf16(uint2 v) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = (bf16)(float)(int)(signed char)(v.x >> (8 * e));
+    r[4 + e] = (bf16)(float)(int)(signed char)(v.y >> (8 * e));
+  }
+  return r;
+}
+
+template <int MT, bool I8>
 struct Smem {
+  using G = Geo<I8>;
   static constexpr int NRB = MT / 16;
   static constexpr int QBW = NRB == 4 ? 2 : 1;  // 16-row blocks per score wave
   static constexpr int KS = 4 / (NRB / QBW);    // k-parts (score waves) per group of QBW blocks
-  char cst[kNStage][kCStage];   // latent ring
-  char rst[kNRStage][kRStage];  // rotary ring
+  char cst[G::NST][kCStage];    // 16-bit latent ring
+  char rst[G::NRST][kRStage];   // rotary ring
   char p[2][MT * kPStr];         // P (bf16) of two tiles
   // exchanged partial scores [slot][tb][lane][4]: QBW = 1, k-parts 1..KS-1 of each
   // row block; QBW = 2, the partner's k-part of each row block.  After a
@@ -232,18 +281,21 @@ struct Smem {
   int n_pieces;
   int done;
   int red_i[2 * kWaves];
+  char land[G::NLAND][I8 ? kTile * kDc : 16];  // int8 landing ring (int8 rows only)
 };
 
 // Loader `ld`: wait until at most `after` tiles issued after the needed one
 // are still in flight; `after_full` says they are all full tiles (a partial
 // tile issues fewer instructions, then everything is waited for).
+template <bool I8>
 __device__ __forceinline__ void wait_tiles(int after, bool after_full) {
+  constexpr int W = dma_per_wave<I8>();
   if (!after_full || after == 0) {
     wait_vmcnt<0>();
   } else if (after == 1) {
-    wait_vmcnt<kDmaPerWave>();
+    wait_vmcnt<W>();
   } else {
-    wait_vmcnt<2 * kDmaPerWave>();
+    wait_vmcnt<2 * W>();
   }
 }
 
@@ -252,7 +304,10 @@ __device__ __forceinline__ void wait_tiles(int after, bool after_full) {
 // QF32: q_lat / q_rot are fp32 and split into bf16 hi + lo parts.
 // QKN: QK-Norm, the latent part of every score is multiplied by the stored
 // row's inverse key RMS (seg.row_rinv).
-template <int MT, bool QF32, bool QKN>
+// I8: int8 latent rows; the latent part of every score is multiplied by the
+// row's scale (seg.row_scale), and so is the row's softmax weight before the
+// weighted sum of codes: sum_t p_t scale_t code_t = sum_t p_t c_t.
+template <int MT, bool QF32, bool QKN, bool I8>
 __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, int n_share, int n_rg,
                                                                   int rows_total) {
   constexpr int NRB = MT / 16;       // 16-row blocks
@@ -271,7 +326,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
   // the lse (LOC below, epilogue).
   // (the first-order correction needs sum_t p_t c_t to carry the latent
   // scores' weights, which QK-Norm's per-row factor breaks)
+  // (an int8 cache's scale multiplies score and weight alike, so the
+  // correction holds there: sum_t p_t scale_t code_t is what the PV waves sum)
   constexpr bool LOC = QF32 && MT == 64 && !QKN;
+  using G = Geo<I8>;
+  constexpr bool FAC = QKN || I8;  // a per-row factor on the latent score
+  constexpr bool UNI = QKN || I8;  // wave-uniform loader index (see pw)
   constexpr int NQH = QF32 && !LOC ? 2 : 1;
   // The KS waves of a group cut the k-steps into parts of equal MFMA count:
   // with LOC the two rotary k-steps cost two MFMAs each, so the 20 MFMA steps
@@ -280,8 +340,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
   static_assert(!LOC || KCOST % KS == 0, "equal parts");
   constexpr int KMAX = (KCOST + KS - 1) / KS;
   constexpr int KLAST = kKSteps - (KS - 1) * (KCOST / KS);  // k-steps of the last part (LOC)
-  __shared__ __attribute__((aligned(16))) Smem<MT> sm;
+  __shared__ __attribute__((aligned(16))) Smem<MT, I8> sm;
   static_assert(sizeof(sm.xbuf) >= 4 * MT * sizeof(float), "lse corrections fit the exchange buffer");
+  static_assert(!LOC || G::NST >= 3, "two latent stages free for the lo rows after the last tile");
 
   // every argument field as a local value (see issue_tile_dma)
   const char* const cache = (const char*)a.seg.cache;
@@ -291,7 +352,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
   const void* const q_lat_p = a.q_lat;
   float* const o_part = a.o_part;
   float* const lse_part = a.lse_part;
-  const float* const row_rinv = a.seg.row_rinv;
+  const float* const row_fac = QKN ? a.seg.row_rinv : a.seg.row_scale;  // FAC: per stored row
   const int64_t max_rows = a.seg.max_rows;
   const int max_pages = a.seg.max_pages;
   const int n_pages = a.seg.n_pages;
@@ -400,10 +461,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
   const int s_row = Rc / hc;
   const int64_t q_off = (int64_t)s_row * n_heads + head_begin + Rc % hc;  // without the request part
   const int s_min = row0 / hc;       // smallest token index among the group's rows
-  // column slice of a PV wave and its loader index.  With QK-Norm (the
-  // register-heaviest variant) it is the scalar copy, so the tile loads
+  // column slice of a PV wave and its loader index.  With a row factor (the
+  // register-heaviest variants) it is the scalar copy, so the tile loads
   // branch on it (issue_dma_one); elsewhere the lane value measured faster.
-  const int pw = (QKN ? wave_s : wave) - 4;
+  const int pw = (UNI ? wave_s : wave) - 4;
 
   int base = 0;  // prefix of padded T over requests scanned so far (wave 0)
   for (int chunk = 0;; ++chunk) {
@@ -480,16 +541,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
       const int n_tiles = (pr1 - pr0 + kTile - 1) / kTile;
       const bool last_full = (pr1 - pr0) % kTile == 0;       // only the last tile can be partial
 
-      const char* const req_base = cache + (int64_t)b * max_rows * kRowBytes;  // contiguous layout
+      const char* const req_base = cache + (int64_t)b * max_rows * G::RB;  // contiguous layout
       const int32_t* const bt_row = block_table ? block_table + (int64_t)b * max_pages : nullptr;
       // where tile `it` comes from and goes to (lim = 0: all zeros)
       auto tile_dma = [&](int it) -> TileDma {
         const int t0 = pr0 + it * kTile;
         bool ok;
-        const char* src = tile_src(cache, req_base, bt_row, n_pages, t0, &ok);
-        return TileDma{sm.cst[it % kNStage], sm.rst[it % kNRStage], src, ok ? min(kTile, pr1 - t0) * kRowBytes : 0};
+        const char* src = tile_src<I8>(cache, req_base, bt_row, n_pages, t0, &ok);
+        char* const cdst = I8 ? sm.land[it % G::NLAND] : sm.cst[it % G::NST];
+        return TileDma{cdst, sm.rst[it % G::NRST], src, ok ? min(kTile, pr1 - t0) * G::RB : 0};
       };
-      auto load_tile = [&](int it) { issue_tile_dma<QKN>(tile_dma(it), pw, lane); };
+      auto load_tile = [&](int it) { issue_tile_dma<UNI, I8>(tile_dma(it), pw, lane); };
 
       // The two roles run separate copies of the tile loop with the same
       // barrier sequence (1 + n_tiles + 1 barriers, plus one exchange barrier
@@ -566,9 +628,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
         // pool (its tile reads as zeros and takes factor 1).
         auto rinv_row = [&](int it) -> const float* {
           const int t0 = pr0 + it * kTile;
-          if (!bt_row) return row_rinv + (int64_t)b * max_rows + t0;
+          if (!bt_row) return row_fac + (int64_t)b * max_rows + t0;
           const int pg = sload_i32(bt_row + t0 / kPageSize);
-          return (pg >= 0 && pg < n_pages) ? row_rinv + (int64_t)pg * kPageSize + t0 % kPageSize : nullptr;
+          return (pg >= 0 && pg < n_pages) ? row_fac + (int64_t)pg * kPageSize + t0 % kPageSize : nullptr;
         };
         // The loads are unconditional (a select on a loaded value would wait
         // for it here): rows past the piece repeat its last row's factor, in
@@ -576,7 +638,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
         // whether the factors are real (false: use 1).
         auto load_rinv = [&](int it, const float* rr, f32x4& r0v, f32x4& r1v) -> bool {
           const int lim = pr1 - 1 - (pr0 + it * kTile);  // >= 0: the tile starts inside the piece
-          const float* src = rr ? rr : row_rinv;
+          const float* src = rr ? rr : row_fac;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int t = 4 * lg + e;
@@ -589,12 +651,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
         // registers; once they are applied, the same registers receive the
         // factors of tile it+1 (applied a tile later, so the loads have time)
         auto score_tile = [&](int it, f32x4& rf0, f32x4& rf1, bool& rf_ok) {
-          const char* cs = sm.cst[it % kNStage];
-          const char* rs = sm.rst[it % kNRStage];
+          const char* cs = sm.cst[it % G::NST];
+          const char* rs = sm.rst[it % G::NRST];
           const int t0 = pr0 + it * kTile;
           const int buf = it & 1;
           const float* rr_next = nullptr;
-          if constexpr (QKN)
+          if constexpr (FAC)
             if (it + 1 < n_tiles) rr_next = rinv_row(it + 1);
           // accumulators: hi and lo parts (else even and odd k-steps)
           // separately with one row block (two independent chains would stall
@@ -643,7 +705,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb) ak[(i + kPre) % (kPre + 1)][tb] = kop(i + kPre, tb);
               }
-              if (QKN && ks0 + i == kDc / 32) {
+              if (FAC && ks0 + i == kDc / 32) {
                 // QK-Norm: the latent part so far takes the rows' factors
                 // before the rotary k-steps add to it (they take none)
 #pragma unroll
@@ -685,9 +747,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
               sc[tb][j] = sacc[tb][j][0];
               if constexpr (NACC > 1) sc[tb][j] += sacc[tb][j][1];
             }
-          if constexpr (QKN) {
+          if constexpr (FAC) {
             // a k-part with no rotary step applies the factors here; then the
-            // next tile's factors
+            // next tile's factors (int8 rows: the softmax wave still needs
+            // this tile's scales for P, it loads them after writing P)
             if (ks0 + kcnt <= kDc / 32 && rf_ok) {
 #pragma unroll
               for (int j = 0; j < QBW; ++j) {
@@ -695,7 +758,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
                 sc[1][j] *= rf1;
               }
             }
-            if (it + 1 < n_tiles) rf_ok = load_rinv(it + 1, rr_next, rf0, rf1);
+            if (!(I8 && smax_wave) && it + 1 < n_tiles) rf_ok = load_rinv(it + 1, rr_next, rf0, rf1);
           }
           f32x4 sa, sb;  // scores of the softmax block rb, all k-steps
           f32x4* xb = (f32x4*)sm.xbuf;  // [slot][tb][lane]
@@ -759,8 +822,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
             const float p0 = __builtin_amdgcn_exp2f(sa[e] - msub);  // exp2(-inf) = 0
             const float p1 = __builtin_amdgcn_exp2f(sb[e] - msub);
             lsum += p0 + p1;
-            pa[e] = (bf16)p0;
-            pb[e] = (bf16)p1;
+            if constexpr (I8) {  // the weight of row t multiplies scale_t code_t
+              pa[e] = (bf16)(rf_ok ? p0 * rf0[e] : p0);
+              pb[e] = (bf16)(rf_ok ? p1 * rf1[e] : p1);
+            } else {
+              pa[e] = (bf16)p0;
+              pb[e] = (bf16)p1;
+            }
           }
           l_part += lsum;
           char* prow = sm.p[buf] + qrow * kPStr + 4 * lg * 2;
@@ -768,12 +836,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
           *(bf16x4*)(prow + 32) = pb;
           if (lg == 0) sm.alpha[buf][qrow] = alpha;
           if (lane == 0) sm.flag[buf][rb] = any ? 1 : 0;
+          if constexpr (I8)
+            if (it + 1 < n_tiles) rf_ok = load_rinv(it + 1, rr_next, rf0, rf1);
         };
 
         // QK-Norm factors of the tile being scored (1 without QK-Norm)
         f32x4 rf0 = f32x4{1.f, 1.f, 1.f, 1.f}, rf1 = rf0;
         bool rf_ok = false;
-        if constexpr (QKN) rf_ok = load_rinv(0, rinv_row(0), rf0, rf1);
+        if constexpr (FAC) rf_ok = load_rinv(0, rinv_row(0), rf0, rf1);
         // tile 0 is in LDS after the first barrier (the PV waves load)
         barrier_raw();
         score_tile(0, rf0, rf1, rf_ok);
@@ -793,8 +863,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
           // query rows, lo = q - bf16(q) in bf16, into two free latent stages
           // (rows 0..31 / 32..63, 16-byte chunks swizzled like the tiles).
           // Score wave w takes rows 16 w .. 16 w + 15, four at a time.
-          char* const lo_a = sm.cst[n_tiles % kNStage];
-          char* const lo_b = sm.cst[(n_tiles + 1) % kNStage];
+          char* const lo_a = sm.cst[n_tiles % G::NST];
+          char* const lo_b = sm.cst[(n_tiles + 1) % G::NST];
 #pragma unroll 1
           for (int r4 = 0; r4 < MT / 4; r4 += 4)
 #pragma unroll
@@ -822,8 +892,32 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
       } else {
         // ---- PV wave (waves 4..7): 128 latent columns of all rows, and all tile loads ----
 #pragma unroll
-        for (int t = 0; t < kAhead; ++t)
+        // (int8 rows: tiles 0 and 1 first, tile 2 once they are converted)
+        for (int t = 0; t < (I8 ? 2 : G::AHEAD); ++t)
           if (t < n_tiles) load_tile(t);
+        // int8 rows: this wave's landed columns of tile j (after its own loads
+        // of it are waited for) into the tile's 16-bit stage, chunks swizzled
+        // as the 16-bit loads place them (chunk c of row r at c ^ (r & 15)).
+        // Lane l of instruction k = w + 4 i holds row 8 i + l / 8, codes
+        // 128 w + 16 (l % 8) .. + 15: 16-bit chunks 16 w + 2 (l % 8) and +1.
+        // All four reads go out before the first write.
+        auto convert_tile = [&](int j) {
+          if constexpr (I8) {
+            const char* __restrict__ src = sm.land[j % G::NLAND];
+            char* __restrict__ dst = sm.cst[j % G::NST];
+            constexpr int NI = G::LAT / kLoaders;
+            uint4 v[NI];
+#pragma unroll
+            for (int i = 0; i < NI; ++i) v[i] = *(const uint4*)(src + (pw + kLoaders * i) * 1024 + 16 * lane);
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+              const int r = 8 * i + (lane >> 3);
+              const int c = 16 * pw + 2 * (lane & 7);
+              *(bf16x8*)(dst + r * kCBytes + ((c ^ (r & 15)) << 4)) = i8x8_to_bf16(uint2{v[i].x, v[i].y});
+              *(bf16x8*)(dst + r * kCBytes + (((c + 1) ^ (r & 15)) << 4)) = i8x8_to_bf16(uint2{v[i].z, v[i].w});
+            }
+          }
+        };
         f32x4 acc_o[8][NRB];
 #pragma unroll
         for (int db = 0; db < 8; ++db)
@@ -839,7 +933,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
         auto pv_tile = [&](const char* __restrict__ st, const char* __restrict__ pbuf,
                            const float* __restrict__ alph, const int* __restrict__ flg,
                            char* __restrict__ dma_cdst, char* __restrict__ dma_rdst, const char* dma_src,
-                           int dma_lim, bool with_dma, bool with_x) {
+                           int dma_lim, bool with_dma, bool with_x, int conv_j) {
           const TileDma dma{dma_cdst, dma_rdst, dma_src, dma_lim};
           // all C^T operands of the tile first (16 transposed reads in flight),
           // then P, the rescale flags and factors
@@ -874,9 +968,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
           // between the MFMAs
           int dlane = lane;
           asm volatile("" : "+v"(dlane));
-          if (with_dma) {
+          constexpr int kW = dma_per_wave<I8>();
+          constexpr int kFirst = kW - 4;  // the rest go between the MFMAs (db = 0, 2, 4, 6)
+          if (with_dma && !I8) {
 #pragma unroll
-            for (int i = 0; i < 5; ++i) issue_dma_fast<QKN>(dma, pw, i, dlane);
+            for (int i = 0; i < kFirst; ++i) issue_dma_fast<UNI, I8>(dma, pw, i, dlane);
           }
 
           if (flag) {
@@ -893,39 +989,66 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
             // the score waves' mid-tile exchange barrier (their next tile): half
             // of this tile's MFMAs and loads overlap their QK, half their softmax
             if (db == 4 && with_x) barrier_raw();
-            if (with_dma && db % 2 == 0) issue_dma_fast<QKN>(dma, pw, 5 + db / 2, dlane);
+            if constexpr (I8) {
+              // int8 rows: under the second half of the MFMAs, this wave's
+              // columns of tile conv_j (its only loads in flight) are waited
+              // for and converted into that tile's stage; then the loads of
+              // the tile after it, into the landing stage just read
+              if (db == 4) {
+                if (conv_j >= 0) {
+                  wait_vmcnt<0>();
+                  convert_tile(conv_j);
+                }
+                if (with_dma) issue_dma_fast<UNI, I8>(dma, pw, 0, dlane);
+              }
+              if (with_dma && db >= 4) issue_dma_fast<UNI, I8>(dma, pw, db - 3, dlane);
+            } else {
+              if (with_dma && db % 2 == 0) issue_dma_fast<UNI, I8>(dma, pw, kFirst + db / 2, dlane);
+            }
 #pragma unroll
             for (int q = 0; q < NRB; ++q)
               acc_o[db][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ac[db], bq[q], acc_o[db][q], 0, 0, 0);
           }
         };
 
-        // tile 0 must be in LDS; tiles 1 .. kAhead-1 may still be in flight
-        wait_tiles(min(n_tiles - 1, kAhead - 1), min(n_tiles - 1, kAhead - 1) < n_tiles - 1 || last_full);
+        if constexpr (I8) {
+          // tiles 0 and 1 must be converted before the score waves need them
+          // (each later tile is converted two tiles ahead, inside pv_tile)
+          wait_vmcnt<0>();
+          convert_tile(0);
+          if (n_tiles > 1) convert_tile(1);
+          if (n_tiles > 2) load_tile(2);
+        } else {
+          // tile 0 must be in LDS; tiles 1 .. AHEAD-1 may still be in flight
+          wait_tiles<I8>(min(n_tiles - 1, G::AHEAD - 1), min(n_tiles - 1, G::AHEAD - 1) < n_tiles - 1 || last_full);
+        }
         wait_lgkm0();
         barrier_raw();
         if constexpr (KS > 1) barrier_raw();  // the score waves' exchange of tile 0
         for (int it = 0; it < n_tiles; ++it) {
           // before barrier `it`: tile it+1 is in LDS (tile it+2 may be in flight)
-          if (it + 1 < n_tiles) {
-            const int issued = min(it + kAhead - 1, n_tiles - 1);
-            wait_tiles(issued - (it + 1), issued < n_tiles - 1 || last_full);
+          if (!I8 && it + 1 < n_tiles) {
+            const int issued = min(it + G::AHEAD - 1, n_tiles - 1);
+            wait_tiles<I8>(issued - (it + 1), issued < n_tiles - 1 || last_full);
           }
           wait_lgkm0();
           barrier_raw();
-          // tile it+kAhead goes into the stage of tile it-1, free after its PV
-          const bool with_dma = it + kAhead < n_tiles;
-          const TileDma dma = with_dma ? tile_dma(it + kAhead)
-                                       : TileDma{sm.cst[(it + kAhead) % kNStage], sm.rst[(it + kAhead) % kNRStage], cache, 0};
+          // tile it+AHEAD goes into the stage of tile it-1, free after its PV
+          // (int8 rows: the landing stage of tile it, converted by this wave
+          // before barrier it-1)
+          const bool with_dma = it + G::AHEAD < n_tiles;
+          const TileDma dma = with_dma ? tile_dma(it + G::AHEAD)
+                                       : TileDma{I8 ? sm.land[(it + G::AHEAD) % G::NLAND] : sm.cst[(it + G::AHEAD) % G::NST],
+                                                 sm.rst[(it + G::AHEAD) % G::NRST], cache, 0};
           const int buf = it & 1;
-          pv_tile(sm.cst[it % kNStage], sm.p[buf], sm.alpha[buf], sm.flag[buf], dma.cdst, dma.rdst, dma.src,
-                  dma.lim, with_dma, KS > 1 && it + 1 < n_tiles);
+          pv_tile(sm.cst[it % G::NST], sm.p[buf], sm.alpha[buf], sm.flag[buf], dma.cdst, dma.rdst, dma.src,
+                  dma.lim, with_dma, KS > 1 && it + 1 < n_tiles, I8 && it + 2 < n_tiles ? it + 2 : -1);
         }
         wait_lgkm0();
         barrier_raw();
         {
-          const char* const lo_a = sm.cst[n_tiles % kNStage];
-          const char* const lo_b = sm.cst[(n_tiles + 1) % kNStage];
+          const char* const lo_a = sm.cst[n_tiles % G::NST];
+          const char* const lo_b = sm.cst[(n_tiles + 1) % G::NST];
 #pragma unroll
           for (int q = 0; q < NRB; ++q) {
             const int qr = 16 * q + l16;
@@ -979,41 +1102,31 @@ void decode_bf16_grid(int rows_total, int n_wg, int* n_share, int* n_rg) {
   *n_share = ns < 1 ? 1 : ns;
 }
 
-template <bool QF32>
+template <bool QF32, bool QKN, bool I8>
 static hipError_t launch_mt(const DecodeArgs& a, int mt, dim3 grid, int n_share, int n_rg, int rows_total,
                             hipStream_t stream) {
-  if constexpr (QF32) {
-    if (a.seg.row_rinv) {
-      const dim3 block(kThreads);
-      switch (mt) {
-        case 16:
-          return launch((decode_bf16_kernel<16, true, true>), grid, block, stream, a, n_share, n_rg, rows_total);
-        case 32:
-          return launch((decode_bf16_kernel<32, true, true>), grid, block, stream, a, n_share, n_rg, rows_total);
-        default:
-          return launch((decode_bf16_kernel<64, true, true>), grid, block, stream, a, n_share, n_rg, rows_total);
-      }
-    }
-  }
   const dim3 block(kThreads);
   switch (mt) {
     case 16:
-      return launch((decode_bf16_kernel<16, QF32, false>), grid, block, stream, a, n_share, n_rg, rows_total);
+      return launch((decode_bf16_kernel<16, QF32, QKN, I8>), grid, block, stream, a, n_share, n_rg, rows_total);
     case 32:
-      return launch((decode_bf16_kernel<32, QF32, false>), grid, block, stream, a, n_share, n_rg, rows_total);
+      return launch((decode_bf16_kernel<32, QF32, QKN, I8>), grid, block, stream, a, n_share, n_rg, rows_total);
     default:
-      return launch((decode_bf16_kernel<64, QF32, false>), grid, block, stream, a, n_share, n_rg, rows_total);
+      return launch((decode_bf16_kernel<64, QF32, QKN, I8>), grid, block, stream, a, n_share, n_rg, rows_total);
   }
 }
 
-hipError_t launch_decode_bf16(const DecodeArgs& a, int n_wg, bool q_f32, hipStream_t stream) {
+hipError_t launch_decode_bf16(const DecodeArgs& a, int n_wg, bool q_f32, bool i8, hipStream_t stream) {
   const int rows_total = a.s_q * a.seg.head_count;
   const int mt = row_tile(rows_total);
   int n_share, n_rg;
   decode_bf16_grid(rows_total, n_wg, &n_share, &n_rg);
   const dim3 grid(n_share * n_rg);
-  if (q_f32) return launch_mt<true>(a, mt, grid, n_share, n_rg, rows_total, stream);
-  return launch_mt<false>(a, mt, grid, n_share, n_rg, rows_total, stream);
+  // the QK-Norm and int8 variants exist for an fp32 query only (checked by the caller)
+  if (q_f32 && i8) return launch_mt<true, false, true>(a, mt, grid, n_share, n_rg, rows_total, stream);
+  if (q_f32 && a.seg.row_rinv) return launch_mt<true, true, false>(a, mt, grid, n_share, n_rg, rows_total, stream);
+  if (q_f32) return launch_mt<true, false, false>(a, mt, grid, n_share, n_rg, rows_total, stream);
+  return launch_mt<false, false, false>(a, mt, grid, n_share, n_rg, rows_total, stream);
 }
 
 }  // namespace mla

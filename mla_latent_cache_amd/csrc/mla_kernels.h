@@ -23,6 +23,7 @@ struct SegArgs {
   int part_begin;
   int n_split;
   const float* row_rinv;       // QK-Norm: inverse key RMS per stored row, nullptr => none
+  const float* row_scale;      // int8 cache: latent scale per stored row, nullptr => 16-bit cache
 };
 
 struct DecodeArgs {
@@ -72,6 +73,9 @@ hipError_t launch_combine(const float* o_part, const float* lse_part, int n_rows
 hipError_t launch_combine_out_uv(const float* o_part, const float* lse_part, int n_tok, int n_heads, int n_part,
                                  int d_c, const void* w_uv, bool w_bf16, int d_v, void* o_lat, float* lse,
                                  void* out, bool out_bf16, hipStream_t stream);
+// int8 latent cache writer: bf16 rows [n][d_c + d_rope] -> packed rows [n][d_c + 2 d_rope] bytes + scales.
+hipError_t launch_quantize_latent_i8(const void* rows, int64_t n_rows, int d_c, int d_rope, void* out,
+                                     float* scales, hipStream_t stream);
 // QK-Norm: query scaling, the key Gram matrix and the per-row inverse RMS.
 hipError_t launch_qknorm_query(const void* q_nope, bool in_bf16, const float* g_q, const float* g_k, int n_tok,
                                int n_heads, int d_nope, float eps, float* q_out, hipStream_t stream);
@@ -85,7 +89,8 @@ hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
 // bf16 MFMA decode (d_c = 512, d_rope = 64, page 64).  n_wg workgroups per
 // row group; balanced split of all rows of the segment over them.
 // q_f32: q_lat / q_rot are fp32 (split into bf16 hi + lo) instead of bf16.
-hipError_t launch_decode_bf16(const DecodeArgs& a, int n_wg, bool q_f32, hipStream_t stream);
+// i8: the cache rows are int8 latent codes (scale seg.row_scale) + bf16 rotary keys.
+hipError_t launch_decode_bf16(const DecodeArgs& a, int n_wg, bool q_f32, bool i8, hipStream_t stream);
 // Grid shape of the bf16 decode for one segment: row groups and shares.
 void decode_bf16_grid(int rows_total, int n_wg, int* n_share, int* n_rg);
 

@@ -461,6 +461,64 @@ hipError_t launch_combine_out_uv(const float* o_part, const float* lse_part, int
 }
 
 // ---------------------------------------------------------------------------
+// int8 latent cache writer (QuantMLA abstract: a low-bit latent cache that
+// attention dequantizes; here the plain per-row symmetric int8 form): one
+// wave per stored row.  amax = max |c_i| over the row's d_c latent entries,
+// scale = amax / 127 (IEEE fp32 quotient), code_i = the nearest integer to
+// c_i / scale (fp32 quotient, ties to even) clamped to [-127, 127]; a zero
+// row has scale 0 and codes 0.  The packed row is the d_c codes followed by
+// the d_rope 16-bit rotary entries copied unchanged.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quantize_latent_i8_kernel(const bf16* __restrict__ rows, int64_t n_rows,
+                                                                 int d_c, int d_rope, char* __restrict__ out,
+                                                                 float* __restrict__ scales) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= n_rows) return;
+  const int lane = threadIdx.x & 63;
+  const int in_w = d_c + d_rope;
+  const int out_w = d_c + 2 * d_rope;
+  const bf16* src = rows + r * in_w;
+  char* dst = out + r * out_w;
+  // lane owns latent entries [8 lane, 8 lane + 8) (d_c <= 512, a multiple of 8)
+  float v[8];
+  const bool mine = 8 * lane < d_c;
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    v[e] = mine ? (float)src[8 * lane + e] : 0.f;
+    amax = fmaxf(amax, fabsf(v[e]));
+  }
+  amax = wave_max(amax);
+  const float scale = amax / 127.f;
+  if (mine) {
+    unsigned lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float q = scale > 0.f ? fminf(fmaxf(rintf(v[e] / scale), -127.f), 127.f) : 0.f;
+      const unsigned byte = (unsigned)((int)q & 0xff);
+      if (e < 4) lo |= byte << (8 * e);
+      else hi |= byte << (8 * (e - 4));
+    }
+    *(uint2*)(dst + 8 * lane) = uint2{lo, hi};
+  }
+  // rotary entries: 2 d_rope bytes in 8-byte pieces
+  const unsigned short* rs = (const unsigned short*)(src + d_c);
+  if (lane < d_rope / 4) {
+    const unsigned short* p = rs + 4 * lane;
+    unsigned lo = (unsigned)p[0] | ((unsigned)p[1] << 16), hi = (unsigned)p[2] | ((unsigned)p[3] << 16);
+    *(uint2*)(dst + d_c + 8 * lane) = uint2{lo, hi};
+  }
+  if (lane == 0) scales[r] = scale;
+}
+
+hipError_t launch_quantize_latent_i8(const void* rows, int64_t n_rows, int d_c, int d_rope, void* out,
+                                     float* scales, hipStream_t stream) {
+  const dim3 grid((unsigned)((n_rows + 3) / 4));
+  return launch(quantize_latent_i8_kernel, grid, dim3(256), stream, (const bf16*)rows, n_rows, d_c, d_rope,
+                (char*)out, scales);
+}
+
+// ---------------------------------------------------------------------------
 // QK-Norm (QK-Norm MLA page, abstract): RMSNorm after the projections, the
 // statistic over a token's whole content projection.
 //  * qknorm_query_kernel: one block per query token; the sum of squares over

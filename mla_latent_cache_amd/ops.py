@@ -11,9 +11,14 @@ from typing import List, Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import MLA_BF16, MLA_F32, MlaSegment
+from ._lib import MLA_BF16, MLA_F32, MLA_I8, MlaSegment
 
 _DT = {torch.float32: MLA_F32, torch.bfloat16: MLA_BF16}
+
+
+def _cache_dt(cache: torch.Tensor) -> int:
+    """Cache format: fp32 / bf16 rows, or packed int8 rows held as uint8 bytes."""
+    return MLA_I8 if cache.dtype == torch.uint8 else _dt(cache)
 
 
 def _dt(t: torch.Tensor) -> int:
@@ -137,6 +142,22 @@ def combine_out_uv(o_part: torch.Tensor, lse_part: torch.Tensor, w_uv: torch.Ten
     return out, o_lat, lse
 
 
+def quantize_latent_i8(rows: torch.Tensor, d_c: int, out: Optional[torch.Tensor] = None,
+                       scales: Optional[torch.Tensor] = None):
+    """Int8 latent cache from bf16 rows [..., d_c + d_rope]: (packed rows uint8
+    [..., d_c + 2 d_rope], scales fp32 [...])."""
+    width = rows.shape[-1]
+    d_rope = width - d_c
+    n_rows = rows.numel() // width
+    if out is None:
+        out = torch.empty(rows.shape[:-1] + (d_c + 2 * d_rope,), dtype=torch.uint8, device=rows.device)
+    if scales is None:
+        scales = torch.empty(rows.shape[:-1], dtype=torch.float32, device=rows.device)
+    _lib.call("mla_quantize_latent_i8", _ptr(rows), _dt(rows), n_rows, d_c, d_rope, _ptr(out), _ptr(scales),
+              _stream())
+    return out, scales
+
+
 def qknorm_query(q_nope: torch.Tensor, g_q: torch.Tensor, g_k: torch.Tensor, eps: float,
                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """QK-Norm of the content query with both static weights folded in:
@@ -187,6 +208,7 @@ class Segment:
     part_begin: int = 0
     n_split: int = 1
     row_rinv: Optional[torch.Tensor] = None      # fp32, cache.shape[:2] (QK-Norm)
+    row_scale: Optional[torch.Tensor] = None     # fp32, cache.shape[:2] (int8 cache, uint8 rows)
 
     def to_c(self) -> MlaSegment:
         s = MlaSegment()
@@ -208,6 +230,7 @@ class Segment:
         s.part_begin = self.part_begin
         s.n_split = self.n_split
         s.row_rinv = _ptr(self.row_rinv)
+        s.row_scale = _ptr(self.row_scale)
         return s
 
 
@@ -217,9 +240,9 @@ def decode_splitkv(segments: Sequence[Segment], q_lat: torch.Tensor, batch: int,
     n_tok, n_heads, d_c = q_lat.shape
     d_rope = segments[0].q_rot.shape[2]
     n_part = o_part.shape[2]
-    cache_dt = _dt(segments[0].cache)
+    cache_dt = _cache_dt(segments[0].cache)
     for s in segments:
-        if _dt(s.cache) != cache_dt or s.q_rot.dtype != q_lat.dtype:
+        if _cache_dt(s.cache) != cache_dt or s.q_rot.dtype != q_lat.dtype:
             raise ValueError("segments must share the cache dtype; q_rot must have q_lat's dtype")
     arr = (MlaSegment * len(segments))(*[s.to_c() for s in segments])
     _lib.call("mla_decode_splitkv", arr, len(segments), _ptr(q_lat), _dt(q_lat), cache_dt, batch, s_q, n_heads,

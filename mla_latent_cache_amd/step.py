@@ -11,7 +11,10 @@ With QK-Norm (``qk_norm=(g_q, g_k, eps)``) the chain starts with
 mla_qknorm_query (the normalised, weighted content query in fp32), absorbs
 that with an fp32 copy of U_K, and each segment carries the inverse RMS of
 its rows' content keys, computed once here from the cache (mla_qknorm_key_gram
-and mla_qknorm_key_rinv: the cache writer's share of the work).
+and mla_qknorm_key_rinv: the cache writer's share of the work).  With an
+int8 cache (``quant="int8"``) each segment's bf16 rows are quantized here by
+mla_quantize_latent_i8 (again the cache writer's part) and the decode reads
+the packed rows and their scales.
 
 and lays out the partial-state slots: segments with disjoint head ranges that
 follow each other share a slot range (e.g. a document read by the Local heads
@@ -49,7 +52,7 @@ class DecodeStep:
     def __init__(self, q_nope, q_pe, q_pos, w_uk, w_uv, segments: List[StepSegment], batch: int, s_q: int,
                  scale: float, rope_base: float = 10000.0, n_wg: int = 0,
                  n_split: Optional[Sequence[int]] = None, fuse_post: Optional[bool] = None,
-                 qk_norm: Optional[tuple] = None):
+                 qk_norm: Optional[tuple] = None, quant: Optional[str] = None):
         self.q_nope, self.q_pe, self.q_pos = q_nope, q_pe, q_pos
         self.w_uk, self.w_uv = w_uk, w_uv
         self.batch, self.s_q, self.scale, self.rope_base, self.n_wg = batch, s_q, scale, rope_base, n_wg
@@ -110,10 +113,20 @@ class DecodeStep:
             self.gram = ops.qknorm_key_gram(w_uk)
             d_nope = w_uk.shape[1]
             rinvs = [ops.qknorm_key_rinv(s.cache, self.gram, H, d_nope, self.qk_eps) for s in segments]
+        # int8 cache: the cache writer's quantization of each segment's rows
+        caches = [s.cache for s in segments]
+        scales = [None] * len(segments)
+        if quant is not None:
+            if quant != "int8":
+                raise ValueError(f"unknown cache quantization {quant!r}")
+            q8 = [ops.quantize_latent_i8(s.cache, d_c) for s in segments]
+            caches = [c for c, _ in q8]
+            scales = [sc for _, sc in q8]
         self.segments = [
-            ops.Segment(cache=s.cache, seq_lens=s.seq_lens, q_rot=self.q_rots[self.seg_rot[i]][1],
+            ops.Segment(cache=caches[i], seq_lens=s.seq_lens, q_rot=self.q_rots[self.seg_rot[i]][1],
                         block_table=s.block_table, head_begin=s.head_begin, head_count=s.head_count,
-                        causal=s.causal, part_begin=part_begin[i], n_split=self.n_split[i], row_rinv=rinvs[i])
+                        causal=s.causal, part_begin=part_begin[i], n_split=self.n_split[i], row_rinv=rinvs[i],
+                        row_scale=scales[i])
             for i, s in enumerate(segments)
         ]
         self.q_lat = torch.empty((n_tok, H, d_c), dtype=q_dt, device=dev)
@@ -218,7 +231,7 @@ class DecodeStep:
                                                self.q_lat.data_ptr(), dt(self.q_lat), n_tok, H, d_nope, d_c, st)))
         self._seg_arr = (_lib.MlaSegment * len(self.segments))(*[sg.to_c() for sg in self.segments])
         dec = [(lib.mla_decode_splitkv, (self._seg_arr, len(self.segments), self.q_lat.data_ptr(), dt(self.q_lat),
-                                         dt(self.segments[0].cache), self.batch, self.s_q, H, d_c, d_r,
+                                         ops._cache_dt(self.segments[0].cache), self.batch, self.s_q, H, d_c, d_r,
                                          float(self.scale), self.o_part.data_ptr(), self.lse_part.data_ptr(),
                                          self.n_part, self.n_wg, st))]
         if self.fuse_post:
@@ -259,4 +272,4 @@ def step_from_inputs(x, device="cuda", n_wg: int = 0, n_split=None, fuse_post=No
         qk = (x.g_q.to(d), x.g_k.to(d), x.spec.qk_eps)
     return DecodeStep(x.q_nope.to(d), x.q_pe.to(d), x.q_pos.to(d), x.w_uk.to(d), x.w_uv.to(d), segs,
                       x.spec.batch, x.spec.s_q, x.scale, x.rope_base, n_wg=n_wg, n_split=n_split,
-                      fuse_post=fuse_post, qk_norm=qk)
+                      fuse_post=fuse_post, qk_norm=qk, quant=getattr(x.spec, "quant", None))

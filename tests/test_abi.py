@@ -111,6 +111,14 @@ def test_null_and_shape_errors_before_any_gpu_call(lib):
     assert _st(lib, "mla_qknorm_key_rinv", P, 1, 10, 576, P, 512, 16, 128, float("nan"), P, None) == 2
     assert _st(lib, "mla_qknorm_key_rinv", P, 1, 10, 576, None, 512, 16, 128, 1e-6, P, None) == 1
     assert _st(lib, "mla_qknorm_key_rinv", P, 1, 0, 576, P, 512, 16, 128, 1e-6, P, None) == 0
+    # mla_quantize_latent_i8(rows, row_dtype, n_rows, d_c, d_rope, out_rows, scales, stream)
+    assert _st(lib, "mla_quantize_latent_i8", P, 1, 10, 512, 64, None, P, None) == 1
+    assert _st(lib, "mla_quantize_latent_i8", P, 0, 10, 512, 64, P, P, None) == 3
+    assert _st(lib, "mla_quantize_latent_i8", P, 1, 10, 1024, 64, P, P, None) == 2
+    assert _st(lib, "mla_quantize_latent_i8", P, 1, 10, 500, 64, P, P, None) == 2
+    assert _st(lib, "mla_quantize_latent_i8", P, 1, 10, 512, 66, P, P, None) == 2
+    assert _st(lib, "mla_quantize_latent_i8", P + 4, 1, 10, 512, 64, P, P, None) == 4
+    assert _st(lib, "mla_quantize_latent_i8", P, 1, 0, 512, 64, P, P, None) == 0
     # zero-size calls succeed without launching anything
     assert _st(lib, "mla_absorb_q", P, P, 1, P, 0, 0, 1, 128, 512, None) == 0
 
@@ -141,3 +149,9 @@ def test_null_and_shape_errors_before_any_gpu_call(lib):
     assert dec([seg(head_count=4)], n_heads=4, dtype=7) == 3
     assert dec([seg()], dtype=0, q_dtype=1) == 5          # fp32 cache needs an fp32 query
     assert dec([seg(row_rinv=P)], q_dtype=1) == 5         # QK-Norm factors need an fp32 query
+    # int8 cache (cache_dtype 2): fp32 query, row_scale on every segment, no QK-Norm
+    assert dec([seg()], dtype=2) == 1                     # row_scale missing
+    assert dec([seg(row_scale=P)], dtype=2, q_dtype=1) == 5
+    assert dec([seg(row_scale=P, row_rinv=P)], dtype=2) == 5
+    assert dec([seg(row_scale=P)], dtype=1) == 5          # row_scale only with an int8 cache
+    assert dec([seg(row_scale=P)], dtype=3) == 3

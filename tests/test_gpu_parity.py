@@ -125,6 +125,16 @@ EDGE = {
         SegSpec("kv", lengths=(2, 95, 513), causal=True, online=True),)),
     "qknorm_toy_f32": _custom("edge-qknf32", dtype="f32", batch=3, heads=2, qk_norm=True, segs=(
         SegSpec("kv", lengths=(16, 0, 130), layout="paged", page_size=8, spare_pages=1, online=True),)),
+    # int8 latent cache: row scales through each row-group size, contiguous
+    # and paged, empty and one-row requests, causal rows, and the 64-row
+    # groups' first-order lse correction with twice-spread scores
+    "int8_rows16": _custom("edge-i8-16", batch=4, heads=16, quant="int8", segs=(
+        SegSpec("kv", lengths=(0, 1, 37, 300), online=True),)),
+    "int8_rows32_causal": _custom("edge-i8-32", batch=3, heads=16, s_q=2, quant="int8", segs=(
+        SegSpec("kv", lengths=(2, 95, 513), causal=True, layout="paged", page_size=64, spare_pages=1,
+                online=True),)),
+    "int8_peaked_rows64": _custom("edge-i8-64", batch=4, heads=64, quant="int8", scale=2 / math.sqrt(192), segs=(
+        SegSpec("kv", lengths=(1, 37, 300, 1000), online=True),)),
 }
 
 
@@ -270,6 +280,33 @@ def test_qknorm_calls(dtype, dims):
     assert np.all(np.abs(f64(rinv) - r_ref) <= 1e-4 * r_ref)
 
 
+def test_quantize_call():
+    """mla_quantize_latent_i8 against the oracle's quantizer, bit for bit:
+    codes, scales and the rotary bytes.  Rows: random at many magnitudes, a
+    zero row, a row at unit scale with exact ties, one with a single nonzero."""
+    import oracle.mla_quant as Q
+    from mla_latent_cache_amd import ops
+    g = torch.Generator().manual_seed(17)
+    n, d_c, d_r = 1000, 512, 64
+    rows = torch.randn((n, d_c + d_r), generator=g) * torch.exp(torch.empty((n, 1)).uniform_(-10, 10, generator=g))
+    rows[3] = 0
+    rows[4, :d_c] = torch.tensor([127.0, 0.5, 1.5, 2.5, -0.5, -1.5, -126.5, 126.5] * 64)
+    rows[5, :d_c] = 0
+    rows[5, 17] = -3.0
+    rows = rows.to(torch.bfloat16)
+    packed, scales = ops.quantize_latent_i8(rows.cuda(), d_c)
+    torch.cuda.synchronize()
+    packed = packed.cpu()
+    codes_ref, scales_ref = Q.quantize_latent_i8(rows[:, :d_c].float().numpy())
+    got_codes = packed[:, :d_c].view(torch.int8).numpy()
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), scales_ref.view(np.uint32))
+    assert np.array_equal(got_codes, codes_ref), int(np.sum(got_codes != codes_ref))
+    assert np.array_equal(packed[:, d_c:].numpy(), rows[:, d_c:].contiguous().view(torch.uint8).numpy())
+    assert got_codes[4, :8].tolist() == [127, 0, 2, 2, 0, -2, -126, 126]
+    assert float(scales[3]) == 0.0 and not np.any(got_codes[3])
+    assert got_codes[5, 17] == -127 and int(np.count_nonzero(got_codes[5])) == 1
+
+
 # ------------------------------------------------------------ full sizes, sampled
 @pytest.mark.parametrize("out_dtype,w_dtype,dims", [
     (torch.bfloat16, torch.bfloat16, (4, 16, 65, 512, 128)),   # the 512-column register path
@@ -309,14 +346,14 @@ def test_combine_out_uv_call(out_dtype, w_dtype, dims):
     assert np.all(np.abs(f64(out) - out_ref) <= rel * np.abs(out_ref) + 1e-5 * rms)
 
 
-@pytest.mark.parametrize("name", ["small", "dsv3", "long", "merge", "prefill", "qknorm"])
+@pytest.mark.parametrize("name", ["small", "dsv3", "long", "merge", "prefill", "qknorm", "int8"])
 def test_full_size_sampled(name):
     """The bench's launch configuration (default grid) at full size; the
     oracle checks sampled (request, head) pairs."""
     x = M.make(name, SEEDS[name])
     print(f"[parity] full {name} seed {SEEDS[name]}", flush=True)
     _, out, o_lat, lse = _run(x)
-    n_req = {"small": 2, "dsv3": 3, "long": 1, "merge": 2, "prefill": 1, "qknorm": 2}[name]
+    n_req = {"small": 2, "dsv3": 3, "long": 1, "merge": 2, "prefill": 1, "qknorm": 2, "int8": 1}[name]
     reqs, heads = sample_pairs(x, n_req, 3, seed=SEEDS[name])
     errs = check_step(x, out, o_lat, lse, requests=reqs, heads=heads, label=f"{name} full")
     print(f"[parity] {name} full reqs={reqs} heads={heads}: {errs}", flush=True)
