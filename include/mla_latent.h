@@ -219,14 +219,18 @@ mla_status mla_combine_lse(const float* o_part, const float* lse_part, int n_row
  *   q_rots[k] = rope_relocate_q(q_pe, pos, shifts[k])      (rot_dtype), k < n_shift
  *
  * q_nope, w_uk, q_lat, q_pe, pos: as in mla_absorb_q / rope_relocate_q; q_pe
- * has in_dtype.  q_rots: host array of n_shift device pointers
- * [n_tok][n_heads][d_rope]; shifts: host array of n_shift device pointers
- * ([n_tok] int64, an entry may be NULL = no shift) or NULL for all zero.
- * n_shift 0..8.  A small decode batch spends most of these two kernels in
- * launch latency, so one launch instead of 1 + n_shift shortens the step.
+ * and w_uk have in_dtype, q_nope has q_dtype: either in_dtype, or MLA_F32
+ * with bf16 weights on the MFMA path (an fp32 query, e.g. the output of
+ * mla_qknorm_query, enters as bf16 hi + lo parts with fp32 accumulation;
+ * other shapes return MLA_ERR_UNSUPPORTED).  q_rots: host array of n_shift
+ * device pointers [n_tok][n_heads][d_rope]; shifts: host array of n_shift
+ * device pointers ([n_tok] int64, an entry may be NULL = no shift) or NULL for
+ * all zero.  n_shift 0..8.  A small decode batch spends most of these two
+ * kernels in launch latency, so one launch instead of 1 + n_shift shortens
+ * the step.
  */
-mla_status mla_prepare_q(const void* q_nope, const void* q_pe, const void* w_uk, int in_dtype, void* q_lat,
-                         int lat_dtype, void* const* q_rots, const int64_t* const* shifts, int n_shift,
+mla_status mla_prepare_q(const void* q_nope, int q_dtype, const void* q_pe, const void* w_uk, int in_dtype,
+                         void* q_lat, int lat_dtype, void* const* q_rots, const int64_t* const* shifts, int n_shift,
                          int rot_dtype, const int64_t* pos, int n_tok, int n_heads, int d_nope, int d_rope, int d_c,
                          double base, void* stream);
 
@@ -306,7 +310,8 @@ mla_status mla_quantize_latent_i8(const void* rows, int row_dtype, int64_t n_row
  * mla_qknorm_query: q_out[t][h][i] = g_q[h][i] g_k[h][i] q_nope[t][h][i] / rms_t,
  *   rms_t = sqrt(mean_{h,i} q_nope[t][h][i]^2 + eps).
  *   q_nope [n_tok][n_heads][d_nope] in_dtype; g_q, g_k [n_heads][d_nope] fp32;
- *   q_out [n_tok][n_heads][d_nope] fp32 (then mla_absorb_q with in_dtype MLA_F32).
+ *   q_out [n_tok][n_heads][d_nope] fp32 (then mla_prepare_q with q_dtype MLA_F32 and
+ *   the bf16 w_uk, or mla_absorb_q with fp32 weights).
  * mla_qknorm_key_gram: gram[a][b] = sum_{h,i} w_uk[h][i][a] w_uk[h][i][b],
  *   w_uk [n_heads][d_nope][d_c] w_dtype, gram [d_c][d_c] fp32 (d_c <= 512).
  * mla_qknorm_key_rinv: rinv[r] = 1 / sqrt(c_r^T gram c_r / (n_heads * d_nope) + eps)

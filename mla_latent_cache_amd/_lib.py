@@ -55,7 +55,7 @@ SIGNATURES = {
                            c_void_p]),
     "mla_combine_out_uv": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_int, c_int,
                                    c_void_p, c_void_p, c_void_p, c_int, c_void_p]),
-    "mla_prepare_q": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_int, POINTER(c_void_p),
+    "mla_prepare_q": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_int, c_void_p, c_int, POINTER(c_void_p),
                               POINTER(c_void_p), c_int, c_int, c_void_p, c_int, c_int, c_int, c_int, c_int,
                               c_double, c_void_p]),
     "mla_quantize_latent_i8": (c_int, [c_void_p, c_int, c_int64, c_int, c_int, c_void_p, c_void_p, c_void_p]),

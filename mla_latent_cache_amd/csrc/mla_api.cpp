@@ -120,14 +120,14 @@ mla_status mla_absorb_q(const void* q_nope, const void* w_uk, int in_dtype, void
                     "mla_absorb_q launch");
 }
 
-mla_status mla_prepare_q(const void* q_nope, const void* q_pe, const void* w_uk, int in_dtype, void* q_lat,
-                         int lat_dtype, void* const* q_rots, const int64_t* const* shifts, int n_shift,
+mla_status mla_prepare_q(const void* q_nope, int q_dtype, const void* q_pe, const void* w_uk, int in_dtype,
+                         void* q_lat, int lat_dtype, void* const* q_rots, const int64_t* const* shifts, int n_shift,
                          int rot_dtype, const int64_t* pos, int n_tok, int n_heads, int d_nope, int d_rope, int d_c,
                          double base, void* stream) {
   if (!q_nope || !q_pe || !w_uk || !q_lat || !pos || (n_shift > 0 && !q_rots))
     return fail(MLA_ERR_NULL, "mla_prepare_q: null pointer");
-  if (!dtype_ok(in_dtype) || !dtype_ok(lat_dtype) || !dtype_ok(rot_dtype))
-    return fail(MLA_ERR_DTYPE, "mla_prepare_q: dtypes %d, %d, %d", in_dtype, lat_dtype, rot_dtype);
+  if (!dtype_ok(q_dtype) || !dtype_ok(in_dtype) || !dtype_ok(lat_dtype) || !dtype_ok(rot_dtype))
+    return fail(MLA_ERR_DTYPE, "mla_prepare_q: dtypes %d, %d, %d, %d", q_dtype, in_dtype, lat_dtype, rot_dtype);
   if (n_shift < 0 || n_shift > mla::kMaxShift)
     return fail(MLA_ERR_SHAPE, "mla_prepare_q: n_shift=%d (0..%d)", n_shift, mla::kMaxShift);
   for (int k = 0; k < n_shift; ++k)
@@ -137,17 +137,21 @@ mla_status mla_prepare_q(const void* q_nope, const void* q_pe, const void* w_uk,
     return fail(MLA_ERR_SHAPE, "mla_prepare_q: n_tok=%d n_heads=%d d_nope=%d d_rope=%d d_c=%d", n_tok, n_heads,
                 d_nope, d_rope, d_c);
   if (!(base > 1.0) || !std::isfinite(base)) return fail(MLA_ERR_SHAPE, "mla_prepare_q: base=%g", base);
+  const bool mfma = in_dtype == MLA_BF16 && mla::absorb_mfma_ok(q_nope, w_uk, d_nope, d_c);
+  if (q_dtype != in_dtype && !(q_dtype == MLA_F32 && mfma))
+    return fail(MLA_ERR_UNSUPPORTED, "mla_prepare_q: an fp32 query with bf16 weights needs d_nope=128, d_c=512 "
+                "and 16-byte aligned q_nope and w_uk");
   if (n_tok == 0) return ok();
   const hipStream_t st = (hipStream_t)stream;
-  if (in_dtype == MLA_BF16 && mla::absorb_mfma_ok(q_nope, w_uk, d_nope, d_c)) {
+  if (mfma) {
     mla::RopeTargets rt{};
     rt.n = n_shift;
     for (int k = 0; k < n_shift; ++k) {
       rt.q_rot[k] = q_rots[k];
       rt.shift[k] = shifts ? shifts[k] : nullptr;
     }
-    return hip_status(mla::launch_prepare_mfma(q_nope, w_uk, q_lat, lat_dtype == MLA_BF16, q_pe, pos, rt,
-                                               rot_dtype == MLA_BF16, n_tok, n_heads, d_rope, base, st),
+    return hip_status(mla::launch_prepare_mfma(q_nope, q_dtype == MLA_F32, w_uk, q_lat, lat_dtype == MLA_BF16, q_pe,
+                                               pos, rt, rot_dtype == MLA_BF16, n_tok, n_heads, d_rope, base, st),
                       "mla_prepare_q launch");
   }
   // other shapes and dtypes: the two kernels one after the other

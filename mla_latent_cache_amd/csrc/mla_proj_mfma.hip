@@ -24,10 +24,13 @@ constexpr int kLat = 512;         // d_c
 constexpr int kAbsCols = 128;     // output columns per absorb workgroup
 constexpr int kAbsLds = kAbsCols * 2 + 16;  // bytes per LDS weight row (padded)
 
-// Workgroup (head h, output columns j0 .. j0 + 127) of the absorption.
-template <typename TO>
-__device__ __forceinline__ void absorb_block(const bf16* __restrict__ q_nope, const bf16* __restrict__ w_uk,
+// Workgroup (head h, output columns j0 .. j0 + 127) of the absorption.  An
+// fp32 query (TQ = float) enters as bf16 hi + lo parts (q = hi + lo to about
+// 2^-17), each multiplied by the bf16 weights with fp32 accumulation.
+template <typename TO, typename TQ = bf16>
+__device__ __forceinline__ void absorb_block(const TQ* __restrict__ q_nope, const bf16* __restrict__ w_uk,
                                              TO* __restrict__ q_lat, int n_tok, int n_heads, int h, int j0) {
+  constexpr bool QF = sizeof(TQ) == 4;
   __shared__ __attribute__((aligned(16))) char wl[kNope * kAbsLds];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, lg = lane >> 4;
@@ -41,12 +44,29 @@ __device__ __forceinline__ void absorb_block(const bf16* __restrict__ q_nope, co
   const int rq = l16 >> 2, qq = lane & 3;
   for (int t0 = 0; t0 < n_tok; t0 += 16) {
     // A operand: 16 tokens x 128 i, lane row l16, k = 32 ks + 8 lg + (0..7)
-    bf16x8 qa[4];
+    bf16x8 qa[4], ql[QF ? 4 : 1];
     const int t = t0 + l16;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      qa[ks] = t < n_tok ? *(const bf16x8*)(q_nope + ((int64_t)t * n_heads + h) * kNope + 32 * ks + 8 * lg)
-                         : bf16x8{};
+    for (int ks = 0; ks < 4; ++ks) {
+      if constexpr (QF) {
+        f32x4 v0 = f32x4{0.f, 0.f, 0.f, 0.f}, v1 = v0;
+        if (t < n_tok) {
+          const float* src = (const float*)q_nope + ((int64_t)t * n_heads + h) * kNope + 32 * ks + 8 * lg;
+          v0 = *(const f32x4*)src;
+          v1 = *(const f32x4*)(src + 4);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = e < 4 ? v0[e] : v1[e - 4];
+          const bf16 hi = (bf16)v;
+          qa[ks][e] = hi;
+          ql[ks][e] = (bf16)(v - (float)hi);
+        }
+      } else {
+        qa[ks] = t < n_tok ? *(const bf16x8*)(q_nope + ((int64_t)t * n_heads + h) * kNope + 32 * ks + 8 * lg)
+                           : bf16x8{};
+      }
+    }
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       const int c0 = 32 * wave + 16 * cb;  // column block within the slice
@@ -59,6 +79,7 @@ __device__ __forceinline__ void absorb_block(const bf16* __restrict__ q_nope, co
         const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p0 + 4 * kAbsLds));
         const bf16x8 wb = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], wb, acc, 0, 0, 0);
+        if constexpr (QF) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[ks % (QF ? 4 : 1)], wb, acc, 0, 0, 0);
       }
       // D layout: lane holds column c0 + l16, rows (tokens) 4 lg + e
 #pragma unroll
@@ -80,8 +101,8 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const bf16* __restrict
 // rope_relocate_q for up to kMaxShift shifts and the absorption in one launch:
 // grid (heads, 4 + R); y < 4 are the absorption workgroups, y = 4 .. 4+R-1
 // rotate the head's rotary query pairs (all tokens and shifts) between them.
-template <typename TL, typename TR>
-__global__ __launch_bounds__(256) void prepare_mfma_kernel(const bf16* __restrict__ q_nope,
+template <typename TL, typename TR, typename TQ>
+__global__ __launch_bounds__(256) void prepare_mfma_kernel(const TQ* __restrict__ q_nope,
                                                            const bf16* __restrict__ w_uk, TL* __restrict__ q_lat,
                                                            const bf16* __restrict__ q_pe,
                                                            const int64_t* __restrict__ pos, RopeTargets rt,
@@ -155,28 +176,39 @@ bool absorb_mfma_ok(const void* q_nope, const void* w_uk, int d_nope, int d_c) {
   return d_nope == kNope && d_c == kLat && al16(q_nope) && al16(w_uk);
 }
 
-template <typename TL, typename TR>
+template <typename TL, typename TR, typename TQ>
 static hipError_t prepare_launch(const void* q_nope, const void* w_uk, void* q_lat, const void* q_pe,
                                  const int64_t* pos, const RopeTargets& rt, int n_tok, int n_heads, int d_rope,
                                  double base, hipStream_t stream) {
   // rotation workgroups per head: one per 256 pairs (all tokens and shifts), at most 64
   const int pairs = rt.n * n_tok * (d_rope / 2);
   const int n_r = std::max(1, std::min(64, (pairs + 255) / 256));
-  return launch(prepare_mfma_kernel<TL, TR>, dim3(n_heads, kLat / kAbsCols + n_r), dim3(256), stream,
-                (const bf16*)q_nope, (const bf16*)w_uk, (TL*)q_lat, (const bf16*)q_pe, pos, rt, n_tok, n_heads,
+  return launch(prepare_mfma_kernel<TL, TR, TQ>, dim3(n_heads, kLat / kAbsCols + n_r), dim3(256), stream,
+                (const TQ*)q_nope, (const bf16*)w_uk, (TL*)q_lat, (const bf16*)q_pe, pos, rt, n_tok, n_heads,
                 d_rope, base);
 }
 
-hipError_t launch_prepare_mfma(const void* q_nope, const void* w_uk, void* q_lat, bool lat_bf16, const void* q_pe,
-                               const int64_t* pos, const RopeTargets& rt, bool rot_bf16, int n_tok, int n_heads,
-                               int d_rope, double base, hipStream_t stream) {
+template <typename TQ>
+static hipError_t prepare_dispatch(const void* q_nope, const void* w_uk, void* q_lat, bool lat_bf16,
+                                   const void* q_pe, const int64_t* pos, const RopeTargets& rt, bool rot_bf16,
+                                   int n_tok, int n_heads, int d_rope, double base, hipStream_t stream) {
   if (lat_bf16 && rot_bf16)
-    return prepare_launch<bf16, bf16>(q_nope, w_uk, q_lat, q_pe, pos, rt, n_tok, n_heads, d_rope, base, stream);
+    return prepare_launch<bf16, bf16, TQ>(q_nope, w_uk, q_lat, q_pe, pos, rt, n_tok, n_heads, d_rope, base, stream);
   if (lat_bf16)
-    return prepare_launch<bf16, float>(q_nope, w_uk, q_lat, q_pe, pos, rt, n_tok, n_heads, d_rope, base, stream);
+    return prepare_launch<bf16, float, TQ>(q_nope, w_uk, q_lat, q_pe, pos, rt, n_tok, n_heads, d_rope, base, stream);
   if (rot_bf16)
-    return prepare_launch<float, bf16>(q_nope, w_uk, q_lat, q_pe, pos, rt, n_tok, n_heads, d_rope, base, stream);
-  return prepare_launch<float, float>(q_nope, w_uk, q_lat, q_pe, pos, rt, n_tok, n_heads, d_rope, base, stream);
+    return prepare_launch<float, bf16, TQ>(q_nope, w_uk, q_lat, q_pe, pos, rt, n_tok, n_heads, d_rope, base, stream);
+  return prepare_launch<float, float, TQ>(q_nope, w_uk, q_lat, q_pe, pos, rt, n_tok, n_heads, d_rope, base, stream);
+}
+
+hipError_t launch_prepare_mfma(const void* q_nope, bool q_f32, const void* w_uk, void* q_lat, bool lat_bf16,
+                               const void* q_pe, const int64_t* pos, const RopeTargets& rt, bool rot_bf16, int n_tok,
+                               int n_heads, int d_rope, double base, hipStream_t stream) {
+  if (q_f32)
+    return prepare_dispatch<float>(q_nope, w_uk, q_lat, lat_bf16, q_pe, pos, rt, rot_bf16, n_tok, n_heads, d_rope,
+                                   base, stream);
+  return prepare_dispatch<bf16>(q_nope, w_uk, q_lat, lat_bf16, q_pe, pos, rt, rot_bf16, n_tok, n_heads, d_rope, base,
+                                stream);
 }
 
 hipError_t launch_absorb_mfma(const void* q_nope, const void* w_uk, void* q_lat, bool out_bf16, int n_tok,

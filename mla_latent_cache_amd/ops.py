@@ -78,8 +78,8 @@ def prepare_args(q_nope: torch.Tensor, q_pe: torch.Tensor, w_uk: torch.Tensor, q
     rot_arr = (ctypes.c_void_p * max(1, n))(*[r.data_ptr() for r in q_rots])
     sh_arr = (ctypes.c_void_p * max(1, n))(*[_ptr(s) for s in shifts])
     rot_dt = _dt(q_rots[0]) if n else 0
-    return (_ptr(q_nope), _ptr(q_pe), _ptr(w_uk), _dt(q_nope), _ptr(q_lat), _dt(q_lat), rot_arr, sh_arr, n, rot_dt,
-            _ptr(pos), n_tok, n_heads, d_nope, d_rope, d_c, float(base), stream)
+    return (_ptr(q_nope), _dt(q_nope), _ptr(q_pe), _ptr(w_uk), _dt(w_uk), _ptr(q_lat), _dt(q_lat), rot_arr, sh_arr, n,
+            rot_dt, _ptr(pos), n_tok, n_heads, d_nope, d_rope, d_c, float(base), stream)
 
 
 def prepare_q(q_nope: torch.Tensor, q_pe: torch.Tensor, w_uk: torch.Tensor, pos: torch.Tensor,

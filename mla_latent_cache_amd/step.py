@@ -8,10 +8,12 @@
 (the first two as one mla_prepare_q launch for up to 8 distinct shifts).
 
 With QK-Norm (``qk_norm=(g_q, g_k, eps)``) the chain starts with
-mla_qknorm_query (the normalised, weighted content query in fp32), absorbs
-that with an fp32 copy of U_K, and each segment carries the inverse RMS of
-its rows' content keys, computed once here from the cache (mla_qknorm_key_gram
-and mla_qknorm_key_rinv: the cache writer's share of the work).  With an
+mla_qknorm_query (the normalised, weighted content query in fp32), which
+mla_prepare_q absorbs against the bf16 U_K (hi + lo parts of the query on
+MFMA; other shapes use an fp32 copy of U_K), and each segment carries the
+inverse RMS of its rows' content keys, computed once here from the cache
+(mla_qknorm_key_gram and mla_qknorm_key_rinv: the cache writer's share of
+the work).  With an
 int8 cache (``quant="int8"``) each segment's bf16 rows are quantized here by
 mla_quantize_latent_i8 (again the cache writer's part) and the decode reads
 the packed rows and their scales.
@@ -108,7 +110,10 @@ class DecodeStep:
             self.g_q = g_q.to(device=dev, dtype=torch.float32).contiguous()
             self.g_k = g_k.to(device=dev, dtype=torch.float32).contiguous()
             self.qk_eps = float(eps)
-            self.w_uk_f32 = w_uk.to(torch.float32).contiguous()
+            # the MFMA prepare takes the fp32 query with the bf16 weights;
+            # elsewhere the absorption needs weights of the query's dtype
+            mfma_shape = w_uk.dtype == torch.bfloat16 and w_uk.shape[1] == 128 and d_c == 512
+            self.w_uk_q = w_uk if mfma_shape else w_uk.to(torch.float32).contiguous()
             self.q_norm = torch.empty(q_nope.shape, dtype=torch.float32, device=dev)
             self.gram = ops.qknorm_key_gram(w_uk)
             d_nope = w_uk.shape[1]
@@ -160,7 +165,12 @@ class DecodeStep:
     def absorb(self):
         if self.qk_norm:
             ops.qknorm_query(self.q_nope, self.g_q, self.g_k, self.qk_eps, out=self.q_norm)
-            ops.absorb_q(self.q_norm, self.w_uk_f32, out=self.q_lat)
+            if self.w_uk_q.dtype == torch.float32:
+                ops.absorb_q(self.q_norm, self.w_uk_q, out=self.q_lat)
+            else:  # fp32 query against bf16 weights: only the fused prepare path offers it
+                from . import _lib
+                _lib.call("mla_prepare_q", *ops.prepare_args(self.q_norm, self.q_pe, self.w_uk_q, self.q_lat, [],
+                                                              [], self.q_pos, self.rope_base, ops._stream()))
         else:
             ops.absorb_q(self.q_nope, self.w_uk, out=self.q_lat)
 
@@ -174,14 +184,23 @@ class DecodeStep:
     def expand(self):
         ops.out_uv(self.o_lat, self.w_uv, out=self.out)
 
+    def _fused_prepare(self) -> bool:
+        """rope (all shifts) and absorb in one mla_prepare_q launch?"""
+        return len(self.q_rots) <= 8 and (not self.qk_norm or self.w_uk_q.dtype == torch.bfloat16)
+
     def prepare(self):
-        """rope (all shifts) and absorb in one launch (mla_prepare_q)."""
-        if len(self.q_rots) > 8 or self.qk_norm:
+        """rope (all shifts) and absorb, in one launch (mla_prepare_q) where it
+        can; with QK-Norm the query normalisation runs first."""
+        if not self._fused_prepare():
             self.rope()
             self.absorb()
             return
         from . import _lib
-        _lib.call("mla_prepare_q", *ops.prepare_args(self.q_nope, self.q_pe, self.w_uk, self.q_lat,
+        q, w = self.q_nope, self.w_uk
+        if self.qk_norm:
+            ops.qknorm_query(self.q_nope, self.g_q, self.g_k, self.qk_eps, out=self.q_norm)
+            q, w = self.q_norm, self.w_uk_q
+        _lib.call("mla_prepare_q", *ops.prepare_args(q, self.q_pe, w, self.q_lat,
                                                       [r for _, r in self.q_rots], [s for s, _ in self.q_rots],
                                                       self.q_pos, self.rope_base, ops._stream()))
 
@@ -210,11 +229,18 @@ class DecodeStep:
         n_tok, H, d_nope = self.q_nope.shape
         d_c = self.w_uk.shape[2]
         d_r = self.q_pe.shape[2]
-        if len(self.q_rots) <= 8 and not self.qk_norm:  # one launch for rope (all shifts) and absorb
-            self._prep_args = ops.prepare_args(self.q_nope, self.q_pe, self.w_uk, self.q_lat,
+        if self._fused_prepare():  # one launch for rope (all shifts) and absorb
+            q, w = self.q_nope, self.w_uk
+            pre = []
+            if self.qk_norm:
+                pre.append((lib.mla_qknorm_query, (self.q_nope.data_ptr(), dt(self.q_nope), self.g_q.data_ptr(),
+                                                   self.g_k.data_ptr(), n_tok, H, d_nope, self.qk_eps,
+                                                   self.q_norm.data_ptr(), st)))
+                q, w = self.q_norm, self.w_uk_q
+            self._prep_args = ops.prepare_args(q, self.q_pe, w, self.q_lat,
                                                [r for _, r in self.q_rots], [s for s, _ in self.q_rots],
                                                self.q_pos, self.rope_base, st)
-            pre = [(lib.mla_prepare_q, self._prep_args)]
+            pre.append((lib.mla_prepare_q, self._prep_args))
         else:
             pre = [(lib.rope_relocate_q, (self.q_pe.data_ptr(), dt(self.q_pe), q_rot.data_ptr(), dt(q_rot),
                                           self.q_pos.data_ptr(), shift.data_ptr(), n_tok, H, d_r,
@@ -224,8 +250,13 @@ class DecodeStep:
                 pre.append((lib.mla_qknorm_query, (self.q_nope.data_ptr(), dt(self.q_nope), self.g_q.data_ptr(),
                                                    self.g_k.data_ptr(), n_tok, H, d_nope, self.qk_eps,
                                                    self.q_norm.data_ptr(), st)))
-                pre.append((lib.mla_absorb_q, (self.q_norm.data_ptr(), self.w_uk_f32.data_ptr(), dt(self.q_norm),
-                                               self.q_lat.data_ptr(), dt(self.q_lat), n_tok, H, d_nope, d_c, st)))
+                if self.w_uk_q.dtype == torch.float32:
+                    pre.append((lib.mla_absorb_q, (self.q_norm.data_ptr(), self.w_uk_q.data_ptr(), dt(self.q_norm),
+                                                   self.q_lat.data_ptr(), dt(self.q_lat), n_tok, H, d_nope, d_c, st)))
+                else:
+                    self._absorb_args = ops.prepare_args(self.q_norm, self.q_pe, self.w_uk_q, self.q_lat, [], [],
+                                                         self.q_pos, self.rope_base, st)
+                    pre.append((lib.mla_prepare_q, self._absorb_args))
             else:
                 pre.append((lib.mla_absorb_q, (self.q_nope.data_ptr(), self.w_uk.data_ptr(), dt(self.q_nope),
                                                self.q_lat.data_ptr(), dt(self.q_lat), n_tok, H, d_nope, d_c, st)))

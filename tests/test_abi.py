@@ -111,6 +111,14 @@ def test_null_and_shape_errors_before_any_gpu_call(lib):
     assert _st(lib, "mla_qknorm_key_rinv", P, 1, 10, 576, P, 512, 16, 128, float("nan"), P, None) == 2
     assert _st(lib, "mla_qknorm_key_rinv", P, 1, 10, 576, None, 512, 16, 128, 1e-6, P, None) == 1
     assert _st(lib, "mla_qknorm_key_rinv", P, 1, 0, 576, P, 512, 16, 128, 1e-6, P, None) == 0
+    # mla_prepare_q(q_nope, q_dtype, q_pe, w_uk, in_dtype, q_lat, lat_dtype, q_rots, shifts, n_shift, rot_dtype,
+    #               pos, n_tok, n_heads, d_nope, d_rope, d_c, base, stream): an fp32 query with bf16 weights
+    # needs the MFMA shape; a bf16 query with fp32 weights is not offered
+    assert _st(lib, "mla_prepare_q", P, 0, P, P, 1, P, 0, None, None, 0, 0, P, 1, 4, 64, 64, 512, 1e4, None) == 5
+    assert _st(lib, "mla_prepare_q", P, 1, P, P, 0, P, 0, None, None, 0, 0, P, 1, 4, 128, 64, 512, 1e4, None) == 5
+    assert _st(lib, "mla_prepare_q", P, 0, P, P + 8, 1, P, 0, None, None, 0, 0, P, 1, 4, 128, 64, 512, 1e4,
+               None) == 5
+    assert _st(lib, "mla_prepare_q", P, 4, P, P, 1, P, 0, None, None, 0, 0, P, 1, 4, 128, 64, 512, 1e4, None) == 3
     # mla_quantize_latent_i8(rows, row_dtype, n_rows, d_c, d_rope, out_rows, scales, stream)
     assert _st(lib, "mla_quantize_latent_i8", P, 1, 10, 512, 64, None, P, None) == 1
     assert _st(lib, "mla_quantize_latent_i8", P, 0, 10, 512, 64, P, P, None) == 3

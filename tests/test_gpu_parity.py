@@ -226,6 +226,30 @@ def test_prepare_call(dtype, dims):
         assert np.abs(f64(r) - ref_r).max() <= 1e-5
 
 
+def test_prepare_fp32_query_bf16_weights():
+    """mla_prepare_q with an fp32 query and bf16 U_K (the QK-Norm query): the
+    MFMA path multiplies bf16 hi + lo parts of the query, so q_lat matches
+    the fp64 absorption of the fp32 query to fp32 accumulation."""
+    from mla_latent_cache_amd import ops
+    H, d_nope, d_c, d_r, n_tok = 16, 128, 512, 64, 37
+    q = _rand((n_tok, H, d_nope), torch.float32, 31) * 3
+    q_pe = _rand((n_tok, H, d_r), torch.bfloat16, 32)
+    w = (_rand((H, d_nope, d_c), torch.float32, 33) / math.sqrt(d_c)).to(torch.bfloat16)
+    pos = torch.arange(n_tok, dtype=torch.int64) * 97
+    q_lat, q_rots = ops.prepare_q(q.cuda(), q_pe.cuda(), w.cuda(), pos.cuda(), [None], 10000.0,
+                                  lat_dtype=torch.float32, rot_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = O.absorb_query(f64(w), f64(q))
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    err = np.abs(f64(q_lat) - ref)
+    assert np.all(err <= 1e-5 * np.abs(ref) + 2e-5 * rms), float(np.max(err / rms))
+    # a bf16-rounded query would be off by ~2^-9 relative: the lo part is used
+    ref_hi = O.absorb_query(f64(w), f64(q.to(torch.bfloat16)))
+    assert np.max(np.abs(ref_hi - ref)) > 50 * np.max(err)
+    ref_r = O.rope_relocate(f64(q_pe), pos.numpy(), np.zeros(n_tok, np.int64), 10000.0)
+    assert np.abs(f64(q_rots[0]) - ref_r).max() <= 1e-5
+
+
 @pytest.mark.parametrize("out_dtype,n_rows", [(torch.float32, 37), (torch.bfloat16, 37), (torch.float32, 600),
                                               (torch.float32, 1100)])
 def test_combine_call(out_dtype, n_rows):
