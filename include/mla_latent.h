@@ -181,7 +181,8 @@ typedef struct {
  *          with QK-Norm.
  * o_part   [n_tok][n_heads][n_part][d_c] fp32    output
  * lse_part [n_tok][n_heads][n_part]      fp32    output
- * n_tok = batch * s_q.  n_wg = workgroups per segment (0 = one per compute unit).
+ * n_tok = batch * s_q.  n_wg = workgroups per segment (0 = one per compute unit,
+ * at most 65536).
  * bf16 and int8 paths: d_c = 512, d_rope = 64, page_size = 64, s_q * head_count <= 4096
  * (multi-token chunks: the rows form groups of 64, each streaming the rows).
  */
@@ -199,7 +200,8 @@ mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q
  * A row whose slots are all -inf gives o_lat = 0, lse = -inf.  o_part rows of
  * -inf slots are never read.
  *
- * o_part   [n_rows][n_part][d_c] fp32 (16-byte aligned, d_c a multiple of 4)
+ * o_part   [n_rows][n_part][d_c] fp32 (16-byte aligned, d_c a multiple of 4;
+ *          n_rows < 2^24)
  * lse_part [n_rows][n_part]      fp32 (n_part <= 1024)
  * o_lat    [n_rows][d_c]         out_dtype (MLA_BF16 or MLA_F32)
  * lse      [n_rows]              fp32, or NULL if not wanted
@@ -270,7 +272,7 @@ mla_status mla_out_uv(const void* o_lat, int o_dtype, const void* w_uv, int w_dt
  * lse      [n_tok][n_heads]              fp32, or NULL if not wanted
  * out      [n_tok][n_heads][d_v]         out_dtype
  * Shapes: d_c a multiple of 4, d_c <= 512; d_v <= 128; n_tok, n_heads <= 65535,
- * n_tok * n_heads <= 2^24.
+ * n_tok * n_heads <= 2^21.
  * Errors: MLA_ERR_NULL, MLA_ERR_DTYPE, MLA_ERR_SHAPE as for the two calls.
  */
 mla_status mla_combine_out_uv(const float* o_part, const float* lse_part, int n_tok, int n_heads, int n_part,
@@ -288,8 +290,8 @@ mla_status mla_combine_out_uv(const float* o_part, const float* lse_part, int n_
  *   out_rows[r] = [code_0 .. code_{d_c-1} (int8) | k^R (the d_rope bf16 entries, unchanged)]
  *   scales[r]   = scale
  * rows [n_rows][d_c + d_rope] bf16; out_rows [n_rows][d_c + 2 d_rope] bytes;
- * scales [n_rows] fp32.  d_c a multiple of 8, <= 512; d_rope a multiple of 4,
- * <= 128; rows and out_rows 8-byte aligned.
+ * scales [n_rows] fp32.  n_rows <= 2^32; d_c a multiple of 8, <= 512; d_rope a
+ * multiple of 4, <= 128; rows and out_rows 8-byte aligned.
  * Errors: MLA_ERR_NULL, MLA_ERR_DTYPE (rows not bf16), MLA_ERR_SHAPE, MLA_ERR_ALIGN.
  */
 mla_status mla_quantize_latent_i8(const void* rows, int row_dtype, int64_t n_rows, int d_c, int d_rope,

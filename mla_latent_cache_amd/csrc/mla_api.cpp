@@ -184,7 +184,7 @@ mla_status mla_combine_lse(const float* o_part, const float* lse_part, int n_row
                            void* o_lat, int out_dtype, float* lse, void* stream) {
   if (!o_part || !lse_part || !o_lat) return fail(MLA_ERR_NULL, "mla_combine_lse: null pointer");
   if (!dtype_ok(out_dtype)) return fail(MLA_ERR_DTYPE, "mla_combine_lse: out_dtype %d", out_dtype);
-  if (n_rows < 0 || n_part <= 0 || n_part > 1024 || d_c <= 0 || d_c > 4096 || (d_c & 3) ||
+  if (n_rows < 0 || n_rows >= (1 << 24) || n_part <= 0 || n_part > 1024 || d_c <= 0 || d_c > 4096 || (d_c & 3) ||
       ((reinterpret_cast<uintptr_t>(o_part) & 15u) != 0))
     return fail(MLA_ERR_SHAPE, "mla_combine_lse: n_rows=%d n_part=%d (<= 1024) d_c=%d (multiple of 4, "
                 "o_part 16-byte aligned)", n_rows, n_part, d_c);
@@ -200,10 +200,10 @@ mla_status mla_combine_out_uv(const float* o_part, const float* lse_part, int n_
   if (!o_part || !lse_part || !w_uv || !out) return fail(MLA_ERR_NULL, "mla_combine_out_uv: null pointer");
   if (!dtype_ok(w_dtype) || !dtype_ok(out_dtype))
     return fail(MLA_ERR_DTYPE, "mla_combine_out_uv: dtypes %d, %d", w_dtype, out_dtype);
-  if (n_tok < 0 || n_tok > 65535 || n_heads <= 0 || n_heads > 65535 || (int64_t)n_tok * n_heads > (1 << 24) ||
+  if (n_tok < 0 || n_tok > 65535 || n_heads <= 0 || n_heads > 65535 || (int64_t)n_tok * n_heads > (1 << 21) ||
       n_part <= 0 || n_part > 1024 || d_c <= 0 || d_c > 512 || (d_c & 3) || d_v <= 0 || d_v > 128 ||
       ((reinterpret_cast<uintptr_t>(o_part) & 15u) != 0))
-    return fail(MLA_ERR_SHAPE, "mla_combine_out_uv: n_tok=%d n_heads=%d (rows <= 2^24) n_part=%d (<= 1024) d_c=%d "
+    return fail(MLA_ERR_SHAPE, "mla_combine_out_uv: n_tok=%d n_heads=%d (rows <= 2^21) n_part=%d (<= 1024) d_c=%d "
                 "(multiple of 4, <= 512) d_v=%d (<= 128), o_part 16-byte aligned", n_tok, n_heads, n_part, d_c, d_v);
   if (n_tok == 0) return ok();
   return hip_status(mla::launch_combine_out_uv(o_part, lse_part, n_tok, n_heads, n_part, d_c, w_uv,
@@ -216,7 +216,7 @@ mla_status mla_quantize_latent_i8(const void* rows, int row_dtype, int64_t n_row
                                   void* out_rows, float* scales, void* stream) {
   if (!rows || !out_rows || !scales) return fail(MLA_ERR_NULL, "mla_quantize_latent_i8: null pointer");
   if (row_dtype != MLA_BF16) return fail(MLA_ERR_DTYPE, "mla_quantize_latent_i8: rows must be bf16 (got %d)", row_dtype);
-  if (n_rows < 0 || n_rows > ((int64_t)1 << 34) || d_c <= 0 || d_c > 512 || (d_c & 7) || d_rope < 0 ||
+  if (n_rows < 0 || n_rows > ((int64_t)1 << 32) || d_c <= 0 || d_c > 512 || (d_c & 7) || d_rope < 0 ||
       d_rope > 128 || (d_rope & 3))
     return fail(MLA_ERR_SHAPE, "mla_quantize_latent_i8: n_rows=%lld d_c=%d (multiple of 8, <= 512) d_rope=%d "
                 "(multiple of 4, <= 128)", (long long)n_rows, d_c, d_rope);
@@ -273,7 +273,7 @@ mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q
     return fail(MLA_ERR_DTYPE, "mla_decode_splitkv: dtypes %d, %d", q_dtype, cache_dtype);
   if (cache_dtype == MLA_F32 && q_dtype != MLA_F32)
     return fail(MLA_ERR_UNSUPPORTED, "mla_decode_splitkv: an fp32 cache needs an fp32 query");
-  if (n_segs <= 0 || n_segs > 64 || batch < 0 || s_q <= 0 || n_heads <= 0 || n_part <= 0 || n_wg < 0)
+  if (n_segs <= 0 || n_segs > 64 || batch < 0 || s_q <= 0 || n_heads <= 0 || n_part <= 0 || n_wg < 0 || n_wg > 65536)
     return fail(MLA_ERR_SHAPE, "mla_decode_splitkv: n_segs=%d batch=%d s_q=%d n_heads=%d n_part=%d n_wg=%d",
                 n_segs, batch, s_q, n_heads, n_part, n_wg);
   if (!std::isfinite(scale)) return fail(MLA_ERR_SHAPE, "mla_decode_splitkv: scale is not finite");

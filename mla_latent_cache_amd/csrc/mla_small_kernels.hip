@@ -5,6 +5,8 @@
 #include "mla_common.h"
 #include "mla_kernels.h"
 
+#include <algorithm>
+
 #include <math.h>
 
 namespace mla {
@@ -472,48 +474,52 @@ hipError_t launch_combine_out_uv(const float* o_part, const float* lse_part, int
 __global__ __launch_bounds__(256) void quantize_latent_i8_kernel(const bf16* __restrict__ rows, int64_t n_rows,
                                                                  int d_c, int d_rope, char* __restrict__ out,
                                                                  float* __restrict__ scales) {
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= n_rows) return;
   const int lane = threadIdx.x & 63;
-  const int in_w = d_c + d_rope;
-  const int out_w = d_c + 2 * d_rope;
-  const bf16* src = rows + r * in_w;
-  char* dst = out + r * out_w;
-  // lane owns latent entries [8 lane, 8 lane + 8) (d_c <= 512, a multiple of 8)
-  float v[8];
-  const bool mine = 8 * lane < d_c;
-  float amax = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    v[e] = mine ? (float)src[8 * lane + e] : 0.f;
-    amax = fmaxf(amax, fabsf(v[e]));
-  }
-  amax = wave_max(amax);
-  const float scale = amax / 127.f;
-  if (mine) {
-    unsigned lo = 0, hi = 0;
-#pragma unroll
+  for (int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); r < n_rows; r += (int64_t)gridDim.x * 4) {
+    const int in_w = d_c + d_rope;
+    const int out_w = d_c + 2 * d_rope;
+    const bf16* src = rows + r * in_w;
+    char* dst = out + r * out_w;
+    // lane owns latent entries [8 lane, 8 lane + 8) (d_c <= 512, a multiple of 8)
+    float v[8];
+    const bool mine = 8 * lane < d_c;
+    float amax = 0.f;
+  #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float q = scale > 0.f ? fminf(fmaxf(rintf(v[e] / scale), -127.f), 127.f) : 0.f;
-      const unsigned byte = (unsigned)((int)q & 0xff);
-      if (e < 4) lo |= byte << (8 * e);
-      else hi |= byte << (8 * (e - 4));
+      v[e] = mine ? (float)src[8 * lane + e] : 0.f;
+      amax = fmaxf(amax, fabsf(v[e]));
     }
-    *(uint2*)(dst + 8 * lane) = uint2{lo, hi};
-  }
-  // rotary entries: 2 d_rope bytes in 8-byte pieces
-  const unsigned short* rs = (const unsigned short*)(src + d_c);
-  if (lane < d_rope / 4) {
-    const unsigned short* p = rs + 4 * lane;
-    unsigned lo = (unsigned)p[0] | ((unsigned)p[1] << 16), hi = (unsigned)p[2] | ((unsigned)p[3] << 16);
-    *(uint2*)(dst + d_c + 8 * lane) = uint2{lo, hi};
-  }
-  if (lane == 0) scales[r] = scale;
+    amax = wave_max(amax);
+    const float scale = amax / 127.f;
+    if (mine) {
+      unsigned lo = 0, hi = 0;
+  #pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float q = scale > 0.f ? fminf(fmaxf(rintf(v[e] / scale), -127.f), 127.f) : 0.f;
+        const unsigned byte = (unsigned)((int)q & 0xff);
+        if (e < 4) lo |= byte << (8 * e);
+        else hi |= byte << (8 * (e - 4));
+      }
+      *(uint2*)(dst + 8 * lane) = uint2{lo, hi};
+    }
+    // rotary entries: 2 d_rope bytes in 8-byte pieces
+    const unsigned short* rs = (const unsigned short*)(src + d_c);
+    if (lane < d_rope / 4) {
+      const unsigned short* p = rs + 4 * lane;
+      unsigned lo = (unsigned)p[0] | ((unsigned)p[1] << 16), hi = (unsigned)p[2] | ((unsigned)p[3] << 16);
+      *(uint2*)(dst + d_c + 8 * lane) = uint2{lo, hi};
+    }
+    if (lane == 0) scales[r] = scale;
+  }  // rows (grid-stride: the grid is capped)
 }
+
+// Grid-stride kernels take at most this many workgroups (a launch's work-items
+// must fit 32 bits per dimension).
+constexpr int64_t kMaxStrideBlocks = 65536;
 
 hipError_t launch_quantize_latent_i8(const void* rows, int64_t n_rows, int d_c, int d_rope, void* out,
                                      float* scales, hipStream_t stream) {
-  const dim3 grid((unsigned)((n_rows + 3) / 4));
+  const dim3 grid((unsigned)std::min<int64_t>((n_rows + 3) / 4, kMaxStrideBlocks));
   return launch(quantize_latent_i8_kernel, grid, dim3(256), stream, (const bf16*)rows, n_rows, d_c, d_rope,
                 (char*)out, scales);
 }
@@ -571,38 +577,40 @@ __global__ __launch_bounds__(256) void qknorm_rinv_kernel(const TI* __restrict__
   constexpr int R = 16;  // rows per block
   __shared__ float cs[R][512];
   __shared__ float part[4][R];
-  const int64_t r0 = (int64_t)blockIdx.x * R;
-  for (int i = threadIdx.x; i < R * d_c; i += 256) {
-    const int rr = i / d_c, k = i % d_c;
-    cs[rr][k] = r0 + rr < n_rows ? load_f(rows + (r0 + rr) * row_width + k) : 0.f;
-  }
-  __syncthreads();
-  float q[R];
+  for (int64_t r0 = (int64_t)blockIdx.x * R; r0 < n_rows; r0 += (int64_t)gridDim.x * R) {  // grid-stride
+    __syncthreads();  // the previous rows' LDS reads are done
+    for (int i = threadIdx.x; i < R * d_c; i += 256) {
+      const int rr = i / d_c, k = i % d_c;
+      cs[rr][k] = r0 + rr < n_rows ? load_f(rows + (r0 + rr) * row_width + k) : 0.f;
+    }
+    __syncthreads();
+    float q[R];
 #pragma unroll
-  for (int rr = 0; rr < R; ++rr) q[rr] = 0.f;
-  for (int j = threadIdx.x; j < d_c; j += 256) {
-    float y[R];
+    for (int rr = 0; rr < R; ++rr) q[rr] = 0.f;
+    for (int j = threadIdx.x; j < d_c; j += 256) {
+      float y[R];
 #pragma unroll
-    for (int rr = 0; rr < R; ++rr) y[rr] = 0.f;
-    for (int k = 0; k < d_c; ++k) {
-      const float gkj = gram[(int64_t)k * d_c + j];  // = G[j][k]
+      for (int rr = 0; rr < R; ++rr) y[rr] = 0.f;
+      for (int k = 0; k < d_c; ++k) {
+        const float gkj = gram[(int64_t)k * d_c + j];  // = G[j][k]
 #pragma unroll
-      for (int rr = 0; rr < R; ++rr) y[rr] += gkj * cs[rr][k];
+        for (int rr = 0; rr < R; ++rr) y[rr] += gkj * cs[rr][k];
+      }
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) q[rr] += cs[rr][j] * y[rr];
     }
 #pragma unroll
-    for (int rr = 0; rr < R; ++rr) q[rr] += cs[rr][j] * y[rr];
-  }
-#pragma unroll
-  for (int rr = 0; rr < R; ++rr) {
-    const float v = wave_sum(q[rr]);
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6][rr] = v;
-  }
-  __syncthreads();
-  if (threadIdx.x < R && r0 + threadIdx.x < n_rows) {
-    const int rr = threadIdx.x;
-    const float tot = (part[0][rr] + part[1][rr]) + (part[2][rr] + part[3][rr]);
-    rinv[r0 + rr] = 1.f / sqrtf(tot / (float)n_hd + eps);
-  }
+    for (int rr = 0; rr < R; ++rr) {
+      const float v = wave_sum(q[rr]);
+      if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6][rr] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < R && r0 + threadIdx.x < n_rows) {
+      const int rr = threadIdx.x;
+      const float tot = (part[0][rr] + part[1][rr]) + (part[2][rr] + part[3][rr]);
+      rinv[r0 + rr] = 1.f / sqrtf(tot / (float)n_hd + eps);
+    }
+  }  // r0
 }
 
 hipError_t launch_qknorm_query(const void* q_nope, bool in_bf16, const float* g_q, const float* g_k, int n_tok,
@@ -626,7 +634,7 @@ hipError_t launch_qknorm_key_gram(const void* w_uk, bool w_bf16, int n_heads, in
 
 hipError_t launch_qknorm_key_rinv(const void* rows, bool row_bf16, int64_t n_rows, int row_width, const float* gram,
                                   int d_c, int n_hd, float eps, float* rinv, hipStream_t stream) {
-  const dim3 grid((unsigned)((n_rows + 15) / 16));
+  const dim3 grid((unsigned)std::min<int64_t>((n_rows + 15) / 16, kMaxStrideBlocks));
   if (row_bf16)
     return launch(qknorm_rinv_kernel<bf16>, grid, dim3(256), stream, (const bf16*)rows, n_rows, row_width, gram, d_c,
                   n_hd, eps, rinv);

@@ -95,6 +95,8 @@ def test_null_and_shape_errors_before_any_gpu_call(lib):
     assert _st(lib, "mla_combine_out_uv", P + 4, P, 1, 1, 4, 512, P, 1, 128, None, None, P, 1, None) == 2
     assert _st(lib, "mla_combine_out_uv", P, P, 0, 1, 4, 512, P, 1, 128, None, None, P, 1, None) == 0
     assert _st(lib, "mla_combine_out_uv", P, P, 65535, 65535, 4, 512, P, 1, 128, None, None, P, 1, None) == 2
+    assert _st(lib, "mla_combine_out_uv", P, P, 2048, 1025, 4, 512, P, 1, 128, None, None, P, 1, None) == 2
+    assert _st(lib, "mla_combine_lse", P, P, 1 << 24, 4, 512, P, 1, None, None) == 2
     # mla_qknorm_query(q_nope, in_dtype, g_q, g_k, n_tok, n_heads, d_nope, eps, q_out, stream)
     assert _st(lib, "mla_qknorm_query", P, 1, P, None, 1, 16, 128, 1e-6, P, None) == 1
     assert _st(lib, "mla_qknorm_query", P, 3, P, P, 1, 16, 128, 1e-6, P, None) == 3
@@ -127,6 +129,7 @@ def test_null_and_shape_errors_before_any_gpu_call(lib):
     assert _st(lib, "mla_quantize_latent_i8", P, 1, 10, 512, 66, P, P, None) == 2
     assert _st(lib, "mla_quantize_latent_i8", P + 4, 1, 10, 512, 64, P, P, None) == 4
     assert _st(lib, "mla_quantize_latent_i8", P, 1, 0, 512, 64, P, P, None) == 0
+    assert _st(lib, "mla_quantize_latent_i8", P, 1, (1 << 32) + 1, 512, 64, P, P, None) == 2
     # zero-size calls succeed without launching anything
     assert _st(lib, "mla_absorb_q", P, P, 1, P, 0, 0, 1, 128, 512, None) == 0
 
