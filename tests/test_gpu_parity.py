@@ -386,7 +386,7 @@ def test_full_size_sampled(name):
 
 
 # ------------------------------------------------------------ graph capture
-@pytest.mark.parametrize("name", ["dsv3", "merge"])
+@pytest.mark.parametrize("name", ["dsv3", "merge", "qknorm", "int8", "small"])
 def test_graph_replay_matches_eager(name):
     """The five calls enqueue only kernels on the caller's stream, so a step
     can be captured into a HIP graph; every replay must equal the eager run."""
