@@ -2,7 +2,7 @@
 
 Compiles every source under ``csrc/`` for gfx950 with hipcc (each source to
 an object in ``_build/``, in parallel, then one shared-library link).  It
-needs no GPU, so it runs in the build container as well as on the GPU machine.
+needs no GPU: hipcc cross-compiles for gfx950 on any machine with ROCm.
 """
 from __future__ import annotations
 
