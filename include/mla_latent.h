@@ -237,6 +237,33 @@ mla_status mla_prepare_q(const void* q_nope, int q_dtype, const void* q_pe, cons
                          double base, void* stream);
 
 /*
+ * mla_prepare_q_qknorm -- mla_qknorm_query folded into mla_prepare_q's one
+ * launch (QK-Norm MLA page, abstract: RMSNorm of the content query after its
+ * projection; the static key weight moved into the query).  Result, layouts
+ * and rotary outputs as mla_qknorm_query followed by mla_prepare_q with
+ * q_dtype MLA_F32:
+ *
+ *   q_lat     = U_K^T (g_q g_k q_nope / rms_t),   rms_t = sqrt(mean_{h,i} q_nope[t][h][i]^2 + eps)
+ *   q_rots[k] = rope_relocate_q(q_pe, pos, shifts[k])
+ *
+ * Every absorption workgroup sums the squares of all heads of its tokens
+ * itself, so the call is meant for decode batches: n_tok * n_heads <= 512.
+ * q_nope [n_tok][n_heads][128] q_dtype (MLA_BF16 or MLA_F32, 16-byte
+ * aligned); g_q, g_k [n_heads][128] fp32; w_uk [n_heads][128][512] bf16
+ * (16-byte aligned), in_dtype MLA_BF16 (also the dtype of q_pe); eps >= 0.
+ * The fp32 product enters the MFMA as bf16 hi + lo parts with fp32
+ * accumulation.  Other arguments as mla_prepare_q.
+ * Errors: MLA_ERR_NULL, MLA_ERR_DTYPE, MLA_ERR_SHAPE, MLA_ERR_UNSUPPORTED
+ * (other dims, dtypes or alignment, or n_tok * n_heads > 512: use
+ * mla_qknorm_query, then mla_prepare_q).
+ */
+mla_status mla_prepare_q_qknorm(const void* q_nope, int q_dtype, const float* g_q, const float* g_k, float eps,
+                                const void* q_pe, const void* w_uk, int in_dtype, void* q_lat, int lat_dtype,
+                                void* const* q_rots, const int64_t* const* shifts, int n_shift, int rot_dtype,
+                                const int64_t* pos, int n_tok, int n_heads, int d_nope, int d_rope, int d_c,
+                                double base, void* stream);
+
+/*
  * mla_out_uv -- expand the mixed latent once per query.
  * [T] "Move the Value Expansion After the Weighted Sum": U_V (sum_t a_t c_t)
  * equals sum_t a_t (U_V c_t), so the value up-projection follows the sum.

@@ -58,6 +58,9 @@ SIGNATURES = {
     "mla_prepare_q": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_int, c_void_p, c_int, POINTER(c_void_p),
                               POINTER(c_void_p), c_int, c_int, c_void_p, c_int, c_int, c_int, c_int, c_int,
                               c_double, c_void_p]),
+    "mla_prepare_q_qknorm": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_float, c_void_p, c_void_p, c_int,
+                                     c_void_p, c_int, POINTER(c_void_p), POINTER(c_void_p), c_int, c_int, c_void_p,
+                                     c_int, c_int, c_int, c_int, c_int, c_double, c_void_p]),
     "mla_quantize_latent_i8": (c_int, [c_void_p, c_int, c_int64, c_int, c_int, c_void_p, c_void_p, c_void_p]),
     "mla_qknorm_query": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_int, c_int, c_int, c_double, c_void_p,
                                  c_void_p]),

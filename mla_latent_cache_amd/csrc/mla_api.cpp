@@ -151,7 +151,8 @@ mla_status mla_prepare_q(const void* q_nope, int q_dtype, const void* q_pe, cons
       rt.shift[k] = shifts ? shifts[k] : nullptr;
     }
     return hip_status(mla::launch_prepare_mfma(q_nope, q_dtype == MLA_F32, w_uk, q_lat, lat_dtype == MLA_BF16, q_pe,
-                                               pos, rt, rot_dtype == MLA_BF16, n_tok, n_heads, d_rope, base, st),
+                                               pos, rt, rot_dtype == MLA_BF16, n_tok, n_heads, d_rope, base,
+                                               mla::QkArgs{}, st),
                       "mla_prepare_q launch");
   }
   // other shapes and dtypes: the two kernels one after the other
@@ -165,6 +166,47 @@ mla_status mla_prepare_q(const void* q_nope, int q_dtype, const void* q_pe, cons
   return hip_status(mla::launch_absorb(q_nope, w_uk, in_dtype == MLA_BF16, q_lat, lat_dtype == MLA_BF16, n_tok,
                                        n_heads, d_nope, d_c, st),
                     "mla_prepare_q absorb launch");
+}
+
+mla_status mla_prepare_q_qknorm(const void* q_nope, int q_dtype, const float* g_q, const float* g_k, float eps,
+                                const void* q_pe, const void* w_uk, int in_dtype, void* q_lat, int lat_dtype,
+                                void* const* q_rots, const int64_t* const* shifts, int n_shift, int rot_dtype,
+                                const int64_t* pos, int n_tok, int n_heads, int d_nope, int d_rope, int d_c,
+                                double base, void* stream) {
+  if (!q_nope || !g_q || !g_k || !q_pe || !w_uk || !q_lat || !pos || (n_shift > 0 && !q_rots))
+    return fail(MLA_ERR_NULL, "mla_prepare_q_qknorm: null pointer");
+  if (!dtype_ok(q_dtype) || !dtype_ok(in_dtype) || !dtype_ok(lat_dtype) || !dtype_ok(rot_dtype))
+    return fail(MLA_ERR_DTYPE, "mla_prepare_q_qknorm: dtypes %d, %d, %d, %d", q_dtype, in_dtype, lat_dtype,
+                rot_dtype);
+  if (n_shift < 0 || n_shift > mla::kMaxShift)
+    return fail(MLA_ERR_SHAPE, "mla_prepare_q_qknorm: n_shift=%d (0..%d)", n_shift, mla::kMaxShift);
+  for (int k = 0; k < n_shift; ++k)
+    if (!q_rots[k]) return fail(MLA_ERR_NULL, "mla_prepare_q_qknorm: q_rots[%d] is NULL", k);
+  if (n_tok < 0 || n_heads <= 0 || n_heads > 65535 || d_rope < 2 || d_rope > 128 || (d_rope & 1))
+    return fail(MLA_ERR_SHAPE, "mla_prepare_q_qknorm: n_tok=%d n_heads=%d d_rope=%d", n_tok, n_heads, d_rope);
+  if (!(base > 1.0) || !std::isfinite(base)) return fail(MLA_ERR_SHAPE, "mla_prepare_q_qknorm: base=%g", base);
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(MLA_ERR_SHAPE, "mla_prepare_q_qknorm: eps=%g", (double)eps);
+  if (in_dtype != MLA_BF16 || !mla::absorb_mfma_ok(q_nope, w_uk, d_nope, d_c))
+    return fail(MLA_ERR_UNSUPPORTED, "mla_prepare_q_qknorm: needs bf16 w_uk and q_pe, d_nope=128, d_c=512 and "
+                "16-byte aligned q_nope and w_uk");
+  if ((int64_t)n_tok * n_heads > mla::kQkFusedRows)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_prepare_q_qknorm: n_tok * n_heads = %lld (at most %d; use "
+                "mla_qknorm_query, then mla_prepare_q)", (long long)n_tok * n_heads, mla::kQkFusedRows);
+  if (n_tok == 0) return ok();
+  mla::RopeTargets rt{};
+  rt.n = n_shift;
+  for (int k = 0; k < n_shift; ++k) {
+    rt.q_rot[k] = q_rots[k];
+    rt.shift[k] = shifts ? shifts[k] : nullptr;
+  }
+  mla::QkArgs qk;
+  qk.g_q = g_q;
+  qk.g_k = g_k;
+  qk.eps = eps;
+  return hip_status(mla::launch_prepare_mfma(q_nope, q_dtype == MLA_F32, w_uk, q_lat, lat_dtype == MLA_BF16, q_pe,
+                                             pos, rt, rot_dtype == MLA_BF16, n_tok, n_heads, d_rope, base, qk,
+                                             (hipStream_t)stream),
+                    "mla_prepare_q_qknorm launch");
 }
 
 mla_status mla_out_uv(const void* o_lat, int o_dtype, const void* w_uv, int w_dtype, void* out, int out_dtype,

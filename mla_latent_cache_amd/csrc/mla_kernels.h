@@ -58,9 +58,19 @@ struct RopeTargets {
   const int64_t* shift[kMaxShift];
   int n;
 };
+// QK-Norm of the query inside the absorption (g_q == nullptr: none).  Every
+// absorption workgroup reads all heads of its tokens for their RMS, so the
+// fused form is bounded to n_tok * n_heads <= kQkFusedRows.
+constexpr int kQkFusedRows = 512;
+// QK-Norm of the query inside the absorption (g_q == nullptr: none).
+struct QkArgs {
+  const float* g_q = nullptr;  // [n_heads][d_nope]
+  const float* g_k = nullptr;  // [n_heads][d_nope]
+  float eps = 0.f;
+};
 hipError_t launch_prepare_mfma(const void* q_nope, bool q_f32, const void* w_uk, void* q_lat, bool lat_bf16,
                                const void* q_pe, const int64_t* pos, const RopeTargets& rt, bool rot_bf16, int n_tok,
-                               int n_heads, int d_rope, double base, hipStream_t stream);
+                               int n_heads, int d_rope, double base, const QkArgs& qk, hipStream_t stream);
 hipError_t launch_absorb_mfma(const void* q_nope, const void* w_uk, void* q_lat, bool out_bf16, int n_tok,
                               int n_heads, hipStream_t stream);
 bool out_uv_mfma_ok(const void* o_lat, const void* w_uv, int d_c, int d_v);

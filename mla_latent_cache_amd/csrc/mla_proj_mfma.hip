@@ -27,10 +27,17 @@ constexpr int kAbsLds = kAbsCols * 2 + 16;  // bytes per LDS weight row (padded)
 // Workgroup (head h, output columns j0 .. j0 + 127) of the absorption.  An
 // fp32 query (TQ = float) enters as bf16 hi + lo parts (q = hi + lo to about
 // 2^-17), each multiplied by the bf16 weights with fp32 accumulation.
-template <typename TO, typename TQ = bf16>
+// QKN (QK-Norm MLA page, abstract): the content query is RMS-normalised over
+// all heads of its token and weighted by g_q g_k first (the static key weight
+// moved into the query); the workgroup derives each token's inverse RMS
+// itself, from all n_heads * 128 entries of the token, so this suits few
+// tokens; the product again enters as hi + lo parts.
+template <typename TO, typename TQ = bf16, bool QKN = false>
 __device__ __forceinline__ void absorb_block(const TQ* __restrict__ q_nope, const bf16* __restrict__ w_uk,
-                                             TO* __restrict__ q_lat, int n_tok, int n_heads, int h, int j0) {
-  constexpr bool QF = sizeof(TQ) == 4;
+                                             TO* __restrict__ q_lat, int n_tok, int n_heads, int h, int j0,
+                                             const QkArgs& qk = QkArgs{}) {
+  constexpr bool QF = sizeof(TQ) == 4 || QKN;  // hi + lo parts
+  __shared__ float inv_s[16];
   __shared__ __attribute__((aligned(16))) char wl[kNope * kAbsLds];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, lg = lane >> 4;
@@ -46,26 +53,85 @@ __device__ __forceinline__ void absorb_block(const TQ* __restrict__ q_nope, cons
     // A operand: 16 tokens x 128 i, lane row l16, k = 32 ks + 8 lg + (0..7)
     bf16x8 qa[4], ql[QF ? 4 : 1];
     const int t = t0 + l16;
+    if constexpr (QF) {
+      f32x4 va[4][2];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if constexpr (QF) {
-        f32x4 v0 = f32x4{0.f, 0.f, 0.f, 0.f}, v1 = v0;
+      for (int ks = 0; ks < 4; ++ks) {
+        va[ks][0] = va[ks][1] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (t < n_tok) {
-          const float* src = (const float*)q_nope + ((int64_t)t * n_heads + h) * kNope + 32 * ks + 8 * lg;
-          v0 = *(const f32x4*)src;
-          v1 = *(const f32x4*)(src + 4);
+          const int64_t off = ((int64_t)t * n_heads + h) * kNope + 32 * ks + 8 * lg;
+          if constexpr (sizeof(TQ) == 4) {
+            va[ks][0] = *(const f32x4*)((const float*)q_nope + off);
+            va[ks][1] = *(const f32x4*)((const float*)q_nope + off + 4);
+          } else {
+            const bf16x8 a = *(const bf16x8*)(q_nope + off);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              va[ks][0][e] = (float)a[e];
+              va[ks][1][e] = (float)a[4 + e];
+            }
+          }
         }
+      }
+      if constexpr (QKN) {
+        // inverse RMS of the block's tokens over all heads: wave w sums the
+        // squares of tokens w, w + 4, w + 8, w + 12 with all 64 lanes, 8
+        // entries per lane and load, the loads of a token issued together
+        const int n_hd = n_heads * kNope;
+        float ss[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int tt = t0 + wave + 4 * j;
+          float acc = 0.f;
+          if (tt < n_tok) {
+            const TQ* qt = q_nope + (int64_t)tt * n_hd;
+#pragma unroll 4
+            for (int i = 8 * lane; i < n_hd; i += 512) {
+              if constexpr (sizeof(TQ) == 4) {
+                const f32x4 a = *(const f32x4*)(qt + i), b = *(const f32x4*)(qt + i + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc += a[e] * a[e] + b[e] * b[e];
+              } else {
+                const bf16x8 a = *(const bf16x8*)(qt + i);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)a[e];
+              }
+            }
+          }
+          ss[j] = wave_sum(acc);
+        }
+        __syncthreads();  // the previous token block's factors are read
+        if (lane == 0) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) inv_s[wave + 4 * j] = 1.f / sqrtf(ss[j] / (float)n_hd + qk.eps);
+        }
+        __syncthreads();
+        const float inv = inv_s[l16];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int gi = h * kNope + 32 * ks + 8 * lg;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            va[ks][0][e] = qk.g_q[gi + e] * qk.g_k[gi + e] * va[ks][0][e] * inv;
+            va[ks][1][e] = qk.g_q[gi + 4 + e] * qk.g_k[gi + 4 + e] * va[ks][1][e] * inv;
+          }
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float v = e < 4 ? v0[e] : v1[e - 4];
+          const float v = e < 4 ? va[ks][0][e] : va[ks][1][e - 4];
           const bf16 hi = (bf16)v;
           qa[ks][e] = hi;
           ql[ks][e] = (bf16)(v - (float)hi);
         }
-      } else {
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
         qa[ks] = t < n_tok ? *(const bf16x8*)(q_nope + ((int64_t)t * n_heads + h) * kNope + 32 * ks + 8 * lg)
                            : bf16x8{};
-      }
     }
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
@@ -101,15 +167,16 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const bf16* __restrict
 // rope_relocate_q for up to kMaxShift shifts and the absorption in one launch:
 // grid (heads, 4 + R); y < 4 are the absorption workgroups, y = 4 .. 4+R-1
 // rotate the head's rotary query pairs (all tokens and shifts) between them.
-template <typename TL, typename TR, typename TQ>
+template <typename TL, typename TR, typename TQ, bool QKN>
 __global__ __launch_bounds__(256) void prepare_mfma_kernel(const TQ* __restrict__ q_nope,
                                                            const bf16* __restrict__ w_uk, TL* __restrict__ q_lat,
                                                            const bf16* __restrict__ q_pe,
                                                            const int64_t* __restrict__ pos, RopeTargets rt,
-                                                           int n_tok, int n_heads, int d_rope, double base) {
+                                                           int n_tok, int n_heads, int d_rope, double base,
+                                                           QkArgs qk) {
   const int h = blockIdx.x;
   if (blockIdx.y < kLat / kAbsCols) {
-    absorb_block(q_nope, w_uk, q_lat, n_tok, n_heads, h, blockIdx.y * kAbsCols);
+    absorb_block<TL, TQ, QKN>(q_nope, w_uk, q_lat, n_tok, n_heads, h, blockIdx.y * kAbsCols, qk);
     return;
   }
   const int half = d_rope / 2;
@@ -179,36 +246,44 @@ bool absorb_mfma_ok(const void* q_nope, const void* w_uk, int d_nope, int d_c) {
 template <typename TL, typename TR, typename TQ>
 static hipError_t prepare_launch(const void* q_nope, const void* w_uk, void* q_lat, const void* q_pe,
                                  const int64_t* pos, const RopeTargets& rt, int n_tok, int n_heads, int d_rope,
-                                 double base, hipStream_t stream) {
+                                 double base, const QkArgs& qk, hipStream_t stream) {
   // rotation workgroups per head: one per 256 pairs (all tokens and shifts), at most 64
   const int pairs = rt.n * n_tok * (d_rope / 2);
   const int n_r = std::max(1, std::min(64, (pairs + 255) / 256));
-  return launch(prepare_mfma_kernel<TL, TR, TQ>, dim3(n_heads, kLat / kAbsCols + n_r), dim3(256), stream,
-                (const TQ*)q_nope, (const bf16*)w_uk, (TL*)q_lat, (const bf16*)q_pe, pos, rt, n_tok, n_heads,
-                d_rope, base);
+  const dim3 grid(n_heads, kLat / kAbsCols + n_r);
+  if (qk.g_q)
+    return launch(prepare_mfma_kernel<TL, TR, TQ, true>, grid, dim3(256), stream, (const TQ*)q_nope,
+                  (const bf16*)w_uk, (TL*)q_lat, (const bf16*)q_pe, pos, rt, n_tok, n_heads, d_rope, base, qk);
+  return launch(prepare_mfma_kernel<TL, TR, TQ, false>, grid, dim3(256), stream, (const TQ*)q_nope,
+                (const bf16*)w_uk, (TL*)q_lat, (const bf16*)q_pe, pos, rt, n_tok, n_heads, d_rope, base, qk);
 }
 
 template <typename TQ>
 static hipError_t prepare_dispatch(const void* q_nope, const void* w_uk, void* q_lat, bool lat_bf16,
                                    const void* q_pe, const int64_t* pos, const RopeTargets& rt, bool rot_bf16,
-                                   int n_tok, int n_heads, int d_rope, double base, hipStream_t stream) {
+                                   int n_tok, int n_heads, int d_rope, double base, const QkArgs& qk,
+                                   hipStream_t stream) {
   if (lat_bf16 && rot_bf16)
-    return prepare_launch<bf16, bf16, TQ>(q_nope, w_uk, q_lat, q_pe, pos, rt, n_tok, n_heads, d_rope, base, stream);
+    return prepare_launch<bf16, bf16, TQ>(q_nope, w_uk, q_lat, q_pe, pos, rt, n_tok, n_heads, d_rope, base, qk,
+                                          stream);
   if (lat_bf16)
-    return prepare_launch<bf16, float, TQ>(q_nope, w_uk, q_lat, q_pe, pos, rt, n_tok, n_heads, d_rope, base, stream);
+    return prepare_launch<bf16, float, TQ>(q_nope, w_uk, q_lat, q_pe, pos, rt, n_tok, n_heads, d_rope, base, qk,
+                                           stream);
   if (rot_bf16)
-    return prepare_launch<float, bf16, TQ>(q_nope, w_uk, q_lat, q_pe, pos, rt, n_tok, n_heads, d_rope, base, stream);
-  return prepare_launch<float, float, TQ>(q_nope, w_uk, q_lat, q_pe, pos, rt, n_tok, n_heads, d_rope, base, stream);
+    return prepare_launch<float, bf16, TQ>(q_nope, w_uk, q_lat, q_pe, pos, rt, n_tok, n_heads, d_rope, base, qk,
+                                           stream);
+  return prepare_launch<float, float, TQ>(q_nope, w_uk, q_lat, q_pe, pos, rt, n_tok, n_heads, d_rope, base, qk,
+                                          stream);
 }
 
 hipError_t launch_prepare_mfma(const void* q_nope, bool q_f32, const void* w_uk, void* q_lat, bool lat_bf16,
                                const void* q_pe, const int64_t* pos, const RopeTargets& rt, bool rot_bf16, int n_tok,
-                               int n_heads, int d_rope, double base, hipStream_t stream) {
+                               int n_heads, int d_rope, double base, const QkArgs& qk, hipStream_t stream) {
   if (q_f32)
     return prepare_dispatch<float>(q_nope, w_uk, q_lat, lat_bf16, q_pe, pos, rt, rot_bf16, n_tok, n_heads, d_rope,
-                                   base, stream);
+                                   base, qk, stream);
   return prepare_dispatch<bf16>(q_nope, w_uk, q_lat, lat_bf16, q_pe, pos, rt, rot_bf16, n_tok, n_heads, d_rope, base,
-                                stream);
+                                qk, stream);
 }
 
 hipError_t launch_absorb_mfma(const void* q_nope, const void* w_uk, void* q_lat, bool out_bf16, int n_tok,

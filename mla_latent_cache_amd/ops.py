@@ -82,6 +82,33 @@ def prepare_args(q_nope: torch.Tensor, q_pe: torch.Tensor, w_uk: torch.Tensor, q
             rot_dt, _ptr(pos), n_tok, n_heads, d_nope, d_rope, d_c, float(base), stream)
 
 
+def prepare_qknorm_args(q_nope: torch.Tensor, g_q: torch.Tensor, g_k: torch.Tensor, eps: float,
+                        q_pe: torch.Tensor, w_uk: torch.Tensor, q_lat: torch.Tensor,
+                        q_rots: Sequence[torch.Tensor], shifts: Sequence[Optional[torch.Tensor]], pos: torch.Tensor,
+                        base: float, stream: int):
+    """Argument tuple of mla_prepare_q_qknorm (its pointer arrays must stay
+    alive while the tuple is used)."""
+    a = prepare_args(q_nope, q_pe, w_uk, q_lat, q_rots, shifts, pos, base, stream)
+    for g in (g_q, g_k):
+        if g.dtype != torch.float32 or not g.is_contiguous() or g.shape != q_nope.shape[1:]:
+            raise ValueError("g_q, g_k must be contiguous fp32 [n_heads, d_nope]")
+    return a[:2] + (g_q.data_ptr(), g_k.data_ptr(), float(eps)) + a[2:]
+
+
+def prepare_q_qknorm(q_nope: torch.Tensor, g_q: torch.Tensor, g_k: torch.Tensor, eps: float, q_pe: torch.Tensor,
+                     w_uk: torch.Tensor, pos: torch.Tensor, shifts: Sequence[Optional[torch.Tensor]],
+                     base: float = 10000.0, lat_dtype: Optional[torch.dtype] = None,
+                     rot_dtype: Optional[torch.dtype] = None):
+    """mla_prepare_q_qknorm: the QK-Norm query absorbed, and the rotary query
+    per shift, in one launch."""
+    n_tok, n_heads, _ = q_nope.shape
+    q_lat = torch.empty((n_tok, n_heads, w_uk.shape[2]), dtype=lat_dtype or torch.float32, device=q_nope.device)
+    q_rots = [torch.empty_like(q_pe, dtype=rot_dtype or q_pe.dtype) for _ in shifts]
+    _lib.call("mla_prepare_q_qknorm", *prepare_qknorm_args(q_nope, g_q, g_k, eps, q_pe, w_uk, q_lat, q_rots, shifts,
+                                                           pos, base, _stream()))
+    return q_lat, q_rots
+
+
 def prepare_q(q_nope: torch.Tensor, q_pe: torch.Tensor, w_uk: torch.Tensor, pos: torch.Tensor,
               shifts: Sequence[Optional[torch.Tensor]], base: float = 10000.0,
               lat_dtype: Optional[torch.dtype] = None, rot_dtype: Optional[torch.dtype] = None):

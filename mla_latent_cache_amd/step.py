@@ -5,23 +5,23 @@
     rope_relocate_q (once per distinct segment shift) -> mla_absorb_q
     -> mla_decode_splitkv (all segments) -> mla_combine_lse -> mla_out_uv
 
-(the first two as one mla_prepare_q launch for up to 8 distinct shifts).
-
-With QK-Norm (``qk_norm=(g_q, g_k, eps)``) the chain starts with
-mla_qknorm_query (the normalised, weighted content query in fp32), which
-mla_prepare_q absorbs against the bf16 U_K (hi + lo parts of the query on
-MFMA; other shapes use an fp32 copy of U_K), and each segment carries the
-inverse RMS of its rows' content keys, computed once here from the cache
-(mla_qknorm_key_gram and mla_qknorm_key_rinv: the cache writer's share of
-the work).  With an
-int8 cache (``quant="int8"``) each segment's bf16 rows are quantized here by
-mla_quantize_latent_i8 (again the cache writer's part) and the decode reads
-the packed rows and their scales.
-
+(the first two as one mla_prepare_q launch for up to 8 distinct shifts),
 and lays out the partial-state slots: segments with disjoint head ranges that
 follow each other share a slot range (e.g. a document read by the Local heads
 at a relocated position and its recomputed copy read by the Global heads),
 later ranges stack after it, so each head's slots tile [0, n_part).
+
+With QK-Norm (``qk_norm=(g_q, g_k, eps)``) the content query is normalised
+and weighted first.  For few query rows (n_tok * n_heads <= 512, the MFMA
+shape) that happens inside the same launch (mla_prepare_q_qknorm); otherwise
+mla_qknorm_query writes the query in fp32 and mla_prepare_q absorbs it
+against the bf16 U_K (hi + lo parts of the query on MFMA; other shapes use
+an fp32 copy of U_K).  Each segment carries the inverse RMS of its rows'
+content keys, computed once here from the cache (mla_qknorm_key_gram and
+mla_qknorm_key_rinv: the cache writer's share of the work).  With an int8
+cache (``quant="int8"``) each segment's bf16 rows are quantized here by
+mla_quantize_latent_i8 (again the cache writer's part) and the decode reads
+the packed rows and their scales.
 """
 from __future__ import annotations
 
@@ -31,6 +31,10 @@ from typing import List, Optional, Sequence
 import torch
 
 from . import ops
+
+# query rows (tokens x heads) up to which the QK-Norm query normalisation runs
+# inside the prepare launch
+QK_FUSED_ROWS = 512
 
 
 @dataclass
@@ -188,6 +192,21 @@ class DecodeStep:
         """rope (all shifts) and absorb in one mla_prepare_q launch?"""
         return len(self.q_rots) <= 8 and (not self.qk_norm or self.w_uk_q.dtype == torch.bfloat16)
 
+    def _qk_fused(self) -> bool:
+        """QK-Norm of the query inside that launch too (mla_prepare_q_qknorm:
+        few query rows, the MFMA shape)?"""
+        n_tok, H, _ = self.q_nope.shape
+        return (self.qk_norm and self._fused_prepare() and n_tok * H <= QK_FUSED_ROWS
+                and self.q_nope.data_ptr() % 16 == 0 and self.w_uk_q.data_ptr() % 16 == 0)
+
+    def _prepare_args(self, stream: int):
+        rots, shifts = [r for _, r in self.q_rots], [s for s, _ in self.q_rots]
+        if self._qk_fused():
+            return ops.prepare_qknorm_args(self.q_nope, self.g_q, self.g_k, self.qk_eps, self.q_pe, self.w_uk_q,
+                                           self.q_lat, rots, shifts, self.q_pos, self.rope_base, stream)
+        q, w = (self.q_norm, self.w_uk_q) if self.qk_norm else (self.q_nope, self.w_uk)
+        return ops.prepare_args(q, self.q_pe, w, self.q_lat, rots, shifts, self.q_pos, self.rope_base, stream)
+
     def prepare(self):
         """rope (all shifts) and absorb, in one launch (mla_prepare_q) where it
         can; with QK-Norm the query normalisation runs first."""
@@ -196,13 +215,12 @@ class DecodeStep:
             self.absorb()
             return
         from . import _lib
-        q, w = self.q_nope, self.w_uk
+        if self._qk_fused():
+            _lib.call("mla_prepare_q_qknorm", *self._prepare_args(ops._stream()))
+            return
         if self.qk_norm:
             ops.qknorm_query(self.q_nope, self.g_q, self.g_k, self.qk_eps, out=self.q_norm)
-            q, w = self.q_norm, self.w_uk_q
-        _lib.call("mla_prepare_q", *ops.prepare_args(q, self.q_pe, w, self.q_lat,
-                                                      [r for _, r in self.q_rots], [s for s, _ in self.q_rots],
-                                                      self.q_pos, self.rope_base, ops._stream()))
+        _lib.call("mla_prepare_q", *self._prepare_args(ops._stream()))
 
     def combine_expand(self):
         ops.combine_out_uv(self.o_part, self.lse_part, self.w_uv, self.out.dtype, out=self.out, o_lat=self.o_lat,
@@ -229,17 +247,16 @@ class DecodeStep:
         n_tok, H, d_nope = self.q_nope.shape
         d_c = self.w_uk.shape[2]
         d_r = self.q_pe.shape[2]
-        if self._fused_prepare():  # one launch for rope (all shifts) and absorb
-            q, w = self.q_nope, self.w_uk
+        if self._qk_fused():  # QK-Norm, rope (all shifts) and absorb in one launch
+            self._prep_args = self._prepare_args(st)
+            pre = [(lib.mla_prepare_q_qknorm, self._prep_args)]
+        elif self._fused_prepare():  # one launch for rope (all shifts) and absorb
             pre = []
             if self.qk_norm:
                 pre.append((lib.mla_qknorm_query, (self.q_nope.data_ptr(), dt(self.q_nope), self.g_q.data_ptr(),
                                                    self.g_k.data_ptr(), n_tok, H, d_nope, self.qk_eps,
                                                    self.q_norm.data_ptr(), st)))
-                q, w = self.q_norm, self.w_uk_q
-            self._prep_args = ops.prepare_args(q, self.q_pe, w, self.q_lat,
-                                               [r for _, r in self.q_rots], [s for s, _ in self.q_rots],
-                                               self.q_pos, self.rope_base, st)
+            self._prep_args = self._prepare_args(st)
             pre.append((lib.mla_prepare_q, self._prep_args))
         else:
             pre = [(lib.rope_relocate_q, (self.q_pe.data_ptr(), dt(self.q_pe), q_rot.data_ptr(), dt(q_rot),

@@ -121,6 +121,21 @@ def test_null_and_shape_errors_before_any_gpu_call(lib):
     assert _st(lib, "mla_prepare_q", P, 0, P, P + 8, 1, P, 0, None, None, 0, 0, P, 1, 4, 128, 64, 512, 1e4,
                None) == 5
     assert _st(lib, "mla_prepare_q", P, 4, P, P, 1, P, 0, None, None, 0, 0, P, 1, 4, 128, 64, 512, 1e4, None) == 3
+    # mla_prepare_q_qknorm(q_nope, q_dtype, g_q, g_k, eps, q_pe, w_uk, in_dtype, q_lat, lat_dtype, q_rots,
+    #                      shifts, n_shift, rot_dtype, pos, n_tok, n_heads, d_nope, d_rope, d_c, base, stream)
+    qk = lambda q_dt, gq, eps, in_dt, n_tok, H, d_nope: _st(  # noqa: E731
+        lib, "mla_prepare_q_qknorm", P, q_dt, gq, P, eps, P, P, in_dt, P, 0, None, None, 0, 0, P, n_tok, H, d_nope,
+        64, 512, 1e4, None)
+    assert qk(0, None, 1e-6, 1, 4, 16, 128) == 1       # g_q NULL
+    assert qk(4, P, 1e-6, 1, 4, 16, 128) == 3          # unknown q dtype
+    assert qk(0, P, -1.0, 1, 4, 16, 128) == 2          # eps < 0
+    assert qk(0, P, float("nan"), 1, 4, 16, 128) == 2
+    assert qk(0, P, 1e-6, 0, 4, 16, 128) == 5          # fp32 weights: not the MFMA path
+    assert qk(0, P, 1e-6, 1, 4, 16, 64) == 5           # d_nope 64
+    assert _st(lib, "mla_prepare_q_qknorm", P + 8, 0, P, P, 1e-6, P, P, 1, P, 0, None, None, 0, 0, P, 4, 16, 128,
+               64, 512, 1e4, None) == 5                 # q_nope not 16-byte aligned
+    assert qk(0, P, 1e-6, 1, 33, 16, 128) == 5         # 528 query rows > 512
+    assert qk(0, P, 1e-6, 1, 0, 16, 128) == 0          # no tokens: nothing enqueued
     # mla_quantize_latent_i8(rows, row_dtype, n_rows, d_c, d_rope, out_rows, scales, stream)
     assert _st(lib, "mla_quantize_latent_i8", P, 1, 10, 512, 64, None, P, None) == 1
     assert _st(lib, "mla_quantize_latent_i8", P, 0, 10, 512, 64, P, P, None) == 3

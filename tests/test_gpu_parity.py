@@ -123,6 +123,10 @@ EDGE = {
         SegSpec("kv", lengths=(1, 37, 300, 1000), layout="paged", page_size=64, spare_pages=2, online=True),)),
     "qknorm_rows32_sq2": _custom("edge-qkn32", batch=3, heads=16, s_q=2, qk_norm=True, qk_eps=0.5, segs=(
         SegSpec("kv", lengths=(2, 95, 513), causal=True, online=True),)),
+    # 9 x 64 = 576 query rows: beyond the fused QK-Norm prepare, so the
+    # query normalisation runs as its own launch before mla_prepare_q
+    "qknorm_two_launch_rows576": _custom("edge-qkn576", batch=9, heads=64, qk_norm=True, segs=(
+        SegSpec("kv", lengths=(0, 1, 5, 37, 64, 65, 100, 130, 300), online=True),)),
     "qknorm_toy_f32": _custom("edge-qknf32", dtype="f32", batch=3, heads=2, qk_norm=True, segs=(
         SegSpec("kv", lengths=(16, 0, 130), layout="paged", page_size=8, spare_pages=1, online=True),)),
     # int8 latent cache: row scales through each row-group size, contiguous
@@ -248,6 +252,40 @@ def test_prepare_fp32_query_bf16_weights():
     assert np.max(np.abs(ref_hi - ref)) > 50 * np.max(err)
     ref_r = O.rope_relocate(f64(q_pe), pos.numpy(), np.zeros(n_tok, np.int64), 10000.0)
     assert np.abs(f64(q_rots[0]) - ref_r).max() <= 1e-5
+
+
+@pytest.mark.parametrize("q_dtype,n_tok,H", [(torch.bfloat16, 1, 16), (torch.float32, 17, 16),
+                                             (torch.bfloat16, 32, 16), (torch.float32, 4, 128)])
+def test_prepare_qknorm_call(q_dtype, n_tok, H):
+    """mla_prepare_q_qknorm: q_lat = U_K^T (g_q g_k q / rms over all heads)
+    against the oracle's definition (one token, a ragged second token block,
+    the 512-row limit with 16 and with 128 heads), its rotary outputs, and
+    agreement with the two-launch form (mla_qknorm_query, then mla_prepare_q
+    with the fp32 query) to the same fp32 bound."""
+    from mla_latent_cache_amd import ops
+    d_nope, d_c, d_r, eps = 128, 512, 64, 0.25
+    q = _rand((n_tok, H, d_nope), q_dtype, 51) * 3
+    q[0, 0] = 0                                     # one zero head: the statistic still spans all heads
+    g_q = 1 + 0.1 * _rand((H, d_nope), torch.float32, 52)
+    g_k = 1 + 0.1 * _rand((H, d_nope), torch.float32, 53)
+    q_pe = _rand((n_tok, H, d_r), torch.bfloat16, 54)
+    w = (_rand((H, d_nope, d_c), torch.float32, 55) / math.sqrt(d_c)).to(torch.bfloat16)
+    pos = torch.arange(n_tok, dtype=torch.int64) * 131
+    shift = torch.arange(n_tok, dtype=torch.int64) * 7 + 3
+    qc, gqc, gkc, pec, wc, posc = (t.cuda() for t in (q, g_q, g_k, q_pe, w, pos))
+    q_lat, q_rots = ops.prepare_q_qknorm(qc, gqc, gkc, eps, pec, wc, posc, [None, shift.cuda()],
+                                         lat_dtype=torch.float32, rot_dtype=torch.float32)
+    q_two, _ = ops.prepare_q(ops.qknorm_query(qc, gqc, gkc, eps), pec, wc, posc, [], lat_dtype=torch.float32)
+    torch.cuda.synchronize()
+    qn = np.stack([f64(g_q) * f64(g_k) * f64(q[t]) * O.rms_inverse(f64(q[t]), eps) for t in range(n_tok)])
+    ref = O.absorb_query(f64(w), qn)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    for got in (q_lat, q_two):
+        err = np.abs(f64(got) - ref)
+        assert np.all(err <= 1e-5 * np.abs(ref) + 2e-5 * rms), float(np.max(err / rms))
+    for sh, got in ((np.zeros(n_tok, np.int64), q_rots[0]), (shift.numpy(), q_rots[1])):
+        ref_r = O.rope_relocate(f64(q_pe), pos.numpy(), sh, 10000.0)
+        assert np.abs(f64(got) - ref_r).max() <= 1e-5
 
 
 @pytest.mark.parametrize("out_dtype,n_rows", [(torch.float32, 37), (torch.bfloat16, 37), (torch.float32, 600),
