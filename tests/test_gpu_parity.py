@@ -378,6 +378,12 @@ def test_quantize_call():
     (torch.bfloat16, torch.float32, (2, 3, 7, 36, 20)),
     (torch.bfloat16, torch.bfloat16, (8, 12, 9, 512, 128)),    # 96 rows: two blocks per row
     (torch.float32, torch.bfloat16, (3, 50, 5, 512, 128)),     # 150 rows: one block per row
+    # slots loaded ahead of their weights (up to 128 at four blocks per row,
+    # 64 below) and the compacted rounds beyond
+    (torch.bfloat16, torch.bfloat16, (1, 16, 65, 512, 128)),   # the small step's 65 slots
+    (torch.float32, torch.bfloat16, (2, 8, 128, 512, 128)),
+    (torch.float32, torch.bfloat16, (1, 4, 200, 512, 128)),
+    (torch.bfloat16, torch.bfloat16, (5, 20, 70, 512, 128)),   # 100 rows: two blocks per row, 70 > 64
 ])
 def test_combine_out_uv_call(out_dtype, w_dtype, dims):
     from mla_latent_cache_amd import ops
