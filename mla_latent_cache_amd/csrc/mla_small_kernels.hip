@@ -529,7 +529,7 @@ hipError_t launch_quantize_latent_i8(const void* rows, int64_t n_rows, int d_c, 
 // statistic over a token's whole content projection.
 //  * qknorm_query_kernel: one block per query token; the sum of squares over
 //    all heads' q_nope, then q_out = g_q g_k q / rms (the static key weight
-//    moved into the query).
+//    moved into the query); qknorm_query_vec_kernel is its 16-byte form.
 //  * qknorm_gram_kernel: G = sum_h U_K[h]^T U_K[h] (d_c x d_c), one block per
 //    row a of G, threads over b; fp32 sums over the n_heads * d_nope terms.
 //  * qknorm_rinv_kernel: 16 stored rows per block, their latents in LDS;
@@ -557,6 +557,61 @@ __global__ __launch_bounds__(256) void qknorm_query_kernel(const TI* __restrict_
   const float inv = 1.f / sqrtf(tot / (float)n_hd + eps);
   float* o = q_out + (int64_t)t * n_hd;
   for (int i = threadIdx.x; i < n_hd; i += 256) o[i] = g_q[i] * g_k[i] * load_f(q + i) * inv;
+}
+
+// The same with 8 consecutive entries per thread and load (n_hd a multiple
+// of 8, every pointer 16-byte aligned): the sum of squares with four loads
+// in flight per thread, then the scaled row from a second (cached) read.
+template <typename TI>
+__global__ __launch_bounds__(256) void qknorm_query_vec_kernel(const TI* __restrict__ q_nope,
+                                                               const float* __restrict__ g_q,
+                                                               const float* __restrict__ g_k, int n_hd, float eps,
+                                                               float* __restrict__ q_out) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  const TI* q = q_nope + (int64_t)t * n_hd;
+  auto load8 = [&](int i, f32x4& a, f32x4& b) {
+    if constexpr (sizeof(TI) == 4) {
+      a = *(const f32x4*)(q + i);
+      b = *(const f32x4*)(q + i + 4);
+    } else {
+      const bf16x8 v = *(const bf16x8*)(q + i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[e] = (float)v[e];
+        b[e] = (float)v[4 + e];
+      }
+    }
+  };
+  float ss = 0.f;
+#pragma unroll 4
+  for (int i = 8 * (int)threadIdx.x; i < n_hd; i += 8 * 256) {
+    f32x4 a, b;
+    load8(i, a, b);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss += a[e] * a[e] + b[e] * b[e];
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  const float inv = 1.f / sqrtf(tot / (float)n_hd + eps);
+  float* o = q_out + (int64_t)t * n_hd;
+#pragma unroll 2
+  for (int i = 8 * (int)threadIdx.x; i < n_hd; i += 8 * 256) {
+    f32x4 a, b;
+    load8(i, a, b);
+    const f32x4 gq0 = *(const f32x4*)(g_q + i), gq1 = *(const f32x4*)(g_q + i + 4);
+    const f32x4 gk0 = *(const f32x4*)(g_k + i), gk1 = *(const f32x4*)(g_k + i + 4);
+    f32x4 y0, y1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      y0[e] = gq0[e] * gk0[e] * a[e] * inv;
+      y1[e] = gq1[e] * gk1[e] * b[e] * inv;
+    }
+    *(f32x4*)(o + i) = y0;
+    *(f32x4*)(o + i + 4) = y1;
+  }
 }
 
 template <typename TW>
@@ -616,6 +671,14 @@ __global__ __launch_bounds__(256) void qknorm_rinv_kernel(const TI* __restrict__
 hipError_t launch_qknorm_query(const void* q_nope, bool in_bf16, const float* g_q, const float* g_k, int n_tok,
                                int n_heads, int d_nope, float eps, float* q_out, hipStream_t stream) {
   const int n_hd = n_heads * d_nope;
+  auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  if (n_hd % 8 == 0 && al16(q_nope) && al16(g_q) && al16(g_k) && al16(q_out)) {
+    if (in_bf16)
+      return launch(qknorm_query_vec_kernel<bf16>, dim3(n_tok), dim3(256), stream, (const bf16*)q_nope, g_q, g_k,
+                    n_hd, eps, q_out);
+    return launch(qknorm_query_vec_kernel<float>, dim3(n_tok), dim3(256), stream, (const float*)q_nope, g_q, g_k,
+                  n_hd, eps, q_out);
+  }
   if (in_bf16)
     return launch(qknorm_query_kernel<bf16>, dim3(n_tok), dim3(256), stream, (const bf16*)q_nope, g_q, g_k, n_hd, eps,
                   q_out);

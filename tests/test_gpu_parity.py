@@ -314,7 +314,9 @@ def test_combine_call(out_dtype, n_rows):
 
 
 @pytest.mark.parametrize("dtype,dims", [(torch.float32, (7, 5, 24, 40, 48, 37)),
-                                        (torch.bfloat16, (3, 16, 128, 512, 576, 70))])
+                                        (torch.bfloat16, (3, 16, 128, 512, 576, 70)),
+                                        (torch.float32, (4, 3, 6, 8, 10, 20)),        # 18 per token: scalar loads
+                                        (torch.bfloat16, (5, 128, 128, 512, 576, 40))])  # 8 loads per thread
 def test_qknorm_calls(dtype, dims):
     """mla_qknorm_query / _key_gram / _key_rinv against the direct RMS of the
     query over all heads and of each row's expanded key U_K c over all heads."""
