@@ -117,6 +117,15 @@ EDGE = {
         SegSpec("kv", lengths=(1, 37, 300, 1000), online=True),)),
     "toy_f32_ragged": _custom("edge-f32", dtype="f32", batch=3, heads=2, scale=1 / math.sqrt(6), segs=(
         SegSpec("kv", lengths=(16, 0, 130), layout="paged", page_size=8, spare_pages=1, online=True),)),
+    # the fp32-cache decode at its largest dims and at odd ones
+    "f32_max_dims": Spec(name="edge-f32-max", batch=3, heads=3, s_q=1, dtype="f32", d_c=512, d_nope=96,
+                         d_rope=128, d_v=40, segments=(
+                             SegSpec("kv", lengths=(1, 70, 257), layout="paged", page_size=64, spare_pages=1,
+                                     online=True),)),
+    "f32_odd_dims": Spec(name="edge-f32-odd", batch=3, heads=5, s_q=2, dtype="f32", d_c=300, d_nope=20,
+                         d_rope=6, d_v=7, segments=(
+                             SegSpec("kv", lengths=(0, 33, 100), causal=True, layout="paged", page_size=16,
+                                     spare_pages=2, online=True),)),
     # QK-Norm: per-row key factors through each row-group size (16, 32, 64
     # query rows), contiguous and paged, and the fp32 path
     "qknorm_paged_rows64": _custom("edge-qkn64", batch=4, heads=64, qk_norm=True, segs=(
