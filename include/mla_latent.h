@@ -250,7 +250,8 @@ mla_status mla_prepare_q(const void* q_nope, int q_dtype, const void* q_pe, cons
  * itself, so the call is meant for decode batches: n_tok * n_heads <= 512.
  * q_nope [n_tok][n_heads][128] q_dtype (MLA_BF16 or MLA_F32, 16-byte
  * aligned); g_q, g_k [n_heads][128] fp32; w_uk [n_heads][128][512] bf16
- * (16-byte aligned), in_dtype MLA_BF16 (also the dtype of q_pe); eps >= 0.
+ * (16-byte aligned), in_dtype MLA_BF16 (also the dtype of q_pe); eps >= 0
+ * (eps = 0 and an all-zero token: that token's q_lat is not finite).
  * The fp32 product enters the MFMA as bf16 hi + lo parts with fp32
  * accumulation.  Other arguments as mla_prepare_q.
  * Errors: MLA_ERR_NULL, MLA_ERR_DTYPE, MLA_ERR_SHAPE, MLA_ERR_UNSUPPORTED
@@ -337,7 +338,8 @@ mla_status mla_quantize_latent_i8(const void* rows, int row_dtype, int64_t n_row
  * The rotary parts are not normalised.
  *
  * mla_qknorm_query: q_out[t][h][i] = g_q[h][i] g_k[h][i] q_nope[t][h][i] / rms_t,
- *   rms_t = sqrt(mean_{h,i} q_nope[t][h][i]^2 + eps).
+ *   rms_t = sqrt(mean_{h,i} q_nope[t][h][i]^2 + eps)  (eps = 0 and an all-zero
+ *   token give rms_t = 0: that token's outputs are not finite, as in the definition).
  *   q_nope [n_tok][n_heads][d_nope] in_dtype; g_q, g_k [n_heads][d_nope] fp32;
  *   q_out [n_tok][n_heads][d_nope] fp32 (then mla_prepare_q with q_dtype MLA_F32 and
  *   the bf16 w_uk, or mla_absorb_q with fp32 weights).
