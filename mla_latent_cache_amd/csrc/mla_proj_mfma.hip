@@ -43,8 +43,9 @@ __device__ __forceinline__ void absorb_block(const TQ* __restrict__ q_nope, cons
   const int l16 = lane & 15, lg = lane >> 4;
   // weight slice w_uk[h][0:128][j0:j0+128] -> LDS (row i: 256 B + pad)
   const bf16* w = w_uk + (int64_t)h * kNope * kLat + j0;
-  for (int e = tid; e < kNope * (kAbsCols / 8); e += 256) {
-    const int i = e / (kAbsCols / 8), c8 = e % (kAbsCols / 8);
+#pragma unroll
+  for (int k = 0; k < kNope * (kAbsCols / 8) / 256; ++k) {  // a fixed count: all loads in flight at once
+    const int e = tid + 256 * k, i = e / (kAbsCols / 8), c8 = e % (kAbsCols / 8);
     *(bf16x8*)(wl + i * kAbsLds + c8 * 16) = *(const bf16x8*)(w + (int64_t)i * kLat + c8 * 8);
   }
   __syncthreads();
@@ -54,23 +55,30 @@ __device__ __forceinline__ void absorb_block(const TQ* __restrict__ q_nope, cons
     bf16x8 qa[4], ql[QF ? 4 : 1];
     const int t = t0 + l16;
     if constexpr (QF) {
+      // loads from a clamped token (always in bounds), rows past n_tok
+      // zeroed afterwards: a load under the row condition compiles to a
+      // branch with a full wait, one memory round trip per load
       f32x4 va[4][2];
+      const int tcl = min(t, n_tok - 1);
+      const bool t_ok = t < n_tok;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        va[ks][0] = va[ks][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (t < n_tok) {
-          const int64_t off = ((int64_t)t * n_heads + h) * kNope + 32 * ks + 8 * lg;
-          if constexpr (sizeof(TQ) == 4) {
-            va[ks][0] = *(const f32x4*)((const float*)q_nope + off);
-            va[ks][1] = *(const f32x4*)((const float*)q_nope + off + 4);
-          } else {
-            const bf16x8 a = *(const bf16x8*)(q_nope + off);
+        const int64_t off = ((int64_t)tcl * n_heads + h) * kNope + 32 * ks + 8 * lg;
+        if constexpr (sizeof(TQ) == 4) {
+          va[ks][0] = *(const f32x4*)((const float*)q_nope + off);
+          va[ks][1] = *(const f32x4*)((const float*)q_nope + off + 4);
+        } else {
+          const bf16x8 a = *(const bf16x8*)(q_nope + off);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              va[ks][0][e] = (float)a[e];
-              va[ks][1][e] = (float)a[4 + e];
-            }
+          for (int e = 0; e < 4; ++e) {
+            va[ks][0][e] = (float)a[e];
+            va[ks][1][e] = (float)a[4 + e];
           }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          va[ks][0][e] = t_ok ? va[ks][0][e] : 0.f;
+          va[ks][1][e] = t_ok ? va[ks][1][e] : 0.f;
         }
       }
       if constexpr (QKN) {
