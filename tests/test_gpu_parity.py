@@ -297,11 +297,13 @@ def test_prepare_qknorm_call(q_dtype, n_tok, H):
         assert np.abs(f64(got) - ref_r).max() <= 1e-5
 
 
-@pytest.mark.parametrize("out_dtype,n_rows", [(torch.float32, 37), (torch.bfloat16, 37), (torch.float32, 600),
-                                              (torch.float32, 1100)])
-def test_combine_call(out_dtype, n_rows):
+@pytest.mark.parametrize("out_dtype,n_rows,n_part", [(torch.float32, 37, 5), (torch.bfloat16, 37, 5),
+                                                     (torch.float32, 600, 5), (torch.float32, 1100, 5),
+                                                     (torch.bfloat16, 9, 300),      # slots beyond 128
+                                                     (torch.float32, 7, 1024)])     # the largest slot count
+def test_combine_call(out_dtype, n_rows, n_part):
     from mla_latent_cache_amd import ops
-    n_part, d_c = 5, 512
+    d_c = 512
     g = torch.Generator().manual_seed(12)
     o_part = torch.randn((n_rows, n_part, d_c), generator=g)
     lse_part = torch.randn((n_rows, n_part), generator=g) * 4
