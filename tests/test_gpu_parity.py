@@ -54,7 +54,7 @@ def test_split_invariance_dsv3_mini(n_wg):
     check_step(x, out, o_lat, lse, label=f"dsv3-mini n_wg={n_wg}")
 
 
-@pytest.mark.parametrize("n_split", [1, 2, 3, 9])
+@pytest.mark.parametrize("n_split", [1, 2, 3, 9, 40, 130])
 def test_forced_n_split(n_split):
     x = M.make("long", 8, mini=True, poison=True)
     _, out, o_lat, lse = _run(x, n_wg=64, n_split=[n_split])
