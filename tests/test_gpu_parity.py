@@ -61,6 +61,17 @@ def test_forced_n_split(n_split):
     check_step(x, out, o_lat, lse, label=f"long-mini n_split={n_split}")
 
 
+@pytest.mark.parametrize("n_wg", [1, 3, 2048])
+def test_grid_extremes(n_wg):
+    """One workgroup for all the work, an odd count, and many more
+    workgroups than shares of work (the idle ones plan, find no piece and
+    exit); the merge layout's three segments and several row groups."""
+    x = M.make("merge", 12, mini=True, poison=True)
+    print(f"[parity] merge-mini n_wg={n_wg}", flush=True)
+    _, out, o_lat, lse = _run(x, n_wg=n_wg)
+    check_step(x, out, o_lat, lse, label=f"merge-mini n_wg={n_wg}")
+
+
 def test_repeatable_bitwise():
     x = M.make("merge", 9, mini=True)
     st, out, o_lat, lse = _run(x)
