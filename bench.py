@@ -7,7 +7,10 @@ inputs already resident in HBM.  Prints one
 JSON line with decode tokens/s, the decode kernel's achieved HBM GB/s against
 the MI355X roofline, and the fp64 CPU oracle timed on a bounded sample.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload small]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3]
+
+The default workload is the largest single-GPU configuration: the
+DeepSeek-V3-style batch (B=64, H=128, T_b ~ U[1024, 32768], 64-row pages).
 """
 from __future__ import annotations
 
@@ -28,7 +31,8 @@ METRIC = "MLA decode tokens/s + achieved HBM GB/s & % roofline (latent-cache att
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 MALL_BYTES = 256 << 20          # Infinity Cache: rotate caches so every step reads HBM
-DECODE_SRC = os.path.join(ROOT, "mla_latent_cache_amd", "csrc", "mla_decode_bf16.hip")
+DECODE_SRCS = [os.path.join(ROOT, "mla_latent_cache_amd", "csrc", f)
+               for f in ("mla_decode_bf16.hip", "mla_decode_rows.hip")]
 SEEDS = {"toy": 0, "small": 1, "dsv3": 2, "long": 3, "merge": 4, "prefill": 5, "qknorm": 6, "int8": 7}
 
 
@@ -64,19 +68,26 @@ def ops_cache_dt(step) -> int:
 
 
 def kernel_hash() -> str:
-    with open(DECODE_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the decode kernels' sources (the files that exist)."""
+    h = hashlib.sha256()
+    for p in DECODE_SRCS:
+        if os.path.exists(p):
+            with open(p, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profile(workload: str):
-    """HBM bytes per decode launch from the committed counter summary, or None
-    when there is none or the kernel source changed since it was taken."""
+    """HBM bytes of one step's decode work (every decode dispatch of a step,
+    summed: a step over several segments may launch more than one) from the
+    committed counter summary, or None when there is none or the decode
+    sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"decode_{workload}_hbm_counters.md")
     if not os.path.exists(path):
         return None
     txt = open(path).read()
     m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", txt)
-    m_val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    m_val = re.search(r"hbm_bytes_per_step:\s*([0-9.eE+]+)", txt)
     if not m_hash or not m_val or m_hash.group(1) != kernel_hash():
         return None
     return float(m_val.group(1))
@@ -136,7 +147,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="small", choices=["small", "dsv3", "long", "merge", "toy", "prefill", "qknorm", "int8"])
+    ap.add_argument("--workload", default="dsv3", choices=["small", "dsv3", "long", "merge", "toy", "prefill", "qknorm", "int8"])
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--n-wg", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)

@@ -10,7 +10,10 @@ import ctypes
 import os
 from ctypes import POINTER, c_double, c_float, c_int, c_int64, c_void_p
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_latent.so")
+# The in-tree build; MLA_LATENT_LIB names another build of the same sources
+# (the host-sanitizer build of the C ABI that the CPU tests load).
+LIB_PATH = os.environ.get("MLA_LATENT_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                            "libmla_latent.so")
 
 MLA_F32 = 0
 MLA_BF16 = 1

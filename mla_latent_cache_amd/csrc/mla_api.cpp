@@ -58,6 +58,12 @@ constexpr int kBf16Dc = 512;
 constexpr int kBf16MaxRows = 4096;
 constexpr int kBf16Dr = 64;
 constexpr int kPage = 64;
+// Split slots per request and segment on the bf16 path (a piece packs its
+// slot into 16 bits).
+constexpr int kMaxSplit = 32767;
+// Query tokens per call of the query-side and output-side calls: their index
+// arithmetic (tokens x rotary pairs x segment shifts) stays within 32 bits.
+constexpr int kMaxTok = 1 << 20;
 
 }  // namespace
 
@@ -98,8 +104,9 @@ mla_status rope_relocate_q(const void* q_pe, int in_dtype, void* q_rot, int out_
   if (!q_pe || !q_rot || !pos) return fail(MLA_ERR_NULL, "rope_relocate_q: q_pe, q_rot and pos are required");
   if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
     return fail(MLA_ERR_DTYPE, "rope_relocate_q: dtypes %d, %d", in_dtype, out_dtype);
-  if (n_tok < 0 || n_heads <= 0 || d_rope < 2 || d_rope > 128 || (d_rope & 1))
-    return fail(MLA_ERR_SHAPE, "rope_relocate_q: n_tok=%d n_heads=%d d_rope=%d", n_tok, n_heads, d_rope);
+  if (n_tok < 0 || n_tok > kMaxTok || n_heads <= 0 || n_heads > 65535 || d_rope < 2 || d_rope > 128 || (d_rope & 1))
+    return fail(MLA_ERR_SHAPE, "rope_relocate_q: n_tok=%d (<= %d) n_heads=%d d_rope=%d", n_tok, kMaxTok, n_heads,
+                d_rope);
   if (!(base > 1.0) || !std::isfinite(base)) return fail(MLA_ERR_SHAPE, "rope_relocate_q: base=%g", base);
   if (n_tok == 0) return ok();
   return hip_status(mla::launch_rope(q_pe, in_dtype == MLA_BF16, q_rot, out_dtype == MLA_BF16, pos, shift,
@@ -112,8 +119,10 @@ mla_status mla_absorb_q(const void* q_nope, const void* w_uk, int in_dtype, void
   if (!q_nope || !w_uk || !q_lat) return fail(MLA_ERR_NULL, "mla_absorb_q: null pointer");
   if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
     return fail(MLA_ERR_DTYPE, "mla_absorb_q: dtypes %d, %d", in_dtype, out_dtype);
-  if (n_tok < 0 || n_heads <= 0 || d_nope <= 0 || d_nope > 256 || d_c <= 0 || d_c > 4096 || n_heads > 65535)
-    return fail(MLA_ERR_SHAPE, "mla_absorb_q: n_tok=%d n_heads=%d d_nope=%d d_c=%d", n_tok, n_heads, d_nope, d_c);
+  if (n_tok < 0 || n_tok > kMaxTok || n_heads <= 0 || d_nope <= 0 || d_nope > 256 || d_c <= 0 || d_c > 4096 ||
+      n_heads > 65535)
+    return fail(MLA_ERR_SHAPE, "mla_absorb_q: n_tok=%d (<= %d) n_heads=%d d_nope=%d d_c=%d", n_tok, kMaxTok, n_heads,
+                d_nope, d_c);
   if (n_tok == 0) return ok();
   return hip_status(mla::launch_absorb(q_nope, w_uk, in_dtype == MLA_BF16, q_lat, out_dtype == MLA_BF16, n_tok,
                                        n_heads, d_nope, d_c, (hipStream_t)stream),
@@ -132,10 +141,10 @@ mla_status mla_prepare_q(const void* q_nope, int q_dtype, const void* q_pe, cons
     return fail(MLA_ERR_SHAPE, "mla_prepare_q: n_shift=%d (0..%d)", n_shift, mla::kMaxShift);
   for (int k = 0; k < n_shift; ++k)
     if (!q_rots[k]) return fail(MLA_ERR_NULL, "mla_prepare_q: q_rots[%d] is NULL", k);
-  if (n_tok < 0 || n_heads <= 0 || n_heads > 65535 || d_nope <= 0 || d_nope > 256 || d_c <= 0 || d_c > 4096 ||
-      d_rope < 2 || d_rope > 128 || (d_rope & 1))
-    return fail(MLA_ERR_SHAPE, "mla_prepare_q: n_tok=%d n_heads=%d d_nope=%d d_rope=%d d_c=%d", n_tok, n_heads,
-                d_nope, d_rope, d_c);
+  if (n_tok < 0 || n_tok > kMaxTok || n_heads <= 0 || n_heads > 65535 || d_nope <= 0 || d_nope > 256 || d_c <= 0 ||
+      d_c > 4096 || d_rope < 2 || d_rope > 128 || (d_rope & 1))
+    return fail(MLA_ERR_SHAPE, "mla_prepare_q: n_tok=%d (<= %d) n_heads=%d d_nope=%d d_rope=%d d_c=%d", n_tok,
+                kMaxTok, n_heads, d_nope, d_rope, d_c);
   if (!(base > 1.0) || !std::isfinite(base)) return fail(MLA_ERR_SHAPE, "mla_prepare_q: base=%g", base);
   const bool mfma = in_dtype == MLA_BF16 && mla::absorb_mfma_ok(q_nope, w_uk, d_nope, d_c);
   if (q_dtype != in_dtype && !(q_dtype == MLA_F32 && mfma))
@@ -182,7 +191,7 @@ mla_status mla_prepare_q_qknorm(const void* q_nope, int q_dtype, const float* g_
     return fail(MLA_ERR_SHAPE, "mla_prepare_q_qknorm: n_shift=%d (0..%d)", n_shift, mla::kMaxShift);
   for (int k = 0; k < n_shift; ++k)
     if (!q_rots[k]) return fail(MLA_ERR_NULL, "mla_prepare_q_qknorm: q_rots[%d] is NULL", k);
-  if (n_tok < 0 || n_heads <= 0 || n_heads > 65535 || d_rope < 2 || d_rope > 128 || (d_rope & 1))
+  if (n_tok < 0 || n_tok > kMaxTok || n_heads <= 0 || n_heads > 65535 || d_rope < 2 || d_rope > 128 || (d_rope & 1))
     return fail(MLA_ERR_SHAPE, "mla_prepare_q_qknorm: n_tok=%d n_heads=%d d_rope=%d", n_tok, n_heads, d_rope);
   if (!(base > 1.0) || !std::isfinite(base)) return fail(MLA_ERR_SHAPE, "mla_prepare_q_qknorm: base=%g", base);
   if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(MLA_ERR_SHAPE, "mla_prepare_q_qknorm: eps=%g", (double)eps);
@@ -214,8 +223,10 @@ mla_status mla_out_uv(const void* o_lat, int o_dtype, const void* w_uv, int w_dt
   if (!o_lat || !w_uv || !out) return fail(MLA_ERR_NULL, "mla_out_uv: null pointer");
   if (!dtype_ok(o_dtype) || !dtype_ok(w_dtype) || !dtype_ok(out_dtype))
     return fail(MLA_ERR_DTYPE, "mla_out_uv: dtypes %d, %d, %d", o_dtype, w_dtype, out_dtype);
-  if (n_tok < 0 || n_heads <= 0 || n_heads > 65535 || d_c <= 0 || d_c > 1024 || d_v <= 0 || d_v > 4 * 65535)
-    return fail(MLA_ERR_SHAPE, "mla_out_uv: n_tok=%d n_heads=%d d_c=%d d_v=%d", n_tok, n_heads, d_c, d_v);
+  if (n_tok < 0 || n_tok > kMaxTok || n_heads <= 0 || n_heads > 65535 || d_c <= 0 || d_c > 1024 || d_v <= 0 ||
+      d_v > 4 * 65535)
+    return fail(MLA_ERR_SHAPE, "mla_out_uv: n_tok=%d (<= %d) n_heads=%d d_c=%d d_v=%d", n_tok, kMaxTok, n_heads, d_c,
+                d_v);
   if (n_tok == 0) return ok();
   return hip_status(mla::launch_out_uv(o_lat, o_dtype == MLA_BF16, w_uv, w_dtype == MLA_BF16, out,
                                        out_dtype == MLA_BF16, n_tok, n_heads, d_c, d_v, (hipStream_t)stream),
@@ -359,8 +370,15 @@ mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q
       if ((int64_t)s_q * s.head_count > kBf16MaxRows)
         return fail(MLA_ERR_UNSUPPORTED, "segment %d: s_q * head_count = %d > %d", g, s_q * s.head_count,
                     kBf16MaxRows);
-      if (batch > 65535 || s.n_split > 65535)
-        return fail(MLA_ERR_UNSUPPORTED, "segment %d: bf16 path needs batch and n_split <= 65535", g);
+      if (batch > 65535 || s.n_split > kMaxSplit)
+        return fail(MLA_ERR_UNSUPPORTED, "segment %d: bf16 path needs batch <= 65535 and n_split <= %d", g,
+                    kMaxSplit);
+      // row counts of the device-side split plan are 32-bit: bound the rows a
+      // segment can hold (2^30 rows of 1152 B is far beyond device memory)
+      const int64_t cap = s.block_table ? (int64_t)s.max_pages * kPage : s.max_rows;
+      if (cap > ((int64_t)1 << 30) || (int64_t)batch * cap > ((int64_t)1 << 30))
+        return fail(MLA_ERR_UNSUPPORTED, "segment %d: batch * rows per request = %lld exceeds 2^30", g,
+                    (long long)((int64_t)batch * cap));
       if (s.row_rinv && q_dtype != MLA_F32)
         return fail(MLA_ERR_UNSUPPORTED, "segment %d: QK-Norm (row_rinv) needs an fp32 query", g);
       if (i8 && !s.row_scale) return fail(MLA_ERR_NULL, "segment %d: an int8 cache needs row_scale", g);

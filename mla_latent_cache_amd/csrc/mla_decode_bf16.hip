@@ -88,7 +88,8 @@ constexpr int kMaxPieces = 64;
 constexpr int kKSteps = (kDc + kDr) / 32;   // 18 MFMA k-steps over [c | kr]
 
 // One piece of a workgroup's share: rows [r0, r1) of request b (T rows in
-// all) into partial slot `slot`; b and slot are packed (both < 2^16).
+// all) into partial slot `slot`; b (< 2^16) and slot (< 2^15) are packed
+// into one non-negative int.
 struct Piece {
   int b_slot, r0, r1, T;
 };
@@ -532,7 +533,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
       const Piece pc = sm.pieces[pi];
       const int b_slot = __builtin_amdgcn_readfirstlane(pc.b_slot);
       const int b = b_slot & 0xffff;
-      const int slot = b_slot >> 16;
+      const int slot = (int)((unsigned)b_slot >> 16);
       const int pr0 = __builtin_amdgcn_readfirstlane(pc.r0);
       const int pr1 = __builtin_amdgcn_readfirstlane(pc.r1);
       const int T = __builtin_amdgcn_readfirstlane(pc.T);

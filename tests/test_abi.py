@@ -181,3 +181,34 @@ def test_null_and_shape_errors_before_any_gpu_call(lib):
     assert dec([seg(row_scale=P, row_rinv=P)], dtype=2) == 5
     assert dec([seg(row_scale=P)], dtype=1) == 5          # row_scale only with an int8 cache
     assert dec([seg(row_scale=P)], dtype=3) == 3
+
+
+def test_size_limits_refused(lib):
+    """Sizes past the 32-bit index arithmetic of the kernels are refused on
+    the host: split counts beyond the 15-bit slot field, segments holding more
+    than 2^30 rows in all, and more than 2^20 query tokens per call."""
+    from mla_latent_cache_amd._lib import MlaSegment
+    P = 16
+
+    def seg(**kw):
+        s = MlaSegment()
+        s.cache, s.seq_lens, s.q_rot = P, P, P
+        s.max_rows, s.head_begin, s.head_count, s.part_begin, s.n_split = 64, 0, 4, 0, 2
+        for k, v in kw.items():
+            setattr(s, k, v)
+        return s
+
+    def dec(segs, n_part, batch=2):
+        arr = (MlaSegment * len(segs))(*segs)
+        return lib.mla_decode_splitkv(arr, len(segs), P, 0, 1, batch, 1, 4, 512, 64, 0.1, P, P, n_part, 0, None)
+
+    assert dec([seg(n_split=32768)], 32768) == 5
+    assert b"n_split" in lib.mla_last_error()
+    assert dec([seg(max_rows=1 << 29)], 2, batch=3) == 5           # 3 * 2^29 rows
+    assert dec([seg(block_table=P, page_size=64, max_pages=1 << 25, n_pages=8)], 2) == 5
+    assert dec([seg(max_rows=1 << 29)], 2, batch=0) == 0             # nothing to launch: accepted
+    n = (1 << 20) + 1
+    assert lib.rope_relocate_q(P, 1, P, 0, P, None, n, 1, 64, 1e4, None) == 2
+    assert lib.mla_absorb_q(P, P, 1, P, 0, n, 1, 128, 512, None) == 2
+    assert lib.mla_out_uv(P, 1, P, 1, P, 1, n, 1, 512, 128, None) == 2
+    assert lib.mla_prepare_q(P, 1, P, P, 1, P, 0, None, None, 0, 0, P, n, 4, 128, 64, 512, 1e4, None) == 2

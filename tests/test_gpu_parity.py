@@ -126,6 +126,11 @@ EDGE = {
     # query miss the lse bound several times over
     "peaked_rows64": _custom("edge-peaked", batch=4, heads=64, scale=2 / math.sqrt(192), segs=(
         SegSpec("kv", lengths=(1, 37, 300, 1000), online=True),)),
+    # four times the default spread: the first-order correction's remaining
+    # lse error, evaluated on the CPU for these inputs, is 5e-5 (uncorrected
+    # 1.5e-2; tests/test_lse_correction.py)
+    "peaked4_rows64": _custom("edge-peaked4", batch=4, heads=64, scale=4 / math.sqrt(192), segs=(
+        SegSpec("kv", lengths=(1, 37, 300, 1000), online=True),)),
     "toy_f32_ragged": _custom("edge-f32", dtype="f32", batch=3, heads=2, scale=1 / math.sqrt(6), segs=(
         SegSpec("kv", lengths=(16, 0, 130), layout="paged", page_size=8, spare_pages=1, online=True),)),
     # the fp32-cache decode at its largest dims and at odd ones
