@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmla_latent.so")
-SOURCES = ["mla_api.cpp", "mla_small_kernels.hip", "mla_decode_bf16.hip", "mla_proj_mfma.hip"]
+SOURCES = ["mla_api.cpp", "mla_small_kernels.hip", "mla_decode_bf16.hip", "mla_decode_rows.hip",
+           "mla_proj_mfma.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are disabled: hipcc would otherwise generate

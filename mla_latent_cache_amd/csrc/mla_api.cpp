@@ -94,7 +94,7 @@ int mla_decode_shares(int s_q, int head_count, int n_wg) {
   const int wg = n_wg > 0 ? n_wg : cu_count();
   if (wg <= 0) return 0;
   int n_share = 0, n_rg = 0;
-  mla::decode_bf16_grid(s_q * head_count, wg, &n_share, &n_rg);
+  mla::decode_bf16_grid(s_q * head_count, mla::decode_bf16_tile(s_q * head_count), wg, &n_share, &n_rg);
   return n_share;
 }
 

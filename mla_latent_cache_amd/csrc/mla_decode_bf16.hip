@@ -59,19 +59,12 @@
 //    __syncthreads()' fence would drain the in-flight tile loads.  Every
 //    branch on a wave's role is a scalar branch.
 #include "mla_common.h"
+#include "mla_decode_tile.h"
 #include "mla_kernels.h"
 
 namespace mla {
 namespace {
 
-constexpr int kDc = 512;
-constexpr int kDr = 64;
-constexpr int kRowBytes = (kDc + kDr) * 2;  // 1152
-constexpr int kTile = 32;                   // cache rows per tile
-constexpr int kCBytes = kDc * 2;            // 1024: latent part c_t of a row
-constexpr int kRBytes = kDr * 2;            // 128: rotary part kr_t of a row
-constexpr int kCStage = kTile * kCBytes;    // latent ring stage (32 KiB)
-constexpr int kRStage = kTile * kRBytes;    // rotary ring stage (4 KiB)
 constexpr int kNStage = 4;                  // latent ring: read by the score waves, then the PV waves
 constexpr int kAhead = kNStage - 1;         // tiles in flight beyond the two being computed on
 constexpr int kNRStage = kAhead;            // rotary ring: dead once its tile is scored
@@ -82,50 +75,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kNDma = kTile + kRStage / 1024;
 static_assert(kNDma == 36 && kRStage % 1024 == 0, "tile geometry");
 constexpr int kPStr = 80;                   // bytes per P row (32 bf16 + pad)
-constexpr float kTau = 8.f;
-constexpr int kPageSize = 64;
 constexpr int kMaxPieces = 64;
-constexpr int kKSteps = (kDc + kDr) / 32;   // 18 MFMA k-steps over [c | kr]
-
-// One piece of a workgroup's share: rows [r0, r1) of request b (T rows in
-// all) into partial slot `slot`; b (< 2^16) and slot (< 2^15) are packed
-// into one non-negative int.
-struct Piece {
-  int b_slot, r0, r1, T;
-};
-
-__device__ __forceinline__ int sload_i32(const int32_t* p) {
-  // Scalar (SMEM) load: counted by lgkmcnt, so it never forces the in-flight
-  // LDS-direct loads (vmcnt, in order) to drain.
-  int v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
-  return v;
-}
-
-// Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32,
-// l^48) with the gfx950 row-swap instructions: VALU only, no LDS round trip.
-// permlane16_swap(x, x) leaves rows (0,0,2,2) / (1,1,3,3) in its two results,
-// permlane32_swap(x, x) rows (0,1,0,1) / (2,3,2,3).
-__device__ __forceinline__ float rows_max(float v) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float rows_sum(float v) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-// LDS layout of a tile (no padding, 16-byte chunks XOR-swizzled per row):
-// latent row r holds chunk c (0..63) at position c ^ (r & 15), rotary row r
-// chunk j (0..7) at position j ^ ((r >> 1) & 7).  A score-operand read (16
-// consecutive rows, one chunk) and a transposed read then touch 16 distinct
-// bank groups, like a padded layout, while the tile fits in 36 KiB.
-__device__ __forceinline__ int cpos(int r, int c) { return c ^ (r & 15); }
-__device__ __forceinline__ int rpos(int r, int j) { return j ^ ((r >> 1) & 7); }
 
 // Ring geometry per cache format.  16-bit rows (1152 B): the tile loads land
 // directly in the latent ring the MFMAs read (4 stages, 3 tiles ahead).
@@ -1092,8 +1042,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
 // block, its O columns and the scores in registers without spilling.
 static int row_tile(int rows_total) { return rows_total <= 16 ? 16 : rows_total <= 32 ? 32 : 64; }
 
-void decode_bf16_grid(int rows_total, int n_wg, int* n_share, int* n_rg) {
-  const int mt = row_tile(rows_total);
+int decode_bf16_tile(int rows_total) { return rows_total > 32 ? decode_rows_tile(rows_total) : row_tile(rows_total); }
+
+void decode_bf16_grid(int rows_total, int mt, int n_wg, int* n_share, int* n_rg) {
   *n_rg = (rows_total + mt - 1) / mt;
   int ns = n_wg;
   if (*n_rg > 1) {
@@ -1119,9 +1070,12 @@ static hipError_t launch_mt(const DecodeArgs& a, int mt, dim3 grid, int n_share,
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, int n_wg, bool q_f32, bool i8, hipStream_t stream) {
   const int rows_total = a.s_q * a.seg.head_count;
+  // more than 32 query rows, fp32 query, 16-bit rows, no row factors: whole
+  // rows per wave (mla_decode_rows.hip)
+  if (rows_total > 32 && q_f32 && !i8 && !a.seg.row_rinv) return launch_decode_rows(a, n_wg, stream);
   const int mt = row_tile(rows_total);
   int n_share, n_rg;
-  decode_bf16_grid(rows_total, n_wg, &n_share, &n_rg);
+  decode_bf16_grid(rows_total, mt, n_wg, &n_share, &n_rg);
   const dim3 grid(n_share * n_rg);
   // the QK-Norm and int8 variants exist for an fp32 query only (checked by the caller)
   if (q_f32 && i8) return launch_mt<true, false, true>(a, mt, grid, n_share, n_rg, rows_total, stream);

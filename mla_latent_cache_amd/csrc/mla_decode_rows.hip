@@ -1,0 +1,777 @@
+// Absorbed MLA decode over a bf16 latent cache for row groups of 64 and 128
+// query rows, gfx950: every wave owns whole query rows.
+//
+// What it computes (MLA tutorial page, "Move the Key Projection Into the
+// Query", "Position Rotations Complicate the Absorption", "Move the Value
+// Expansion After the Weighted Sum"; RedKnot-MLA abstract for the segments):
+// for each query row (token s, head h) of a segment and a contiguous range of
+// cache rows t of one request,
+//   s_t = scale * ([q_lat | q_rot] . [c_t | kr_t]),  p = softmax over the range,
+//   o_part = sum_t p_t c_t  (fp32, normalised),  lse_part = ln sum_t exp(s_t).
+//
+// Design (MI355X: 256 CUs of 4 SIMDs, 160 KiB LDS and 512 KiB of registers
+// per CU, 64-lane waves):
+//  * One workgroup of 4 waves, one per SIMD, owns MT = 64 RB query rows (all
+//    heads of a request for the segment, or a group of them); wave w owns rows
+//    16 RB w .. + 16 RB - 1 completely: its query in registers, the scores of
+//    its rows, their softmax, and their 512 output columns (RB = 2: 256
+//    accumulator registers).  Nothing crosses between waves but the cache
+//    tiles, so the only workgroup barrier is the one that recycles a ring
+//    stage, once per tile.
+//  * Cache rows stream in 32-row tiles [c_t | kr_t] (1152 B per row) HBM ->
+//    LDS with direct-to-LDS loads: a 4-stage latent ring and a 3-stage rotary
+//    ring; each wave issues a quarter of every tile's loads.  Each tile is
+//    read from HBM once and serves all MT rows: for the 128 heads of a
+//    DeepSeek-V3-style request that is every head at once.
+//  * A wave's tile step, for its 16 RB rows, on v_mfma_f32_16x16x32_bf16:
+//    QK:  S^T[32 tokens x rows] = K_tile . q^T over the 18 k-steps of [c | kr]
+//         (K operand: one 16-byte LDS read per 16 tokens per k-step, shared by
+//         the wave's RB row blocks);
+//    PV:  O^T[512 columns x rows] += C_tile^T . P^T (C^T from two
+//         ds_read_b64_tr_b16 transposed reads per 16 columns, shared by the RB
+//         row blocks).
+//    The softmax needs no data movement: the score accumulators hold, per
+//    lane, query row l % 16 and tokens 4 (l / 16) + e and 16 + 4 (l / 16) + e,
+//    and that is exactly the P^T operand of the PV product once its k order
+//    is defined as those tokens (the transposed C reads are addressed to
+//    match).
+//  * Software pipeline, per iteration `it` after the ring barrier: the QK of
+//    tile it+1, then the PV of tile it with the softmax of tile it+1 between
+//    its MFMAs (the softmax of it+1 does not feed the PV of it), then the
+//    rare lazy rescale of O.  So the score chain, the softmax's dependent
+//    VALU/transcendental chain and both products share one instruction stream
+//    per SIMD without waiting on one another.
+//  * Query precision: q_lat and q_rot arrive in fp32.  The latent part is
+//    multiplied as bf16 hi only; the rotary part as hi + lo.  With
+//    delta_t = scale (lo . c_t) the neglected part of a latent score,
+//    ln sum exp(s_t + delta_t) = lse + sum_t p_t delta_t + O(var_p delta), so
+//    the lse gains scale (lo . o) (o = the normalised weighted latent, which
+//    each wave holds for its rows), leaving a second-order error (about 1e-5
+//    at unit-variance inputs).
+//  * Softmax in the exp2 domain with lazy rescaling: the running max moves
+//    only when a tile max exceeds it by more than kRowsTau (log2 units), so
+//    the O rescale almost never runs; when it does, it runs outside the tile
+//    loop.
+//  * Work split: the segment's rows, concatenated over requests (each padded
+//    to whole tiles), are cut into equal shares, one per workgroup of a row
+//    group; a share crossing request boundaries yields several pieces, each
+//    written to its own partial slot (at most n_split per request; unused
+//    slots get lse = -inf).  The workgroup's first wave derives the pieces from
+//    seq_lens on the device.
+//  * Grid: n_share workgroups per row group; the row groups of one share sit
+//    on the same XCD (workgroups are dispatched round-robin over 8 XCDs), so
+//    the second read of a tile hits that XCD's L2.
+#include "mla_common.h"
+#include "mla_decode_tile.h"
+#include "mla_kernels.h"
+
+namespace mla {
+namespace {
+
+constexpr int kRowsThreads = 256;      // 4 waves, one per SIMD
+constexpr int kRowsWaves = kRowsThreads / 64;
+constexpr int kLatStages = 4;          // tiles it (PV), it+1 (QK), it+2, it+3 (loading)
+constexpr int kRotStages = 3;          // tiles it+1 (QK), it+2, it+3
+constexpr int kLoadAhead = 3;          // tiles issued before the first QK
+constexpr int kTileDma = kTile + kRStage / 1024;       // 36 wave-instructions per tile
+constexpr int kDmaPerWave = kTileDma / kRowsWaves;     // 9
+static_assert(kTileDma % kRowsWaves == 0, "every wave issues the same share of a tile's loads");
+constexpr int kRowsMaxPieces = 64;
+constexpr int kPvPre = 4;              // PV: column blocks of transposed reads in flight
+constexpr int kQkPre = 3;              // QK: k-steps of K-operand reads in flight
+// Lazy rescale threshold (log2 units): a row's running max moves only when a
+// tile's max exceeds it by more than this, so weights reach 2^32 at most.
+// bf16 weights and fp32 sums keep their relative precision at any magnitude
+// and stay far from overflow (2^32 times 32768 rows times the largest cache
+// entry), while the rescale of O, which leaves the tile loop, almost never
+// runs.
+constexpr float kRowsTau = 32.f;
+
+// Instruction order of the scheduling regions of a tile step, for the
+// compiler's scheduler (which otherwise issues each LDS read just before its
+// MFMA and waits for it).  Groups of instruction kinds are filled in order:
+constexpr int kSchedDs = 0x080, kSchedMfma = 0x008, kSchedValu = 0x002;
+
+struct RowsSmem {
+  char lat[kLatStages][kCStage];   // 128 KiB
+  char rot[kRotStages][kRStage];   // 12 KiB
+  // bf16 hi parts of the rotary query of the group's 128 rows (a wave uses
+  // only its own rows): rows of 128 B, chunks placed like the rotary ring's
+  char qrot[16 * 2 * kRowsWaves][kRBytes];  // 16 KiB
+  Piece pieces[kRowsMaxPieces];
+  int n_pieces;
+  int done;
+  int red[2 * kRowsWaves];
+};
+
+// Direct-to-LDS buffer load of 16 bytes per lane: LDS address = lds + 16 *
+// lane, memory address = the resource's base + voffset.  A lane whose bytes
+// lie past the resource's record count reads zeros, so a partial tile (or a
+// page outside the pool, record count 0) needs no branch and no zero-fill
+// store: its rows arrive as zeros.  Written as asm so that the compiler does
+// not order later LDS reads of *other* ring stages behind these loads (it
+// cannot tell the stages apart and would drain every load in flight); the
+// kernel waits for each tile itself (vmcnt, in order) before the barrier
+// that publishes it.  No register is written; M0 takes the LDS address, one
+// wait state before the load reads it.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+// int in the constant address space: uniform reads become scalar loads
+typedef const __attribute__((address_space(4))) int32_t CInt;
+__device__ __forceinline__ void dma16(i32x4_t rsrc, const char* lds, int voffset) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(MLA_LDS const char*)lds;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// Buffer resource over `bytes` bytes at `base` (stride 0, raw addressing;
+// the third dword is the gfx9-family data-format word).
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, int bytes) {
+  const uint64_t a = (uint64_t)base;
+  return i32x4_t{(int)(uint32_t)a, (int)(uint32_t)(a >> 32) & 0xffff, bytes, 0x00020000};
+}
+
+// One tile's loads of wave w from the rows at `src`, of which `lim` bytes
+// (whole rows) are valid; the rest read as zeros.  Wave w fills latent rows
+// k = w + 4 i (i < 8; lane l moves the chunk stored at position l, i.e.
+// chunk l ^ (k & 15)) and rotary rows 8 w + l / 8 (lane l: position l % 8,
+// chunk (l % 8) ^ ((r >> 1) & 7)).
+__device__ __forceinline__ void load_tile_part(char* lat, char* rot, const char* src, int lim, int w, int lane) {
+  const i32x4_t rsrc = buffer_rsrc(src, lim);
+  // opaque lane copy: the offsets are recomputed per instruction instead of
+  // being hoisted into registers held across the tile loop
+  asm volatile("" : "+v"(lane));
+#pragma unroll
+  for (int i = 0; i < kTile / kRowsWaves; ++i) {
+    const int k = w + kRowsWaves * i;
+    dma16(rsrc, lat + k * kCBytes, k * kRowBytes + (cpos(k, lane) << 4));
+  }
+  const int r = 8 * w + (lane >> 3);
+  dma16(rsrc, rot + w * 1024, r * kRowBytes + kCBytes + (rpos(r, lane & 7) << 4));
+}
+
+// Scores of one tile for the wave's RB row blocks: S^T[32 tokens x 16 rows]
+// per block as two 16-token halves.  ls / rs: the tile's latent and rotary
+// stages (restrict: the compiler may then order these reads freely against
+// the direct-to-LDS loads in flight to other stages).  Per-lane LDS address
+// parts, from an opaque copy of the lane index (so none is held across the
+// loop): K operand of latent k-step ks = 4 a + n, rows 16 tb + l16, chunk
+// 4 ks + lg, sits at position (4 ks + lg) ^ l16 = 16 a + 4 (n ^ (l16 >> 2)) +
+// (lg ^ (l16 & 3)); rotary k-step jr: chunk 4 jr + lg at (4 jr + lg) ^
+// ((l16 >> 1) & 7).  Rows 16 + l16 share the swizzle key of row l16.
+template <int RB>
+__device__ __forceinline__ void qk_tile(const char* __restrict__ ls, const char* __restrict__ rs,
+                                        const char* __restrict__ qs, int lane, const bf16x8 (&qh)[RB][kDc / 32],
+                                        const bf16x8 (&qrl)[RB][2], f32x4 (&s)[2][RB]) {
+  asm volatile("" : "+v"(lane));
+  const int xl = lane & 15, xg = lane >> 4;
+  const char* kb[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) kb[n] = ls + xl * kCBytes + ((n ^ (xl >> 2)) << 6) + ((xg ^ (xl & 3)) << 4);
+  const char* rb0 = rs + xl * kRBytes;
+  const int xr = (xl >> 1) & 7;
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) s[tb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // K operands of k-step ks (ks < 16 latent, then 2 rotary), read kPre
+  // k-steps ahead of their MFMAs
+  auto kop = [&](int ks, int tb) -> bf16x8 {
+    if (ks < kDc / 32) return *(const bf16x8*)(kb[ks & 3] + (ks >> 2) * 256 + tb * 16 * kCBytes);
+    return *(const bf16x8*)(rb0 + (((4 * (ks - kDc / 32) + xg) ^ xr) << 4) + tb * 16 * kRBytes);
+  };
+  constexpr int kPre = kQkPre;
+  bf16x8 ka[kPre + 1][2];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) {
+    ka[i][0] = kop(i, 0);
+    ka[i][1] = kop(i, 1);
+  }
+#pragma unroll
+  for (int ks = 0; ks < kKSteps; ++ks) {
+    if (ks + kPre < kKSteps) {
+      ka[(ks + kPre) % (kPre + 1)][0] = kop(ks + kPre, 0);
+      ka[(ks + kPre) % (kPre + 1)][1] = kop(ks + kPre, 1);
+    }
+    const bf16x8 k0 = ka[ks % (kPre + 1)][0], k1 = ka[ks % (kPre + 1)][1];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if (ks < kDc / 32) {
+        s[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qh[rb][ks], s[0][rb], 0, 0, 0);
+        s[1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qh[rb][ks], s[1][rb], 0, 0, 0);
+      } else {
+        const int jr = ks - kDc / 32;
+        // the rotary query's hi part from LDS: row 16 rb + l16 of the wave's
+        // rows, chunk 4 jr + lg (placed like the rotary ring)
+        const int qr = 16 * rb + xl;
+        const bf16x8 qrh = *(const bf16x8*)(qs + qr * kRBytes + (rpos(qr, 4 * jr + xg) << 4));
+        s[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qrh, s[0][rb], 0, 0, 0);
+        s[1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qrh, s[1][rb], 0, 0, 0);
+        s[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qrl[rb][jr], s[0][rb], 0, 0, 0);
+        s[1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qrl[rb][jr], s[1][rb], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// O^T[512 columns x 16 rows] += C^T . P^T for the wave's RB row blocks.  The
+// P^T operand of lane l holds its row's weights of tokens 4 lg + e (k = 8 lg
+// + e) and 16 + 4 lg + e (k = 8 lg + 4 + e), exactly the lane's score
+// registers; the C^T operand of column block db is read to match: the first
+// transposed read of lane (lg, rq, qq) addresses tile row x = 4 lg + rq, the
+// second row x + 16 (same swizzle key), columns 16 db + 4 qq .. + 3, i.e.
+// chunk 2 db + (qq >> 1) at position 2 (db ^ (x >> 1)) + ((qq >> 1) ^ (x & 1)),
+// byte 8 (qq & 1) within it; each 16-lane group then holds C[rows][16 db + l16].
+template <int RB>
+__device__ __forceinline__ void pv_tile(const char* __restrict__ ls, int lane, const bf16x8 (&p)[RB],
+                                        f32x4 (&acc)[32][RB]) {
+  asm volatile("" : "+v"(lane));
+  const int qq = lane & 3, rq = (lane >> 2) & 3, xg = lane >> 4;
+  const int xr = 4 * xg + rq;
+  const char* cb = ls + xr * kCBytes + 8 * (qq & 1) + 16 * ((qq >> 1) ^ (xr & 1));
+  const int xh = xr >> 1;
+  auto cop = [&](int db) -> bf16x8 {
+    const char* pa = cb + 256 * (db >> 3) + (((db & 7) ^ xh) << 5);
+    const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(pa));
+    const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(pa + 16 * kCBytes));
+    return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  // C^T operands read kPvPre column blocks ahead of their MFMAs
+  constexpr int kPre = kPvPre;
+  bf16x8 ca[kPre + 1];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) ca[i] = cop(i);
+#pragma unroll
+  for (int db = 0; db < 32; ++db) {
+    if (db + kPre < 32) ca[(db + kPre) % (kPre + 1)] = cop(db + kPre);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      acc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[db % (kPre + 1)], p[rb], acc[db][rb], 0, 0, 0);
+      asm("" : "+a"(acc[db][rb]));  // the accumulators live in AGPRs throughout
+    }
+  }
+}
+
+// Online softmax of one tile's scores (exp2 domain, lazy rescale): the P^T
+// operands (bf16), the factor each row's O must take and whether any row of
+// the wave moved its max.  Tokens past the piece or the row's causal limit
+// (relative index `lim` per lane: token 4 lg + e of the first half is
+// visible when e <= lim) get weight 0.  Branch-free, so it can be scheduled
+// between the MFMAs of the product before it.
+template <int RB>
+__device__ __forceinline__ bool softmax_tile(const f32x4 (&s)[2][RB], float sl2, const int (&lim)[RB],
+                                             float (&m_used)[RB], float (&l_part)[RB], bf16x8 (&p)[RB],
+                                             float (&alpha)[RB]) {
+  bool need_any = false;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    f32x4 sa = s[0][rb] * sl2, sb = s[1][rb] * sl2;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sa[e] = e <= lim[rb] ? sa[e] : -INFINITY;
+      sb[e] = 16 + e <= lim[rb] ? sb[e] : -INFINITY;
+    }
+    float mt = fmaxf(fmaxf(fmaxf(sa[0], sa[1]), fmaxf(sa[2], sa[3])), fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3])));
+    mt = rows_max(mt);
+    const bool need = mt > m_used[rb] + kRowsTau;
+    const float al = need ? __builtin_amdgcn_exp2f(m_used[rb] - mt) : 1.f;  // 0 when m_used was -inf
+    m_used[rb] = need ? mt : m_used[rb];
+    alpha[rb] = al;
+    need_any |= need;
+    const float msub = m_used[rb] == -INFINITY ? 0.f : m_used[rb];
+    float lsum = 0.f;
+    bf16x8 pv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p0 = __builtin_amdgcn_exp2f(sa[e] - msub);  // exp2(-inf) = 0
+      const float p1 = __builtin_amdgcn_exp2f(sb[e] - msub);
+      lsum += p0 + p1;
+      pv[e] = (bf16)p0;
+      pv[4 + e] = (bf16)p1;
+    }
+    l_part[rb] = l_part[rb] * al + lsum;
+    p[rb] = pv;
+  }
+  return __ballot(need_any) != 0;
+}
+
+// O *= alpha (per row) in place in the accumulator registers, for the rare
+// tile whose softmax moved a row's max.  Each entry is read, scaled and
+// written back by one asm block, so the accumulators never leave their
+// registers (a plain vector multiply would make the compiler hold them in
+// vector registers across the whole tile loop).  The MFMAs that last wrote
+// them are waited out first (the longest MFMA-result-to-read distance is
+// 19 wait states).
+template <int RB>
+__device__ __forceinline__ void scale_acc(f32x4 (&acc)[32][RB], const float (&alpha)[RB]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int db = 0; db < 32; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = acc[db][rb][e];
+        float t;
+        asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\ts_nop 1\n\tv_accvgpr_write_b32 %0, %1"
+                     : "+a"(x), "=&v"(t) : "v"(alpha[rb]));
+        acc[db][rb][e] = x;
+      }
+}
+
+// Scores: the K operands of kQkPre k-steps ahead are in flight while a k-step's
+// MFMAs issue (4 per k-step per row block pair, twice that on the two rotary
+// k-steps, which multiply the hi and lo query parts).
+template <int RB>
+__device__ __forceinline__ void sched_qk() {
+  __builtin_amdgcn_sched_group_barrier(kSchedDs, 2 * kQkPre, 0);
+#pragma unroll
+  for (int ks = 0; ks < kDc / 32; ++ks) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * RB, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDs, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedDs, RB, 0);
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4 * RB, 0);
+  __builtin_amdgcn_sched_group_barrier(kSchedDs, RB, 0);
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4 * RB, 0);
+}
+
+// PV of one tile: the transposed reads of the next column blocks are in
+// flight while a block's RB MFMAs issue.  (The next tile's softmax follows
+// the MFMAs; vector-ALU groups between them make the scheduler drop the
+// pattern.)
+template <int RB>
+__device__ __forceinline__ void sched_pv() {
+  __builtin_amdgcn_sched_group_barrier(kSchedDs, 2 * kPvPre, 0);
+#pragma unroll
+  for (int db = 0; db < 32; ++db) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, RB, 0);
+    if (db + kPvPre < 32) __builtin_amdgcn_sched_group_barrier(kSchedDs, 2, 0);
+  }
+}
+
+}  // namespace
+
+// RB: 16-row blocks per wave (1: 64-row groups, 2: 128-row groups).
+template <int RB>
+__global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(DecodeArgs a, int n_share, int n_rg,
+                                                                      int rows_total) {
+  constexpr int MT = 16 * RB * kRowsWaves;  // query rows of a row group
+  __shared__ __attribute__((aligned(16))) RowsSmem sm;
+
+  const char* const cache = (const char*)a.seg.cache;
+  const int32_t* const block_table = a.seg.block_table;
+  const int32_t* const seq_lens = a.seg.seq_lens;
+  const float* const q_rot = (const float*)a.seg.q_rot;
+  const float* const q_lat = (const float*)a.q_lat;
+  float* const o_part = a.o_part;
+  float* const lse_part = a.lse_part;
+  const int64_t max_rows = a.seg.max_rows;
+  const int max_pages = a.seg.max_pages;
+  const int n_pages = a.seg.n_pages;
+  const int head_begin = a.seg.head_begin;
+  const int hc = a.seg.head_count;
+  const int causal = a.seg.causal;
+  const int part_begin = a.seg.part_begin;
+  const int n_split = a.seg.n_split;
+  const int s_q = a.s_q;
+  const int n_heads = a.n_heads;
+  const int n_part = a.n_part;
+  const int B = a.batch;
+  const float scale = a.scale;
+  const float sl2 = scale * kLog2e;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int l16 = lane & 15;
+  const int lg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // ---- which share / row group this workgroup owns (XCD-aware order) ----
+  int j, rg;
+  if (n_rg == 1) {
+    j = blockIdx.x;
+    rg = 0;
+  } else {
+    rg = (blockIdx.x / 8) % n_rg;
+    j = (blockIdx.x / (8 * n_rg)) * 8 + blockIdx.x % 8;
+  }
+  const int row0 = rg * MT;
+  const int nrows = min(MT, rows_total - row0);
+  const int wrow0 = 16 * RB * wave;            // first row of this wave within the group
+  const bool wave_rows = wrow0 < nrows;        // wave-uniform: the wave has query rows (it computes
+                                               // either way; only a wave with rows stores results)
+  const int64_t cap = block_table ? (int64_t)max_pages * kPageSize : max_rows;
+  auto clampT = [cap](int t) -> int { return (int)max((int64_t)0, min((int64_t)t, cap)); };
+  auto padT = [](int t) -> int { return (t + kTile - 1) / kTile * kTile; };
+
+  // ---- plan pass 1: total and longest request, each padded to whole tiles ----
+  int tsum = 0, tmax = 0;
+  int Tr_lane = 0;
+  if (B <= 64) {
+    if (wave == 0) {
+      Tr_lane = lane < B ? clampT(seq_lens[lane]) : 0;
+      tsum = padT(Tr_lane);
+      tmax = tsum;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        tsum += __shfl_xor(tsum, o);
+        tmax = max(tmax, __shfl_xor(tmax, o));
+      }
+    }
+  } else {
+    for (int b = tid; b < B; b += kRowsThreads) {
+      const int T = padT(clampT(seq_lens[b]));
+      tsum += T;
+      tmax = max(tmax, T);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      tsum += __shfl_xor(tsum, o);
+      tmax = max(tmax, __shfl_xor(tmax, o));
+    }
+    if (lane == 0) {
+      sm.red[wave] = tsum;
+      sm.red[kRowsWaves + wave] = tmax;
+    }
+    __syncthreads();
+    tsum = 0;
+    tmax = 0;
+#pragma unroll
+    for (int w = 0; w < kRowsWaves; ++w) {
+      tsum += sm.red[w];
+      tmax = max(tmax, sm.red[kRowsWaves + w]);
+    }
+  }
+  const bool req_mode = n_split == 1;
+  int share = 0;
+  if (!req_mode) {
+    share = (tsum + n_share - 1) / n_share;
+    share = max(share, (tmax + n_split - 2) / (n_split - 1));
+    share = max(kTile, (share + kTile - 1) / kTile * kTile);
+  }
+  const int lo = j * share, hi = lo + share;
+
+  // ---- this wave's query rows: block rb, lane row l16 (recomputed where
+  // used, from an opaque lane copy, so nothing of it is held across the
+  // tile loop) ----
+  struct RowInfo {
+    bool valid;    // the row exists
+    int tok;       // query token within the request
+    int64_t qoff;  // token * n_heads + head, without the request part
+  };
+  auto row_info = [&](int rb) -> RowInfo {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int r = wrow0 + 16 * rb + (ln & 15);
+    const bool valid = r < nrows;
+    const int Rr = row0 + (valid ? r : 0);  // a row past the group stands in for row0
+    const int tok = Rr / hc;
+    return RowInfo{valid, tok, (int64_t)tok * n_heads + head_begin + Rr % hc};
+  };
+
+  int base = 0;  // prefix of padded T over the requests scanned so far (wave 0)
+  for (int chunk = 0;; ++chunk) {
+    // ---- plan pass 2: wave 0 scans 64 requests, lists pieces, writes -inf tails ----
+    if (wave == 0) {
+      const int b = chunk * 64 + lane;
+      const int Tr = B <= 64 ? Tr_lane : b < B ? clampT(seq_lens[b]) : 0;
+      const int T = padT(Tr);
+      int incl = T;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o);
+        if (lane >= o) incl += v;
+      }
+      const int S = base + incl - T;
+      bool is_piece, tail;
+      int r0 = 0, r1 = 0, slot = 0, cnt = 0;
+      if (req_mode) {
+        is_piece = b < B && T > 0 && (b % n_share) == j;
+        r1 = Tr;
+        tail = b < B && T == 0 && (b % n_share) == j;
+      } else {
+        is_piece = b < B && T > 0 && S < hi && S + T > lo;
+        r0 = max(lo, S) - S;
+        r1 = min(min(hi, S + T) - S, Tr);
+        slot = j - S / share;
+        const int jf = min(S / share, n_share - 1);
+        cnt = T > 0 ? (S + T - 1) / share - S / share + 1 : 0;
+        tail = b < B && jf == j && cnt < n_split;
+      }
+      const uint64_t pm = __ballot(is_piece);
+      if (is_piece) {
+        const int pos = __popcll(pm & ((1ull << lane) - 1));
+        sm.pieces[pos] = Piece{b | (slot << 16), r0, r1, Tr};
+      }
+      // slots a request does not use: lse = -inf (their o_part rows are never read)
+      uint64_t tm = __ballot(tail);
+      while (tm) {
+        const int src = __ffsll((long long)tm) - 1;
+        tm &= tm - 1;
+        const int tb_ = __shfl(b, src);
+        const int tc = __shfl(cnt, src);
+        const int nsl = n_split - tc;
+        for (int e = lane; e < nsl * nrows; e += 64) {
+          const int k = tc + e / nrows;
+          const int Rr = row0 + e % nrows;
+          const int tok = tb_ * s_q + Rr / hc;
+          const int h = head_begin + Rr % hc;
+          lse_part[((int64_t)tok * n_heads + h) * n_part + part_begin + k] = -INFINITY;
+        }
+      }
+      const int total = __shfl(incl, 63);
+      if (lane == 0) {
+        sm.n_pieces = __popcll(pm);
+        const bool past = !req_mode && base + total >= hi && j < n_share - 1;
+        sm.done = (chunk * 64 + 64 >= B) || past;
+      }
+      base += total;
+    }
+    __syncthreads();
+    const int n_pieces = sm.n_pieces;
+    const int done = sm.done;
+
+    for (int pi = 0; pi < n_pieces; ++pi) {
+      const Piece pc = sm.pieces[pi];
+      const int b_slot = __builtin_amdgcn_readfirstlane(pc.b_slot);
+      const int b = b_slot & 0xffff;
+      const int slot = (int)((unsigned)b_slot >> 16);
+      const int pr0 = __builtin_amdgcn_readfirstlane(pc.r0);
+      const int pr1 = __builtin_amdgcn_readfirstlane(pc.r1);
+      const int T = __builtin_amdgcn_readfirstlane(pc.T);
+      const int n_tiles = (pr1 - pr0 + kTile - 1) / kTile;
+      // last visible row of each of this lane's query rows
+      int vis[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) vis[rb] = causal ? T - s_q + row_info(rb).tok : T - 1;
+
+      const char* const req_base = cache + (int64_t)b * max_rows * kRowBytes;
+      // block-table row of the request, read with scalar loads (the table is
+      // constant for the launch): a tile's page id is requested one
+      // iteration before its loads are issued, so the round trip is hidden
+      const CInt* const bt_row = block_table ? (const CInt*)(block_table + (int64_t)b * max_pages) : nullptr;
+      auto page_of = [&](int it) -> int { return bt_row[(pr0 + it * kTile) / kPageSize]; };
+      auto load_tile = [&](int it, int pg) {
+        const int t0 = pr0 + it * kTile;
+        const char* src;
+        bool ok = true;
+        if (!bt_row) {
+          src = req_base + (int64_t)t0 * kRowBytes;
+        } else {
+          ok = pg >= 0 && pg < n_pages;
+          src = cache + ((int64_t)(ok ? pg : 0) * kPageSize + (t0 % kPageSize)) * kRowBytes;
+        }
+        const int lim = ok ? min(kTile, pr1 - t0) * kRowBytes : 0;
+        load_tile_part(sm.lat[it % kLatStages], sm.rot[it % kRotStages], src, lim, wave, lane);
+      };
+      // wait until this wave's loads of tile `need` have landed, given that
+      // tiles up to `issued` are issued (the later ones may stay in flight;
+      // every tile, partial or not, is kDmaPerWave loads per wave, and they
+      // complete in order)
+      auto wait_tile = [&](int need, int issued) {
+        const int after = min(issued, n_tiles - 1) - need;
+        if (after <= 0) {
+          wait_vmcnt<0>();
+        } else if (after == 1) {
+          wait_vmcnt<kDmaPerWave>();
+        } else {
+          wait_vmcnt<2 * kDmaPerWave>();
+        }
+      };
+
+      int pg_next = 0;  // page of the next tile to load (paged layout)
+      // ---- the first tiles go out before the query loads ----
+      {
+        int pg[kLoadAhead + 1];
+#pragma unroll
+        for (int t = 0; t <= kLoadAhead; ++t) pg[t] = bt_row && t < n_tiles ? page_of(t) : 0;
+#pragma unroll
+        for (int t = 0; t < kLoadAhead; ++t)
+          if (t < n_tiles) load_tile(t, pg[t]);
+        pg_next = pg[kLoadAhead];
+      }
+
+      // ---- query: latent hi parts, rotary hi + lo parts (B operands) ----
+      bf16x8 qh[RB][kDc / 32];
+      bf16x8 qrl[RB][2];
+      char* const qrot_w = sm.qrot[16 * RB * wave];  // this wave's rows
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const RowInfo ri = row_info(rb);
+        const int64_t qi = (int64_t)b * s_q * n_heads + ri.qoff;
+        const float* ql = q_lat + qi * kDc + 8 * lg;
+        const float* qr = q_rot + qi * kDr + 8 * lg;
+        // two batches of 9 k-steps: the 18 loads of a batch go out together
+        // (unconditional: a row past the group reads row0's query and is
+        // zeroed), then their conversions, each pinned where it is formed so
+        // the fp32 staging registers die before the next batch
+        constexpr int kBatch = kKSteps / 2;
+#pragma unroll
+        for (int k0 = 0; k0 < kKSteps; k0 += kBatch) {
+          f32x4 v[kBatch][2];
+#pragma unroll
+          for (int i = 0; i < kBatch; ++i) {
+            const int ks = k0 + i;
+            const float* src = ks < kDc / 32 ? ql + 32 * ks : qr + 32 * (ks - kDc / 32);
+            v[i][0] = *(const f32x4*)src;
+            v[i][1] = *(const f32x4*)(src + 4);
+          }
+#pragma unroll
+          for (int i = 0; i < kBatch; ++i) {
+            const int ks = k0 + i;
+            if (!ri.valid) v[i][0] = v[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+            bf16x8 h8, l8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float x = v[i][e >> 2][e & 3];
+              const bf16 h = (bf16)x;
+              h8[e] = h;
+              l8[e] = (bf16)(x - (float)h);
+            }
+            if (ks < kDc / 32) {
+              qh[rb][ks] = h8;
+              asm volatile("" ::"v"(h8));
+            } else {
+              const int jr = ks - kDc / 32, qr2 = 16 * rb + l16;
+              *(bf16x8*)(qrot_w + qr2 * kRBytes + (rpos(qr2, 4 * jr + lg) << 4)) = h8;
+              qrl[rb][jr] = l8;
+              asm volatile("" ::"v"(l8));
+            }
+          }
+        }
+      }
+
+      f32x4 acc[32][RB];  // O^T: lane holds columns 16 db + 4 lg + e of row (rb, l16)
+#pragma unroll
+      for (int db = 0; db < 32; ++db)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          acc[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          asm("" : "+a"(acc[db][rb]));
+        }
+      float m_used[RB], l_part[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        m_used[rb] = -INFINITY;
+        l_part[rb] = 0.f;
+      }
+
+      // relative index of the last visible token of tile `it` for each row
+      // block, as the masked softmax takes it (block 0 of the tile: e <= lim)
+      auto tile_lim = [&](int it, int (&lim)[RB]) {
+        const int t0 = pr0 + it * kTile;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) lim[rb] = min(pr1 - 1, vis[rb]) - t0 - 4 * lg;
+      };
+
+      f32x4 sacc[2][RB];
+      bf16x8 p[RB];
+      float alpha[RB];
+      int lim[RB];
+      // ---- tile 0: scores and softmax ----
+      wait_tile(0, kLoadAhead - 1);
+      wait_lgkm0();
+      barrier_raw();
+      qk_tile<RB>(sm.lat[0], sm.rot[0], qrot_w, lane, qh, qrl, sacc);
+      tile_lim(0, lim);
+      softmax_tile<RB>(sacc, sl2, lim, m_used, l_part, p, alpha);  // (its factor multiplies an empty O)
+      for (int it = 0; it + 1 < n_tiles; ++it) {
+        // tile it+1 in LDS (this wave's loads, then everyone's); every wave is
+        // past the PV of tile it-1 and the scores of tile it, so their stages
+        // take tile it+3
+        wait_tile(it + 1, it + kLoadAhead - 1);
+        wait_lgkm0();
+        barrier_raw();
+        if (it + kLoadAhead < n_tiles) {
+          load_tile(it + kLoadAhead, pg_next);
+          // the page of the tile after it, used next iteration
+          if (bt_row && it + kLoadAhead + 1 < n_tiles) pg_next = page_of(it + kLoadAhead + 1);
+        }
+        // the scores of tile it+1, then the PV of tile it with the softmax of
+        // tile it+1 free to go between its MFMAs (it reads only the scores)
+        tile_lim(it + 1, lim);
+        qk_tile<RB>(sm.lat[(it + 1) % kLatStages], sm.rot[(it + 1) % kRotStages], qrot_w, lane, qh, qrl, sacc);
+        sched_qk<RB>();
+        // the softmax of tile it+1 (its scores die here: only the two tiles'
+        // P operands live across the PV product), then the PV of tile it
+        bf16x8 pn[RB];
+        const bool moved = softmax_tile<RB>(sacc, sl2, lim, m_used, l_part, pn, alpha);
+        __builtin_amdgcn_sched_barrier(0);
+        pv_tile<RB>(sm.lat[it % kLatStages], lane, p, acc);
+        sched_pv<RB>();
+        __builtin_amdgcn_sched_barrier(0);
+        if (moved) scale_acc<RB>(acc, alpha);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) p[rb] = pn[rb];
+      }
+      // the last tile's PV
+      wait_lgkm0();
+      barrier_raw();
+      pv_tile<RB>(sm.lat[(n_tiles - 1) % kLatStages], lane, p, acc);
+
+      // ---- epilogue: 1/l, the lse with the latent lo part's first-order
+      // share, the normalised partial output.  Every load and product comes
+      // before the first store: a store is counted until written, so a load
+      // after it would wait for the write too. ----
+      if (wave_rows) {
+        float lt[RB], cs[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          lt[rb] = rows_sum(l_part[rb]);
+          // sum_d lo_d acc_d over this lane's columns 16 db + 4 lg + e; the
+          // 32 query loads go out together (a row past the group reads
+          // row0's query), then the products
+          const RowInfo ri = row_info(rb);
+          const float* ql = q_lat + ((int64_t)b * s_q * n_heads + ri.qoff) * kDc + 4 * lg;
+          f32x4 qv[32];
+#pragma unroll
+          for (int db = 0; db < 32; ++db) qv[db] = *(const f32x4*)(ql + 16 * db);
+          __builtin_amdgcn_sched_barrier(0);
+          float c = 0.f;
+#pragma unroll
+          for (int db = 0; db < 32; ++db)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) c += (float)(bf16)(qv[db][e] - (float)(bf16)qv[db][e]) * acc[db][rb][e];
+          cs[rb] = rows_sum(c);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const float linv = lt[rb] > 0.f ? 1.f / lt[rb] : 0.f;
+          const RowInfo ri = row_info(rb);
+          const int64_t lse_i = ((int64_t)b * s_q * n_heads + ri.qoff) * n_part + part_begin + slot;
+          if (ri.valid && lg == 0)
+            lse_part[lse_i] = lt[rb] > 0.f ? (m_used[rb] + __log2f(lt[rb])) * kLn2 + scale * linv * cs[rb] : -INFINITY;
+          if (ri.valid && lt[rb] > 0.f) {
+            float* o = o_part + lse_i * kDc + 4 * lg;
+#pragma unroll
+            for (int db = 0; db < 32; ++db) *(f32x4*)(o + 16 * db) = acc[db][rb] * linv;
+          }
+        }
+      }
+      wait_lgkm0();
+      barrier_raw();  // every wave is past its last reads of the ring before the next piece loads
+    }
+    __syncthreads();
+    if (done) break;
+  }
+}
+
+template __global__ void decode_rows_kernel<1>(DecodeArgs, int, int, int);
+template __global__ void decode_rows_kernel<2>(DecodeArgs, int, int, int);
+
+int decode_rows_tile(int rows_total) { return rows_total <= 64 ? 64 : 128; }
+
+hipError_t launch_decode_rows(const DecodeArgs& a, int n_wg, hipStream_t stream) {
+  const int rows_total = a.s_q * a.seg.head_count;
+  const int mt = decode_rows_tile(rows_total);
+  int n_share, n_rg;
+  decode_bf16_grid(rows_total, mt, n_wg, &n_share, &n_rg);
+  const dim3 grid(n_share * n_rg), block(kRowsThreads);
+  if (mt == 64) return launch(decode_rows_kernel<1>, grid, block, stream, a, n_share, n_rg, rows_total);
+  return launch(decode_rows_kernel<2>, grid, block, stream, a, n_share, n_rg, rows_total);
+}
+
+}  // namespace mla

@@ -101,7 +101,18 @@ hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
 // q_f32: q_lat / q_rot are fp32 (split into bf16 hi + lo) instead of bf16.
 // i8: the cache rows are int8 latent codes (scale seg.row_scale) + bf16 rotary keys.
 hipError_t launch_decode_bf16(const DecodeArgs& a, int n_wg, bool q_f32, bool i8, hipStream_t stream);
-// Grid shape of the bf16 decode for one segment: row groups and shares.
-void decode_bf16_grid(int rows_total, int n_wg, int* n_share, int* n_rg);
+// Grid shape of a bf16 decode of one segment with row groups of mt rows:
+// row groups and shares (n_wg workgroups per row group, a multiple of 8 when
+// there are several row groups).
+void decode_bf16_grid(int rows_total, int mt, int n_wg, int* n_share, int* n_rg);
+// Rows of the row group the bf16 decode uses for a segment (the kernel
+// chosen by launch_decode_bf16 for an fp32 query and a 16-bit cache).
+int decode_bf16_tile(int rows_total);
+// bf16 MFMA decode with whole query rows per wave, for segments of more than
+// 32 query rows with an fp32 query, a 16-bit cache and no QK-Norm factors:
+// row groups of 64 (up to 64 rows) or 128; n_wg workgroups per row group.
+hipError_t launch_decode_rows(const DecodeArgs& a, int n_wg, hipStream_t stream);
+// Rows of that kernel's row group for a segment of rows_total query rows.
+int decode_rows_tile(int rows_total);
 
 }  // namespace mla
