@@ -76,6 +76,7 @@ constexpr int kLoadAhead = 3;          // tiles issued before the first QK
 constexpr int kTileDma = kTile + kRStage / 1024;       // 36 wave-instructions per tile
 constexpr int kDmaPerWave = kTileDma / kRowsWaves;     // 9
 static_assert(kTileDma % kRowsWaves == 0, "every wave issues the same share of a tile's loads");
+static_assert(kKSteps / 2 == kDmaPerWave, "one load of the next tile after every second score k-step");
 constexpr int kRowsMaxPieces = 64;
 constexpr int kPvPre = 4;              // PV: column blocks of transposed reads in flight
 constexpr int kQkPre = 3;              // QK: k-steps of K-operand reads in flight
@@ -132,23 +133,22 @@ __device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, int bytes) {
   return i32x4_t{(int)(uint32_t)a, (int)(uint32_t)(a >> 32) & 0xffff, bytes, 0x00020000};
 }
 
-// One tile's loads of wave w from the rows at `src`, of which `lim` bytes
-// (whole rows) are valid; the rest read as zeros.  Wave w fills latent rows
-// k = w + 4 i (i < 8; lane l moves the chunk stored at position l, i.e.
-// chunk l ^ (k & 15)) and rotary rows 8 w + l / 8 (lane l: position l % 8,
-// chunk (l % 8) ^ ((r >> 1) & 7)).
-__device__ __forceinline__ void load_tile_part(char* lat, char* rot, const char* src, int lim, int w, int lane) {
-  const i32x4_t rsrc = buffer_rsrc(src, lim);
+// Load i (< kDmaPerWave) of wave w's share of one tile, from the rows that
+// `rsrc` covers (rows past its record count read as zeros).  Wave w fills
+// latent rows k = w + 4 i (i < 8; lane l moves the chunk stored at position
+// l, i.e. chunk l ^ (k & 15)) and, as its last load, rotary rows 8 w + l / 8
+// (lane l: position l % 8, chunk (l % 8) ^ ((r >> 1) & 7)).
+__device__ __forceinline__ void tile_load(i32x4_t rsrc, char* lat, char* rot, int w, int lane, int i) {
   // opaque lane copy: the offsets are recomputed per instruction instead of
   // being hoisted into registers held across the tile loop
   asm volatile("" : "+v"(lane));
-#pragma unroll
-  for (int i = 0; i < kTile / kRowsWaves; ++i) {
+  if (i < kTile / kRowsWaves) {
     const int k = w + kRowsWaves * i;
     dma16(rsrc, lat + k * kCBytes, k * kRowBytes + (cpos(k, lane) << 4));
+  } else {
+    const int r = 8 * w + (lane >> 3);
+    dma16(rsrc, rot + w * 1024, r * kRowBytes + kCBytes + (rpos(r, lane & 7) << 4));
   }
-  const int r = 8 * w + (lane >> 3);
-  dma16(rsrc, rot + w * 1024, r * kRowBytes + kCBytes + (rpos(r, lane & 7) << 4));
 }
 
 // Scores of one tile for the wave's RB row blocks: S^T[32 tokens x 16 rows]
@@ -160,10 +160,13 @@ __device__ __forceinline__ void load_tile_part(char* lat, char* rot, const char*
 // 4 ks + lg, sits at position (4 ks + lg) ^ l16 = 16 a + 4 (n ^ (l16 >> 2)) +
 // (lg ^ (l16 & 3)); rotary k-step jr: chunk 4 jr + lg at (4 jr + lg) ^
 // ((l16 >> 1) & 7).  Rows 16 + l16 share the swizzle key of row l16.
-template <int RB>
+// `load(i)` issues load i of the next tile's share after the MFMAs of k-step
+// 2 i + 1, so the nine loads spread over the product instead of queueing
+// behind one another.
+template <int RB, class Load>
 __device__ __forceinline__ void qk_tile(const char* __restrict__ ls, const char* __restrict__ rs,
                                         const char* __restrict__ qs, int lane, const bf16x8 (&qh)[RB][kDc / 32],
-                                        const bf16x8 (&qrl)[RB][2], f32x4 (&s)[2][RB]) {
+                                        const bf16x8 (&qrl)[RB][2], f32x4 (&s)[2][RB], const Load& load) {
   asm volatile("" : "+v"(lane));
   const int xl = lane & 15, xg = lane >> 4;
   const char* kb[4];
@@ -212,6 +215,7 @@ __device__ __forceinline__ void qk_tile(const char* __restrict__ ls, const char*
         s[1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qrl[rb][jr], s[1][rb], 0, 0, 0);
       }
     }
+    if (ks % 2 == 1) load(ks / 2);
   }
 }
 
@@ -553,32 +557,22 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(DecodeArgs
       // iteration before its loads are issued, so the round trip is hidden
       const CInt* const bt_row = block_table ? (const CInt*)(block_table + (int64_t)b * max_pages) : nullptr;
       auto page_of = [&](int it) -> int { return bt_row[(pr0 + it * kTile) / kPageSize]; };
-      auto load_tile = [&](int it, int pg) {
+      // resource over the rows of tile `it` (page `pg` in the paged layout);
+      // a tile past the piece, or on a page outside the pool, gets record
+      // count 0 and reads as zeros.  Every tile index, past the piece or not,
+      // gets its kDmaPerWave loads per wave, so the loads in flight are
+      // counted the same way in every iteration (they complete in order).
+      auto tile_rsrc = [&](int it, int pg) -> i32x4_t {
         const int t0 = pr0 + it * kTile;
         const char* src;
-        bool ok = true;
+        bool ok = it < n_tiles;
         if (!bt_row) {
           src = req_base + (int64_t)t0 * kRowBytes;
         } else {
-          ok = pg >= 0 && pg < n_pages;
+          ok = ok && pg >= 0 && pg < n_pages;
           src = cache + ((int64_t)(ok ? pg : 0) * kPageSize + (t0 % kPageSize)) * kRowBytes;
         }
-        const int lim = ok ? min(kTile, pr1 - t0) * kRowBytes : 0;
-        load_tile_part(sm.lat[it % kLatStages], sm.rot[it % kRotStages], src, lim, wave, lane);
-      };
-      // wait until this wave's loads of tile `need` have landed, given that
-      // tiles up to `issued` are issued (the later ones may stay in flight;
-      // every tile, partial or not, is kDmaPerWave loads per wave, and they
-      // complete in order)
-      auto wait_tile = [&](int need, int issued) {
-        const int after = min(issued, n_tiles - 1) - need;
-        if (after <= 0) {
-          wait_vmcnt<0>();
-        } else if (after == 1) {
-          wait_vmcnt<kDmaPerWave>();
-        } else {
-          wait_vmcnt<2 * kDmaPerWave>();
-        }
+        return buffer_rsrc(ok ? src : cache, ok ? min(kTile, pr1 - t0) * kRowBytes : 0);
       };
 
       int pg_next = 0;  // page of the next tile to load (paged layout)
@@ -588,8 +582,11 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(DecodeArgs
 #pragma unroll
         for (int t = 0; t <= kLoadAhead; ++t) pg[t] = bt_row && t < n_tiles ? page_of(t) : 0;
 #pragma unroll
-        for (int t = 0; t < kLoadAhead; ++t)
-          if (t < n_tiles) load_tile(t, pg[t]);
+        for (int t = 0; t < kLoadAhead; ++t) {
+          const i32x4_t rs = tile_rsrc(t, pg[t]);
+#pragma unroll
+          for (int i = 0; i < kDmaPerWave; ++i) tile_load(rs, sm.lat[t], sm.rot[t], wave, lane, i);
+        }
         pg_next = pg[kLoadAhead];
       }
 
@@ -671,28 +668,27 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(DecodeArgs
       float alpha[RB];
       int lim[RB];
       // ---- tile 0: scores and softmax ----
-      wait_tile(0, kLoadAhead - 1);
+      static_assert(kLoadAhead == 3, "tiles 1 and 2 stay in flight over tile 0");
+      wait_vmcnt<2 * kDmaPerWave>();
       wait_lgkm0();
       barrier_raw();
-      qk_tile<RB>(sm.lat[0], sm.rot[0], qrot_w, lane, qh, qrl, sacc);
+      qk_tile<RB>(sm.lat[0], sm.rot[0], qrot_w, lane, qh, qrl, sacc, [](int) {});
       tile_lim(0, lim);
       softmax_tile<RB>(sacc, sl2, lim, m_used, l_part, p, alpha);  // (its factor multiplies an empty O)
       for (int it = 0; it + 1 < n_tiles; ++it) {
-        // tile it+1 in LDS (this wave's loads, then everyone's); every wave is
-        // past the PV of tile it-1 and the scores of tile it, so their stages
-        // take tile it+3
-        wait_tile(it + 1, it + kLoadAhead - 1);
+        // tile it+1 in LDS (this wave's loads, with tile it+2 still in
+        // flight, then everyone's); every wave is past the PV of tile it-1 and
+        // the scores of tile it, so their stages take tile it+3, whose loads
+        // go out between the score MFMAs of tile it+1
+        wait_vmcnt<kDmaPerWave>();
         wait_lgkm0();
         barrier_raw();
-        if (it + kLoadAhead < n_tiles) {
-          load_tile(it + kLoadAhead, pg_next);
-          // the page of the tile after it, used next iteration
-          if (bt_row && it + kLoadAhead + 1 < n_tiles) pg_next = page_of(it + kLoadAhead + 1);
-        }
-        // the scores of tile it+1, then the PV of tile it with the softmax of
-        // tile it+1 free to go between its MFMAs (it reads only the scores)
+        const i32x4_t rs_next = tile_rsrc(it + kLoadAhead, pg_next);
+        char* const lat_next = sm.lat[(it + kLoadAhead) % kLatStages];
+        char* const rot_next = sm.rot[(it + kLoadAhead) % kRotStages];
         tile_lim(it + 1, lim);
-        qk_tile<RB>(sm.lat[(it + 1) % kLatStages], sm.rot[(it + 1) % kRotStages], qrot_w, lane, qh, qrl, sacc);
+        qk_tile<RB>(sm.lat[(it + 1) % kLatStages], sm.rot[(it + 1) % kRotStages], qrot_w, lane, qh, qrl, sacc,
+                    [&](int i) { tile_load(rs_next, lat_next, rot_next, wave, lane, i); });
         sched_qk<RB>();
         // the softmax of tile it+1 (its scores die here: only the two tiles'
         // P operands live across the PV product), then the PV of tile it
@@ -705,8 +701,15 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(DecodeArgs
         if (moved) scale_acc<RB>(acc, alpha);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) p[rb] = pn[rb];
+        // the page of the tile loaded next iteration: its scalar load returns
+        // during the wait at the top (not inside the score product, where it
+        // would force full waits on the LDS reads)
+        if (bt_row && it + kLoadAhead + 1 < n_tiles) pg_next = page_of(it + kLoadAhead + 1);
       }
-      // the last tile's PV
+      // the last tile's PV (the loads past the piece, which only wrote zeros
+      // into free stages, are drained too: none may land after the
+      // workgroup's LDS is released)
+      wait_vmcnt<0>();
       wait_lgkm0();
       barrier_raw();
       pv_tile<RB>(sm.lat[(n_tiles - 1) % kLatStages], lane, p, acc);
