@@ -115,6 +115,37 @@ def output_expand(w_uv: np.ndarray, o_lat: np.ndarray) -> np.ndarray:
     return out
 
 
+def output_projection(w_o: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """The shared output projection over the heads' value outputs: each head
+    adds its own contribution, the columns of W_O that belong to it applied to
+    that head's d_v outputs (MLA tutorial page, "Move the Value Expansion After
+    the Weighted Sum", its closing remark that U_V combines with the head's
+    contribution to the final output projection; RedKnot-MLA abstract: one
+    shared output projection after the merge).
+
+    w_o [d_model, H * d_v] (head h owns columns h*d_v .. h*d_v + d_v - 1),
+    v [n_tok, H, d_v] -> [n_tok, d_model]."""
+    w = np.asarray(w_o, dtype=np.float64)
+    x = np.asarray(v, dtype=np.float64)
+    n_tok, H, d_v = x.shape
+    out = np.zeros((n_tok, w.shape[0]), dtype=np.float64)
+    for h in range(H):
+        out += x[:, h, :] @ w[:, h * d_v:(h + 1) * d_v].T
+    return out
+
+
+def fold_value_into_output(w_o: np.ndarray, w_uv: np.ndarray) -> np.ndarray:
+    """W_O's columns of head h times that head's U_V: one [d_model, d_c] map per
+    head that takes the weighted latent straight to the head's share of the
+    layer output (the same remark of the MLA tutorial page).
+
+    w_o [d_model, H * d_v], w_uv [H, d_v, d_c] -> [H, d_model, d_c]."""
+    w = np.asarray(w_o, dtype=np.float64)
+    u = np.asarray(w_uv, dtype=np.float64)
+    H, d_v, d_c = u.shape
+    return np.stack([w[:, h * d_v:(h + 1) * d_v] @ u[h] for h in range(H)])
+
+
 # --------------------------------------------------------------------------
 # Softmax with its log-sum-exp
 # --------------------------------------------------------------------------

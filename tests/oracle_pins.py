@@ -219,6 +219,43 @@ def pin_direct_equals_absorbed(O):
         _close(mixed, a @ O.expand(w_uv[h], c), 1e-12, "value-side linearity")
 
 
+def pin_output_projection(O):
+    """The shared output projection against torch's linear layer (fp64), a
+    pure-Python sum, the per-head fold of U_V into W_O (MLA tutorial page,
+    "Move the Value Expansion After the Weighted Sum"), and block special
+    cases."""
+    import torch
+    rng = np.random.default_rng(21)
+    n_tok, H, d_v, d_c, d_model = 3, 4, 5, 6, 7
+    w_o = rng.standard_normal((d_model, H * d_v))
+    v = rng.standard_normal((n_tok, H, d_v))
+    out = O.output_projection(w_o, v)
+    ref = torch.nn.functional.linear(torch.from_numpy(v.reshape(n_tok, H * d_v)), torch.from_numpy(w_o)).numpy()
+    _close(out, ref, 1e-12, "W_O vs torch linear")
+    for t in range(n_tok):
+        for n in range(d_model):
+            e = sum(w_o[n, h * d_v + i] * v[t, h, i] for h in range(H) for i in range(d_v))
+            assert abs(out[t, n] - e) <= 1e-12, "W_O explicit sum"
+    # the fold: (W_O block h . U_V[h]) o_lat[h], summed over heads, equals
+    # W_O applied to the expanded heads
+    w_uv = rng.standard_normal((H, d_v, d_c))
+    o_lat = rng.standard_normal((n_tok, H, d_c))
+    fold = O.fold_value_into_output(w_o, w_uv)
+    assert fold.shape == (H, d_model, d_c)
+    via_fold = sum(o_lat[:, h, :] @ fold[h].T for h in range(H))
+    expanded = np.einsum("hvc,thc->thv", w_uv, o_lat)
+    ref2 = torch.nn.functional.linear(torch.from_numpy(expanded.reshape(n_tok, H * d_v)),
+                                      torch.from_numpy(w_o)).numpy()
+    _close(via_fold, ref2, 1e-12, "folded U_V W_O")
+    # one head with W_O = identity passes the head's output through; W_O
+    # nonzero only on head 2's columns sees head 2 alone
+    v1 = rng.standard_normal((2, 1, d_v))
+    _close(O.output_projection(np.eye(d_v), v1), v1[:, 0, :], 1e-15, "identity W_O")
+    w_blk = np.zeros_like(w_o)
+    w_blk[:, 2 * d_v:3 * d_v] = w_o[:, 2 * d_v:3 * d_v]
+    _close(O.output_projection(w_blk, v), v[:, 2, :] @ w_o[:, 2 * d_v:3 * d_v].T, 1e-12, "single head block")
+
+
 # ------------------------------------------------------------------- RoPE
 def pin_rope(O):
     rng = np.random.default_rng(15)
@@ -492,4 +529,5 @@ ALL_PINS = [
     pin_qknorm_closed_form,
     pin_qknorm_invariances,
     pin_qknorm_absorbed,
+    pin_output_projection,
 ]

@@ -11,6 +11,13 @@ from oracle_pins import ALL_PINS
 SRC = open(O.__file__).read()
 
 MUTANTS = {
+    "wo_wrong_block": ("out += x[:, h, :] @ w[:, h * d_v:(h + 1) * d_v].T", "out += x[:, h, :] @ w[:, 0:d_v].T"),
+    "wo_untransposed_block": ("out += x[:, h, :] @ w[:, h * d_v:(h + 1) * d_v].T",
+                              "out += (w[:, h * d_v:(h + 1) * d_v] @ x[:, h, :].T).T[:, ::-1]"),
+    "wo_last_head_only": ("out += x[:, h, :] @ w[:, h * d_v:(h + 1) * d_v].T",
+                          "out = x[:, h, :] @ w[:, h * d_v:(h + 1) * d_v].T"),
+    "fold_transposed_uv": ("return np.stack([w[:, h * d_v:(h + 1) * d_v] @ u[h] for h in range(H)])",
+                           "return np.stack([w[:, h * d_v:(h + 1) * d_v] @ u[H - 1 - h] for h in range(H)])"),
     "rope_sign": ("out[..., 0::2] = x0 * cos - x1 * sin", "out[..., 0::2] = x0 * cos + x1 * sin"),
     "rope_freq": ("return base ** (-2.0 * i / d_rope)", "return base ** (-1.0 * i / d_rope)"),
     "rope_pairs_halves": ("x0, x1 = x[..., 0::2], x[..., 1::2]",
