@@ -20,8 +20,9 @@
  *   mla_decode_splitkv -> partial (o_lat, lse) states per KV split / segment
  *   mla_combine_lse  -> o_lat, lse (log-sum-exp merge of the partial states)
  *   mla_out_uv       -> out        (U_V o_lat, once per query)
+ *   mla_out_proj     -> layer out  (the shared output projection W_O over all heads)
  * mla_prepare_q runs the first two in one launch (all segment shifts at once);
- * mla_combine_out_uv runs the last two in one launch (few query tokens).
+ * mla_combine_out_uv runs the combine and U_V in one launch (few query tokens).
  *
  * Conventions shared by every call
  *  - All tensor pointers are DEVICE pointers (HIP device memory), row-major,
@@ -277,6 +278,35 @@ mla_status mla_prepare_q_qknorm(const void* q_nope, int q_dtype, const float* g_
  */
 mla_status mla_out_uv(const void* o_lat, int o_dtype, const void* w_uv, int w_dtype, void* out,
                       int out_dtype, int n_tok, int n_heads, int d_c, int d_v, void* stream);
+
+/*
+ * mla_out_proj -- the shared output projection W_O over the heads' outputs.
+ * [T] "Move the Value Expansion After the Weighted Sum" (its closing remark:
+ * the value up-projection combines with each head's contribution to the
+ * final output projection); [R]: the merged state of the two paths goes
+ * through one shared output projection.
+ *
+ *   out[t][n] = sum_k x[t][k] * w_o[n][k]         (fp32 accumulation)
+ *
+ * x     [n_tok][k_in]     x_dtype: the heads' outputs back to back, i.e.
+ *                         mla_out_uv's out viewed as [n_tok][n_heads * d_v]
+ *                         (k = h * d_v + i)
+ * w_o   [d_model][k_in]   w_dtype: row n = output feature n; head h owns
+ *                         columns h * d_v .. h * d_v + d_v - 1
+ * out   [n_tok][d_model]  out_dtype
+ * The folded form takes x = o_lat viewed as [n_tok][n_heads * d_c] and, as
+ * w_o, the per-head products W_O[:, head h] U_V[h] side by side
+ * ([d_model][n_heads * d_c]); it reads more weight bytes than mla_out_uv
+ * followed by this call whenever d_c > d_v.
+ * bf16 x and w_o with k_in a multiple of 256 and both 16-byte aligned run on
+ * MFMA (each W_O row is read once per 64 tokens); any other case runs a
+ * plain fp32 kernel.  d_model is the layer's model width, a parameter.
+ * Shapes: n_tok <= 2^20, 1 <= k_in <= 2^20, 1 <= d_model <= 2^20.
+ * Errors: MLA_ERR_NULL, MLA_ERR_DTYPE, MLA_ERR_SHAPE.  The caller owns every
+ * buffer; nothing is allocated.
+ */
+mla_status mla_out_proj(const void* x, int x_dtype, const void* w_o, int w_dtype, void* out, int out_dtype,
+                        int n_tok, int k_in, int d_model, void* stream);
 
 /*
  * mla_combine_out_uv -- mla_combine_lse followed by mla_out_uv, in one launch.

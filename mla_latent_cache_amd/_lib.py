@@ -56,6 +56,8 @@ SIGNATURES = {
                                 c_void_p]),
     "mla_out_uv": (c_int, [c_void_p, c_int, c_void_p, c_int, c_void_p, c_int, c_int, c_int, c_int, c_int,
                            c_void_p]),
+    "mla_out_proj": (c_int, [c_void_p, c_int, c_void_p, c_int, c_void_p, c_int, c_int, c_int, c_int,
+                             c_void_p]),
     "mla_combine_out_uv": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_int, c_int,
                                    c_void_p, c_void_p, c_void_p, c_int, c_void_p]),
     "mla_prepare_q": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_int, c_void_p, c_int, POINTER(c_void_p),

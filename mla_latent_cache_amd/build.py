@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmla_latent.so")
 SOURCES = ["mla_api.cpp", "mla_small_kernels.hip", "mla_decode_bf16.hip", "mla_decode_rows.hip",
-           "mla_proj_mfma.hip"]
+           "mla_proj_mfma.hip", "mla_out_proj.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are disabled: hipcc would otherwise generate

@@ -233,6 +233,20 @@ mla_status mla_out_uv(const void* o_lat, int o_dtype, const void* w_uv, int w_dt
                     "mla_out_uv launch");
 }
 
+mla_status mla_out_proj(const void* x, int x_dtype, const void* w_o, int w_dtype, void* out, int out_dtype,
+                        int n_tok, int k_in, int d_model, void* stream) {
+  if (!x || !w_o || !out) return fail(MLA_ERR_NULL, "mla_out_proj: null pointer");
+  if (!dtype_ok(x_dtype) || !dtype_ok(w_dtype) || !dtype_ok(out_dtype))
+    return fail(MLA_ERR_DTYPE, "mla_out_proj: dtypes %d, %d, %d", x_dtype, w_dtype, out_dtype);
+  if (n_tok < 0 || n_tok > kMaxTok || k_in <= 0 || k_in > (1 << 20) || d_model <= 0 || d_model > (1 << 20))
+    return fail(MLA_ERR_SHAPE, "mla_out_proj: n_tok=%d (<= %d) k_in=%d d_model=%d (each <= 2^20)", n_tok, kMaxTok,
+                k_in, d_model);
+  if (n_tok == 0) return ok();
+  return hip_status(mla::launch_out_proj(x, x_dtype == MLA_BF16, w_o, w_dtype == MLA_BF16, out,
+                                         out_dtype == MLA_BF16, n_tok, k_in, d_model, (hipStream_t)stream),
+                    "mla_out_proj launch");
+}
+
 mla_status mla_combine_lse(const float* o_part, const float* lse_part, int n_rows, int n_part, int d_c,
                            void* o_lat, int out_dtype, float* lse, void* stream) {
   if (!o_part || !lse_part || !o_lat) return fail(MLA_ERR_NULL, "mla_combine_lse: null pointer");

@@ -48,6 +48,10 @@ hipError_t launch_absorb(const void* q_nope, const void* w_uk, bool in_bf16, voi
                          int n_tok, int n_heads, int d_nope, int d_c, hipStream_t stream);
 hipError_t launch_out_uv(const void* o_lat, bool o_bf16, const void* w_uv, bool w_bf16, void* out,
                          bool out_bf16, int n_tok, int n_heads, int d_c, int d_v, hipStream_t stream);
+// out[t][n] = sum_k x[t][k] w[n][k] (MFMA for bf16 operands, k_in % 256 == 0, 16-byte aligned)
+bool out_proj_mfma_ok(const void* x, bool x_bf16, const void* w, bool w_bf16, int k_in);
+hipError_t launch_out_proj(const void* x, bool x_bf16, const void* w, bool w_bf16, void* out, bool out_bf16,
+                           int n_tok, int k_in, int d_model, hipStream_t stream);
 // bf16 MFMA variants (d_nope = 128, d_c = 512, d_v = 128, 16-byte aligned).
 bool absorb_mfma_ok(const void* q_nope, const void* w_uk, int d_nope, int d_c);
 

@@ -133,6 +133,23 @@ def out_uv(o_lat: torch.Tensor, w_uv: torch.Tensor, out: Optional[torch.Tensor] 
     return out
 
 
+def out_proj(x: torch.Tensor, w_o: torch.Tensor, out: Optional[torch.Tensor] = None,
+             out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    """x [n_tok, ...] (flattened to [n_tok, k_in]), w_o [d_model, k_in] -> out [n_tok, d_model]."""
+    n_tok = x.shape[0]
+    k_in = x[0].numel() if n_tok else w_o.shape[1]
+    d_model = w_o.shape[0]
+    if w_o.dim() != 2 or w_o.shape[1] != k_in:
+        raise ValueError("w_o must be [d_model, k_in] with k_in = the product of x's trailing dims")
+    if not x.is_contiguous() or not w_o.is_contiguous():
+        raise ValueError("x and w_o must be contiguous")
+    if out is None:
+        out = torch.empty((n_tok, d_model), dtype=out_dtype or w_o.dtype, device=x.device)
+    _lib.call("mla_out_proj", _ptr(x), _dt(x), _ptr(w_o), _dt(w_o), _ptr(out), _dt(out), n_tok, k_in, d_model,
+              _stream())
+    return out
+
+
 def combine_lse(o_part: torch.Tensor, lse_part: torch.Tensor, out_dtype: torch.dtype,
                 o_lat: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
     """o_part [..., n_part, d_c] fp32, lse_part [..., n_part] -> (o_lat [..., d_c], lse [...])."""

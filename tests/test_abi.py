@@ -85,6 +85,15 @@ def test_null_and_shape_errors_before_any_gpu_call(lib):
     assert _st(lib, "mla_absorb_q", P, P, 1, P, 0, 1, 0, 128, 512, None) == 2
     assert _st(lib, "mla_out_uv", P, 1, P, 1, P, 1, -1, 1, 512, 128, None) == 2
     assert _st(lib, "mla_combine_lse", P, P, 1, 0, 512, P, 1, None, None) == 2
+    # mla_out_proj(x, x_dtype, w_o, w_dtype, out, out_dtype, n_tok, k_in, d_model)
+    assert _st(lib, "mla_out_proj", None, 1, P, 1, P, 1, 1, 256, 64, None) == 1
+    assert _st(lib, "mla_out_proj", P, 1, P, 7, P, 1, 1, 256, 64, None) == 3
+    assert _st(lib, "mla_out_proj", P, 1, P, 1, P, 1, -1, 256, 64, None) == 2
+    assert _st(lib, "mla_out_proj", P, 1, P, 1, P, 1, 1, 0, 64, None) == 2
+    assert _st(lib, "mla_out_proj", P, 1, P, 1, P, 1, 1, 256, 0, None) == 2
+    assert _st(lib, "mla_out_proj", P, 1, P, 1, P, 1, 1, (1 << 20) + 1, 64, None) == 2
+    assert _st(lib, "mla_out_proj", P, 1, P, 1, P, 1, 1, 256, (1 << 20) + 1, None) == 2
+    assert _st(lib, "mla_out_proj", P, 1, P, 1, P, 1, 0, 256, 64, None) == 0  # nothing to do: no launch
     assert _st(lib, "mla_combine_lse", P, None, 1, 1, 512, P, 1, None, None) == 1
     # mla_combine_out_uv(o_part, lse_part, n_tok, n_heads, n_part, d_c, w_uv, w_dtype, d_v, o_lat, lse, out, dt)
     assert _st(lib, "mla_combine_out_uv", P, P, 1, 1, 4, 512, None, 1, 128, None, None, P, 1, None) == 1
@@ -211,4 +220,5 @@ def test_size_limits_refused(lib):
     assert lib.rope_relocate_q(P, 1, P, 0, P, None, n, 1, 64, 1e4, None) == 2
     assert lib.mla_absorb_q(P, P, 1, P, 0, n, 1, 128, 512, None) == 2
     assert lib.mla_out_uv(P, 1, P, 1, P, 1, n, 1, 512, 128, None) == 2
+    assert lib.mla_out_proj(P, 1, P, 1, P, 1, n, 256, 64, None) == 2
     assert lib.mla_prepare_q(P, 1, P, P, 1, P, 0, None, None, 0, 0, P, n, 4, 128, 64, 512, 1e4, None) == 2

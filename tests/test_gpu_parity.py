@@ -224,6 +224,67 @@ def test_absorb_and_out_uv_calls(dtype, dims):
         assert np.all(np.abs(f64(got) - ref) <= rel * np.abs(ref) + 1e-5 * rms), odt
 
 
+def _out_proj_bound(x, w, ref, rel):
+    """|got - ref| <= rel |ref| (output rounding) + 1e-6 sum_k |x_k w_k| (fp32
+    accumulation over k_in <= 16384 terms)."""
+    s = np.abs(f64(x).reshape(x.shape[0], -1)) @ np.abs(f64(w)).T
+    return rel * np.abs(ref) + 1e-6 * s
+
+
+@pytest.mark.parametrize("dtype,n_tok,k_in,d_model", [
+    (torch.float32, 1, 8, 8),            # fp32 toy: 2 heads x d_v 4
+    (torch.bfloat16, 1, 2048, 2048),     # one token, 16 heads x 128
+    (torch.bfloat16, 5, 2048, 2088),     # ragged feature tail (2088 = 32 x 64 + 40)
+    (torch.bfloat16, 70, 4096, 1000),    # two token blocks, ragged tokens and features
+    (torch.bfloat16, 64, 16384, 7168),   # 128 heads x 128, a wide model
+    (torch.bfloat16, 3, 264, 100),       # k_in not a multiple of 256: the plain kernel
+])
+def test_out_proj_call(dtype, n_tok, k_in, d_model):
+    """mla_out_proj against the oracle's shared output projection (fp64)."""
+    from mla_latent_cache_amd import ops
+    H = 2 if k_in == 8 else (k_in // 128 if k_in % 128 == 0 else 1)
+    d_v = k_in // H
+    v = _rand((n_tok, H, d_v), dtype, 31)
+    w_o = (_rand((d_model, k_in), torch.float32, 32) / math.sqrt(k_in)).to(dtype)
+    ref = O.output_projection(f64(w_o), f64(v))
+    for odt in {dtype, torch.float32}:
+        got = ops.out_proj(v.cuda(), w_o.cuda(), out_dtype=odt)
+        assert got.shape == (n_tok, d_model)
+        rel = 0.0 if odt == torch.float32 else 2.0 ** -8
+        bound = _out_proj_bound(v, w_o, ref, rel)
+        if dtype == torch.float32:  # the toy's bar: 1e-5 relative
+            bound = np.maximum(bound, 1e-5 * np.abs(ref).max())
+        err = np.abs(f64(got) - ref)
+        assert np.all(err <= bound), (odt, float(err.max()), float((err - bound).max()))
+
+
+def test_out_proj_after_out_uv_and_folded():
+    """U_V then W_O (two calls, bf16 in between) and the folded form (o_lat
+    against W_O[:, head h] U_V[h] side by side) both match the oracle's
+    output_projection(W_O, output_expand(U_V, o_lat))."""
+    from mla_latent_cache_amd import ops
+    n_tok, H, d_c, d_v, d_model = 9, 16, 512, 128, 1536
+    o = _rand((n_tok, H, d_c), torch.bfloat16, 33)
+    wv = (_rand((H, d_v, d_c), torch.float32, 34) / math.sqrt(d_c)).to(torch.bfloat16)
+    w_o = (_rand((d_model, H * d_v), torch.float32, 35) / math.sqrt(H * d_v)).to(torch.bfloat16)
+    ref = O.output_projection(f64(w_o), O.output_expand(f64(wv), f64(o)))
+    # two calls: the heads' outputs rounded to bf16 (relative 2^-9 each) before W_O
+    v = ops.out_uv(o.cuda(), wv.cuda(), out_dtype=torch.bfloat16)
+    got = ops.out_proj(v, w_o.cuda(), out_dtype=torch.float32)
+    v_ref = O.output_expand(f64(wv), f64(o))
+    s_v = np.abs(v_ref).reshape(n_tok, -1) @ np.abs(f64(w_o)).T
+    err = np.abs(f64(got) - ref)
+    assert np.all(err <= 2.0 ** -8 * s_v + 1e-5 * s_v), float(err.max())
+    # folded: the fold rounded to bf16 (relative 2^-9 per entry)
+    fold = O.fold_value_into_output(f64(w_o), f64(wv))          # [H, d_model, d_c]
+    w_f = torch.from_numpy(np.ascontiguousarray(fold.transpose(1, 0, 2).reshape(d_model, H * d_c)))
+    w_f = w_f.to(torch.bfloat16)
+    got_f = ops.out_proj(o.cuda().reshape(n_tok, H * d_c), w_f.cuda(), out_dtype=torch.float32)
+    s_f = np.abs(f64(o)).reshape(n_tok, -1) @ np.abs(f64(w_f)).T
+    err_f = np.abs(f64(got_f) - ref)
+    assert np.all(err_f <= 2.0 ** -8 * s_f + 1e-5 * s_f), float(err_f.max())
+
+
 @pytest.mark.parametrize("dtype,dims", [(torch.float32, (4, 4, 2, 7)), (torch.bfloat16, (128, 512, 64, 33))])
 def test_prepare_call(dtype, dims):
     """mla_prepare_q (rope for several shifts + absorb in one launch, or the
