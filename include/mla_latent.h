@@ -182,10 +182,15 @@ typedef struct {
  *          with QK-Norm.
  * o_part   [n_tok][n_heads][n_part][d_c] fp32    output
  * lse_part [n_tok][n_heads][n_part]      fp32    output
- * n_tok = batch * s_q.  n_wg = workgroups per segment (0 = one per compute unit,
- * at most 65536).
+ * n_tok = batch * s_q.  n_wg = workgroups per launch (0 = one per compute unit,
+ * at most 65536).  With an fp32 query and a bf16 cache, segments of more than
+ * 32 query rows, and every segment of a call with several, run on the
+ * row-owning kernel (groups of 64 or 128 rows, 16 or 32 per wave): the
+ * segments of a call share one launch (up to 8 per launch), each taking a
+ * part of the n_wg workgroups proportional to row groups x batch x its row
+ * capacity.  Other segments get n_wg workgroups each, one launch per segment.
  * bf16 and int8 paths: d_c = 512, d_rope = 64, page_size = 64, s_q * head_count <= 4096
- * (multi-token chunks: the rows form groups of 64, each streaming the rows).
+ * (multi-token chunks: the rows form groups, each streaming the rows).
  */
 mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q_lat, int q_dtype,
                               int cache_dtype, int batch, int s_q, int n_heads, int d_c, int d_rope,

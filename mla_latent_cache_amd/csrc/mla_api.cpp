@@ -414,22 +414,33 @@ mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q
   if (batch == 0) return ok();
   int wg = n_wg > 0 ? n_wg : cu_count();
   if (wg <= 0) return fail(MLA_ERR_HIP, "mla_decode_splitkv: could not query the device");
+  std::vector<mla::SegArgs> sa((size_t)n_segs);
+  bool rows_path = bf && q32 && !i8;  // fp32 query, 16-bit rows, no QK-Norm row factors
   for (int g = 0; g < n_segs; ++g) {
     const mla_segment& s = segs[g];
-    mla::DecodeArgs a;
-    a.seg = mla::SegArgs{s.cache,     s.block_table, s.seq_lens,  s.q_rot,      s.max_rows,
+    sa[g] = mla::SegArgs{s.cache,     s.block_table, s.seq_lens,  s.q_rot,      s.max_rows,
                          s.page_size, s.max_pages,   s.n_pages,   s.head_begin, s.head_count,
                          s.causal,    s.part_begin,  s.n_split,   s.row_rinv,   s.row_scale};
-    a.q_lat = q_lat;
-    a.o_part = o_part;
-    a.lse_part = lse_part;
-    a.batch = batch;
-    a.s_q = s_q;
-    a.n_heads = n_heads;
-    a.d_c = d_c;
-    a.d_rope = d_rope;
-    a.n_part = n_part;
-    a.scale = scale;
+    rows_path = rows_path && !s.row_rinv;
+  }
+  mla::DecodeArgs a{};
+  a.q_lat = q_lat;
+  a.o_part = o_part;
+  a.lse_part = lse_part;
+  a.batch = batch;
+  a.s_q = s_q;
+  a.n_heads = n_heads;
+  a.d_c = d_c;
+  a.d_rope = d_rope;
+  a.n_part = n_part;
+  a.scale = scale;
+  // several segments on the row-owning path: one launch over all of them,
+  // the grid split by each segment's share of the work
+  if (rows_path && n_segs > 1)
+    return hip_status(mla::launch_decode_rows_multi(a, sa.data(), n_segs, wg, (hipStream_t)stream),
+                      "mla_decode_splitkv launch");
+  for (int g = 0; g < n_segs; ++g) {
+    a.seg = sa[g];
     hipError_t e = bf ? mla::launch_decode_bf16(a, wg, q32, i8, (hipStream_t)stream)
                       : mla::launch_decode_f32(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "mla_decode_splitkv launch");

@@ -61,9 +61,22 @@
 //  * Grid: n_share workgroups per row group; the row groups of one share sit
 //    on the same XCD (workgroups are dispatched round-robin over 8 XCDs), so
 //    the second read of a tile hits that XCD's L2.
+//  * Several segments (the offline document, the recomputed document and the
+//    online tokens of the RedKnot-MLA abstract) share one launch: each gets a
+//    range of workgroups sized so that all finish together under a per-tile
+//    cost model, and the HBM-bound and MFMA-bound segments run side by side.
+//    Within a range the shares in whole octets keep the XCD placement above;
+//    the last n_share % 8 shares are placed in order.
+//  * A wave whose 16 RB rows are all past the group (a group of fewer rows
+//    than the workgroup holds) only moves its share of each tile and skips
+//    the products, leaving the LDS and the other SIMDs' issue to the waves
+//    with rows.
 #include "mla_common.h"
 #include "mla_decode_tile.h"
 #include "mla_kernels.h"
+
+#include <algorithm>
+#include <cmath>
 
 namespace mla {
 namespace {
@@ -359,26 +372,33 @@ __device__ __forceinline__ void sched_pv() {
 
 // RB: 16-row blocks per wave (1: 64-row groups, 2: 128-row groups).
 template <int RB>
-__global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(DecodeArgs a, int n_share, int n_rg,
-                                                                      int rows_total) {
+__global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch L) {
   constexpr int MT = 16 * RB * kRowsWaves;  // query rows of a row group
   __shared__ __attribute__((aligned(16))) RowsSmem sm;
 
-  const char* const cache = (const char*)a.seg.cache;
-  const int32_t* const block_table = a.seg.block_table;
-  const int32_t* const seq_lens = a.seg.seq_lens;
-  const float* const q_rot = (const float*)a.seg.q_rot;
+  // ---- the segment of this workgroup, and its place in the segment's grid ----
+  int g = 0;
+  while (g + 1 < L.n_segs && (int)blockIdx.x >= L.wg_begin[g + 1]) ++g;
+  const DecodeArgs& a = L.a;
+  const SegArgs& sg = L.segs[g];
+  const int n_share = L.n_share[g], n_rg = L.n_rg[g], rows_total = L.rows_total[g];
+  const int bid = (int)blockIdx.x - L.wg_begin[g];
+
+  const char* const cache = (const char*)sg.cache;
+  const int32_t* const block_table = sg.block_table;
+  const int32_t* const seq_lens = sg.seq_lens;
+  const float* const q_rot = (const float*)sg.q_rot;
   const float* const q_lat = (const float*)a.q_lat;
   float* const o_part = a.o_part;
   float* const lse_part = a.lse_part;
-  const int64_t max_rows = a.seg.max_rows;
-  const int max_pages = a.seg.max_pages;
-  const int n_pages = a.seg.n_pages;
-  const int head_begin = a.seg.head_begin;
-  const int hc = a.seg.head_count;
-  const int causal = a.seg.causal;
-  const int part_begin = a.seg.part_begin;
-  const int n_split = a.seg.n_split;
+  const int64_t max_rows = sg.max_rows;
+  const int max_pages = sg.max_pages;
+  const int n_pages = sg.n_pages;
+  const int head_begin = sg.head_begin;
+  const int hc = sg.head_count;
+  const int causal = sg.causal;
+  const int part_begin = sg.part_begin;
+  const int n_split = sg.n_split;
   const int s_q = a.s_q;
   const int n_heads = a.n_heads;
   const int n_part = a.n_part;
@@ -395,17 +415,21 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(DecodeArgs
   // ---- which share / row group this workgroup owns (XCD-aware order) ----
   int j, rg;
   if (n_rg == 1) {
-    j = blockIdx.x;
+    j = bid;
     rg = 0;
-  } else {
-    rg = (blockIdx.x / 8) % n_rg;
-    j = (blockIdx.x / (8 * n_rg)) * 8 + blockIdx.x % 8;
+  } else if (bid < n_share / 8 * 8 * n_rg) {  // shares in whole octets: row groups on one XCD
+    rg = (bid / 8) % n_rg;
+    j = (bid / (8 * n_rg)) * 8 + bid % 8;
+  } else {  // the last n_share % 8 shares
+    const int full = n_share / 8 * 8, r = n_share - full, b2 = bid - full * n_rg;
+    rg = b2 / r;
+    j = full + b2 % r;
   }
   const int row0 = rg * MT;
   const int nrows = min(MT, rows_total - row0);
   const int wrow0 = 16 * RB * wave;            // first row of this wave within the group
-  const bool wave_rows = wrow0 < nrows;        // wave-uniform: the wave has query rows (it computes
-                                               // either way; only a wave with rows stores results)
+  const bool wave_rows = wrow0 < nrows;        // wave-uniform: the wave has query rows (a wave
+                                               // without rows only loads tiles)
   const int64_t cap = block_table ? (int64_t)max_pages * kPageSize : max_rows;
   auto clampT = [cap](int t) -> int { return (int)max((int64_t)0, min((int64_t)t, cap)); };
   auto padT = [](int t) -> int { return (t + kTile - 1) / kTile * kTile; };
@@ -596,6 +620,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(DecodeArgs
       char* const qrot_w = sm.qrot[16 * RB * wave];  // this wave's rows
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
+        if (!wave_rows) break;
         const RowInfo ri = row_info(rb);
         const int64_t qi = (int64_t)b * s_q * n_heads + ri.qoff;
         const float* ql = q_lat + qi * kDc + 8 * lg;
@@ -672,9 +697,11 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(DecodeArgs
       wait_vmcnt<2 * kDmaPerWave>();
       wait_lgkm0();
       barrier_raw();
-      qk_tile<RB>(sm.lat[0], sm.rot[0], qrot_w, lane, qh, qrl, sacc, [](int) {});
-      tile_lim(0, lim);
-      softmax_tile<RB>(sacc, sl2, lim, m_used, l_part, p, alpha);  // (its factor multiplies an empty O)
+      if (wave_rows) {
+        qk_tile<RB>(sm.lat[0], sm.rot[0], qrot_w, lane, qh, qrl, sacc, [](int) {});
+        tile_lim(0, lim);
+        softmax_tile<RB>(sacc, sl2, lim, m_used, l_part, p, alpha);  // (its factor multiplies an empty O)
+      }
       for (int it = 0; it + 1 < n_tiles; ++it) {
         // tile it+1 in LDS (this wave's loads, with tile it+2 still in
         // flight, then everyone's); every wave is past the PV of tile it-1 and
@@ -686,21 +713,26 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(DecodeArgs
         const i32x4_t rs_next = tile_rsrc(it + kLoadAhead, pg_next);
         char* const lat_next = sm.lat[(it + kLoadAhead) % kLatStages];
         char* const rot_next = sm.rot[(it + kLoadAhead) % kRotStages];
-        tile_lim(it + 1, lim);
-        qk_tile<RB>(sm.lat[(it + 1) % kLatStages], sm.rot[(it + 1) % kRotStages], qrot_w, lane, qh, qrl, sacc,
-                    [&](int i) { tile_load(rs_next, lat_next, rot_next, wave, lane, i); });
-        sched_qk<RB>();
-        // the softmax of tile it+1 (its scores die here: only the two tiles'
-        // P operands live across the PV product), then the PV of tile it
-        bf16x8 pn[RB];
-        const bool moved = softmax_tile<RB>(sacc, sl2, lim, m_used, l_part, pn, alpha);
-        __builtin_amdgcn_sched_barrier(0);
-        pv_tile<RB>(sm.lat[it % kLatStages], lane, p, acc);
-        sched_pv<RB>();
-        __builtin_amdgcn_sched_barrier(0);
-        if (moved) scale_acc<RB>(acc, alpha);
+        if (!wave_rows) {
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) p[rb] = pn[rb];
+          for (int i = 0; i < kDmaPerWave; ++i) tile_load(rs_next, lat_next, rot_next, wave, lane, i);
+        } else {
+          tile_lim(it + 1, lim);
+          qk_tile<RB>(sm.lat[(it + 1) % kLatStages], sm.rot[(it + 1) % kRotStages], qrot_w, lane, qh, qrl, sacc,
+                      [&](int i) { tile_load(rs_next, lat_next, rot_next, wave, lane, i); });
+          sched_qk<RB>();
+          // the softmax of tile it+1 (its scores die here: only the two tiles'
+          // P operands live across the PV product), then the PV of tile it
+          bf16x8 pn[RB];
+          const bool moved = softmax_tile<RB>(sacc, sl2, lim, m_used, l_part, pn, alpha);
+          __builtin_amdgcn_sched_barrier(0);
+          pv_tile<RB>(sm.lat[it % kLatStages], lane, p, acc);
+          sched_pv<RB>();
+          __builtin_amdgcn_sched_barrier(0);
+          if (moved) scale_acc<RB>(acc, alpha);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) p[rb] = pn[rb];
+        }
         // the page of the tile loaded next iteration: its scalar load returns
         // during the wait at the top (not inside the score product, where it
         // would force full waits on the LDS reads)
@@ -712,7 +744,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(DecodeArgs
       wait_vmcnt<0>();
       wait_lgkm0();
       barrier_raw();
-      pv_tile<RB>(sm.lat[(n_tiles - 1) % kLatStages], lane, p, acc);
+      if (wave_rows) pv_tile<RB>(sm.lat[(n_tiles - 1) % kLatStages], lane, p, acc);
 
       // ---- epilogue: 1/l, the lse with the latent lo part's first-order
       // share, the normalised partial output.  Every load and product comes
@@ -762,19 +794,101 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(DecodeArgs
   }
 }
 
-template __global__ void decode_rows_kernel<1>(DecodeArgs, int, int, int);
-template __global__ void decode_rows_kernel<2>(DecodeArgs, int, int, int);
+template __global__ void decode_rows_kernel<1>(RowsLaunch);
+template __global__ void decode_rows_kernel<2>(RowsLaunch);
 
 int decode_rows_tile(int rows_total) { return rows_total <= 64 ? 64 : 128; }
 
+namespace {
+
+// Cost model of a segment for splitting a shared grid: its tiles (batch x row
+// capacity / 32) and the cycles of one tile in its fullest row group.  A
+// tile's time is mostly one wave's own chain (scores, softmax, PV, its
+// loads), so it grows only a little with the number of waves that have rows
+// (measured at 128-row groups: about 4.25k cycles with one such wave, 5k
+// with four; at 64-row groups about 3.9k with four).
+struct SegCost {
+  double tiles;
+  double t_tile;
+  int n_rg;
+};
+
+SegCost seg_cost(const DecodeArgs& a, const SegArgs& s, int mt) {
+  const int64_t cap = s.block_table ? (int64_t)s.max_pages * kPageSize : s.max_rows;
+  const int rows = a.s_q * s.head_count;
+  const int rpw = mt / kRowsWaves;  // rows per wave
+  SegCost c;
+  c.n_rg = (rows + mt - 1) / mt;
+  const int busy = (std::min(rows, mt) + rpw - 1) / rpw;  // waves with rows in the fullest group
+  c.t_tile = (mt == 64 ? 3400.0 + 125.0 * busy : 4000.0 + 250.0 * busy);
+  c.tiles = std::max(1.0, (double)a.batch * (double)std::max<int64_t>(cap, 1) / kTile);
+  return c;
+}
+
+hipError_t launch_rows(const RowsLaunch& L, int mt, int grid, hipStream_t stream) {
+  const dim3 block(kRowsThreads);
+  if (mt == 64) return launch(decode_rows_kernel<1>, dim3(grid), block, stream, L);
+  return launch(decode_rows_kernel<2>, dim3(grid), block, stream, L);
+}
+
+}  // namespace
+
 hipError_t launch_decode_rows(const DecodeArgs& a, int n_wg, hipStream_t stream) {
-  const int rows_total = a.s_q * a.seg.head_count;
-  const int mt = decode_rows_tile(rows_total);
-  int n_share, n_rg;
-  decode_bf16_grid(rows_total, mt, n_wg, &n_share, &n_rg);
-  const dim3 grid(n_share * n_rg), block(kRowsThreads);
-  if (mt == 64) return launch(decode_rows_kernel<1>, grid, block, stream, a, n_share, n_rg, rows_total);
-  return launch(decode_rows_kernel<2>, grid, block, stream, a, n_share, n_rg, rows_total);
+  return launch_decode_rows_multi(a, &a.seg, 1, n_wg, stream);
+}
+
+hipError_t launch_decode_rows_multi(const DecodeArgs& a, const SegArgs* segs, int n_segs, int n_wg,
+                                    hipStream_t stream) {
+  for (int g0 = 0; g0 < n_segs; g0 += kRowsMaxSegs) {
+    const int n = std::min(kRowsMaxSegs, n_segs - g0);
+    int rows_max = 0;
+    for (int g = 0; g < n; ++g) rows_max = std::max(rows_max, a.s_q * segs[g0 + g].head_count);
+    const int mt = decode_rows_tile(rows_max);
+    RowsLaunch L{};
+    L.a = a;
+    L.n_segs = n;
+    for (int g = 0; g < n; ++g) {
+      L.segs[g] = segs[g0 + g];
+      L.rows_total[g] = a.s_q * segs[g0 + g].head_count;
+    }
+    if (n == 1) {
+      decode_bf16_grid(L.rows_total[0], mt, n_wg, &L.n_share[0], &L.n_rg[0]);
+    } else {
+      // shares per segment for equal finish times: the smallest time T at
+      // which ceil(tiles x t_tile / T) shares per segment fit in n_wg
+      SegCost c[kRowsMaxSegs];
+      double hi = 1.0;
+      for (int g = 0; g < n; ++g) {
+        c[g] = seg_cost(a, L.segs[g], mt);
+        hi = std::max(hi, c[g].tiles * c[g].t_tile);
+      }
+      auto shares = [&](double T, int g) {
+        return (int)std::min<double>(c[g].tiles, std::max(1.0, std::ceil(c[g].tiles * c[g].t_tile / T)));
+      };
+      auto used = [&](double T) {
+        int64_t w = 0;
+        for (int g = 0; g < n; ++g) w += (int64_t)shares(T, g) * c[g].n_rg;
+        return w;
+      };
+      double lo = hi / std::max(n_wg, 1) / 4;
+      for (int it = 0; it < 60; ++it) {
+        const double mid = 0.5 * (lo + hi);
+        if (used(mid) <= n_wg) hi = mid; else lo = mid;
+      }
+      for (int g = 0; g < n; ++g) {
+        L.n_share[g] = shares(hi, g);
+        L.n_rg[g] = c[g].n_rg;
+      }
+    }
+    int grid = 0;
+    for (int g = 0; g < n; ++g) {
+      L.wg_begin[g] = grid;
+      grid += L.n_share[g] * L.n_rg[g];
+    }
+    const hipError_t e = launch_rows(L, mt, grid, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace mla

@@ -40,6 +40,20 @@ struct DecodeArgs {
   float scale;
 };
 
+// One launch of the row-owning decode over up to kRowsMaxSegs segments:
+// segment g owns workgroups [wg_begin[g], wg_begin[g + 1]) (the last one to
+// the end of the grid), cut into n_share[g] shares x n_rg[g] row groups.
+constexpr int kRowsMaxSegs = 8;
+struct RowsLaunch {
+  DecodeArgs a;  // the call's shared arguments (a.seg unused)
+  SegArgs segs[kRowsMaxSegs];
+  int wg_begin[kRowsMaxSegs];
+  int n_share[kRowsMaxSegs];
+  int n_rg[kRowsMaxSegs];
+  int rows_total[kRowsMaxSegs];
+  int n_segs;
+};
+
 // Dtype flags below: true = bf16 storage, false = fp32.
 hipError_t launch_rope(const void* q_pe, bool in_bf16, void* q_rot, bool out_bf16, const int64_t* pos,
                        const int64_t* shift, int n_tok, int n_heads, int d_rope, double base,
@@ -116,6 +130,10 @@ int decode_bf16_tile(int rows_total);
 // 32 query rows with an fp32 query, a 16-bit cache and no QK-Norm factors:
 // row groups of 64 (up to 64 rows) or 128; n_wg workgroups per row group.
 hipError_t launch_decode_rows(const DecodeArgs& a, int n_wg, hipStream_t stream);
+// All n_segs segments (any number; kRowsMaxSegs per launch) in row-owning
+// launches that split n_wg workgroups by estimated tile work.
+hipError_t launch_decode_rows_multi(const DecodeArgs& a, const SegArgs* segs, int n_segs, int n_wg,
+                                    hipStream_t stream);
 // Rows of that kernel's row group for a segment of rows_total query rows.
 int decode_rows_tile(int rows_total);
 
