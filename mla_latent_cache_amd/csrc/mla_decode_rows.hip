@@ -83,13 +83,20 @@ namespace {
 
 constexpr int kRowsThreads = 256;      // 4 waves, one per SIMD
 constexpr int kRowsWaves = kRowsThreads / 64;
+// Loads in flight: a CU's memory queue takes about one tile of direct-to-LDS
+// loads (36 KiB) at a time, and a load issued into a full queue stalls the
+// issuing wave until space frees up (measured: about 3.4k cycles per tile
+// per CU at one workgroup per CU, 5.7-6 TB/s in all, with one tile or more in
+// flight).  One tile ahead leaves the latency exposed behind one iteration of
+// compute; so tile it+3 goes out during the PV of tile it, by when the loads
+// of tile it+2 (issued one iteration earlier) have drained, and has about
+// 1.5 iterations to land.
 constexpr int kLatStages = 4;          // tiles it (PV), it+1 (QK), it+2, it+3 (loading)
 constexpr int kRotStages = 3;          // tiles it+1 (QK), it+2, it+3
 constexpr int kLoadAhead = 3;          // tiles issued before the first QK
 constexpr int kTileDma = kTile + kRStage / 1024;       // 36 wave-instructions per tile
 constexpr int kDmaPerWave = kTileDma / kRowsWaves;     // 9
 static_assert(kTileDma % kRowsWaves == 0, "every wave issues the same share of a tile's loads");
-static_assert(kKSteps / 2 == kDmaPerWave, "one load of the next tile after every second score k-step");
 constexpr int kRowsMaxPieces = 64;
 constexpr int kPvPre = 4;              // PV: column blocks of transposed reads in flight
 constexpr int kQkPre = 3;              // QK: k-steps of K-operand reads in flight
@@ -173,13 +180,10 @@ __device__ __forceinline__ void tile_load(i32x4_t rsrc, char* lat, char* rot, in
 // 4 ks + lg, sits at position (4 ks + lg) ^ l16 = 16 a + 4 (n ^ (l16 >> 2)) +
 // (lg ^ (l16 & 3)); rotary k-step jr: chunk 4 jr + lg at (4 jr + lg) ^
 // ((l16 >> 1) & 7).  Rows 16 + l16 share the swizzle key of row l16.
-// `load(i)` issues load i of the next tile's share after the MFMAs of k-step
-// 2 i + 1, so the nine loads spread over the product instead of queueing
-// behind one another.
-template <int RB, class Load>
+template <int RB>
 __device__ __forceinline__ void qk_tile(const char* __restrict__ ls, const char* __restrict__ rs,
                                         const char* __restrict__ qs, int lane, const bf16x8 (&qh)[RB][kDc / 32],
-                                        const bf16x8 (&qrl)[RB][2], f32x4 (&s)[2][RB], const Load& load) {
+                                        const bf16x8 (&qrl)[RB][2], f32x4 (&s)[2][RB]) {
   asm volatile("" : "+v"(lane));
   const int xl = lane & 15, xg = lane >> 4;
   const char* kb[4];
@@ -228,7 +232,6 @@ __device__ __forceinline__ void qk_tile(const char* __restrict__ ls, const char*
         s[1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qrl[rb][jr], s[1][rb], 0, 0, 0);
       }
     }
-    if (ks % 2 == 1) load(ks / 2);
   }
 }
 
@@ -240,9 +243,12 @@ __device__ __forceinline__ void qk_tile(const char* __restrict__ ls, const char*
 // second row x + 16 (same swizzle key), columns 16 db + 4 qq .. + 3, i.e.
 // chunk 2 db + (qq >> 1) at position 2 (db ^ (x >> 1)) + ((qq >> 1) ^ (x & 1)),
 // byte 8 (qq & 1) within it; each 16-lane group then holds C[rows][16 db + l16].
-template <int RB>
+// `load(i)` issues load i of the next tile's share after the MFMAs of column
+// block kPvLoadAt[i].
+constexpr int kPvLoadAt[9] = {1, 4, 8, 11, 15, 18, 22, 25, 29};
+template <int RB, class Load>
 __device__ __forceinline__ void pv_tile(const char* __restrict__ ls, int lane, const bf16x8 (&p)[RB],
-                                        f32x4 (&acc)[32][RB]) {
+                                        f32x4 (&acc)[32][RB], const Load& load) {
   asm volatile("" : "+v"(lane));
   const int qq = lane & 3, rq = (lane >> 2) & 3, xg = lane >> 4;
   const int xr = 4 * xg + rq;
@@ -267,6 +273,9 @@ __device__ __forceinline__ void pv_tile(const char* __restrict__ ls, int lane, c
       acc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[db % (kPre + 1)], p[rb], acc[db][rb], 0, 0, 0);
       asm("" : "+a"(acc[db][rb]));  // the accumulators live in AGPRs throughout
     }
+#pragma unroll
+    for (int i = 0; i < 9; ++i)
+      if (kPvLoadAt[i] == db) load(i);
   }
 }
 
@@ -698,7 +707,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
       wait_lgkm0();
       barrier_raw();
       if (wave_rows) {
-        qk_tile<RB>(sm.lat[0], sm.rot[0], qrot_w, lane, qh, qrl, sacc, [](int) {});
+        qk_tile<RB>(sm.lat[0], sm.rot[0], qrot_w, lane, qh, qrl, sacc);
         tile_lim(0, lim);
         softmax_tile<RB>(sacc, sl2, lim, m_used, l_part, p, alpha);  // (its factor multiplies an empty O)
       }
@@ -706,27 +715,27 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
         // tile it+1 in LDS (this wave's loads, with tile it+2 still in
         // flight, then everyone's); every wave is past the PV of tile it-1 and
         // the scores of tile it, so their stages take tile it+3, whose loads
-        // go out between the score MFMAs of tile it+1
+        // go out between the PV MFMAs of tile it
         wait_vmcnt<kDmaPerWave>();
         wait_lgkm0();
         barrier_raw();
         const i32x4_t rs_next = tile_rsrc(it + kLoadAhead, pg_next);
         char* const lat_next = sm.lat[(it + kLoadAhead) % kLatStages];
         char* const rot_next = sm.rot[(it + kLoadAhead) % kRotStages];
+        auto load_next = [&](int i) { tile_load(rs_next, lat_next, rot_next, wave, lane, i); };
         if (!wave_rows) {
 #pragma unroll
-          for (int i = 0; i < kDmaPerWave; ++i) tile_load(rs_next, lat_next, rot_next, wave, lane, i);
+          for (int i = 0; i < kDmaPerWave; ++i) load_next(i);
         } else {
           tile_lim(it + 1, lim);
-          qk_tile<RB>(sm.lat[(it + 1) % kLatStages], sm.rot[(it + 1) % kRotStages], qrot_w, lane, qh, qrl, sacc,
-                      [&](int i) { tile_load(rs_next, lat_next, rot_next, wave, lane, i); });
+          qk_tile<RB>(sm.lat[(it + 1) % kLatStages], sm.rot[(it + 1) % kRotStages], qrot_w, lane, qh, qrl, sacc);
           sched_qk<RB>();
           // the softmax of tile it+1 (its scores die here: only the two tiles'
           // P operands live across the PV product), then the PV of tile it
           bf16x8 pn[RB];
           const bool moved = softmax_tile<RB>(sacc, sl2, lim, m_used, l_part, pn, alpha);
           __builtin_amdgcn_sched_barrier(0);
-          pv_tile<RB>(sm.lat[it % kLatStages], lane, p, acc);
+          pv_tile<RB>(sm.lat[it % kLatStages], lane, p, acc, load_next);
           sched_pv<RB>();
           __builtin_amdgcn_sched_barrier(0);
           if (moved) scale_acc<RB>(acc, alpha);
@@ -744,7 +753,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
       wait_vmcnt<0>();
       wait_lgkm0();
       barrier_raw();
-      if (wave_rows) pv_tile<RB>(sm.lat[(n_tiles - 1) % kLatStages], lane, p, acc);
+      if (wave_rows) pv_tile<RB>(sm.lat[(n_tiles - 1) % kLatStages], lane, p, acc, [](int) {});
 
       // ---- epilogue: 1/l, the lse with the latent lo part's first-order
       // share, the normalised partial output.  Every load and product comes
