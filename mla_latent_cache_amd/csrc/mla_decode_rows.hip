@@ -41,13 +41,15 @@
 //    rare lazy rescale of O.  So the score chain, the softmax's dependent
 //    VALU/transcendental chain and both products share one instruction stream
 //    per SIMD without waiting on one another.
-//  * Query precision: q_lat and q_rot arrive in fp32.  The latent part is
-//    multiplied as bf16 hi only; the rotary part as hi + lo.  With
-//    delta_t = scale (lo . c_t) the neglected part of a latent score,
-//    ln sum exp(s_t + delta_t) = lse + sum_t p_t delta_t + O(var_p delta), so
-//    the lse gains scale (lo . o) (o = the normalised weighted latent, which
-//    each wave holds for its rows), leaving a second-order error (about 1e-5
-//    at unit-variance inputs).
+//  * Query precision: q_lat and q_rot arrive in fp32 and are multiplied by
+//    scale * log2 e (scores come out in log2 units), then split into bf16 hi
+//    and lo parts.  The latent part is multiplied as hi only; the rotary
+//    part as hi + lo.  With delta_t = lo . c_t the neglected part of a
+//    latent score, log2 sum 2^(s_t + delta_t) = lse2 + sum_t p_t delta_t +
+//    O(var_p delta), so the lse gains lo . o (o = the normalised weighted
+//    latent, which each wave holds for its rows; ln 2 times that in natural
+//    units), leaving a second-order error (about 1e-5 at unit-variance
+//    inputs).
 //  * Softmax in the exp2 domain with lazy rescaling: the running max moves
 //    only when a tile max exceeds it by more than kRowsTau (log2 units), so
 //    the O rescale almost never runs; when it does, it runs outside the tile
@@ -279,24 +281,27 @@ __device__ __forceinline__ void pv_tile(const char* __restrict__ ls, int lane, c
   }
 }
 
-// Online softmax of one tile's scores (exp2 domain, lazy rescale): the P^T
-// operands (bf16), the factor each row's O must take and whether any row of
-// the wave moved its max.  Tokens past the piece or the row's causal limit
-// (relative index `lim` per lane: token 4 lg + e of the first half is
-// visible when e <= lim) get weight 0.  Branch-free, so it can be scheduled
-// between the MFMAs of the product before it.
+// Online softmax of one tile's scores, already in log2 units (the query
+// carries scale * log2 e) with lazy rescaling: the P^T operands (bf16), the
+// factor each row's O must take and whether any row of the wave moved its
+// max.  Unless the whole tile is visible to every row of the wave (`full`),
+// tokens past the piece or the row's causal limit (relative index `lim` per
+// lane: token 4 lg + e of the first half is visible when e <= lim) get
+// weight 0.
 template <int RB>
-__device__ __forceinline__ bool softmax_tile(const f32x4 (&s)[2][RB], float sl2, const int (&lim)[RB],
+__device__ __forceinline__ bool softmax_tile(const f32x4 (&s)[2][RB], bool full, const int (&lim)[RB],
                                              float (&m_used)[RB], float (&l_part)[RB], bf16x8 (&p)[RB],
                                              float (&alpha)[RB]) {
   bool need_any = false;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    f32x4 sa = s[0][rb] * sl2, sb = s[1][rb] * sl2;
+    f32x4 sa = s[0][rb], sb = s[1][rb];
+    if (!full) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sa[e] = e <= lim[rb] ? sa[e] : -INFINITY;
-      sb[e] = 16 + e <= lim[rb] ? sb[e] : -INFINITY;
+      for (int e = 0; e < 4; ++e) {
+        sa[e] = e <= lim[rb] ? sa[e] : -INFINITY;
+        sb[e] = 16 + e <= lim[rb] ? sb[e] : -INFINITY;
+      }
     }
     float mt = fmaxf(fmaxf(fmaxf(sa[0], sa[1]), fmaxf(sa[2], sa[3])), fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3])));
     mt = rows_max(mt);
@@ -656,7 +661,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
             bf16x8 h8, l8;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const float x = v[i][e >> 2][e & 3];
+              const float x = v[i][e >> 2][e & 3] * sl2;  // scores come out in log2 units
               const bf16 h = (bf16)x;
               h8[e] = h;
               l8[e] = (bf16)(x - (float)h);
@@ -696,6 +701,15 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) lim[rb] = min(pr1 - 1, vis[rb]) - t0 - 4 * lg;
       };
+      // the wave's earliest last-visible row: tile `it` needs no mask when it
+      // lies inside the piece and before it
+      int vis_min = vis[0];
+#pragma unroll
+      for (int rb = 1; rb < RB; ++rb) vis_min = min(vis_min, vis[rb]);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) vis_min = min(vis_min, __shfl_xor(vis_min, o));
+      vis_min = __builtin_amdgcn_readfirstlane(vis_min);
+      auto tile_full = [&](int it) { return pr0 + (it + 1) * kTile <= min(pr1, vis_min + 1); };
 
       f32x4 sacc[2][RB];
       bf16x8 p[RB];
@@ -709,7 +723,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
       if (wave_rows) {
         qk_tile<RB>(sm.lat[0], sm.rot[0], qrot_w, lane, qh, qrl, sacc);
         tile_lim(0, lim);
-        softmax_tile<RB>(sacc, sl2, lim, m_used, l_part, p, alpha);  // (its factor multiplies an empty O)
+        softmax_tile<RB>(sacc, tile_full(0), lim, m_used, l_part, p, alpha);  // (its factor multiplies an empty O)
       }
       for (int it = 0; it + 1 < n_tiles; ++it) {
         // tile it+1 in LDS (this wave's loads, with tile it+2 still in
@@ -733,7 +747,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
           // the softmax of tile it+1 (its scores die here: only the two tiles'
           // P operands live across the PV product), then the PV of tile it
           bf16x8 pn[RB];
-          const bool moved = softmax_tile<RB>(sacc, sl2, lim, m_used, l_part, pn, alpha);
+          const bool moved = softmax_tile<RB>(sacc, tile_full(it + 1), lim, m_used, l_part, pn, alpha);
           __builtin_amdgcn_sched_barrier(0);
           pv_tile<RB>(sm.lat[it % kLatStages], lane, p, acc, load_next);
           sched_pv<RB>();
@@ -777,7 +791,10 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
 #pragma unroll
           for (int db = 0; db < 32; ++db)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) c += (float)(bf16)(qv[db][e] - (float)(bf16)qv[db][e]) * acc[db][rb][e];
+            for (int e = 0; e < 4; ++e) {
+              const float x = qv[db][e] * sl2;  // the lo part as the prologue split it
+              c += (float)(bf16)(x - (float)(bf16)x) * acc[db][rb][e];
+            }
           cs[rb] = rows_sum(c);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -787,7 +804,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
           const RowInfo ri = row_info(rb);
           const int64_t lse_i = ((int64_t)b * s_q * n_heads + ri.qoff) * n_part + part_begin + slot;
           if (ri.valid && lg == 0)
-            lse_part[lse_i] = lt[rb] > 0.f ? (m_used[rb] + __log2f(lt[rb])) * kLn2 + scale * linv * cs[rb] : -INFINITY;
+            lse_part[lse_i] = lt[rb] > 0.f ? (m_used[rb] + __log2f(lt[rb]) + linv * cs[rb]) * kLn2 : -INFINITY;
           if (ri.valid && lt[rb] > 0.f) {
             float* o = o_part + lse_i * kDc + 4 * lg;
 #pragma unroll
