@@ -109,8 +109,71 @@ def pin_quant_row_bytes(Q):
     assert O.cache_bytes(1, 1, 1, 512, 64, 2) == 1152
 
 
+def pin_i4_exact_unit_scale_and_packing(Q):
+    """amax = 7 gives scale exactly 1: codes are the entries rounded to the
+    nearest integer, ties to even; the packed bytes, written out by hand:
+    (7, 0) -> 0x07, (2, 2) -> 0x22, (0, -2) -> 0xE0, (-6, 6) -> 0x6A,
+    (-7, 3) -> 0x39."""
+    c = np.array([[7.0, 0.5, 1.5, 2.5, -0.5, -1.5, -6.5, 6.5, -7.0, 3.0]], np.float32)
+    codes, scales = Q.quantize_i4(c)
+    assert float(scales[0]) == 1.0 and codes[0].tolist() == [7, 0, 2, 2, 0, -2, -6, 6, -7, 3], codes[0].tolist()
+    packed = Q.pack_i4(codes)
+    assert packed.dtype == np.uint8 and packed[0].tolist() == [0x07, 0x22, 0xE0, 0x6A, 0x39], packed[0].tolist()
+    assert np.array_equal(Q.unpack_i4(packed), codes)
+
+
+def pin_i4_brute_force(Q):
+    """Against a pure-Python quantizer on small rows: content and rotary
+    parts each with their own scale, every nibble checked one by one."""
+    g = np.random.default_rng(8)
+    d_c, d_r = 8, 4
+    rows = (g.standard_normal((6, d_c + d_r)) * np.exp(g.uniform(-5, 5, (6, 1)))).astype(np.float32)
+    rows[2, :d_c] = 0.0
+    packed, scales = Q.quantize_cache_i4(rows, d_c)
+    assert packed.shape == (6, (d_c + d_r) // 2) and scales.shape == (6, 2) and scales.dtype == np.float32
+    for i in range(6):
+        for part, (lo, hi) in enumerate([(0, d_c), (d_c, d_c + d_r)]):
+            x = [float(v) for v in rows[i, lo:hi]]
+            s = float(np.float32(np.float32(max(abs(v) for v in x)) / np.float32(7)))
+            assert float(scales[i, part]) == s
+            for k, v in enumerate(x):
+                e = 0 if s == 0 else max(-7, min(7, int(np.rint(np.float32(np.float32(v) / np.float32(s))))))
+                byte = int(packed[i, (lo + k) // 2])
+                nib = (byte >> (4 * ((lo + k) % 2))) & 0xF
+                assert (nib - 16 if nib >= 8 else nib) == e, (i, lo + k)
+
+
+def pin_i4_bound_and_decode(Q):
+    """|x - s code| <= s / 2 (up to the fp32 quotient) on both parts, the
+    largest entry of each part at +-7; integer rows with a 7 in each part
+    quantize without loss, so the decode over them is unchanged."""
+    g = np.random.default_rng(9)
+    d_c, d_r = 32, 8
+    rows = (g.standard_normal((40, d_c + d_r)) * np.exp(g.uniform(-8, 8, (40, 1)))).astype(np.float32)
+    deq = Q.quantized_rows_i4(rows, d_c)
+    packed, scales = Q.quantize_cache_i4(rows, d_c)
+    codes = Q.unpack_i4(packed)
+    for part, (lo, hi) in enumerate([(0, d_c), (d_c, d_c + d_r)]):
+        s = scales[:, part].astype(np.float64)[:, None]
+        err = np.abs(rows[:, lo:hi].astype(np.float64) - deq[:, lo:hi])
+        assert np.all(err <= s * (0.5 + 2.0 ** -16))
+        arg = np.argmax(np.abs(rows[:, lo:hi]), axis=1)
+        assert np.array_equal(np.abs(codes[np.arange(40), lo + arg].astype(np.int32)), np.full(40, 7))
+    ints = g.integers(-6, 7, (5, d_c + d_r)).astype(np.float64)
+    ints[:, 0] = 7.0
+    ints[:, d_c] = -7.0
+    assert np.array_equal(Q.quantized_rows_i4(ints, d_c), ints)
+
+
+def pin_i4_row_bytes(Q):
+    """An int4 row: 256 content bytes, 32 rotary bytes, two 4-byte scales
+    (296 bytes against 1152 for the bf16 row)."""
+    assert Q.cache_row_bytes_i4(512, 64) == 296
+
+
 QUANT_PINS = [pin_quant_exact_unit_scale, pin_quant_bound_and_range, pin_quant_symmetry_and_scaling,
-              pin_quant_zero_and_per_row, pin_quant_lossless_decode, pin_quant_row_bytes]
+              pin_quant_zero_and_per_row, pin_quant_lossless_decode, pin_quant_row_bytes,
+              pin_i4_exact_unit_scale_and_packing, pin_i4_brute_force, pin_i4_bound_and_decode, pin_i4_row_bytes]
 
 
 @pytest.mark.parametrize("pin", QUANT_PINS, ids=lambda p: p.__name__)
@@ -119,6 +182,18 @@ def test_quant_pin(pin):
 
 
 MUTANTS = {
+    "i4_scale_8": ("scales = (amax / np.float32(QMAX4)).astype(np.float32)",
+                   "scales = (amax / np.float32(8)).astype(np.float32)"),
+    "i4_nibbles_swapped": ("return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)",
+                           "return (c[:, 1::2] | (c[:, 0::2] << 4)).astype(np.uint8)"),
+    "i4_no_sign_extend": ("return np.where(out >= 8, out - 16, out).astype(np.int8)", "return out.astype(np.int8)"),
+    "i4_shared_scale": ("cr, sr = quantize_i4(rows[:, d_c:])",
+                        "cr, sr = quantize_i4(rows[:, d_c:])\n    sr = sc\n    cr = np.clip(np.rint(np.where(sc[:, None] > 0, "
+                        "rows[:, d_c:] / np.where(sc[:, None] > 0, sc[:, None], 1), 0)), -7, 7).astype(np.int8)"),
+    "i4_round_half_away": ("codes[nz] = np.clip(np.rint(q), -QMAX4, QMAX4).astype(np.int8)",
+                           "codes[nz] = np.clip(np.floor(q + 0.5), -QMAX4, QMAX4).astype(np.int8)"),
+    "i4_rotary_scale_from_content": ("out[:, d_c:] = np.asarray(scales[:, 1], np.float64)[:, None] * codes[:, d_c:]",
+                                     "out[:, d_c:] = np.asarray(scales[:, 0], np.float64)[:, None] * codes[:, d_c:]"),
     "scale_128": ("scales = (amax / np.float32(QMAX)).astype(np.float32)",
                   "scales = (amax / np.float32(128)).astype(np.float32)"),
     "round_half_away": ("np.clip(np.rint(q), -QMAX, QMAX)", "np.clip(np.floor(q + 0.5), -QMAX, QMAX)"),
