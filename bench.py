@@ -33,7 +33,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 MALL_BYTES = 256 << 20          # Infinity Cache: rotate caches so every step reads HBM
 DECODE_SRCS = [os.path.join(ROOT, "mla_latent_cache_amd", "csrc", f)
                for f in ("mla_decode_bf16.hip", "mla_decode_rows.hip")]
-SEEDS = {"toy": 0, "small": 1, "dsv3": 2, "long": 3, "merge": 4, "prefill": 5, "qknorm": 6, "int8": 7}
+SEEDS = {"toy": 0, "small": 1, "dsv3": 2, "long": 3, "merge": 4, "prefill": 5, "qknorm": 6, "int8": 7, "int4": 8}
 
 
 def _rows(x):
@@ -46,11 +46,15 @@ def algorithmic(x):
     pair 2 * (576 + 512) FLOPs (scores over [c | kr], weighted sum over c).
     A causal segment shows query s of s_q the rows t <= T - s_q + s.  With
     QK-Norm each row also brings its 4-byte inverse key RMS; an int8 cache row
-    is d_c one-byte codes, the 16-bit rotary key and a 4-byte scale (644 B)."""
+    is d_c one-byte codes, the 16-bit rotary key and a 4-byte scale (644 B);
+    an int4 row is (d_c + d_rope) / 2 bytes of codes and two 4-byte scales
+    (296 B)."""
     sp = x.spec
     el = x.segments[0].cache.element_size()
     if sp.quant == "int8":
         row = sp.d_c + 2 * sp.d_rope + 4
+    elif sp.quant == "int4":
+        row = (sp.d_c + sp.d_rope) // 2 + 8
     else:
         row = sp.row_width * el + (4 if sp.qk_norm else 0)
     nbytes = sum(r * row for r in _rows(x))
@@ -109,8 +113,12 @@ def cpu_baseline(x, budget_s: float):
 
     sp = x.spec
 
-    def rows(s, b):  # as attention reads them (int8 cache: the oracle's quantize/dequantize)
-        return Q.quantized_rows(s.rows(b).float().numpy(), sp.d_c) if sp.quant == "int8" else f64(s.rows(b))
+    def rows(s, b):  # as attention reads them (low-bit cache: the oracle's quantize/dequantize)
+        if sp.quant == "int8":
+            return Q.quantized_rows(s.rows(b).float().numpy(), sp.d_c)
+        if sp.quant == "int4":
+            return Q.quantized_rows_i4(s.rows(b).float().numpy(), sp.d_c)
+        return f64(s.rows(b))
 
     segs = [O.OracleSegment(rows=(lambda b, s=s: rows(s, b)), shift=s.shift.tolist(),
                             head_begin=s.head_begin, head_count=s.head_count, causal=s.causal)
@@ -147,7 +155,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="dsv3", choices=["small", "dsv3", "long", "merge", "toy", "prefill", "qknorm", "int8"])
+    ap.add_argument("--workload", default="dsv3", choices=["small", "dsv3", "long", "merge", "toy", "prefill", "qknorm", "int8", "int4"])
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--n-wg", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)

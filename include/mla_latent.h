@@ -67,11 +67,13 @@ typedef enum {
   MLA_ERR_HIP = 7          /* the HIP runtime reported an error */
 } mla_status;
 
-/* MLA_I8 is a cache format only (mla_decode_splitkv's cache_dtype): rows of
- * d_c int8 latent codes followed by d_rope bf16 rotary entries (d_c + 2 d_rope
- * bytes), one fp32 scale per row in mla_segment.row_scale; see
- * mla_quantize_latent_i8. */
-typedef enum { MLA_F32 = 0, MLA_BF16 = 1, MLA_I8 = 2 } mla_dtype;
+/* MLA_I8 and MLA_I4 are cache formats only (mla_decode_splitkv's cache_dtype).
+ * MLA_I8: rows of d_c int8 latent codes followed by d_rope bf16 rotary entries
+ * (d_c + 2 d_rope bytes), one fp32 scale per row in mla_segment.row_scale; see
+ * mla_quantize_latent_i8.  MLA_I4: rows of d_c / 2 bytes of 4-bit latent codes
+ * followed by d_rope / 2 bytes of 4-bit rotary codes, two fp32 scales per row
+ * (latent, rotary) in mla_segment.row_scale; see mla_quantize_latent_i4. */
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1, MLA_I8 = 2, MLA_I4 = 3 } mla_dtype;
 
 /*
  * rope_relocate_q -- rotary query for one KV segment.
@@ -144,7 +146,10 @@ typedef struct {
   const float* row_scale;     /* int8 cache (cache_dtype MLA_I8): per stored row the
                                  scale of its latent codes (mla_quantize_latent_i8),
                                  indexed like row_rinv; the latent is scale * code.
-                                 Must be NULL for 16-bit and fp32 caches */
+                                 int4 cache (MLA_I4): per stored row the pair
+                                 (latent scale, rotary scale) (mla_quantize_latent_i4),
+                                 8-byte aligned.  Must be NULL for 16-bit and fp32
+                                 caches */
 } mla_segment;
 
 /*
@@ -179,7 +184,13 @@ typedef struct {
  *          segment's row_scale: the latent score of row t is scale_t times
  *          q_lat . code_t and its softmax weight multiplies scale_t code_t,
  *          exactly the attention over the dequantized rows; not combined
- *          with QK-Norm.
+ *          with QK-Norm.  MLA_I4 caches (the abstract's joint INT4
+ *          content and rotary caches) take an fp32 query and every
+ *          segment's (latent, rotary) scale pairs: the score of row t is
+ *          scale * (sc_t q_lat . code_t + sr_t q_rot . rcode_t) and its
+ *          weight multiplies sc_t code_t, the attention over the
+ *          dequantized rows; they run on the row-owning kernel in groups of
+ *          64 query rows, the codes unpacked inside the streaming loop.
  * o_part   [n_tok][n_heads][n_part][d_c] fp32    output
  * lse_part [n_tok][n_heads][n_part]      fp32    output
  * n_tok = batch * s_q.  n_wg = workgroups per launch (0 = one per compute unit,
@@ -358,6 +369,27 @@ mla_status mla_combine_out_uv(const float* o_part, const float* lse_part, int n_
  * Errors: MLA_ERR_NULL, MLA_ERR_DTYPE (rows not bf16), MLA_ERR_SHAPE, MLA_ERR_ALIGN.
  */
 mla_status mla_quantize_latent_i8(const void* rows, int row_dtype, int64_t n_rows, int d_c, int d_rope,
+                                  void* out_rows, float* scales, void* stream);
+
+/*
+ * mla_quantize_latent_i4 -- write an int4 cache (the cache writer's part;
+ * QuantMLA abstract: joint INT4 caching of the content and rotary caches, here
+ * the plain per-row symmetric form).  For each of the n_rows stored rows
+ * [c | k^R] (bf16, d_c + d_rope entries), the latent c and the rotary key k^R
+ * are quantized separately; for each part x:
+ *   scale = max_i |x_i| / 7                         (fp32 quotient)
+ *   code_i = nearest integer to x_i / scale, ties to even, clamped to [-7, 7]
+ *            (the quotient in fp32; scale 0 gives codes 0)
+ * Codes go two per byte, entry 2j in the low nibble of byte j and entry 2j + 1
+ * in the high nibble, as 4-bit two's complement:
+ *   out_rows[r] = [d_c / 2 latent code bytes | d_rope / 2 rotary code bytes]
+ *   scales[r]   = (latent scale, rotary scale)
+ * rows [n_rows][d_c + d_rope] bf16; out_rows [n_rows][(d_c + d_rope) / 2]
+ * bytes; scales [n_rows][2] fp32.  n_rows <= 2^32; d_c a multiple of 8, <= 512;
+ * d_rope a multiple of 8, <= 128; out_rows 4-byte and scales 8-byte aligned.
+ * Errors: MLA_ERR_NULL, MLA_ERR_DTYPE (rows not bf16), MLA_ERR_SHAPE, MLA_ERR_ALIGN.
+ */
+mla_status mla_quantize_latent_i4(const void* rows, int row_dtype, int64_t n_rows, int d_c, int d_rope,
                                   void* out_rows, float* scales, void* stream);
 
 /*

@@ -59,7 +59,7 @@ class Spec:
     offset_range: Optional[Tuple[int, int]] = None  # o_b ~ U{lo..hi}, inclusive
     qk_norm: bool = False          # RMSNorm of the content query and key (weights g_q, g_k drawn)
     qk_eps: float = 1e-6
-    quant: Optional[str] = None    # "int8": the cache holds per-row int8 latent codes (each side quantizes
+    quant: Optional[str] = None    # "int8" / "int4": the cache holds per-row low-bit codes (each side quantizes
                                    # the drawn bf16 rows itself; nothing extra is drawn)
     description: str = ""
 
@@ -147,10 +147,19 @@ WORKLOADS["int8"] = replace(
     description="long context from an int8 latent cache: B=4, H=64, T=262144 contiguous, 1 query token; "
                 "per-row int8 latent codes + bf16 rotary key (640 B + a 4 B scale per row)")
 
+# The long-context configuration read from an int4 cache (QuantMLA abstract:
+# joint INT4 caching of the content and rotary caches; here per-row
+# symmetric 4-bit codes for both parts, each with its own scale).  Again each
+# side quantizes the drawn bf16 rows itself.
+WORKLOADS["int4"] = replace(
+    WORKLOADS["long"], name="int4", quant="int4",
+    description="long context from an int4 cache: B=4, H=64, T=262144 contiguous, 1 query token; "
+                "per-row 4-bit latent and rotary codes (288 B + two 4 B scales per row)")
+
 # Order of the configurations as listed by the benchmark description.
 WORKLOAD_ORDER = ("toy", "small", "dsv3", "long", "merge")
 # Further workloads (beyond the five configurations)
-EXTRA_WORKLOADS = ("prefill", "qknorm", "int8")
+EXTRA_WORKLOADS = ("prefill", "qknorm", "int8", "int4")
 
 
 def spec_for(name: str) -> Spec:
@@ -186,6 +195,10 @@ def mini_spec(name: str) -> Spec:
                        segments=(SegSpec("kv", lengths=(1, 129, 777), online=True),))
     if name == "int8":
         return replace(s, name="int8-mini", batch=3,
+                       segments=(SegSpec("kv", lengths=(1, 777, 2113), layout="paged", page_size=64,
+                                         spare_pages=2, online=True),))
+    if name == "int4":
+        return replace(s, name="int4-mini", batch=3,
                        segments=(SegSpec("kv", lengths=(1, 777, 2113), layout="paged", page_size=64,
                                          spare_pages=2, online=True),))
     if name == "prefill":

@@ -18,6 +18,7 @@ LIB_PATH = os.environ.get("MLA_LATENT_LIB") or os.path.join(os.path.dirname(os.p
 MLA_F32 = 0
 MLA_BF16 = 1
 MLA_I8 = 2  # cache format: int8 latent codes + bf16 rotary entries per row, fp32 scale per row
+MLA_I4 = 3  # cache format: 4-bit latent and rotary codes per row, two fp32 scales per row
 
 STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_DTYPE", 4: "MLA_ERR_ALIGN",
           5: "MLA_ERR_UNSUPPORTED", 6: "MLA_ERR_WORKSPACE", 7: "MLA_ERR_HIP"}
@@ -67,6 +68,7 @@ SIGNATURES = {
                                      c_void_p, c_int, POINTER(c_void_p), POINTER(c_void_p), c_int, c_int, c_void_p,
                                      c_int, c_int, c_int, c_int, c_int, c_double, c_void_p]),
     "mla_quantize_latent_i8": (c_int, [c_void_p, c_int, c_int64, c_int, c_int, c_void_p, c_void_p, c_void_p]),
+    "mla_quantize_latent_i4": (c_int, [c_void_p, c_int, c_int64, c_int, c_int, c_void_p, c_void_p, c_void_p]),
     "mla_qknorm_query": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_int, c_int, c_int, c_double, c_void_p,
                                  c_void_p]),
     "mla_qknorm_key_gram": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p]),

@@ -294,6 +294,22 @@ mla_status mla_quantize_latent_i8(const void* rows, int row_dtype, int64_t n_row
                     "mla_quantize_latent_i8 launch");
 }
 
+mla_status mla_quantize_latent_i4(const void* rows, int row_dtype, int64_t n_rows, int d_c, int d_rope,
+                                  void* out_rows, float* scales, void* stream) {
+  if (!rows || !out_rows || !scales) return fail(MLA_ERR_NULL, "mla_quantize_latent_i4: null pointer");
+  if (row_dtype != MLA_BF16) return fail(MLA_ERR_DTYPE, "mla_quantize_latent_i4: rows must be bf16 (got %d)", row_dtype);
+  if (n_rows < 0 || n_rows > ((int64_t)1 << 32) || d_c <= 0 || d_c > 512 || (d_c & 7) || d_rope <= 0 ||
+      d_rope > 128 || (d_rope & 7))
+    return fail(MLA_ERR_SHAPE, "mla_quantize_latent_i4: n_rows=%lld d_c=%d (multiple of 8, <= 512) d_rope=%d "
+                "(multiple of 8, <= 128)", (long long)n_rows, d_c, d_rope);
+  if ((reinterpret_cast<uintptr_t>(out_rows) & 3u) != 0 || (reinterpret_cast<uintptr_t>(scales) & 7u) != 0 ||
+      (reinterpret_cast<uintptr_t>(rows) & 1u) != 0)
+    return fail(MLA_ERR_ALIGN, "mla_quantize_latent_i4: out_rows 4-byte, scales 8-byte, rows 2-byte aligned");
+  if (n_rows == 0) return ok();
+  return hip_status(mla::launch_quantize_latent_i4(rows, n_rows, d_c, d_rope, out_rows, scales, (hipStream_t)stream),
+                    "mla_quantize_latent_i4 launch");
+}
+
 mla_status mla_qknorm_query(const void* q_nope, int in_dtype, const float* g_q, const float* g_k, int n_tok,
                             int n_heads, int d_nope, double eps, float* q_out, void* stream) {
   if (!q_nope || !g_q || !g_k || !q_out) return fail(MLA_ERR_NULL, "mla_qknorm_query: null pointer");
@@ -336,7 +352,7 @@ mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q
                               int cache_dtype, int batch, int s_q, int n_heads, int d_c, int d_rope, float scale,
                               float* o_part, float* lse_part, int n_part, int n_wg, void* stream) {
   if (!segs || !q_lat || !o_part || !lse_part) return fail(MLA_ERR_NULL, "mla_decode_splitkv: null pointer");
-  if (!dtype_ok(q_dtype) || !(dtype_ok(cache_dtype) || cache_dtype == MLA_I8))
+  if (!dtype_ok(q_dtype) || !(dtype_ok(cache_dtype) || cache_dtype == MLA_I8 || cache_dtype == MLA_I4))
     return fail(MLA_ERR_DTYPE, "mla_decode_splitkv: dtypes %d, %d", q_dtype, cache_dtype);
   if (cache_dtype == MLA_F32 && q_dtype != MLA_F32)
     return fail(MLA_ERR_UNSUPPORTED, "mla_decode_splitkv: an fp32 cache needs an fp32 query");
@@ -344,10 +360,11 @@ mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q
     return fail(MLA_ERR_SHAPE, "mla_decode_splitkv: n_segs=%d batch=%d s_q=%d n_heads=%d n_part=%d n_wg=%d",
                 n_segs, batch, s_q, n_heads, n_part, n_wg);
   if (!std::isfinite(scale)) return fail(MLA_ERR_SHAPE, "mla_decode_splitkv: scale is not finite");
-  const bool i8 = cache_dtype == MLA_I8;
-  const bool bf = cache_dtype == MLA_BF16 || i8;  // the MFMA kernel (16-bit or int8 latent rows)
+  const bool i8 = cache_dtype == MLA_I8, i4 = cache_dtype == MLA_I4;
+  const bool lowbit = i8 || i4;
+  const bool bf = cache_dtype == MLA_BF16 || lowbit;  // the MFMA kernels (16-bit, int8 or int4 rows)
   const bool q32 = q_dtype == MLA_F32;
-  if (i8 && !q32) return fail(MLA_ERR_UNSUPPORTED, "mla_decode_splitkv: an int8 cache needs an fp32 query");
+  if (lowbit && !q32) return fail(MLA_ERR_UNSUPPORTED, "mla_decode_splitkv: a low-bit cache needs an fp32 query");
   if (bf) {
     if (d_c != kBf16Dc || d_rope != kBf16Dr)
       return fail(MLA_ERR_UNSUPPORTED, "mla_decode_splitkv: bf16 path needs d_c=512, d_rope=64 (got %d, %d)", d_c,
@@ -395,14 +412,16 @@ mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q
                     (long long)((int64_t)batch * cap));
       if (s.row_rinv && q_dtype != MLA_F32)
         return fail(MLA_ERR_UNSUPPORTED, "segment %d: QK-Norm (row_rinv) needs an fp32 query", g);
-      if (i8 && !s.row_scale) return fail(MLA_ERR_NULL, "segment %d: an int8 cache needs row_scale", g);
-      if (i8 && s.row_rinv)
-        return fail(MLA_ERR_UNSUPPORTED, "segment %d: QK-Norm with an int8 cache is not supported", g);
+      if (lowbit && !s.row_scale) return fail(MLA_ERR_NULL, "segment %d: a low-bit cache needs row_scale", g);
+      if (lowbit && s.row_rinv)
+        return fail(MLA_ERR_UNSUPPORTED, "segment %d: QK-Norm with a low-bit cache is not supported", g);
+      if (i4 && (reinterpret_cast<uintptr_t>(s.row_scale) & 7u) != 0)
+        return fail(MLA_ERR_ALIGN, "segment %d: int4 row_scale must be 8-byte aligned", g);
     } else if ((int64_t)batch * s_q * s.head_count > 65535 || s.n_split > 65535) {
       return fail(MLA_ERR_UNSUPPORTED, "segment %d: fp32 path grid too large", g);
     }
-    if (!i8 && s.row_scale)
-      return fail(MLA_ERR_UNSUPPORTED, "segment %d: row_scale is only read with an int8 cache", g);
+    if (!lowbit && s.row_scale)
+      return fail(MLA_ERR_UNSUPPORTED, "segment %d: row_scale is only read with a low-bit cache", g);
     for (int h = s.head_begin; h < s.head_begin + s.head_count; ++h)
       for (int k = s.part_begin; k < s.part_begin + s.n_split; ++k) cover[(size_t)h * n_part + k]++;
   }
@@ -415,7 +434,7 @@ mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q
   int wg = n_wg > 0 ? n_wg : cu_count();
   if (wg <= 0) return fail(MLA_ERR_HIP, "mla_decode_splitkv: could not query the device");
   std::vector<mla::SegArgs> sa((size_t)n_segs);
-  bool rows_path = bf && q32 && !i8;  // fp32 query, 16-bit rows, no QK-Norm row factors
+  bool rows_path = bf && q32 && !lowbit;  // fp32 query, 16-bit rows, no QK-Norm row factors
   for (int g = 0; g < n_segs; ++g) {
     const mla_segment& s = segs[g];
     sa[g] = mla::SegArgs{s.cache,     s.block_table, s.seq_lens,  s.q_rot,      s.max_rows,
@@ -436,8 +455,8 @@ mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q
   a.scale = scale;
   // several segments on the row-owning path: one launch over all of them,
   // the grid split by each segment's share of the work
-  if (rows_path && n_segs > 1)
-    return hip_status(mla::launch_decode_rows_multi(a, sa.data(), n_segs, wg, (hipStream_t)stream),
+  if (i4 || (rows_path && n_segs > 1))
+    return hip_status(mla::launch_decode_rows_multi(a, sa.data(), n_segs, wg, i4, (hipStream_t)stream),
                       "mla_decode_splitkv launch");
   for (int g = 0; g < n_segs; ++g) {
     a.seg = sa[g];

@@ -115,12 +115,29 @@ constexpr float kRowsTau = 32.f;
 // MFMA and waits for it).  Groups of instruction kinds are filled in order:
 constexpr int kSchedDs = 0x080, kSchedMfma = 0x008, kSchedValu = 0x002;
 
+// int4 rows (the QuantMLA abstract's joint INT4 content and rotary caches):
+// 256 bytes of latent codes and 32 of rotary codes per stored row, two fp32
+// scales per row beside the cache.  A tile's codes (9 KiB) and scales land in
+// LDS by direct loads, two tiles ahead; each wave then unpacks 8 of its rows
+// into the bf16 stages (the codes themselves, exact small integers), one tile
+// ahead of the scores, and keeps its own copy of the tile's scales.
+constexpr int kI4Row = (kDc + kDr) / 2;                 // 288 bytes per stored row
+constexpr int kI4Codes = kTile * kI4Row;                // 9 KiB of codes per tile
+constexpr int kI4Land = kI4Codes + 256 * kRowsWaves;    // + one copy of the 32 scale pairs per wave
+constexpr int kI4Dma = 4;                               // loads per wave per tile
+static_assert(kI4Codes % (kRowsWaves * 256) == 0, "a wave's share of the codes is whole dword loads");
+
+template <bool I4>
 struct RowsSmem {
-  char lat[kLatStages][kCStage];   // 128 KiB
-  char rot[kRotStages][kRStage];   // 12 KiB
+  static constexpr int NLAT = I4 ? 3 : kLatStages;  // tiles it (PV), it+1 (QK), it+2 (unpacked into)
+  static constexpr int NROT = kRotStages;
+  char lat[NLAT][kCStage];   // 128 KiB (96 KiB)
+  char rot[NROT][kRStage];   // 12 KiB
   // bf16 hi parts of the rotary query of the group's 128 rows (a wave uses
   // only its own rows): rows of 128 B, chunks placed like the rotary ring's
   char qrot[16 * 2 * kRowsWaves][kRBytes];  // 16 KiB
+  char land[I4 ? 3 : 1][I4 ? kI4Land : 16];                   // int4: 30 KiB landing ring
+  float scl[I4 ? 3 : 1][kRowsWaves][I4 ? 2 * kTile : 1];      // int4: each wave's scales of a stage
   Piece pieces[kRowsMaxPieces];
   int n_pieces;
   int done;
@@ -143,6 +160,15 @@ typedef const __attribute__((address_space(4))) int32_t CInt;
 __device__ __forceinline__ void dma16(i32x4_t rsrc, const char* lds, int voffset) {
   const uint32_t m0 = (uint32_t)(uintptr_t)(MLA_LDS const char*)lds;
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// The 4-byte form: LDS address = lds + 4 * lane.
+__device__ __forceinline__ void dma4(i32x4_t rsrc, const char* lds, int voffset) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(MLA_LDS const char*)lds;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :
                : "s"(m0), "v"(voffset), "s"(rsrc)
                : "memory", "m0");
@@ -173,6 +199,46 @@ __device__ __forceinline__ void tile_load(i32x4_t rsrc, char* lat, char* rot, in
   }
 }
 
+// Wave w's kI4Dma loads of an int4 tile: bytes [2304 w, 2304 w + 2304) of its
+// codes (two 16-byte and one 4-byte load per lane) and its 32 scale pairs
+// (256 bytes, into the wave's own copy).
+__device__ __forceinline__ void tile_load_i4(i32x4_t codes, i32x4_t scales, char* land, int w, int lane) {
+  asm volatile("" : "+v"(lane));
+  const int base = w * (kI4Codes / kRowsWaves);
+  dma16(codes, land + base, base + 16 * lane);
+  dma16(codes, land + base + 1024, base + 1024 + 16 * lane);
+  dma4(codes, land + base + 2048, base + 2048 + 4 * lane);
+  dma4(scales, land + kI4Codes + 256 * w, 4 * lane);
+}
+
+// Eight packed 4-bit codes (entry e in bits 4 e .. 4 e + 3, two's complement)
+// as bf16 (exact).
+__device__ __forceinline__ bf16x8 unpack8_i4(uint32_t wd) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (bf16)(float)((int)(wd << (28 - 4 * e)) >> 28);
+  return r;
+}
+
+// Wave w unpacks rows 8 w .. 8 w + 7 of a landed int4 tile into the bf16
+// stages (latent: lane l = chunk l of each row; rotary: lane l = row 8 w +
+// l / 8, chunk l % 8) and copies the tile's scales (its own landed copy) to
+// its scale slot of the stage.
+__device__ __forceinline__ void unpack_tile_i4(const char* land, char* lat, char* rot, float* scl, int w,
+                                               int lane) {
+  asm volatile("" : "+v"(lane));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 8 * w + i;
+    const uint32_t wd = *(const uint32_t*)(land + r * kI4Row + 4 * lane);
+    *(bf16x8*)(lat + r * kCBytes + (cpos(r, lane) << 4)) = unpack8_i4(wd);
+  }
+  const int r = 8 * w + (lane >> 3), j = lane & 7;
+  const uint32_t wd = *(const uint32_t*)(land + r * kI4Row + kDc / 2 + 4 * j);
+  *(bf16x8*)(rot + r * kRBytes + (rpos(r, j) << 4)) = unpack8_i4(wd);
+  scl[lane] = *(const float*)(land + kI4Codes + 256 * w + 4 * lane);
+}
+
 // Scores of one tile for the wave's RB row blocks: S^T[32 tokens x 16 rows]
 // per block as two 16-token halves.  ls / rs: the tile's latent and rotary
 // stages (restrict: the compiler may then order these reads freely against
@@ -182,10 +248,12 @@ __device__ __forceinline__ void tile_load(i32x4_t rsrc, char* lat, char* rot, in
 // 4 ks + lg, sits at position (4 ks + lg) ^ l16 = 16 a + 4 (n ^ (l16 >> 2)) +
 // (lg ^ (l16 & 3)); rotary k-step jr: chunk 4 jr + lg at (4 jr + lg) ^
 // ((l16 >> 1) & 7).  Rows 16 + l16 share the swizzle key of row l16.
+// The rotary k-steps accumulate into sr (the same array as s, except for int4
+// rows, whose two parts take different scales).
 template <int RB>
 __device__ __forceinline__ void qk_tile(const char* __restrict__ ls, const char* __restrict__ rs,
                                         const char* __restrict__ qs, int lane, const bf16x8 (&qh)[RB][kDc / 32],
-                                        const bf16x8 (&qrl)[RB][2], f32x4 (&s)[2][RB]) {
+                                        const bf16x8 (&qrl)[RB][2], f32x4 (&s)[2][RB], f32x4 (&sr)[2][RB]) {
   asm volatile("" : "+v"(lane));
   const int xl = lane & 15, xg = lane >> 4;
   const char* kb[4];
@@ -196,7 +264,7 @@ __device__ __forceinline__ void qk_tile(const char* __restrict__ ls, const char*
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) s[tb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < RB; ++rb) s[tb][rb] = sr[tb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
   // K operands of k-step ks (ks < 16 latent, then 2 rotary), read kPre
   // k-steps ahead of their MFMAs
   auto kop = [&](int ks, int tb) -> bf16x8 {
@@ -228,10 +296,10 @@ __device__ __forceinline__ void qk_tile(const char* __restrict__ ls, const char*
         // rows, chunk 4 jr + lg (placed like the rotary ring)
         const int qr = 16 * rb + xl;
         const bf16x8 qrh = *(const bf16x8*)(qs + qr * kRBytes + (rpos(qr, 4 * jr + xg) << 4));
-        s[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qrh, s[0][rb], 0, 0, 0);
-        s[1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qrh, s[1][rb], 0, 0, 0);
-        s[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qrl[rb][jr], s[0][rb], 0, 0, 0);
-        s[1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qrl[rb][jr], s[1][rb], 0, 0, 0);
+        sr[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qrh, sr[0][rb], 0, 0, 0);
+        sr[1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qrh, sr[1][rb], 0, 0, 0);
+        sr[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qrl[rb][jr], sr[0][rb], 0, 0, 0);
+        sr[1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qrl[rb][jr], sr[1][rb], 0, 0, 0);
       }
     }
   }
@@ -288,14 +356,39 @@ __device__ __forceinline__ void pv_tile(const char* __restrict__ ls, int lane, c
 // tokens past the piece or the row's causal limit (relative index `lim` per
 // lane: token 4 lg + e of the first half is visible when e <= lim) get
 // weight 0.
-template <int RB>
-__device__ __forceinline__ bool softmax_tile(const f32x4 (&s)[2][RB], bool full, const int (&lim)[RB],
-                                             float (&m_used)[RB], float (&l_part)[RB], bf16x8 (&p)[RB],
-                                             float (&alpha)[RB]) {
+// int4 rows (I4): the score is s_c (latent part) + s_r (rotary part) with
+// the row's two scales, read from the wave's scale slot `tsc` of the tile
+// (pairs (s_c, s_r) per row), and each weight enters the PV product times its
+// row's latent scale (the PV multiplies the codes).
+template <int RB, bool I4 = false>
+__device__ __forceinline__ bool softmax_tile(const f32x4 (&s)[2][RB], const f32x4 (&sr)[2][RB], bool full,
+                                             const int (&lim)[RB], float (&m_used)[RB], float (&l_part)[RB],
+                                             bf16x8 (&p)[RB], float (&alpha)[RB], const float* tsc = nullptr) {
   bool need_any = false;
+  f32x4 sc[2][2];  // (tokens 4 lg .. 4 lg + 3 of each half) x (s_c, s_r) pairs
+  if constexpr (I4) {
+    int ln = __lane_id();
+    asm volatile("" : "+v"(ln));
+    const int lg4 = 4 * (ln >> 4);
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      sc[tb][0] = *(const f32x4*)(tsc + 2 * (16 * tb + lg4));
+      sc[tb][1] = *(const f32x4*)(tsc + 2 * (16 * tb + lg4) + 4);
+    }
+  }
+  // scale pair of token 4 lg + e of half tb: (s_c, s_r)
+  auto tok_sc = [&](int tb, int e) -> float { return sc[tb][e >> 1][2 * (e & 1)]; };
+  auto tok_sr = [&](int tb, int e) -> float { return sc[tb][e >> 1][2 * (e & 1) + 1]; };
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     f32x4 sa = s[0][rb], sb = s[1][rb];
+    if constexpr (I4) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sa[e] = tok_sc(0, e) * sa[e] + tok_sr(0, e) * sr[0][rb][e];
+        sb[e] = tok_sc(1, e) * sb[e] + tok_sr(1, e) * sr[1][rb][e];
+      }
+    }
     if (!full) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -318,8 +411,8 @@ __device__ __forceinline__ bool softmax_tile(const f32x4 (&s)[2][RB], bool full,
       const float p0 = __builtin_amdgcn_exp2f(sa[e] - msub);  // exp2(-inf) = 0
       const float p1 = __builtin_amdgcn_exp2f(sb[e] - msub);
       lsum += p0 + p1;
-      pv[e] = (bf16)p0;
-      pv[4 + e] = (bf16)p1;
+      pv[e] = (bf16)(I4 ? p0 * tok_sc(0, e) : p0);
+      pv[4 + e] = (bf16)(I4 ? p1 * tok_sc(1, e) : p1);
     }
     l_part[rb] = l_part[rb] * al + lsum;
     p[rb] = pv;
@@ -382,13 +475,24 @@ __device__ __forceinline__ void sched_pv() {
   }
 }
 
+// a when B, else b (same type): picks an accumulator at compile time
+template <bool B, class T>
+__device__ __forceinline__ T& pick(T& a, T& b) {
+  if constexpr (B) return a;
+  return b;
+}
+
 }  // namespace
 
-// RB: 16-row blocks per wave (1: 64-row groups, 2: 128-row groups).
-template <int RB>
+// RB: 16-row blocks per wave (1: 64-row groups, 2: 128-row groups).  I4:
+// int4 rows (packed latent and rotary codes, two scales per row).
+template <int RB, bool I4>
 __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch L) {
   constexpr int MT = 16 * RB * kRowsWaves;  // query rows of a row group
-  __shared__ __attribute__((aligned(16))) RowsSmem sm;
+  using SM = RowsSmem<I4>;
+  constexpr int NLAT = SM::NLAT;
+  constexpr int RBYTES = I4 ? kI4Row : kRowBytes;  // bytes per stored row
+  __shared__ __attribute__((aligned(16))) SM sm;
 
   // ---- the segment of this workgroup, and its place in the segment's grid ----
   int g = 0;
@@ -403,6 +507,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
   const int32_t* const seq_lens = sg.seq_lens;
   const float* const q_rot = (const float*)sg.q_rot;
   const float* const q_lat = (const float*)a.q_lat;
+  const float* const row_scale = sg.row_scale;
   float* const o_part = a.o_part;
   float* const lse_part = a.lse_part;
   const int64_t max_rows = sg.max_rows;
@@ -589,7 +694,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) vis[rb] = causal ? T - s_q + row_info(rb).tok : T - 1;
 
-      const char* const req_base = cache + (int64_t)b * max_rows * kRowBytes;
+      const char* const req_base = cache + (int64_t)b * max_rows * RBYTES;
       // block-table row of the request, read with scalar loads (the table is
       // constant for the launch): a tile's page id is requested one
       // iteration before its loads are issued, so the round trip is hidden
@@ -600,22 +705,46 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
       // count 0 and reads as zeros.  Every tile index, past the piece or not,
       // gets its kDmaPerWave loads per wave, so the loads in flight are
       // counted the same way in every iteration (they complete in order).
-      auto tile_rsrc = [&](int it, int pg) -> i32x4_t {
+      // (int4 rows: also their scale pairs, indexed like the rows)
+      auto tile_row = [&](int it, int pg, bool* ok) -> int64_t {
         const int t0 = pr0 + it * kTile;
-        const char* src;
-        bool ok = it < n_tiles;
-        if (!bt_row) {
-          src = req_base + (int64_t)t0 * kRowBytes;
-        } else {
-          ok = ok && pg >= 0 && pg < n_pages;
-          src = cache + ((int64_t)(ok ? pg : 0) * kPageSize + (t0 % kPageSize)) * kRowBytes;
-        }
-        return buffer_rsrc(ok ? src : cache, ok ? min(kTile, pr1 - t0) * kRowBytes : 0);
+        *ok = it < n_tiles;
+        if (!bt_row) return (int64_t)b * max_rows + t0;
+        *ok = *ok && pg >= 0 && pg < n_pages;
+        return (int64_t)(*ok ? pg : 0) * kPageSize + (t0 % kPageSize);
+      };
+      auto tile_rsrc = [&](int it, int pg) -> i32x4_t {
+        bool ok;
+        const int64_t row = tile_row(it, pg, &ok);
+        const int n = ok ? min(kTile, pr1 - (pr0 + it * kTile)) : 0;
+        return buffer_rsrc(ok ? cache + row * RBYTES : cache, n * RBYTES);
+      };
+      auto scale_rsrc = [&](int it, int pg) -> i32x4_t {
+        bool ok;
+        const int64_t row = tile_row(it, pg, &ok);
+        const int n = ok ? min(kTile, pr1 - (pr0 + it * kTile)) : 0;
+        return buffer_rsrc(ok ? row_scale + 2 * row : row_scale, n * 8);
+      };
+      auto load_i4 = [&](int it, int pg) {
+        tile_load_i4(tile_rsrc(it, pg), scale_rsrc(it, pg), sm.land[it % 3], wave, lane);
+      };
+      auto unpack_i4 = [&](int it) {
+        unpack_tile_i4(sm.land[it % 3], sm.lat[it % NLAT], sm.rot[it % kRotStages], sm.scl[it % 3][wave], wave,
+                       lane);
       };
 
       int pg_next = 0;  // page of the next tile to load (paged layout)
+      int pg_i4 = 0;    // int4: page of tile 3, loaded once tile 0 is unpacked
       // ---- the first tiles go out before the query loads ----
-      {
+      if constexpr (I4) {
+        int pg[5];
+#pragma unroll
+        for (int t = 0; t < 5; ++t) pg[t] = bt_row && t < n_tiles ? page_of(t) : 0;
+#pragma unroll
+        for (int t = 0; t < 3; ++t) load_i4(t, pg[t]);
+        pg_i4 = pg[3];
+        pg_next = pg[4];
+      } else {
         int pg[kLoadAhead + 1];
 #pragma unroll
         for (int t = 0; t <= kLoadAhead; ++t) pg[t] = bt_row && t < n_tiles ? page_of(t) : 0;
@@ -712,44 +841,75 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
       auto tile_full = [&](int it) { return pr0 + (it + 1) * kTile <= min(pr1, vis_min + 1); };
 
       f32x4 sacc[2][RB];
+      f32x4 racc_i4[2][RB];
+      f32x4(&racc)[2][RB] = pick<I4>(racc_i4, sacc);  // the rotary part's accumulator (apart for int4 only)
+      auto scl_of = [&](int it) -> const float* {
+        if constexpr (I4) return sm.scl[it % 3][wave];
+        return nullptr;
+      };
       bf16x8 p[RB];
       float alpha[RB];
       int lim[RB];
       // ---- tile 0: scores and softmax ----
-      static_assert(kLoadAhead == 3, "tiles 1 and 2 stay in flight over tile 0");
-      wait_vmcnt<2 * kDmaPerWave>();
-      wait_lgkm0();
-      barrier_raw();
+      if constexpr (I4) {
+        // tiles 0 and 1 landed (tile 2 in flight), unpacked by every wave;
+        // then tile 3 goes out into tile 0's landing stage
+        wait_vmcnt<kI4Dma>();
+        wait_lgkm0();
+        barrier_raw();
+        unpack_i4(0);
+        unpack_i4(1);
+        wait_lgkm0();
+        barrier_raw();
+        load_i4(3, pg_i4);
+      } else {
+        static_assert(kLoadAhead == 3, "tiles 1 and 2 stay in flight over tile 0");
+        wait_vmcnt<2 * kDmaPerWave>();
+        wait_lgkm0();
+        barrier_raw();
+      }
       if (wave_rows) {
-        qk_tile<RB>(sm.lat[0], sm.rot[0], qrot_w, lane, qh, qrl, sacc);
+        qk_tile<RB>(sm.lat[0], sm.rot[0], qrot_w, lane, qh, qrl, sacc, racc);
         tile_lim(0, lim);
-        softmax_tile<RB>(sacc, tile_full(0), lim, m_used, l_part, p, alpha);  // (its factor multiplies an empty O)
+        // (its factor multiplies an empty O)
+        softmax_tile<RB, I4>(sacc, racc, tile_full(0), lim, m_used, l_part, p, alpha, scl_of(0));
       }
       for (int it = 0; it + 1 < n_tiles; ++it) {
-        // tile it+1 in LDS (this wave's loads, with tile it+2 still in
-        // flight, then everyone's); every wave is past the PV of tile it-1 and
-        // the scores of tile it, so their stages take tile it+3, whose loads
-        // go out between the PV MFMAs of tile it
-        wait_vmcnt<kDmaPerWave>();
+        // 16-bit rows: tile it+1 in LDS (this wave's loads, with tile it+2
+        // still in flight, then everyone's); every wave is past the PV of
+        // tile it-1 and the scores of tile it, so their stages take tile it+3,
+        // whose loads go out between the PV MFMAs of tile it.
+        // int4 rows: tile it+2 landed (tile it+3 in flight) and tile it+1
+        // unpacked; every wave is past the PV of tile it-1, the scores of tile
+        // it and the unpacking of tile it+1, so tile it+2 is unpacked into the
+        // stages of tile it-1 and tile it+4 lands where tile it+1 did.
+        wait_vmcnt<I4 ? kI4Dma : kDmaPerWave>();
         wait_lgkm0();
         barrier_raw();
         const i32x4_t rs_next = tile_rsrc(it + kLoadAhead, pg_next);
-        char* const lat_next = sm.lat[(it + kLoadAhead) % kLatStages];
+        char* const lat_next = sm.lat[(it + kLoadAhead) % NLAT];
         char* const rot_next = sm.rot[(it + kLoadAhead) % kRotStages];
-        auto load_next = [&](int i) { tile_load(rs_next, lat_next, rot_next, wave, lane, i); };
+        auto load_next = [&](int i) {
+          if constexpr (!I4) tile_load(rs_next, lat_next, rot_next, wave, lane, i);
+        };
+        if constexpr (I4) {
+          load_i4(it + 4, pg_next);
+          unpack_i4(it + 2);
+        }
         if (!wave_rows) {
 #pragma unroll
           for (int i = 0; i < kDmaPerWave; ++i) load_next(i);
         } else {
           tile_lim(it + 1, lim);
-          qk_tile<RB>(sm.lat[(it + 1) % kLatStages], sm.rot[(it + 1) % kRotStages], qrot_w, lane, qh, qrl, sacc);
+          qk_tile<RB>(sm.lat[(it + 1) % NLAT], sm.rot[(it + 1) % kRotStages], qrot_w, lane, qh, qrl, sacc, racc);
           sched_qk<RB>();
           // the softmax of tile it+1 (its scores die here: only the two tiles'
           // P operands live across the PV product), then the PV of tile it
           bf16x8 pn[RB];
-          const bool moved = softmax_tile<RB>(sacc, tile_full(it + 1), lim, m_used, l_part, pn, alpha);
+          const bool moved = softmax_tile<RB, I4>(sacc, racc, tile_full(it + 1), lim, m_used, l_part, pn, alpha,
+                                                  scl_of(it + 1));
           __builtin_amdgcn_sched_barrier(0);
-          pv_tile<RB>(sm.lat[it % kLatStages], lane, p, acc, load_next);
+          pv_tile<RB>(sm.lat[it % NLAT], lane, p, acc, load_next);
           sched_pv<RB>();
           __builtin_amdgcn_sched_barrier(0);
           if (moved) scale_acc<RB>(acc, alpha);
@@ -759,7 +919,10 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
         // the page of the tile loaded next iteration: its scalar load returns
         // during the wait at the top (not inside the score product, where it
         // would force full waits on the LDS reads)
-        if (bt_row && it + kLoadAhead + 1 < n_tiles) pg_next = page_of(it + kLoadAhead + 1);
+        {
+          const int t_pg = it + (I4 ? 5 : kLoadAhead + 1);  // the tile loaded next iteration
+          if (bt_row && t_pg < n_tiles) pg_next = page_of(t_pg);
+        }
       }
       // the last tile's PV (the loads past the piece, which only wrote zeros
       // into free stages, are drained too: none may land after the
@@ -767,7 +930,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
       wait_vmcnt<0>();
       wait_lgkm0();
       barrier_raw();
-      if (wave_rows) pv_tile<RB>(sm.lat[(n_tiles - 1) % kLatStages], lane, p, acc, [](int) {});
+      if (wave_rows) pv_tile<RB>(sm.lat[(n_tiles - 1) % NLAT], lane, p, acc, [](int) {});
 
       // ---- epilogue: 1/l, the lse with the latent lo part's first-order
       // share, the normalised partial output.  Every load and product comes
@@ -820,8 +983,9 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
   }
 }
 
-template __global__ void decode_rows_kernel<1>(RowsLaunch);
-template __global__ void decode_rows_kernel<2>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<2, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, true>(RowsLaunch);
 
 int decode_rows_tile(int rows_total) { return rows_total <= 64 ? 64 : 128; }
 
@@ -851,25 +1015,26 @@ SegCost seg_cost(const DecodeArgs& a, const SegArgs& s, int mt) {
   return c;
 }
 
-hipError_t launch_rows(const RowsLaunch& L, int mt, int grid, hipStream_t stream) {
+hipError_t launch_rows(const RowsLaunch& L, int mt, bool i4, int grid, hipStream_t stream) {
   const dim3 block(kRowsThreads);
-  if (mt == 64) return launch(decode_rows_kernel<1>, dim3(grid), block, stream, L);
-  return launch(decode_rows_kernel<2>, dim3(grid), block, stream, L);
+  if (i4) return launch(decode_rows_kernel<1, true>, dim3(grid), block, stream, L);
+  if (mt == 64) return launch(decode_rows_kernel<1, false>, dim3(grid), block, stream, L);
+  return launch(decode_rows_kernel<2, false>, dim3(grid), block, stream, L);
 }
 
 }  // namespace
 
 hipError_t launch_decode_rows(const DecodeArgs& a, int n_wg, hipStream_t stream) {
-  return launch_decode_rows_multi(a, &a.seg, 1, n_wg, stream);
+  return launch_decode_rows_multi(a, &a.seg, 1, n_wg, false, stream);
 }
 
-hipError_t launch_decode_rows_multi(const DecodeArgs& a, const SegArgs* segs, int n_segs, int n_wg,
+hipError_t launch_decode_rows_multi(const DecodeArgs& a, const SegArgs* segs, int n_segs, int n_wg, bool i4,
                                     hipStream_t stream) {
   for (int g0 = 0; g0 < n_segs; g0 += kRowsMaxSegs) {
     const int n = std::min(kRowsMaxSegs, n_segs - g0);
     int rows_max = 0;
     for (int g = 0; g < n; ++g) rows_max = std::max(rows_max, a.s_q * segs[g0 + g].head_count);
-    const int mt = decode_rows_tile(rows_max);
+    const int mt = i4 ? 64 : decode_rows_tile(rows_max);  // int4 rows: 64-row groups
     RowsLaunch L{};
     L.a = a;
     L.n_segs = n;
@@ -911,7 +1076,7 @@ hipError_t launch_decode_rows_multi(const DecodeArgs& a, const SegArgs* segs, in
       L.wg_begin[g] = grid;
       grid += L.n_share[g] * L.n_rg[g];
     }
-    const hipError_t e = launch_rows(L, mt, grid, stream);
+    const hipError_t e = launch_rows(L, mt, i4, grid, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

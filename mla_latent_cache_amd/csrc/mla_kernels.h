@@ -104,6 +104,8 @@ hipError_t launch_combine_out_uv(const float* o_part, const float* lse_part, int
 // int8 latent cache writer: bf16 rows [n][d_c + d_rope] -> packed rows [n][d_c + 2 d_rope] bytes + scales.
 hipError_t launch_quantize_latent_i8(const void* rows, int64_t n_rows, int d_c, int d_rope, void* out,
                                      float* scales, hipStream_t stream);
+hipError_t launch_quantize_latent_i4(const void* rows, int64_t n_rows, int d_c, int d_rope, void* out,
+                                     float* scales, hipStream_t stream);
 // QK-Norm: query scaling, the key Gram matrix and the per-row inverse RMS.
 hipError_t launch_qknorm_query(const void* q_nope, bool in_bf16, const float* g_q, const float* g_k, int n_tok,
                                int n_heads, int d_nope, float eps, float* q_out, hipStream_t stream);
@@ -131,8 +133,9 @@ int decode_bf16_tile(int rows_total);
 // row groups of 64 (up to 64 rows) or 128; n_wg workgroups per row group.
 hipError_t launch_decode_rows(const DecodeArgs& a, int n_wg, hipStream_t stream);
 // All n_segs segments (any number; kRowsMaxSegs per launch) in row-owning
-// launches that split n_wg workgroups by estimated tile work.
-hipError_t launch_decode_rows_multi(const DecodeArgs& a, const SegArgs* segs, int n_segs, int n_wg,
+// launches that split n_wg workgroups by estimated tile work; i4: int4 rows
+// (64-row groups).
+hipError_t launch_decode_rows_multi(const DecodeArgs& a, const SegArgs* segs, int n_segs, int n_wg, bool i4,
                                     hipStream_t stream);
 // Rows of that kernel's row group for a segment of rows_total query rows.
 int decode_rows_tile(int rows_total);

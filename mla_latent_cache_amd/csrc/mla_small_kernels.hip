@@ -517,6 +517,58 @@ __global__ __launch_bounds__(256) void quantize_latent_i8_kernel(const bf16* __r
 // must fit 32 bits per dimension).
 constexpr int64_t kMaxStrideBlocks = 65536;
 
+// ---------------------------------------------------------------------------
+// int4 cache writer (QuantMLA abstract: joint INT4 caching of the content and
+// rotary caches; here the plain per-row symmetric form): one wave per stored
+// row, the content latent and the rotary key quantized separately.  For each
+// part: scale = amax / 7 (IEEE fp32 quotient), code_i = the nearest integer to
+// x_i / scale (fp32 quotient, ties to even) clamped to [-7, 7] (a zero part:
+// scale 0, codes 0).  Codes are packed two per byte, entry 2j in the low
+// nibble of byte j (4-bit two's complement): the packed row is d_c / 2
+// content bytes then d_rope / 2 rotary bytes; scales[r] = (content, rotary).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ unsigned pack8_i4(const float (&v)[8], float scale) {
+  unsigned w = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float q = scale > 0.f ? fminf(fmaxf(rintf(v[e] / scale), -7.f), 7.f) : 0.f;
+    w |= ((unsigned)(int)q & 0xfu) << (4 * e);
+  }
+  return w;
+}
+
+__global__ __launch_bounds__(256) void quantize_latent_i4_kernel(const bf16* __restrict__ rows, int64_t n_rows,
+                                                                 int d_c, int d_rope, char* __restrict__ out,
+                                                                 float* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  for (int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); r < n_rows; r += (int64_t)gridDim.x * 4) {
+    const bf16* src = rows + r * (d_c + d_rope);
+    char* dst = out + r * ((d_c + d_rope) / 2);
+    // lane owns content entries [8 lane, 8 lane + 8) and rotary entries
+    // [8 lane, 8 lane + 8) (d_c <= 512, d_rope <= 128, multiples of 8)
+    const bool mc = 8 * lane < d_c, mr = 8 * lane < d_rope;
+    float vc[8], vr[8], ac = 0.f, ar = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      vc[e] = mc ? (float)src[8 * lane + e] : 0.f;
+      vr[e] = mr ? (float)src[d_c + 8 * lane + e] : 0.f;
+      ac = fmaxf(ac, fabsf(vc[e]));
+      ar = fmaxf(ar, fabsf(vr[e]));
+    }
+    const float sc = wave_max(ac) / 7.f, sr = wave_max(ar) / 7.f;
+    if (mc) *(unsigned*)(dst + 4 * lane) = pack8_i4(vc, sc);
+    if (mr) *(unsigned*)(dst + d_c / 2 + 4 * lane) = pack8_i4(vr, sr);
+    if (lane == 0) *(float2*)(scales + 2 * r) = float2{sc, sr};
+  }  // rows (grid-stride: the grid is capped)
+}
+
+hipError_t launch_quantize_latent_i4(const void* rows, int64_t n_rows, int d_c, int d_rope, void* out,
+                                     float* scales, hipStream_t stream) {
+  const dim3 grid((unsigned)std::min<int64_t>((n_rows + 3) / 4, kMaxStrideBlocks));
+  return launch(quantize_latent_i4_kernel, grid, dim3(256), stream, (const bf16*)rows, n_rows, d_c, d_rope,
+                (char*)out, scales);
+}
+
 hipError_t launch_quantize_latent_i8(const void* rows, int64_t n_rows, int d_c, int d_rope, void* out,
                                      float* scales, hipStream_t stream) {
   const dim3 grid((unsigned)std::min<int64_t>((n_rows + 3) / 4, kMaxStrideBlocks));

@@ -11,14 +11,17 @@ from typing import List, Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import MLA_BF16, MLA_F32, MLA_I8, MlaSegment
+from ._lib import MLA_BF16, MLA_F32, MLA_I4, MLA_I8, MlaSegment
 
 _DT = {torch.float32: MLA_F32, torch.bfloat16: MLA_BF16}
 
 
-def _cache_dt(cache: torch.Tensor) -> int:
-    """Cache format: fp32 / bf16 rows, or packed int8 rows held as uint8 bytes."""
-    return MLA_I8 if cache.dtype == torch.uint8 else _dt(cache)
+def _cache_dt(cache: torch.Tensor, row_scale: Optional[torch.Tensor] = None) -> int:
+    """Cache format: fp32 / bf16 rows, or packed rows held as uint8 bytes: int8
+    (one scale per row) or int4 (a (latent, rotary) scale pair per row)."""
+    if cache.dtype != torch.uint8:
+        return _dt(cache)
+    return MLA_I4 if row_scale is not None and row_scale.dim() == cache.dim() else MLA_I8
 
 
 def _dt(t: torch.Tensor) -> int:
@@ -202,6 +205,22 @@ def quantize_latent_i8(rows: torch.Tensor, d_c: int, out: Optional[torch.Tensor]
     return out, scales
 
 
+def quantize_latent_i4(rows: torch.Tensor, d_c: int, out: Optional[torch.Tensor] = None,
+                       scales: Optional[torch.Tensor] = None):
+    """Int4 cache from bf16 rows [..., d_c + d_rope]: (packed rows uint8
+    [..., (d_c + d_rope) / 2], scales fp32 [..., 2] = (latent, rotary))."""
+    width = rows.shape[-1]
+    d_rope = width - d_c
+    n_rows = rows.numel() // width
+    if out is None:
+        out = torch.empty(rows.shape[:-1] + (width // 2,), dtype=torch.uint8, device=rows.device)
+    if scales is None:
+        scales = torch.empty(rows.shape[:-1] + (2,), dtype=torch.float32, device=rows.device)
+    _lib.call("mla_quantize_latent_i4", _ptr(rows), _dt(rows), n_rows, d_c, d_rope, _ptr(out), _ptr(scales),
+              _stream())
+    return out, scales
+
+
 def qknorm_query(q_nope: torch.Tensor, g_q: torch.Tensor, g_k: torch.Tensor, eps: float,
                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """QK-Norm of the content query with both static weights folded in:
@@ -252,7 +271,7 @@ class Segment:
     part_begin: int = 0
     n_split: int = 1
     row_rinv: Optional[torch.Tensor] = None      # fp32, cache.shape[:2] (QK-Norm)
-    row_scale: Optional[torch.Tensor] = None     # fp32, cache.shape[:2] (int8 cache, uint8 rows)
+    row_scale: Optional[torch.Tensor] = None     # fp32, cache.shape[:2] (int8) or + (2,) (int4); uint8 rows
 
     def to_c(self) -> MlaSegment:
         s = MlaSegment()
@@ -284,9 +303,9 @@ def decode_splitkv(segments: Sequence[Segment], q_lat: torch.Tensor, batch: int,
     n_tok, n_heads, d_c = q_lat.shape
     d_rope = segments[0].q_rot.shape[2]
     n_part = o_part.shape[2]
-    cache_dt = _cache_dt(segments[0].cache)
+    cache_dt = _cache_dt(segments[0].cache, segments[0].row_scale)
     for s in segments:
-        if _cache_dt(s.cache) != cache_dt or s.q_rot.dtype != q_lat.dtype:
+        if _cache_dt(s.cache, s.row_scale) != cache_dt or s.q_rot.dtype != q_lat.dtype:
             raise ValueError("segments must share the cache dtype; q_rot must have q_lat's dtype")
     arr = (MlaSegment * len(segments))(*[s.to_c() for s in segments])
     _lib.call("mla_decode_splitkv", arr, len(segments), _ptr(q_lat), _dt(q_lat), cache_dt, batch, s_q, n_heads,

@@ -18,10 +18,10 @@ mla_qknorm_query writes the query in fp32 and mla_prepare_q absorbs it
 against the bf16 U_K (hi + lo parts of the query on MFMA; other shapes use
 an fp32 copy of U_K).  Each segment carries the inverse RMS of its rows'
 content keys, computed once here from the cache (mla_qknorm_key_gram and
-mla_qknorm_key_rinv: the cache writer's share of the work).  With an int8
-cache (``quant="int8"``) each segment's bf16 rows are quantized here by
-mla_quantize_latent_i8 (again the cache writer's part) and the decode reads
-the packed rows and their scales.
+mla_qknorm_key_rinv: the cache writer's share of the work).  With an int8 or
+int4 cache (``quant="int8"`` / ``"int4"``) each segment's bf16 rows are
+quantized here by mla_quantize_latent_i8 / _i4 (again the cache writer's
+part) and the decode reads the packed rows and their scales.
 """
 from __future__ import annotations
 
@@ -126,11 +126,12 @@ class DecodeStep:
         caches = [s.cache for s in segments]
         scales = [None] * len(segments)
         if quant is not None:
-            if quant != "int8":
+            if quant not in ("int8", "int4"):
                 raise ValueError(f"unknown cache quantization {quant!r}")
-            q8 = [ops.quantize_latent_i8(s.cache, d_c) for s in segments]
-            caches = [c for c, _ in q8]
-            scales = [sc for _, sc in q8]
+            quantize = ops.quantize_latent_i8 if quant == "int8" else ops.quantize_latent_i4
+            qs = [quantize(s.cache, d_c) for s in segments]
+            caches = [c for c, _ in qs]
+            scales = [sc for _, sc in qs]
         self.segments = [
             ops.Segment(cache=caches[i], seq_lens=s.seq_lens, q_rot=self.q_rots[self.seg_rot[i]][1],
                         block_table=s.block_table, head_begin=s.head_begin, head_count=s.head_count,
@@ -279,7 +280,8 @@ class DecodeStep:
                                                self.q_lat.data_ptr(), dt(self.q_lat), n_tok, H, d_nope, d_c, st)))
         self._seg_arr = (_lib.MlaSegment * len(self.segments))(*[sg.to_c() for sg in self.segments])
         dec = [(lib.mla_decode_splitkv, (self._seg_arr, len(self.segments), self.q_lat.data_ptr(), dt(self.q_lat),
-                                         ops._cache_dt(self.segments[0].cache), self.batch, self.s_q, H, d_c, d_r,
+                                         ops._cache_dt(self.segments[0].cache, self.segments[0].row_scale),
+                                         self.batch, self.s_q, H, d_c, d_r,
                                          float(self.scale), self.o_part.data_ptr(), self.lse_part.data_ptr(),
                                          self.n_part, self.n_wg, st))]
         if self.fuse_post:

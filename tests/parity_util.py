@@ -30,6 +30,8 @@ def oracle_rows(x, seg, b):
     r = f64(seg.rows(b))
     if x.spec.quant == "int8":
         r = Q.quantized_rows(seg.rows(b).float().numpy(), x.spec.d_c)
+    elif x.spec.quant == "int4":
+        r = Q.quantized_rows_i4(seg.rows(b).float().numpy(), x.spec.d_c)
     return r
 
 

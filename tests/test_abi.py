@@ -154,6 +154,15 @@ def test_null_and_shape_errors_before_any_gpu_call(lib):
     assert _st(lib, "mla_quantize_latent_i8", P + 4, 1, 10, 512, 64, P, P, None) == 4
     assert _st(lib, "mla_quantize_latent_i8", P, 1, 0, 512, 64, P, P, None) == 0
     assert _st(lib, "mla_quantize_latent_i8", P, 1, (1 << 32) + 1, 512, 64, P, P, None) == 2
+    # mla_quantize_latent_i4(rows, row_dtype, n_rows, d_c, d_rope, out_rows, scales, stream)
+    assert _st(lib, "mla_quantize_latent_i4", P, 1, 10, 512, 64, P, None, None) == 1
+    assert _st(lib, "mla_quantize_latent_i4", P, 0, 10, 512, 64, P, P, None) == 3
+    assert _st(lib, "mla_quantize_latent_i4", P, 1, 10, 1024, 64, P, P, None) == 2
+    assert _st(lib, "mla_quantize_latent_i4", P, 1, 10, 512, 60, P, P, None) == 2
+    assert _st(lib, "mla_quantize_latent_i4", P, 1, 10, 512, 0, P, P, None) == 2
+    assert _st(lib, "mla_quantize_latent_i4", P, 1, 10, 512, 64, P + 2, P, None) == 4
+    assert _st(lib, "mla_quantize_latent_i4", P, 1, 10, 512, 64, P, P + 4, None) == 4
+    assert _st(lib, "mla_quantize_latent_i4", P, 1, 0, 512, 64, P, P, None) == 0
     # zero-size calls succeed without launching anything
     assert _st(lib, "mla_absorb_q", P, P, 1, P, 0, 0, 1, 128, 512, None) == 0
 
@@ -188,8 +197,12 @@ def test_null_and_shape_errors_before_any_gpu_call(lib):
     assert dec([seg()], dtype=2) == 1                     # row_scale missing
     assert dec([seg(row_scale=P)], dtype=2, q_dtype=1) == 5
     assert dec([seg(row_scale=P, row_rinv=P)], dtype=2) == 5
-    assert dec([seg(row_scale=P)], dtype=1) == 5          # row_scale only with an int8 cache
-    assert dec([seg(row_scale=P)], dtype=3) == 3
+    assert dec([seg(row_scale=P)], dtype=1) == 5          # row_scale only with a low-bit cache
+    # int4 cache (cache_dtype 3): the same rules
+    assert dec([seg()], dtype=3) == 1
+    assert dec([seg(row_scale=P)], dtype=3, q_dtype=1) == 5
+    assert dec([seg(row_scale=P, row_rinv=P)], dtype=3) == 5
+    assert dec([seg(row_scale=P)], dtype=4) == 3
 
 
 def test_size_limits_refused(lib):

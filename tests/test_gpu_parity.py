@@ -164,6 +164,20 @@ EDGE = {
                 online=True),)),
     "int8_peaked_rows64": _custom("edge-i8-64", batch=4, heads=64, quant="int8", scale=2 / math.sqrt(192), segs=(
         SegSpec("kv", lengths=(1, 37, 300, 1000), online=True),)),
+    # int4 cache (latent and rotary codes, two scales per row): one wave with
+    # rows (16 rows), causal rows over pages, 64-row groups with
+    # twice-spread scores, two 64-row groups of one request (128 heads) and
+    # the merge layout's segments in one launch
+    "int4_rows16": _custom("edge-i4-16", batch=4, heads=16, quant="int4", segs=(
+        SegSpec("kv", lengths=(0, 1, 37, 300), online=True),)),
+    "int4_rows32_causal": _custom("edge-i4-32", batch=3, heads=16, s_q=2, quant="int4", segs=(
+        SegSpec("kv", lengths=(2, 95, 513), causal=True, layout="paged", page_size=64, spare_pages=1,
+                online=True),)),
+    "int4_peaked_rows64": _custom("edge-i4-64", batch=4, heads=64, quant="int4", scale=2 / math.sqrt(192), segs=(
+        SegSpec("kv", lengths=(1, 37, 300, 1000), online=True),)),
+    "int4_rows128_paged": _custom("edge-i4-128", batch=3, heads=128, quant="int4", segs=(
+        SegSpec("kv", lengths=(64, 130, 1500), layout="paged", page_size=64, spare_pages=3, online=True),)),
+    "int4_merge_layout": replace(M.mini_spec("merge"), name="edge-i4-merge", quant="int4"),
 }
 
 
@@ -459,6 +473,35 @@ def test_quantize_call():
     assert got_codes[5, 17] == -127 and int(np.count_nonzero(got_codes[5])) == 1
 
 
+def test_quantize_i4_call():
+    """mla_quantize_latent_i4 against the oracle's int4 quantizer, bit for
+    bit: packed bytes and both scales.  Rows: random at many magnitudes, a
+    zero row, a row at unit scale with exact ties in both parts, one with a
+    single nonzero latent entry."""
+    import oracle.mla_quant as Q
+    from mla_latent_cache_amd import ops
+    g = torch.Generator().manual_seed(18)
+    n, d_c, d_r = 1000, 512, 64
+    rows = torch.randn((n, d_c + d_r), generator=g) * torch.exp(torch.empty((n, 1)).uniform_(-10, 10, generator=g))
+    rows[3] = 0
+    rows[4] = torch.tensor([7.0, 0.5, 1.5, 2.5, -0.5, -1.5, -6.5, 6.5] * 72)
+    rows[5, :d_c] = 0
+    rows[5, 17] = -3.0
+    rows = rows.to(torch.bfloat16)
+    packed, scales = ops.quantize_latent_i4(rows.cuda(), d_c)
+    torch.cuda.synchronize()
+    packed, scales = packed.cpu().numpy(), scales.cpu().numpy()
+    p_ref, s_ref = Q.quantize_cache_i4(rows.float().numpy(), d_c)
+    assert packed.shape == p_ref.shape and scales.shape == s_ref.shape
+    assert np.array_equal(scales.view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(packed, p_ref), int(np.sum(packed != p_ref))
+    codes = Q.unpack_i4(packed)
+    assert codes[4, :8].tolist() == [7, 0, 2, 2, 0, -2, -6, 6]
+    assert codes[4, d_c:d_c + 8].tolist() == [7, 0, 2, 2, 0, -2, -6, 6]
+    assert float(scales[3, 0]) == 0.0 and float(scales[3, 1]) == 0.0 and not np.any(packed[3])
+    assert codes[5, 17] == -7 and int(np.count_nonzero(codes[5, :d_c])) == 1
+
+
 # ------------------------------------------------------------ full sizes, sampled
 @pytest.mark.parametrize("out_dtype,w_dtype,dims", [
     (torch.bfloat16, torch.bfloat16, (4, 16, 65, 512, 128)),   # the 512-column register path
@@ -504,14 +547,14 @@ def test_combine_out_uv_call(out_dtype, w_dtype, dims):
     assert np.all(np.abs(f64(out) - out_ref) <= rel * np.abs(out_ref) + 1e-5 * rms)
 
 
-@pytest.mark.parametrize("name", ["small", "dsv3", "long", "merge", "prefill", "qknorm", "int8"])
+@pytest.mark.parametrize("name", ["small", "dsv3", "long", "merge", "prefill", "qknorm", "int8", "int4"])
 def test_full_size_sampled(name):
     """The bench's launch configuration (default grid) at full size; the
     oracle checks sampled (request, head) pairs."""
     x = M.make(name, SEEDS[name])
     print(f"[parity] full {name} seed {SEEDS[name]}", flush=True)
     _, out, o_lat, lse = _run(x)
-    n_req = {"small": 2, "dsv3": 3, "long": 1, "merge": 2, "prefill": 1, "qknorm": 2, "int8": 1}[name]
+    n_req = {"small": 2, "dsv3": 3, "long": 1, "merge": 2, "prefill": 1, "qknorm": 2, "int8": 1, "int4": 1}[name]
     reqs, heads = sample_pairs(x, n_req, 3, seed=SEEDS[name])
     errs = check_step(x, out, o_lat, lse, requests=reqs, heads=heads, label=f"{name} full")
     print(f"[parity] {name} full reqs={reqs} heads={heads}: {errs}", flush=True)
