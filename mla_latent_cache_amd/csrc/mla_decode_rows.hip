@@ -212,11 +212,35 @@ __device__ __forceinline__ void tile_load_i4(i32x4_t codes, i32x4_t scales, char
 }
 
 // Eight packed 4-bit codes (entry e in bits 4 e .. 4 e + 3, two's complement)
-// as bf16 (exact).
+// as bf16 codes / 16 (exact; the scales carry the factor 16).  The gfx9
+// signed-nibble conversion takes bits 0..3 of a byte picked by SDWA: entry
+// 2k from byte k of the word, entry 2k + 1 from byte k of the word shifted
+// right by 4.
+template <int K>
+__device__ __forceinline__ float nib16(uint32_t w) {
+  float r;
+  if constexpr (K == 0)
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(r) : "v"(w));
+  else if constexpr (K == 1)
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(w));
+  else if constexpr (K == 2)
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(w));
+  else
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(w));
+  return r;
+}
+constexpr float kI4Unit = 16.f;  // unpacked value = code / kI4Unit
 __device__ __forceinline__ bf16x8 unpack8_i4(uint32_t wd) {
+  const uint32_t hi = wd >> 4;
   bf16x8 r;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = (bf16)(float)((int)(wd << (28 - 4 * e)) >> 28);
+  r[0] = (bf16)nib16<0>(wd);
+  r[1] = (bf16)nib16<0>(hi);
+  r[2] = (bf16)nib16<1>(wd);
+  r[3] = (bf16)nib16<1>(hi);
+  r[4] = (bf16)nib16<2>(wd);
+  r[5] = (bf16)nib16<2>(hi);
+  r[6] = (bf16)nib16<3>(wd);
+  r[7] = (bf16)nib16<3>(hi);
   return r;
 }
 
@@ -224,19 +248,24 @@ __device__ __forceinline__ bf16x8 unpack8_i4(uint32_t wd) {
 // stages (latent: lane l = chunk l of each row; rotary: lane l = row 8 w +
 // l / 8, chunk l % 8) and copies the tile's scales (its own landed copy) to
 // its scale slot of the stage.
-__device__ __forceinline__ void unpack_tile_i4(const char* land, char* lat, char* rot, float* scl, int w,
-                                               int lane) {
+__device__ __forceinline__ void unpack_tile_i4(const char* __restrict__ land, char* __restrict__ lat,
+                                               char* __restrict__ rot, float* __restrict__ scl, int w, int lane) {
   asm volatile("" : "+v"(lane));
+  // every read first (the landing stage and the bf16 stages never overlap),
+  // then the conversions and writes
+  const int rr = 8 * w + (lane >> 3), j = lane & 7;
+  uint32_t wd[9];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) wd[i] = *(const uint32_t*)(land + (8 * w + i) * kI4Row + 4 * lane);
+  wd[8] = *(const uint32_t*)(land + rr * kI4Row + kDc / 2 + 4 * j);
+  const float sv = *(const float*)(land + kI4Codes + 256 * w + 4 * lane);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = 8 * w + i;
-    const uint32_t wd = *(const uint32_t*)(land + r * kI4Row + 4 * lane);
-    *(bf16x8*)(lat + r * kCBytes + (cpos(r, lane) << 4)) = unpack8_i4(wd);
+    *(bf16x8*)(lat + r * kCBytes + (cpos(r, lane) << 4)) = unpack8_i4(wd[i]);
   }
-  const int r = 8 * w + (lane >> 3), j = lane & 7;
-  const uint32_t wd = *(const uint32_t*)(land + r * kI4Row + kDc / 2 + 4 * j);
-  *(bf16x8*)(rot + r * kRBytes + (rpos(r, j) << 4)) = unpack8_i4(wd);
-  scl[lane] = *(const float*)(land + kI4Codes + 256 * w + 4 * lane);
+  *(bf16x8*)(rot + rr * kRBytes + (rpos(rr, j) << 4)) = unpack8_i4(wd[8]);
+  scl[lane] = sv;
 }
 
 // Scores of one tile for the wave's RB row blocks: S^T[32 tokens x 16 rows]
@@ -376,9 +405,10 @@ __device__ __forceinline__ bool softmax_tile(const f32x4 (&s)[2][RB], const f32x
       sc[tb][1] = *(const f32x4*)(tsc + 2 * (16 * tb + lg4) + 4);
     }
   }
-  // scale pair of token 4 lg + e of half tb: (s_c, s_r)
-  auto tok_sc = [&](int tb, int e) -> float { return sc[tb][e >> 1][2 * (e & 1)]; };
-  auto tok_sr = [&](int tb, int e) -> float { return sc[tb][e >> 1][2 * (e & 1) + 1]; };
+  // scale pair of token 4 lg + e of half tb: (s_c, s_r), times the factor
+  // the unpacked codes lack
+  auto tok_sc = [&](int tb, int e) -> float { return kI4Unit * sc[tb][e >> 1][2 * (e & 1)]; };
+  auto tok_sr = [&](int tb, int e) -> float { return kI4Unit * sc[tb][e >> 1][2 * (e & 1) + 1]; };
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     f32x4 sa = s[0][rb], sb = s[1][rb];
