@@ -100,8 +100,10 @@ constexpr int kTileDma = kTile + kRStage / 1024;       // 36 wave-instructions p
 constexpr int kDmaPerWave = kTileDma / kRowsWaves;     // 9
 static_assert(kTileDma % kRowsWaves == 0, "every wave issues the same share of a tile's loads");
 constexpr int kRowsMaxPieces = 64;
-constexpr int kPvPre = 4;              // PV: column blocks of transposed reads in flight
-constexpr int kQkPre = 3;              // QK: k-steps of K-operand reads in flight
+// Operand reads in flight ahead of their MFMAs (deeper with 16 rows per wave,
+// which has registers to spare and fewer MFMAs per read to cover latency)
+template <int RB> constexpr int kPvPre = RB == 1 ? 8 : 4;   // PV: column blocks of transposed reads
+template <int RB> constexpr int kQkPre = RB == 1 ? 6 : 3;   // QK: k-steps of K-operand reads
 // Lazy rescale threshold (log2 units): a row's running max moves only when a
 // tile's max exceeds it by more than this, so weights reach 2^32 at most.
 // bf16 weights and fp32 sums keep their relative precision at any magnitude
@@ -300,7 +302,7 @@ __device__ __forceinline__ void qk_tile(const char* __restrict__ ls, const char*
     if (ks < kDc / 32) return *(const bf16x8*)(kb[ks & 3] + (ks >> 2) * 256 + tb * 16 * kCBytes);
     return *(const bf16x8*)(rb0 + (((4 * (ks - kDc / 32) + xg) ^ xr) << 4) + tb * 16 * kRBytes);
   };
-  constexpr int kPre = kQkPre;
+  constexpr int kPre = kQkPre<RB>;
   bf16x8 ka[kPre + 1][2];
 #pragma unroll
   for (int i = 0; i < kPre; ++i) {
@@ -360,7 +362,7 @@ __device__ __forceinline__ void pv_tile(const char* __restrict__ ls, int lane, c
     return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
   };
   // C^T operands read kPvPre column blocks ahead of their MFMAs
-  constexpr int kPre = kPvPre;
+  constexpr int kPre = kPvPre<RB>;
   bf16x8 ca[kPre + 1];
 #pragma unroll
   for (int i = 0; i < kPre; ++i) ca[i] = cop(i);
@@ -479,7 +481,7 @@ __device__ __forceinline__ void scale_acc(f32x4 (&acc)[32][RB], const float (&al
 // k-steps, which multiply the hi and lo query parts).
 template <int RB>
 __device__ __forceinline__ void sched_qk() {
-  __builtin_amdgcn_sched_group_barrier(kSchedDs, 2 * kQkPre, 0);
+  __builtin_amdgcn_sched_group_barrier(kSchedDs, 2 * kQkPre<RB>, 0);
 #pragma unroll
   for (int ks = 0; ks < kDc / 32; ++ks) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * RB, 0);
@@ -497,11 +499,11 @@ __device__ __forceinline__ void sched_qk() {
 // pattern.)
 template <int RB>
 __device__ __forceinline__ void sched_pv() {
-  __builtin_amdgcn_sched_group_barrier(kSchedDs, 2 * kPvPre, 0);
+  __builtin_amdgcn_sched_group_barrier(kSchedDs, 2 * kPvPre<RB>, 0);
 #pragma unroll
   for (int db = 0; db < 32; ++db) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, RB, 0);
-    if (db + kPvPre < 32) __builtin_amdgcn_sched_group_barrier(kSchedDs, 2, 0);
+    if (db + kPvPre<RB> < 32) __builtin_amdgcn_sched_group_barrier(kSchedDs, 2, 0);
   }
 }
 
