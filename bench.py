@@ -32,7 +32,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 MALL_BYTES = 256 << 20          # Infinity Cache: rotate caches so every step reads HBM
 DECODE_SRCS = [os.path.join(ROOT, "mla_latent_cache_amd", "csrc", f)
-               for f in ("mla_decode_bf16.hip", "mla_decode_rows.hip")]
+               for f in ("mla_decode_bf16.hip", "mla_decode_rows.hip", "mla_decode_tile.h")]
 SEEDS = {"toy": 0, "small": 1, "dsv3": 2, "long": 3, "merge": 4, "prefill": 5, "qknorm": 6, "int8": 7, "int4": 8}
 
 
@@ -68,7 +68,22 @@ def algorithmic(x):
 
 def ops_cache_dt(step) -> int:
     from mla_latent_cache_amd import ops
-    return ops._cache_dt(step.segments[0].cache)
+    return ops._cache_dt(step.segments[0].cache, step.segments[0].row_scale)
+
+
+def decode_kernel_name(x) -> str:
+    """The decode kernel a workload's launches run (the routing of
+    mla_decode_splitkv)."""
+    sp = x.spec
+    rows = [sp.s_q * (s.head_count or sp.heads) for s in x.segments]
+    if sp.dtype != "bf16":
+        return "decode_f32_kernel"
+    if sp.quant == "int4":
+        return "decode_rows_kernel<1, true> (int4 rows, 64-row groups)"
+    if sp.quant == "int8" or sp.qk_norm or (len(rows) == 1 and rows[0] <= 32):
+        return "decode_bf16_kernel"
+    rb = 1 if max(rows) <= 64 else 2
+    return f"decode_rows_kernel<{rb}, false> ({64 * rb}-row groups)"
 
 
 def kernel_hash() -> str:
@@ -351,7 +366,7 @@ def main():
              if mfma_bound else
              {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
               "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}),
-            kernel="mla_decode_splitkv (decode_bf16_kernel)", decode_us=round(dec_us, 3),
+            kernel=f"mla_decode_splitkv ({decode_kernel_name(x)})", decode_us=round(dec_us, 3),
             algorithmic_bytes=nbytes, algorithmic_flops=flops, tflops=round(tflops, 2),
             mfma_frac=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)),
         "cpu_baseline": None,
