@@ -191,7 +191,10 @@ typedef struct {
  *          weight multiplies sc_t code_t, the attention over the
  *          dequantized rows; they run on the row-owning kernel in groups of
  *          64 query rows, the codes unpacked inside the streaming loop.
- * o_part   [n_tok][n_heads][n_part][d_c] fp32    output
+ * o_part   [n_tok][n_heads][n_part][d_c] part_dtype  output: fp32, or bf16 (the
+ *          normalised partial rounded to nearest; half the bytes to write
+ *          and to merge, relative error 2^-9 per entry; fp32 caches write
+ *          fp32 partials only)
  * lse_part [n_tok][n_heads][n_part]      fp32    output
  * n_tok = batch * s_q.  n_wg = workgroups per launch (0 = one per compute unit,
  * at most 65536).  With an fp32 query and a bf16 cache, segments of more than
@@ -205,7 +208,7 @@ typedef struct {
  */
 mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q_lat, int q_dtype,
                               int cache_dtype, int batch, int s_q, int n_heads, int d_c, int d_rope,
-                              float scale, float* o_part, float* lse_part, int n_part, int n_wg,
+                              float scale, void* o_part, int part_dtype, float* lse_part, int n_part, int n_wg,
                               void* stream);
 
 /*
@@ -217,13 +220,14 @@ mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q
  * A row whose slots are all -inf gives o_lat = 0, lse = -inf.  o_part rows of
  * -inf slots are never read.
  *
- * o_part   [n_rows][n_part][d_c] fp32 (16-byte aligned, d_c a multiple of 4;
- *          n_rows < 2^24)
+ * o_part   [n_rows][n_part][d_c] part_dtype (fp32 or bf16; 16-byte aligned, d_c a
+ *          multiple of 4; n_rows < 2^24)
  * lse_part [n_rows][n_part]      fp32 (n_part <= 1024)
  * o_lat    [n_rows][d_c]         out_dtype (MLA_BF16 or MLA_F32)
  * lse      [n_rows]              fp32, or NULL if not wanted
+ * The sums are taken in fp32 whatever the partials' storage.
  */
-mla_status mla_combine_lse(const float* o_part, const float* lse_part, int n_rows, int n_part,
+mla_status mla_combine_lse(const void* o_part, int part_dtype, const float* lse_part, int n_rows, int n_part,
                            int d_c, void* o_lat, int out_dtype, float* lse, void* stream);
 
 /*
@@ -339,7 +343,7 @@ mla_status mla_out_proj(const void* x, int x_dtype, const void* w_o, int w_dtype
  * each row's output columns are split over 2 or 4 workgroups, each of which
  * merges the row itself.
  *
- * o_part   [n_tok][n_heads][n_part][d_c] fp32 (16-byte aligned)
+ * o_part   [n_tok][n_heads][n_part][d_c] part_dtype (fp32 or bf16; 16-byte aligned)
  * lse_part [n_tok][n_heads][n_part]      fp32 (n_part <= 1024)
  * w_uv     [n_heads][d_v][d_c]           w_dtype
  * o_lat    [n_tok][n_heads][d_c]         out_dtype, or NULL if not wanted
@@ -349,9 +353,9 @@ mla_status mla_out_proj(const void* x, int x_dtype, const void* w_o, int w_dtype
  * n_tok * n_heads <= 2^21.
  * Errors: MLA_ERR_NULL, MLA_ERR_DTYPE, MLA_ERR_SHAPE as for the two calls.
  */
-mla_status mla_combine_out_uv(const float* o_part, const float* lse_part, int n_tok, int n_heads, int n_part,
-                              int d_c, const void* w_uv, int w_dtype, int d_v, void* o_lat, float* lse, void* out,
-                              int out_dtype, void* stream);
+mla_status mla_combine_out_uv(const void* o_part, int part_dtype, const float* lse_part, int n_tok, int n_heads,
+                              int n_part, int d_c, const void* w_uv, int w_dtype, int d_v, void* o_lat, float* lse,
+                              void* out, int out_dtype, void* stream);
 
 /*
  * mla_quantize_latent_i8 -- write an int8 latent cache (the cache writer's

@@ -52,14 +52,14 @@ SIGNATURES = {
     "mla_absorb_q": (c_int, [c_void_p, c_void_p, c_int, c_void_p, c_int, c_int, c_int, c_int, c_int,
                              c_void_p]),
     "mla_decode_splitkv": (c_int, [POINTER(MlaSegment), c_int, c_void_p, c_int, c_int, c_int, c_int, c_int,
-                                   c_int, c_int, c_float, c_void_p, c_void_p, c_int, c_int, c_void_p]),
-    "mla_combine_lse": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_void_p, c_int, c_void_p,
+                                   c_int, c_int, c_float, c_void_p, c_int, c_void_p, c_int, c_int, c_void_p]),
+    "mla_combine_lse": (c_int, [c_void_p, c_int, c_void_p, c_int, c_int, c_int, c_void_p, c_int, c_void_p,
                                 c_void_p]),
     "mla_out_uv": (c_int, [c_void_p, c_int, c_void_p, c_int, c_void_p, c_int, c_int, c_int, c_int, c_int,
                            c_void_p]),
     "mla_out_proj": (c_int, [c_void_p, c_int, c_void_p, c_int, c_void_p, c_int, c_int, c_int, c_int,
                              c_void_p]),
-    "mla_combine_out_uv": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_int, c_int,
+    "mla_combine_out_uv": (c_int, [c_void_p, c_int, c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_int, c_int,
                                    c_void_p, c_void_p, c_void_p, c_int, c_void_p]),
     "mla_prepare_q": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_int, c_void_p, c_int, POINTER(c_void_p),
                               POINTER(c_void_p), c_int, c_int, c_void_p, c_int, c_int, c_int, c_int, c_int,

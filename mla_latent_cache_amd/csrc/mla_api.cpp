@@ -247,33 +247,36 @@ mla_status mla_out_proj(const void* x, int x_dtype, const void* w_o, int w_dtype
                     "mla_out_proj launch");
 }
 
-mla_status mla_combine_lse(const float* o_part, const float* lse_part, int n_rows, int n_part, int d_c,
-                           void* o_lat, int out_dtype, float* lse, void* stream) {
+mla_status mla_combine_lse(const void* o_part, int part_dtype, const float* lse_part, int n_rows, int n_part,
+                           int d_c, void* o_lat, int out_dtype, float* lse, void* stream) {
   if (!o_part || !lse_part || !o_lat) return fail(MLA_ERR_NULL, "mla_combine_lse: null pointer");
-  if (!dtype_ok(out_dtype)) return fail(MLA_ERR_DTYPE, "mla_combine_lse: out_dtype %d", out_dtype);
+  if (!dtype_ok(out_dtype) || !dtype_ok(part_dtype))
+    return fail(MLA_ERR_DTYPE, "mla_combine_lse: dtypes %d, %d", part_dtype, out_dtype);
   if (n_rows < 0 || n_rows >= (1 << 24) || n_part <= 0 || n_part > 1024 || d_c <= 0 || d_c > 4096 || (d_c & 3) ||
       ((reinterpret_cast<uintptr_t>(o_part) & 15u) != 0))
     return fail(MLA_ERR_SHAPE, "mla_combine_lse: n_rows=%d n_part=%d (<= 1024) d_c=%d (multiple of 4, "
                 "o_part 16-byte aligned)", n_rows, n_part, d_c);
   if (n_rows == 0) return ok();
-  return hip_status(mla::launch_combine(o_part, lse_part, n_rows, n_part, d_c, o_lat, out_dtype == MLA_BF16,
+  return hip_status(mla::launch_combine(o_part, part_dtype == MLA_BF16, lse_part, n_rows, n_part, d_c, o_lat,
+                                        out_dtype == MLA_BF16,
                                         lse, (hipStream_t)stream),
                     "mla_combine_lse launch");
 }
 
-mla_status mla_combine_out_uv(const float* o_part, const float* lse_part, int n_tok, int n_heads, int n_part,
-                              int d_c, const void* w_uv, int w_dtype, int d_v, void* o_lat, float* lse, void* out,
-                              int out_dtype, void* stream) {
+mla_status mla_combine_out_uv(const void* o_part, int part_dtype, const float* lse_part, int n_tok, int n_heads,
+                              int n_part, int d_c, const void* w_uv, int w_dtype, int d_v, void* o_lat, float* lse,
+                              void* out, int out_dtype, void* stream) {
   if (!o_part || !lse_part || !w_uv || !out) return fail(MLA_ERR_NULL, "mla_combine_out_uv: null pointer");
-  if (!dtype_ok(w_dtype) || !dtype_ok(out_dtype))
-    return fail(MLA_ERR_DTYPE, "mla_combine_out_uv: dtypes %d, %d", w_dtype, out_dtype);
+  if (!dtype_ok(w_dtype) || !dtype_ok(out_dtype) || !dtype_ok(part_dtype))
+    return fail(MLA_ERR_DTYPE, "mla_combine_out_uv: dtypes %d, %d, %d", part_dtype, w_dtype, out_dtype);
   if (n_tok < 0 || n_tok > 65535 || n_heads <= 0 || n_heads > 65535 || (int64_t)n_tok * n_heads > (1 << 21) ||
       n_part <= 0 || n_part > 1024 || d_c <= 0 || d_c > 512 || (d_c & 3) || d_v <= 0 || d_v > 128 ||
       ((reinterpret_cast<uintptr_t>(o_part) & 15u) != 0))
     return fail(MLA_ERR_SHAPE, "mla_combine_out_uv: n_tok=%d n_heads=%d (rows <= 2^21) n_part=%d (<= 1024) d_c=%d "
                 "(multiple of 4, <= 512) d_v=%d (<= 128), o_part 16-byte aligned", n_tok, n_heads, n_part, d_c, d_v);
   if (n_tok == 0) return ok();
-  return hip_status(mla::launch_combine_out_uv(o_part, lse_part, n_tok, n_heads, n_part, d_c, w_uv,
+  return hip_status(mla::launch_combine_out_uv(o_part, part_dtype == MLA_BF16, lse_part, n_tok, n_heads, n_part,
+                                               d_c, w_uv,
                                                w_dtype == MLA_BF16, d_v, o_lat, lse, out, out_dtype == MLA_BF16,
                                                (hipStream_t)stream),
                     "mla_combine_out_uv launch");
@@ -350,12 +353,15 @@ mla_status mla_qknorm_key_rinv(const void* rows, int row_dtype, int64_t n_rows, 
 
 mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q_lat, int q_dtype,
                               int cache_dtype, int batch, int s_q, int n_heads, int d_c, int d_rope, float scale,
-                              float* o_part, float* lse_part, int n_part, int n_wg, void* stream) {
+                              void* o_part, int part_dtype, float* lse_part, int n_part, int n_wg, void* stream) {
   if (!segs || !q_lat || !o_part || !lse_part) return fail(MLA_ERR_NULL, "mla_decode_splitkv: null pointer");
-  if (!dtype_ok(q_dtype) || !(dtype_ok(cache_dtype) || cache_dtype == MLA_I8 || cache_dtype == MLA_I4))
-    return fail(MLA_ERR_DTYPE, "mla_decode_splitkv: dtypes %d, %d", q_dtype, cache_dtype);
+  if (!dtype_ok(q_dtype) || !(dtype_ok(cache_dtype) || cache_dtype == MLA_I8 || cache_dtype == MLA_I4) ||
+      !dtype_ok(part_dtype))
+    return fail(MLA_ERR_DTYPE, "mla_decode_splitkv: dtypes %d, %d, %d", q_dtype, cache_dtype, part_dtype);
   if (cache_dtype == MLA_F32 && q_dtype != MLA_F32)
     return fail(MLA_ERR_UNSUPPORTED, "mla_decode_splitkv: an fp32 cache needs an fp32 query");
+  if (cache_dtype == MLA_F32 && part_dtype != MLA_F32)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_decode_splitkv: an fp32 cache writes fp32 partials");
   if (n_segs <= 0 || n_segs > 64 || batch < 0 || s_q <= 0 || n_heads <= 0 || n_part <= 0 || n_wg < 0 || n_wg > 65536)
     return fail(MLA_ERR_SHAPE, "mla_decode_splitkv: n_segs=%d batch=%d s_q=%d n_heads=%d n_part=%d n_wg=%d",
                 n_segs, batch, s_q, n_heads, n_part, n_wg);
@@ -445,6 +451,7 @@ mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q
   mla::DecodeArgs a{};
   a.q_lat = q_lat;
   a.o_part = o_part;
+  a.part_bf16 = part_dtype == MLA_BF16;
   a.lse_part = lse_part;
   a.batch = batch;
   a.s_q = s_q;

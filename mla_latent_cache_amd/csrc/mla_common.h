@@ -28,6 +28,20 @@ __device__ __forceinline__ bf16 f2bf(float x) { return (bf16)x; }  // round to n
 template <typename T> __device__ __forceinline__ float load_f(const T* p);
 template <> __device__ __forceinline__ float load_f<float>(const float* p) { return *p; }
 template <> __device__ __forceinline__ float load_f<bf16>(const bf16* p) { return (float)*p; }
+// Four consecutive partial-output entries, fp32 or bf16 storage.
+__device__ __forceinline__ void store_part4(void* base, int64_t idx, f32x4 v, bool bf) {
+  if (bf)
+    *(bf16x4*)((bf16*)base + idx) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+  else
+    *(f32x4*)((float*)base + idx) = v;
+}
+template <typename T> __device__ __forceinline__ f32x4 load_part4(const T* p);
+template <> __device__ __forceinline__ f32x4 load_part4<float>(const float* p) { return *(const f32x4*)p; }
+template <> __device__ __forceinline__ f32x4 load_part4<bf16>(const bf16* p) {
+  const bf16x4 h = *(const bf16x4*)p;
+  return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+}
+
 template <typename T> __device__ __forceinline__ void store_f(T* p, float v);
 template <> __device__ __forceinline__ void store_f<float>(float* p, float v) { *p = v; }
 template <> __device__ __forceinline__ void store_f<bf16>(bf16* p, float v) { *p = (bf16)v; }

@@ -301,7 +301,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
   const int32_t* const seq_lens = a.seg.seq_lens;
   const void* const q_rot_p = a.seg.q_rot;
   const void* const q_lat_p = a.q_lat;
-  float* const o_part = a.o_part;
+  void* const o_part = a.o_part;
+  const bool part_bf = a.part_bf16;
   float* const lse_part = a.lse_part;
   const float* const row_fac = QKN ? a.seg.row_rinv : a.seg.row_scale;  // FAC: per stored row
   const int64_t max_rows = a.seg.max_rows;
@@ -1022,10 +1023,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a, 
               const int R = row0 + qr;
               const int tok = b * s_q + R / hc;
               const int h = head_begin + R % hc;
-              float* o = o_part + (((int64_t)tok * n_heads + h) * n_part + part_begin + slot) * kDc + 128 * pw +
-                         4 * lg;
+              const int64_t o = (((int64_t)tok * n_heads + h) * n_part + part_begin + slot) * kDc + 128 * pw +
+                                4 * lg;
 #pragma unroll
-              for (int db = 0; db < 8; ++db) *(f32x4*)(o + 16 * db) = acc_o[db][q] * inv;
+              for (int db = 0; db < 8; ++db) store_part4(o_part, o + 16 * db, acc_o[db][q] * inv, part_bf);
             }
           }
         }

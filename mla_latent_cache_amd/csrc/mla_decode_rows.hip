@@ -517,8 +517,10 @@ __device__ __forceinline__ T& pick(T& a, T& b) {
 }  // namespace
 
 // RB: 16-row blocks per wave (1: 64-row groups, 2: 128-row groups).  I4:
-// int4 rows (packed latent and rotary codes, two scales per row).
-template <int RB, bool I4>
+// int4 rows (packed latent and rotary codes, two scales per row).  PB: bf16
+// partial outputs (a compile-time choice: a branch in the epilogue changes
+// the register allocation of the tile loop).
+template <int RB, bool I4, bool PB>
 __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch L) {
   constexpr int MT = 16 * RB * kRowsWaves;  // query rows of a row group
   using SM = RowsSmem<I4>;
@@ -540,7 +542,8 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
   const float* const q_rot = (const float*)sg.q_rot;
   const float* const q_lat = (const float*)a.q_lat;
   const float* const row_scale = sg.row_scale;
-  float* const o_part = a.o_part;
+  void* const o_part = a.o_part;
+  constexpr bool part_bf = PB;
   float* const lse_part = a.lse_part;
   const int64_t max_rows = sg.max_rows;
   const int max_pages = sg.max_pages;
@@ -1001,9 +1004,9 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
           if (ri.valid && lg == 0)
             lse_part[lse_i] = lt[rb] > 0.f ? (m_used[rb] + __log2f(lt[rb]) + linv * cs[rb]) * kLn2 : -INFINITY;
           if (ri.valid && lt[rb] > 0.f) {
-            float* o = o_part + lse_i * kDc + 4 * lg;
+            const int64_t o = lse_i * kDc + 4 * lg;
 #pragma unroll
-            for (int db = 0; db < 32; ++db) *(f32x4*)(o + 16 * db) = acc[db][rb] * linv;
+            for (int db = 0; db < 32; ++db) store_part4(o_part, o + 16 * db, acc[db][rb] * linv, part_bf);
           }
         }
       }
@@ -1015,9 +1018,12 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
   }
 }
 
-template __global__ void decode_rows_kernel<1, false>(RowsLaunch);
-template __global__ void decode_rows_kernel<2, false>(RowsLaunch);
-template __global__ void decode_rows_kernel<1, true>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, false, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<2, false, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, true, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, false, true>(RowsLaunch);
+template __global__ void decode_rows_kernel<2, false, true>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, true, true>(RowsLaunch);
 
 int decode_rows_tile(int rows_total) { return rows_total <= 64 ? 64 : 128; }
 
@@ -1047,11 +1053,17 @@ SegCost seg_cost(const DecodeArgs& a, const SegArgs& s, int mt) {
   return c;
 }
 
-hipError_t launch_rows(const RowsLaunch& L, int mt, bool i4, int grid, hipStream_t stream) {
+template <bool PB>
+hipError_t launch_rows_pb(const RowsLaunch& L, int mt, bool i4, int grid, hipStream_t stream) {
   const dim3 block(kRowsThreads);
-  if (i4) return launch(decode_rows_kernel<1, true>, dim3(grid), block, stream, L);
-  if (mt == 64) return launch(decode_rows_kernel<1, false>, dim3(grid), block, stream, L);
-  return launch(decode_rows_kernel<2, false>, dim3(grid), block, stream, L);
+  if (i4) return launch(decode_rows_kernel<1, true, PB>, dim3(grid), block, stream, L);
+  if (mt == 64) return launch(decode_rows_kernel<1, false, PB>, dim3(grid), block, stream, L);
+  return launch(decode_rows_kernel<2, false, PB>, dim3(grid), block, stream, L);
+}
+
+hipError_t launch_rows(const RowsLaunch& L, int mt, bool i4, int grid, hipStream_t stream) {
+  if (L.a.part_bf16) return launch_rows_pb<true>(L, mt, i4, grid, stream);
+  return launch_rows_pb<false>(L, mt, i4, grid, stream);
 }
 
 }  // namespace

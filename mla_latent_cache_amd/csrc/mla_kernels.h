@@ -29,7 +29,8 @@ struct SegArgs {
 struct DecodeArgs {
   SegArgs seg;
   const void* q_lat;
-  float* o_part;
+  void* o_part;       // fp32, or bf16 when part_bf16
+  int part_bf16;
   float* lse_part;
   int batch;
   int s_q;
@@ -94,11 +95,11 @@ hipError_t launch_absorb_mfma(const void* q_nope, const void* w_uk, void* q_lat,
 bool out_uv_mfma_ok(const void* o_lat, const void* w_uv, int d_c, int d_v);
 hipError_t launch_out_uv_mfma(const void* o_lat, const void* w_uv, void* out, bool out_bf16, int n_tok,
                               int n_heads, hipStream_t stream);
-hipError_t launch_combine(const float* o_part, const float* lse_part, int n_rows, int n_part,
+hipError_t launch_combine(const void* o_part, bool part_bf16, const float* lse_part, int n_rows, int n_part,
                           int d_c, void* o_lat, bool out_bf16, float* lse, hipStream_t stream);
 // Merge and value expansion of (token, head) rows in one launch (d_c <= 512,
 // d_v <= 128); o_lat and lse may be null.
-hipError_t launch_combine_out_uv(const float* o_part, const float* lse_part, int n_tok, int n_heads, int n_part,
+hipError_t launch_combine_out_uv(const void* o_part, bool part_bf16, const float* lse_part, int n_tok, int n_heads, int n_part,
                                  int d_c, const void* w_uv, bool w_bf16, int d_v, void* o_lat, float* lse,
                                  void* out, bool out_bf16, hipStream_t stream);
 // int8 latent cache writer: bf16 rows [n][d_c + d_rope] -> packed rows [n][d_c + 2 d_rope] bytes + scales.

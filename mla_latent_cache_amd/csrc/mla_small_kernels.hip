@@ -186,8 +186,8 @@ hipError_t launch_out_uv(const void* o_lat, bool o_bf, const void* w_uv, bool w_
 // ---------------------------------------------------------------------------
 constexpr int kCombMaxPart = 1024;
 
-template <typename TO>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o_part,
+template <typename TO, typename TP>
+__global__ __launch_bounds__(256) void combine_kernel(const TP* __restrict__ o_part,
                                                       const float* __restrict__ lse_part, int n_rows,
                                                       int n_part, int d_c, int cols, TO* __restrict__ o_lat,
                                                       float* __restrict__ lse) {
@@ -235,18 +235,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int G = 256 / ct_n;        // slot groups
   const int g = tid / ct_n, ct = tid % ct_n;
   const int c = blockIdx.y * cols + 4 * ct;  // d_c is a multiple of 4: c < d_c means 4 whole columns
-  const float* op = o_part + (int64_t)row * n_part * d_c + c;
+  const TP* op = o_part + (int64_t)row * n_part * d_c + c;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   if (c < d_c) {
     int i = g;
     for (; i + 3 * G < n; i += 4 * G) {
       f32x4 v[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = *(const f32x4*)(op + (int64_t)live_idx[i + u * G] * d_c);
+      for (int u = 0; u < 4; ++u) v[u] = load_part4(op + (int64_t)live_idx[i + u * G] * d_c);
 #pragma unroll
       for (int u = 0; u < 4; ++u) acc += live_w[i + u * G] * v[u];
     }
-    for (; i < n; i += G) acc += live_w[i] * *(const f32x4*)(op + (int64_t)live_idx[i] * d_c);
+    for (; i < n; i += G) acc += live_w[i] * load_part4(op + (int64_t)live_idx[i] * d_c);
   }
   if (g > 0) red[(g - 1) * ct_n + ct] = acc;
   __syncthreads();
@@ -258,17 +258,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
-hipError_t launch_combine(const float* o_part, const float* lse_part, int n_rows, int n_part, int d_c,
-                          void* o_lat, bool out_bf16, float* lse, hipStream_t stream) {
+template <typename TP>
+static hipError_t combine_launch(const TP* o_part, const float* lse_part, int n_rows, int n_part, int d_c,
+                                 void* o_lat, bool out_bf16, float* lse, hipStream_t stream) {
   // chunk width: ~1024 blocks in flight for few rows, whole 512-column rows for many
   const int cols = n_rows >= 1024 ? 512 : n_rows >= 512 ? 256 : 128;
   const dim3 grid(n_rows, (d_c + cols - 1) / cols);
   if (out_bf16)
-    return launch(combine_kernel<bf16>, grid, dim3(256), stream, o_part, lse_part, n_rows, n_part, d_c, cols,
+    return launch(combine_kernel<bf16, TP>, grid, dim3(256), stream, o_part, lse_part, n_rows, n_part, d_c, cols,
                   (bf16*)o_lat, lse);
-  else
-    return launch(combine_kernel<float>, grid, dim3(256), stream, o_part, lse_part, n_rows, n_part, d_c, cols,
-                  (float*)o_lat, lse);
+  return launch(combine_kernel<float, TP>, grid, dim3(256), stream, o_part, lse_part, n_rows, n_part, d_c, cols,
+                (float*)o_lat, lse);
+}
+
+hipError_t launch_combine(const void* o_part, bool part_bf16, const float* lse_part, int n_rows, int n_part,
+                          int d_c, void* o_lat, bool out_bf16, float* lse, hipStream_t stream) {
+  if (part_bf16)
+    return combine_launch((const bf16*)o_part, lse_part, n_rows, n_part, d_c, o_lat, out_bf16, lse, stream);
+  return combine_launch((const float*)o_part, lse_part, n_rows, n_part, d_c, o_lat, out_bf16, lse, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -296,8 +303,8 @@ hipError_t launch_combine(const float* o_part, const float* lse_part, int n_rows
 // spreads few rows over more CUs (each block is bound by what one CU can
 // fetch).
 // ---------------------------------------------------------------------------
-template <typename TO, typename TW, bool VEC, int NQ>
-__global__ __launch_bounds__(1024) void combine_out_uv_kernel(const float* __restrict__ o_part,
+template <typename TO, typename TW, bool VEC, int NQ, typename TP>
+__global__ __launch_bounds__(1024) void combine_out_uv_kernel(const TP* __restrict__ o_part,
                                                               const float* __restrict__ lse_part, int n_tok,
                                                               int n_heads, int n_part, int d_c,
                                                               const TW* __restrict__ w_uv, int d_v,
@@ -375,18 +382,18 @@ __global__ __launch_bounds__(1024) void combine_out_uv_kernel(const float* __res
   if (lse && tid == 0 && q == 0) lse[row] = s_lse;
   const int g = tid >> 7, ct = tid & 127;  // 8 slot groups x 128 column threads
   const int c = 4 * ct;
-  const float* op = o_part + row * n_part * d_c + c;
+  const TP* op = o_part + row * n_part * d_c + c;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   if (c < d_c) {
     int i = g;
     for (; i + 7 * 8 < n; i += 8 * 8) {  // 8 loads in flight: 64 live slots in one round
       f32x4 x[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = *(const f32x4*)(op + (int64_t)live_idx[i + u * 8] * d_c);
+      for (int u = 0; u < 8; ++u) x[u] = load_part4(op + (int64_t)live_idx[i + u * 8] * d_c);
 #pragma unroll
       for (int u = 0; u < 8; ++u) acc += live_w[i + u * 8] * x[u];
     }
-    for (; i < n; i += 8) acc += live_w[i] * *(const f32x4*)(op + (int64_t)live_idx[i] * d_c);
+    for (; i < n; i += 8) acc += live_w[i] * load_part4(op + (int64_t)live_idx[i] * d_c);
   }
   if (g > 0) red[(g - 1) * 128 + ct] = acc;
   __syncthreads();
@@ -419,24 +426,24 @@ __global__ __launch_bounds__(1024) void combine_out_uv_kernel(const float* __res
   if (v_ok && part == 0) store_f(out + row * d_v + v, sum);
 }
 
-template <typename TO, typename TW, int NQ>
-static hipError_t cou_launch_nq(const float* o_part, const float* lse_part, int n_tok, int n_heads, int n_part,
+template <typename TO, typename TW, int NQ, typename TP>
+static hipError_t cou_launch_nq(const TP* o_part, const float* lse_part, int n_tok, int n_heads, int n_part,
                                 int d_c, const void* w_uv, int d_v, void* o_lat, float* lse, void* out,
                                 hipStream_t stream) {
   const int64_t n_items = (int64_t)n_heads * n_tok * NQ;
   const dim3 grid((unsigned)(8 * ((n_items + 7) / 8)));
   if constexpr (sizeof(TW) == 2) {
     if (d_c == 512 && (reinterpret_cast<uintptr_t>(w_uv) & 15u) == 0)
-      return launch(combine_out_uv_kernel<TO, TW, true, NQ>, grid, dim3(1024), stream, o_part, lse_part, n_tok,
+      return launch(combine_out_uv_kernel<TO, TW, true, NQ, TP>, grid, dim3(1024), stream, o_part, lse_part, n_tok,
                     n_heads, n_part, d_c, (const TW*)w_uv, d_v, (TO*)o_lat, lse, (TO*)out);
   }
-  return launch(combine_out_uv_kernel<TO, TW, false, NQ>, grid, dim3(1024), stream, o_part, lse_part, n_tok,
+  return launch(combine_out_uv_kernel<TO, TW, false, NQ, TP>, grid, dim3(1024), stream, o_part, lse_part, n_tok,
                 n_heads, n_part, d_c, (const TW*)w_uv, d_v, (TO*)o_lat, lse, (TO*)out);
 }
 
 // NQ: blocks per row, so that about 256 blocks (one per CU) run
-template <typename TO, typename TW>
-static hipError_t cou_launch(const float* o_part, const float* lse_part, int n_tok, int n_heads, int n_part,
+template <typename TO, typename TW, typename TP>
+static hipError_t cou_launch(const TP* o_part, const float* lse_part, int n_tok, int n_heads, int n_part,
                              int d_c, const void* w_uv, int d_v, void* o_lat, float* lse, void* out,
                              hipStream_t stream) {
   const int64_t rows = (int64_t)n_tok * n_heads;
@@ -450,9 +457,10 @@ static hipError_t cou_launch(const float* o_part, const float* lse_part, int n_t
                                   stream);
 }
 
-hipError_t launch_combine_out_uv(const float* o_part, const float* lse_part, int n_tok, int n_heads, int n_part,
-                                 int d_c, const void* w_uv, bool w_bf16, int d_v, void* o_lat, float* lse,
-                                 void* out, bool out_bf16, hipStream_t stream) {
+template <typename TP>
+static hipError_t cou_dispatch(const TP* o_part, const float* lse_part, int n_tok, int n_heads, int n_part, int d_c,
+                               const void* w_uv, bool w_bf16, int d_v, void* o_lat, float* lse, void* out,
+                               bool out_bf16, hipStream_t stream) {
   if (out_bf16 && w_bf16)
     return cou_launch<bf16, bf16>(o_part, lse_part, n_tok, n_heads, n_part, d_c, w_uv, d_v, o_lat, lse, out, stream);
   if (out_bf16)
@@ -460,6 +468,16 @@ hipError_t launch_combine_out_uv(const float* o_part, const float* lse_part, int
   if (w_bf16)
     return cou_launch<float, bf16>(o_part, lse_part, n_tok, n_heads, n_part, d_c, w_uv, d_v, o_lat, lse, out, stream);
   return cou_launch<float, float>(o_part, lse_part, n_tok, n_heads, n_part, d_c, w_uv, d_v, o_lat, lse, out, stream);
+}
+
+hipError_t launch_combine_out_uv(const void* o_part, bool part_bf16, const float* lse_part, int n_tok, int n_heads,
+                                 int n_part, int d_c, const void* w_uv, bool w_bf16, int d_v, void* o_lat,
+                                 float* lse, void* out, bool out_bf16, hipStream_t stream) {
+  if (part_bf16)
+    return cou_dispatch((const bf16*)o_part, lse_part, n_tok, n_heads, n_part, d_c, w_uv, w_bf16, d_v, o_lat, lse,
+                        out, out_bf16, stream);
+  return cou_dispatch((const float*)o_part, lse_part, n_tok, n_heads, n_part, d_c, w_uv, w_bf16, d_v, o_lat, lse,
+                      out, out_bf16, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -854,7 +872,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
   }
   if (l > 0.f) {
     const float inv = 1.f / l;
-    float* o = a.o_part + out_row * d_c;
+    float* o = (float*)a.o_part + out_row * d_c;  // fp32 partials only on this path
 #pragma unroll
     for (int k = 0; k < kF32MaxDc / 64; ++k) {
       const int d = lane + 64 * k;

@@ -155,7 +155,7 @@ def out_proj(x: torch.Tensor, w_o: torch.Tensor, out: Optional[torch.Tensor] = N
 
 def combine_lse(o_part: torch.Tensor, lse_part: torch.Tensor, out_dtype: torch.dtype,
                 o_lat: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
-    """o_part [..., n_part, d_c] fp32, lse_part [..., n_part] -> (o_lat [..., d_c], lse [...])."""
+    """o_part [..., n_part, d_c] fp32 or bf16, lse_part [..., n_part] -> (o_lat [..., d_c], lse [...])."""
     lead = o_part.shape[:-2]
     n_part, d_c = o_part.shape[-2:]
     n_rows = 1
@@ -165,7 +165,7 @@ def combine_lse(o_part: torch.Tensor, lse_part: torch.Tensor, out_dtype: torch.d
         o_lat = torch.empty(tuple(lead) + (d_c,), dtype=out_dtype, device=o_part.device)
     if lse is None:
         lse = torch.empty(tuple(lead), dtype=torch.float32, device=o_part.device)
-    _lib.call("mla_combine_lse", _ptr(o_part), _ptr(lse_part), n_rows, n_part, d_c, _ptr(o_lat),
+    _lib.call("mla_combine_lse", _ptr(o_part), _dt(o_part), _ptr(lse_part), n_rows, n_part, d_c, _ptr(o_lat),
               _DT[out_dtype], _ptr(lse), _stream())
     return o_lat, lse
 
@@ -173,7 +173,7 @@ def combine_lse(o_part: torch.Tensor, lse_part: torch.Tensor, out_dtype: torch.d
 def combine_out_uv(o_part: torch.Tensor, lse_part: torch.Tensor, w_uv: torch.Tensor, out_dtype: torch.dtype,
                    out: Optional[torch.Tensor] = None, o_lat: Optional[torch.Tensor] = None,
                    lse: Optional[torch.Tensor] = None, want_o_lat: bool = True, want_lse: bool = True):
-    """o_part [n_tok, H, n_part, d_c] fp32, lse_part [n_tok, H, n_part], w_uv [H, d_v, d_c]
+    """o_part [n_tok, H, n_part, d_c] fp32 or bf16, lse_part [n_tok, H, n_part], w_uv [H, d_v, d_c]
     -> (out [n_tok, H, d_v], o_lat [n_tok, H, d_c] or None, lse [n_tok, H] or None)."""
     n_tok, H, n_part, d_c = o_part.shape
     d_v = w_uv.shape[1]
@@ -184,7 +184,7 @@ def combine_out_uv(o_part: torch.Tensor, lse_part: torch.Tensor, w_uv: torch.Ten
         o_lat = torch.empty((n_tok, H, d_c), dtype=out_dtype, device=dev)
     if lse is None and want_lse:
         lse = torch.empty((n_tok, H), dtype=torch.float32, device=dev)
-    _lib.call("mla_combine_out_uv", _ptr(o_part), _ptr(lse_part), n_tok, H, n_part, d_c, _ptr(w_uv),
+    _lib.call("mla_combine_out_uv", _ptr(o_part), _dt(o_part), _ptr(lse_part), n_tok, H, n_part, d_c, _ptr(w_uv),
               _DT[w_uv.dtype], d_v, _ptr(o_lat), _ptr(lse), _ptr(out), _DT[out_dtype], _stream())
     return out, o_lat, lse
 
@@ -299,7 +299,7 @@ class Segment:
 
 def decode_splitkv(segments: Sequence[Segment], q_lat: torch.Tensor, batch: int, s_q: int, scale: float,
                    o_part: torch.Tensor, lse_part: torch.Tensor, n_wg: int = 0) -> None:
-    """o_part [n_tok, H, n_part, d_c] fp32 and lse_part [n_tok, H, n_part] are written."""
+    """o_part [n_tok, H, n_part, d_c] (fp32 or bf16) and lse_part [n_tok, H, n_part] are written."""
     n_tok, n_heads, d_c = q_lat.shape
     d_rope = segments[0].q_rot.shape[2]
     n_part = o_part.shape[2]
@@ -309,7 +309,7 @@ def decode_splitkv(segments: Sequence[Segment], q_lat: torch.Tensor, batch: int,
             raise ValueError("segments must share the cache dtype; q_rot must have q_lat's dtype")
     arr = (MlaSegment * len(segments))(*[s.to_c() for s in segments])
     _lib.call("mla_decode_splitkv", arr, len(segments), _ptr(q_lat), _dt(q_lat), cache_dt, batch, s_q, n_heads,
-              d_c, d_rope, float(scale), _ptr(o_part), _ptr(lse_part), n_part, n_wg, _stream())
+              d_c, d_rope, float(scale), _ptr(o_part), _dt(o_part), _ptr(lse_part), n_part, n_wg, _stream())
 
 
 def cu_count() -> int:

@@ -140,7 +140,10 @@ class DecodeStep:
             for i, s in enumerate(segments)
         ]
         self.q_lat = torch.empty((n_tok, H, d_c), dtype=q_dt, device=dev)
-        self.o_part = torch.empty((n_tok, H, self.n_part, d_c), dtype=torch.float32, device=dev)
+        # partial outputs in bf16 beside a bf16 cache (half the bytes written
+        # and merged), fp32 on the fp32 path
+        part_dt = torch.float32 if segments[0].cache.dtype == torch.float32 else torch.bfloat16
+        self.o_part = torch.empty((n_tok, H, self.n_part, d_c), dtype=part_dt, device=dev)
         self.lse_part = torch.empty((n_tok, H, self.n_part), dtype=torch.float32, device=dev)
         self.o_lat = torch.empty((n_tok, H, d_c), dtype=dt, device=dev)
         self.lse = torch.empty((n_tok, H), dtype=torch.float32, device=dev)
@@ -282,15 +285,18 @@ class DecodeStep:
         dec = [(lib.mla_decode_splitkv, (self._seg_arr, len(self.segments), self.q_lat.data_ptr(), dt(self.q_lat),
                                          ops._cache_dt(self.segments[0].cache, self.segments[0].row_scale),
                                          self.batch, self.s_q, H, d_c, d_r,
-                                         float(self.scale), self.o_part.data_ptr(), self.lse_part.data_ptr(),
+                                         float(self.scale), self.o_part.data_ptr(), dt(self.o_part),
+                                         self.lse_part.data_ptr(),
                                          self.n_part, self.n_wg, st))]
         if self.fuse_post:
-            post = [(lib.mla_combine_out_uv, (self.o_part.data_ptr(), self.lse_part.data_ptr(), n_tok, H, self.n_part,
+            post = [(lib.mla_combine_out_uv, (self.o_part.data_ptr(), dt(self.o_part), self.lse_part.data_ptr(), n_tok,
+                                              H, self.n_part,
                                               d_c, self.w_uv.data_ptr(), dt(self.w_uv), self.w_uv.shape[1],
                                               self.o_lat.data_ptr(), self.lse.data_ptr(), self.out.data_ptr(),
                                               dt(self.out), st))]
         else:
-            post = [(lib.mla_combine_lse, (self.o_part.data_ptr(), self.lse_part.data_ptr(), n_tok * H, self.n_part,
+            post = [(lib.mla_combine_lse, (self.o_part.data_ptr(), dt(self.o_part), self.lse_part.data_ptr(), n_tok * H,
+                                           self.n_part,
                                            d_c, self.o_lat.data_ptr(), dt(self.o_lat), self.lse.data_ptr(), st)),
                     (lib.mla_out_uv, (self.o_lat.data_ptr(), dt(self.o_lat), self.w_uv.data_ptr(), dt(self.w_uv),
                                       self.out.data_ptr(), dt(self.out), n_tok, H, d_c, self.w_uv.shape[1], st))]

@@ -84,7 +84,8 @@ def test_null_and_shape_errors_before_any_gpu_call(lib):
     assert _st(lib, "mla_absorb_q", P, P, 1, P, 9, 1, 1, 128, 512, None) == 3
     assert _st(lib, "mla_absorb_q", P, P, 1, P, 0, 1, 0, 128, 512, None) == 2
     assert _st(lib, "mla_out_uv", P, 1, P, 1, P, 1, -1, 1, 512, 128, None) == 2
-    assert _st(lib, "mla_combine_lse", P, P, 1, 0, 512, P, 1, None, None) == 2
+    assert _st(lib, "mla_combine_lse", P, 0, P, 1, 0, 512, P, 1, None, None) == 2
+    assert _st(lib, "mla_combine_lse", P, 7, P, 1, 4, 512, P, 1, None, None) == 3
     # mla_out_proj(x, x_dtype, w_o, w_dtype, out, out_dtype, n_tok, k_in, d_model)
     assert _st(lib, "mla_out_proj", None, 1, P, 1, P, 1, 1, 256, 64, None) == 1
     assert _st(lib, "mla_out_proj", P, 1, P, 7, P, 1, 1, 256, 64, None) == 3
@@ -94,18 +95,20 @@ def test_null_and_shape_errors_before_any_gpu_call(lib):
     assert _st(lib, "mla_out_proj", P, 1, P, 1, P, 1, 1, (1 << 20) + 1, 64, None) == 2
     assert _st(lib, "mla_out_proj", P, 1, P, 1, P, 1, 1, 256, (1 << 20) + 1, None) == 2
     assert _st(lib, "mla_out_proj", P, 1, P, 1, P, 1, 0, 256, 64, None) == 0  # nothing to do: no launch
-    assert _st(lib, "mla_combine_lse", P, None, 1, 1, 512, P, 1, None, None) == 1
-    # mla_combine_out_uv(o_part, lse_part, n_tok, n_heads, n_part, d_c, w_uv, w_dtype, d_v, o_lat, lse, out, dt)
-    assert _st(lib, "mla_combine_out_uv", P, P, 1, 1, 4, 512, None, 1, 128, None, None, P, 1, None) == 1
-    assert _st(lib, "mla_combine_out_uv", P, P, 1, 1, 4, 512, P, 4, 128, None, None, P, 1, None) == 3
-    assert _st(lib, "mla_combine_out_uv", P, P, 1, 1, 4, 1024, P, 1, 128, None, None, P, 1, None) == 2
-    assert _st(lib, "mla_combine_out_uv", P, P, 1, 1, 4, 512, P, 1, 129, None, None, P, 1, None) == 2
-    assert _st(lib, "mla_combine_out_uv", P, P, 1, 1, 4, 510, P, 1, 128, None, None, P, 1, None) == 2
-    assert _st(lib, "mla_combine_out_uv", P + 4, P, 1, 1, 4, 512, P, 1, 128, None, None, P, 1, None) == 2
-    assert _st(lib, "mla_combine_out_uv", P, P, 0, 1, 4, 512, P, 1, 128, None, None, P, 1, None) == 0
-    assert _st(lib, "mla_combine_out_uv", P, P, 65535, 65535, 4, 512, P, 1, 128, None, None, P, 1, None) == 2
-    assert _st(lib, "mla_combine_out_uv", P, P, 2048, 1025, 4, 512, P, 1, 128, None, None, P, 1, None) == 2
-    assert _st(lib, "mla_combine_lse", P, P, 1 << 24, 4, 512, P, 1, None, None) == 2
+    assert _st(lib, "mla_combine_lse", P, 1, None, 1, 1, 512, P, 1, None, None) == 1
+    # mla_combine_out_uv(o_part, part_dtype, lse_part, n_tok, n_heads, n_part, d_c, w_uv, w_dtype, d_v, o_lat,
+    #                    lse, out, dt)
+    assert _st(lib, "mla_combine_out_uv", P, 5, P, 1, 1, 4, 512, P, 1, 128, None, None, P, 1, None) == 3
+    assert _st(lib, "mla_combine_out_uv", P, 1, P, 1, 1, 4, 512, None, 1, 128, None, None, P, 1, None) == 1
+    assert _st(lib, "mla_combine_out_uv", P, 1, P, 1, 1, 4, 512, P, 4, 128, None, None, P, 1, None) == 3
+    assert _st(lib, "mla_combine_out_uv", P, 1, P, 1, 1, 4, 1024, P, 1, 128, None, None, P, 1, None) == 2
+    assert _st(lib, "mla_combine_out_uv", P, 1, P, 1, 1, 4, 512, P, 1, 129, None, None, P, 1, None) == 2
+    assert _st(lib, "mla_combine_out_uv", P, 1, P, 1, 1, 4, 510, P, 1, 128, None, None, P, 1, None) == 2
+    assert _st(lib, "mla_combine_out_uv", P + 4, 1, P, 1, 1, 4, 512, P, 1, 128, None, None, P, 1, None) == 2
+    assert _st(lib, "mla_combine_out_uv", P, 1, P, 0, 1, 4, 512, P, 1, 128, None, None, P, 1, None) == 0
+    assert _st(lib, "mla_combine_out_uv", P, 1, P, 65535, 65535, 4, 512, P, 1, 128, None, None, P, 1, None) == 2
+    assert _st(lib, "mla_combine_out_uv", P, 1, P, 2048, 1025, 4, 512, P, 1, 128, None, None, P, 1, None) == 2
+    assert _st(lib, "mla_combine_lse", P, 1, P, 1 << 24, 4, 512, P, 1, None, None) == 2
     # mla_qknorm_query(q_nope, in_dtype, g_q, g_k, n_tok, n_heads, d_nope, eps, q_out, stream)
     assert _st(lib, "mla_qknorm_query", P, 1, P, None, 1, 16, 128, 1e-6, P, None) == 1
     assert _st(lib, "mla_qknorm_query", P, 3, P, P, 1, 16, 128, 1e-6, P, None) == 3
@@ -174,10 +177,10 @@ def test_null_and_shape_errors_before_any_gpu_call(lib):
             setattr(s, k, v)
         return s
 
-    def dec(segs, n_heads=4, n_part=2, dtype=1, d_c=512, d_r=64, q=P, o=P, q_dtype=0):
+    def dec(segs, n_heads=4, n_part=2, dtype=1, d_c=512, d_r=64, q=P, o=P, q_dtype=0, part_dtype=0):
         arr = (MlaSegment * len(segs))(*segs)
         return _st(lib, "mla_decode_splitkv", arr, len(segs), q, q_dtype, dtype, 2, 1, n_heads, d_c, d_r, 0.1,
-                   o, P, n_part, 0, None)
+                   o, part_dtype, P, n_part, 0, None)
 
     assert dec([seg()], q=None) == 1
     assert dec([seg(cache=None)]) == 1
@@ -192,6 +195,8 @@ def test_null_and_shape_errors_before_any_gpu_call(lib):
     assert dec([seg(causal=2)]) == 2
     assert dec([seg(head_count=4)], n_heads=4, dtype=7) == 3
     assert dec([seg()], dtype=0, q_dtype=1) == 5          # fp32 cache needs an fp32 query
+    assert dec([seg()], dtype=0, part_dtype=1) == 5       # and writes fp32 partials
+    assert dec([seg()], part_dtype=3) == 3                # partials are fp32 or bf16
     assert dec([seg(row_rinv=P)], q_dtype=1) == 5         # QK-Norm factors need an fp32 query
     # int8 cache (cache_dtype 2): fp32 query, row_scale on every segment, no QK-Norm
     assert dec([seg()], dtype=2) == 1                     # row_scale missing
@@ -222,7 +227,7 @@ def test_size_limits_refused(lib):
 
     def dec(segs, n_part, batch=2):
         arr = (MlaSegment * len(segs))(*segs)
-        return lib.mla_decode_splitkv(arr, len(segs), P, 0, 1, batch, 1, 4, 512, 64, 0.1, P, P, n_part, 0, None)
+        return lib.mla_decode_splitkv(arr, len(segs), P, 0, 1, batch, 1, 4, 512, 64, 0.1, P, 0, P, n_part, 0, None)
 
     assert dec([seg(n_split=32768)], 32768) == 5
     assert b"n_split" in lib.mla_last_error()

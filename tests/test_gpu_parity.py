@@ -392,11 +392,13 @@ def test_prepare_qknorm_call(q_dtype, n_tok, H):
                                                      (torch.float32, 600, 5), (torch.float32, 1100, 5),
                                                      (torch.bfloat16, 9, 300),      # slots beyond 128
                                                      (torch.float32, 7, 1024)])     # the largest slot count
-def test_combine_call(out_dtype, n_rows, n_part):
+@pytest.mark.parametrize("part_dtype", [torch.float32, torch.bfloat16])
+def test_combine_call(out_dtype, n_rows, n_part, part_dtype):
+    """Partials stored fp32 or bf16 (the oracle merges the same stored values)."""
     from mla_latent_cache_amd import ops
     d_c = 512
     g = torch.Generator().manual_seed(12)
-    o_part = torch.randn((n_rows, n_part, d_c), generator=g)
+    o_part = torch.randn((n_rows, n_part, d_c), generator=g).to(part_dtype)
     lse_part = torch.randn((n_rows, n_part), generator=g) * 4
     lse_part[3, :] = -math.inf                # empty row
     lse_part[4, 1:] = -math.inf               # one live slot
@@ -518,11 +520,13 @@ def test_quantize_i4_call():
     (torch.float32, torch.bfloat16, (1, 4, 200, 512, 128)),
     (torch.bfloat16, torch.bfloat16, (5, 20, 70, 512, 128)),   # 100 rows: two blocks per row, 70 > 64
 ])
-def test_combine_out_uv_call(out_dtype, w_dtype, dims):
+@pytest.mark.parametrize("part_dtype", [torch.float32, torch.bfloat16])
+def test_combine_out_uv_call(out_dtype, w_dtype, dims, part_dtype):
+    """Partials stored fp32 or bf16 (the oracle merges the same stored values)."""
     from mla_latent_cache_amd import ops
     n_tok, H, n_part, d_c, d_v = dims
     g = torch.Generator().manual_seed(13)
-    o_part = torch.randn((n_tok, H, n_part, d_c), generator=g)
+    o_part = torch.randn((n_tok, H, n_part, d_c), generator=g).to(part_dtype)
     lse_part = torch.randn((n_tok, H, n_part), generator=g) * 4
     lse_part[0, 0, :] = -math.inf              # empty row
     lse_part[0, 1 % H, 1:] = -math.inf         # one live slot
