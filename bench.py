@@ -32,7 +32,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 MALL_BYTES = 256 << 20          # Infinity Cache: rotate caches so every step reads HBM
 DECODE_SRCS = [os.path.join(ROOT, "mla_latent_cache_amd", "csrc", f)
-               for f in ("mla_decode_bf16.hip", "mla_decode_rows.hip", "mla_decode_tile.h")]
+               for f in ("mla_decode_bf16.hip", "mla_decode_rows.hip", "mla_decode_tile.h", "mla_common.h",
+                         "mla_kernels.h")]
 SEEDS = {"toy": 0, "small": 1, "dsv3": 2, "long": 3, "merge": 4, "prefill": 5, "qknorm": 6, "int8": 7, "int4": 8}
 
 
@@ -73,21 +74,22 @@ def ops_cache_dt(step) -> int:
 
 def decode_kernel_name(x) -> str:
     """The decode kernel a workload's launches run (the routing of
-    mla_decode_splitkv)."""
+    mla_decode_splitkv; 16-bit and low-bit caches write bf16 partials)."""
     sp = x.spec
     rows = [sp.s_q * (s.head_count or sp.heads) for s in x.segments]
     if sp.dtype != "bf16":
         return "decode_f32_kernel"
     if sp.quant == "int4":
-        return "decode_rows_kernel<1, true> (int4 rows, 64-row groups)"
+        return "decode_rows_kernel<1, true, true> (int4 rows, 64-row groups)"
     if sp.quant == "int8" or sp.qk_norm or (len(rows) == 1 and rows[0] <= 32):
         return "decode_bf16_kernel"
     rb = 1 if max(rows) <= 64 else 2
-    return f"decode_rows_kernel<{rb}, false> ({64 * rb}-row groups)"
+    return f"decode_rows_kernel<{rb}, false, true> ({64 * rb}-row groups)"
 
 
 def kernel_hash() -> str:
-    """Hash of the decode kernels' sources (the files that exist)."""
+    """Hash of the decode kernels' sources and the headers they include (the
+    files that exist)."""
     h = hashlib.sha256()
     for p in DECODE_SRCS:
         if os.path.exists(p):
