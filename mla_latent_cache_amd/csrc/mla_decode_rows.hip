@@ -270,6 +270,30 @@ __device__ __forceinline__ void unpack_tile_i4(const char* __restrict__ land, ch
   scl[lane] = sv;
 }
 
+// Score MFMAs with their accumulators in VGPRs.  Once any MFMA of a kernel
+// keeps its accumulator in AGPRs (O does, all 256 of them at 32 rows per
+// wave), the compiler selects the AGPR form for every MFMA, so the scores
+// too would take AGPRs, and part of O would move to VGPRs and back on every
+// tile.  Written as asm, the compiler sees no MFMA here and cannot insert
+// the wait states that an MFMA result needs before a vector-ALU read;
+// scores_ready() provides them (8, as the compiler gives this 16x16x32
+// form) and orders every later read of the scores after them.  A chain of
+// MFMAs into one accumulator needs none.
+__device__ __forceinline__ void mfma_v(f32x4& c, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v0(f32x4& c, const bf16x8& a, const bf16x8& b) {  // c = a . b
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=v"(c) : "v"(a), "v"(b));
+}
+template <int RB>
+__device__ __forceinline__ void scores_ready(f32x4 (&s)[2][RB], f32x4 (&sr)[2][RB]) {
+  asm volatile("s_nop 7" ::: "memory");
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) asm volatile("" : "+v"(s[tb][rb]), "+v"(sr[tb][rb]));
+}
+
 // Scores of one tile for the wave's RB row blocks: S^T[32 tokens x 16 rows]
 // per block as two 16-token halves.  ls / rs: the tile's latent and rotary
 // stages (restrict: the compiler may then order these reads freely against
@@ -292,10 +316,18 @@ __device__ __forceinline__ void qk_tile(const char* __restrict__ ls, const char*
   for (int n = 0; n < 4; ++n) kb[n] = ls + xl * kCBytes + ((n ^ (xl >> 2)) << 6) + ((xg ^ (xl & 3)) << 4);
   const char* rb0 = rs + xl * kRBytes;
   const int xr = (xl >> 1) & 7;
+  const bool split_rot = &sr[0][0] != &s[0][0];  // int4 rows: the rotary part apart
+  // the rotary query's hi parts from LDS (row 16 rb + l16 of the wave's rows,
+  // chunk 4 jr + lg, placed like the rotary ring), read first so that their
+  // latency hides behind the latent k-steps
+  bf16x8 qrh[RB][2];
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) s[tb][rb] = sr[tb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int jr = 0; jr < 2; ++jr) {
+      const int qr = 16 * rb + xl;
+      qrh[rb][jr] = *(const bf16x8*)(qs + qr * kRBytes + (rpos(qr, 4 * jr + xg) << 4));
+    }
   // K operands of k-step ks (ks < 16 latent, then 2 rotary), read kPre
   // k-steps ahead of their MFMAs
   auto kop = [&](int ks, int tb) -> bf16x8 {
@@ -319,21 +351,28 @@ __device__ __forceinline__ void qk_tile(const char* __restrict__ ls, const char*
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       if (ks < kDc / 32) {
-        s[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qh[rb][ks], s[0][rb], 0, 0, 0);
-        s[1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qh[rb][ks], s[1][rb], 0, 0, 0);
+        if (ks == 0) {
+          mfma_v0(s[0][rb], k0, qh[rb][ks]);
+          mfma_v0(s[1][rb], k1, qh[rb][ks]);
+        } else {
+          mfma_v(s[0][rb], k0, qh[rb][ks]);
+          mfma_v(s[1][rb], k1, qh[rb][ks]);
+        }
       } else {
         const int jr = ks - kDc / 32;
-        // the rotary query's hi part from LDS: row 16 rb + l16 of the wave's
-        // rows, chunk 4 jr + lg (placed like the rotary ring)
-        const int qr = 16 * rb + xl;
-        const bf16x8 qrh = *(const bf16x8*)(qs + qr * kRBytes + (rpos(qr, 4 * jr + xg) << 4));
-        sr[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qrh, sr[0][rb], 0, 0, 0);
-        sr[1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qrh, sr[1][rb], 0, 0, 0);
-        sr[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qrl[rb][jr], sr[0][rb], 0, 0, 0);
-        sr[1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qrl[rb][jr], sr[1][rb], 0, 0, 0);
+        if (jr == 0 && split_rot) {
+          mfma_v0(sr[0][rb], k0, qrh[rb][jr]);
+          mfma_v0(sr[1][rb], k1, qrh[rb][jr]);
+        } else {
+          mfma_v(sr[0][rb], k0, qrh[rb][jr]);
+          mfma_v(sr[1][rb], k1, qrh[rb][jr]);
+        }
+        mfma_v(sr[0][rb], k0, qrl[rb][jr]);
+        mfma_v(sr[1][rb], k1, qrl[rb][jr]);
       }
     }
   }
+  scores_ready<RB>(s, sr);
 }
 
 // O^T[512 columns x 16 rows] += C^T . P^T for the wave's RB row blocks.  The
