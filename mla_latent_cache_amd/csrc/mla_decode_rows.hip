@@ -100,6 +100,17 @@ constexpr int kTileDma = kTile + kRStage / 1024;       // 36 wave-instructions p
 constexpr int kDmaPerWave = kTileDma / kRowsWaves;     // 9
 static_assert(kTileDma % kRowsWaves == 0, "every wave issues the same share of a tile's loads");
 constexpr int kRowsMaxPieces = 64;
+// Cost of a piece beyond its tiles, in tiles: its prologue reads the query
+// of the group's rows (fp32 latent and rotary parts), its epilogue reads the
+// latent part again and writes the partial output, all at the CU's share of
+// HBM bandwidth like the cache tiles (measured: about 19 tiles at 128-row
+// groups, as the bytes predict).  The work split counts this many extra
+// tiles at the start of every request, so a workgroup whose range crosses a
+// request boundary (two pieces) takes correspondingly fewer rows.
+__host__ __device__ constexpr int piece_tiles(int mt, bool part_bf16) {
+  return (mt * ((kDc + kDr) * 4 + kDc * 4 + kDc * (part_bf16 ? 2 : 4)) + kTile * kRowBytes / 2) /
+         (kTile * kRowBytes);
+}
 // Operand reads in flight ahead of their MFMAs (deeper with 16 rows per wave,
 // which has registers to spare and fewer MFMAs per read to cover latency)
 template <int RB> constexpr int kPvPre = RB == 1 ? 8 : 4;   // PV: column blocks of transposed reads
@@ -562,6 +573,7 @@ __device__ __forceinline__ T& pick(T& a, T& b) {
 template <int RB, bool I4, bool PB>
 __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch L) {
   constexpr int MT = 16 * RB * kRowsWaves;  // query rows of a row group
+  constexpr int kOv = piece_tiles(MT, PB) * kTile;  // a request's start, in rows of the work split
   using SM = RowsSmem<I4>;
   constexpr int NLAT = SM::NLAT;
   constexpr int RBYTES = I4 ? kI4Row : kRowBytes;  // bytes per stored row
@@ -626,14 +638,16 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
   const int64_t cap = block_table ? (int64_t)max_pages * kPageSize : max_rows;
   auto clampT = [cap](int t) -> int { return (int)max((int64_t)0, min((int64_t)t, cap)); };
   auto padT = [](int t) -> int { return (t + kTile - 1) / kTile * kTile; };
+  // a request's length in the work split: whole tiles plus the piece cost
+  auto splitT = [padT](int t) -> int { return t > 0 ? padT(t) + kOv : 0; };
 
-  // ---- plan pass 1: total and longest request, each padded to whole tiles ----
+  // ---- plan pass 1: total and longest request in the split's units ----
   int tsum = 0, tmax = 0;
   int Tr_lane = 0;
   if (B <= 64) {
     if (wave == 0) {
       Tr_lane = lane < B ? clampT(seq_lens[lane]) : 0;
-      tsum = padT(Tr_lane);
+      tsum = splitT(Tr_lane);
       tmax = tsum;
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) {
@@ -643,7 +657,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
     }
   } else {
     for (int b = tid; b < B; b += kRowsThreads) {
-      const int T = padT(clampT(seq_lens[b]));
+      const int T = splitT(clampT(seq_lens[b]));
       tsum += T;
       tmax = max(tmax, T);
     }
@@ -669,7 +683,9 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
   int share = 0;
   if (!req_mode) {
     share = (tsum + n_share - 1) / n_share;
-    share = max(share, (tmax + n_split - 2) / (n_split - 1));
+    // the longest request's rows (without its piece cost) span at most n_split shares
+    const int tmax_rows = max(0, tmax - kOv);
+    share = max(share, (tmax_rows + n_split - 2) / (n_split - 1));
     share = max(kTile, (share + kTile - 1) / kTile * kTile);
   }
   const int lo = j * share, hi = lo + share;
@@ -692,20 +708,22 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
     return RowInfo{valid, tok, (int64_t)tok * n_heads + head_begin + Rr % hc};
   };
 
-  int base = 0;  // prefix of padded T over the requests scanned so far (wave 0)
+  int base = 0;  // prefix of the split lengths over the requests scanned so far (wave 0)
   for (int chunk = 0;; ++chunk) {
     // ---- plan pass 2: wave 0 scans 64 requests, lists pieces, writes -inf tails ----
     if (wave == 0) {
       const int b = chunk * 64 + lane;
       const int Tr = B <= 64 ? Tr_lane : b < B ? clampT(seq_lens[b]) : 0;
       const int T = padT(Tr);
-      int incl = T;
+      const int V = splitT(Tr);
+      int incl = V;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const int v = __shfl_up(incl, o);
         if (lane >= o) incl += v;
       }
-      const int S = base + incl - T;
+      // the request's rows start at S in the split's units (after its piece cost)
+      const int S = base + incl - V + (V > 0 ? kOv : 0);
       bool is_piece, tail;
       int r0 = 0, r1 = 0, slot = 0, cnt = 0;
       if (req_mode) {
@@ -1077,6 +1095,8 @@ namespace {
 struct SegCost {
   double tiles;
   double t_tile;
+  double piece;  // a piece's cost beyond its tiles, in tiles
+  int batch;
   int n_rg;
 };
 
@@ -1089,6 +1109,8 @@ SegCost seg_cost(const DecodeArgs& a, const SegArgs& s, int mt) {
   const int busy = (std::min(rows, mt) + rpw - 1) / rpw;  // waves with rows in the fullest group
   c.t_tile = (mt == 64 ? 3400.0 + 125.0 * busy : 4000.0 + 250.0 * busy);
   c.tiles = std::max(1.0, (double)a.batch * (double)std::max<int64_t>(cap, 1) / kTile);
+  c.piece = piece_tiles(mt, a.part_bf16 != 0);
+  c.batch = a.batch;
   return c;
 }
 
@@ -1129,15 +1151,19 @@ hipError_t launch_decode_rows_multi(const DecodeArgs& a, const SegArgs* segs, in
       decode_bf16_grid(L.rows_total[0], mt, n_wg, &L.n_share[0], &L.n_rg[0]);
     } else {
       // shares per segment for equal finish times: the smallest time T at
-      // which ceil(tiles x t_tile / T) shares per segment fit in n_wg
+      // which the shares every segment needs fit in n_wg.  A share of n
+      // takes (tiles + batch x piece) / n + piece tiles (its requests' piece
+      // costs spread over the shares, and its own first piece).
       SegCost c[kRowsMaxSegs];
       double hi = 1.0;
       for (int g = 0; g < n; ++g) {
         c[g] = seg_cost(a, L.segs[g], mt);
-        hi = std::max(hi, c[g].tiles * c[g].t_tile);
+        hi = std::max(hi, (c[g].tiles + (c[g].batch + 1) * c[g].piece) * c[g].t_tile);
       }
       auto shares = [&](double T, int g) {
-        return (int)std::min<double>(c[g].tiles, std::max(1.0, std::ceil(c[g].tiles * c[g].t_tile / T)));
+        const double avail = std::max(T / c[g].t_tile - c[g].piece, 1e-9);
+        return (int)std::min<double>(c[g].tiles,
+                                     std::max(1.0, std::ceil((c[g].tiles + c[g].batch * c[g].piece) / avail)));
       };
       auto used = [&](double T) {
         int64_t w = 0;
