@@ -78,6 +78,7 @@
 #include "mla_kernels.h"
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 
 namespace mla {
@@ -126,7 +127,7 @@ constexpr float kRowsTau = 32.f;
 // Instruction order of the scheduling regions of a tile step, for the
 // compiler's scheduler (which otherwise issues each LDS read just before its
 // MFMA and waits for it).  Groups of instruction kinds are filled in order:
-constexpr int kSchedDs = 0x080, kSchedMfma = 0x008, kSchedValu = 0x002;
+constexpr int kSchedDs = 0x080, kSchedMfma = 0x008;
 
 // int4 rows (the QuantMLA abstract's joint INT4 content and rotary caches):
 // 256 bytes of latent codes and 32 of rotary codes per stored row, two fp32
@@ -154,7 +155,7 @@ struct RowsSmem {
   Piece pieces[kRowsMaxPieces];
   int n_pieces;
   int done;
-  int red[2 * kRowsWaves];
+  int red[4 * kRowsWaves];
 };
 
 // Direct-to-LDS buffer load of 16 bytes per lane: LDS address = lds + 16 *
@@ -395,11 +396,14 @@ __device__ __forceinline__ void qk_tile(const char* __restrict__ ls, const char*
 // chunk 2 db + (qq >> 1) at position 2 (db ^ (x >> 1)) + ((qq >> 1) ^ (x & 1)),
 // byte 8 (qq & 1) within it; each 16-lane group then holds C[rows][16 db + l16].
 // `load(i)` issues load i of the next tile's share after the MFMAs of column
-// block kPvLoadAt[i].
+// block kPvLoadAt[i]; `mid(db)` runs after those of block db (the next tile's
+// softmax, in stages).  Each block's instructions stay in program order (a
+// wave issues in order: vector-ALU work placed right after an MFMA issues
+// while the MFMA runs).
 constexpr int kPvLoadAt[9] = {1, 4, 8, 11, 15, 18, 22, 25, 29};
-template <int RB, class Load>
+template <int RB, class Load, class Mid>
 __device__ __forceinline__ void pv_tile(const char* __restrict__ ls, int lane, const bf16x8 (&p)[RB],
-                                        f32x4 (&acc)[32][RB], const Load& load) {
+                                        f32x4 (&acc)[32][RB], const Load& load, const Mid& mid) {
   asm volatile("" : "+v"(lane));
   const int qq = lane & 3, rq = (lane >> 2) & 3, xg = lane >> 4;
   const int xr = 4 * xg + rq;
@@ -424,82 +428,118 @@ __device__ __forceinline__ void pv_tile(const char* __restrict__ ls, int lane, c
       acc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[db % (kPre + 1)], p[rb], acc[db][rb], 0, 0, 0);
       asm("" : "+a"(acc[db][rb]));  // the accumulators live in AGPRs throughout
     }
+    mid(db);
 #pragma unroll
     for (int i = 0; i < 9; ++i)
       if (kPvLoadAt[i] == db) load(i);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Online softmax of one tile's scores, already in log2 units (the query
-// carries scale * log2 e) with lazy rescaling: the P^T operands (bf16), the
-// factor each row's O must take and whether any row of the wave moved its
-// max.  Unless the whole tile is visible to every row of the wave (`full`),
-// tokens past the piece or the row's causal limit (relative index `lim` per
-// lane: token 4 lg + e of the first half is visible when e <= lim) get
-// weight 0.
-// int4 rows (I4): the score is s_c (latent part) + s_r (rotary part) with
-// the row's two scales, read from the wave's scale slot `tsc` of the tile
-// (pairs (s_c, s_r) per row), and each weight enters the PV product times its
-// row's latent scale (the PV multiplies the codes).
-template <int RB, bool I4 = false>
-__device__ __forceinline__ bool softmax_tile(const f32x4 (&s)[2][RB], const f32x4 (&sr)[2][RB], bool full,
-                                             const int (&lim)[RB], float (&m_used)[RB], float (&l_part)[RB],
-                                             bf16x8 (&p)[RB], float (&alpha)[RB], const float* tsc = nullptr) {
-  bool need_any = false;
-  f32x4 sc[2][2];  // (tokens 4 lg .. 4 lg + 3 of each half) x (s_c, s_r) pairs
+// A tile's scores made ready for the softmax, in place.  int4 rows (I4):
+// the score is s_c (latent part) + s_r (rotary part) with the row's two
+// scales, read from the wave's scale slot `tsc` of the tile (pairs (s_c,
+// s_r) per row); the latent scales (times the factor the unpacked codes
+// lack) stay in `wsc` for the weights, which enter the PV product times them
+// (the PV multiplies the codes).  Unless the whole tile is visible to every
+// row of the wave (`full`), tokens past the piece or the row's causal limit
+// (relative index `lim` per lane: token 4 lg + e of the first half is
+// visible when e <= lim) get -inf, i.e. weight 0.  A branch on `full` is
+// fine here: the softmax proper, which runs between the PV MFMAs, has none.
+template <int RB, bool I4>
+__device__ __forceinline__ void prep_scores(f32x4 (&s)[2][RB], const f32x4 (&sr)[2][RB], bool full,
+                                            const int (&lim)[RB], const float* tsc, f32x4 (&wsc)[2]) {
   if constexpr (I4) {
     int ln = __lane_id();
     asm volatile("" : "+v"(ln));
     const int lg4 = 4 * (ln >> 4);
+    f32x4 sc[2][2];  // (tokens 4 lg .. 4 lg + 3 of each half) x (s_c, s_r) pairs
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       sc[tb][0] = *(const f32x4*)(tsc + 2 * (16 * tb + lg4));
       sc[tb][1] = *(const f32x4*)(tsc + 2 * (16 * tb + lg4) + 4);
     }
-  }
-  // scale pair of token 4 lg + e of half tb: (s_c, s_r), times the factor
-  // the unpacked codes lack
-  auto tok_sc = [&](int tb, int e) -> float { return kI4Unit * sc[tb][e >> 1][2 * (e & 1)]; };
-  auto tok_sr = [&](int tb, int e) -> float { return kI4Unit * sc[tb][e >> 1][2 * (e & 1) + 1]; };
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    f32x4 sa = s[0][rb], sb = s[1][rb];
-    if constexpr (I4) {
+    for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        sa[e] = tok_sc(0, e) * sa[e] + tok_sr(0, e) * sr[0][rb][e];
-        sb[e] = tok_sc(1, e) * sb[e] + tok_sr(1, e) * sr[1][rb][e];
+        const float c = kI4Unit * sc[tb][e >> 1][2 * (e & 1)], r = kI4Unit * sc[tb][e >> 1][2 * (e & 1) + 1];
+        wsc[tb][e] = c;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) s[tb][rb][e] = c * s[tb][rb][e] + r * sr[tb][rb][e];
       }
-    }
-    if (!full) {
+  }
+  if (!full) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        sa[e] = e <= lim[rb] ? sa[e] : -INFINITY;
-        sb[e] = 16 + e <= lim[rb] ? sb[e] : -INFINITY;
+        s[0][rb][e] = e <= lim[rb] ? s[0][rb][e] : -INFINITY;
+        s[1][rb][e] = 16 + e <= lim[rb] ? s[1][rb][e] : -INFINITY;
       }
-    }
-    float mt = fmaxf(fmaxf(fmaxf(sa[0], sa[1]), fmaxf(sa[2], sa[3])), fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3])));
-    mt = rows_max(mt);
-    const bool need = mt > m_used[rb] + kRowsTau;
-    const float al = need ? __builtin_amdgcn_exp2f(m_used[rb] - mt) : 1.f;  // 0 when m_used was -inf
-    m_used[rb] = need ? mt : m_used[rb];
-    alpha[rb] = al;
-    need_any |= need;
-    const float msub = m_used[rb] == -INFINITY ? 0.f : m_used[rb];
-    float lsum = 0.f;
-    bf16x8 pv;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float p0 = __builtin_amdgcn_exp2f(sa[e] - msub);  // exp2(-inf) = 0
-      const float p1 = __builtin_amdgcn_exp2f(sb[e] - msub);
-      lsum += p0 + p1;
-      pv[e] = (bf16)(I4 ? p0 * tok_sc(0, e) : p0);
-      pv[4 + e] = (bf16)(I4 ? p1 * tok_sc(1, e) : p1);
-    }
-    l_part[rb] = l_part[rb] * al + lsum;
-    p[rb] = pv;
   }
-  return __ballot(need_any) != 0;
+}
+
+// Online softmax of one tile's prepared scores, already in log2 units (the
+// query carries scale * log2 e), with lazy rescaling: the P^T operands
+// (bf16), the factor each row's O must take and whether any row of the wave
+// moved its max.  Cut into kStages short stages (per row block: the tile
+// max, its reduction over the lane groups, the max update, four pairs of
+// weights, the packing) that run one per PV column block, between the MFMAs
+// of the previous tile's PV.
+template <int RB, bool I4>
+struct SoftmaxStages {
+  static constexpr int kPerRb = 8;
+  static constexpr int kStages = kPerRb * RB;
+  const f32x4 (&s)[2][RB];
+  float (&m_used)[RB];
+  float (&l_part)[RB];
+  bf16x8 (&p)[RB];
+  float (&alpha)[RB];
+  const f32x4 (&wsc)[2];
+  float mt[RB], msub[RB], lsum[RB];
+  bool need_any = false;
+
+  __device__ __forceinline__ void run(int k) {
+    if (k >= kStages) return;
+    const int rb = k / kPerRb, st = k % kPerRb;
+    const f32x4 sa = s[0][rb], sb = s[1][rb];
+    if (st == 0) {
+      mt[rb] = fmaxf(fmaxf(fmaxf(sa[0], sa[1]), fmaxf(sa[2], sa[3])), fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3])));
+    } else if (st == 1) {
+      mt[rb] = rows_max(mt[rb]);
+    } else if (st == 2) {
+      const bool need = mt[rb] > m_used[rb] + kRowsTau;
+      const float al = need ? __builtin_amdgcn_exp2f(m_used[rb] - mt[rb]) : 1.f;  // 0 when m_used was -inf
+      m_used[rb] = need ? mt[rb] : m_used[rb];
+      alpha[rb] = al;
+      need_any |= need;
+      msub[rb] = m_used[rb] == -INFINITY ? 0.f : m_used[rb];
+      lsum[rb] = 0.f;
+    } else if (st < 7) {
+      const int e = st - 3;
+      const float p0 = __builtin_amdgcn_exp2f(sa[e] - msub[rb]);  // exp2(-inf) = 0
+      const float p1 = __builtin_amdgcn_exp2f(sb[e] - msub[rb]);
+      lsum[rb] += p0 + p1;
+      p[rb][e] = (bf16)(I4 ? p0 * wsc[0][e] : p0);
+      p[rb][4 + e] = (bf16)(I4 ? p1 * wsc[1][e] : p1);
+    } else {
+      l_part[rb] = l_part[rb] * alpha[rb] + lsum[rb];
+      // formed here, not sunk towards their first use in the next tile
+      asm volatile("" : "+v"(p[rb]), "+v"(l_part[rb]));
+    }
+  }
+  __device__ __forceinline__ bool moved() const { return __ballot(need_any) != 0; }
+};
+
+// The whole softmax at once (the first tile of a piece)
+template <int RB, bool I4>
+__device__ __forceinline__ bool softmax_tile(const f32x4 (&s)[2][RB], float (&m_used)[RB], float (&l_part)[RB],
+                                             bf16x8 (&p)[RB], float (&alpha)[RB], const f32x4 (&wsc)[2]) {
+  SoftmaxStages<RB, I4> sm{s, m_used, l_part, p, alpha, wsc};
+#pragma unroll
+  for (int k = 0; k < SoftmaxStages<RB, I4>::kStages; ++k) sm.run(k);
+  return sm.moved();
 }
 
 // O *= alpha (per row) in place in the accumulator registers, for the rare
@@ -541,20 +581,6 @@ __device__ __forceinline__ void sched_qk() {
   __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4 * RB, 0);
   __builtin_amdgcn_sched_group_barrier(kSchedDs, RB, 0);
   __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4 * RB, 0);
-}
-
-// PV of one tile: the transposed reads of the next column blocks are in
-// flight while a block's RB MFMAs issue.  (The next tile's softmax follows
-// the MFMAs; vector-ALU groups between them make the scheduler drop the
-// pattern.)
-template <int RB>
-__device__ __forceinline__ void sched_pv() {
-  __builtin_amdgcn_sched_group_barrier(kSchedDs, 2 * kPvPre<RB>, 0);
-#pragma unroll
-  for (int db = 0; db < 32; ++db) {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, RB, 0);
-    if (db + kPvPre<RB> < 32) __builtin_amdgcn_sched_group_barrier(kSchedDs, 2, 0);
-  }
 }
 
 // a when B, else b (same type): picks an accumulator at compile time
@@ -639,53 +665,68 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
   auto clampT = [cap](int t) -> int { return (int)max((int64_t)0, min((int64_t)t, cap)); };
   auto padT = [](int t) -> int { return (t + kTile - 1) / kTile * kTile; };
   // a request's length in the work split: whole tiles plus the piece cost
-  auto splitT = [padT](int t) -> int { return t > 0 ? padT(t) + kOv : 0; };
+  int ov = kOv;
+  auto splitT = [padT, &ov](int t) -> int { return t > 0 ? padT(t) + ov : 0; };
 
-  // ---- plan pass 1: total and longest request in the split's units ----
-  int tsum = 0, tmax = 0;
-  int Tr_lane = 0;
-  if (B <= 64) {
-    if (wave == 0) {
-      Tr_lane = lane < B ? clampT(seq_lens[lane]) : 0;
-      tsum = splitT(Tr_lane);
-      tmax = tsum;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        tsum += __shfl_xor(tsum, o);
-        tmax = max(tmax, __shfl_xor(tmax, o));
-      }
-    }
-  } else {
-    for (int b = tid; b < B; b += kRowsThreads) {
-      const int T = splitT(clampT(seq_lens[b]));
-      tsum += T;
-      tmax = max(tmax, T);
-    }
+  // ---- plan pass 1: total, longest and shortest request, each padded to
+  // whole tiles, and the requests with rows ----
+  int tsum = 0, tmax = 0, tmin = INT_MAX, nz = 0;
+  auto add_req = [&](int Tr) {
+    const int T = padT(Tr);
+    tsum += T;
+    tmax = max(tmax, T);
+    tmin = min(tmin, T);
+    nz += Tr > 0;
+  };
+  auto reduce_wave = [&]() {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       tsum += __shfl_xor(tsum, o);
       tmax = max(tmax, __shfl_xor(tmax, o));
+      tmin = min(tmin, __shfl_xor(tmin, o));
+      nz += __shfl_xor(nz, o);
     }
+  };
+  int Tr_lane = 0;
+  if (B <= 64) {
+    if (wave == 0) {
+      Tr_lane = lane < B ? clampT(seq_lens[lane]) : 0;
+      if (lane < B) add_req(Tr_lane);
+      reduce_wave();
+    }
+  } else {
+    for (int b = tid; b < B; b += kRowsThreads) add_req(clampT(seq_lens[b]));
+    reduce_wave();
     if (lane == 0) {
       sm.red[wave] = tsum;
       sm.red[kRowsWaves + wave] = tmax;
+      sm.red[2 * kRowsWaves + wave] = tmin;
+      sm.red[3 * kRowsWaves + wave] = nz;
     }
     __syncthreads();
-    tsum = 0;
+    tsum = nz = 0;
     tmax = 0;
+    tmin = INT_MAX;
 #pragma unroll
     for (int w = 0; w < kRowsWaves; ++w) {
       tsum += sm.red[w];
       tmax = max(tmax, sm.red[kRowsWaves + w]);
+      tmin = min(tmin, sm.red[2 * kRowsWaves + w]);
+      nz += sm.red[3 * kRowsWaves + w];
     }
   }
   const bool req_mode = n_split == 1;
   int share = 0;
   if (!req_mode) {
-    share = (tsum + n_share - 1) / n_share;
-    // the longest request's rows (without its piece cost) span at most n_split shares
-    const int tmax_rows = max(0, tmax - kOv);
-    share = max(share, (tmax_rows + n_split - 2) / (n_split - 1));
+    // requests of one length that whole shares tile exactly keep that split
+    // (one piece per share; the piece costs change nothing there, and the
+    // power-of-two strides between workgroups it gives long requests stream
+    // measurably faster than the shifted ones)
+    const int share0 = max(kTile, ((tsum + n_share - 1) / n_share + kTile - 1) / kTile * kTile);
+    if (tmin == tmax && tmax % share0 == 0) ov = 0;
+    share = (tsum + nz * ov + n_share - 1) / n_share;
+    // the longest request's rows span at most n_split shares
+    share = max(share, (tmax + n_split - 2) / (n_split - 1));
     share = max(kTile, (share + kTile - 1) / kTile * kTile);
   }
   const int lo = j * share, hi = lo + share;
@@ -723,7 +764,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
         if (lane >= o) incl += v;
       }
       // the request's rows start at S in the split's units (after its piece cost)
-      const int S = base + incl - V + (V > 0 ? kOv : 0);
+      const int S = base + incl - V + (V > 0 ? ov : 0);
       bool is_piece, tail;
       int r0 = 0, r1 = 0, slot = 0, cnt = 0;
       if (req_mode) {
@@ -942,6 +983,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
       bf16x8 p[RB];
       float alpha[RB];
       int lim[RB];
+      f32x4 wsc[2];  // int4 rows: the latent scales of the current tile's tokens
       // ---- tile 0: scores and softmax ----
       if constexpr (I4) {
         // tiles 0 and 1 landed (tile 2 in flight), unpacked by every wave;
@@ -964,7 +1006,8 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
         qk_tile<RB>(sm.lat[0], sm.rot[0], qrot_w, lane, qh, qrl, sacc, racc);
         tile_lim(0, lim);
         // (its factor multiplies an empty O)
-        softmax_tile<RB, I4>(sacc, racc, tile_full(0), lim, m_used, l_part, p, alpha, scl_of(0));
+        prep_scores<RB, I4>(sacc, racc, tile_full(0), lim, scl_of(0), wsc);
+        softmax_tile<RB, I4>(sacc, m_used, l_part, p, alpha, wsc);
       }
       for (int it = 0; it + 1 < n_tiles; ++it) {
         // 16-bit rows: tile it+1 in LDS (this wave's loads, with tile it+2
@@ -995,14 +1038,15 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
           tile_lim(it + 1, lim);
           qk_tile<RB>(sm.lat[(it + 1) % NLAT], sm.rot[(it + 1) % kRotStages], qrot_w, lane, qh, qrl, sacc, racc);
           sched_qk<RB>();
-          // the softmax of tile it+1 (its scores die here: only the two tiles'
-          // P operands live across the PV product), then the PV of tile it
-          bf16x8 pn[RB];
-          const bool moved = softmax_tile<RB, I4>(sacc, racc, tile_full(it + 1), lim, m_used, l_part, pn, alpha,
-                                                  scl_of(it + 1));
+          prep_scores<RB, I4>(sacc, racc, tile_full(it + 1), lim, scl_of(it + 1), wsc);
           __builtin_amdgcn_sched_barrier(0);
-          pv_tile<RB>(sm.lat[it % NLAT], lane, p, acc, load_next);
-          sched_pv<RB>();
+          // the PV of tile it with the softmax of tile it+1 between its MFMAs
+          // (the scores die there: only the two tiles' P operands live across
+          // the PV product)
+          bf16x8 pn[RB];
+          SoftmaxStages<RB, I4> smx{sacc, m_used, l_part, pn, alpha, wsc};
+          pv_tile<RB>(sm.lat[it % NLAT], lane, p, acc, load_next, [&](int db) { smx.run(db); });
+          const bool moved = smx.moved();
           __builtin_amdgcn_sched_barrier(0);
           if (moved) scale_acc<RB>(acc, alpha);
 #pragma unroll
@@ -1022,7 +1066,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
       wait_vmcnt<0>();
       wait_lgkm0();
       barrier_raw();
-      if (wave_rows) pv_tile<RB>(sm.lat[(n_tiles - 1) % NLAT], lane, p, acc, [](int) {});
+      if (wave_rows) pv_tile<RB>(sm.lat[(n_tiles - 1) % NLAT], lane, p, acc, [](int) {}, [](int) {});
 
       // ---- epilogue: 1/l, the lse with the latent lo part's first-order
       // share, the normalised partial output.  Every load and product comes
