@@ -480,6 +480,21 @@ __device__ __forceinline__ void prep_scores(f32x4 (&s)[2][RB], const f32x4 (&sr)
   }
 }
 
+// max of three (scores are finite or -inf, never NaN: no quieting of inputs,
+// which fmaxf costs the compiler one extra instruction per operand here)
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+// the max over the four lane groups of a row (lanes l, l + 16, l + 32, l + 48)
+__device__ __forceinline__ float rows_max_raw(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = max3_raw(__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return max3_raw(__uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[1]));
+}
+
 // Online softmax of one tile's prepared scores, already in log2 units (the
 // query carries scale * log2 e), with lazy rescaling: the P^T operands
 // (bf16), the factor each row's O must take and whether any row of the wave
@@ -505,9 +520,10 @@ struct SoftmaxStages {
     const int rb = k / kPerRb, st = k % kPerRb;
     const f32x4 sa = s[0][rb], sb = s[1][rb];
     if (st == 0) {
-      mt[rb] = fmaxf(fmaxf(fmaxf(sa[0], sa[1]), fmaxf(sa[2], sa[3])), fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3])));
+      const float m0 = max3_raw(sa[0], sa[1], sa[2]), m1 = max3_raw(sa[3], sb[0], sb[1]);
+      mt[rb] = max3_raw(m0, m1, max3_raw(sb[2], sb[3], sb[3]));
     } else if (st == 1) {
-      mt[rb] = rows_max(mt[rb]);
+      mt[rb] = rows_max_raw(mt[rb]);
     } else if (st == 2) {
       const bool need = mt[rb] > m_used[rb] + kRowsTau;
       const float al = need ? __builtin_amdgcn_exp2f(m_used[rb] - mt[rb]) : 1.f;  // 0 when m_used was -inf
