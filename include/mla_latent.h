@@ -73,7 +73,14 @@ typedef enum {
  * mla_quantize_latent_i8.  MLA_I4: rows of d_c / 2 bytes of 4-bit latent codes
  * followed by d_rope / 2 bytes of 4-bit rotary codes, two fp32 scales per row
  * (latent, rotary) in mla_segment.row_scale; see mla_quantize_latent_i4. */
-typedef enum { MLA_F32 = 0, MLA_BF16 = 1, MLA_I8 = 2, MLA_I4 = 3 } mla_dtype;
+/* MLA_BF16X2 is a query format only (mla_prepare_q's lat_dtype,
+ * mla_decode_splitkv's q_dtype): each fp32 value x held as two bf16 parts,
+ * hi = bf16(x) and lo = bf16(x - hi) (round to nearest), the d values of a
+ * row stored as a hi plane then a lo plane ([..][2][d] bf16, 4 bytes per
+ * value like fp32).  The decode reads only the hi plane while streaming the
+ * cache and only the lo plane at the end of each piece: half the query bytes
+ * of an fp32 query each time. */
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1, MLA_I8 = 2, MLA_I4 = 3, MLA_BF16X2 = 4 } mla_dtype;
 
 /*
  * rope_relocate_q -- rotary query for one KV segment.
@@ -171,8 +178,13 @@ typedef struct {
  * written, and its o_part row too when the lse is finite.  Across segments the
  * slot ranges of each head must tile [0, n_part) exactly.
  *
- * q_lat    [n_tok][n_heads][d_c]                 q_dtype, from mla_absorb_q; each
- *          segment's q_rot has q_dtype too
+ * q_lat    [n_tok][n_heads][d_c]                 q_dtype, from mla_absorb_q /
+ *          mla_prepare_q; each segment's q_rot has q_dtype too (fp32 for
+ *          MLA_BF16X2).  MLA_BF16X2: [n_tok][n_heads][2][d_c] bf16 hi and lo
+ *          planes (mla_prepare_q with lat_dtype MLA_BF16X2), for a bf16 cache
+ *          (not QK-Norm) or an int4 one; always the row-owning kernel; the
+ *          same arithmetic as an fp32 query (which is split into exactly
+ *          these parts inside the kernel).
  * caches   cache_dtype.  MLA_BF16 caches take an fp32 query or a bf16 one.
  *          An fp32 query is split into bf16 hi + lo parts: groups of up to
  *          32 query rows multiply both parts; 64-row groups multiply lo
@@ -185,7 +197,7 @@ typedef struct {
  *          q_lat . code_t and its softmax weight multiplies scale_t code_t,
  *          exactly the attention over the dequantized rows; not combined
  *          with QK-Norm.  MLA_I4 caches (the abstract's joint INT4
- *          content and rotary caches) take an fp32 query and every
+ *          content and rotary caches) take an fp32 or split query and every
  *          segment's (latent, rotary) scale pairs: the score of row t is
  *          scale * (sc_t q_lat . code_t + sr_t q_rot . rcode_t) and its
  *          weight multiplies sc_t code_t, the attention over the
@@ -241,7 +253,9 @@ mla_status mla_combine_lse(const void* o_part, int part_dtype, const float* lse_
  *   q_lat     = mla_absorb_q(q_nope, w_uk)                 (lat_dtype)
  *   q_rots[k] = rope_relocate_q(q_pe, pos, shifts[k])      (rot_dtype), k < n_shift
  *
- * q_nope, w_uk, q_lat, q_pe, pos: as in mla_absorb_q / rope_relocate_q; q_pe
+ * q_nope, w_uk, q_lat, q_pe, pos: as in mla_absorb_q / rope_relocate_q (lat_dtype
+ * may also be MLA_BF16X2 on the MFMA path: the fp32 result written as its
+ * bf16 hi and lo planes, [n_tok][n_heads][2][d_c]); q_pe
  * and w_uk have in_dtype, q_nope has q_dtype: either in_dtype, or MLA_F32
  * with bf16 weights on the MFMA path (an fp32 query, e.g. the output of
  * mla_qknorm_query, enters as bf16 hi + lo parts with fp32 accumulation;

@@ -19,6 +19,7 @@ MLA_F32 = 0
 MLA_BF16 = 1
 MLA_I8 = 2  # cache format: int8 latent codes + bf16 rotary entries per row, fp32 scale per row
 MLA_I4 = 3  # cache format: 4-bit latent and rotary codes per row, two fp32 scales per row
+MLA_BF16X2 = 4  # query format: bf16 hi and lo planes of fp32 values, [..][2][d]
 
 STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_DTYPE", 4: "MLA_ERR_ALIGN",
           5: "MLA_ERR_UNSUPPORTED", 6: "MLA_ERR_WORKSPACE", 7: "MLA_ERR_HIP"}

@@ -37,6 +37,8 @@ mla_status hip_status(hipError_t e, const char* what) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool dtype_ok(int dt) { return dt == MLA_F32 || dt == MLA_BF16; }
+// q_lat storage of the fused query kernel: 0 fp32, 1 bf16, 2 bf16 hi and lo planes
+int lat_mode(int dt) { return dt == MLA_BF16X2 ? 2 : dt == MLA_BF16 ? 1 : 0; }
 
 int cu_count() {
   static std::mutex mu;
@@ -135,7 +137,8 @@ mla_status mla_prepare_q(const void* q_nope, int q_dtype, const void* q_pe, cons
                          double base, void* stream) {
   if (!q_nope || !q_pe || !w_uk || !q_lat || !pos || (n_shift > 0 && !q_rots))
     return fail(MLA_ERR_NULL, "mla_prepare_q: null pointer");
-  if (!dtype_ok(q_dtype) || !dtype_ok(in_dtype) || !dtype_ok(lat_dtype) || !dtype_ok(rot_dtype))
+  if (!dtype_ok(q_dtype) || !dtype_ok(in_dtype) || !(dtype_ok(lat_dtype) || lat_dtype == MLA_BF16X2) ||
+      !dtype_ok(rot_dtype))
     return fail(MLA_ERR_DTYPE, "mla_prepare_q: dtypes %d, %d, %d, %d", q_dtype, in_dtype, lat_dtype, rot_dtype);
   if (n_shift < 0 || n_shift > mla::kMaxShift)
     return fail(MLA_ERR_SHAPE, "mla_prepare_q: n_shift=%d (0..%d)", n_shift, mla::kMaxShift);
@@ -150,6 +153,9 @@ mla_status mla_prepare_q(const void* q_nope, int q_dtype, const void* q_pe, cons
   if (q_dtype != in_dtype && !(q_dtype == MLA_F32 && mfma))
     return fail(MLA_ERR_UNSUPPORTED, "mla_prepare_q: an fp32 query with bf16 weights needs d_nope=128, d_c=512 "
                 "and 16-byte aligned q_nope and w_uk");
+  if (lat_dtype == MLA_BF16X2 && !mfma)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_prepare_q: a split q_lat (MLA_BF16X2) needs bf16 weights, d_nope=128, "
+                "d_c=512 and 16-byte aligned q_nope and w_uk");
   if (n_tok == 0) return ok();
   const hipStream_t st = (hipStream_t)stream;
   if (mfma) {
@@ -159,7 +165,7 @@ mla_status mla_prepare_q(const void* q_nope, int q_dtype, const void* q_pe, cons
       rt.q_rot[k] = q_rots[k];
       rt.shift[k] = shifts ? shifts[k] : nullptr;
     }
-    return hip_status(mla::launch_prepare_mfma(q_nope, q_dtype == MLA_F32, w_uk, q_lat, lat_dtype == MLA_BF16, q_pe,
+    return hip_status(mla::launch_prepare_mfma(q_nope, q_dtype == MLA_F32, w_uk, q_lat, lat_mode(lat_dtype), q_pe,
                                                pos, rt, rot_dtype == MLA_BF16, n_tok, n_heads, d_rope, base,
                                                mla::QkArgs{}, st),
                       "mla_prepare_q launch");
@@ -184,7 +190,8 @@ mla_status mla_prepare_q_qknorm(const void* q_nope, int q_dtype, const float* g_
                                 double base, void* stream) {
   if (!q_nope || !g_q || !g_k || !q_pe || !w_uk || !q_lat || !pos || (n_shift > 0 && !q_rots))
     return fail(MLA_ERR_NULL, "mla_prepare_q_qknorm: null pointer");
-  if (!dtype_ok(q_dtype) || !dtype_ok(in_dtype) || !dtype_ok(lat_dtype) || !dtype_ok(rot_dtype))
+  if (!dtype_ok(q_dtype) || !dtype_ok(in_dtype) || !(dtype_ok(lat_dtype) || lat_dtype == MLA_BF16X2) ||
+      !dtype_ok(rot_dtype))
     return fail(MLA_ERR_DTYPE, "mla_prepare_q_qknorm: dtypes %d, %d, %d, %d", q_dtype, in_dtype, lat_dtype,
                 rot_dtype);
   if (n_shift < 0 || n_shift > mla::kMaxShift)
@@ -212,7 +219,7 @@ mla_status mla_prepare_q_qknorm(const void* q_nope, int q_dtype, const float* g_
   qk.g_q = g_q;
   qk.g_k = g_k;
   qk.eps = eps;
-  return hip_status(mla::launch_prepare_mfma(q_nope, q_dtype == MLA_F32, w_uk, q_lat, lat_dtype == MLA_BF16, q_pe,
+  return hip_status(mla::launch_prepare_mfma(q_nope, q_dtype == MLA_F32, w_uk, q_lat, lat_mode(lat_dtype), q_pe,
                                              pos, rt, rot_dtype == MLA_BF16, n_tok, n_heads, d_rope, base, qk,
                                              (hipStream_t)stream),
                     "mla_prepare_q_qknorm launch");
@@ -355,9 +362,12 @@ mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q
                               int cache_dtype, int batch, int s_q, int n_heads, int d_c, int d_rope, float scale,
                               void* o_part, int part_dtype, float* lse_part, int n_part, int n_wg, void* stream) {
   if (!segs || !q_lat || !o_part || !lse_part) return fail(MLA_ERR_NULL, "mla_decode_splitkv: null pointer");
-  if (!dtype_ok(q_dtype) || !(dtype_ok(cache_dtype) || cache_dtype == MLA_I8 || cache_dtype == MLA_I4) ||
-      !dtype_ok(part_dtype))
+  if (!(dtype_ok(q_dtype) || q_dtype == MLA_BF16X2) ||
+      !(dtype_ok(cache_dtype) || cache_dtype == MLA_I8 || cache_dtype == MLA_I4) || !dtype_ok(part_dtype))
     return fail(MLA_ERR_DTYPE, "mla_decode_splitkv: dtypes %d, %d, %d", q_dtype, cache_dtype, part_dtype);
+  const bool qx2 = q_dtype == MLA_BF16X2;
+  if (qx2 && cache_dtype != MLA_BF16 && cache_dtype != MLA_I4)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_decode_splitkv: a split query (MLA_BF16X2) needs a bf16 or int4 cache");
   if (cache_dtype == MLA_F32 && q_dtype != MLA_F32)
     return fail(MLA_ERR_UNSUPPORTED, "mla_decode_splitkv: an fp32 cache needs an fp32 query");
   if (cache_dtype == MLA_F32 && part_dtype != MLA_F32)
@@ -370,7 +380,9 @@ mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q
   const bool lowbit = i8 || i4;
   const bool bf = cache_dtype == MLA_BF16 || lowbit;  // the MFMA kernels (16-bit, int8 or int4 rows)
   const bool q32 = q_dtype == MLA_F32;
-  if (lowbit && !q32) return fail(MLA_ERR_UNSUPPORTED, "mla_decode_splitkv: a low-bit cache needs an fp32 query");
+  if (i8 && !q32) return fail(MLA_ERR_UNSUPPORTED, "mla_decode_splitkv: an int8 cache needs an fp32 query");
+  if (i4 && !q32 && !qx2)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_decode_splitkv: an int4 cache needs an fp32 or split query");
   if (bf) {
     if (d_c != kBf16Dc || d_rope != kBf16Dr)
       return fail(MLA_ERR_UNSUPPORTED, "mla_decode_splitkv: bf16 path needs d_c=512, d_rope=64 (got %d, %d)", d_c,
@@ -452,6 +464,7 @@ mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q
   a.q_lat = q_lat;
   a.o_part = o_part;
   a.part_bf16 = part_dtype == MLA_BF16;
+  a.q_split = qx2;
   a.lse_part = lse_part;
   a.batch = batch;
   a.s_q = s_q;
@@ -460,9 +473,10 @@ mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q
   a.d_rope = d_rope;
   a.n_part = n_part;
   a.scale = scale;
-  // several segments on the row-owning path: one launch over all of them,
-  // the grid split by each segment's share of the work
-  if (i4 || (rows_path && n_segs > 1))
+  // several segments on the row-owning path (or an int4 cache, or a split
+  // query, which only that kernel reads): one launch over all of them, the
+  // grid split by each segment's share of the work
+  if (i4 || qx2 || (rows_path && n_segs > 1))
     return hip_status(mla::launch_decode_rows_multi(a, sa.data(), n_segs, wg, i4, (hipStream_t)stream),
                       "mla_decode_splitkv launch");
   for (int g = 0; g < n_segs; ++g) {

@@ -42,6 +42,9 @@ template <> __device__ __forceinline__ f32x4 load_part4<bf16>(const bf16* p) {
   return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
 }
 
+// Tag type of a query written as bf16 hi and lo planes ([..][2][d]: hi =
+// bf16(x), lo = bf16(x - hi)); pointers of this type are cast before use.
+struct SplitBf16 {};
 template <typename T> __device__ __forceinline__ void store_f(T* p, float v);
 template <> __device__ __forceinline__ void store_f<float>(float* p, float v) { *p = v; }
 template <> __device__ __forceinline__ void store_f<bf16>(bf16* p, float v) { *p = (bf16)v; }

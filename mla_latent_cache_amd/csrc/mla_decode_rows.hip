@@ -41,15 +41,17 @@
 //    rare lazy rescale of O.  So the score chain, the softmax's dependent
 //    VALU/transcendental chain and both products share one instruction stream
 //    per SIMD without waiting on one another.
-//  * Query precision: q_lat and q_rot arrive in fp32 and are multiplied by
-//    scale * log2 e (scores come out in log2 units), then split into bf16 hi
-//    and lo parts.  The latent part is multiplied as hi only; the rotary
-//    part as hi + lo.  With delta_t = lo . c_t the neglected part of a
-//    latent score, log2 sum 2^(s_t + delta_t) = lse2 + sum_t p_t delta_t +
-//    O(var_p delta), so the lse gains lo . o (o = the normalised weighted
-//    latent, which each wave holds for its rows; ln 2 times that in natural
-//    units), leaving a second-order error (about 1e-5 at unit-variance
-//    inputs).
+//  * Query precision: the query is split into bf16 hi and lo parts (q_rot
+//    here, from fp32; q_lat here too, or by the producer, which then stores
+//    the two parts as planes so that the prologue reads only the hi plane
+//    and the epilogue only the lo plane: half the bytes of the fp32 query
+//    each).  The latent part is multiplied as hi only; the rotary part as
+//    hi + lo.  With delta_t = lo . c_t the neglected part of a latent
+//    score, log sum exp(s_t + delta_t) = lse + sum_t p_t delta_t +
+//    O(var_p delta), so the lse gains scale * lo . o (o = the normalised
+//    weighted latent, which each wave holds for its rows), leaving a
+//    second-order error (about 1e-5 at unit-variance inputs).  The scores
+//    are q . k; the softmax scale (times log2 e) enters in its exponent.
 //  * Softmax in the exp2 domain with lazy rescaling: the running max moves
 //    only when a tile max exceeds it by more than kRowsTau (log2 units), so
 //    the O rescale almost never runs; when it does, it runs outside the tile
@@ -330,16 +332,19 @@ __device__ __forceinline__ void qk_tile(const char* __restrict__ ls, const char*
   const int xr = (xl >> 1) & 7;
   const bool split_rot = &sr[0][0] != &s[0][0];  // int4 rows: the rotary part apart
   // the rotary query's hi parts from LDS (row 16 rb + l16 of the wave's rows,
-  // chunk 4 jr + lg, placed like the rotary ring), read first so that their
-  // latency hides behind the latent k-steps
+  // chunk 4 jr + lg, placed like the rotary ring), read kQrAhead latent
+  // k-steps before they are needed, so that their latency hides behind those
   bf16x8 qrh[RB][2];
+  constexpr int kQrAhead = 6;
+  auto read_qrh = [&]() {
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int jr = 0; jr < 2; ++jr) {
-      const int qr = 16 * rb + xl;
-      qrh[rb][jr] = *(const bf16x8*)(qs + qr * kRBytes + (rpos(qr, 4 * jr + xg) << 4));
-    }
+      for (int jr = 0; jr < 2; ++jr) {
+        const int qr = 16 * rb + xl;
+        qrh[rb][jr] = *(const bf16x8*)(qs + qr * kRBytes + (rpos(qr, 4 * jr + xg) << 4));
+      }
+  };
   // K operands of k-step ks (ks < 16 latent, then 2 rotary), read kPre
   // k-steps ahead of their MFMAs
   auto kop = [&](int ks, int tb) -> bf16x8 {
@@ -355,6 +360,7 @@ __device__ __forceinline__ void qk_tile(const char* __restrict__ ls, const char*
   }
 #pragma unroll
   for (int ks = 0; ks < kKSteps; ++ks) {
+    if (ks == kDc / 32 - kQrAhead) read_qrh();
     if (ks + kPre < kKSteps) {
       ka[(ks + kPre) % (kPre + 1)][0] = kop(ks + kPre, 0);
       ka[(ks + kPre) % (kPre + 1)][1] = kop(ks + kPre, 1);
@@ -495,10 +501,10 @@ __device__ __forceinline__ float rows_max_raw(float v) {
   return max3_raw(__uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[1]));
 }
 
-// Online softmax of one tile's prepared scores, already in log2 units (the
-// query carries scale * log2 e), with lazy rescaling: the P^T operands
-// (bf16), the factor each row's O must take and whether any row of the wave
-// moved its max.  Cut into kStages short stages (per row block: the tile
+// Online softmax of one tile's prepared scores (q . k, before the softmax
+// scale), in the exp2 domain: weights 2^(sl2 s - m) with sl2 = scale * log2 e,
+// with lazy rescaling: the P^T operands (bf16), the factor each row's O must
+// take and whether any row of the wave moved its max.  Cut into kStages short stages (per row block: the tile
 // max, its reduction over the lane groups, the max update, four pairs of
 // weights, the packing) that run one per PV column block, between the MFMAs
 // of the previous tile's PV.
@@ -512,6 +518,7 @@ struct SoftmaxStages {
   bf16x8 (&p)[RB];
   float (&alpha)[RB];
   const f32x4 (&wsc)[2];
+  float sl2;
   float mt[RB], msub[RB], lsum[RB];
   bool need_any = false;
 
@@ -521,7 +528,7 @@ struct SoftmaxStages {
     const f32x4 sa = s[0][rb], sb = s[1][rb];
     if (st == 0) {
       const float m0 = max3_raw(sa[0], sa[1], sa[2]), m1 = max3_raw(sa[3], sb[0], sb[1]);
-      mt[rb] = max3_raw(m0, m1, max3_raw(sb[2], sb[3], sb[3]));
+      mt[rb] = max3_raw(m0, m1, max3_raw(sb[2], sb[3], sb[3])) * sl2;  // sl2 > 0
     } else if (st == 1) {
       mt[rb] = rows_max_raw(mt[rb]);
     } else if (st == 2) {
@@ -534,8 +541,8 @@ struct SoftmaxStages {
       lsum[rb] = 0.f;
     } else if (st < 7) {
       const int e = st - 3;
-      const float p0 = __builtin_amdgcn_exp2f(sa[e] - msub[rb]);  // exp2(-inf) = 0
-      const float p1 = __builtin_amdgcn_exp2f(sb[e] - msub[rb]);
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[e], sl2, -msub[rb]));  // exp2(-inf) = 0
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[e], sl2, -msub[rb]));
       lsum[rb] += p0 + p1;
       p[rb][e] = (bf16)(I4 ? p0 * wsc[0][e] : p0);
       p[rb][4 + e] = (bf16)(I4 ? p1 * wsc[1][e] : p1);
@@ -551,8 +558,9 @@ struct SoftmaxStages {
 // The whole softmax at once (the first tile of a piece)
 template <int RB, bool I4>
 __device__ __forceinline__ bool softmax_tile(const f32x4 (&s)[2][RB], float (&m_used)[RB], float (&l_part)[RB],
-                                             bf16x8 (&p)[RB], float (&alpha)[RB], const f32x4 (&wsc)[2]) {
-  SoftmaxStages<RB, I4> sm{s, m_used, l_part, p, alpha, wsc};
+                                             bf16x8 (&p)[RB], float (&alpha)[RB], const f32x4 (&wsc)[2],
+                                             float sl2) {
+  SoftmaxStages<RB, I4> sm{s, m_used, l_part, p, alpha, wsc, sl2};
 #pragma unroll
   for (int k = 0; k < SoftmaxStages<RB, I4>::kStages; ++k) sm.run(k);
   return sm.moved();
@@ -612,7 +620,7 @@ __device__ __forceinline__ T& pick(T& a, T& b) {
 // int4 rows (packed latent and rotary codes, two scales per row).  PB: bf16
 // partial outputs (a compile-time choice: a branch in the epilogue changes
 // the register allocation of the tile loop).
-template <int RB, bool I4, bool PB>
+template <int RB, bool I4, bool PB, bool QS>
 __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch L) {
   constexpr int MT = 16 * RB * kRowsWaves;  // query rows of a row group
   constexpr int kOv = piece_tiles(MT, PB) * kTile;  // a request's start, in rows of the work split
@@ -915,31 +923,45 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
         if (!wave_rows) break;
         const RowInfo ri = row_info(rb);
         const int64_t qi = (int64_t)b * s_q * n_heads + ri.qoff;
-        const float* ql = q_lat + qi * kDc + 8 * lg;
         const float* qr = q_rot + qi * kDr + 8 * lg;
-        // two batches of 9 k-steps: the 18 loads of a batch go out together
-        // (unconditional: a row past the group reads row0's query and is
-        // zeroed), then their conversions, each pinned where it is formed so
-        // the fp32 staging registers die before the next batch
+        const float* ql = q_lat + qi * kDc + 8 * lg;                   // fp32 query
+        const bf16* qlh = (const bf16*)q_lat + qi * (2 * kDc) + 8 * lg;  // split query: its hi plane
+        // two batches of 9 k-steps: the loads of a batch go out together
+        // (unconditional: a row past the group reads row0's query), then
+        // their conversions, each pinned where it is formed so the staging
+        // registers die before the next batch.  The rotary part, and the
+        // latent part of an fp32 query, are split here (a row past the group
+        // gets zeros); a split query's hi plane is used as it is (a row past
+        // the group keeps row0's: its results are never stored).
         constexpr int kBatch = kKSteps / 2;
 #pragma unroll
         for (int k0 = 0; k0 < kKSteps; k0 += kBatch) {
           f32x4 v[kBatch][2];
+          bf16x8 hv[kBatch];
 #pragma unroll
           for (int i = 0; i < kBatch; ++i) {
             const int ks = k0 + i;
-            const float* src = ks < kDc / 32 ? ql + 32 * ks : qr + 32 * (ks - kDc / 32);
-            v[i][0] = *(const f32x4*)src;
-            v[i][1] = *(const f32x4*)(src + 4);
+            if (QS && ks < kDc / 32) {
+              hv[i] = *(const bf16x8*)(qlh + 32 * ks);
+            } else {
+              const float* src = ks < kDc / 32 ? ql + 32 * ks : qr + 32 * (ks - kDc / 32);
+              v[i][0] = *(const f32x4*)src;
+              v[i][1] = *(const f32x4*)(src + 4);
+            }
           }
 #pragma unroll
           for (int i = 0; i < kBatch; ++i) {
             const int ks = k0 + i;
+            if (QS && ks < kDc / 32) {
+              qh[rb][ks] = hv[i];
+              asm volatile("" ::"v"(hv[i]));
+              continue;
+            }
             if (!ri.valid) v[i][0] = v[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
             bf16x8 h8, l8;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const float x = v[i][e >> 2][e & 3] * sl2;  // scores come out in log2 units
+              const float x = v[i][e >> 2][e & 3];
               const bf16 h = (bf16)x;
               h8[e] = h;
               l8[e] = (bf16)(x - (float)h);
@@ -1023,7 +1045,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
         tile_lim(0, lim);
         // (its factor multiplies an empty O)
         prep_scores<RB, I4>(sacc, racc, tile_full(0), lim, scl_of(0), wsc);
-        softmax_tile<RB, I4>(sacc, m_used, l_part, p, alpha, wsc);
+        softmax_tile<RB, I4>(sacc, m_used, l_part, p, alpha, wsc, sl2);
       }
       for (int it = 0; it + 1 < n_tiles; ++it) {
         // 16-bit rows: tile it+1 in LDS (this wave's loads, with tile it+2
@@ -1060,7 +1082,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
           // (the scores die there: only the two tiles' P operands live across
           // the PV product)
           bf16x8 pn[RB];
-          SoftmaxStages<RB, I4> smx{sacc, m_used, l_part, pn, alpha, wsc};
+          SoftmaxStages<RB, I4> smx{sacc, m_used, l_part, pn, alpha, wsc, sl2};
           pv_tile<RB>(sm.lat[it % NLAT], lane, p, acc, load_next, [&](int db) { smx.run(db); });
           const bool moved = smx.moved();
           __builtin_amdgcn_sched_barrier(0);
@@ -1097,20 +1119,43 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
           // 32 query loads go out together (a row past the group reads
           // row0's query), then the products
           const RowInfo ri = row_info(rb);
-          const float* ql = q_lat + ((int64_t)b * s_q * n_heads + ri.qoff) * kDc + 4 * lg;
-          f32x4 qv[32];
-#pragma unroll
-          for (int db = 0; db < 32; ++db) qv[db] = *(const f32x4*)(ql + 16 * db);
-          __builtin_amdgcn_sched_barrier(0);
+          const int64_t qi = (int64_t)b * s_q * n_heads + ri.qoff;
           float c = 0.f;
+          if constexpr (QS) {
+            // the lo plane as it is: this lane's 4 columns of each block are
+            // half of a 16-byte load that the lane of the neighbouring lane
+            // group shares (8-byte loads here make the compiler spill the
+            // query's hi parts inside the tile loop)
+            const float* qll = (const float*)((const bf16*)q_lat + qi * (2 * kDc) + kDc + 8 * (lg >> 1));
+            const bool odd = lg & 1;
+            f32x4 qv[32];
 #pragma unroll
-          for (int db = 0; db < 32; ++db)
+            for (int db = 0; db < 32; ++db) qv[db] = *(const f32x4*)(qll + 8 * db);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float x = qv[db][e] * sl2;  // the lo part as the prologue split it
-              c += (float)(bf16)(x - (float)(bf16)x) * acc[db][rb][e];
+            for (int db = 0; db < 32; ++db) {
+              const uint32_t w0 = __float_as_uint(odd ? qv[db][2] : qv[db][0]);
+              const uint32_t w1 = __float_as_uint(odd ? qv[db][3] : qv[db][1]);
+              c += __uint_as_float(w0 << 16) * acc[db][rb][0];
+              c += __uint_as_float(w0 & 0xffff0000u) * acc[db][rb][1];
+              c += __uint_as_float(w1 << 16) * acc[db][rb][2];
+              c += __uint_as_float(w1 & 0xffff0000u) * acc[db][rb][3];
             }
-          cs[rb] = rows_sum(c);
+          } else {
+            const float* ql = q_lat + qi * kDc + 4 * lg;
+            f32x4 qv[32];
+#pragma unroll
+            for (int db = 0; db < 32; ++db) qv[db] = *(const f32x4*)(ql + 16 * db);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int db = 0; db < 32; ++db)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float x = qv[db][e];  // the lo part as the prologue split it
+                c += (float)(bf16)(x - (float)(bf16)x) * acc[db][rb][e];
+              }
+          }
+          cs[rb] = rows_sum(c) * sl2;
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -1135,12 +1180,18 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
   }
 }
 
-template __global__ void decode_rows_kernel<1, false, false>(RowsLaunch);
-template __global__ void decode_rows_kernel<2, false, false>(RowsLaunch);
-template __global__ void decode_rows_kernel<1, true, false>(RowsLaunch);
-template __global__ void decode_rows_kernel<1, false, true>(RowsLaunch);
-template __global__ void decode_rows_kernel<2, false, true>(RowsLaunch);
-template __global__ void decode_rows_kernel<1, true, true>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, false, false, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<2, false, false, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, true, false, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, false, true, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<2, false, true, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, true, true, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, false, false, true>(RowsLaunch);
+template __global__ void decode_rows_kernel<2, false, false, true>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, true, false, true>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, false, true, true>(RowsLaunch);
+template __global__ void decode_rows_kernel<2, false, true, true>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, true, true, true>(RowsLaunch);
 
 int decode_rows_tile(int rows_total) { return rows_total <= 64 ? 64 : 128; }
 
@@ -1174,17 +1225,21 @@ SegCost seg_cost(const DecodeArgs& a, const SegArgs& s, int mt) {
   return c;
 }
 
-template <bool PB>
+template <bool PB, bool QS>
 hipError_t launch_rows_pb(const RowsLaunch& L, int mt, bool i4, int grid, hipStream_t stream) {
   const dim3 block(kRowsThreads);
-  if (i4) return launch(decode_rows_kernel<1, true, PB>, dim3(grid), block, stream, L);
-  if (mt == 64) return launch(decode_rows_kernel<1, false, PB>, dim3(grid), block, stream, L);
-  return launch(decode_rows_kernel<2, false, PB>, dim3(grid), block, stream, L);
+  if (i4) return launch(decode_rows_kernel<1, true, PB, QS>, dim3(grid), block, stream, L);
+  if (mt == 64) return launch(decode_rows_kernel<1, false, PB, QS>, dim3(grid), block, stream, L);
+  return launch(decode_rows_kernel<2, false, PB, QS>, dim3(grid), block, stream, L);
 }
 
 hipError_t launch_rows(const RowsLaunch& L, int mt, bool i4, int grid, hipStream_t stream) {
-  if (L.a.part_bf16) return launch_rows_pb<true>(L, mt, i4, grid, stream);
-  return launch_rows_pb<false>(L, mt, i4, grid, stream);
+  if (L.a.q_split) {
+    if (L.a.part_bf16) return launch_rows_pb<true, true>(L, mt, i4, grid, stream);
+    return launch_rows_pb<false, true>(L, mt, i4, grid, stream);
+  }
+  if (L.a.part_bf16) return launch_rows_pb<true, false>(L, mt, i4, grid, stream);
+  return launch_rows_pb<false, false>(L, mt, i4, grid, stream);
 }
 
 }  // namespace

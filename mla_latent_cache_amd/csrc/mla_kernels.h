@@ -31,6 +31,7 @@ struct DecodeArgs {
   const void* q_lat;
   void* o_part;       // fp32, or bf16 when part_bf16
   int part_bf16;
+  int q_split;        // q_lat as bf16 hi and lo planes [..][2][d_c] (else fp32 [..][d_c])
   float* lse_part;
   int batch;
   int s_q;
@@ -87,7 +88,8 @@ struct QkArgs {
   const float* g_k = nullptr;  // [n_heads][d_nope]
   float eps = 0.f;
 };
-hipError_t launch_prepare_mfma(const void* q_nope, bool q_f32, const void* w_uk, void* q_lat, bool lat_bf16,
+// lat_mode: 0 fp32, 1 bf16, 2 bf16 hi and lo planes
+hipError_t launch_prepare_mfma(const void* q_nope, bool q_f32, const void* w_uk, void* q_lat, int lat_mode,
                                const void* q_pe, const int64_t* pos, const RopeTargets& rt, bool rot_bf16, int n_tok,
                                int n_heads, int d_rope, double base, const QkArgs& qk, hipStream_t stream);
 hipError_t launch_absorb_mfma(const void* q_nope, const void* w_uk, void* q_lat, bool out_bf16, int n_tok,

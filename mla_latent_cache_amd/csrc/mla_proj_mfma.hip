@@ -15,6 +15,7 @@
 #include "mla_kernels.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace mla {
 namespace {
@@ -159,7 +160,16 @@ __device__ __forceinline__ void absorb_block(const TQ* __restrict__ q_nope, cons
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int tt = t0 + 4 * lg + e;
-        if (tt < n_tok) store_f(q_lat + ((int64_t)tt * n_heads + h) * kLat + j0 + c0 + l16, acc[e]);
+        if (tt >= n_tok) continue;
+        if constexpr (std::is_same_v<TO, SplitBf16>) {
+          // hi plane, then lo plane, of the token's row
+          bf16* row = (bf16*)q_lat + ((int64_t)tt * n_heads + h) * (2 * kLat);
+          const bf16 hi = (bf16)acc[e];
+          row[j0 + c0 + l16] = hi;
+          row[kLat + j0 + c0 + l16] = (bf16)(acc[e] - (float)hi);
+        } else {
+          store_f(q_lat + ((int64_t)tt * n_heads + h) * kLat + j0 + c0 + l16, acc[e]);
+        }
       }
     }
   }
@@ -267,10 +277,17 @@ static hipError_t prepare_launch(const void* q_nope, const void* w_uk, void* q_l
 }
 
 template <typename TQ>
-static hipError_t prepare_dispatch(const void* q_nope, const void* w_uk, void* q_lat, bool lat_bf16,
+static hipError_t prepare_dispatch(const void* q_nope, const void* w_uk, void* q_lat, int lat_mode,
                                    const void* q_pe, const int64_t* pos, const RopeTargets& rt, bool rot_bf16,
                                    int n_tok, int n_heads, int d_rope, double base, const QkArgs& qk,
                                    hipStream_t stream) {
+  if (lat_mode == 2 && rot_bf16)
+    return prepare_launch<SplitBf16, bf16, TQ>(q_nope, w_uk, q_lat, q_pe, pos, rt, n_tok, n_heads, d_rope, base, qk,
+                                               stream);
+  if (lat_mode == 2)
+    return prepare_launch<SplitBf16, float, TQ>(q_nope, w_uk, q_lat, q_pe, pos, rt, n_tok, n_heads, d_rope, base,
+                                                qk, stream);
+  const bool lat_bf16 = lat_mode == 1;
   if (lat_bf16 && rot_bf16)
     return prepare_launch<bf16, bf16, TQ>(q_nope, w_uk, q_lat, q_pe, pos, rt, n_tok, n_heads, d_rope, base, qk,
                                           stream);
@@ -284,13 +301,13 @@ static hipError_t prepare_dispatch(const void* q_nope, const void* w_uk, void* q
                                           stream);
 }
 
-hipError_t launch_prepare_mfma(const void* q_nope, bool q_f32, const void* w_uk, void* q_lat, bool lat_bf16,
+hipError_t launch_prepare_mfma(const void* q_nope, bool q_f32, const void* w_uk, void* q_lat, int lat_mode,
                                const void* q_pe, const int64_t* pos, const RopeTargets& rt, bool rot_bf16, int n_tok,
                                int n_heads, int d_rope, double base, const QkArgs& qk, hipStream_t stream) {
   if (q_f32)
-    return prepare_dispatch<float>(q_nope, w_uk, q_lat, lat_bf16, q_pe, pos, rt, rot_bf16, n_tok, n_heads, d_rope,
+    return prepare_dispatch<float>(q_nope, w_uk, q_lat, lat_mode, q_pe, pos, rt, rot_bf16, n_tok, n_heads, d_rope,
                                    base, qk, stream);
-  return prepare_dispatch<bf16>(q_nope, w_uk, q_lat, lat_bf16, q_pe, pos, rt, rot_bf16, n_tok, n_heads, d_rope, base,
+  return prepare_dispatch<bf16>(q_nope, w_uk, q_lat, lat_mode, q_pe, pos, rt, rot_bf16, n_tok, n_heads, d_rope, base,
                                 qk, stream);
 }
 

@@ -11,7 +11,7 @@ from typing import List, Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import MLA_BF16, MLA_F32, MLA_I4, MLA_I8, MlaSegment
+from ._lib import MLA_BF16, MLA_BF16X2, MLA_F32, MLA_I4, MLA_I8, MlaSegment
 
 _DT = {torch.float32: MLA_F32, torch.bfloat16: MLA_BF16}
 
@@ -28,6 +28,21 @@ def _dt(t: torch.Tensor) -> int:
     if t.dtype not in _DT:
         raise TypeError(f"unsupported dtype {t.dtype}")
     return _DT[t.dtype]
+
+
+def is_split_query(q_lat: torch.Tensor) -> bool:
+    """A query held as bf16 hi and lo planes: bf16 [n_tok, n_heads, 2, d_c]."""
+    return q_lat.dtype == torch.bfloat16 and q_lat.dim() == 4 and q_lat.shape[2] == 2
+
+
+def _lat_dt(q_lat: torch.Tensor) -> int:
+    """dtype code of a q_lat tensor (MLA_BF16X2 for the split form)."""
+    return MLA_BF16X2 if is_split_query(q_lat) else _dt(q_lat)
+
+
+def split_query(n_tok: int, n_heads: int, d_c: int, device) -> torch.Tensor:
+    """An empty split query (mla_prepare_q writes it with lat_dtype MLA_BF16X2)."""
+    return torch.empty((n_tok, n_heads, 2, d_c), dtype=torch.bfloat16, device=device)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -81,7 +96,7 @@ def prepare_args(q_nope: torch.Tensor, q_pe: torch.Tensor, w_uk: torch.Tensor, q
     rot_arr = (ctypes.c_void_p * max(1, n))(*[r.data_ptr() for r in q_rots])
     sh_arr = (ctypes.c_void_p * max(1, n))(*[_ptr(s) for s in shifts])
     rot_dt = _dt(q_rots[0]) if n else 0
-    return (_ptr(q_nope), _dt(q_nope), _ptr(q_pe), _ptr(w_uk), _dt(w_uk), _ptr(q_lat), _dt(q_lat), rot_arr, sh_arr, n,
+    return (_ptr(q_nope), _dt(q_nope), _ptr(q_pe), _ptr(w_uk), _dt(w_uk), _ptr(q_lat), _lat_dt(q_lat), rot_arr, sh_arr, n,
             rot_dt, _ptr(pos), n_tok, n_heads, d_nope, d_rope, d_c, float(base), stream)
 
 
@@ -114,10 +129,15 @@ def prepare_q_qknorm(q_nope: torch.Tensor, g_q: torch.Tensor, g_k: torch.Tensor,
 
 def prepare_q(q_nope: torch.Tensor, q_pe: torch.Tensor, w_uk: torch.Tensor, pos: torch.Tensor,
               shifts: Sequence[Optional[torch.Tensor]], base: float = 10000.0,
-              lat_dtype: Optional[torch.dtype] = None, rot_dtype: Optional[torch.dtype] = None):
-    """mla_prepare_q: (q_lat, [q_rot per shift]) in one launch."""
+              lat_dtype: Optional[torch.dtype] = None, rot_dtype: Optional[torch.dtype] = None,
+              split: bool = False):
+    """mla_prepare_q: (q_lat, [q_rot per shift]) in one launch.  split: q_lat
+    as bf16 hi and lo planes [n_tok, n_heads, 2, d_c] (MLA_BF16X2)."""
     n_tok, n_heads, _ = q_nope.shape
-    q_lat = torch.empty((n_tok, n_heads, w_uk.shape[2]), dtype=lat_dtype or q_nope.dtype, device=q_nope.device)
+    if split:
+        q_lat = split_query(n_tok, n_heads, w_uk.shape[2], q_nope.device)
+    else:
+        q_lat = torch.empty((n_tok, n_heads, w_uk.shape[2]), dtype=lat_dtype or q_nope.dtype, device=q_nope.device)
     q_rots = [torch.empty_like(q_pe, dtype=rot_dtype or q_pe.dtype) for _ in shifts]
     _lib.call("mla_prepare_q", *prepare_args(q_nope, q_pe, w_uk, q_lat, q_rots, shifts, pos, base, _stream()))
     return q_lat, q_rots
@@ -299,16 +319,21 @@ class Segment:
 
 def decode_splitkv(segments: Sequence[Segment], q_lat: torch.Tensor, batch: int, s_q: int, scale: float,
                    o_part: torch.Tensor, lse_part: torch.Tensor, n_wg: int = 0) -> None:
-    """o_part [n_tok, H, n_part, d_c] (fp32 or bf16) and lse_part [n_tok, H, n_part] are written."""
-    n_tok, n_heads, d_c = q_lat.shape
+    """o_part [n_tok, H, n_part, d_c] (fp32 or bf16) and lse_part [n_tok, H, n_part] are written.
+    q_lat: [n_tok, H, d_c], or a split query [n_tok, H, 2, d_c] (then q_rot is fp32)."""
+    split = is_split_query(q_lat)
+    n_tok, n_heads = q_lat.shape[:2]
+    d_c = q_lat.shape[-1]
     d_rope = segments[0].q_rot.shape[2]
     n_part = o_part.shape[2]
     cache_dt = _cache_dt(segments[0].cache, segments[0].row_scale)
+    rot_dt = torch.float32 if split else q_lat.dtype
     for s in segments:
-        if _cache_dt(s.cache, s.row_scale) != cache_dt or s.q_rot.dtype != q_lat.dtype:
-            raise ValueError("segments must share the cache dtype; q_rot must have q_lat's dtype")
+        if _cache_dt(s.cache, s.row_scale) != cache_dt or s.q_rot.dtype != rot_dt:
+            raise ValueError("segments must share the cache dtype; q_rot must have q_lat's dtype (fp32 beside a "
+                             "split query)")
     arr = (MlaSegment * len(segments))(*[s.to_c() for s in segments])
-    _lib.call("mla_decode_splitkv", arr, len(segments), _ptr(q_lat), _dt(q_lat), cache_dt, batch, s_q, n_heads,
+    _lib.call("mla_decode_splitkv", arr, len(segments), _ptr(q_lat), _lat_dt(q_lat), cache_dt, batch, s_q, n_heads,
               d_c, d_rope, float(scale), _ptr(o_part), _dt(o_part), _ptr(lse_part), n_part, n_wg, _stream())
 
 

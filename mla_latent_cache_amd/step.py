@@ -58,7 +58,8 @@ class DecodeStep:
     def __init__(self, q_nope, q_pe, q_pos, w_uk, w_uv, segments: List[StepSegment], batch: int, s_q: int,
                  scale: float, rope_base: float = 10000.0, n_wg: int = 0,
                  n_split: Optional[Sequence[int]] = None, fuse_post: Optional[bool] = None,
-                 qk_norm: Optional[tuple] = None, quant: Optional[str] = None):
+                 qk_norm: Optional[tuple] = None, quant: Optional[str] = None,
+                 split_query: Optional[bool] = None):
         self.q_nope, self.q_pe, self.q_pos = q_nope, q_pe, q_pos
         self.w_uk, self.w_uv = w_uk, w_uv
         self.batch, self.s_q, self.scale, self.rope_base, self.n_wg = batch, s_q, scale, rope_base, n_wg
@@ -139,7 +140,21 @@ class DecodeStep:
                         row_scale=scales[i])
             for i, s in enumerate(segments)
         ]
-        self.q_lat = torch.empty((n_tok, H, d_c), dtype=q_dt, device=dev)
+        # The row-owning kernel reads the latent query as bf16 hi and lo
+        # planes written by the fused query kernel (half the bytes per read
+        # of an fp32 query): on that kernel's calls (several segments, more
+        # than 32 query rows, an int4 cache) without QK-Norm, where the fused
+        # kernel has its MFMA shape.
+        rows = max(s_q * s.head_count for s in segments)
+        rows_kernel = quant == "int4" or (quant is None and (len(segments) > 1 or rows > 32))
+        mfma_shape = w_uk.dtype == torch.bfloat16 and w_uk.shape[1] == 128 and d_c == 512
+        can_split = (self.bf16 and rows_kernel and mfma_shape and qk_norm is None and len(self.q_rots) <= 8
+                     and q_nope.data_ptr() % 16 == 0 and w_uk.data_ptr() % 16 == 0)
+        if split_query and not can_split:
+            raise ValueError("a split query needs the row-owning kernel's calls and the fused query kernel")
+        self.q_split = can_split if split_query is None else bool(split_query)
+        self.q_lat = (ops.split_query(n_tok, H, d_c, dev) if self.q_split
+                      else torch.empty((n_tok, H, d_c), dtype=q_dt, device=dev))
         # partial outputs in bf16 beside a bf16 cache (half the bytes written
         # and merged), fp32 on the fp32 path
         part_dt = torch.float32 if segments[0].cache.dtype == torch.float32 else torch.bfloat16
@@ -282,7 +297,8 @@ class DecodeStep:
                 pre.append((lib.mla_absorb_q, (self.q_nope.data_ptr(), self.w_uk.data_ptr(), dt(self.q_nope),
                                                self.q_lat.data_ptr(), dt(self.q_lat), n_tok, H, d_nope, d_c, st)))
         self._seg_arr = (_lib.MlaSegment * len(self.segments))(*[sg.to_c() for sg in self.segments])
-        dec = [(lib.mla_decode_splitkv, (self._seg_arr, len(self.segments), self.q_lat.data_ptr(), dt(self.q_lat),
+        dec = [(lib.mla_decode_splitkv, (self._seg_arr, len(self.segments), self.q_lat.data_ptr(),
+                                         ops._lat_dt(self.q_lat),
                                          ops._cache_dt(self.segments[0].cache, self.segments[0].row_scale),
                                          self.batch, self.s_q, H, d_c, d_r,
                                          float(self.scale), self.o_part.data_ptr(), dt(self.o_part),
@@ -312,7 +328,8 @@ def run_calls(calls) -> None:
             raise _lib.MlaError(fn.__name__, st, _lib.load().mla_last_error().decode())
 
 
-def step_from_inputs(x, device="cuda", n_wg: int = 0, n_split=None, fuse_post=None) -> DecodeStep:
+def step_from_inputs(x, device="cuda", n_wg: int = 0, n_split=None, fuse_post=None,
+                     split_query=None) -> DecodeStep:
     """Upload a seeded input set (``mla_inputs.MlaInputs``) and build its step."""
     d = torch.device(device)
     segs = []
@@ -328,4 +345,5 @@ def step_from_inputs(x, device="cuda", n_wg: int = 0, n_split=None, fuse_post=No
         qk = (x.g_q.to(d), x.g_k.to(d), x.spec.qk_eps)
     return DecodeStep(x.q_nope.to(d), x.q_pe.to(d), x.q_pos.to(d), x.w_uk.to(d), x.w_uv.to(d), segs,
                       x.spec.batch, x.spec.s_q, x.scale, x.rope_base, n_wg=n_wg, n_split=n_split,
-                      fuse_post=fuse_post, qk_norm=qk, quant=getattr(x.spec, "quant", None))
+                      fuse_post=fuse_post, qk_norm=qk, quant=getattr(x.spec, "quant", None),
+                      split_query=split_query)

@@ -133,6 +133,11 @@ def test_null_and_shape_errors_before_any_gpu_call(lib):
     assert _st(lib, "mla_prepare_q", P, 0, P, P + 8, 1, P, 0, None, None, 0, 0, P, 1, 4, 128, 64, 512, 1e4,
                None) == 5
     assert _st(lib, "mla_prepare_q", P, 4, P, P, 1, P, 0, None, None, 0, 0, P, 1, 4, 128, 64, 512, 1e4, None) == 3
+    # a split q_lat (lat_dtype 4) only on the MFMA path (bf16 weights, 128 x 512, aligned)
+    assert _st(lib, "mla_prepare_q", P, 0, P, P, 0, P, 4, None, None, 0, 0, P, 1, 4, 128, 64, 512, 1e4, None) == 5
+    assert _st(lib, "mla_prepare_q", P, 1, P, P + 8, 1, P, 4, None, None, 0, 0, P, 1, 4, 128, 64, 512, 1e4,
+               None) == 5
+    assert _st(lib, "mla_prepare_q", P, 1, P, P, 1, P, 5, None, None, 0, 0, P, 1, 4, 128, 64, 512, 1e4, None) == 3
     # mla_prepare_q_qknorm(q_nope, q_dtype, g_q, g_k, eps, q_pe, w_uk, in_dtype, q_lat, lat_dtype, q_rots,
     #                      shifts, n_shift, rot_dtype, pos, n_tok, n_heads, d_nope, d_rope, d_c, base, stream)
     qk = lambda q_dt, gq, eps, in_dt, n_tok, H, d_nope: _st(  # noqa: E731
@@ -208,6 +213,11 @@ def test_null_and_shape_errors_before_any_gpu_call(lib):
     assert dec([seg(row_scale=P)], dtype=3, q_dtype=1) == 5
     assert dec([seg(row_scale=P, row_rinv=P)], dtype=3) == 5
     assert dec([seg(row_scale=P)], dtype=4) == 3
+    # split query (q_dtype 4, bf16 hi and lo planes): bf16 or int4 cache, no QK-Norm
+    assert dec([seg()], dtype=0, q_dtype=4) == 5
+    assert dec([seg(row_scale=P)], dtype=2, q_dtype=4) == 5
+    assert dec([seg(row_rinv=P)], q_dtype=4) == 5
+    assert dec([seg()], q_dtype=5) == 3
 
 
 def test_size_limits_refused(lib):

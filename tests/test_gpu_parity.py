@@ -47,6 +47,19 @@ def test_chain_mini(name):
     print(f"[parity] {name}: {errs}", flush=True)
 
 
+@pytest.mark.parametrize("name", ["dsv3", "long", "merge", "prefill", "int4"])
+@pytest.mark.parametrize("split_query", [True, False])
+def test_chain_mini_query_format(name, split_query):
+    """The row-owning kernel's two query formats: bf16 hi and lo planes
+    written by the fused query kernel (what the step picks for these
+    workloads), and the fp32 query split inside the decode."""
+    x = M.make(name, SEEDS[name] + 40, mini=True, poison=True)
+    print(f"[parity] mini {name} split_query={split_query}", flush=True)
+    st, out, o_lat, lse = _run(x, split_query=split_query)
+    assert st.q_split == split_query
+    check_step(x, out, o_lat, lse, label=f"{name} split_query={split_query}")
+
+
 @pytest.mark.parametrize("n_wg", [1, 3, 8, 64, 256])
 def test_split_invariance_dsv3_mini(n_wg):
     x = M.make("dsv3", 7, mini=True, poison=True)
@@ -352,6 +365,29 @@ def test_prepare_fp32_query_bf16_weights():
     assert np.max(np.abs(ref_hi - ref)) > 50 * np.max(err)
     ref_r = O.rope_relocate(f64(q_pe), pos.numpy(), np.zeros(n_tok, np.int64), 10000.0)
     assert np.abs(f64(q_rots[0]) - ref_r).max() <= 1e-5
+
+
+@pytest.mark.parametrize("q_dtype", [torch.bfloat16, torch.float32])
+def test_prepare_split_query(q_dtype):
+    """mla_prepare_q with lat_dtype MLA_BF16X2: its two planes are exactly
+    the bf16 rounding of the fp32 result and the bf16 rounding of what that
+    leaves (the same MFMA sums, only stored differently)."""
+    from mla_latent_cache_amd import ops
+    H, d_nope, d_c, d_r, n_tok = 16, 128, 512, 64, 37
+    q = (_rand((n_tok, H, d_nope), torch.float32, 41) * 3).to(q_dtype)
+    q_pe = _rand((n_tok, H, d_r), torch.bfloat16, 42)
+    w = (_rand((H, d_nope, d_c), torch.float32, 43) / math.sqrt(d_c)).to(torch.bfloat16)
+    pos = torch.arange(n_tok, dtype=torch.int64) * 31
+    dq, dpe, dw, dpos = q.cuda(), q_pe.cuda(), w.cuda(), pos.cuda()
+    q32, r32 = ops.prepare_q(dq, dpe, dw, dpos, [None], 10000.0, lat_dtype=torch.float32, rot_dtype=torch.float32)
+    qx2, rx2 = ops.prepare_q(dq, dpe, dw, dpos, [None], 10000.0, rot_dtype=torch.float32, split=True)
+    torch.cuda.synchronize()
+    assert qx2.shape == (n_tok, H, 2, d_c) and qx2.dtype == torch.bfloat16
+    hi = q32.to(torch.bfloat16)
+    lo = (q32 - hi.float()).to(torch.bfloat16)
+    assert torch.equal(qx2[:, :, 0], hi)
+    assert torch.equal(qx2[:, :, 1], lo)
+    assert torch.equal(rx2[0], r32[0])
 
 
 @pytest.mark.parametrize("q_dtype,n_tok,H", [(torch.bfloat16, 1, 16), (torch.float32, 17, 16),
