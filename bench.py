@@ -208,7 +208,8 @@ def main():
     # Cache copies: enough that the rotated set exceeds twice the 256 MiB
     # Infinity Cache, so every step streams its cache from HBM.
     nbytes, flops = algorithmic(x)
-    n_copies = max(1, math.ceil(2 * MALL_BYTES / max(1, nbytes)))
+    # (at most 64 copies: a cache of a few KiB, the toy, stays cached anyway)
+    n_copies = min(64, max(1, math.ceil(2 * MALL_BYTES / max(1, nbytes))))
     fuse = False if args.no_fuse_post else None
     base = step_from_inputs(x, n_wg=args.n_wg, fuse_post=fuse)
     step_fused = base.fuse_post
