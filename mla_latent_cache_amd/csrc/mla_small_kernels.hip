@@ -258,9 +258,86 @@ __global__ __launch_bounds__(256) void combine_kernel(const TP* __restrict__ o_p
   }
 }
 
+// The same merge for many rows of 512 columns: one wave per row (four rows
+// per 256-thread block), lane l owning columns 8 l .. 8 l + 7, so a live
+// slot is one 16-byte load per lane (bf16 partials) and no block-wide
+// synchronisation is needed.  The wave walks the live slots in slot order,
+// four loads in flight, so the sum is bitwise repeatable.
+template <typename TO, typename TP>
+__global__ __launch_bounds__(256) void combine_rows_kernel(const TP* __restrict__ o_part,
+                                                           const float* __restrict__ lse_part, int n_rows,
+                                                           int n_part, TO* __restrict__ o_lat,
+                                                           float* __restrict__ lse) {
+  constexpr int kD = 512;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n_rows) return;
+  const float* lp = lse_part + (int64_t)row * n_part;
+  float m = -INFINITY;
+  for (int j = lane; j < n_part; j += 64) m = fmaxf(m, lp[j]);
+  m = wave_max(m);
+  const TP* op = o_part + (int64_t)row * n_part * kD + 8 * lane;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto load8 = [&](int j, float (&v)[8]) {
+    const TP* p = op + (int64_t)j * kD;
+    const f32x4 a = load_part4(p), b = load_part4(p + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = a[e];
+      v[4 + e] = b[e];
+    }
+  };
+  float tot = 0.f;
+  for (int base = 0; base < n_part; base += 64) {
+    const int j = base + lane;
+    const float l = j < n_part ? lp[j] : -INFINITY;
+    const bool live = l != -INFINITY;
+    const float w = live ? expf(l - m) : 0.f;
+    tot += w;
+    uint64_t bal = __ballot(live);
+    while (bal) {
+      int src[4];
+      int k = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        src[u] = bal ? __ffsll((long long)bal) - 1 : -1;
+        if (bal) {
+          bal &= bal - 1;
+          ++k;
+        }
+      }
+      float v[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (u < k) load8(base + src[u], v[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (u < k) {
+          const float wu = __shfl(w, src[u]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] += wu * v[u][e];
+        }
+    }
+  }
+  tot = wave_sum(tot);
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;  // tot > 0 exactly when a slot is live
+  if (lse && lane == 0) lse[row] = tot > 0.f ? m + logf(tot) : -INFINITY;
+  TO* orow = o_lat + (int64_t)row * kD + 8 * lane;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) store_f(orow + e, acc[e] * inv);
+}
+
 template <typename TP>
 static hipError_t combine_launch(const TP* o_part, const float* lse_part, int n_rows, int n_part, int d_c,
                                  void* o_lat, bool out_bf16, float* lse, hipStream_t stream) {
+  if (d_c == 512 && n_rows >= 1024) {  // many whole rows: a wave per row
+    const dim3 grid((n_rows + 3) / 4);
+    if (out_bf16)
+      return launch(combine_rows_kernel<bf16, TP>, grid, dim3(256), stream, o_part, lse_part, n_rows, n_part,
+                    (bf16*)o_lat, lse);
+    return launch(combine_rows_kernel<float, TP>, grid, dim3(256), stream, o_part, lse_part, n_rows, n_part,
+                  (float*)o_lat, lse);
+  }
   // chunk width: ~1024 blocks in flight for few rows, whole 512-column rows for many
   const int cols = n_rows >= 1024 ? 512 : n_rows >= 512 ? 256 : 128;
   const dim3 grid(n_rows, (d_c + cols - 1) / cols);

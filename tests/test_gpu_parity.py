@@ -426,6 +426,8 @@ def test_prepare_qknorm_call(q_dtype, n_tok, H):
 
 @pytest.mark.parametrize("out_dtype,n_rows,n_part", [(torch.float32, 37, 5), (torch.bfloat16, 37, 5),
                                                      (torch.float32, 600, 5), (torch.float32, 1100, 5),
+                                                     (torch.bfloat16, 1030, 9),     # a wave per row from 1024 rows
+                                                     (torch.float32, 1024, 130),    # ... over three slot chunks
                                                      (torch.bfloat16, 9, 300),      # slots beyond 128
                                                      (torch.float32, 7, 1024)])     # the largest slot count
 @pytest.mark.parametrize("part_dtype", [torch.float32, torch.bfloat16])
