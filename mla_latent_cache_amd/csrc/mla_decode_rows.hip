@@ -920,7 +920,6 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
       char* const qrot_w = sm.qrot[16 * RB * wave];  // this wave's rows
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        if (!wave_rows) break;
         const RowInfo ri = row_info(rb);
         const int64_t qi = (int64_t)b * s_q * n_heads + ri.qoff;
         const float* qr = q_rot + qi * kDr + 8 * lg;
@@ -932,7 +931,11 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
         // registers die before the next batch.  The rotary part, and the
         // latent part of an fp32 query, are split here (a row past the group
         // gets zeros); a split query's hi plane is used as it is (a row past
-        // the group keeps row0's: its results are never stored).
+        // the group keeps row0's: its results are never stored).  A wave
+        // without rows loads them too: with the loads skipped on its path the
+        // registers were undefined there, and the compiler carried the last
+        // piece's query across the epilogue instead (48 VGPRs written to
+        // scratch and read back in every piece at 128-row groups).
         constexpr int kBatch = kKSteps / 2;
 #pragma unroll
         for (int k0 = 0; k0 < kKSteps; k0 += kBatch) {
