@@ -197,10 +197,21 @@ __device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, int bytes) {
   return i32x4_t{(int)(uint32_t)a, (int)(uint32_t)(a >> 32) & 0xffff, bytes, 0x00020000};
 }
 
+// Latent rows in LDS: the 16-byte chunk c (0..63) of tile row r sits at
+// position c ^ lkey(r), lkey(r) = 2 (r & 7) (rotary rows keep rpos).  The LDS
+// serves a ds_read_b128 16 lanes per cycle (lanes 32 h + 4 q .. 32 h + 4 q + 3
+// for the four quads q of equal bit parity) and a ds_read_b64, the transposed
+// form too, 32 consecutive lanes per cycle, over 64 banks of 4 bytes (bank
+// conflict counters of single lane pairs and of whole patterns).  With this
+// key both operand reads below reach 64 distinct banks per cycle; the key
+// r & 15 left every transposed read two-way conflicted.
+__device__ __forceinline__ int lkey(int r) { return (r & 7) << 1; }
+__device__ __forceinline__ int lpos(int r, int c) { return c ^ lkey(r); }
+
 // Load i (< kDmaPerWave) of wave w's share of one tile, from the rows that
 // `rsrc` covers (rows past its record count read as zeros).  Wave w fills
 // latent rows k = w + 4 i (i < 8; lane l moves the chunk stored at position
-// l, i.e. chunk l ^ (k & 15)) and, as its last load, rotary rows 8 w + l / 8
+// l, i.e. chunk lpos(k, l)) and, as its last load, rotary rows 8 w + l / 8
 // (lane l: position l % 8, chunk (l % 8) ^ ((r >> 1) & 7)).
 __device__ __forceinline__ void tile_load(i32x4_t rsrc, char* lat, char* rot, int w, int lane, int i) {
   // opaque lane copy: the offsets are recomputed per instruction instead of
@@ -208,7 +219,7 @@ __device__ __forceinline__ void tile_load(i32x4_t rsrc, char* lat, char* rot, in
   asm volatile("" : "+v"(lane));
   if (i < kTile / kRowsWaves) {
     const int k = w + kRowsWaves * i;
-    dma16(rsrc, lat + k * kCBytes, k * kRowBytes + (cpos(k, lane) << 4));
+    dma16(rsrc, lat + k * kCBytes, k * kRowBytes + (lpos(k, lane) << 4));
   } else {
     const int r = 8 * w + (lane >> 3);
     dma16(rsrc, rot + w * 1024, r * kRowBytes + kCBytes + (rpos(r, lane & 7) << 4));
@@ -278,7 +289,7 @@ __device__ __forceinline__ void unpack_tile_i4(const char* __restrict__ land, ch
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = 8 * w + i;
-    *(bf16x8*)(lat + r * kCBytes + (cpos(r, lane) << 4)) = unpack8_i4(wd[i]);
+    *(bf16x8*)(lat + r * kCBytes + (lpos(r, lane) << 4)) = unpack8_i4(wd[i]);
   }
   *(bf16x8*)(rot + rr * kRBytes + (rpos(rr, j) << 4)) = unpack8_i4(wd[8]);
   scl[lane] = sv;
@@ -314,9 +325,9 @@ __device__ __forceinline__ void scores_ready(f32x4 (&s)[2][RB], f32x4 (&sr)[2][R
 // the direct-to-LDS loads in flight to other stages).  Per-lane LDS address
 // parts, from an opaque copy of the lane index (so none is held across the
 // loop): K operand of latent k-step ks = 4 a + n, rows 16 tb + l16, chunk
-// 4 ks + lg, sits at position (4 ks + lg) ^ l16 = 16 a + 4 (n ^ (l16 >> 2)) +
-// (lg ^ (l16 & 3)); rotary k-step jr: chunk 4 jr + lg at (4 jr + lg) ^
-// ((l16 >> 1) & 7).  Rows 16 + l16 share the swizzle key of row l16.
+// 4 ks + lg, sits at position (4 ks + lg) ^ lkey(l16) = 16 a + 4 (n ^ (lkey
+// >> 2)) + (lg ^ (lkey & 3)); rotary k-step jr: chunk 4 jr + lg at (4 jr +
+// lg) ^ ((l16 >> 1) & 7).  Rows 16 + l16 share the swizzle key of row l16.
 // The rotary k-steps accumulate into sr (the same array as s, except for int4
 // rows, whose two parts take different scales).
 template <int RB>
@@ -327,7 +338,7 @@ __device__ __forceinline__ void qk_tile(const char* __restrict__ ls, const char*
   const int xl = lane & 15, xg = lane >> 4;
   const char* kb[4];
 #pragma unroll
-  for (int n = 0; n < 4; ++n) kb[n] = ls + xl * kCBytes + ((n ^ (xl >> 2)) << 6) + ((xg ^ (xl & 3)) << 4);
+  for (int n = 0; n < 4; ++n) kb[n] = ls + xl * kCBytes + ((n ^ (lkey(xl) >> 2)) << 6) + ((xg ^ (lkey(xl) & 3)) << 4);
   const char* rb0 = rs + xl * kRBytes;
   const int xr = (xl >> 1) & 7;
   const bool split_rot = &sr[0][0] != &s[0][0];  // int4 rows: the rotary part apart
@@ -399,8 +410,9 @@ __device__ __forceinline__ void qk_tile(const char* __restrict__ ls, const char*
 // registers; the C^T operand of column block db is read to match: the first
 // transposed read of lane (lg, rq, qq) addresses tile row x = 4 lg + rq, the
 // second row x + 16 (same swizzle key), columns 16 db + 4 qq .. + 3, i.e.
-// chunk 2 db + (qq >> 1) at position 2 (db ^ (x >> 1)) + ((qq >> 1) ^ (x & 1)),
-// byte 8 (qq & 1) within it; each 16-lane group then holds C[rows][16 db + l16].
+// chunk 2 db + (qq >> 1) at position 2 ((db & 7) ^ (lkey(x) >> 1)) + ((qq >> 1) ^
+// (lkey(x) & 1)) (plus 16 (db >> 3)), byte 8 (qq & 1) within it; each 16-lane
+// group then holds C[rows][16 db + l16].
 // `load(i)` issues load i of the next tile's share after the MFMAs of column
 // block kPvLoadAt[i]; `mid(db)` runs after those of block db (the next tile's
 // softmax, in stages).  Each block's instructions stay in program order (a
@@ -413,8 +425,8 @@ __device__ __forceinline__ void pv_tile(const char* __restrict__ ls, int lane, c
   asm volatile("" : "+v"(lane));
   const int qq = lane & 3, rq = (lane >> 2) & 3, xg = lane >> 4;
   const int xr = 4 * xg + rq;
-  const char* cb = ls + xr * kCBytes + 8 * (qq & 1) + 16 * ((qq >> 1) ^ (xr & 1));
-  const int xh = xr >> 1;
+  const char* cb = ls + xr * kCBytes + 8 * (qq & 1) + 16 * ((qq >> 1) ^ (lkey(xr) & 1));
+  const int xh = lkey(xr) >> 1;
   auto cop = [&](int db) -> bf16x8 {
     const char* pa = cb + 256 * (db >> 3) + (((db & 7) ^ xh) << 5);
     const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(pa));
