@@ -1128,40 +1128,50 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
       if (wave_rows) {
         float lt[RB], cs[RB];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          lt[rb] = rows_sum(l_part[rb]);
-          // sum_d lo_d acc_d over this lane's columns 16 db + 4 lg + e; the
-          // 32 query loads go out together (a row past the group reads
-          // row0's query), then the products
-          const RowInfo ri = row_info(rb);
-          const int64_t qi = (int64_t)b * s_q * n_heads + ri.qoff;
-          float c = 0.f;
-          if constexpr (QS) {
-            // the lo plane as it is: this lane's 4 columns of each block are
-            // half of a 16-byte load that the lane of the neighbouring lane
-            // group shares (8-byte loads here make the compiler spill the
-            // query's hi parts inside the tile loop)
-            const float* qll = (const float*)((const bf16*)q_lat + qi * (2 * kDc) + kDc + 8 * (lg >> 1));
-            const bool odd = lg & 1;
-            f32x4 qv[32];
+        for (int rb = 0; rb < RB; ++rb) lt[rb] = rows_sum(l_part[rb]);
+        // sum_d lo_d acc_d over this lane's columns 16 db + 4 lg + e, per row
+        // block; every query load goes out before the first product (a row
+        // past the group reads row0's query)
+        if constexpr (QS) {
+          // the lo plane as it is: this lane's 4 columns of a block are 8
+          // bytes; the loads of every row block go out together (the hi
+          // parts are dead here, so their registers take them)
+          uint32_t qv[RB][32][2];
 #pragma unroll
-            for (int db = 0; db < 32; ++db) qv[db] = *(const f32x4*)(qll + 8 * db);
-            __builtin_amdgcn_sched_barrier(0);
+          for (int rb = 0; rb < RB; ++rb) {
+            const int64_t qi = (int64_t)b * s_q * n_heads + row_info(rb).qoff;
+            const char* qll = (const char*)((const bf16*)q_lat + qi * (2 * kDc) + kDc) + 8 * lg;
 #pragma unroll
             for (int db = 0; db < 32; ++db) {
-              const uint32_t w0 = __float_as_uint(odd ? qv[db][2] : qv[db][0]);
-              const uint32_t w1 = __float_as_uint(odd ? qv[db][3] : qv[db][1]);
+              const auto w = *(const uint2*)(qll + 32 * db);
+              qv[rb][db][0] = w.x;
+              qv[rb][db][1] = w.y;
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            float c = 0.f;
+#pragma unroll
+            for (int db = 0; db < 32; ++db) {
+              const uint32_t w0 = qv[rb][db][0], w1 = qv[rb][db][1];
               c += __uint_as_float(w0 << 16) * acc[db][rb][0];
               c += __uint_as_float(w0 & 0xffff0000u) * acc[db][rb][1];
               c += __uint_as_float(w1 << 16) * acc[db][rb][2];
               c += __uint_as_float(w1 & 0xffff0000u) * acc[db][rb][3];
             }
-          } else {
+            cs[rb] = rows_sum(c) * sl2;
+          }
+        } else {
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            const int64_t qi = (int64_t)b * s_q * n_heads + row_info(rb).qoff;
             const float* ql = q_lat + qi * kDc + 4 * lg;
             f32x4 qv[32];
 #pragma unroll
             for (int db = 0; db < 32; ++db) qv[db] = *(const f32x4*)(ql + 16 * db);
             __builtin_amdgcn_sched_barrier(0);
+            float c = 0.f;
 #pragma unroll
             for (int db = 0; db < 32; ++db)
 #pragma unroll
@@ -1169,8 +1179,8 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
                 const float x = qv[db][e];  // the lo part as the prologue split it
                 c += (float)(bf16)(x - (float)(bf16)x) * acc[db][rb][e];
               }
+            cs[rb] = rows_sum(c) * sl2;
           }
-          cs[rb] = rows_sum(c) * sl2;
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
