@@ -104,15 +104,18 @@ constexpr int kDmaPerWave = kTileDma / kRowsWaves;     // 9
 static_assert(kTileDma % kRowsWaves == 0, "every wave issues the same share of a tile's loads");
 constexpr int kRowsMaxPieces = 64;
 // Cost of a piece beyond its tiles, in tiles: its prologue reads the query
-// of the group's rows (fp32 latent and rotary parts), its epilogue reads the
-// latent part again and writes the partial output, all at the CU's share of
-// HBM bandwidth like the cache tiles (measured: about 19 tiles at 128-row
-// groups, as the bytes predict).  The work split counts this many extra
-// tiles at the start of every request, so a workgroup whose range crosses a
-// request boundary (two pieces) takes correspondingly fewer rows.
-__host__ __device__ constexpr int piece_tiles(int mt, bool part_bf16) {
-  return (mt * ((kDc + kDr) * 4 + kDc * 4 + kDc * (part_bf16 ? 2 : 4)) + kTile * kRowBytes / 2) /
-         (kTile * kRowBytes);
+// of the group's rows (fp32 latent and rotary parts, or a split query's hi
+// plane and the fp32 rotary part), its epilogue reads the latent part again
+// (the split query's lo plane) and writes the partial output, all at the
+// CU's share of HBM bandwidth like the cache tiles (measured at 128-row
+// groups: about 19 tiles with an fp32 query, as the bytes predict; 13.6 +
+// 17.4 us against 2.2 us per tile, about 14, with a split query, whose bytes
+// give 12).  The work split counts this many extra tiles at the start of
+// every request, so a workgroup whose range crosses a request boundary (two
+// pieces) takes correspondingly fewer rows.
+__host__ __device__ constexpr int piece_tiles(int mt, bool part_bf16, bool q_split) {
+  const int q_bytes = q_split ? kDc * 2 + kDr * 4 + kDc * 2 : (kDc + kDr) * 4 + kDc * 4;
+  return (mt * (q_bytes + kDc * (part_bf16 ? 2 : 4)) + kTile * kRowBytes / 2) / (kTile * kRowBytes);
 }
 // Operand reads in flight ahead of their MFMAs (deeper with 16 rows per wave,
 // which has registers to spare and fewer MFMAs per read to cover latency)
@@ -635,7 +638,7 @@ __device__ __forceinline__ T& pick(T& a, T& b) {
 template <int RB, bool I4, bool PB, bool QS>
 __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch L) {
   constexpr int MT = 16 * RB * kRowsWaves;  // query rows of a row group
-  constexpr int kOv = piece_tiles(MT, PB) * kTile;  // a request's start, in rows of the work split
+  constexpr int kOv = piece_tiles(MT, PB, QS) * kTile;  // a request's start, in rows of the work split
   using SM = RowsSmem<I4>;
   constexpr int NLAT = SM::NLAT;
   constexpr int RBYTES = I4 ? kI4Row : kRowBytes;  // bytes per stored row
@@ -1245,7 +1248,7 @@ SegCost seg_cost(const DecodeArgs& a, const SegArgs& s, int mt) {
   const int busy = (std::min(rows, mt) + rpw - 1) / rpw;  // waves with rows in the fullest group
   c.t_tile = (mt == 64 ? 3400.0 + 125.0 * busy : 4000.0 + 250.0 * busy);
   c.tiles = std::max(1.0, (double)a.batch * (double)std::max<int64_t>(cap, 1) / kTile);
-  c.piece = piece_tiles(mt, a.part_bf16 != 0);
+  c.piece = piece_tiles(mt, a.part_bf16 != 0, a.q_split != 0);
   c.batch = a.batch;
   return c;
 }
