@@ -79,12 +79,13 @@ def decode_kernel_name(x) -> str:
     rows = [sp.s_q * (s.head_count or sp.heads) for s in x.segments]
     if sp.dtype != "bf16":
         return "decode_f32_kernel"
-    if sp.quant == "int4":
-        return "decode_rows_kernel<1, true, true> (int4 rows, 64-row groups)"
-    if sp.quant == "int8" or sp.qk_norm or (len(rows) == 1 and rows[0] <= 32):
+    if sp.quant in ("int4", "int8"):
+        qm = 1 if sp.quant == "int4" else 2
+        return f"decode_rows_kernel<1, {qm}, true> ({sp.quant} rows, 64-row groups)"
+    if sp.qk_norm or (len(rows) == 1 and rows[0] <= 32):
         return "decode_bf16_kernel"
     rb = 1 if max(rows) <= 64 else 2
-    return f"decode_rows_kernel<{rb}, false, true> ({64 * rb}-row groups)"
+    return f"decode_rows_kernel<{rb}, 0, true> ({64 * rb}-row groups)"
 
 
 def kernel_hash() -> str:

@@ -182,7 +182,7 @@ typedef struct {
  *          mla_prepare_q; each segment's q_rot has q_dtype too (fp32 for
  *          MLA_BF16X2).  MLA_BF16X2: [n_tok][n_heads][2][d_c] bf16 hi and lo
  *          planes (mla_prepare_q with lat_dtype MLA_BF16X2), for a bf16 cache
- *          (not QK-Norm) or an int4 one; always the row-owning kernel; the
+ *          (not QK-Norm) or a low-bit one; always the row-owning kernel; the
  *          same arithmetic as an fp32 query (which is split into exactly
  *          these parts inside the kernel).
  * caches   cache_dtype.  MLA_BF16 caches take an fp32 query or a bf16 one.
@@ -192,11 +192,13 @@ typedef struct {
  *          the lse to first order (scale * lo . o_part; lse error second
  *          order, ~1e-5 at unit-variance inputs).  MLA_F32 caches take an
  *          fp32 query.  MLA_I8 caches (QuantMLA abstract: a low-bit latent
- *          cache dequantized inside attention) take an fp32 query and every
- *          segment's row_scale: the latent score of row t is scale_t times
- *          q_lat . code_t and its softmax weight multiplies scale_t code_t,
- *          exactly the attention over the dequantized rows; not combined
- *          with QK-Norm.  MLA_I4 caches (the abstract's joint INT4
+ *          cache dequantized inside attention) take an fp32 or split query
+ *          and every segment's row_scale: the latent score of row t is
+ *          scale_t times q_lat . code_t and its softmax weight multiplies
+ *          scale_t code_t, exactly the attention over the dequantized rows;
+ *          not combined with QK-Norm; they run on the row-owning kernel in
+ *          groups of 64 query rows, the codes unpacked inside the streaming
+ *          loop.  MLA_I4 caches (the abstract's joint INT4
  *          content and rotary caches) take an fp32 or split query and every
  *          segment's (latent, rotary) scale pairs: the score of row t is
  *          scale * (sc_t q_lat . code_t + sr_t q_rot . rcode_t) and its

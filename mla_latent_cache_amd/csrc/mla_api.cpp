@@ -366,8 +366,9 @@ mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q
       !(dtype_ok(cache_dtype) || cache_dtype == MLA_I8 || cache_dtype == MLA_I4) || !dtype_ok(part_dtype))
     return fail(MLA_ERR_DTYPE, "mla_decode_splitkv: dtypes %d, %d, %d", q_dtype, cache_dtype, part_dtype);
   const bool qx2 = q_dtype == MLA_BF16X2;
-  if (qx2 && cache_dtype != MLA_BF16 && cache_dtype != MLA_I4)
-    return fail(MLA_ERR_UNSUPPORTED, "mla_decode_splitkv: a split query (MLA_BF16X2) needs a bf16 or int4 cache");
+  if (qx2 && cache_dtype != MLA_BF16 && cache_dtype != MLA_I8 && cache_dtype != MLA_I4)
+    return fail(MLA_ERR_UNSUPPORTED,
+                "mla_decode_splitkv: a split query (MLA_BF16X2) needs a bf16, int8 or int4 cache");
   if (cache_dtype == MLA_F32 && q_dtype != MLA_F32)
     return fail(MLA_ERR_UNSUPPORTED, "mla_decode_splitkv: an fp32 cache needs an fp32 query");
   if (cache_dtype == MLA_F32 && part_dtype != MLA_F32)
@@ -380,9 +381,8 @@ mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q
   const bool lowbit = i8 || i4;
   const bool bf = cache_dtype == MLA_BF16 || lowbit;  // the MFMA kernels (16-bit, int8 or int4 rows)
   const bool q32 = q_dtype == MLA_F32;
-  if (i8 && !q32) return fail(MLA_ERR_UNSUPPORTED, "mla_decode_splitkv: an int8 cache needs an fp32 query");
-  if (i4 && !q32 && !qx2)
-    return fail(MLA_ERR_UNSUPPORTED, "mla_decode_splitkv: an int4 cache needs an fp32 or split query");
+  if (lowbit && !q32 && !qx2)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_decode_splitkv: a low-bit cache needs an fp32 or split query");
   if (bf) {
     if (d_c != kBf16Dc || d_rope != kBf16Dr)
       return fail(MLA_ERR_UNSUPPORTED, "mla_decode_splitkv: bf16 path needs d_c=512, d_rope=64 (got %d, %d)", d_c,
@@ -473,11 +473,12 @@ mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q
   a.d_rope = d_rope;
   a.n_part = n_part;
   a.scale = scale;
-  // several segments on the row-owning path (or an int4 cache, or a split
+  // several segments on the row-owning path (or a low-bit cache, or a split
   // query, which only that kernel reads): one launch over all of them, the
   // grid split by each segment's share of the work
-  if (i4 || qx2 || (rows_path && n_segs > 1))
-    return hip_status(mla::launch_decode_rows_multi(a, sa.data(), n_segs, wg, i4, (hipStream_t)stream),
+  if (lowbit || qx2 || (rows_path && n_segs > 1))
+    return hip_status(mla::launch_decode_rows_multi(a, sa.data(), n_segs, wg, i4 ? 1 : i8 ? 2 : 0,
+                                                    (hipStream_t)stream),
                       "mla_decode_splitkv launch");
   for (int g = 0; g < n_segs; ++g) {
     a.seg = sa[g];

@@ -146,17 +146,34 @@ constexpr int kI4Land = kI4Codes + 256 * kRowsWaves;    // + one copy of the 32 
 constexpr int kI4Dma = 4;                               // loads per wave per tile
 static_assert(kI4Codes % (kRowsWaves * 256) == 0, "a wave's share of the codes is whole dword loads");
 
-template <bool I4>
+// int8 rows (the QuantMLA abstract's low-bit latent cache in its plain form):
+// 512 bytes of latent codes and the 64 bf16 rotary entries per stored row,
+// one fp32 scale per row beside the cache.  A tile's codes (16 KiB) and
+// scales land in LDS by direct loads one tile ahead of their unpacking (two
+// landing stages: a third does not fit beside the bf16 stages), its rotary
+// entries go straight into the rotary ring like 16-bit rows; each wave then
+// unpacks 8 of its rows into the bf16 stages (the codes, exact in bf16) and
+// keeps its own copy of the tile's scales.
+constexpr int kI8Row = kDc + 2 * kDr;                   // 640 bytes per stored row
+constexpr int kI8Codes = kTile * kDc;                   // 16 KiB of codes per tile
+constexpr int kI8Land = kI8Codes + 256 * kRowsWaves;    // + one copy of the 32 scales per wave
+constexpr int kI8Dma = 6;                               // loads per wave per tile
+
+// QM: the stored rows (0: 16-bit, 1: int4, 2: int8).  Low-bit rows land
+// packed and are unpacked into three bf16 stages: tiles it (PV), it+1 (QK)
+// and it+2 (unpacked into).
+template <int QM, int RB>
 struct RowsSmem {
-  static constexpr int NLAT = I4 ? 3 : kLatStages;  // tiles it (PV), it+1 (QK), it+2 (unpacked into)
-  static constexpr int NROT = kRotStages;
+  static constexpr int NLAT = QM ? 3 : kLatStages;
+  static constexpr int NLAND = QM == 1 ? 3 : QM == 2 ? 2 : 1;
+  static constexpr int LAND = QM == 1 ? kI4Land : QM == 2 ? kI8Land : 16;
   char lat[NLAT][kCStage];   // 128 KiB (96 KiB)
-  char rot[NROT][kRStage];   // 12 KiB
-  // bf16 hi parts of the rotary query of the group's 128 rows (a wave uses
-  // only its own rows): rows of 128 B, chunks placed like the rotary ring's
-  char qrot[16 * 2 * kRowsWaves][kRBytes];  // 16 KiB
-  char land[I4 ? 3 : 1][I4 ? kI4Land : 16];                   // int4: 30 KiB landing ring
-  float scl[I4 ? 3 : 1][kRowsWaves][I4 ? 2 * kTile : 1];      // int4: each wave's scales of a stage
+  char rot[kRotStages][kRStage];   // 12 KiB
+  // bf16 hi parts of the rotary query of the group's rows (a wave uses only
+  // its own rows): rows of 128 B, chunks placed like the rotary ring's
+  char qrot[16 * RB * kRowsWaves][kRBytes];  // 16 KiB at 128-row groups
+  char land[NLAND][LAND];    // int4: 30 KiB landing ring, int8: 34 KiB
+  float scl[QM ? 3 : 1][kRowsWaves][QM == 1 ? 2 * kTile : QM == 2 ? kTile : 1];  // each wave's scales of a stage
   Piece pieces[kRowsMaxPieces];
   int n_pieces;
   int done;
@@ -296,6 +313,56 @@ __device__ __forceinline__ void unpack_tile_i4(const char* __restrict__ land, ch
   }
   *(bf16x8*)(rot + rr * kRBytes + (rpos(rr, j) << 4)) = unpack8_i4(wd[8]);
   scl[lane] = sv;
+}
+
+// Wave w's kI8Dma loads of an int8 tile: the codes of rows 8 w .. 8 w + 7 (two
+// rows per load, into the landing stage row by row), their rotary entries
+// (into the rotary ring, placed as for 16-bit rows) and the tile's 32 scales
+// (into the wave's own copy; lanes past the record count read zeros).
+__device__ __forceinline__ void tile_load_i8(i32x4_t rows, i32x4_t scales, char* land, char* rot, int w,
+                                             int lane) {
+  asm volatile("" : "+v"(lane));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 8 * w + 2 * j + (lane >> 5);
+    dma16(rows, land + (8 * w + 2 * j) * kDc, r * kI8Row + 16 * (lane & 31));
+  }
+  const int r = 8 * w + (lane >> 3);
+  dma16(rows, rot + w * 1024, r * kI8Row + kDc + (rpos(r, lane & 7) << 4));
+  dma4(scales, land + kI8Codes + 256 * w, 4 * lane);
+}
+
+// Eight int8 codes (byte e = entry e, two's complement) as bf16, exact.
+__device__ __forceinline__ bf16x8 unpack8_i8(uint32_t w0, uint32_t w1) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = (bf16)(float)(int8_t)(w0 >> (8 * e));
+    r[4 + e] = (bf16)(float)(int8_t)(w1 >> (8 * e));
+  }
+  return r;
+}
+
+// Wave w unpacks rows 8 w .. 8 w + 7 of a landed int8 tile into the bf16
+// latent stage (lane l: chunk l, codes 8 l .. 8 l + 7, of each row) and
+// copies the tile's scales (its own landed copy) to its scale slot.
+__device__ __forceinline__ void unpack_tile_i8(const char* __restrict__ land, char* __restrict__ lat,
+                                               float* __restrict__ scl, int w, int lane) {
+  asm volatile("" : "+v"(lane));
+  uint32_t wd[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint2 v = *(const uint2*)(land + (8 * w + i) * kDc + 8 * lane);
+    wd[i][0] = v.x;
+    wd[i][1] = v.y;
+  }
+  const float sv = *(const float*)(land + kI8Codes + 256 * w + 4 * lane);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 8 * w + i;
+    *(bf16x8*)(lat + r * kCBytes + (lpos(r, lane) << 4)) = unpack8_i8(wd[i][0], wd[i][1]);
+  }
+  if (lane < kTile) scl[lane] = sv;
 }
 
 // Score MFMAs with their accumulators in VGPRs.  Once any MFMA of a kernel
@@ -457,20 +524,36 @@ __device__ __forceinline__ void pv_tile(const char* __restrict__ ls, int lane, c
   }
 }
 
-// A tile's scores made ready for the softmax, in place.  int4 rows (I4):
-// the score is s_c (latent part) + s_r (rotary part) with the row's two
-// scales, read from the wave's scale slot `tsc` of the tile (pairs (s_c,
-// s_r) per row); the latent scales (times the factor the unpacked codes
-// lack) stay in `wsc` for the weights, which enter the PV product times them
-// (the PV multiplies the codes).  Unless the whole tile is visible to every
+// A tile's scores made ready for the softmax, in place.  Low-bit rows (QM):
+// the score is s_c (latent part) + s_r (rotary part) with the row's scales,
+// read from the wave's scale slot `tsc` of the tile (int4: pairs (s_c, s_r)
+// per row; int8: s_c per row, the 16-bit rotary part unscaled); the latent
+// scales (times the factor the unpacked codes lack) stay in `wsc` for the
+// weights, which enter the PV product times them (the PV multiplies the
+// codes).  Unless the whole tile is visible to every
 // row of the wave (`full`), tokens past the piece or the row's causal limit
 // (relative index `lim` per lane: token 4 lg + e of the first half is
 // visible when e <= lim) get -inf, i.e. weight 0.  A branch on `full` is
 // fine here: the softmax proper, which runs between the PV MFMAs, has none.
-template <int RB, bool I4>
+template <int RB, int QM>
 __device__ __forceinline__ void prep_scores(f32x4 (&s)[2][RB], const f32x4 (&sr)[2][RB], bool full,
                                             const int (&lim)[RB], const float* tsc, f32x4 (&wsc)[2]) {
-  if constexpr (I4) {
+  if constexpr (QM == 2) {
+    int ln = __lane_id();
+    asm volatile("" : "+v"(ln));
+    const int lg4 = 4 * (ln >> 4);
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const f32x4 sc = *(const f32x4*)(tsc + 16 * tb + lg4);  // tokens 4 lg .. 4 lg + 3 of the half
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        wsc[tb][e] = sc[e];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) s[tb][rb][e] = sc[e] * s[tb][rb][e] + sr[tb][rb][e];
+      }
+    }
+  }
+  if constexpr (QM == 1) {
     int ln = __lane_id();
     asm volatile("" : "+v"(ln));
     const int lg4 = 4 * (ln >> 4);
@@ -523,7 +606,7 @@ __device__ __forceinline__ float rows_max_raw(float v) {
 // max, its reduction over the lane groups, the max update, four pairs of
 // weights, the packing) that run one per PV column block, between the MFMAs
 // of the previous tile's PV.
-template <int RB, bool I4>
+template <int RB, bool LB>
 struct SoftmaxStages {
   static constexpr int kPerRb = 8;
   static constexpr int kStages = kPerRb * RB;
@@ -559,8 +642,8 @@ struct SoftmaxStages {
       const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[e], sl2, -msub[rb]));  // exp2(-inf) = 0
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[e], sl2, -msub[rb]));
       lsum[rb] += p0 + p1;
-      p[rb][e] = (bf16)(I4 ? p0 * wsc[0][e] : p0);
-      p[rb][4 + e] = (bf16)(I4 ? p1 * wsc[1][e] : p1);
+      p[rb][e] = (bf16)(LB ? p0 * wsc[0][e] : p0);
+      p[rb][4 + e] = (bf16)(LB ? p1 * wsc[1][e] : p1);
     } else {
       l_part[rb] = l_part[rb] * alpha[rb] + lsum[rb];
       // formed here, not sunk towards their first use in the next tile
@@ -571,13 +654,13 @@ struct SoftmaxStages {
 };
 
 // The whole softmax at once (the first tile of a piece)
-template <int RB, bool I4>
+template <int RB, bool LB>
 __device__ __forceinline__ bool softmax_tile(const f32x4 (&s)[2][RB], float (&m_used)[RB], float (&l_part)[RB],
                                              bf16x8 (&p)[RB], float (&alpha)[RB], const f32x4 (&wsc)[2],
                                              float sl2) {
-  SoftmaxStages<RB, I4> sm{s, m_used, l_part, p, alpha, wsc, sl2};
+  SoftmaxStages<RB, LB> sm{s, m_used, l_part, p, alpha, wsc, sl2};
 #pragma unroll
-  for (int k = 0; k < SoftmaxStages<RB, I4>::kStages; ++k) sm.run(k);
+  for (int k = 0; k < SoftmaxStages<RB, LB>::kStages; ++k) sm.run(k);
   return sm.moved();
 }
 
@@ -631,17 +714,20 @@ __device__ __forceinline__ T& pick(T& a, T& b) {
 
 }  // namespace
 
-// RB: 16-row blocks per wave (1: 64-row groups, 2: 128-row groups).  I4:
-// int4 rows (packed latent and rotary codes, two scales per row).  PB: bf16
-// partial outputs (a compile-time choice: a branch in the epilogue changes
-// the register allocation of the tile loop).
-template <int RB, bool I4, bool PB, bool QS>
+// RB: 16-row blocks per wave (1: 64-row groups, 2: 128-row groups).  QM: the
+// stored rows (0: 16-bit; 1: int4, packed latent and rotary codes, two
+// scales per row; 2: int8 latent codes and 16-bit rotary entries, one scale
+// per row).  PB: bf16 partial outputs (a compile-time choice: a branch in
+// the epilogue changes the register allocation of the tile loop).  QS: a
+// split query.
+template <int RB, int QM, bool PB, bool QS>
 __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch L) {
   constexpr int MT = 16 * RB * kRowsWaves;  // query rows of a row group
   constexpr int kOv = piece_tiles(MT, PB, QS) * kTile;  // a request's start, in rows of the work split
-  using SM = RowsSmem<I4>;
+  constexpr bool LB = QM != 0;                           // low-bit rows: landed, then unpacked
+  using SM = RowsSmem<QM, RB>;
   constexpr int NLAT = SM::NLAT;
-  constexpr int RBYTES = I4 ? kI4Row : kRowBytes;  // bytes per stored row
+  constexpr int RBYTES = QM == 1 ? kI4Row : QM == 2 ? kI8Row : kRowBytes;  // bytes per stored row
   __shared__ __attribute__((aligned(16))) SM sm;
 
   // ---- the segment of this workgroup, and its place in the segment's grid ----
@@ -891,31 +977,41 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
         const int n = ok ? min(kTile, pr1 - (pr0 + it * kTile)) : 0;
         return buffer_rsrc(ok ? cache + row * RBYTES : cache, n * RBYTES);
       };
+      constexpr int kSpr = QM == 1 ? 2 : 1;  // scales per stored row
       auto scale_rsrc = [&](int it, int pg) -> i32x4_t {
         bool ok;
         const int64_t row = tile_row(it, pg, &ok);
         const int n = ok ? min(kTile, pr1 - (pr0 + it * kTile)) : 0;
-        return buffer_rsrc(ok ? row_scale + 2 * row : row_scale, n * 8);
+        return buffer_rsrc(ok ? row_scale + kSpr * row : row_scale, n * 4 * kSpr);
       };
-      auto load_i4 = [&](int it, int pg) {
-        tile_load_i4(tile_rsrc(it, pg), scale_rsrc(it, pg), sm.land[it % 3], wave, lane);
+      auto load_lb = [&](int it, int pg) {
+        if constexpr (QM == 1) tile_load_i4(tile_rsrc(it, pg), scale_rsrc(it, pg), sm.land[it % 3], wave, lane);
+        if constexpr (QM == 2)
+          tile_load_i8(tile_rsrc(it, pg), scale_rsrc(it, pg), sm.land[it % 2], sm.rot[it % kRotStages], wave, lane);
       };
-      auto unpack_i4 = [&](int it) {
-        unpack_tile_i4(sm.land[it % 3], sm.lat[it % NLAT], sm.rot[it % kRotStages], sm.scl[it % 3][wave], wave,
-                       lane);
+      auto unpack_lb = [&](int it) {
+        if constexpr (QM == 1)
+          unpack_tile_i4(sm.land[it % 3], sm.lat[it % NLAT], sm.rot[it % kRotStages], sm.scl[it % 3][wave], wave,
+                         lane);
+        if constexpr (QM == 2) unpack_tile_i8(sm.land[it % 2], sm.lat[it % NLAT], sm.scl[it % 3][wave], wave, lane);
       };
+      // low-bit rows: loads run kLbAhead tiles ahead of the scores (int4:
+      // tiles 0..2 go out first and tile 3 once tile 0 is unpacked; int8,
+      // with two landing stages: tiles 0 and 1, then tile 2)
+      constexpr int kLbAhead = QM == 1 ? 4 : 3;
+      constexpr int kLbFirst = QM == 1 ? 3 : 2;  // tiles loaded before the first unpacking
 
       int pg_next = 0;  // page of the next tile to load (paged layout)
-      int pg_i4 = 0;    // int4: page of tile 3, loaded once tile 0 is unpacked
+      int pg_lb = 0;    // low-bit rows: page of the tile loaded once tiles 0 and 1 are unpacked
       // ---- the first tiles go out before the query loads ----
-      if constexpr (I4) {
-        int pg[5];
+      if constexpr (LB) {
+        int pg[kLbAhead + 1];
 #pragma unroll
-        for (int t = 0; t < 5; ++t) pg[t] = bt_row && t < n_tiles ? page_of(t) : 0;
+        for (int t = 0; t <= kLbAhead; ++t) pg[t] = bt_row && t < n_tiles ? page_of(t) : 0;
 #pragma unroll
-        for (int t = 0; t < 3; ++t) load_i4(t, pg[t]);
-        pg_i4 = pg[3];
-        pg_next = pg[4];
+        for (int t = 0; t < kLbFirst; ++t) load_lb(t, pg[t]);
+        pg_lb = pg[kLbFirst];
+        pg_next = pg[kLbFirst + 1];
       } else {
         int pg[kLoadAhead + 1];
 #pragma unroll
@@ -1031,27 +1127,27 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
 
       f32x4 sacc[2][RB];
       f32x4 racc_i4[2][RB];
-      f32x4(&racc)[2][RB] = pick<I4>(racc_i4, sacc);  // the rotary part's accumulator (apart for int4 only)
+      f32x4(&racc)[2][RB] = pick<LB>(racc_i4, sacc);  // the rotary part's accumulator (apart for low-bit rows)
       auto scl_of = [&](int it) -> const float* {
-        if constexpr (I4) return sm.scl[it % 3][wave];
+        if constexpr (LB) return sm.scl[it % 3][wave];
         return nullptr;
       };
       bf16x8 p[RB];
       float alpha[RB];
       int lim[RB];
-      f32x4 wsc[2];  // int4 rows: the latent scales of the current tile's tokens
+      f32x4 wsc[2];  // low-bit rows: the latent scales of the current tile's tokens
       // ---- tile 0: scores and softmax ----
-      if constexpr (I4) {
-        // tiles 0 and 1 landed (tile 2 in flight), unpacked by every wave;
-        // then tile 3 goes out into tile 0's landing stage
-        wait_vmcnt<kI4Dma>();
+      if constexpr (LB) {
+        // tiles 0 and 1 landed (int4: tile 2 in flight), unpacked by every
+        // wave; then the next tile goes out into tile 0's landing stage
+        wait_vmcnt<QM == 1 ? kI4Dma : 0>();
         wait_lgkm0();
         barrier_raw();
-        unpack_i4(0);
-        unpack_i4(1);
+        unpack_lb(0);
+        unpack_lb(1);
         wait_lgkm0();
         barrier_raw();
-        load_i4(3, pg_i4);
+        load_lb(kLbFirst, pg_lb);
       } else {
         static_assert(kLoadAhead == 3, "tiles 1 and 2 stay in flight over tile 0");
         wait_vmcnt<2 * kDmaPerWave>();
@@ -1062,30 +1158,31 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
         qk_tile<RB>(sm.lat[0], sm.rot[0], qrot_w, lane, qh, qrl, sacc, racc);
         tile_lim(0, lim);
         // (its factor multiplies an empty O)
-        prep_scores<RB, I4>(sacc, racc, tile_full(0), lim, scl_of(0), wsc);
-        softmax_tile<RB, I4>(sacc, m_used, l_part, p, alpha, wsc, sl2);
+        prep_scores<RB, QM>(sacc, racc, tile_full(0), lim, scl_of(0), wsc);
+        softmax_tile<RB, LB>(sacc, m_used, l_part, p, alpha, wsc, sl2);
       }
       for (int it = 0; it + 1 < n_tiles; ++it) {
         // 16-bit rows: tile it+1 in LDS (this wave's loads, with tile it+2
         // still in flight, then everyone's); every wave is past the PV of
         // tile it-1 and the scores of tile it, so their stages take tile it+3,
         // whose loads go out between the PV MFMAs of tile it.
-        // int4 rows: tile it+2 landed (tile it+3 in flight) and tile it+1
-        // unpacked; every wave is past the PV of tile it-1, the scores of tile
-        // it and the unpacking of tile it+1, so tile it+2 is unpacked into the
-        // stages of tile it-1 and tile it+4 lands where tile it+1 did.
-        wait_vmcnt<I4 ? kI4Dma : kDmaPerWave>();
+        // Low-bit rows: tile it+2 landed (int4: tile it+3 in flight) and tile
+        // it+1 unpacked; every wave is past the PV of tile it-1, the scores of
+        // tile it and the unpacking of tile it+1, so tile it+2 is unpacked into
+        // the stages of tile it-1 and tile it + kLbAhead lands where tile it+1
+        // did (int8: its rotary entries where tile it's were).
+        wait_vmcnt<QM == 1 ? kI4Dma : QM == 2 ? 0 : kDmaPerWave>();
         wait_lgkm0();
         barrier_raw();
         const i32x4_t rs_next = tile_rsrc(it + kLoadAhead, pg_next);
         char* const lat_next = sm.lat[(it + kLoadAhead) % NLAT];
         char* const rot_next = sm.rot[(it + kLoadAhead) % kRotStages];
         auto load_next = [&](int i) {
-          if constexpr (!I4) tile_load(rs_next, lat_next, rot_next, wave, lane, i);
+          if constexpr (!LB) tile_load(rs_next, lat_next, rot_next, wave, lane, i);
         };
-        if constexpr (I4) {
-          load_i4(it + 4, pg_next);
-          unpack_i4(it + 2);
+        if constexpr (LB) {
+          load_lb(it + kLbAhead, pg_next);
+          unpack_lb(it + 2);
         }
         if (!wave_rows) {
 #pragma unroll
@@ -1094,13 +1191,13 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
           tile_lim(it + 1, lim);
           qk_tile<RB>(sm.lat[(it + 1) % NLAT], sm.rot[(it + 1) % kRotStages], qrot_w, lane, qh, qrl, sacc, racc);
           sched_qk<RB>();
-          prep_scores<RB, I4>(sacc, racc, tile_full(it + 1), lim, scl_of(it + 1), wsc);
+          prep_scores<RB, QM>(sacc, racc, tile_full(it + 1), lim, scl_of(it + 1), wsc);
           __builtin_amdgcn_sched_barrier(0);
           // the PV of tile it with the softmax of tile it+1 between its MFMAs
           // (the scores die there: only the two tiles' P operands live across
           // the PV product)
           bf16x8 pn[RB];
-          SoftmaxStages<RB, I4> smx{sacc, m_used, l_part, pn, alpha, wsc, sl2};
+          SoftmaxStages<RB, LB> smx{sacc, m_used, l_part, pn, alpha, wsc, sl2};
           pv_tile<RB>(sm.lat[it % NLAT], lane, p, acc, load_next, [&](int db) { smx.run(db); });
           const bool moved = smx.moved();
           __builtin_amdgcn_sched_barrier(0);
@@ -1112,7 +1209,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
         // during the wait at the top (not inside the score product, where it
         // would force full waits on the LDS reads)
         {
-          const int t_pg = it + (I4 ? 5 : kLoadAhead + 1);  // the tile loaded next iteration
+          const int t_pg = it + (LB ? kLbAhead + 1 : kLoadAhead + 1);  // the tile loaded next iteration
           if (bt_row && t_pg < n_tiles) pg_next = page_of(t_pg);
         }
       }
@@ -1208,18 +1305,22 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
   }
 }
 
-template __global__ void decode_rows_kernel<1, false, false, false>(RowsLaunch);
-template __global__ void decode_rows_kernel<2, false, false, false>(RowsLaunch);
-template __global__ void decode_rows_kernel<1, true, false, false>(RowsLaunch);
-template __global__ void decode_rows_kernel<1, false, true, false>(RowsLaunch);
-template __global__ void decode_rows_kernel<2, false, true, false>(RowsLaunch);
-template __global__ void decode_rows_kernel<1, true, true, false>(RowsLaunch);
-template __global__ void decode_rows_kernel<1, false, false, true>(RowsLaunch);
-template __global__ void decode_rows_kernel<2, false, false, true>(RowsLaunch);
-template __global__ void decode_rows_kernel<1, true, false, true>(RowsLaunch);
-template __global__ void decode_rows_kernel<1, false, true, true>(RowsLaunch);
-template __global__ void decode_rows_kernel<2, false, true, true>(RowsLaunch);
-template __global__ void decode_rows_kernel<1, true, true, true>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, 0, false, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<2, 0, false, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, 1, false, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, 2, false, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, 0, true, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<2, 0, true, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, 1, true, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, 2, true, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, 0, false, true>(RowsLaunch);
+template __global__ void decode_rows_kernel<2, 0, false, true>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, 1, false, true>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, 2, false, true>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, 0, true, true>(RowsLaunch);
+template __global__ void decode_rows_kernel<2, 0, true, true>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, 1, true, true>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, 2, true, true>(RowsLaunch);
 
 int decode_rows_tile(int rows_total) { return rows_total <= 64 ? 64 : 128; }
 
@@ -1254,35 +1355,36 @@ SegCost seg_cost(const DecodeArgs& a, const SegArgs& s, int mt) {
 }
 
 template <bool PB, bool QS>
-hipError_t launch_rows_pb(const RowsLaunch& L, int mt, bool i4, int grid, hipStream_t stream) {
+hipError_t launch_rows_pb(const RowsLaunch& L, int mt, int qm, int grid, hipStream_t stream) {
   const dim3 block(kRowsThreads);
-  if (i4) return launch(decode_rows_kernel<1, true, PB, QS>, dim3(grid), block, stream, L);
-  if (mt == 64) return launch(decode_rows_kernel<1, false, PB, QS>, dim3(grid), block, stream, L);
-  return launch(decode_rows_kernel<2, false, PB, QS>, dim3(grid), block, stream, L);
+  if (qm == 1) return launch(decode_rows_kernel<1, 1, PB, QS>, dim3(grid), block, stream, L);
+  if (qm == 2) return launch(decode_rows_kernel<1, 2, PB, QS>, dim3(grid), block, stream, L);
+  if (mt == 64) return launch(decode_rows_kernel<1, 0, PB, QS>, dim3(grid), block, stream, L);
+  return launch(decode_rows_kernel<2, 0, PB, QS>, dim3(grid), block, stream, L);
 }
 
-hipError_t launch_rows(const RowsLaunch& L, int mt, bool i4, int grid, hipStream_t stream) {
+hipError_t launch_rows(const RowsLaunch& L, int mt, int qm, int grid, hipStream_t stream) {
   if (L.a.q_split) {
-    if (L.a.part_bf16) return launch_rows_pb<true, true>(L, mt, i4, grid, stream);
-    return launch_rows_pb<false, true>(L, mt, i4, grid, stream);
+    if (L.a.part_bf16) return launch_rows_pb<true, true>(L, mt, qm, grid, stream);
+    return launch_rows_pb<false, true>(L, mt, qm, grid, stream);
   }
-  if (L.a.part_bf16) return launch_rows_pb<true, false>(L, mt, i4, grid, stream);
-  return launch_rows_pb<false, false>(L, mt, i4, grid, stream);
+  if (L.a.part_bf16) return launch_rows_pb<true, false>(L, mt, qm, grid, stream);
+  return launch_rows_pb<false, false>(L, mt, qm, grid, stream);
 }
 
 }  // namespace
 
 hipError_t launch_decode_rows(const DecodeArgs& a, int n_wg, hipStream_t stream) {
-  return launch_decode_rows_multi(a, &a.seg, 1, n_wg, false, stream);
+  return launch_decode_rows_multi(a, &a.seg, 1, n_wg, 0, stream);
 }
 
-hipError_t launch_decode_rows_multi(const DecodeArgs& a, const SegArgs* segs, int n_segs, int n_wg, bool i4,
+hipError_t launch_decode_rows_multi(const DecodeArgs& a, const SegArgs* segs, int n_segs, int n_wg, int qm,
                                     hipStream_t stream) {
   for (int g0 = 0; g0 < n_segs; g0 += kRowsMaxSegs) {
     const int n = std::min(kRowsMaxSegs, n_segs - g0);
     int rows_max = 0;
     for (int g = 0; g < n; ++g) rows_max = std::max(rows_max, a.s_q * segs[g0 + g].head_count);
-    const int mt = i4 ? 64 : decode_rows_tile(rows_max);  // int4 rows: 64-row groups
+    const int mt = qm ? 64 : decode_rows_tile(rows_max);  // low-bit rows: 64-row groups
     RowsLaunch L{};
     L.a = a;
     L.n_segs = n;
@@ -1328,7 +1430,7 @@ hipError_t launch_decode_rows_multi(const DecodeArgs& a, const SegArgs* segs, in
       L.wg_begin[g] = grid;
       grid += L.n_share[g] * L.n_rg[g];
     }
-    const hipError_t e = launch_rows(L, mt, i4, grid, stream);
+    const hipError_t e = launch_rows(L, mt, qm, grid, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

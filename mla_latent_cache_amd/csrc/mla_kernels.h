@@ -136,9 +136,9 @@ int decode_bf16_tile(int rows_total);
 // row groups of 64 (up to 64 rows) or 128; n_wg workgroups per row group.
 hipError_t launch_decode_rows(const DecodeArgs& a, int n_wg, hipStream_t stream);
 // All n_segs segments (any number; kRowsMaxSegs per launch) in row-owning
-// launches that split n_wg workgroups by estimated tile work; i4: int4 rows
-// (64-row groups).
-hipError_t launch_decode_rows_multi(const DecodeArgs& a, const SegArgs* segs, int n_segs, int n_wg, bool i4,
+// launches that split n_wg workgroups by estimated tile work; qm: the stored
+// rows (0: 16-bit, 1: int4, 2: int8; low-bit rows take 64-row groups).
+hipError_t launch_decode_rows_multi(const DecodeArgs& a, const SegArgs* segs, int n_segs, int n_wg, int qm,
                                     hipStream_t stream);
 // Rows of that kernel's row group for a segment of rows_total query rows.
 int decode_rows_tile(int rows_total);

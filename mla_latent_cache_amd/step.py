@@ -143,10 +143,10 @@ class DecodeStep:
         # The row-owning kernel reads the latent query as bf16 hi and lo
         # planes written by the fused query kernel (half the bytes per read
         # of an fp32 query): on that kernel's calls (several segments, more
-        # than 32 query rows, an int4 cache) without QK-Norm, where the fused
+        # than 32 query rows, a low-bit cache) without QK-Norm, where the fused
         # kernel has its MFMA shape.
         rows = max(s_q * s.head_count for s in segments)
-        rows_kernel = quant == "int4" or (quant is None and (len(segments) > 1 or rows > 32))
+        rows_kernel = quant is not None or len(segments) > 1 or rows > 32
         mfma_shape = w_uk.dtype == torch.bfloat16 and w_uk.shape[1] == 128 and d_c == 512
         can_split = (self.bf16 and rows_kernel and mfma_shape and qk_norm is None and len(self.q_rots) <= 8
                      and q_nope.data_ptr() % 16 == 0 and w_uk.data_ptr() % 16 == 0)

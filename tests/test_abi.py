@@ -182,10 +182,11 @@ def test_null_and_shape_errors_before_any_gpu_call(lib):
             setattr(s, k, v)
         return s
 
-    def dec(segs, n_heads=4, n_part=2, dtype=1, d_c=512, d_r=64, q=P, o=P, q_dtype=0, part_dtype=0):
+    def dec(segs, n_heads=4, n_part=2, dtype=1, d_c=512, d_r=64, q=P, o=P, q_dtype=0, part_dtype=0, batch=2):
+        # batch 0: every argument is checked, then nothing is launched (0 = accepted)
         arr = (MlaSegment * len(segs))(*segs)
-        return _st(lib, "mla_decode_splitkv", arr, len(segs), q, q_dtype, dtype, 2, 1, n_heads, d_c, d_r, 0.1,
-                   o, part_dtype, P, n_part, 0, None)
+        return _st(lib, "mla_decode_splitkv", arr, len(segs), q, q_dtype, dtype, batch, 1, n_heads, d_c, d_r,
+                   0.1, o, part_dtype, P, n_part, 0, None)
 
     assert dec([seg()], q=None) == 1
     assert dec([seg(cache=None)]) == 1
@@ -203,7 +204,7 @@ def test_null_and_shape_errors_before_any_gpu_call(lib):
     assert dec([seg()], dtype=0, part_dtype=1) == 5       # and writes fp32 partials
     assert dec([seg()], part_dtype=3) == 3                # partials are fp32 or bf16
     assert dec([seg(row_rinv=P)], q_dtype=1) == 5         # QK-Norm factors need an fp32 query
-    # int8 cache (cache_dtype 2): fp32 query, row_scale on every segment, no QK-Norm
+    # int8 cache (cache_dtype 2): fp32 or split query, row_scale on every segment, no QK-Norm
     assert dec([seg()], dtype=2) == 1                     # row_scale missing
     assert dec([seg(row_scale=P)], dtype=2, q_dtype=1) == 5
     assert dec([seg(row_scale=P, row_rinv=P)], dtype=2) == 5
@@ -213,9 +214,10 @@ def test_null_and_shape_errors_before_any_gpu_call(lib):
     assert dec([seg(row_scale=P)], dtype=3, q_dtype=1) == 5
     assert dec([seg(row_scale=P, row_rinv=P)], dtype=3) == 5
     assert dec([seg(row_scale=P)], dtype=4) == 3
-    # split query (q_dtype 4, bf16 hi and lo planes): bf16 or int4 cache, no QK-Norm
+    # split query (q_dtype 4, bf16 hi and lo planes): bf16, int8 or int4 cache, no QK-Norm
     assert dec([seg()], dtype=0, q_dtype=4) == 5
-    assert dec([seg(row_scale=P)], dtype=2, q_dtype=4) == 5
+    assert dec([seg(row_scale=P)], dtype=2, q_dtype=4, batch=0) == 0
+    assert dec([seg(row_scale=P)], dtype=3, q_dtype=4, batch=0) == 0
     assert dec([seg(row_rinv=P)], q_dtype=4) == 5
     assert dec([seg()], q_dtype=5) == 3
 

@@ -47,7 +47,7 @@ def test_chain_mini(name):
     print(f"[parity] {name}: {errs}", flush=True)
 
 
-@pytest.mark.parametrize("name", ["dsv3", "long", "merge", "prefill", "int4"])
+@pytest.mark.parametrize("name", ["dsv3", "long", "merge", "prefill", "int4", "int8"])
 @pytest.mark.parametrize("split_query", [True, False])
 def test_chain_mini_query_format(name, split_query):
     """The row-owning kernel's two query formats: bf16 hi and lo planes
