@@ -482,7 +482,7 @@ mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q
                       "mla_decode_splitkv launch");
   for (int g = 0; g < n_segs; ++g) {
     a.seg = sa[g];
-    hipError_t e = bf ? mla::launch_decode_bf16(a, wg, q32, i8, (hipStream_t)stream)
+    hipError_t e = bf ? mla::launch_decode_bf16(a, wg, q32, (hipStream_t)stream)
                       : mla::launch_decode_f32(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "mla_decode_splitkv launch");
   }

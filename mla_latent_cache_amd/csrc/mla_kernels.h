@@ -122,8 +122,8 @@ hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
 // bf16 MFMA decode (d_c = 512, d_rope = 64, page 64).  n_wg workgroups per
 // row group; balanced split of all rows of the segment over them.
 // q_f32: q_lat / q_rot are fp32 (split into bf16 hi + lo) instead of bf16.
-// i8: the cache rows are int8 latent codes (scale seg.row_scale) + bf16 rotary keys.
-hipError_t launch_decode_bf16(const DecodeArgs& a, int n_wg, bool q_f32, bool i8, hipStream_t stream);
+// Low-bit caches run on the row-owning kernel (launch_decode_rows_multi).
+hipError_t launch_decode_bf16(const DecodeArgs& a, int n_wg, bool q_f32, hipStream_t stream);
 // Grid shape of a bf16 decode of one segment with row groups of mt rows:
 // row groups and shares (n_wg workgroups per row group, a multiple of 8 when
 // there are several row groups).
