@@ -167,9 +167,11 @@ EDGE = {
         SegSpec("kv", lengths=(0, 1, 5, 37, 64, 65, 100, 130, 300), online=True),)),
     "qknorm_toy_f32": _custom("edge-qknf32", dtype="f32", batch=3, heads=2, qk_norm=True, segs=(
         SegSpec("kv", lengths=(16, 0, 130), layout="paged", page_size=8, spare_pages=1, online=True),)),
-    # int8 latent cache: row scales through each row-group size, contiguous
-    # and paged, empty and one-row requests, causal rows, and the 64-row
-    # groups' first-order lse correction with twice-spread scores
+    # int8 latent cache (64-row groups of the row-owning kernel): one wave
+    # with rows (16 rows), contiguous and paged, empty and one-row requests,
+    # causal rows, the first-order lse correction with twice-spread scores,
+    # two 64-row groups of one request (128 heads) and the merge layout's
+    # segments in one launch
     "int8_rows16": _custom("edge-i8-16", batch=4, heads=16, quant="int8", segs=(
         SegSpec("kv", lengths=(0, 1, 37, 300), online=True),)),
     "int8_rows32_causal": _custom("edge-i8-32", batch=3, heads=16, s_q=2, quant="int8", segs=(
@@ -177,6 +179,9 @@ EDGE = {
                 online=True),)),
     "int8_peaked_rows64": _custom("edge-i8-64", batch=4, heads=64, quant="int8", scale=2 / math.sqrt(192), segs=(
         SegSpec("kv", lengths=(1, 37, 300, 1000), online=True),)),
+    "int8_rows128_paged": _custom("edge-i8-128", batch=3, heads=128, quant="int8", segs=(
+        SegSpec("kv", lengths=(64, 130, 1500), layout="paged", page_size=64, spare_pages=3, online=True),)),
+    "int8_merge_layout": replace(M.mini_spec("merge"), name="edge-i8-merge", quant="int8"),
     # int4 cache (latent and rotary codes, two scales per row): one wave with
     # rows (16 rows), causal rows over pages, 64-row groups with
     # twice-spread scores, two 64-row groups of one request (128 heads) and
