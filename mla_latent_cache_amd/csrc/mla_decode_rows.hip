@@ -75,6 +75,12 @@
 //    than the workgroup holds) only moves its share of each tile and skips
 //    the products, leaving the LDS and the other SIMDs' issue to the waves
 //    with rows.
+//  * Low-bit rows (QuantMLA abstract; 64-row groups): int8 latent codes with
+//    16-bit rotary entries, or int4 latent and rotary codes, land packed in
+//    LDS and every wave unpacks its 8 rows of a tile into the bf16 stages
+//    (the codes are exact in bf16) one tile before their scores; the row
+//    scales multiply the scores after the QK product and the weights before
+//    the PV product, so the PV sums weights times dequantized rows.
 #include "mla_common.h"
 #include "mla_decode_tile.h"
 #include "mla_kernels.h"

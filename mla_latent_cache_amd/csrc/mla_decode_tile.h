@@ -53,9 +53,14 @@ __device__ __forceinline__ float rows_sum(float v) {
 
 // LDS layout of a tile (no padding, 16-byte chunks XOR-swizzled per row):
 // latent row r holds chunk c (0..63) at position c ^ (r & 15), rotary row r
-// chunk j (0..7) at position j ^ ((r >> 1) & 7).  A score-operand read (16
-// consecutive rows, one chunk) and a transposed read then touch 16 distinct
-// bank groups, like a padded layout, while the tile fits in 36 KiB.
+// chunk j (0..7) at position j ^ ((r >> 1) & 7), and the tile fits in 36 KiB.
+// A score-operand read (16 consecutive rows, one chunk) then reaches 64
+// distinct banks per cycle; in a transposed read (ds_read_b64_tr_b16, 32
+// lanes per cycle) rows r and r ^ 1 share their banks, a two-way conflict
+// (the bank-conflict counter gives 0.24 on the kernel for up to 32 rows,
+// which keeps this layout; its time did not depend on it).  The
+// row-owning kernel (mla_decode_rows.hip) keys its latent rows by 2 (r & 7)
+// instead, which serves both reads without conflicts.
 __device__ __forceinline__ int cpos(int r, int c) { return c ^ (r & 15); }
 __device__ __forceinline__ int rpos(int r, int j) { return j ^ ((r >> 1) & 7); }
 
