@@ -58,9 +58,9 @@ __device__ __forceinline__ float rows_sum(float v) {
 // distinct banks per cycle; in a transposed read (ds_read_b64_tr_b16, 32
 // lanes per cycle) rows r and r ^ 1 share their banks, a two-way conflict
 // (the bank-conflict counter gives 0.24 on the kernel for up to 32 rows,
-// which keeps this layout; its time did not depend on it).  The
-// row-owning kernel (mla_decode_rows.hip) keys its latent rows by 2 (r & 7)
-// instead, which serves both reads without conflicts.
+// which keeps this layout).  The row-owning kernel (mla_decode_rows.hip)
+// keys its latent rows by 2 (r & 7) instead, which serves both reads
+// without conflicts (its time did not change).
 __device__ __forceinline__ int cpos(int r, int c) { return c ^ (r & 15); }
 __device__ __forceinline__ int rpos(int r, int j) { return j ^ ((r >> 1) & 7); }
 
