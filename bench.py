@@ -89,13 +89,17 @@ def decode_kernel_name(x) -> str:
 
 
 def kernel_hash() -> str:
-    """Hash of the decode kernels' sources and the headers they include (the
-    files that exist)."""
+    """Hash of the code of the decode kernels' sources and the headers they
+    include (the files that exist): comments removed and whitespace runs
+    folded, so that an edit of the comments keeps the counters valid."""
     h = hashlib.sha256()
     for p in DECODE_SRCS:
         if os.path.exists(p):
-            with open(p, "rb") as f:
-                h.update(f.read())
+            with open(p, encoding="utf-8") as f:
+                text = f.read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
+            h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
