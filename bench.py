@@ -34,7 +34,8 @@ MALL_BYTES = 256 << 20          # Infinity Cache: rotate caches so every step re
 DECODE_SRCS = [os.path.join(ROOT, "mla_latent_cache_amd", "csrc", f)
                for f in ("mla_decode_bf16.hip", "mla_decode_rows.hip", "mla_decode_tile.h", "mla_common.h",
                          "mla_kernels.h")]
-SEEDS = {"toy": 0, "small": 1, "dsv3": 2, "long": 3, "merge": 4, "prefill": 5, "qknorm": 6, "int8": 7, "int4": 8}
+SEEDS = {"toy": 0, "small": 1, "dsv3": 2, "long": 3, "merge": 4, "prefill": 5, "qknorm": 6, "int8": 7, "int4": 8,
+         "qknorm_dsv3": 9}
 
 
 def _rows(x):
@@ -82,10 +83,11 @@ def decode_kernel_name(x) -> str:
     if sp.quant in ("int4", "int8"):
         qm = 1 if sp.quant == "int4" else 2
         return f"decode_rows_kernel<1, {qm}, true> ({sp.quant} rows, 64-row groups)"
-    if sp.qk_norm or (len(rows) == 1 and rows[0] <= 32):
+    if len(rows) == 1 and rows[0] <= 32:
         return "decode_bf16_kernel"
     rb = 1 if max(rows) <= 64 else 2
-    return f"decode_rows_kernel<{rb}, 0, true> ({64 * rb}-row groups)"
+    qkn = ", QK-Norm row factors" if sp.qk_norm else ""
+    return f"decode_rows_kernel<{rb}, 0, true> ({64 * rb}-row groups{qkn})"
 
 
 def kernel_hash() -> str:
@@ -177,7 +179,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="dsv3", choices=["small", "dsv3", "long", "merge", "toy", "prefill", "qknorm", "int8", "int4"])
+    ap.add_argument("--workload", default="dsv3", choices=["small", "dsv3", "long", "merge", "toy", "prefill", "qknorm", "int8", "int4",
+                                                               "qknorm_dsv3"])
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--n-wg", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)

@@ -149,7 +149,10 @@ typedef struct {
                                  key (mla_qknorm_key_rinv), indexed like the cache rows
                                  ([batch][max_rows] or [n_pages][page_size]); the
                                  latent part of each score is multiplied by it.
-                                 NULL => no QK-Norm */
+                                 NULL => no QK-Norm.  Given for every segment
+                                 of a call or for none (else
+                                 MLA_ERR_UNSUPPORTED); needs an fp32 or split
+                                 query and a 16-bit cache */
   const float* row_scale;     /* int8 cache (cache_dtype MLA_I8): per stored row the
                                  scale of its latent codes (mla_quantize_latent_i8),
                                  indexed like row_rinv; the latent is scale * code.
@@ -182,7 +185,7 @@ typedef struct {
  *          mla_prepare_q; each segment's q_rot has q_dtype too (fp32 for
  *          MLA_BF16X2).  MLA_BF16X2: [n_tok][n_heads][2][d_c] bf16 hi and lo
  *          planes (mla_prepare_q with lat_dtype MLA_BF16X2), for a bf16 cache
- *          (not QK-Norm) or a low-bit one; always the row-owning kernel; the
+ *          (with or without QK-Norm) or a low-bit one; always the row-owning kernel; the
  *          same arithmetic as an fp32 query (which is split into exactly
  *          these parts inside the kernel).
  * caches   cache_dtype.  MLA_BF16 caches take an fp32 query or a bf16 one.
@@ -190,7 +193,10 @@ typedef struct {
  *          32 query rows multiply both parts; 64-row groups multiply lo
  *          only on the rotary dims and add the latent lo part's share to
  *          the lse to first order (scale * lo . o_part; lse error second
- *          order, ~1e-5 at unit-variance inputs).  MLA_F32 caches take an
+ *          order, ~1e-5 at unit-variance inputs; with QK-Norm row factors
+ *          the share is scale * rbar * lo . o_part, rbar the softmax-weighted
+ *          mean factor of the piece, whose error is the weighted covariance
+ *          of the factors and the lo scores, again second order).  MLA_F32 caches take an
  *          fp32 query.  MLA_I8 caches (QuantMLA abstract: a low-bit latent
  *          cache dequantized inside attention) take an fp32 or split query
  *          and every segment's row_scale: the latent score of row t is

@@ -156,10 +156,17 @@ WORKLOADS["int4"] = replace(
     description="long context from an int4 cache: B=4, H=64, T=262144 contiguous, 1 query token; "
                 "per-row 4-bit latent and rotary codes (288 B + two 4 B scales per row)")
 
+# The DeepSeek-V3-style batch with QK-Norm (QK-Norm MLA abstract): 128 heads
+# per request, so the row factors ride on the 128-row groups of the decode.
+WORKLOADS["qknorm_dsv3"] = replace(
+    WORKLOADS["dsv3"], name="qknorm_dsv3", qk_norm=True,
+    description="DeepSeek-V3-style with QK-Norm: B=64, H=128, T~U[1024,32768], 64-row pages, shuffled block "
+                "table, RMSNorm of the content query and key")
+
 # Order of the configurations as listed by the benchmark description.
 WORKLOAD_ORDER = ("toy", "small", "dsv3", "long", "merge")
 # Further workloads (beyond the five configurations)
-EXTRA_WORKLOADS = ("prefill", "qknorm", "int8", "int4")
+EXTRA_WORKLOADS = ("prefill", "qknorm", "int8", "int4", "qknorm_dsv3")
 
 
 def spec_for(name: str) -> Spec:
@@ -190,6 +197,10 @@ def mini_spec(name: str) -> Spec:
             replace(s.segments[2], length=None, lengths=(70, 4, 65)),
         )
         return replace(s, name="merge-mini", batch=3, segments=segs)
+    if name == "qknorm_dsv3":
+        return replace(s, name="qknorm_dsv3-mini", batch=5,
+                       segments=(SegSpec("kv", lengths=(700, 64, 1, 333, 1000), layout="paged",
+                                         page_size=64, spare_pages=3, online=True),))
     if name == "qknorm":
         return replace(s, name="qknorm-mini", batch=3,
                        segments=(SegSpec("kv", lengths=(1, 129, 777), online=True),))

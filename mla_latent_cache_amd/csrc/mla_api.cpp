@@ -428,8 +428,10 @@ mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q
       if (cap > ((int64_t)1 << 30) || (int64_t)batch * cap > ((int64_t)1 << 30))
         return fail(MLA_ERR_UNSUPPORTED, "segment %d: batch * rows per request = %lld exceeds 2^30", g,
                     (long long)((int64_t)batch * cap));
-      if (s.row_rinv && q_dtype != MLA_F32)
-        return fail(MLA_ERR_UNSUPPORTED, "segment %d: QK-Norm (row_rinv) needs an fp32 query", g);
+      if (s.row_rinv && q_dtype == MLA_BF16)
+        return fail(MLA_ERR_UNSUPPORTED, "segment %d: QK-Norm (row_rinv) needs an fp32 or split query", g);
+      if ((s.row_rinv != nullptr) != (segs[0].row_rinv != nullptr))
+        return fail(MLA_ERR_UNSUPPORTED, "segment %d: row_rinv must be given for every segment or for none", g);
       if (lowbit && !s.row_scale) return fail(MLA_ERR_NULL, "segment %d: a low-bit cache needs row_scale", g);
       if (lowbit && s.row_rinv)
         return fail(MLA_ERR_UNSUPPORTED, "segment %d: QK-Norm with a low-bit cache is not supported", g);
@@ -452,13 +454,12 @@ mla_status mla_decode_splitkv(const mla_segment* segs, int n_segs, const void* q
   int wg = n_wg > 0 ? n_wg : cu_count();
   if (wg <= 0) return fail(MLA_ERR_HIP, "mla_decode_splitkv: could not query the device");
   std::vector<mla::SegArgs> sa((size_t)n_segs);
-  bool rows_path = bf && q32 && !lowbit;  // fp32 query, 16-bit rows, no QK-Norm row factors
+  const bool rows_path = bf && q32 && !lowbit;  // fp32 query, 16-bit rows
   for (int g = 0; g < n_segs; ++g) {
     const mla_segment& s = segs[g];
     sa[g] = mla::SegArgs{s.cache,     s.block_table, s.seq_lens,  s.q_rot,      s.max_rows,
                          s.page_size, s.max_pages,   s.n_pages,   s.head_begin, s.head_count,
                          s.causal,    s.part_begin,  s.n_split,   s.row_rinv,   s.row_scale};
-    rows_path = rows_path && !s.row_rinv;
   }
   mla::DecodeArgs a{};
   a.q_lat = q_lat;

@@ -972,9 +972,9 @@ static hipError_t launch_mt(const DecodeArgs& a, int mt, dim3 grid, int n_share,
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, int n_wg, bool q_f32, hipStream_t stream) {
   const int rows_total = a.s_q * a.seg.head_count;
-  // more than 32 query rows, fp32 query, no row factors: whole rows per wave
-  // (mla_decode_rows.hip)
-  if (rows_total > 32 && q_f32 && !a.seg.row_rinv) return launch_decode_rows(a, n_wg, stream);
+  // more than 32 query rows with an fp32 query (with or without QK-Norm row
+  // factors): whole rows per wave (mla_decode_rows.hip)
+  if (rows_total > 32 && q_f32) return launch_decode_rows(a, n_wg, stream);
   const int mt = row_tile(rows_total);
   int n_share, n_rg;
   decode_bf16_grid(rows_total, mt, n_wg, &n_share, &n_rg);

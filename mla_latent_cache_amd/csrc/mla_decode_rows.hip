@@ -81,6 +81,15 @@
 //    (the codes are exact in bf16) one tile before their scores; the row
 //    scales multiply the scores after the QK product and the weights before
 //    the PV product, so the PV sums weights times dequantized rows.
+//  * QK-Norm (QK-Norm MLA abstract; 16-bit rows): each stored row carries the
+//    inverse RMS of its content key.  A tile's 32 factors come with its loads
+//    (one more 4-byte load per wave) and multiply the latent part of the
+//    scores, the rotary part apart, as the int8 scales do; they do not touch
+//    the PV weights (the values are the plain latents).  The lo part's lse
+//    share then carries each token's factor: the kernel also sums weights
+//    times factors and takes the share as the weighted mean factor times
+//    scale * lo . o, leaving the weighted covariance of the factors and the
+//    lo scores, a second-order term.
 #include "mla_common.h"
 #include "mla_decode_tile.h"
 #include "mla_kernels.h"
@@ -168,7 +177,7 @@ constexpr int kI8Dma = 6;                               // loads per wave per ti
 // QM: the stored rows (0: 16-bit, 1: int4, 2: int8).  Low-bit rows land
 // packed and are unpacked into three bf16 stages: tiles it (PV), it+1 (QK)
 // and it+2 (unpacked into).
-template <int QM, int RB>
+template <int QM, int RB, bool QKN>
 struct RowsSmem {
   static constexpr int NLAT = QM ? 3 : kLatStages;
   static constexpr int NLAND = QM == 1 ? 3 : QM == 2 ? 2 : 1;
@@ -180,6 +189,9 @@ struct RowsSmem {
   char qrot[16 * RB * kRowsWaves][kRBytes];  // 16 KiB at 128-row groups
   char land[NLAND][LAND];    // int4: 30 KiB landing ring, int8: 34 KiB
   float scl[QM ? 3 : 1][kRowsWaves][QM == 1 ? 2 * kTile : QM == 2 ? kTile : 1];  // each wave's scales of a stage
+  // QK-Norm: the row factors of the tiles in flight (one shared copy per
+  // stage; entries 32..63 take the zeros of lanes past the tile)
+  float rinv[QKN ? 3 : 1][QKN ? 64 : 1];
   Piece pieces[kRowsMaxPieces];
   int n_pieces;
   int done;
@@ -541,10 +553,14 @@ __device__ __forceinline__ void pv_tile(const char* __restrict__ ls, int lane, c
 // (relative index `lim` per lane: token 4 lg + e of the first half is
 // visible when e <= lim) get -inf, i.e. weight 0.  A branch on `full` is
 // fine here: the softmax proper, which runs between the PV MFMAs, has none.
-template <int RB, int QM>
+// QM == 2 (int8 rows: the row scale) and RF (QK-Norm: the row factor) scale
+// the latent part of each score by the factor of its token; for int8 rows the
+// scale also weights the token in the PV product (wsc), for QK-Norm it only
+// enters the mean factor of the lse correction.
+template <int RB, int QM, bool RF = false>
 __device__ __forceinline__ void prep_scores(f32x4 (&s)[2][RB], const f32x4 (&sr)[2][RB], bool full,
                                             const int (&lim)[RB], const float* tsc, f32x4 (&wsc)[2]) {
-  if constexpr (QM == 2) {
+  if constexpr (QM == 2 || RF) {
     int ln = __lane_id();
     asm volatile("" : "+v"(ln));
     const int lg4 = 4 * (ln >> 4);
@@ -612,18 +628,19 @@ __device__ __forceinline__ float rows_max_raw(float v) {
 // max, its reduction over the lane groups, the max update, four pairs of
 // weights, the packing) that run one per PV column block, between the MFMAs
 // of the previous tile's PV.
-template <int RB, bool LB>
+template <int RB, bool LB, bool RF = false>
 struct SoftmaxStages {
   static constexpr int kPerRb = 8;
   static constexpr int kStages = kPerRb * RB;
   const f32x4 (&s)[2][RB];
   float (&m_used)[RB];
   float (&l_part)[RB];
+  float (&r_part)[RB];  // RF: sum of weights times row factors (QK-Norm)
   bf16x8 (&p)[RB];
   float (&alpha)[RB];
   const f32x4 (&wsc)[2];
   float sl2;
-  float mt[RB], msub[RB], lsum[RB];
+  float mt[RB], msub[RB], lsum[RB], rsum[RB];
   bool need_any = false;
 
   __device__ __forceinline__ void run(int k) {
@@ -643,15 +660,18 @@ struct SoftmaxStages {
       need_any |= need;
       msub[rb] = m_used[rb] == -INFINITY ? 0.f : m_used[rb];
       lsum[rb] = 0.f;
+      rsum[rb] = 0.f;
     } else if (st < 7) {
       const int e = st - 3;
       const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[e], sl2, -msub[rb]));  // exp2(-inf) = 0
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[e], sl2, -msub[rb]));
       lsum[rb] += p0 + p1;
+      if constexpr (RF) rsum[rb] += p0 * wsc[0][e] + p1 * wsc[1][e];
       p[rb][e] = (bf16)(LB ? p0 * wsc[0][e] : p0);
       p[rb][4 + e] = (bf16)(LB ? p1 * wsc[1][e] : p1);
     } else {
       l_part[rb] = l_part[rb] * alpha[rb] + lsum[rb];
+      if constexpr (RF) r_part[rb] = r_part[rb] * alpha[rb] + rsum[rb];
       // formed here, not sunk towards their first use in the next tile
       asm volatile("" : "+v"(p[rb]), "+v"(l_part[rb]));
     }
@@ -660,13 +680,13 @@ struct SoftmaxStages {
 };
 
 // The whole softmax at once (the first tile of a piece)
-template <int RB, bool LB>
+template <int RB, bool LB, bool RF>
 __device__ __forceinline__ bool softmax_tile(const f32x4 (&s)[2][RB], float (&m_used)[RB], float (&l_part)[RB],
-                                             bf16x8 (&p)[RB], float (&alpha)[RB], const f32x4 (&wsc)[2],
-                                             float sl2) {
-  SoftmaxStages<RB, LB> sm{s, m_used, l_part, p, alpha, wsc, sl2};
+                                             float (&r_part)[RB], bf16x8 (&p)[RB], float (&alpha)[RB],
+                                             const f32x4 (&wsc)[2], float sl2) {
+  SoftmaxStages<RB, LB, RF> sm{s, m_used, l_part, r_part, p, alpha, wsc, sl2};
 #pragma unroll
-  for (int k = 0; k < SoftmaxStages<RB, LB>::kStages; ++k) sm.run(k);
+  for (int k = 0; k < SoftmaxStages<RB, LB, RF>::kStages; ++k) sm.run(k);
   return sm.moved();
 }
 
@@ -726,12 +746,16 @@ __device__ __forceinline__ T& pick(T& a, T& b) {
 // per row).  PB: bf16 partial outputs (a compile-time choice: a branch in
 // the epilogue changes the register allocation of the tile loop).  QS: a
 // split query.
-template <int RB, int QM, bool PB, bool QS>
+template <int RB, int QM, bool PB, bool QS, bool QKN>
 __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch L) {
   constexpr int MT = 16 * RB * kRowsWaves;  // query rows of a row group
   constexpr int kOv = piece_tiles(MT, PB, QS) * kTile;  // a request's start, in rows of the work split
   constexpr bool LB = QM != 0;                           // low-bit rows: landed, then unpacked
-  using SM = RowsSmem<QM, RB>;
+  using SM = RowsSmem<QM, RB, QKN>;
+  static_assert(!QKN || QM == 0, "QK-Norm row factors with 16-bit rows only");
+  // loads per wave per 16-bit tile: its share of the rows, and with QK-Norm
+  // one more for the tile's row factors
+  constexpr int kDmaW = kDmaPerWave + (QKN ? 1 : 0);
   constexpr int NLAT = SM::NLAT;
   constexpr int RBYTES = QM == 1 ? kI4Row : QM == 2 ? kI8Row : kRowBytes;  // bytes per stored row
   __shared__ __attribute__((aligned(16))) SM sm;
@@ -750,6 +774,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
   const float* const q_rot = (const float*)sg.q_rot;
   const float* const q_lat = (const float*)a.q_lat;
   const float* const row_scale = sg.row_scale;
+  const float* const row_rinv = sg.row_rinv;
   void* const o_part = a.o_part;
   constexpr bool part_bf = PB;
   float* const lse_part = a.lse_part;
@@ -990,6 +1015,19 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
         const int n = ok ? min(kTile, pr1 - (pr0 + it * kTile)) : 0;
         return buffer_rsrc(ok ? row_scale + kSpr * row : row_scale, n * 4 * kSpr);
       };
+      // QK-Norm: the row factors of tile `it` (indexed like the rows) into
+      // their stage, one 4-byte load per lane of every wave (the waves write
+      // the same values; each counts the load like its tile loads)
+      auto load_rinv = [&](int it, int pg) {
+        if constexpr (QKN) {
+          bool ok;
+          const int64_t row = tile_row(it, pg, &ok);
+          const int n = ok ? min(kTile, pr1 - (pr0 + it * kTile)) : 0;
+          int ln = lane;
+          asm volatile("" : "+v"(ln));
+          dma4(buffer_rsrc(ok ? row_rinv + row : row_rinv, n * 4), (const char*)sm.rinv[it % 3], 4 * ln);
+        }
+      };
       auto load_lb = [&](int it, int pg) {
         if constexpr (QM == 1) tile_load_i4(tile_rsrc(it, pg), scale_rsrc(it, pg), sm.land[it % 3], wave, lane);
         if constexpr (QM == 2)
@@ -1027,6 +1065,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
           const i32x4_t rs = tile_rsrc(t, pg[t]);
 #pragma unroll
           for (int i = 0; i < kDmaPerWave; ++i) tile_load(rs, sm.lat[t], sm.rot[t], wave, lane, i);
+          load_rinv(t, pg[t]);
         }
         pg_next = pg[kLoadAhead];
       }
@@ -1107,11 +1146,12 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
           acc[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
           asm("" : "+a"(acc[db][rb]));
         }
-      float m_used[RB], l_part[RB];
+      float m_used[RB], l_part[RB], r_part[RB];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         m_used[rb] = -INFINITY;
         l_part[rb] = 0.f;
+        r_part[rb] = 0.f;
       }
 
       // relative index of the last visible token of tile `it` for each row
@@ -1133,9 +1173,12 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
 
       f32x4 sacc[2][RB];
       f32x4 racc_i4[2][RB];
-      f32x4(&racc)[2][RB] = pick<LB>(racc_i4, sacc);  // the rotary part's accumulator (apart for low-bit rows)
+      // the rotary part's accumulator (apart for low-bit rows and QK-Norm,
+      // whose factors scale the latent part only)
+      f32x4(&racc)[2][RB] = pick<LB || QKN>(racc_i4, sacc);
       auto scl_of = [&](int it) -> const float* {
         if constexpr (LB) return sm.scl[it % 3][wave];
+        if constexpr (QKN) return sm.rinv[it % 3];
         return nullptr;
       };
       bf16x8 p[RB];
@@ -1156,7 +1199,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
         load_lb(kLbFirst, pg_lb);
       } else {
         static_assert(kLoadAhead == 3, "tiles 1 and 2 stay in flight over tile 0");
-        wait_vmcnt<2 * kDmaPerWave>();
+        wait_vmcnt<2 * kDmaW>();
         wait_lgkm0();
         barrier_raw();
       }
@@ -1164,8 +1207,8 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
         qk_tile<RB>(sm.lat[0], sm.rot[0], qrot_w, lane, qh, qrl, sacc, racc);
         tile_lim(0, lim);
         // (its factor multiplies an empty O)
-        prep_scores<RB, QM>(sacc, racc, tile_full(0), lim, scl_of(0), wsc);
-        softmax_tile<RB, LB>(sacc, m_used, l_part, p, alpha, wsc, sl2);
+        prep_scores<RB, QM, QKN>(sacc, racc, tile_full(0), lim, scl_of(0), wsc);
+        softmax_tile<RB, LB, QKN>(sacc, m_used, l_part, r_part, p, alpha, wsc, sl2);
       }
       for (int it = 0; it + 1 < n_tiles; ++it) {
         // 16-bit rows: tile it+1 in LDS (this wave's loads, with tile it+2
@@ -1177,7 +1220,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
         // tile it and the unpacking of tile it+1, so tile it+2 is unpacked into
         // the stages of tile it-1 and tile it + kLbAhead lands where tile it+1
         // did (int8: its rotary entries where tile it's were).
-        wait_vmcnt<QM == 1 ? kI4Dma : QM == 2 ? 0 : kDmaPerWave>();
+        wait_vmcnt<QM == 1 ? kI4Dma : QM == 2 ? 0 : kDmaW>();
         wait_lgkm0();
         barrier_raw();
         const i32x4_t rs_next = tile_rsrc(it + kLoadAhead, pg_next);
@@ -1185,6 +1228,7 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
         char* const rot_next = sm.rot[(it + kLoadAhead) % kRotStages];
         auto load_next = [&](int i) {
           if constexpr (!LB) tile_load(rs_next, lat_next, rot_next, wave, lane, i);
+          if (i == kDmaPerWave - 1) load_rinv(it + kLoadAhead, pg_next);
         };
         if constexpr (LB) {
           load_lb(it + kLbAhead, pg_next);
@@ -1197,13 +1241,13 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
           tile_lim(it + 1, lim);
           qk_tile<RB>(sm.lat[(it + 1) % NLAT], sm.rot[(it + 1) % kRotStages], qrot_w, lane, qh, qrl, sacc, racc);
           sched_qk<RB>();
-          prep_scores<RB, QM>(sacc, racc, tile_full(it + 1), lim, scl_of(it + 1), wsc);
+          prep_scores<RB, QM, QKN>(sacc, racc, tile_full(it + 1), lim, scl_of(it + 1), wsc);
           __builtin_amdgcn_sched_barrier(0);
           // the PV of tile it with the softmax of tile it+1 between its MFMAs
           // (the scores die there: only the two tiles' P operands live across
           // the PV product)
           bf16x8 pn[RB];
-          SoftmaxStages<RB, LB> smx{sacc, m_used, l_part, pn, alpha, wsc, sl2};
+          SoftmaxStages<RB, LB, QKN> smx{sacc, m_used, l_part, r_part, pn, alpha, wsc, sl2};
           pv_tile<RB>(sm.lat[it % NLAT], lane, p, acc, load_next, [&](int db) { smx.run(db); });
           const bool moved = smx.moved();
           __builtin_amdgcn_sched_barrier(0);
@@ -1292,6 +1336,9 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const float linv = lt[rb] > 0.f ? 1.f / lt[rb] : 0.f;
+          // QK-Norm: each token's lo share carries its row factor; to first
+          // order that is the weighted mean factor times the lo share of o
+          if constexpr (QKN) cs[rb] *= rows_sum(r_part[rb]) * linv;
           const RowInfo ri = row_info(rb);
           const int64_t lse_i = ((int64_t)b * s_q * n_heads + ri.qoff) * n_part + part_begin + slot;
           if (ri.valid && lg == 0)
@@ -1311,22 +1358,30 @@ __global__ __launch_bounds__(kRowsThreads, 1) void decode_rows_kernel(RowsLaunch
   }
 }
 
-template __global__ void decode_rows_kernel<1, 0, false, false>(RowsLaunch);
-template __global__ void decode_rows_kernel<2, 0, false, false>(RowsLaunch);
-template __global__ void decode_rows_kernel<1, 1, false, false>(RowsLaunch);
-template __global__ void decode_rows_kernel<1, 2, false, false>(RowsLaunch);
-template __global__ void decode_rows_kernel<1, 0, true, false>(RowsLaunch);
-template __global__ void decode_rows_kernel<2, 0, true, false>(RowsLaunch);
-template __global__ void decode_rows_kernel<1, 1, true, false>(RowsLaunch);
-template __global__ void decode_rows_kernel<1, 2, true, false>(RowsLaunch);
-template __global__ void decode_rows_kernel<1, 0, false, true>(RowsLaunch);
-template __global__ void decode_rows_kernel<2, 0, false, true>(RowsLaunch);
-template __global__ void decode_rows_kernel<1, 1, false, true>(RowsLaunch);
-template __global__ void decode_rows_kernel<1, 2, false, true>(RowsLaunch);
-template __global__ void decode_rows_kernel<1, 0, true, true>(RowsLaunch);
-template __global__ void decode_rows_kernel<2, 0, true, true>(RowsLaunch);
-template __global__ void decode_rows_kernel<1, 1, true, true>(RowsLaunch);
-template __global__ void decode_rows_kernel<1, 2, true, true>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, 0, false, false, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<2, 0, false, false, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, 1, false, false, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, 2, false, false, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, 0, false, false, true>(RowsLaunch);
+template __global__ void decode_rows_kernel<2, 0, false, false, true>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, 0, true, false, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<2, 0, true, false, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, 1, true, false, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, 2, true, false, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, 0, true, false, true>(RowsLaunch);
+template __global__ void decode_rows_kernel<2, 0, true, false, true>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, 0, false, true, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<2, 0, false, true, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, 1, false, true, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, 2, false, true, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, 0, false, true, true>(RowsLaunch);
+template __global__ void decode_rows_kernel<2, 0, false, true, true>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, 0, true, true, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<2, 0, true, true, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, 1, true, true, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, 2, true, true, false>(RowsLaunch);
+template __global__ void decode_rows_kernel<1, 0, true, true, true>(RowsLaunch);
+template __global__ void decode_rows_kernel<2, 0, true, true, true>(RowsLaunch);
 
 int decode_rows_tile(int rows_total) { return rows_total <= 64 ? 64 : 128; }
 
@@ -1360,22 +1415,32 @@ SegCost seg_cost(const DecodeArgs& a, const SegArgs& s, int mt) {
   return c;
 }
 
-template <bool PB, bool QS>
+template <bool PB, bool QS, bool QKN>
 hipError_t launch_rows_pb(const RowsLaunch& L, int mt, int qm, int grid, hipStream_t stream) {
   const dim3 block(kRowsThreads);
-  if (qm == 1) return launch(decode_rows_kernel<1, 1, PB, QS>, dim3(grid), block, stream, L);
-  if (qm == 2) return launch(decode_rows_kernel<1, 2, PB, QS>, dim3(grid), block, stream, L);
-  if (mt == 64) return launch(decode_rows_kernel<1, 0, PB, QS>, dim3(grid), block, stream, L);
-  return launch(decode_rows_kernel<2, 0, PB, QS>, dim3(grid), block, stream, L);
+  if constexpr (!QKN) {
+    if (qm == 1) return launch(decode_rows_kernel<1, 1, PB, QS, false>, dim3(grid), block, stream, L);
+    if (qm == 2) return launch(decode_rows_kernel<1, 2, PB, QS, false>, dim3(grid), block, stream, L);
+  }
+  if (mt == 64) return launch(decode_rows_kernel<1, 0, PB, QS, QKN>, dim3(grid), block, stream, L);
+  return launch(decode_rows_kernel<2, 0, PB, QS, QKN>, dim3(grid), block, stream, L);
 }
 
-hipError_t launch_rows(const RowsLaunch& L, int mt, int qm, int grid, hipStream_t stream) {
+template <bool QKN>
+hipError_t launch_rows_q(const RowsLaunch& L, int mt, int qm, int grid, hipStream_t stream) {
   if (L.a.q_split) {
-    if (L.a.part_bf16) return launch_rows_pb<true, true>(L, mt, qm, grid, stream);
-    return launch_rows_pb<false, true>(L, mt, qm, grid, stream);
+    if (L.a.part_bf16) return launch_rows_pb<true, true, QKN>(L, mt, qm, grid, stream);
+    return launch_rows_pb<false, true, QKN>(L, mt, qm, grid, stream);
   }
-  if (L.a.part_bf16) return launch_rows_pb<true, false>(L, mt, qm, grid, stream);
-  return launch_rows_pb<false, false>(L, mt, qm, grid, stream);
+  if (L.a.part_bf16) return launch_rows_pb<true, false, QKN>(L, mt, qm, grid, stream);
+  return launch_rows_pb<false, false, QKN>(L, mt, qm, grid, stream);
+}
+
+// QK-Norm row factors are given for every segment of a launch or for none
+// (checked by the caller); they exist with 16-bit rows only.
+hipError_t launch_rows(const RowsLaunch& L, int mt, int qm, int grid, hipStream_t stream) {
+  if (L.segs[0].row_rinv) return qm ? hipErrorInvalidValue : launch_rows_q<true>(L, mt, qm, grid, stream);
+  return launch_rows_q<false>(L, mt, qm, grid, stream);
 }
 
 }  // namespace

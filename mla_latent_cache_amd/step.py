@@ -143,12 +143,12 @@ class DecodeStep:
         # The row-owning kernel reads the latent query as bf16 hi and lo
         # planes written by the fused query kernel (half the bytes per read
         # of an fp32 query): on that kernel's calls (several segments, more
-        # than 32 query rows, a low-bit cache) without QK-Norm, where the fused
-        # kernel has its MFMA shape.
+        # than 32 query rows, a low-bit cache), where the fused kernel has its
+        # MFMA shape (with QK-Norm too: the query is normalised first).
         rows = max(s_q * s.head_count for s in segments)
         rows_kernel = quant is not None or len(segments) > 1 or rows > 32
         mfma_shape = w_uk.dtype == torch.bfloat16 and w_uk.shape[1] == 128 and d_c == 512
-        can_split = (self.bf16 and rows_kernel and mfma_shape and qk_norm is None and len(self.q_rots) <= 8
+        can_split = (self.bf16 and rows_kernel and mfma_shape and len(self.q_rots) <= 8
                      and q_nope.data_ptr() % 16 == 0 and w_uk.data_ptr() % 16 == 0)
         if split_query and not can_split:
             raise ValueError("a split query needs the row-owning kernel's calls and the fused query kernel")

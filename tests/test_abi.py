@@ -203,7 +203,11 @@ def test_null_and_shape_errors_before_any_gpu_call(lib):
     assert dec([seg()], dtype=0, q_dtype=1) == 5          # fp32 cache needs an fp32 query
     assert dec([seg()], dtype=0, part_dtype=1) == 5       # and writes fp32 partials
     assert dec([seg()], part_dtype=3) == 3                # partials are fp32 or bf16
-    assert dec([seg(row_rinv=P)], q_dtype=1) == 5         # QK-Norm factors need an fp32 query
+    assert dec([seg(row_rinv=P)], q_dtype=1) == 5         # QK-Norm factors need an fp32 or split query
+    # row factors on every segment of a call or on none
+    assert dec([seg(row_rinv=P, n_split=1), seg(part_begin=1, n_split=1)]) == 5
+    assert dec([seg(n_split=1), seg(row_rinv=P, part_begin=1, n_split=1)]) == 5
+    assert dec([seg(row_rinv=P, n_split=1), seg(row_rinv=P, part_begin=1, n_split=1)], batch=0) == 0
     # int8 cache (cache_dtype 2): fp32 or split query, row_scale on every segment, no QK-Norm
     assert dec([seg()], dtype=2) == 1                     # row_scale missing
     assert dec([seg(row_scale=P)], dtype=2, q_dtype=1) == 5
@@ -214,11 +218,11 @@ def test_null_and_shape_errors_before_any_gpu_call(lib):
     assert dec([seg(row_scale=P)], dtype=3, q_dtype=1) == 5
     assert dec([seg(row_scale=P, row_rinv=P)], dtype=3) == 5
     assert dec([seg(row_scale=P)], dtype=4) == 3
-    # split query (q_dtype 4, bf16 hi and lo planes): bf16, int8 or int4 cache, no QK-Norm
+    # split query (q_dtype 4, bf16 hi and lo planes): bf16, int8 or int4 cache; QK-Norm with bf16 only
     assert dec([seg()], dtype=0, q_dtype=4) == 5
     assert dec([seg(row_scale=P)], dtype=2, q_dtype=4, batch=0) == 0
     assert dec([seg(row_scale=P)], dtype=3, q_dtype=4, batch=0) == 0
-    assert dec([seg(row_rinv=P)], q_dtype=4) == 5
+    assert dec([seg(row_rinv=P)], q_dtype=4, batch=0) == 0
     assert dec([seg()], q_dtype=5) == 3
 
 

@@ -165,6 +165,19 @@ EDGE = {
     # query normalisation runs as its own launch before mla_prepare_q
     "qknorm_two_launch_rows576": _custom("edge-qkn576", batch=9, heads=64, qk_norm=True, segs=(
         SegSpec("kv", lengths=(0, 1, 5, 37, 64, 65, 100, 130, 300), online=True),)),
+    # QK-Norm on the row-owning kernel: 128-row groups (two groups at 192
+    # rows), twice-spread scores against the lse's first-order lo share with
+    # the mean row factor, and the merge layout's segments in one launch
+    "qknorm_rows128_peaked": _custom("edge-qkn128", batch=4, heads=128, qk_norm=True, scale=2 / math.sqrt(192),
+                                     segs=(SegSpec("kv", lengths=(1, 37, 300, 1000), layout="paged", page_size=64,
+                                                   spare_pages=2, online=True),)),
+    "qknorm_rows192": _custom("edge-qkn192", batch=3, heads=64, s_q=3, qk_norm=True, segs=(
+        SegSpec("kv", lengths=(3, 95, 513), causal=True, online=True),)),
+    "qknorm_merge": _custom("edge-qknm", batch=2, heads=64, s_q=4, qk_norm=True, offset_range=(0, 200000), segs=(
+        SegSpec("doc_off", lengths=(300, 33), head_begin=0, head_count=56, shift_offset=True),
+        SegSpec("doc_on", lengths=(300, 33), head_begin=56, head_count=8, base_offset=True),
+        SegSpec("online", lengths=(70, 4), causal=True, base_offset=True, base_after="doc_on", online=True),
+    )),
     "qknorm_toy_f32": _custom("edge-qknf32", dtype="f32", batch=3, heads=2, qk_norm=True, segs=(
         SegSpec("kv", lengths=(16, 0, 130), layout="paged", page_size=8, spare_pages=1, online=True),)),
     # int8 latent cache (64-row groups of the row-owning kernel): one wave
@@ -205,6 +218,17 @@ def test_edge_case(case):
     print(f"[parity] edge {case}", flush=True)
     _, out, o_lat, lse = _run(x)
     check_step(x, out, o_lat, lse, label=case)
+
+
+@pytest.mark.parametrize("case", ["qknorm_rows128_peaked", "qknorm_rows192", "qknorm_merge"])
+def test_qknorm_rows_fp32_query(case):
+    """QK-Norm on the row-owning kernel with the fp32 latent query (the kernel
+    splits it itself) instead of the split planes the step writes by default."""
+    x = M.make_inputs(EDGE[case], seed=12, poison=True)
+    print(f"[parity] edge {case} fp32 query", flush=True)
+    st, out, o_lat, lse = _run(x, split_query=False)
+    assert not st.q_split
+    check_step(x, out, o_lat, lse, label=case + " fp32 query")
 
 
 # ------------------------------------------------------------ single calls
@@ -594,14 +618,16 @@ def test_combine_out_uv_call(out_dtype, w_dtype, dims, part_dtype):
     assert np.all(np.abs(f64(out) - out_ref) <= rel * np.abs(out_ref) + 1e-5 * rms)
 
 
-@pytest.mark.parametrize("name", ["small", "dsv3", "long", "merge", "prefill", "qknorm", "int8", "int4"])
+@pytest.mark.parametrize("name", ["small", "dsv3", "long", "merge", "prefill", "qknorm", "int8", "int4",
+                                  "qknorm_dsv3"])
 def test_full_size_sampled(name):
     """The bench's launch configuration (default grid) at full size; the
     oracle checks sampled (request, head) pairs."""
     x = M.make(name, SEEDS[name])
     print(f"[parity] full {name} seed {SEEDS[name]}", flush=True)
     _, out, o_lat, lse = _run(x)
-    n_req = {"small": 2, "dsv3": 3, "long": 1, "merge": 2, "prefill": 1, "qknorm": 2, "int8": 1, "int4": 1}[name]
+    n_req = {"small": 2, "dsv3": 3, "long": 1, "merge": 2, "prefill": 1, "qknorm": 2, "int8": 1, "int4": 1,
+             "qknorm_dsv3": 3}[name]
     reqs, heads = sample_pairs(x, n_req, 3, seed=SEEDS[name])
     errs = check_step(x, out, o_lat, lse, requests=reqs, heads=heads, label=f"{name} full")
     print(f"[parity] {name} full reqs={reqs} heads={heads}: {errs}", flush=True)
