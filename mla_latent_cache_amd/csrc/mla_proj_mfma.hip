@@ -10,7 +10,8 @@
 // 16-row MFMA blocks.  For absorb the contraction index i is the row index of
 // w_uk, so the B operand (8 consecutive i per lane) is taken from an LDS copy
 // of the weight slice with ds_read_b64_tr_b16; for out_uv the contraction
-// index c is contiguous in both operands, which are loaded straight from HBM.
+// index c is contiguous in both operands: the weights are loaded straight
+// from HBM, the o_lat rows staged once in LDS for all the workgroup's waves.
 #include "mla_common.h"
 #include "mla_kernels.h"
 
@@ -215,39 +216,63 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(const TQ* __restrict_
 }
 
 constexpr int kDv = 128;
-constexpr int kUvCols = 16;  // output columns per workgroup (one wave)
+constexpr int kUvTok = 32;                 // tokens per workgroup
+constexpr int kUvWaves = kDv / 16;         // 8 waves, one per 16 output columns
+constexpr int kUvLds = kLat * 2 + 16;      // bytes per LDS row of o_lat (padded)
 
-// One wave per (head, 16 output columns): the wave holds its 16 x 512 slice
-// of w_uv as the B operand (64 registers), so a head's weights are spread
-// over 8 workgroups and the loads of a small batch are not serialised on a
-// few compute units.
+// Workgroup (head h, tokens t0 .. t0 + 31): the o_lat rows of the block are
+// staged in LDS once and shared by the 8 waves, wave w computing output
+// columns 16 w .. 16 w + 15 with its 16 x 512 slice of w_uv as the B operand
+// (64 registers, loaded before the rows so that both fetches overlap).  Each
+// o_lat row is fetched once and a head's weights once per 32 tokens; the
+// token blocks of a head are numbered onto one XCD (blocks h + n_heads * y,
+// n_heads a multiple of 8), so their repeated weight reads meet in its L2.
 template <typename TO>
-__global__ __launch_bounds__(64) void out_uv_mfma_kernel(const bf16* __restrict__ o_lat,
-                                                         const bf16* __restrict__ w_uv, TO* __restrict__ out,
-                                                         int n_tok, int n_heads) {
+__global__ __launch_bounds__(64 * kUvWaves) void out_uv_mfma_kernel(const bf16* __restrict__ o_lat,
+                                                                    const bf16* __restrict__ w_uv,
+                                                                    TO* __restrict__ out, int n_tok, int n_heads) {
+  __shared__ __attribute__((aligned(16))) char os[kUvTok * kUvLds];
   const int h = blockIdx.x;
-  const int v0 = blockIdx.y * kUvCols;
-  const int lane = threadIdx.x;
+  const int t0 = blockIdx.y * kUvTok;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, lg = lane >> 4;
+  const int v0 = 16 * wave;
   // B operand straight from HBM: lane col v = v0 + l16, k = 32 ks + 8 lg + (0..7)
   bf16x8 wb[16];
   const bf16* wr = w_uv + ((int64_t)h * kDv + v0 + l16) * kLat + 8 * lg;
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks) wb[ks] = *(const bf16x8*)(wr + 32 * ks);
-  for (int t0 = 0; t0 < n_tok; t0 += 16) {
-    const int t = t0 + l16;
-    const bf16* orow = o_lat + ((int64_t)t * n_heads + h) * kLat + 8 * lg;
-    bf16x8 oa[16];
+  // rows t0 .. t0 + 31 (clamped to the last token: always in bounds; rows
+  // past n_tok are computed and never stored), 16 bytes per thread and load
+  constexpr int kChunks = kUvTok * (kLat / 8) / (64 * kUvWaves);  // 4
+  bf16x8 stage[kChunks];
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) oa[ks] = t < n_tok ? *(const bf16x8*)(orow + 32 * ks) : bf16x8{};
+  for (int k = 0; k < kChunks; ++k) {
+    const int e = tid + 64 * kUvWaves * k, r = e / (kLat / 8), c = e % (kLat / 8);
+    const int t = min(t0 + r, n_tok - 1);
+    stage[k] = *(const bf16x8*)(o_lat + ((int64_t)t * n_heads + h) * kLat + 8 * c);
+  }
+#pragma unroll
+  for (int k = 0; k < kChunks; ++k) {
+    const int e = tid + 64 * kUvWaves * k, r = e / (kLat / 8), c = e % (kLat / 8);
+    *(bf16x8*)(os + r * kUvLds + 16 * c) = stage[k];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int tb = 0; tb < kUvTok / 16; ++tb) {
+    if (t0 + 16 * tb >= n_tok) break;
+    // A operand: lane row 16 tb + l16, k = 32 ks + 8 lg + (0..7)
+    const char* arow = os + (16 * tb + l16) * kUvLds + 16 * lg;
     f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks)
-      acc[ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa[ks], wb[ks], acc[ks & 1], 0, 0, 0);
+    for (int ks = 0; ks < 16; ++ks) {
+      const bf16x8 a = *(const bf16x8*)(arow + 64 * ks);
+      acc[ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wb[ks], acc[ks & 1], 0, 0, 0);
+    }
     const f32x4 r = acc[0] + acc[1];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int tt = t0 + 4 * lg + e;
+      const int tt = t0 + 16 * tb + 4 * lg + e;
       if (tt < n_tok) store_f(out + ((int64_t)tt * n_heads + h) * kDv + v0 + l16, r[e]);
     }
   }
@@ -328,12 +353,12 @@ bool out_uv_mfma_ok(const void* o_lat, const void* w_uv, int d_c, int d_v) {
 
 hipError_t launch_out_uv_mfma(const void* o_lat, const void* w_uv, void* out, bool out_bf16, int n_tok,
                               int n_heads, hipStream_t stream) {
-  dim3 grid(n_heads, kDv / kUvCols);
+  const dim3 grid(n_heads, (n_tok + kUvTok - 1) / kUvTok);
   if (out_bf16)
-    return launch(out_uv_mfma_kernel<bf16>, grid, dim3(64), stream, (const bf16*)o_lat, (const bf16*)w_uv,
+    return launch(out_uv_mfma_kernel<bf16>, grid, dim3(64 * kUvWaves), stream, (const bf16*)o_lat, (const bf16*)w_uv,
                        (bf16*)out, n_tok, n_heads);
   else
-    return launch(out_uv_mfma_kernel<float>, grid, dim3(64), stream, (const bf16*)o_lat,
+    return launch(out_uv_mfma_kernel<float>, grid, dim3(64 * kUvWaves), stream, (const bf16*)o_lat,
                        (const bf16*)w_uv, (float*)out, n_tok, n_heads);
 }
 

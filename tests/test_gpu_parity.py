@@ -257,7 +257,8 @@ def test_rope_relocate_call(dtype):
             assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-5), err.max()
 
 
-@pytest.mark.parametrize("dtype,dims", [(torch.float32, (4, 4, 7)), (torch.bfloat16, (128, 512, 33))])
+@pytest.mark.parametrize("dtype,dims", [(torch.float32, (4, 4, 7)), (torch.bfloat16, (128, 512, 33)),
+                                        (torch.bfloat16, (128, 512, 1)), (torch.bfloat16, (128, 512, 100))])
 def test_absorb_and_out_uv_calls(dtype, dims):
     from mla_latent_cache_amd import ops
     d_nope, d_c, n_tok = dims
