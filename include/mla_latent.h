@@ -253,7 +253,7 @@ mla_status mla_combine_lse(const void* o_part, int part_dtype, const float* lse_
 /*
  * mla_prepare_q -- rope_relocate_q for n_shift segment shifts and
  * mla_absorb_q, fused into one launch where the absorption runs on its MFMA
- * path (in_dtype bf16, d_nope 128, d_c 512, 16-byte aligned q_nope / w_uk);
+ * path (in_dtype bf16, d_nope 128, d_c 512, 16-byte aligned q_nope / w_uk / q_lat);
  * other shapes run the two kernels one after the other.  Same arithmetic and
  * layouts as those two calls ([T] "Move the Key Projection Into the Query",
  * "Position Rotations Complicate the Absorption"; [R] query-side relocation):

@@ -149,13 +149,13 @@ mla_status mla_prepare_q(const void* q_nope, int q_dtype, const void* q_pe, cons
     return fail(MLA_ERR_SHAPE, "mla_prepare_q: n_tok=%d (<= %d) n_heads=%d d_nope=%d d_rope=%d d_c=%d", n_tok,
                 kMaxTok, n_heads, d_nope, d_rope, d_c);
   if (!(base > 1.0) || !std::isfinite(base)) return fail(MLA_ERR_SHAPE, "mla_prepare_q: base=%g", base);
-  const bool mfma = in_dtype == MLA_BF16 && mla::absorb_mfma_ok(q_nope, w_uk, d_nope, d_c);
+  const bool mfma = in_dtype == MLA_BF16 && mla::absorb_mfma_ok(q_nope, w_uk, q_lat, d_nope, d_c);
   if (q_dtype != in_dtype && !(q_dtype == MLA_F32 && mfma))
     return fail(MLA_ERR_UNSUPPORTED, "mla_prepare_q: an fp32 query with bf16 weights needs d_nope=128, d_c=512 "
-                "and 16-byte aligned q_nope and w_uk");
+                "and 16-byte aligned q_nope, w_uk and q_lat");
   if (lat_dtype == MLA_BF16X2 && !mfma)
     return fail(MLA_ERR_UNSUPPORTED, "mla_prepare_q: a split q_lat (MLA_BF16X2) needs bf16 weights, d_nope=128, "
-                "d_c=512 and 16-byte aligned q_nope and w_uk");
+                "d_c=512 and 16-byte aligned q_nope, w_uk and q_lat");
   if (n_tok == 0) return ok();
   const hipStream_t st = (hipStream_t)stream;
   if (mfma) {
@@ -202,9 +202,9 @@ mla_status mla_prepare_q_qknorm(const void* q_nope, int q_dtype, const float* g_
     return fail(MLA_ERR_SHAPE, "mla_prepare_q_qknorm: n_tok=%d n_heads=%d d_rope=%d", n_tok, n_heads, d_rope);
   if (!(base > 1.0) || !std::isfinite(base)) return fail(MLA_ERR_SHAPE, "mla_prepare_q_qknorm: base=%g", base);
   if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(MLA_ERR_SHAPE, "mla_prepare_q_qknorm: eps=%g", (double)eps);
-  if (in_dtype != MLA_BF16 || !mla::absorb_mfma_ok(q_nope, w_uk, d_nope, d_c))
+  if (in_dtype != MLA_BF16 || !mla::absorb_mfma_ok(q_nope, w_uk, q_lat, d_nope, d_c))
     return fail(MLA_ERR_UNSUPPORTED, "mla_prepare_q_qknorm: needs bf16 w_uk and q_pe, d_nope=128, d_c=512 and "
-                "16-byte aligned q_nope and w_uk");
+                "16-byte aligned q_nope, w_uk and q_lat");
   if ((int64_t)n_tok * n_heads > mla::kQkFusedRows)
     return fail(MLA_ERR_UNSUPPORTED, "mla_prepare_q_qknorm: n_tok * n_heads = %lld (at most %d; use "
                 "mla_qknorm_query, then mla_prepare_q)", (long long)n_tok * n_heads, mla::kQkFusedRows);

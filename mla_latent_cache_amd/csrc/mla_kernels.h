@@ -69,7 +69,7 @@ bool out_proj_mfma_ok(const void* x, bool x_bf16, const void* w, bool w_bf16, in
 hipError_t launch_out_proj(const void* x, bool x_bf16, const void* w, bool w_bf16, void* out, bool out_bf16,
                            int n_tok, int k_in, int d_model, hipStream_t stream);
 // bf16 MFMA variants (d_nope = 128, d_c = 512, d_v = 128, 16-byte aligned).
-bool absorb_mfma_ok(const void* q_nope, const void* w_uk, int d_nope, int d_c);
+bool absorb_mfma_ok(const void* q_nope, const void* w_uk, const void* q_lat, int d_nope, int d_c);
 
 // Rotation targets of the fused query preparation (one per segment shift).
 constexpr int kMaxShift = 8;

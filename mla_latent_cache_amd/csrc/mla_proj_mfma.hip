@@ -25,6 +25,7 @@ constexpr int kNope = 128;        // d_nope of the bf16 fast path
 constexpr int kLat = 512;         // d_c
 constexpr int kAbsCols = 128;     // output columns per absorb workgroup
 constexpr int kAbsLds = kAbsCols * 2 + 16;  // bytes per LDS weight row (padded)
+constexpr int kAbsOut = kAbsCols + 4;       // floats per LDS row of a token block's results (padded)
 
 // Workgroup (head h, output columns j0 .. j0 + 127) of the absorption.  An
 // fp32 query (TQ = float) enters as bf16 hi + lo parts (q = hi + lo to about
@@ -41,6 +42,15 @@ __device__ __forceinline__ void absorb_block(const TQ* __restrict__ q_nope, cons
   constexpr bool QF = sizeof(TQ) == 4 || QKN;  // hi + lo parts
   __shared__ float inv_s[16];
   __shared__ __attribute__((aligned(16))) char wl[kNope * kAbsLds];
+  // up to 16 tokens (one token block): the results go through LDS, the 4
+  // waves writing their column blocks, then every thread storing 8
+  // consecutive columns of one token (16-byte stores of whole row segments
+  // instead of 2- or 4-byte ones; measured 4.65 -> 4.20 us for 4 tokens x 16
+  // heads).  With more blocks each would add two barriers, which cost more
+  // than the stores save (64 tokens x 128 heads: 15.1 -> 16.3 us), so those
+  // store from the MFMA layout directly.
+  __shared__ __attribute__((aligned(16))) float res[16 * kAbsOut];
+  const bool staged = n_tok <= 16;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, lg = lane >> 4;
   // weight slice w_uk[h][0:128][j0:j0+128] -> LDS (row i: 256 B + pad)
@@ -158,6 +168,11 @@ __device__ __forceinline__ void absorb_block(const TQ* __restrict__ q_nope, cons
         if constexpr (QF) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[ks % (QF ? 4 : 1)], wb, acc, 0, 0, 0);
       }
       // D layout: lane holds column c0 + l16, rows (tokens) 4 lg + e
+      if (staged) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) res[(4 * lg + e) * kAbsOut + c0 + l16] = acc[e];
+        continue;
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int tt = t0 + 4 * lg + e;
@@ -170,6 +185,40 @@ __device__ __forceinline__ void absorb_block(const TQ* __restrict__ q_nope, cons
           row[kLat + j0 + c0 + l16] = (bf16)(acc[e] - (float)hi);
         } else {
           store_f(q_lat + ((int64_t)tt * n_heads + h) * kLat + j0 + c0 + l16, acc[e]);
+        }
+      }
+    }
+    if (staged) {
+      __syncthreads();
+      // thread: token r of the block, columns 8 c8 .. 8 c8 + 7 of the slice
+      const int r = tid >> 4, c8 = tid & 15;
+      const int tt = t0 + r;
+      const f32x4 a = *(const f32x4*)(res + r * kAbsOut + 8 * c8);
+      const f32x4 b = *(const f32x4*)(res + r * kAbsOut + 8 * c8 + 4);
+      if (tt < n_tok) {
+        const int64_t th = (int64_t)tt * n_heads + h;
+        if constexpr (std::is_same_v<TO, SplitBf16>) {
+          // hi plane, then lo plane, of the token's row
+          bf16x8 hi8, lo8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x = e < 4 ? a[e] : b[e - 4];
+            const bf16 hi = (bf16)x;
+            hi8[e] = hi;
+            lo8[e] = (bf16)(x - (float)hi);
+          }
+          bf16* row = (bf16*)q_lat + th * (2 * kLat) + j0 + 8 * c8;
+          *(bf16x8*)row = hi8;
+          *(bf16x8*)(row + kLat) = lo8;
+        } else if constexpr (std::is_same_v<TO, float>) {
+          float* row = q_lat + th * kLat + j0 + 8 * c8;
+          *(f32x4*)row = a;
+          *(f32x4*)(row + 4) = b;
+        } else {
+          bf16x8 v8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v8[e] = (bf16)(e < 4 ? a[e] : b[e - 4]);
+          *(bf16x8*)(q_lat + th * kLat + j0 + 8 * c8) = v8;
         }
       }
     }
@@ -282,8 +331,8 @@ bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
 
-bool absorb_mfma_ok(const void* q_nope, const void* w_uk, int d_nope, int d_c) {
-  return d_nope == kNope && d_c == kLat && al16(q_nope) && al16(w_uk);
+bool absorb_mfma_ok(const void* q_nope, const void* w_uk, const void* q_lat, int d_nope, int d_c) {
+  return d_nope == kNope && d_c == kLat && al16(q_nope) && al16(w_uk) && al16(q_lat);
 }
 
 template <typename TL, typename TR, typename TQ>

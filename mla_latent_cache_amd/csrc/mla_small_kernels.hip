@@ -102,7 +102,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(const T* __restrict__ q_nop
 
 hipError_t launch_absorb(const void* q_nope, const void* w_uk, bool in_bf, void* q_lat, bool out_bf, int n_tok,
                          int n_heads, int d_nope, int d_c, hipStream_t stream) {
-  if (in_bf && absorb_mfma_ok(q_nope, w_uk, d_nope, d_c))
+  if (in_bf && absorb_mfma_ok(q_nope, w_uk, q_lat, d_nope, d_c))
     return launch_absorb_mfma(q_nope, w_uk, q_lat, out_bf, n_tok, n_heads, stream);
   dim3 grid(n_heads, (d_c + 255) / 256);
 #define MLA_ABSORB(TI, TO)                                                                                \
