@@ -47,7 +47,7 @@ def test_chain_mini(name):
     print(f"[parity] {name}: {errs}", flush=True)
 
 
-@pytest.mark.parametrize("name", ["dsv3", "long", "merge", "prefill", "int4", "int8"])
+@pytest.mark.parametrize("name", ["dsv3", "long", "merge", "prefill", "int4", "int8", "qknorm_dsv3"])
 @pytest.mark.parametrize("split_query", [True, False])
 def test_chain_mini_query_format(name, split_query):
     """The row-owning kernel's two query formats: bf16 hi and lo planes
@@ -85,8 +85,9 @@ def test_grid_extremes(n_wg):
     check_step(x, out, o_lat, lse, label=f"merge-mini n_wg={n_wg}")
 
 
-def test_repeatable_bitwise():
-    x = M.make("merge", 9, mini=True)
+@pytest.mark.parametrize("name", ["merge", "qknorm_dsv3"])
+def test_repeatable_bitwise(name):
+    x = M.make(name, 9, mini=True)
     st, out, o_lat, lse = _run(x)
     a = (out.clone(), o_lat.clone(), lse.clone())
     st.run()
@@ -637,7 +638,7 @@ def test_full_size_sampled(name):
 
 
 # ------------------------------------------------------------ graph capture
-@pytest.mark.parametrize("name", ["dsv3", "merge", "qknorm", "int8", "small"])
+@pytest.mark.parametrize("name", ["dsv3", "merge", "qknorm", "int8", "small", "qknorm_dsv3"])
 def test_graph_replay_matches_eager(name):
     """The five calls enqueue only kernels on the caller's stream, so a step
     can be captured into a HIP graph; every replay must equal the eager run."""
