@@ -706,6 +706,70 @@ __global__ __launch_bounds__(256) void qknorm_query_kernel(const TI* __restrict_
   for (int i = threadIdx.x; i < n_hd; i += 256) o[i] = g_q[i] * g_k[i] * load_f(q + i) * inv;
 }
 
+// Rows of up to 16384 entries (n_hd a multiple of 8, every pointer 16-byte
+// aligned): 1024 threads, each holding two groups of 8 consecutive entries
+// with their g_q and g_k in registers, so the row and both weight vectors are
+// read once, in one round of loads, before the sum of squares.
+template <typename TI>
+__global__ __launch_bounds__(1024) void qknorm_query_reg_kernel(const TI* __restrict__ q_nope,
+                                                                const float* __restrict__ g_q,
+                                                                const float* __restrict__ g_k, int n_hd, float eps,
+                                                                float* __restrict__ q_out) {
+  constexpr int kG = 2;  // groups of 8 entries per thread
+  __shared__ float red[16];
+  const int t = blockIdx.x;
+  const TI* q = q_nope + (int64_t)t * n_hd;
+  f32x4 v[kG][2], gq[kG][2], gk[kG][2];
+#pragma unroll
+  for (int k = 0; k < kG; ++k) {
+    const int i = 8 * ((int)threadIdx.x + 1024 * k);
+    const bool ok = i < n_hd;
+    const int ic = ok ? i : 0;  // always in bounds; the group is dropped below
+    if constexpr (sizeof(TI) == 4) {
+      v[k][0] = *(const f32x4*)(q + ic);
+      v[k][1] = *(const f32x4*)(q + ic + 4);
+    } else {
+      const bf16x8 b = *(const bf16x8*)(q + ic);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[k][0][e] = (float)b[e];
+        v[k][1][e] = (float)b[4 + e];
+      }
+    }
+    gq[k][0] = *(const f32x4*)(g_q + ic);
+    gq[k][1] = *(const f32x4*)(g_q + ic + 4);
+    gk[k][0] = *(const f32x4*)(g_k + ic);
+    gk[k][1] = *(const f32x4*)(g_k + ic + 4);
+    if (!ok) v[k][0] = v[k][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < kG; ++k)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss += v[k][0][e] * v[k][0][e] + v[k][1][e] * v[k][1][e];
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) tot += red[w];  // a fixed order
+  const float inv = 1.f / sqrtf(tot / (float)n_hd + eps);
+  float* o = q_out + (int64_t)t * n_hd;
+#pragma unroll
+  for (int k = 0; k < kG; ++k) {
+    const int i = 8 * ((int)threadIdx.x + 1024 * k);
+    if (i >= n_hd) continue;
+    f32x4 y0, y1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      y0[e] = gq[k][0][e] * gk[k][0][e] * v[k][0][e] * inv;
+      y1[e] = gq[k][1][e] * gk[k][1][e] * v[k][1][e] * inv;
+    }
+    *(f32x4*)(o + i) = y0;
+    *(f32x4*)(o + i + 4) = y1;
+  }
+}
+
 // The same with 8 consecutive entries per thread and load (n_hd a multiple
 // of 8, every pointer 16-byte aligned): the sum of squares with four loads
 // in flight per thread, then the scaled row from a second (cached) read.
@@ -819,6 +883,13 @@ hipError_t launch_qknorm_query(const void* q_nope, bool in_bf16, const float* g_
                                int n_heads, int d_nope, float eps, float* q_out, hipStream_t stream) {
   const int n_hd = n_heads * d_nope;
   auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  if (n_hd % 8 == 0 && n_hd <= 8 * 1024 * 2 && al16(q_nope) && al16(g_q) && al16(g_k) && al16(q_out)) {
+    if (in_bf16)
+      return launch(qknorm_query_reg_kernel<bf16>, dim3(n_tok), dim3(1024), stream, (const bf16*)q_nope, g_q, g_k,
+                    n_hd, eps, q_out);
+    return launch(qknorm_query_reg_kernel<float>, dim3(n_tok), dim3(1024), stream, (const float*)q_nope, g_q, g_k,
+                  n_hd, eps, q_out);
+  }
   if (n_hd % 8 == 0 && al16(q_nope) && al16(g_q) && al16(g_k) && al16(q_out)) {
     if (in_bf16)
       return launch(qknorm_query_vec_kernel<bf16>, dim3(n_tok), dim3(256), stream, (const bf16*)q_nope, g_q, g_k,

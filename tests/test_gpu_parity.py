@@ -486,10 +486,26 @@ def test_combine_call(out_dtype, n_rows, n_part, part_dtype):
         assert np.all(np.abs(got - o_ref) <= rel * np.abs(o_ref) + 1e-6), r
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_qknorm_query_wide(dtype):
+    """mla_qknorm_query on rows wider than 16384 entries (160 heads x 128):
+    the kernel that reads each row in rounds of four loads per thread."""
+    from mla_latent_cache_amd import ops
+    n_tok, H, d_nope, eps = 3, 160, 128, 1e-6
+    q = _rand((n_tok, H, d_nope), dtype, 51)
+    g_q = 1 + 0.1 * _rand((H, d_nope), torch.float32, 52)
+    g_k = 1 + 0.1 * _rand((H, d_nope), torch.float32, 53)
+    q_out = ops.qknorm_query(q.cuda(), g_q.cuda(), g_k.cuda(), eps)
+    torch.cuda.synchronize()
+    for t in range(n_tok):
+        ref = f64(g_q) * f64(g_k) * f64(q[t]) * O.rms_inverse(f64(q[t]), eps)
+        assert np.all(np.abs(f64(q_out[t]) - ref) <= 1e-5 * np.abs(ref) + 1e-7), t
+
+
 @pytest.mark.parametrize("dtype,dims", [(torch.float32, (7, 5, 24, 40, 48, 37)),
                                         (torch.bfloat16, (3, 16, 128, 512, 576, 70)),
                                         (torch.float32, (4, 3, 6, 8, 10, 20)),        # 18 per token: scalar loads
-                                        (torch.bfloat16, (5, 128, 128, 512, 576, 40))])  # 8 loads per thread
+                                        (torch.bfloat16, (5, 128, 128, 512, 576, 40))])  # 16384 per token
 def test_qknorm_calls(dtype, dims):
     """mla_qknorm_query / _key_gram / _key_rinv against the direct RMS of the
     query over all heads and of each row's expanded key U_K c over all heads."""
